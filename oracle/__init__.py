@@ -1,0 +1,359 @@
+"""CPU oracle for the matmul sum-check prover.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The product path never imports this
+package, and this package imports nothing from the product.
+
+``oracle.c`` holds the arithmetic (plain C, exact: field products through
+unsigned __int128 and ``%``, integer sums in int64). This module marshals numpy
+arrays into it and strings the steps of a layer proof together in the order of
+"How fast can FlashProve go", §2 (witness, then sum-check claims about the
+committed tables and weights) and §3.1 (the remainder of each rescale is
+committed beside the rescaled output). Small scalar field arithmetic here uses
+Python integers with ``% P``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+P = 0xFFFFFFFF00000001
+INV2 = (P + 1) // 2
+REASONS = {0: "OK", 1: "INITIAL_CLAIM", 2: "ROUND_SUM", 3: "FINAL_CLAIM", 4: "FINAL_OPENING",
+           5: "RESCALE_IDENTITY", 6: "WITNESS_MISMATCH"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (never hipcc)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        sig = {
+            "or_add": (u64, [u64, u64]), "or_sub": (u64, [u64, u64]), "or_mul": (u64, [u64, u64]),
+            "or_from_int": (u64, [i64]), "or_pow": (u64, [u64, u64]),
+            "or_eval_deg2": (u64, [u64, u64, u64, u64]),
+            "or_witness": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp]),
+            "or_witness_entries": (None, [vp, i64, vp, i64, i32, i64, vp, vp, vp]),
+            "or_eq_table": (None, [vp, i32, vp]),
+            "or_eq_at": (u64, [vp, i32, i64]),
+            "or_fold_rows": (None, [vp, i32, i64, i32, i32, vp, vp, i32]),
+            "or_fold_cols": (None, [vp, i32, i64, i32, vp, i64, vp, vp]),
+            "or_mle_brute": (u64, [vp, i32, vp]),
+            "or_mle_seq": (u64, [vp, i32, vp]),
+            "or_mle_matrix": (u64, [vp, i32, i64, i32, i32, vp, i32, vp, i32]),
+            "or_sumcheck": (None, [i32, vp, vp, vp, i32, vp, vp, vp, vp]),
+            "or_check_sumcheck": (ctypes.c_int, [i32, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
+            "or_check_rescale": (ctypes.c_int, [vp, vp, vp, i64, i32, vp]),
+            "or_check_witness": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle needs C-contiguous arrays"
+    return a.ctypes.data
+
+
+def _u64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint64))
+
+
+def log2ceil(v: int) -> int:
+    return 0 if v <= 1 else (int(v) - 1).bit_length()
+
+
+# ------------------------------------------------------------------ field --
+def add(a, b): return int(lib().or_add(a, b))
+def sub(a, b): return int(lib().or_sub(a, b))
+def mul(a, b): return int(lib().or_mul(a, b))
+def from_int(v): return int(lib().or_from_int(int(v)))
+def power(a, e): return int(lib().or_pow(a, e))
+def eval_deg2(g0, g1, g2, x): return int(lib().or_eval_deg2(g0, g1, g2, x))
+
+
+# ---------------------------------------------------------------- witness --
+def witness(X: np.ndarray, W: np.ndarray, s: int):
+    """Z = X W^T (int32), Y = clamp(floor((Z + 2^(s-1)) / 2^s)), R = Z - 2^s Q."""
+    X, W = np.ascontiguousarray(X, np.int8), np.ascontiguousarray(W, np.int8)
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    assert W.shape[1] == d_in and 1 <= s <= 8
+    Z = np.empty((T, d_out), np.int32)
+    Y = np.empty((T, d_out), np.int8)
+    R = np.empty((T, d_out), np.int8)
+    rc = lib().or_witness(_p(X), d_in, _p(W), d_in, T, d_in, d_out, s, _p(Z), _p(Y), _p(R))
+    if rc != 0:
+        raise OverflowError("|Z| >= 2^31")
+    return Z, Y, R
+
+
+def witness_entries(X, W, ts, os_):
+    X, W = np.ascontiguousarray(X, np.int8), np.ascontiguousarray(W, np.int8)
+    ts = np.ascontiguousarray(ts, np.int32)
+    os_ = np.ascontiguousarray(os_, np.int32)
+    out = np.empty(len(ts), np.int64)
+    lib().or_witness_entries(_p(X), X.shape[1], _p(W), W.shape[1], X.shape[1], len(ts), _p(ts), _p(os_), _p(out))
+    return out
+
+
+def rescale(Z: np.ndarray, s: int):
+    """Q, R, Y of integer values Z, by explicit floor division (no shifts)."""
+    Z = np.asarray(Z, np.int64)
+    Q = np.floor_divide(Z + (1 << (s - 1)), 1 << s)
+    R = Z - Q * (1 << s)
+    return Q, R, np.clip(Q, -128, 127)
+
+
+# --------------------------------------------------------------------- eq --
+def eq_table(r) -> np.ndarray:
+    r = _u64(r)
+    E = np.empty(1 << len(r), np.uint64)
+    lib().or_eq_table(_p(r), len(r), _p(E))
+    return E
+
+
+def eq_at(r, k: int) -> int:
+    r = _u64(r)
+    return int(lib().or_eq_at(_p(r), len(r), k))
+
+
+# ------------------------------------------------------------------ folds --
+def fold_rows(M: np.ndarray, E, cols_pad: int | None = None) -> np.ndarray:
+    """out[k] = sum_{t < rows} E[t] M[t, k]; zero for cols <= k < cols_pad."""
+    M = np.ascontiguousarray(M)
+    assert M.dtype in (np.int8, np.int32)
+    rows, cols = M.shape
+    E = _u64(E)
+    assert len(E) >= rows
+    cols_pad = cols if cols_pad is None else cols_pad
+    out = np.empty(cols_pad, np.uint64)
+    lib().or_fold_rows(_p(M), M.dtype.itemsize, cols, rows, cols, _p(E), _p(out), cols_pad)
+    return out
+
+
+def fold_cols(M: np.ndarray, E, ks) -> np.ndarray:
+    M = np.ascontiguousarray(M)
+    rows, cols = M.shape
+    E = _u64(E)
+    ks = np.ascontiguousarray(ks, np.int32)
+    out = np.empty(len(ks), np.uint64)
+    lib().or_fold_cols(_p(M), M.dtype.itemsize, cols, rows, _p(E), len(ks), _p(ks), _p(out))
+    return out
+
+
+# -------------------------------------------------------------------- MLE --
+def mle_brute(A, z) -> int:
+    A, z = _u64(A), _u64(z)
+    assert len(A) == 1 << len(z)
+    return int(lib().or_mle_brute(_p(A), len(z), _p(z)))
+
+
+def mle_seq(A, z) -> int:
+    A, z = _u64(A), _u64(z)
+    assert len(A) == 1 << len(z)
+    return int(lib().or_mle_seq(_p(A), len(z), _p(z)))
+
+
+def mle_matrix(M: np.ndarray, r_rows, r_cols) -> int:
+    """M~(r_cols || r_rows) of an int8/int32 matrix zero-padded to powers of two."""
+    M = np.ascontiguousarray(M)
+    rows, cols = M.shape
+    r_rows, r_cols = _u64(r_rows), _u64(r_cols)
+    assert rows <= 1 << len(r_rows) and cols <= 1 << len(r_cols)
+    return int(lib().or_mle_matrix(_p(M), M.dtype.itemsize, cols, rows, cols,
+                                   _p(r_rows), len(r_rows), _p(r_cols), len(r_cols)))
+
+
+# -------------------------------------------------------------- sum-check --
+def sumcheck(As, Bs, r, rho=None):
+    """Sum-check over pairs (A_j, B_j) of 2^n tables; returns (rounds[n,3],
+    finals[n_pairs,2], claim0)."""
+    As = [_u64(a) for a in As]
+    Bs = [_u64(b) for b in Bs]
+    r = _u64(r)
+    n = len(r)
+    for a, b in zip(As, Bs):
+        assert len(a) == len(b) == 1 << n
+    k = len(As)
+    pa = (ctypes.c_void_p * k)(*[_p(a) for a in As])
+    pb = (ctypes.c_void_p * k)(*[_p(b) for b in Bs])
+    rho_a = None if rho is None else _u64(rho)
+    rounds = np.zeros((max(n, 1), 3), np.uint64)
+    finals = np.empty((k, 2), np.uint64)
+    c0 = ctypes.c_uint64()
+    lib().or_sumcheck(k, pa, pb, _p(rho_a), n, _p(r), _p(rounds), _p(finals), ctypes.byref(c0))
+    return rounds[:n], finals, int(c0.value)
+
+
+def check_sumcheck(rounds, finals, r, c0, rho=None, As=None, Bs=None):
+    """Verifier-side checks; returns (reason name, where)."""
+    rounds = _u64(rounds).reshape(-1, 3)
+    finals = _u64(finals).reshape(-1, 2)
+    r = _u64(r)
+    k = finals.shape[0]
+    pa = pb = None
+    if As is not None:
+        As = [_u64(a) for a in As]
+        Bs = [_u64(b) for b in Bs]
+        pa = (ctypes.c_void_p * k)(*[_p(a) for a in As])
+        pb = (ctypes.c_void_p * k)(*[_p(b) for b in Bs])
+    rho_a = None if rho is None else _u64(rho)
+    where = ctypes.c_int32()
+    rc = lib().or_check_sumcheck(k, pa, pb, _p(rho_a), len(r), _p(r), _p(rounds), _p(finals),
+                                 int(c0) % P, ctypes.byref(where))
+    return REASONS[rc], int(where.value)
+
+
+def check_rescale(Z, Y, R, s):
+    Z = np.ascontiguousarray(Z, np.int32)
+    Y = np.ascontiguousarray(Y, np.int8)
+    R = np.ascontiguousarray(R, np.int8)
+    where = ctypes.c_int64()
+    rc = lib().or_check_rescale(_p(Z), _p(Y), _p(R), Z.size, s, ctypes.byref(where))
+    return REASONS[rc], int(where.value)
+
+
+def check_witness(X, W, Z):
+    X, W = np.ascontiguousarray(X, np.int8), np.ascontiguousarray(W, np.int8)
+    Z = np.ascontiguousarray(Z, np.int32)
+    where = ctypes.c_int64()
+    rc = lib().or_check_witness(_p(X), X.shape[1], _p(W), W.shape[1], X.shape[0], X.shape[1], W.shape[0],
+                                _p(Z), ctypes.byref(where))
+    return REASONS[rc], int(where.value)
+
+
+# ----------------------------------------------------------- layer proofs --
+def pad_to(v: np.ndarray, size: int) -> np.ndarray:
+    out = np.zeros(size, np.uint64)
+    out[:len(v)] = v
+    return out
+
+
+def prove_matmul(X, W, s, r_t, r_o, r_rounds, witness_full=True, n_pad=None, x_fold=None):
+    """One matmul claim: witness, eq tables, folds, claim and sum-check.
+
+    The claim is c0 = Z~(r_o || r_t); the sum-check runs over k on
+    x'[k] = X~(k || r_t) and w'[k] = W~(k || r_o), zero-padded to 2^n.
+    With ``witness_full`` False the witness is skipped and c0 is the
+    sum-check's own initial claim sum_k x'[k] w'[k] (equal to Z~ because
+    Z = X W^T); callers use this at sizes where the full matmul is too slow.
+    """
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    n = log2ceil(d_in) if n_pad is None else n_pad
+    assert len(r_rounds) == n and len(r_t) == log2ceil(T) and len(r_o) == log2ceil(d_out)
+    out = {}
+    E_t, E_o = eq_table(r_t), eq_table(r_o)
+    out["E_t"], out["E_o"] = E_t, E_o
+    out["x_fold"] = fold_rows(X, E_t, 1 << n) if x_fold is None else x_fold
+    out["w_fold"] = fold_rows(W, E_o, 1 << n)
+    rounds, finals, claim0 = sumcheck([out["x_fold"]], [out["w_fold"]], r_rounds)
+    out["rounds"], out["finals"], out["claim0"] = rounds, finals, claim0
+    if witness_full:
+        Z, Y, R = witness(X, W, s)
+        out["Z"], out["Y"], out["R"] = Z, Y, R
+        out["c0"] = mle_matrix(Z, r_t, r_o)
+    else:
+        out["c0"] = claim0
+    return out
+
+
+def group_tokens(route: np.ndarray, n_experts: int):
+    """Tokens of each expert in ascending token order (stable by expert)."""
+    order = np.argsort(route, kind="stable")
+    counts = np.bincount(route, minlength=n_experts)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    return [order[offs[e]:offs[e + 1]] for e in range(n_experts)]
+
+
+def prove_config(cfg, inp: dict, ch: dict, witness_full=True, experts=None):
+    """The whole layer proof for one workload description (see synth)."""
+    s = cfg.s
+    if cfg.kind == "single":
+        m = cfg.matmuls[0]
+        return {m.name: prove_matmul(inp[m.x], inp[m.w], s, ch["r_t"], ch["r_o"], ch["rounds"], witness_full)}
+    if cfg.kind == "rlc_out":
+        res, xf = {}, {}
+        E_t = eq_table(ch["r_t"])
+        for m in cfg.matmuls:
+            key = (m.x, m.n)
+            if key not in xf:
+                xf[key] = fold_rows(inp[m.x], E_t, 1 << m.n)
+            res[m.name] = prove_matmul(inp[m.x], inp[m.w], s, ch["r_t"], ch["r_o/" + m.name],
+                                       ch["rounds/" + m.name], witness_full, x_fold=xf[key])
+        C = 0
+        for m in cfg.matmuls:
+            g = res[m.name]["rounds"][-1]
+            gn = eval_deg2(int(g[0]), int(g[1]), int(g[2]), int(ch["rounds/" + m.name][-1]))
+            C = (C + int(ch["rho/" + m.name][0]) * gn) % P
+        res["rlc"] = C
+        return res
+    if cfg.kind == "batched":
+        res, xf = {}, {}
+        n = cfg.batched_n
+        E_t = eq_table(ch["r_t"])
+        As, Bs, rho = [], [], []
+        c0 = 0
+        for m in cfg.matmuls:
+            if m.x not in xf:
+                xf[m.x] = fold_rows(inp[m.x], E_t, 1 << n)
+            E_o = eq_table(ch["r_o/" + m.name])
+            wf = fold_rows(inp[m.w], E_o, 1 << n)
+            one = {"E_o": E_o, "x_fold": xf[m.x], "w_fold": wf}
+            if witness_full:
+                Z, Y, R = witness(inp[m.x], inp[m.w], s)
+                one.update(Z=Z, Y=Y, R=R, c0=mle_matrix(Z, ch["r_t"], ch["r_o/" + m.name]))
+            res[m.name] = one
+            As.append(xf[m.x])
+            Bs.append(wf)
+            rho.append(int(ch["rho/" + m.name][0]))
+        rounds, finals, claim0 = sumcheck(As, Bs, ch["rounds"], rho=rho)
+        res["E_t"] = E_t
+        res["batch"] = {"rounds": rounds, "finals": finals, "claim0": claim0, "rho": rho}
+        if witness_full:
+            for m, rj in zip(cfg.matmuls, rho):
+                c0 = (c0 + rj * res[m.name]["c0"]) % P
+            res["batch"]["c0"] = c0
+        return res
+    if cfg.kind == "moe":
+        route = inp["route"]
+        groups = group_tokens(route, cfg.n_experts)
+        res = {}
+        for e in range(cfg.n_experts):
+            toks = groups[e]
+            if len(toks) == 0 or (experts is not None and e not in experts):
+                continue
+            Xe = np.ascontiguousarray(inp["X"][toks])
+            He = np.ascontiguousarray(inp["H"][toks])
+            r_t = ch["r_t/%d" % e]
+            up = prove_matmul(Xe, inp["W1_%d" % e], s, r_t, ch["r_o_up/%d" % e], ch["rounds_up/%d" % e],
+                              witness_full)
+            dn = prove_matmul(He, inp["W2_%d" % e], s, r_t, ch["r_o_down/%d" % e], ch["rounds_down/%d" % e],
+                              witness_full)
+            res[e] = {"tokens": toks, "up": up, "down": dn}
+        return res
+    raise ValueError(cfg.kind)

@@ -1,0 +1,21 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload (minutes of host CPU)")
+
+
+@pytest.fixture(scope="session")
+def fp():
+    """The product library; GPU tests fail loudly if it is missing."""
+    import zero_knowledge_proof_amd as fp_mod
+    fp_mod.require_gpu()
+    return fp_mod

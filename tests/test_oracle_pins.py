@@ -1,0 +1,357 @@
+"""Pins for the CPU oracle: closed forms, worked cases, invariants and brute
+force, chosen so that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them. CPU only."""
+import itertools
+import os
+import random
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+P = O.P
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ------------------------------------------------------------------ field --
+def test_field_closed_forms():
+    # 2^64 = 2^32 - 1 and 2^96 = -1 (mod p), so 2 has multiplicative order 192.
+    assert O.power(2, 64) == 2**32 - 1
+    assert O.power(2, 96) == P - 1
+    assert O.power(2, 192) == 1
+    assert O.mul(2, O.INV2) == 1
+    assert O.INV2 == 0x7FFFFFFF80000001
+    # p - 1 = 2^32 (2^32 - 1): Fermat and the 2-adic part of the group order.
+    rng = random.Random(7)
+    for _ in range(200):
+        a = rng.randrange(1, P)
+        assert O.power(a, P - 1) == 1
+        assert O.power(a, (P - 1) // 2) in (1, P - 1)  # Euler's criterion
+    # 7 generates the multiplicative group: 7^((p-1)/q) != 1 for each prime q | p-1
+    for q in (2, 3, 5, 17, 257, 65537):
+        assert (P - 1) % q == 0
+        assert O.power(7, (P - 1) // q) != 1
+    assert O.from_int(-1) == P - 1 and O.from_int(-128) == P - 128 and O.from_int(5) == 5
+
+
+def test_field_against_bigint_and_ring_laws():
+    rng = random.Random(11)
+    edges = [0, 1, 2, P - 1, P - 2, 2**32, 2**32 - 1, 2**63, 2**63 - 1, P // 2, P // 2 + 1]
+    vals = edges + [rng.randrange(P) for _ in range(3000)]
+    for a in vals[:200]:
+        for b in edges:
+            assert O.add(a, b) == (a + b) % P
+            assert O.sub(a, b) == (a - b) % P
+            assert O.mul(a, b) == (a * b) % P
+    for _ in range(3000):
+        a, b, c = rng.choice(vals), rng.choice(vals), rng.choice(vals)
+        assert O.mul(a, O.add(b, c)) == O.add(O.mul(a, b), O.mul(a, c))
+        assert O.mul(O.mul(a, b), c) == O.mul(a, O.mul(b, c))
+        assert O.add(O.sub(a, b), b) == a
+        assert O.mul(a, b) == O.mul(b, a)
+
+
+def test_eval_deg2_interpolates():
+    rng = random.Random(3)
+    for _ in range(300):
+        c0, c1, c2 = rng.randrange(P), rng.randrange(P), rng.randrange(P)
+        f = lambda x: (c0 + c1 * x + c2 * x * x) % P
+        g0, g1, g2 = f(0), f(1), f(2)
+        x = rng.randrange(P)
+        assert O.eval_deg2(g0, g1, g2, x) == f(x)
+        assert O.eval_deg2(g0, g1, g2, 0) == g0 and O.eval_deg2(g0, g1, g2, 2) == g2
+        # degree <= 2 extrapolation at 3
+        assert O.eval_deg2(g0, g1, g2, 3) == (g0 - 3 * g1 + 3 * g2) % P
+
+
+# -------------------------------------------------------------- SplitMix64 --
+def test_splitmix64_known_outputs():
+    for line in open(os.path.join(HERE, "golden", "splitmix64.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        seed, idx, val = line.split()
+        assert int(synth.raw(int(seed), 1, start=int(idx))[0]) == int(val, 16)
+
+
+def test_challenge_stream_is_output_mod_p():
+    x = synth.raw(1, 64)
+    c = synth.challenges(1, 64)
+    assert all(int(a) % P == int(b) for a, b in zip(x, c))
+    assert int(c[0]) == 10451216379200822465
+
+
+def test_generator_distributions():
+    g = synth.matrix(123, (400000,), "gauss32").astype(np.float64)
+    assert abs(g.mean()) < 0.5 and 30.5 < g.std() < 33.5
+    lp = synth.matrix(124, (400000,), "laplace16").astype(np.float64)
+    assert abs(lp.mean()) < 0.3 and abs(np.abs(lp).mean() - 16.0) < 0.6
+    u = synth.matrix(125, (400000,), "uniform127")
+    assert u.min() == -127 and u.max() == 127
+    q = synth.matrix(126, (100000,), "int4")
+    assert q.min() == -7 and q.max() == 7
+    z = synth.zipf(127, 200000, 128, 1.1)
+    cnt = np.bincount(z, minlength=128)
+    ratio = cnt[0] / cnt[1]
+    assert abs(ratio - 2 ** 1.1) < 0.1
+
+
+# ---------------------------------------------------------------- witness --
+def test_rescale_worked_cases():
+    for line in open(os.path.join(HERE, "golden", "rescale_edges.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        s, Z, Q, R, Y = map(int, line.split())
+        q, r, y = O.rescale(np.array([Z]), s)
+        assert (int(q[0]), int(r[0]), int(y[0])) == (Q, R, Y)
+        # the C witness on a 1x1 "matmul" producing Z where representable
+        if abs(Z) <= 127 * 127:
+            for a in range(1, 128):
+                if Z % a == 0 and abs(Z // a) <= 127:
+                    z, yy, rr = O.witness(np.array([[a]], np.int8), np.array([[Z // a]], np.int8), s)
+                    assert (int(z[0, 0]), int(yy[0, 0]), int(rr[0, 0])) == (Z, Y, R)
+                    break
+
+
+def test_witness_against_numpy_matmul_and_rounding():
+    rng = np.random.default_rng(1)
+    for (T, d_in, d_out, s) in [(1, 1, 1, 8), (3, 17, 5, 7), (16, 256, 33, 8), (40, 300, 70, 1)]:
+        X = rng.integers(-128, 128, size=(T, d_in), dtype=np.int8)
+        W = rng.integers(-128, 128, size=(d_out, d_in), dtype=np.int8)
+        Z, Y, R = O.witness(X, W, s)
+        Zref = X.astype(np.int64) @ W.astype(np.int64).T
+        assert np.array_equal(Z.astype(np.int64), Zref)
+        # round-to-nearest property: |Z/2^s - Q| <= 1/2, ties up
+        Q = (Z.astype(np.int64) - R) // (1 << s)
+        assert np.array_equal(Q * (1 << s) + R, Zref)
+        diff = Zref - Q * (1 << s)  # = R
+        assert np.all(np.abs(2 * diff) <= (1 << s))
+        tie = 2 * diff == -(1 << s)
+        assert np.all(~(2 * diff == (1 << s)))  # a tie never rounds down
+        assert np.all(Y == np.clip(Q, -128, 127))
+        assert O.check_rescale(Z, Y, R, s) == ("OK", -1)
+        _ = tie
+
+
+def test_witness_extremes_and_overflow():
+    X = np.full((2, 4096), -128, np.int8)
+    W = np.full((3, 4096), -128, np.int8)
+    Z, Y, R = O.witness(X, W, 8)
+    assert np.all(Z == 128 * 128 * 4096)
+    X = np.full((1, 131073), -128, np.int8)
+    W = np.full((1, 131073), -128, np.int8)
+    with pytest.raises(OverflowError):
+        O.witness(X, W, 8)
+
+
+# --------------------------------------------------------------------- eq --
+def _eq_doubling(r):
+    """eq table by doubling (a second routine): E_{j+1}[k + b 2^j] = E_j[k] (b ? r_j : 1 - r_j)."""
+    E = [1]
+    for rj in r:
+        E = [e * ((1 - rj) % P) % P for e in E] + [e * rj % P for e in E]
+    return E
+
+
+def test_eq_identities():
+    rng = random.Random(5)
+    assert list(O.eq_table([])) == [1]
+    for n in range(0, 9):
+        r = [rng.randrange(P) for _ in range(n)]
+        E = O.eq_table(r)
+        assert sum(int(e) for e in E) % P == 1
+        assert [int(e) for e in E] == _eq_doubling(r)
+        # Boolean point -> one-hot at sum_j r_j 2^j
+        bits = [rng.randrange(2) for _ in range(n)]
+        Eb = O.eq_table(bits)
+        idx = sum(b << j for j, b in enumerate(bits))
+        assert [int(e) for e in Eb] == [1 if k == idx else 0 for k in range(1 << n)]
+        if n:
+            k = rng.randrange(1 << n)
+            assert O.eq_at(r, k) == int(E[k])
+
+
+# ------------------------------------------------------------------ folds --
+def test_fold_boolean_point_selects_row_and_linearity():
+    rng = np.random.default_rng(2)
+    M = rng.integers(-128, 128, size=(13, 37), dtype=np.int8)
+    for t in range(13):
+        bits = [(t >> j) & 1 for j in range(4)]
+        f = O.fold_rows(M, O.eq_table(bits), 64)
+        assert [int(v) for v in f[:37]] == [O.from_int(int(v)) for v in M[t]]
+        assert np.all(f[37:] == 0)
+    r = [int(v) for v in synth.challenges(99, 4)]
+    E = O.eq_table(r)
+    A = rng.integers(-2**30, 2**30, size=(13, 37), dtype=np.int32)
+    B = rng.integers(-2**30, 2**30, size=(13, 37), dtype=np.int32)
+    fa, fb, fab = O.fold_rows(A, E), O.fold_rows(B, E), O.fold_rows((A.astype(np.int64) + B).astype(np.int32), E)
+    assert all(O.add(int(x), int(y)) == int(z) for x, y, z in zip(fa, fb, fab))
+    # definition by hand on one column, with Python integers
+    k = 5
+    want = sum(int(E[t]) * (int(A[t, k]) % P) for t in range(13)) % P
+    assert int(fa[k]) == want
+    # rows past `rows` are ignored: a 13-row fold equals a 16-row fold with zero rows
+    Apad = np.zeros((16, 37), np.int32)
+    Apad[:13] = A
+    assert np.array_equal(O.fold_rows(Apad, E), fa)
+    assert np.array_equal(O.fold_cols(A, E, [0, 5, 36]), fa[[0, 5, 36]])
+
+
+def test_mle_two_routes_and_boolean_points():
+    rng = random.Random(8)
+    for n in range(0, 9):
+        A = [rng.randrange(P) for _ in range(1 << n)]
+        z = [rng.randrange(P) for _ in range(n)]
+        assert O.mle_brute(A, z) == O.mle_seq(A, z)
+        k = rng.randrange(1 << n)
+        zb = [(k >> j) & 1 for j in range(n)]
+        assert O.mle_brute(A, zb) == A[k] == O.mle_seq(A, zb)
+    # multilinearity in the first variable: A~(x, ...) is affine in x
+    n = 5
+    A = [rng.randrange(P) for _ in range(1 << n)]
+    z = [rng.randrange(P) for _ in range(n)]
+    f = lambda x: O.mle_seq(A, [x] + z[1:])
+    assert (f(0) + 2 * (f(1) - f(0))) % P == f(2)
+
+
+def test_mle_matrix_layout_and_boolean_points():
+    rng = np.random.default_rng(3)
+    Z = rng.integers(-2**31, 2**31, size=(5, 6), dtype=np.int32)
+    r_rows = [int(v) for v in synth.challenges(5, 3)]
+    r_cols = [int(v) for v in synth.challenges(6, 3)]
+    # flatten with the column in the low bits, zero-padded to [8, 8]
+    flat = np.zeros(64, np.uint64)
+    for t in range(5):
+        for o in range(6):
+            flat[t * 8 + o] = O.from_int(int(Z[t, o]))
+    assert O.mle_matrix(Z, r_rows, r_cols) == O.mle_brute(flat, r_cols + r_rows)
+    # a transposed operand gives a different value
+    assert O.mle_matrix(Z, r_rows, r_cols) != O.mle_brute(flat, r_rows + r_cols)
+    for t, o in [(0, 0), (4, 5), (2, 3)]:
+        rb = [(t >> j) & 1 for j in range(3)]
+        cb = [(o >> j) & 1 for j in range(3)]
+        assert O.mle_matrix(Z, rb, cb) == O.from_int(int(Z[t, o]))
+
+
+# -------------------------------------------------------------- sum-check --
+def _brute_round_values(A, B, r, i, n):
+    """g_i(c) by enumerating the hypercube: sum over b in {0,1}^(n-i-1) of
+    A~(r_0..r_{i-1}, c, b) B~(r_0..r_{i-1}, c, b), evaluated from the
+    multilinear extensions by definition."""
+    out = []
+    for c in (0, 1, 2):
+        tot = 0
+        for b in itertools.product((0, 1), repeat=n - i - 1):
+            pt = list(r[:i]) + [c] + list(b)
+            tot = (tot + O.mle_brute(A, pt) * O.mle_brute(B, pt)) % P
+        out.append(tot)
+    return out
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 4])
+def test_sumcheck_against_hypercube_enumeration(n):
+    rng = random.Random(100 + n)
+    A = [rng.randrange(P) for _ in range(1 << n)]
+    B = [rng.randrange(P) for _ in range(1 << n)]
+    r = [rng.randrange(P) for _ in range(n)]
+    rounds, finals, c0 = O.sumcheck([A], [B], r)
+    assert c0 == sum(a * b for a, b in zip(A, B)) % P
+    for i in range(n):
+        assert [int(v) for v in rounds[i]] == _brute_round_values(A, B, r, i, n)
+    assert int(finals[0, 0]) == O.mle_brute(A, r) and int(finals[0, 1]) == O.mle_brute(B, r)
+    assert O.check_sumcheck(rounds, finals, r, c0, As=[A], Bs=[B])[0] == "OK"
+
+
+def test_sumcheck_batched_is_rho_combination():
+    rng = random.Random(21)
+    n, k = 5, 3
+    As = [[rng.randrange(P) for _ in range(1 << n)] for _ in range(k)]
+    Bs = [[rng.randrange(P) for _ in range(1 << n)] for _ in range(k)]
+    r = [rng.randrange(P) for _ in range(n)]
+    rho = [rng.randrange(P) for _ in range(k)]
+    rounds, finals, c0 = O.sumcheck(As, Bs, r, rho=rho)
+    single = [O.sumcheck([a], [b], r) for a, b in zip(As, Bs)]
+    assert c0 == sum(rj * s[2] for rj, s in zip(rho, single)) % P
+    for i in range(n):
+        for c in range(3):
+            assert int(rounds[i, c]) == sum(rj * int(s[0][i, c]) for rj, s in zip(rho, single)) % P
+    assert O.check_sumcheck(rounds, finals, r, c0, rho=rho, As=As, Bs=Bs)[0] == "OK"
+
+
+def test_sumcheck_boolean_challenges_reduce_to_dot_product():
+    rng = np.random.default_rng(4)
+    X = rng.integers(-127, 128, size=(8, 16), dtype=np.int8)
+    W = rng.integers(-127, 128, size=(4, 16), dtype=np.int8)
+    t, o = 5, 2
+    r_t = [(t >> j) & 1 for j in range(3)]
+    r_o = [(o >> j) & 1 for j in range(2)]
+    res = O.prove_matmul(X, W, 8, r_t, r_o, [int(v) for v in synth.challenges(9, 4)])
+    textbook = int(np.dot(X[t].astype(np.int64), W[o].astype(np.int64)))
+    assert res["c0"] == O.from_int(textbook) == res["claim0"]
+
+
+# ------------------------------------------------------- negative controls --
+def _proof(n=6, seed=31):
+    rng = random.Random(seed)
+    A = [rng.randrange(P) for _ in range(1 << n)]
+    B = [rng.randrange(P) for _ in range(1 << n)]
+    r = [rng.randrange(P) for _ in range(n)]
+    rounds, finals, c0 = O.sumcheck([A], [B], r)
+    return A, B, r, rounds, finals, c0
+
+
+def test_negative_controls_sumcheck():
+    A, B, r, rounds, finals, c0 = _proof()
+    assert O.check_sumcheck(rounds, finals, r, c0, As=[A], Bs=[B])[0] == "OK"
+    assert O.check_sumcheck(rounds, finals, r, (c0 + 1) % P)[0] == "INITIAL_CLAIM"
+    for i in range(len(r)):
+        for c in range(3):
+            bad = rounds.copy()
+            bad[i, c] = (int(bad[i, c]) + 1) % P
+            reason, where = O.check_sumcheck(bad, finals, r, c0)
+            if c < 2:
+                assert (reason, where) == (("INITIAL_CLAIM", 0) if i == 0 else ("ROUND_SUM", i))
+            else:  # g_i(2) only enters through g_i(r_i)
+                assert (reason, where) == (("ROUND_SUM", i + 1) if i + 1 < len(r) else ("FINAL_CLAIM", len(r)))
+    bad = finals.copy()
+    bad[0, 1] = (int(bad[0, 1]) + 1) % P
+    assert O.check_sumcheck(rounds, bad, r, c0)[0] == "FINAL_CLAIM"
+    # a tampered table: finals no longer open to the committed table's MLE
+    A2 = list(A)
+    A2[3] = (A2[3] + 1) % P
+    assert O.check_sumcheck(rounds, finals, r, c0, As=[A2], Bs=[B])[0] == "FINAL_OPENING"
+    # a challenge the prover did not use
+    r2 = list(r)
+    r2[2] = (r2[2] + 1) % P
+    assert O.check_sumcheck(rounds, finals, r2, c0)[0] in ("ROUND_SUM", "FINAL_CLAIM")
+    # MSB-first binding gives a transcript this verifier rejects
+    n = len(r)
+    perm = lambda T: [T[int(format(k, "0%db" % n)[::-1], 2)] for k in range(1 << n)]
+    rr, ff, cc = O.sumcheck([perm(A)], [perm(B)], r)
+    assert cc == c0
+    assert O.check_sumcheck(rr, ff, r, c0, As=[A], Bs=[B])[0] == "FINAL_OPENING"
+
+
+def test_negative_controls_witness():
+    rng = np.random.default_rng(6)
+    X = rng.integers(-127, 128, size=(9, 40), dtype=np.int8)
+    W = rng.integers(-127, 128, size=(11, 40), dtype=np.int8)
+    Z, Y, R = O.witness(X, W, 8)
+    assert O.check_witness(X, W, Z) == ("OK", -1)
+    Z2 = Z.copy()
+    Z2[4, 7] += 1
+    assert O.check_witness(X, W, Z2) == ("WITNESS_MISMATCH", 4 * 11 + 7)
+    assert O.check_rescale(Z2, Y, R, 8)[0] == "RESCALE_IDENTITY"
+    R2 = R.copy()
+    R2[1, 1] ^= 1
+    assert O.check_rescale(Z, Y, R2, 8) == ("RESCALE_IDENTITY", 1 * 11 + 1)
+    Y2 = Y.copy()
+    Y2[0, 0] = Y2[0, 0] + 1 if Y2[0, 0] < 127 else 126
+    assert O.check_rescale(Z, Y2, R, 8) == ("RESCALE_IDENTITY", 0)
+    # the wrong shift: Y and R of s = 8 fail the s = 7 identity somewhere
+    assert O.check_rescale(Z, Y, R, 7)[0] == "RESCALE_IDENTITY"
+    # the claim follows Z: one changed entry changes Z~ at a random point
+    r_t = [int(v) for v in synth.challenges(1, 4)]
+    r_o = [int(v) for v in synth.challenges(2, 4)]
+    assert O.mle_matrix(Z, r_t, r_o) != O.mle_matrix(Z2, r_t, r_o)
