@@ -1,0 +1,180 @@
+"""Benchmark: proved tokens/s for one fixed-point linear layer on one GPU.
+
+A step is one whole layer proof (witness GEMM with rescale epilogue, eq tables,
+row folds of X and W, the claim Z~(r_o || r_t), the sum-check over d_in, and
+any random linear combination) over one batch of synthetic tokens whose
+inputs and challenges are resident in HBM before timing starts. The default
+workload is the Llama-3.1-8B-shaped up-projection (T=512, 4096 -> 14336,
+s=8); ``--config N`` selects another workload description (1..5).
+
+Prints one JSON line. ``roofline`` describes the kernel with the largest
+average launch time, timed with HIP events on the stream the kernels run on;
+``cpu_baseline`` times the CPU oracle on the same workload (rank 0, N=1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # bytes/s, MI355X HBM3E
+MFMA_I8_PEAK = 5.0e15    # ops/s, MI355X dense int8 matrix cores
+METRIC = "matmul sum-check proved tokens/s per layer; fold GB/s & int8 MFMA % of peak"
+WORKLOADS = {1: "single linear layer T=16 256x256 (uniform int8, s=7)",
+             2: "Llama-3.1-8B up-projection T=512 4096->14336 (s=8)",
+             3: "Llama-4-Maverick-width dense MLP gate/up/down T=1024 d=5120 d_ff=16384 (s=8), RLC of 3 claims",
+             4: "MoE block 128 experts top-1 Zipf(1.1) routing of T=2048, 5120->8192->5120 int4 weights (s=8)",
+             5: "dense layer linear maps T=4096 d=4096 GQA 32/8 heads d_ff=14336, 7 claims batched (s=8)"}
+
+
+def kernel_work(cfg, name: str, prover) -> tuple:
+    """(algorithmic bytes, algorithmic int8 ops) of one launch group."""
+    import numpy as np
+    if cfg.kind == "moe":
+        T = cfg.T
+        d, dff = cfg.d_model, cfg.d_ff
+        ne = len(prover.experts)
+        wbytes = ne * 2 * d * dff
+        if name == "witness":
+            return wbytes + T * (d + dff) + 6 * T * (d + dff), 2 * T * d * dff * 2
+        if name == "fold":
+            return wbytes + T * (d + dff) + 8 * 2 * ne * ((1 << prover.n_up) + (1 << prover.n_dn)), 0
+        if name == "claim":
+            return 4 * T * (d + dff), 0
+        if name == "sumcheck":
+            return 16 * ne * ((1 << prover.n_up) + (1 << prover.n_dn)), 0
+        return 0, 0
+    mms = cfg.matmuls
+    T = cfg.T
+    if name == "witness":
+        b = sum(m.d_in * m.d_out + T * m.d_in + 6 * T * m.d_out for m in mms)
+        return b, sum(2 * T * m.d_in * m.d_out for m in mms)
+    if name == "fold":
+        xs = {(m.x, m.d_in) for m in mms}
+        b = sum(m.d_in * m.d_out for m in mms) + sum(T * di for _, di in xs)
+        return b, 0
+    if name == "claim":
+        return sum(4 * T * m.d_out for m in mms), 0
+    if name == "sumcheck":
+        n = cfg.batched_n if cfg.kind == "batched" else None
+        return sum(16 * (1 << (n if n else m.n)) for m in mms), 0
+    return 0, 0
+
+
+def cpu_baseline(cfg, inp, ch) -> dict:
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if cfg.cid in (1, 2):
+        t0 = time.perf_counter()
+        oracle.prove_config(cfg, inp, ch)
+        dt = time.perf_counter() - t0
+        return {"value": cfg.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "the whole layer proof of this workload (all %d tokens), one pass, %.1f s" % (cfg.T, dt)}
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this prover runs on one GPU; --gpus %d is not supported (each box has one GPU)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+    from zero_knowledge_proof_amd.prover import make_prover
+
+    fp.require_gpu()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = synth.config(args.config)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch, dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        prover.run()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, with per-step-phase HIP events on the same stream
+    marks = []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((name, ev))
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        prover.run(mark=mark)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    tokens = cfg.T
+    value = tokens / (ms * 1e-3)
+
+    # per-phase averages: a phase runs from its mark to the next mark of the step
+    phase_ms = {}
+    for i in range(len(marks) - 1):
+        name, ev = marks[i]
+        if name == "end":
+            continue
+        phase_ms[name] = phase_ms.get(name, 0.0) + ev.elapsed_time(marks[i + 1][1])
+    for k in phase_ms:
+        phase_ms[k] /= args.steps
+    dom = max(phase_ms, key=lambda k: phase_ms[k])
+    b, ops = kernel_work(cfg, dom, prover)
+    t = phase_ms[dom] * 1e-3
+    t_hbm, t_mfma = b / HBM_PEAK, ops / MFMA_I8_PEAK
+    if ops and t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": ops / t / 1e12, "peak": MFMA_I8_PEAK / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": b / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    extras = {}
+    for k, v in phase_ms.items():
+        bb, oo = kernel_work(cfg, k, prover)
+        extras[k] = {"ms": round(v, 5), "GB/s": round(bb / (v * 1e-3) / 1e9, 1) if bb else None,
+                     "TOPS": round(oo / (v * 1e-3) / 1e12, 1) if oo else None}
+    wb, wops = kernel_work(cfg, "witness", prover)
+    fb, _ = kernel_work(cfg, "fold", prover)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8->int32 witness; u64 Goldilocks field", "data": "synthetic",
+        "config": {"workload": WORKLOADS[cfg.cid], "T": cfg.T, "seed": cfg.seed, "s": cfg.s,
+                   "matmuls": [[m.name, m.d_in, m.d_out] for m in cfg.matmuls] if cfg.matmuls else None},
+        "roofline": roof,
+        "fold_GBps": extras.get("fold", {}).get("GB/s"),
+        "witness_int8_TOPS": extras.get("witness", {}).get("TOPS"),
+        "witness_mfma_frac": round(wops / (phase_ms["witness"] * 1e-3) / MFMA_I8_PEAK, 4),
+        "phases": extras,
+        "wall_s": round(wall, 3),
+    }
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, inp, ch)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * fp.h - C ABI of libfp, the gfx950 prover for fixed-point linear layers.
+ *
+ * What is proved. For a quantized linear layer the prover computes the integer
+ * witness Z = X W^T (int8 x int8 -> int32), the rescaled output
+ * Y = clamp(round(Z / 2^s), -128, 127) and the rescale remainders
+ * R = Z - 2^s round(Z / 2^s), then runs the sum-check protocol for the matmul
+ * claim over the Goldilocks field p = 2^64 - 2^32 + 1.
+ * Source: "How fast can FlashProve go", §2 Background (fixed-point model whose
+ * products are rescaled and clamped; sum-check reduces each matmul to claims
+ * about committed tables and the weights; a table's folded row is the
+ * eq-weighted sum of its rows) and §3.1 (rescale g_w = round(g^ / 2^k), the
+ * committed remainder r = g^ - 2^k g_w that the matmul's sum-check uses in
+ * place of g^; Goldilocks).
+ *
+ * Conventions (readings where the page is silent):
+ *  - rounding ties go up: Q = floor((Z + 2^(s-1)) / 2^s); R = Z - 2^s Q is taken
+ *    against the unclamped Q; 1 <= s <= 8 so R fits int8;
+ *  - tables are indexed LSB-first: eq(r, k) = prod_j (k_j ? r_j : 1 - r_j) and
+ *    the multilinear extension is A~(z) = sum_k eq(z, k) A[k];
+ *  - a row-major [rows, cols] matrix flattens with the column index in the low
+ *    bits, so M~(r_cols || r_rows) = sum_t sum_c eq(r_rows,t) eq(r_cols,c) M[t,c];
+ *    every axis is zero-padded to the next power of two;
+ *  - sum-check round i (0-based) binds table bit i (pairs 2q, 2q+1) and sends
+ *    the degree-2 round polynomial as its values at 0, 1 and 2.
+ *
+ * Memory and errors. Unless marked "host", every pointer is a device pointer
+ * owned by the caller; inputs are read-only, outputs are fully overwritten.
+ * Field elements (fp_elem) are canonical uint64 in [0, p). Integer matrices are
+ * row-major with an explicit leading dimension in elements. Calls only enqueue
+ * work on `stream` and return; none synchronizes or allocates device memory.
+ * Scratch space comes from a caller workspace sized by the matching
+ * *_workspace() query. Arguments are validated before any launch; a failing
+ * call returns a nonzero FP_E* code, launches nothing, and sets a thread-local
+ * message readable with fp_last_error(). Faults inside kernels surface at the
+ * caller's next stream synchronization. The library keeps no state between
+ * calls (thread-safe; calls on one stream run in order).
+ */
+#ifndef FP_H
+#define FP_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint64_t fp_elem;
+
+typedef enum { FP_I8 = 0, FP_I32 = 1 } fp_dtype;
+
+enum {
+  FP_OK = 0,
+  FP_EARG = 1,       /* null pointer, negative or overflowing size */
+  FP_ESHAPE = 2,     /* inconsistent shapes, n > 30, d_in > 131072, padding too small */
+  FP_ERANGE = 3,     /* s outside [1, 8] */
+  FP_EWORKSPACE = 4, /* workspace smaller than the *_workspace() size */
+  FP_EHIP = 5        /* the HIP runtime reported an error at launch */
+};
+
+#define FP_MAX_DIN 131072 /* 127^2 * d_in < 2^31 keeps Z exact in int32 */
+#define FP_MAX_N 30       /* largest table: 2^30 entries */
+#define FP_MAX_GROUPS 256 /* groups in one grouped witness launch */
+
+/* Thread-local message of the last failing call ("" after success). */
+const char* fp_last_error(void);
+
+/* ------------------------------------------------------------ witness --- */
+/* Witness of one linear layer ("How fast can FlashProve go", §2 and §3.1).
+ * X: int8 [T, d_in] (leading dim ldx >= d_in); W: int8 [d_out, d_in] (ldw).
+ * Writes Z int32 [T, d_out] (may be NULL: not stored), Y and R int8
+ * [T, d_out], all dense row-major. Requires 1 <= s <= 8, d_in <= FP_MAX_DIN.
+ * Runs on int8 matrix cores with the rescale/clamp/remainder in the epilogue. */
+int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T, int32_t d_in,
+                      int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
+
+/* Grouped witness: G independent layers sharing d_in, d_out and s in ONE
+ * launch (one group per MoE expert). Group g owns rows [row_off[g],
+ * row_off[g+1]) of X (int8 [row_off[G], d_in], leading dim ldx) and of the
+ * outputs Z/Y/R ([row_off[G], d_out], dense); its weight is W_ptrs[g]
+ * (int8 [d_out, d_in], leading dim ldw). row_off (host, G+1 entries,
+ * non-decreasing, row_off[0] = 0) and W_ptrs (host array of G device
+ * pointers) are read during the call only. Empty groups are allowed.
+ * G <= FP_MAX_GROUPS. Z may be NULL. */
+int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int8_t* const* W_ptrs, int64_t ldw,
+                              const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out, int32_t s,
+                              int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
+
+/* ----------------------------------------------------------- grouping --- */
+/* MoE grouping plan, host only (no device work). route (host, T entries in
+ * [0, n_experts)) gives each token's expert. Writes counts[e] (host,
+ * n_experts), offsets (host, n_experts + 1, offsets[e] = first grouped row of
+ * expert e) and perm (host, T: grouped row -> token), grouping stably by
+ * expert with tokens ascending within a group ("How fast can FlashProve go",
+ * §2: each token goes to one routed expert). */
+int fp_moe_plan(const int32_t* route, int32_t T, int32_t n_experts, int32_t* counts, int32_t* offsets,
+                int32_t* perm);
+
+/* Xg[i, :] = X[perm[i], :] for i < n_rows (perm: device int32 [n_rows]);
+ * X leading dim ldx, Xg dense [n_rows, cols]. */
+int fp_gather_rows(const int8_t* X, int64_t ldx, const int32_t* perm, int32_t n_rows, int32_t cols, int8_t* Xg,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ eq --- */
+/* E[k] = eq(r, k) for k < 2^n (r: n field elements, E: 2^n). n in [0, 30]
+ * ("How fast can FlashProve go", §2: the weights of the folded row). */
+int fp_eq_table(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t stream);
+
+typedef struct {
+  const fp_elem* r; /* device, n elements */
+  int32_t n;        /* 0..24 */
+  fp_elem* E;       /* device, 2^n elements */
+} fp_eq_desc;
+
+/* Several eq tables in one launch. descs is a HOST array of `count`
+ * descriptors; it is copied into the workspace on `stream` (the host array may
+ * be reused once the call returns). Workspace: fp_eq_table_batched_workspace. */
+int fp_eq_table_batched(int32_t count, const fp_eq_desc* descs, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t fp_eq_table_batched_workspace(int32_t count);
+
+/* --------------------------------------------------------------- folds --- */
+/* Folded row of an integer matrix ("How fast can FlashProve go", §2: the
+ * weighted sum of all of a table's rows): out[k] = sum_{t<rows} E[t] M[t,k]
+ * for k < cols and out[k] = 0 for cols <= k < cols_pad. M is int8 or int32
+ * [rows, cols] with leading dim ld; E holds at least `rows` field elements
+ * (entries past `rows` are ignored, as if M had zero rows there). With
+ * E = eq(r_t, .) over X this is x'[k] = X~(k || r_t); over W with eq(r_o, .)
+ * it is w'[k] = W~(k || r_o). Runs on the vector ALUs, bandwidth-bound. */
+int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* E,
+                   fp_elem* out, int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t fp_fold_matrix_workspace(fp_dtype dt, int32_t rows, int32_t cols);
+
+typedef struct {
+  const void* M;   /* device, int8 or int32 (one dtype per batched call) */
+  int64_t ld;
+  int32_t rows, cols, cols_pad;
+  const fp_elem* E; /* device, >= rows */
+  fp_elem* out;     /* device, cols_pad */
+} fp_fold_desc;
+
+/* Several folds of one dtype in one pair of launches (descs: HOST array,
+ * copied into the workspace on `stream`). */
+int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* descs, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* descs);
+
+/* ----------------------------------------------------------------- MLE --- */
+/* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading
+ * dim ld) zero-padded to [2^n_rows, 2^n_cols]; rows <= 2^n_rows and
+ * cols <= 2^n_cols. Used for the matmul claim c0 = Z~(r_o || r_t)
+ * ("How fast can FlashProve go", §3.1: the claim about the rescaled product). */
+int fp_mle_eval(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* r_rows,
+                int32_t n_rows, const fp_elem* r_cols, int32_t n_cols, fp_elem* out, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+size_t fp_mle_eval_workspace(fp_dtype dt, int32_t rows, int32_t cols, int32_t n_rows, int32_t n_cols);
+
+typedef struct {
+  const void* M;          /* device, int8 or int32 (one dtype per call) */
+  int64_t ld;
+  int32_t rows, cols;
+  const fp_elem* E_rows;  /* device, >= rows */
+  const fp_elem* E_cols;  /* device, >= cols */
+  fp_elem* out;           /* device, 1 element */
+} fp_claim_desc;
+
+/* Several matmul claims from precomputed eq tables in one pair of launches:
+ * out_j = sum_t sum_c E_rows_j[t] E_cols_j[c] M_j[t, c], i.e. M_j~(r_cols ||
+ * r_rows) when the tables are eq(r_rows, .) and eq(r_cols, .). descs is a
+ * HOST array copied into the workspace on `stream`. */
+int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* descs, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* descs);
+
+/* ----------------------------------------------------------- sum-check --- */
+/* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of
+ * tables of 2^n entries ("How fast can FlashProve go", §2: sum-check reduces
+ * the matmul to claims about the committed tables). A and B are HOST arrays of
+ * n_pairs device pointers; rho is a device array of n_pairs field elements or
+ * NULL (all ones). r (device, n) are the round challenges. For each round i
+ * the prover sends g_i(0), g_i(1), g_i(2) with
+ *   g_i(c) = sum_j rho_j sum_q A_j,c[q] B_j,c[q],  A_c[q] = A[2q] + c (A[2q+1] - A[2q]),
+ * then binds A[q] <- A[2q] + r_i (A[2q+1] - A[2q]) (B likewise); round i
+ * reads r_i only after g_i is fully reduced. Outputs (device): rounds [n][3],
+ * finals [n_pairs][2] = (A_j~(r), B_j~(r)), claim0 (1 element, may be NULL) =
+ * the initial claim. Tables are not modified. n in [1, 30]. */
+int fp_sumcheck_prove(int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B, const fp_elem* rho,
+                      int32_t n, const fp_elem* r, fp_elem* rounds, fp_elem* finals, fp_elem* claim0, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+size_t fp_sumcheck_workspace(int32_t n_pairs, int32_t n);
+
+/* n_inst independent single-pair sum-checks of 2^n entries in one launch
+ * (one MoE expert's claim each). A, B: device [n_inst][2^n]; r: [n_inst][n];
+ * rounds: [n_inst][n][3]; finals: [n_inst][2]; claim0: [n_inst] or NULL.
+ * n in [1, 13]. */
+int fp_sumcheck_prove_multi(int32_t n_inst, int32_t n, const fp_elem* A, const fp_elem* B, const fp_elem* r,
+                            fp_elem* rounds, fp_elem* finals, fp_elem* claim0, hipStream_t stream);
+
+/* Random linear combination of finished sum-check claims ("How fast can
+ * FlashProve go", §2: claims about the weights are merged into one):
+ * out[0] = sum_j rho[j] g_j(x_j), where g_j is the last round polynomial of
+ * claim j given by its values at 0, 1, 2 (g_last[j]: device pointer to 3
+ * elements) and x_j its last challenge (x_last[j]: device pointer to 1
+ * element). g_last and x_last are HOST arrays of `count` device pointers;
+ * rho is a device array of `count`. count <= 16. */
+int fp_combine_claims(int32_t count, const fp_elem* const* g_last, const fp_elem* const* x_last,
+                      const fp_elem* rho, fp_elem* out, hipStream_t stream);
+
+/* out[0] = sum_j rho[j] v_j: the random linear combination of `count`
+ * claims ("How fast can FlashProve go", §2: claims are merged), with vals a
+ * HOST array of device pointers to one element each; rho device [count];
+ * count <= 16. */
+int fp_linear_combine(int32_t count, const fp_elem* const* vals, const fp_elem* rho, fp_elem* out,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP_H */

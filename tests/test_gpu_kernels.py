@@ -1,0 +1,277 @@
+"""GPU parity of each libfp entry point against the CPU oracle, element by
+element and bit-exact, on seeded inputs that span several tiles and ragged
+tails, plus the degenerate cases (empty, single row/column, n = 0 or 1,
+challenges 0, 1, p-1, extreme int8 values, rounding ties)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+P = O.P
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _field(rng, n, specials=True):
+    v = rng.integers(0, 2**63, size=n, dtype=np.uint64) * np.uint64(2) + rng.integers(0, 2, size=n, dtype=np.uint64)
+    v = np.where(v >= np.uint64(P), v - np.uint64(P), v).astype(np.uint64)
+    if specials and n >= 4:
+        v[:3] = [0, 1, P - 1]
+    return v
+
+
+def _i8(rng, shape, lo=-128, hi=127):
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int8)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ------------------------------------------------------------------- eq ---
+@pytest.mark.parametrize("n", [0, 1, 2, 7, 8, 9, 13, 16])
+def test_eq_table(fp, n):
+    rng = _rng(100 + n)
+    r = _field(rng, n, specials=(n >= 4))
+    E = fp.eq_table(fp.to_field_tensor(r) if n else torch.empty(0, dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(fp.field_numpy(E), O.eq_table(r))
+
+
+def test_eq_table_batched(fp):
+    rng = _rng(7)
+    ns = [0, 3, 8, 9, 12, 1]
+    rs = [_field(rng, n, specials=False) for n in ns]
+    Es = fp.eq_table_batched([fp.to_field_tensor(r) if len(r) else torch.empty(0, dtype=torch.int64, device="cuda")
+                              for r in rs])
+    torch.cuda.synchronize()
+    for r, E in zip(rs, Es):
+        assert np.array_equal(fp.field_numpy(E), O.eq_table(r))
+
+
+# ---------------------------------------------------------------- folds ---
+FOLD_SHAPES = [(1, 1, 1), (3, 5, 8), (17, 37, 64), (300, 256, 256), (1000, 300, 512), (2500, 1030, 2048),
+               (4, 4, 4), (1025, 257, 512)]
+
+
+@pytest.mark.parametrize("rows,cols,cols_pad", FOLD_SHAPES)
+def test_fold_int8(fp, rows, cols, cols_pad):
+    rng = _rng(rows * 7 + cols)
+    M = _i8(rng, (rows, cols))
+    E = _field(rng, rows)
+    out = fp.fold_matrix(_dev(M), fp.to_field_tensor(E), cols_pad)
+    torch.cuda.synchronize()
+    assert np.array_equal(fp.field_numpy(out), O.fold_rows(M, E, cols_pad))
+
+
+@pytest.mark.parametrize("rows,cols,cols_pad", FOLD_SHAPES)
+def test_fold_int32(fp, rows, cols, cols_pad):
+    rng = _rng(rows * 11 + cols)
+    M = rng.integers(-2**31, 2**31, size=(rows, cols), dtype=np.int64).astype(np.int32)
+    M.flat[:3] = [-2**31, 2**31 - 1, 0][:min(3, M.size)]
+    E = _field(rng, rows)
+    out = fp.fold_matrix(_dev(M), fp.to_field_tensor(E), cols_pad)
+    torch.cuda.synchronize()
+    assert np.array_equal(fp.field_numpy(out), O.fold_rows(M, E, cols_pad))
+
+
+def test_fold_strided_and_extremes(fp):
+    rng = _rng(5)
+    base = _i8(rng, (700, 333))
+    base[:, 0] = -128
+    base[:, 1] = 127
+    M = base[:, 3:300]  # leading dim 333, unaligned start
+    E = _field(rng, 700)
+    E[5:] = P - 1
+    Mt = _dev(base)[:, 3:300]
+    out = fp.fold_matrix(Mt, fp.to_field_tensor(E), 512)
+    torch.cuda.synchronize()
+    assert np.array_equal(fp.field_numpy(out), O.fold_rows(np.ascontiguousarray(M), E, 512))
+
+
+def test_fold_batched(fp):
+    rng = _rng(9)
+    shapes = [(5, 7, 8), (0, 9, 16), (600, 300, 512), (33, 1, 4)]
+    jobs, want = [], []
+    for rows, cols, cp in shapes:
+        M = _i8(rng, (rows, cols))
+        E = _field(rng, max(rows, 1))
+        jobs.append((_dev(M), fp.to_field_tensor(E), cp, torch.empty(cp, dtype=torch.int64, device="cuda")))
+        want.append(O.fold_rows(M, E, cp) if rows else np.zeros(cp, np.uint64))
+    outs = fp.fold_matrix_batched(jobs)
+    torch.cuda.synchronize()
+    for o, w in zip(outs, want):
+        assert np.array_equal(fp.field_numpy(o), w)
+
+
+# ------------------------------------------------------------------ MLE ---
+@pytest.mark.parametrize("rows,cols", [(1, 1), (5, 6), (16, 256), (100, 300), (513, 1030)])
+@pytest.mark.parametrize("dt", [np.int8, np.int32])
+def test_mle_eval(fp, rows, cols, dt):
+    rng = _rng(rows + 3 * cols)
+    if dt == np.int8:
+        M = _i8(rng, (rows, cols))
+    else:
+        M = rng.integers(-2**31, 2**31, size=(rows, cols), dtype=np.int64).astype(np.int32)
+    nr, nc = O.log2ceil(rows), O.log2ceil(cols)
+    r_rows, r_cols = _field(rng, nr, False), _field(rng, nc, False)
+    z = torch.empty(0, dtype=torch.int64, device="cuda")
+    out = fp.mle_eval(_dev(M), fp.to_field_tensor(r_rows) if nr else z, fp.to_field_tensor(r_cols) if nc else z)
+    torch.cuda.synchronize()
+    assert int(fp.field_numpy(out)[0]) == O.mle_matrix(M, r_rows, r_cols)
+
+
+def test_claim_eval_batched(fp):
+    rng = _rng(12)
+    jobs, want = [], []
+    for rows, cols in [(16, 256), (7, 9), (300, 1000)]:
+        M = rng.integers(-2**31, 2**31, size=(rows, cols), dtype=np.int64).astype(np.int32)
+        r_rows, r_cols = _field(rng, O.log2ceil(rows), False), _field(rng, O.log2ceil(cols), False)
+        jobs.append((_dev(M), fp.to_field_tensor(O.eq_table(r_rows)), fp.to_field_tensor(O.eq_table(r_cols)),
+                     torch.empty(1, dtype=torch.int64, device="cuda")))
+        want.append(O.mle_matrix(M, r_rows, r_cols))
+    outs = fp.claim_eval_batched(jobs)
+    torch.cuda.synchronize()
+    assert [int(fp.field_numpy(o)[0]) for o in outs] == want
+
+
+# ------------------------------------------------------------ sum-check ---
+@pytest.mark.parametrize("n", [1, 2, 5, 12, 13, 14, 15])
+def test_sumcheck_single(fp, n):
+    rng = _rng(200 + n)
+    A, B = _field(rng, 1 << n), _field(rng, 1 << n)
+    r = _field(rng, n, specials=(n >= 4))
+    rounds, finals, c0 = fp.sumcheck_prove([fp.to_field_tensor(A)], [fp.to_field_tensor(B)], fp.to_field_tensor(r))
+    torch.cuda.synchronize()
+    wr, wf, wc = O.sumcheck([A], [B], r)
+    assert np.array_equal(fp.field_numpy(rounds), wr)
+    assert np.array_equal(fp.field_numpy(finals), wf)
+    assert int(fp.field_numpy(c0)[0]) == wc
+
+
+@pytest.mark.parametrize("k,n", [(2, 3), (3, 11), (7, 14), (7, 10)])
+def test_sumcheck_batched_rho(fp, k, n):
+    rng = _rng(300 + 17 * k + n)
+    As = [_field(rng, 1 << n, False) for _ in range(k)]
+    Bs = [_field(rng, 1 << n, False) for _ in range(k)]
+    rho = _field(rng, k, False)
+    r = _field(rng, n, False)
+    rounds, finals, c0 = fp.sumcheck_prove([fp.to_field_tensor(a) for a in As], [fp.to_field_tensor(b) for b in Bs],
+                                           fp.to_field_tensor(r), rho=fp.to_field_tensor(rho))
+    torch.cuda.synchronize()
+    wr, wf, wc = O.sumcheck(As, Bs, r, rho=rho)
+    assert np.array_equal(fp.field_numpy(rounds), wr)
+    assert np.array_equal(fp.field_numpy(finals), wf)
+    assert int(fp.field_numpy(c0)[0]) == wc
+
+
+@pytest.mark.parametrize("n_inst,n", [(1, 1), (5, 6), (40, 13)])
+def test_sumcheck_multi(fp, n_inst, n):
+    rng = _rng(400 + n_inst + n)
+    A = np.stack([_field(rng, 1 << n, False) for _ in range(n_inst)])
+    B = np.stack([_field(rng, 1 << n, False) for _ in range(n_inst)])
+    r = np.stack([_field(rng, n, False) for _ in range(n_inst)])
+    rounds, finals, c0 = fp.sumcheck_prove_multi(fp.to_field_tensor(A.reshape(-1)).view(n_inst, -1),
+                                                 fp.to_field_tensor(B.reshape(-1)).view(n_inst, -1),
+                                                 fp.to_field_tensor(r.reshape(-1)).view(n_inst, n))
+    torch.cuda.synchronize()
+    R, F, C = fp.field_numpy(rounds), fp.field_numpy(finals), fp.field_numpy(c0)
+    for i in range(n_inst):
+        wr, wf, wc = O.sumcheck([A[i]], [B[i]], r[i])
+        assert np.array_equal(R[i], wr) and np.array_equal(F[i], wf[0]) and int(C[i]) == wc
+
+
+def test_combine_and_linear_combine(fp):
+    rng = _rng(13)
+    g = [_field(rng, 3, False) for _ in range(3)]
+    x = [_field(rng, 1, False) for _ in range(3)]
+    rho = _field(rng, 3, False)
+    gd = [fp.to_field_tensor(v) for v in g]
+    xd = [fp.to_field_tensor(v) for v in x]
+    out = fp.combine_claims(gd, xd, fp.to_field_tensor(rho))
+    lin = fp.linear_combine([fp.to_field_tensor(v[:1]) for v in g], fp.to_field_tensor(rho))
+    torch.cuda.synchronize()
+    want = sum(int(rho[j]) * O.eval_deg2(*[int(v) for v in g[j]], int(x[j][0])) for j in range(3)) % P
+    assert int(fp.field_numpy(out)[0]) == want
+    assert int(fp.field_numpy(lin)[0]) == sum(int(rho[j]) * int(g[j][0]) for j in range(3)) % P
+
+
+# -------------------------------------------------------------- witness ---
+WIT_SHAPES = [(1, 1, 1, 8), (5, 17, 7, 7), (16, 256, 256, 7), (33, 64, 129, 8), (130, 300, 300, 1),
+              (200, 1000, 260, 8), (257, 128, 513, 4)]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,s", WIT_SHAPES)
+def test_witness(fp, T, d_in, d_out, s):
+    rng = _rng(T * 1000 + d_in + d_out)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    Z, Y, R = fp.witness_linear(_dev(X), _dev(W), s)
+    torch.cuda.synchronize()
+    wz, wy, wr = O.witness(X, W, s)
+    assert np.array_equal(Z.cpu().numpy(), wz)
+    assert np.array_equal(Y.cpu().numpy(), wy)
+    assert np.array_equal(R.cpu().numpy(), wr)
+
+
+def test_witness_extremes_and_ties(fp):
+    # |Z| at its largest (all -128), all +127 rows, and exact rounding ties
+    T, d_in, d_out = 40, 4096, 70
+    X = np.full((T, d_in), -128, np.int8)
+    X[1::2] = 127
+    W = np.full((d_out, d_in), -128, np.int8)
+    W[3::3] = 127
+    W[5, :] = 0
+    W[5, 0] = 1                # Z = X[t, 0] exactly: -128 or 127
+    X[7, :] = 0
+    X[7, :128] = 1
+    W[6, :] = 0
+    W[6, :128] = 1             # Z[7, 6] = 128: a tie at s = 8
+    for s in (8, 7, 1):
+        Z, Y, R = fp.witness_linear(_dev(X), _dev(W), s)
+        torch.cuda.synchronize()
+        wz, wy, wr = O.witness(X, W, s)
+        assert np.array_equal(Z.cpu().numpy(), wz)
+        assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+
+
+def test_witness_strided_inputs(fp):
+    rng = _rng(21)
+    Xb, Wb = _i8(rng, (50, 320)), _i8(rng, (90, 330))
+    X, W = Xb[:, 5:305], Wb[:, 7:307]
+    Z, Y, R = fp.witness_linear(_dev(Xb)[:, 5:305], _dev(Wb)[:, 7:307], 8)
+    torch.cuda.synchronize()
+    wz, wy, wr = O.witness(np.ascontiguousarray(X), np.ascontiguousarray(W), 8)
+    assert np.array_equal(Z.cpu().numpy(), wz) and np.array_equal(Y.cpu().numpy(), wy)
+    assert np.array_equal(R.cpu().numpy(), wr)
+
+
+def test_witness_grouped(fp):
+    rng = _rng(22)
+    sizes = [3, 0, 40, 1, 0, 65, 17]
+    d_in, d_out = 200, 150
+    row_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    Xg = _i8(rng, (int(row_off[-1]), d_in))
+    Ws = [_i8(rng, (d_out, d_in)) for _ in sizes]
+    Z, Y, R = fp.witness_linear_grouped(_dev(Xg), [_dev(w) for w in Ws], row_off, 8)
+    torch.cuda.synchronize()
+    Z, Y, R = Z.cpu().numpy(), Y.cpu().numpy(), R.cpu().numpy()
+    for g, w in enumerate(Ws):
+        a, b = row_off[g], row_off[g + 1]
+        if a == b:
+            continue
+        wz, wy, wr = O.witness(Xg[a:b], w, 8)
+        assert np.array_equal(Z[a:b], wz) and np.array_equal(Y[a:b], wy) and np.array_equal(R[a:b], wr)
+
+
+def test_gather_rows(fp):
+    rng = _rng(23)
+    X = _i8(rng, (50, 96))
+    perm = rng.permutation(50).astype(np.int32)[:31]
+    out = fp.gather_rows(_dev(X), _dev(perm))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), X[perm])

@@ -1,0 +1,188 @@
+"""Whole layer proofs on the GPU against the CPU oracle.
+
+Reduced shapes of all five workloads are compared output by output and bit
+for bit (witness, eq tables, folds, claims, every round polynomial, finals,
+random linear combinations). The full-size workloads run in the exact launch
+configuration the benchmark times; there every fold, claim, round and final is
+compared exactly with the oracle (computed from the folds, which is cheap),
+the witness is compared on sampled entries against the oracle's own dot
+products, and every Y and R entry is checked against the GPU's Z through the
+rescale identity, and Z as a whole through its claim Z~(r_o || r_t) =
+sum_k x'[k] w'[k]."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from zero_knowledge_proof_amd.prover import make_prover
+
+pytestmark = pytest.mark.gpu
+P = O.P
+
+
+def _cmp_matmul(got, want, keys=("Z", "Y", "R", "x_fold", "w_fold", "rounds", "finals", "c0", "claim0")):
+    for k in keys:
+        if k not in want:
+            continue
+        g, w = got[k], want[k]
+        if isinstance(w, (int, np.integer)):
+            assert int(g) == int(w), k
+        else:
+            assert np.array_equal(np.asarray(g).reshape(np.asarray(w).shape), np.asarray(w)), k
+
+
+def _run(cfg):
+    inp = synth.make_inputs(cfg)
+    route = inp.get("route")
+    ch = synth.draw_challenges(cfg, route)
+    prover = make_prover(cfg, inp, ch)
+    prover.run()
+    torch.cuda.synchronize()
+    return inp, ch, prover.results()
+
+
+def test_layer_cfg1_full(fp):
+    cfg = synth.config(1)
+    inp, ch, got = _run(cfg)
+    want = O.prove_config(cfg, inp, ch)["main"]
+    _cmp_matmul(got, want)
+    assert np.array_equal(got["E_t"], want["E_t"]) and np.array_equal(got["E_o"], want["E_o"])
+    assert got["c0"] == got["claim0"]
+
+
+@pytest.mark.parametrize("shape", [dict(T=12, d_in=40, d_out=23), dict(T=100, d_in=1000, d_out=700),
+                                   dict(T=1, d_in=64, d_out=64), dict(T=2, d_in=2, d_out=1)])
+def test_layer_single_reduced(fp, shape):
+    cfg = synth.config(2, **shape)
+    inp, ch, got = _run(cfg)
+    want = O.prove_config(cfg, inp, ch)["up"]
+    _cmp_matmul(got, want)
+
+
+def test_layer_rlc_reduced(fp):
+    cfg = synth.config(3, T=40, d=320, d_ff=600)
+    inp, ch, got = _run(cfg)
+    want = O.prove_config(cfg, inp, ch)
+    for m in cfg.matmuls:
+        _cmp_matmul(got[m.name], want[m.name])
+    assert got["rlc"] == want["rlc"]
+
+
+def test_layer_batched_reduced(fp):
+    cfg = synth.config(5, T=24, d=96, d_kv=40, d_ff=300)
+    inp, ch, got = _run(cfg)
+    want = O.prove_config(cfg, inp, ch)
+    for m in cfg.matmuls:
+        _cmp_matmul(got[m.name], want[m.name], keys=("Z", "Y", "R", "x_fold", "w_fold", "c0"))
+    for k in ("rounds", "finals"):
+        assert np.array_equal(got["batch"][k], want["batch"][k]), k
+    assert got["batch"]["claim0"] == want["batch"]["claim0"] == want["batch"]["c0"] == got["batch"]["c0"]
+
+
+def test_layer_moe_reduced(fp):
+    cfg = synth.config(4, T=200, d=96, d_ff=160, n_experts=12)
+    inp, ch, got = _run(cfg)
+    want = O.prove_config(cfg, inp, ch)
+    assert sorted(got.keys()) == sorted(want.keys())
+    for e in want:
+        assert np.array_equal(got[e]["tokens"], want[e]["tokens"])
+        _cmp_matmul(got[e]["up"], want[e]["up"])
+        _cmp_matmul(got[e]["down"], want[e]["down"])
+
+
+# ------------------------------------------------------- full-size checks --
+def _sampled_witness(X, W, got, s, n=2048, seed=0):
+    rng = np.random.default_rng(seed)
+    T, d_out = got["Z"].shape
+    ts = rng.integers(0, T, n).astype(np.int32)
+    os_ = rng.integers(0, d_out, n).astype(np.int32)
+    ts[:4] = [0, T - 1, 0, T - 1]
+    os_[:4] = [0, d_out - 1, d_out - 1, 0]
+    want = O.witness_entries(X, W, ts, os_)
+    assert np.array_equal(got["Z"][ts, os_].astype(np.int64), want)
+    # every Y, R entry against the GPU's Z
+    assert O.check_rescale(got["Z"], got["Y"], got["R"], s) == ("OK", -1)
+
+
+def _check_full_matmul(X, W, s, got, r_t, r_o, r_rounds, x_fold=None):
+    E_t, E_o = O.eq_table(r_t), O.eq_table(r_o)
+    n = len(r_rounds)
+    xf = O.fold_rows(X, E_t, 1 << n) if x_fold is None else x_fold
+    wf = O.fold_rows(W, E_o, 1 << n)
+    assert np.array_equal(got["x_fold"], xf) and np.array_equal(got["w_fold"], wf)
+    rounds, finals, claim0 = O.sumcheck([xf], [wf], r_rounds)
+    # the claim of Z equals the sum-check's initial claim (Z = X W^T)
+    assert got["c0"] == claim0
+    if "rounds" in got:
+        assert np.array_equal(got["rounds"], rounds) and np.array_equal(np.asarray(got["finals"]).reshape(-1, 2), finals)
+        assert got["claim0"] == claim0
+    _sampled_witness(X, W, got, s)
+    return xf, wf
+
+
+def test_full_cfg2(fp):
+    cfg = synth.config(2)
+    inp, ch, got = _run(cfg)
+    _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
+
+
+def test_full_cfg3(fp):
+    cfg = synth.config(3)
+    inp, ch, got = _run(cfg)
+    C = 0
+    for m in cfg.matmuls:
+        _check_full_matmul(inp[m.x], inp[m.w], cfg.s, got[m.name], ch["r_t"], ch["r_o/" + m.name],
+                           ch["rounds/" + m.name])
+        g = got[m.name]["rounds"][-1]
+        C = (C + int(ch["rho/" + m.name][0]) * O.eval_deg2(int(g[0]), int(g[1]), int(g[2]),
+                                                          int(ch["rounds/" + m.name][-1]))) % P
+    assert got["rlc"] == C
+
+
+def test_full_cfg5(fp):
+    cfg = synth.config(5)
+    inp, ch, got = _run(cfg)
+    n = cfg.batched_n
+    As, Bs, rho = [], [], []
+    xcache = {}
+    c0 = 0
+    for m in cfg.matmuls:
+        r_o = ch["r_o/" + m.name]
+        if m.x not in xcache:
+            xcache[m.x] = O.fold_rows(inp[m.x], O.eq_table(ch["r_t"]), 1 << n)
+        g = got[m.name]
+        xf, wf = _check_full_matmul(inp[m.x], inp[m.w], cfg.s, g, ch["r_t"], r_o, [0] * n, x_fold=xcache[m.x])
+        As.append(xf)
+        Bs.append(wf)
+        rho.append(int(ch["rho/" + m.name][0]))
+        c0 = (c0 + rho[-1] * g["c0"]) % P
+    rounds, finals, claim0 = O.sumcheck(As, Bs, ch["rounds"], rho=rho)
+    b = got["batch"]
+    assert np.array_equal(b["rounds"], rounds) and np.array_equal(b["finals"], finals)
+    assert b["claim0"] == claim0 == c0 == b["c0"]
+
+
+def test_full_cfg4_sampled_experts(fp):
+    cfg = synth.config(4)
+    inp, ch, got = _run(cfg)
+    groups = O.group_tokens(inp["route"], cfg.n_experts)
+    present = [e for e in range(cfg.n_experts) if len(groups[e])]
+    assert sorted(got.keys()) == present
+    sizes = {e: len(groups[e]) for e in present}
+    pick = sorted({present[0], present[-1], max(present, key=lambda e: sizes[e]), min(present, key=lambda e: sizes[e]),
+                   present[len(present) // 2], present[len(present) // 3]})
+    for e in pick:
+        toks = groups[e]
+        assert np.array_equal(got[e]["tokens"], toks)
+        Xe, He = np.ascontiguousarray(inp["X"][toks]), np.ascontiguousarray(inp["H"][toks])
+        _check_full_matmul(Xe, inp["W1_%d" % e], cfg.s, got[e]["up"], ch["r_t/%d" % e], ch["r_o_up/%d" % e],
+                           ch["rounds_up/%d" % e])
+        _check_full_matmul(He, inp["W2_%d" % e], cfg.s, got[e]["down"], ch["r_t/%d" % e], ch["r_o_down/%d" % e],
+                           ch["rounds_down/%d" % e])
+    # every expert: the sum-check transcript verifies against its own claim
+    for e in present:
+        for side in ("up", "down"):
+            g = got[e][side]
+            key = "rounds_up/%d" % e if side == "up" else "rounds_down/%d" % e
+            assert O.check_sumcheck(g["rounds"], g["finals"], ch[key], g["c0"])[0] == "OK"

@@ -1,0 +1,326 @@
+"""MI355X (gfx950) prover for fixed-point linear layers: the witness of each
+quantized matmul and the sum-check proof of its claim over Goldilocks.
+
+This module is the thin binding over ``libfp.so`` (declared in
+``include/fp.h``): it marshals torch tensors into device pointers and the
+current HIP stream, and nothing else. Every step runs in the library's HIP
+kernels; there is no CPU fallback. Field elements travel as int64 tensors
+holding the raw 64-bit patterns of canonical values in [0, p).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+P = 0xFFFFFFFF00000001
+FP_I8, FP_I32 = 0, 1
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp.so")
+EXPORTS = [
+    "fp_last_error", "fp_witness_linear", "fp_witness_linear_grouped", "fp_moe_plan", "fp_gather_rows",
+    "fp_eq_table", "fp_eq_table_batched", "fp_eq_table_batched_workspace",
+    "fp_fold_matrix", "fp_fold_matrix_workspace", "fp_fold_matrix_batched", "fp_fold_matrix_batched_workspace",
+    "fp_mle_eval", "fp_mle_eval_workspace", "fp_sumcheck_prove", "fp_sumcheck_workspace",
+    "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
+    "fp_linear_combine",
+]
+
+_lib = None
+
+
+class FPError(RuntimeError):
+    pass
+
+
+class _EqDesc(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_void_p), ("n", ctypes.c_int32), ("E", ctypes.c_void_p)]
+
+
+class _ClaimDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("E_rows", ctypes.c_void_p), ("E_cols", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class _FoldDesc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("cols_pad", ctypes.c_int32), ("E", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+def lib():
+    """Load libfp.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FPError("libfp.so is not built (run __graft_entry__.build()): %s" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "fp_last_error": (ctypes.c_char_p, []),
+            "fp_witness_linear": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "fp_witness_linear_grouped": (ctypes.c_int, [vp, i64, vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "fp_moe_plan": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
+            "fp_gather_rows": (ctypes.c_int, [vp, i64, vp, i32, i32, vp, vp]),
+            "fp_eq_table": (ctypes.c_int, [vp, i32, vp, vp]),
+            "fp_eq_table_batched": (ctypes.c_int, [i32, vp, vp, sz, vp]),
+            "fp_eq_table_batched_workspace": (sz, [i32]),
+            "fp_fold_matrix": (ctypes.c_int, [i32, vp, i64, i32, i32, vp, vp, i32, vp, sz, vp]),
+            "fp_fold_matrix_workspace": (sz, [i32, i32, i32]),
+            "fp_fold_matrix_batched": (ctypes.c_int, [i32, i32, vp, vp, sz, vp]),
+            "fp_fold_matrix_batched_workspace": (sz, [i32, i32, vp]),
+            "fp_mle_eval": (ctypes.c_int, [i32, vp, i64, i32, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
+            "fp_mle_eval_workspace": (sz, [i32, i32, i32, i32, i32]),
+            "fp_sumcheck_prove": (ctypes.c_int, [i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "fp_sumcheck_workspace": (sz, [i32, i32]),
+            "fp_sumcheck_prove_multi": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+            "fp_combine_claims": (ctypes.c_int, [i32, vp, vp, vp, vp, vp]),
+            "fp_claim_eval_batched": (ctypes.c_int, [i32, i32, vp, vp, sz, vp]),
+            "fp_claim_eval_batched_workspace": (sz, [i32, i32, vp]),
+            "fp_linear_combine": (ctypes.c_int, [i32, vp, vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def require_gpu():
+    """Raise unless a GPU and the built library are both present."""
+    if not torch.cuda.is_available():
+        raise FPError("no GPU visible: the prover runs only on the GPU")
+    lib()
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise FPError("%s failed (code %d): %s" % (name, rc, lib().fp_last_error().decode()))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    assert t.is_cuda, "device tensor expected"
+    return t.data_ptr()
+
+
+def _ld(M) -> int:
+    """Leading dimension of a row-major 2-D tensor (any value >= cols when it has <= 1 row)."""
+    return M.stride(0) if M.shape[0] > 1 else max(M.stride(0), M.shape[1])
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev():
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+class Workspace:
+    """A growable device scratch buffer (one per stream use; not thread-shared)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=_dev())
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_ws = Workspace()
+
+
+def to_field_tensor(vals, device=None) -> torch.Tensor:
+    """Field values (ints or a uint64 array) as a device int64 tensor."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(vals, dtype=np.uint64)).view(np.int64)
+    return torch.from_numpy(a.copy()).to(device or _dev())
+
+
+def field_numpy(t: torch.Tensor):
+    """A device int64 field tensor as a numpy uint64 array."""
+    return t.detach().cpu().numpy().view("uint64")
+
+
+# ------------------------------------------------------------------ witness --
+def witness_linear(X, W, s: int, Z=None, Y=None, R=None, with_z: bool = True):
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    assert X.dtype == torch.int8 and W.dtype == torch.int8 and X.stride(1) == 1 and W.stride(1) == 1
+    if with_z and Z is None:
+        Z = torch.empty((T, d_out), dtype=torch.int32, device=X.device)
+    Y = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if Y is None else Y
+    R = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if R is None else R
+    _check(lib().fp_witness_linear(_ptr(X), _ld(X), _ptr(W), _ld(W), T, d_in, d_out, s,
+                                   _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), _stream()),
+           "fp_witness_linear")
+    return Z, Y, R
+
+
+def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):
+    """Xg: int8 [row_off[-1], d_in]; Ws: list of int8 [d_out, d_in]; row_off: host ints (G+1)."""
+    G = len(Ws)
+    d_in = Xg.shape[1]
+    d_out = Ws[0].shape[0]
+    total = int(row_off[-1])
+    if with_z and Z is None:
+        Z = torch.empty((total, d_out), dtype=torch.int32, device=Xg.device)
+    Y = torch.empty((total, d_out), dtype=torch.int8, device=Xg.device) if Y is None else Y
+    R = torch.empty((total, d_out), dtype=torch.int8, device=Xg.device) if R is None else R
+    wp = (ctypes.c_void_p * G)(*[w.data_ptr() for w in Ws])
+    ro = (ctypes.c_int32 * (G + 1))(*[int(v) for v in row_off])
+    _check(lib().fp_witness_linear_grouped(_ptr(Xg), _ld(Xg), wp, _ld(Ws[0]), ro, G, d_in, d_out, s,
+                                           _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), _stream()),
+           "fp_witness_linear_grouped")
+    return Z, Y, R
+
+
+def moe_plan(route, n_experts: int):
+    """Host-only grouping plan: (counts, offsets, perm) as numpy int32 arrays."""
+    import numpy as np
+    route = np.ascontiguousarray(route, dtype=np.int32)
+    T = len(route)
+    counts = np.empty(n_experts, np.int32)
+    offsets = np.empty(n_experts + 1, np.int32)
+    perm = np.empty(max(T, 1), np.int32)
+    _check(lib().fp_moe_plan(route.ctypes.data, T, n_experts, counts.ctypes.data, offsets.ctypes.data,
+                             perm.ctypes.data), "fp_moe_plan")
+    return counts, offsets, perm[:T]
+
+
+def gather_rows(X, perm_dev, out=None):
+    n = perm_dev.numel()
+    cols = X.shape[1]
+    out = torch.empty((n, cols), dtype=X.dtype, device=X.device) if out is None else out
+    _check(lib().fp_gather_rows(_ptr(X), _ld(X), _ptr(perm_dev), n, cols, _ptr(out), _stream()),
+           "fp_gather_rows")
+    return out
+
+
+# ----------------------------------------------------------------------- eq --
+def eq_table(r, E=None):
+    n = r.numel()
+    E = torch.empty(1 << n, dtype=torch.int64, device=_dev()) if E is None else E
+    _check(lib().fp_eq_table(_ptr(r) if n else None, n, _ptr(E), _stream()), "fp_eq_table")
+    return E
+
+
+def eq_table_batched(rs, Es=None):
+    k = len(rs)
+    if Es is None:
+        Es = [torch.empty(1 << r.numel(), dtype=torch.int64, device=_dev()) for r in rs]
+    descs = (_EqDesc * k)(*[_EqDesc(r.data_ptr() if r.numel() else None, r.numel(), E.data_ptr())
+                            for r, E in zip(rs, Es)])
+    need = lib().fp_eq_table_batched_workspace(k)
+    p, nb = _ws.get(need)
+    _check(lib().fp_eq_table_batched(k, descs, p, nb, _stream()), "fp_eq_table_batched")
+    return Es
+
+
+# -------------------------------------------------------------------- folds --
+def _dt(M):
+    if M.dtype == torch.int8:
+        return FP_I8
+    if M.dtype == torch.int32:
+        return FP_I32
+    raise TypeError(M.dtype)
+
+
+def fold_matrix(M, E, cols_pad: int | None = None, rows: int | None = None, out=None):
+    rows = M.shape[0] if rows is None else rows
+    cols = M.shape[1]
+    cols_pad = cols if cols_pad is None else cols_pad
+    out = torch.empty(cols_pad, dtype=torch.int64, device=M.device) if out is None else out
+    need = lib().fp_fold_matrix_workspace(_dt(M), rows, cols)
+    p, nb = _ws.get(need)
+    _check(lib().fp_fold_matrix(_dt(M), _ptr(M), _ld(M), rows, cols, _ptr(E), _ptr(out), cols_pad, p, nb,
+                                _stream()), "fp_fold_matrix")
+    return out
+
+
+def fold_matrix_batched(jobs):
+    """jobs: list of (M, E, cols_pad, out); all M of one dtype."""
+    k = len(jobs)
+    dt = _dt(jobs[0][0])
+    descs = (_FoldDesc * k)(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
+                                        out.data_ptr()) for (M, E, cp, out) in jobs])
+    need = lib().fp_fold_matrix_batched_workspace(dt, k, descs)
+    p, nb = _ws.get(need)
+    _check(lib().fp_fold_matrix_batched(dt, k, descs, p, nb, _stream()), "fp_fold_matrix_batched")
+    return [j[3] for j in jobs]
+
+
+def mle_eval(M, r_rows, r_cols, out=None):
+    rows, cols = M.shape
+    out = torch.empty(1, dtype=torch.int64, device=M.device) if out is None else out
+    nr, nc = r_rows.numel(), r_cols.numel()
+    need = lib().fp_mle_eval_workspace(_dt(M), rows, cols, nr, nc)
+    p, nb = _ws.get(need)
+    _check(lib().fp_mle_eval(_dt(M), _ptr(M), _ld(M), rows, cols, _ptr(r_rows) if nr else None, nr,
+                             _ptr(r_cols) if nc else None, nc, _ptr(out), p, nb, _stream()), "fp_mle_eval")
+    return out
+
+
+# ---------------------------------------------------------------- sum-check --
+def sumcheck_prove(As, Bs, r, rho=None, rounds=None, finals=None, claim0=None):
+    k = len(As)
+    n = r.numel()
+    dev = r.device
+    rounds = torch.empty((n, 3), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty((k, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    claim0 = torch.empty(1, dtype=torch.int64, device=dev) if claim0 is None else claim0
+    pa = (ctypes.c_void_p * k)(*[a.data_ptr() for a in As])
+    pb = (ctypes.c_void_p * k)(*[b.data_ptr() for b in Bs])
+    need = lib().fp_sumcheck_workspace(k, n)
+    p, nb = _ws.get(need)
+    _check(lib().fp_sumcheck_prove(k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds), _ptr(finals), _ptr(claim0),
+                                   p, nb, _stream()), "fp_sumcheck_prove")
+    return rounds, finals, claim0
+
+
+def sumcheck_prove_multi(A, B, r, rounds=None, finals=None, claim0=None):
+    n_inst, m = A.shape
+    n = r.shape[1]
+    assert m == 1 << n
+    dev = A.device
+    rounds = torch.empty((n_inst, n, 3), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty((n_inst, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    claim0 = torch.empty(n_inst, dtype=torch.int64, device=dev) if claim0 is None else claim0
+    _check(lib().fp_sumcheck_prove_multi(n_inst, n, _ptr(A), _ptr(B), _ptr(r), _ptr(rounds), _ptr(finals),
+                                         _ptr(claim0), _stream()), "fp_sumcheck_prove_multi")
+    return rounds, finals, claim0
+
+
+def combine_claims(g_last, x_last, rho, out=None):
+    """out = sum_j rho[j] g_j(x_j); g_last[j]: device view of 3 values, x_last[j]: view of 1."""
+    k = len(g_last)
+    out = torch.empty(1, dtype=torch.int64, device=rho.device) if out is None else out
+    pg = (ctypes.c_void_p * k)(*[g.data_ptr() for g in g_last])
+    px = (ctypes.c_void_p * k)(*[x.data_ptr() for x in x_last])
+    _check(lib().fp_combine_claims(k, pg, px, _ptr(rho), _ptr(out), _stream()), "fp_combine_claims")
+    return out
+
+
+def claim_eval_batched(jobs):
+    """jobs: list of (M, E_rows, E_cols, out); out_j = sum E_rows[t] E_cols[c] M[t, c]."""
+    k = len(jobs)
+    dt = _dt(jobs[0][0])
+    descs = (_ClaimDesc * k)(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
+                                          Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in jobs])
+    need = lib().fp_claim_eval_batched_workspace(dt, k, descs)
+    p, nb = _ws.get(need)
+    _check(lib().fp_claim_eval_batched(dt, k, descs, p, nb, _stream()), "fp_claim_eval_batched")
+    return [j[3] for j in jobs]
+
+
+def linear_combine(vals, rho, out=None):
+    k = len(vals)
+    out = torch.empty(1, dtype=torch.int64, device=rho.device) if out is None else out
+    pv = (ctypes.c_void_p * k)(*[v.data_ptr() for v in vals])
+    _check(lib().fp_linear_combine(k, pv, _ptr(rho), _ptr(out), _stream()), "fp_linear_combine")
+    return out

@@ -1,0 +1,33 @@
+// common.hpp - internal helpers shared by the libfp translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "fp.h"
+
+namespace fpi {
+
+// Sets the thread-local message and returns `code`.
+int fail(int code, const char* fmt, ...);
+// Clears the message; returns FP_OK.
+int ok();
+// Checks hipGetLastError() after a launch.
+int check_launch(const char* what);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Wave64 reductions of a 64-bit value held as two 32-bit halves.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64);
+  uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// --- launchers implemented in the .hip files (no validation inside) -------
+int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st);
+int launch_eq_batched(int32_t count, const fp_eq_desc* descs_host, void* ws, size_t ws_bytes, hipStream_t st);
+size_t eq_batched_ws(int32_t count);
+
+}  // namespace fpi

@@ -1,0 +1,124 @@
+// eq.hip - eq-table expansion: E[k] = eq(r, k) = prod_j (k_j ? r_j : 1 - r_j).
+//
+// "How fast can FlashProve go", §2: a table's folded row is the weighted sum
+// of its rows; these are the weights. Each 256-entry block builds the table of
+// its low 8 variables by doubling in LDS (8 rounds, one multiply per entry per
+// round) and multiplies it by the product over the high variables, which is
+// the same for the whole block. Two multiplies per entry overall beyond the
+// doubling, instead of n in the product form.
+#include <vector>
+
+#include "common.hpp"
+#include "gl.hpp"
+
+namespace {
+
+struct EqJob {
+  const fp_elem* r;
+  fp_elem* E;
+  int32_t n;
+  int32_t block_start;
+};
+
+__device__ __forceinline__ void eq_block(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E,
+                                         int64_t blk) {
+  __shared__ uint64_t L[256];
+  const int tid = threadIdx.x;
+  const int nl = n < 8 ? n : 8;
+  if (tid == 0) L[0] = 1;
+  __syncthreads();
+  for (int j = 0; j < nl; ++j) {
+    const int h = 1 << j;
+    const uint64_t rj = r[j];
+    uint64_t v0 = 0, v1 = 0;
+    if (tid < h) {
+      const uint64_t e = L[tid];
+      v0 = gl::mul(e, gl::sub(1, rj));
+      v1 = gl::mul(e, rj);
+    }
+    __syncthreads();
+    if (tid < h) {
+      L[tid] = v0;
+      L[tid + h] = v1;
+    }
+    __syncthreads();
+  }
+  const int64_t base = blk << 8;
+  uint64_t hp = 1;
+  for (int j = 8; j < n; ++j) {
+    const uint64_t rj = r[j];
+    hp = gl::mul(hp, ((base >> j) & 1) ? rj : gl::sub(1, rj));
+  }
+  if (tid < (1 << nl)) E[base + tid] = (n > 8) ? gl::mul(L[tid], hp) : L[tid];
+}
+
+__global__ __launch_bounds__(256) void eq_kernel(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E) {
+  eq_block(r, n, E, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void eq_batched_kernel(const EqJob* __restrict__ jobs, int count) {
+  // the job whose block range holds this block (jobs sorted by block_start)
+  int lo = 0, hi = count - 1;
+  const int b = blockIdx.x;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (jobs[mid].block_start <= b) lo = mid; else hi = mid - 1;
+  }
+  const EqJob j = jobs[lo];
+  eq_block(j.r, j.n, j.E, b - j.block_start);
+}
+
+inline int64_t eq_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8); }
+
+}  // namespace
+
+namespace fpi {
+
+int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st) {
+  hipLaunchKernelGGL(eq_kernel, dim3((unsigned)eq_blocks(n)), dim3(256), 0, st, r, (int)n, E);
+  return check_launch("eq_kernel");
+}
+
+size_t eq_batched_ws(int32_t count) { return align_up(sizeof(EqJob) * (size_t)(count > 0 ? count : 0), 256); }
+
+int launch_eq_batched(int32_t count, const fp_eq_desc* d, void* ws, size_t ws_bytes, hipStream_t st) {
+  std::vector<EqJob> jobs((size_t)count);
+  int64_t blocks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    jobs[i] = EqJob{d[i].r, d[i].E, d[i].n, (int32_t)blocks};
+    blocks += eq_blocks(d[i].n);
+  }
+  if (blocks > 0x7FFFFFFF) return fail(FP_ESHAPE, "fp_eq_table_batched: too many blocks");
+  (void)ws_bytes;
+  hipError_t e = hipMemcpyAsync(ws, jobs.data(), sizeof(EqJob) * jobs.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return fail(FP_EHIP, "fp_eq_table_batched: descriptor copy: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(eq_batched_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const EqJob*)ws, (int)count);
+  return check_launch("eq_batched_kernel");
+}
+
+}  // namespace fpi
+
+extern "C" int fp_eq_table(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t stream) {
+  if (n < 0 || n > FP_MAX_N) return fpi::fail(FP_ESHAPE, "fp_eq_table: n=%d outside [0, %d]", n, FP_MAX_N);
+  if (!E || (n > 0 && !r)) return fpi::fail(FP_EARG, "fp_eq_table: null pointer");
+  int rc = fpi::launch_eq(r, n, E, stream);
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" size_t fp_eq_table_batched_workspace(int32_t count) { return fpi::eq_batched_ws(count); }
+
+extern "C" int fp_eq_table_batched(int32_t count, const fp_eq_desc* descs, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (count < 0) return fpi::fail(FP_EARG, "fp_eq_table_batched: count < 0");
+  if (count == 0) return fpi::ok();
+  if (!descs || !ws) return fpi::fail(FP_EARG, "fp_eq_table_batched: null pointer");
+  if (ws_bytes < fpi::eq_batched_ws(count)) return fpi::fail(FP_EWORKSPACE, "fp_eq_table_batched: workspace too small");
+  for (int32_t i = 0; i < count; ++i) {
+    if (descs[i].n < 0 || descs[i].n > 24)
+      return fpi::fail(FP_ESHAPE, "fp_eq_table_batched: desc %d has n=%d outside [0, 24]", i, descs[i].n);
+    if (!descs[i].E || (descs[i].n > 0 && !descs[i].r))
+      return fpi::fail(FP_EARG, "fp_eq_table_batched: desc %d has a null pointer", i);
+  }
+  int rc = fpi::launch_eq_batched(count, descs, ws, ws_bytes, stream);
+  return rc ? rc : fpi::ok();
+}

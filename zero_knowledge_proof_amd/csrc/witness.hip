@@ -1,0 +1,316 @@
+// witness.hip - the witness of a fixed-point linear layer on int8 matrix cores.
+//
+// "How fast can FlashProve go", §2: the model is integer-quantized, so every
+// product is rescaled and many results are clamped; §3.1: the rescale
+// g_w = round(g^ / 2^k) commits its remainder r = g^ - 2^k g_w, which the
+// matmul's sum-check uses in place of g^ (so Z itself is kept for the claim).
+// Per output entry:
+//   Z = sum_k X[t,k] W[o,k]          (int8 x int8 -> int32, exact)
+//   Q = floor((Z + 2^(s-1)) / 2^s)   (ties up)  = (Z >> s) + bit_{s-1}(Z)
+//   R = Z - 2^s Q                    = (Z & (2^s - 1)) - bit_{s-1}(Z) 2^s
+//   Y = clamp(Q, -128, 127)
+// The bit form never forms Z + 2^(s-1) or 2^s Q, so it cannot overflow int32.
+//
+// Kernel: X [M=T, K=d_in] and W [N=d_out, K] are both K-contiguous, which is
+// the operand order of v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with the
+// 16 bytes at k = 16*(l/32) of a 32-wide K slice for both operands, so the
+// products pair equal k. Workgroup tiles are BM x BN with a wave tile of
+// WM x WN (32x32 MFMA blocks), K steps of 64 bytes double-buffered through
+// LDS (rows padded to 80 bytes so the 16-byte reads of 16 consecutive rows
+// hit distinct bank groups). Workgroup ids are remapped so that each XCD
+// (workgroups are dealt round-robin to the 8 XCDs) works on a contiguous run
+// of tiles, which share W and X panels in that XCD's L2.
+#include "common.hpp"
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;
+constexpr int PITCH = 80;
+constexpr int MAXG = 128;  // groups per grouped launch
+
+struct WitArgs {
+  const int8_t* X;
+  int64_t ldx;
+  const int8_t* W;
+  int64_t ldw;
+  int32_t M, N, K, s;
+  int32_t* Z;
+  int8_t* Y;
+  int8_t* R;
+  int32_t tiles_m, tiles_n;
+  int32_t vecX, vecW;
+};
+
+struct GroupTab {
+  const int8_t* W[MAXG];
+  int32_t row_off[MAXG + 1];   // output / X rows of each group
+  int32_t tile_off[MAXG + 1];  // first M tile of each group
+  int32_t G;
+};
+
+__device__ __forceinline__ v4i load16(const int8_t* rowp, int k, int K, bool vec) {
+  if (vec && k + 16 <= K) return *(const v4i*)(rowp + k);
+  int w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 16; ++b)
+    if (k + b < K) w[b >> 2] |= (int)((uint32_t)(uint8_t)rowp[k + b] << (8 * (b & 3)));
+  v4i r = {w[0], w[1], w[2], w[3]};
+  return r;
+}
+
+// Map a linear workgroup id to a tile id so that each XCD gets a contiguous
+// range of tiles (ids are dealt to XCDs round-robin).
+__device__ __forceinline__ int xcd_tile(int bid, int nb) {
+  constexpr int NX = 8;
+  const int x = bid % NX, li = bid / NX;
+  const int q = nb / NX, rm = nb % NX;
+  const int start = (x < rm) ? x * (q + 1) : rm * (q + 1) + (x - rm) * q;
+  return start + li;
+}
+
+template <int BM, int BN, int WM, int WN, bool GROUPED>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
+  constexpr int WAVES_N = BN / WN;
+  constexpr int NT = (BM / WM) * WAVES_N * 64;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NCA = BM * (BK / 16), NCB = BN * (BK / 16);  // 16-byte chunks per K step
+  constexpr int CA = (NCA + NT - 1) / NT;                      // chunks per thread
+  constexpr int CB = (NCB + NT - 1) / NT;
+  __shared__ __align__(16) int8_t sA[2][BM * PITCH];
+  __shared__ __align__(16) int8_t sB[2][BN * PITCH];
+
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  int tm = tile % a.tiles_m;
+  const int tn = tile / a.tiles_m;
+
+  const int8_t* Xb = a.X;
+  const int8_t* Wb = a.W;
+  int row_base = 0;       // first X / output row of this tile
+  int row_lim = a.M;      // rows valid in this tile's group: [row_base, row_lim)
+  if constexpr (GROUPED) {
+    int lo = 0, hi = gt.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gt.tile_off[mid] <= tm) lo = mid; else hi = mid - 1;
+    }
+    Wb = gt.W[lo];
+    row_base = gt.row_off[lo] + (tm - gt.tile_off[lo]) * BM;
+    row_lim = gt.row_off[lo + 1];
+  } else {
+    row_base = tm * BM;
+  }
+  const int col_base = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm0 = (wave / WAVES_N) * WM;
+  const int wn0 = (wave % WAVES_N) * WN;
+
+  // global -> register staging
+  const int8_t* pa[CA];
+  const int8_t* pb[CB];
+  int sa_off[CA], sb_off[CB], ka[CA], kb[CB];
+#pragma unroll
+  for (int c = 0; c < CA; ++c) {
+    const int ch = tid + c * NT;
+    const int row = ch >> 2, kc = (ch & 3) * 16;
+    const int g = row_base + row;
+    pa[c] = (ch < NCA && g < row_lim) ? Xb + (int64_t)g * a.ldx : nullptr;
+    ka[c] = kc;
+    sa_off[c] = (ch < NCA) ? row * PITCH + kc : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int ch = tid + c * NT;
+    const int row = ch >> 2, kc = (ch & 3) * 16;
+    const int g = col_base + row;
+    pb[c] = (ch < NCB && g < a.N) ? Wb + (int64_t)g * a.ldw : nullptr;
+    kb[c] = kc;
+    sb_off[c] = (ch < NCB) ? row * PITCH + kc : -1;
+  }
+  const bool vx = a.vecX, vw = a.vecW;
+  v4i ra[CA], rb[CB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      v4i z = {0, 0, 0, 0};
+      ra[c] = pa[c] ? load16(pa[c], k0 + ka[c], a.K, vx) : z;
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      v4i z = {0, 0, 0, 0};
+      rb[c] = pb[c] ? load16(pb[c], k0 + kb[c], a.K, vw) : z;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c)
+      if (NCA % NT == 0 || sa_off[c] >= 0) *(v4i*)&sA[buf][sa_off[c]] = ra[c];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+      if (NCB % NT == 0 || sb_off[c] >= 0) *(v4i*)&sB[buf][sb_off[c]] = rb[c];
+  };
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  const int KT = (a.K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int lrow = lane & 31, lk = (lane >> 5) * 16;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      v4i fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = *(const v4i*)&sA[buf][(wm0 + 32 * i + lrow) * PITCH + kk * 32 + lk];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = *(const v4i*)&sB[buf][(wn0 + 32 * j + lrow) * PITCH + kk * 32 + lk];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: rescale, clamp, remainder
+  const int s = a.s;
+  const int32_t lowmask = (1 << s) - 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = col_base + wn0 + 32 * j + (lane & 31);
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = row_base + wm0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row >= row_lim) continue;
+        const int32_t z = acc[i][j][v];
+        const int32_t bit = (z >> (s - 1)) & 1;
+        const int32_t q = (z >> s) + bit;
+        const int32_t rr = (z & lowmask) - (bit << s);
+        const int32_t y = q < -128 ? -128 : (q > 127 ? 127 : q);
+        const int64_t idx = (int64_t)row * a.N + col;
+        if (a.Z) a.Z[idx] = z;
+        a.Y[idx] = (int8_t)y;
+        a.R[idx] = (int8_t)rr;
+      }
+    }
+  }
+}
+
+// Tile configurations: (BM, BN, WM, WN)
+#define WIT_BIG 128, 128, 64, 64
+#define WIT_SMALL 32, 128, 32, 32
+
+template <int BM, int BN, int WM, int WN, bool GROUPED>
+int launch(const WitArgs& a, const GroupTab& gt, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return FP_OK;
+  if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
+  hipLaunchKernelGGL((witness_kernel<BM, BN, WM, WN, GROUPED>), dim3((unsigned)blocks),
+                     dim3((BM / WM) * (BN / WN) * 64), 0, st, a, gt);
+  return fpi::check_launch("witness_kernel");
+}
+
+int validate(const char* fn, int64_t ldx, int64_t ldw, int32_t T, int32_t d_in, int32_t d_out, int32_t s,
+             const int8_t* Y, const int8_t* R) {
+  if (T < 0 || d_in < 0 || d_out < 0) return fpi::fail(FP_EARG, "%s: negative size", fn);
+  if (d_in > FP_MAX_DIN) return fpi::fail(FP_ESHAPE, "%s: d_in=%d > %d (int32 Z would not be exact)", fn, d_in, FP_MAX_DIN);
+  if (s < 1 || s > 8) return fpi::fail(FP_ERANGE, "%s: s=%d outside [1, 8]", fn, s);
+  if (ldx < d_in || ldw < d_in) return fpi::fail(FP_ESHAPE, "%s: leading dimension < d_in", fn);
+  if ((int64_t)T * d_out > 0 && (!Y || !R)) return fpi::fail(FP_EARG, "%s: null Y or R", fn);
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T, int32_t d_in,
+                                 int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream) {
+  int rc = validate("fp_witness_linear", ldx, ldw, T, d_in, d_out, s, Y, R);
+  if (rc) return rc;
+  if (T == 0 || d_out == 0) return fpi::ok();
+  if (d_in > 0 && (!X || !W)) return fpi::fail(FP_EARG, "fp_witness_linear: null X or W");
+  WitArgs a{};
+  a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
+  a.M = T; a.N = d_out; a.K = d_in; a.s = s;
+  a.Z = Z; a.Y = Y; a.R = R;
+  a.vecX = ((ldx & 15) == 0) && ((((uintptr_t)X) & 15) == 0);
+  a.vecW = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
+  GroupTab gt{};
+  if (T <= 32) {
+    a.tiles_m = (T + 31) / 32;
+    a.tiles_n = (d_out + 127) / 128;
+    rc = launch<WIT_SMALL, false>(a, gt, (int64_t)a.tiles_m * a.tiles_n, stream);
+  } else {
+    a.tiles_m = (T + 127) / 128;
+    a.tiles_n = (d_out + 127) / 128;
+    rc = launch<WIT_BIG, false>(a, gt, (int64_t)a.tiles_m * a.tiles_n, stream);
+  }
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int8_t* const* W_ptrs, int64_t ldw,
+                                         const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out, int32_t s,
+                                         int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream) {
+  if (G < 0 || G > FP_MAX_GROUPS) return fpi::fail(FP_EARG, "fp_witness_linear_grouped: G=%d outside [0, %d]", G, FP_MAX_GROUPS);
+  if (G == 0) return fpi::ok();
+  if (!row_off || !W_ptrs) return fpi::fail(FP_EARG, "fp_witness_linear_grouped: null host array");
+  if (row_off[0] != 0) return fpi::fail(FP_EARG, "fp_witness_linear_grouped: row_off[0] != 0");
+  for (int g = 0; g < G; ++g)
+    if (row_off[g + 1] < row_off[g]) return fpi::fail(FP_EARG, "fp_witness_linear_grouped: row_off decreases at %d", g);
+  const int32_t total = row_off[G];
+  int rc = validate("fp_witness_linear_grouped", ldx, ldw, total, d_in, d_out, s, Y, R);
+  if (rc) return rc;
+  if (total == 0 || d_out == 0) return fpi::ok();
+  if (d_in > 0 && !X) return fpi::fail(FP_EARG, "fp_witness_linear_grouped: null X");
+  for (int g = 0; g < G; ++g)
+    if (row_off[g + 1] > row_off[g] && d_in > 0 && !W_ptrs[g])
+      return fpi::fail(FP_EARG, "fp_witness_linear_grouped: null W for non-empty group %d", g);
+  WitArgs a{};
+  a.X = X; a.ldx = ldx; a.W = nullptr; a.ldw = ldw;
+  a.M = total; a.N = d_out; a.K = d_in; a.s = s;
+  a.Z = Z; a.Y = Y; a.R = R;
+  a.vecX = ((ldx & 15) == 0) && ((((uintptr_t)X) & 15) == 0);
+  bool vw = (ldw & 15) == 0;
+  for (int g = 0; g < G; ++g) vw = vw && ((((uintptr_t)W_ptrs[g]) & 15) == 0);
+  a.vecW = vw;
+  a.tiles_n = (d_out + 127) / 128;
+  constexpr int GBM = 32;
+  for (int g0 = 0; g0 < G; g0 += MAXG) {
+    const int gc = (G - g0) < MAXG ? (G - g0) : MAXG;
+    GroupTab gt{};
+    int tiles = 0, ng = 0;
+    for (int g = g0; g < g0 + gc; ++g) {
+      const int rows = row_off[g + 1] - row_off[g];
+      if (rows == 0) continue;  // empty groups own no tiles
+      gt.W[ng] = W_ptrs[g];
+      gt.row_off[ng] = row_off[g];
+      gt.row_off[ng + 1] = row_off[g + 1];
+      gt.tile_off[ng] = tiles;
+      tiles += (rows + GBM - 1) / GBM;
+      ++ng;
+    }
+    if (ng == 0) continue;
+    gt.tile_off[ng] = tiles;
+    gt.G = ng;
+    a.tiles_m = tiles;
+    rc = launch<WIT_SMALL, true>(a, gt, (int64_t)tiles * a.tiles_n, stream);
+    if (rc) return rc;
+  }
+  return fpi::ok();
+}

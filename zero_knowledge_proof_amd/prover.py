@@ -1,0 +1,327 @@
+"""Layer proofs strung together from the libfp entry points.
+
+"How fast can FlashProve go", §2: for each linear map the prover commits the
+rescaled output and the remainder (§3.1), and sum-check reduces the matmul
+claim about Z to claims about the committed activations and the weights. One
+``run()`` of a layer prover performs, on one stream and in protocol order:
+
+  witness  Z = X W^T, Y, R                     (fp_witness_linear[_grouped])
+  eq       E_t = eq(r_t, .), E_o = eq(r_o, .)  (fp_eq_table_batched)
+  folds    x' = X~(. || r_t), w' = W~(. || r_o) (fp_fold_matrix_batched)
+  claim    c0 = Z~(r_o || r_t)                  (fp_claim_eval_batched)
+  rounds   sum-check over k on (x', w')         (fp_sumcheck_prove[_multi])
+  merge    random linear combinations           (fp_combine_claims, fp_linear_combine)
+
+The challenges (drawn before the run and passed in) follow the witness in the
+stream order; each round challenge is read on the device only after its round
+polynomial is complete. Every buffer is allocated at construction, so ``run``
+only enqueues kernels. Inputs are host numpy arrays uploaded once.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (claim_eval_batched, combine_claims, eq_table_batched, fold_matrix_batched, gather_rows,
+               linear_combine, moe_plan, sumcheck_prove, sumcheck_prove_multi, to_field_tensor, field_numpy,
+               witness_linear, witness_linear_grouped)
+
+
+def _nomark(name):
+    pass
+
+
+def log2ceil(v: int) -> int:
+    return 0 if v <= 1 else (int(v) - 1).bit_length()
+
+
+def _i8(a: np.ndarray, dev) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _f(n, dev):
+    return torch.empty(n, dtype=torch.int64, device=dev)
+
+
+class _Challenges:
+    """All challenges of a workload in one device buffer, with named views."""
+
+    def __init__(self, ch: dict, dev):
+        keys = list(ch.keys())
+        flat = np.concatenate([np.asarray(ch[k], np.uint64) for k in keys]) if keys else np.zeros(0, np.uint64)
+        self.buf = to_field_tensor(flat, dev) if len(flat) else _f(0, dev)
+        self.views, pos = {}, 0
+        for k in keys:
+            n = len(ch[k])
+            self.views[k] = self.buf[pos:pos + n]
+            pos += n
+
+    def __getitem__(self, k):
+        return self.views[k]
+
+
+class SingleLayerProver:
+    """One linear map: witness, claim and sum-check over d_in."""
+
+    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None, with_z: bool = True):
+        dev = dev or torch.device("cuda")
+        self.s = s
+        self.X, self.W = _i8(X, dev), _i8(W, dev)
+        T, d_in = X.shape
+        d_out = W.shape[0]
+        self.n = log2ceil(d_in)
+        self.ch = _Challenges({"r_t": ch["r_t"], "r_o": ch["r_o"], "rounds": ch["rounds"]}, dev)
+        self.Z = torch.empty((T, d_out), dtype=torch.int32, device=dev)
+        self.Y = torch.empty((T, d_out), dtype=torch.int8, device=dev)
+        self.R = torch.empty((T, d_out), dtype=torch.int8, device=dev)
+        self.E_t, self.E_o = _f(1 << log2ceil(T), dev), _f(1 << log2ceil(d_out), dev)
+        self.xf, self.wf = _f(1 << self.n, dev), _f(1 << self.n, dev)
+        self.c0 = _f(1, dev)
+        self.rounds = torch.empty((self.n, 3), dtype=torch.int64, device=dev)
+        self.finals = torch.empty((1, 2), dtype=torch.int64, device=dev)
+        self.claim0 = _f(1, dev)
+
+    def run(self, mark=_nomark):
+        mark("witness")
+        witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)
+        mark("eq")
+        eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o])
+        mark("fold")
+        fold_matrix_batched([(self.X, self.E_t, 1 << self.n, self.xf), (self.W, self.E_o, 1 << self.n, self.wf)])
+        mark("claim")
+        claim_eval_batched([(self.Z, self.E_t, self.E_o, self.c0)])
+        mark("sumcheck")
+        sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                       claim0=self.claim0)
+        mark("end")
+
+    def results(self) -> dict:
+        return {"Z": self.Z.cpu().numpy(), "Y": self.Y.cpu().numpy(), "R": self.R.cpu().numpy(),
+                "E_t": field_numpy(self.E_t), "E_o": field_numpy(self.E_o),
+                "x_fold": field_numpy(self.xf), "w_fold": field_numpy(self.wf),
+                "c0": int(field_numpy(self.c0)[0]), "rounds": field_numpy(self.rounds),
+                "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
+
+
+class MultiMatmulProver:
+    """Several linear maps of one layer sharing the token axis (one r_t).
+
+    mode "rlc_out": each claim gets its own sum-check; the finished claims are
+    merged by a random linear combination (the dense MLP's gate/up/down).
+    mode "batched": the claims are merged first (rho-weighted) and proved by
+    one batched sum-check over tables padded to 2^batched_n (all seven maps of
+    a transformer layer)."""
+
+    def __init__(self, cfg, inp: dict, ch: dict, dev=None):
+        dev = dev or torch.device("cuda")
+        self.cfg = cfg
+        self.mode = cfg.kind
+        s = cfg.s
+        self.s = s
+        self.tens = {}
+        for m in cfg.matmuls:
+            for nm in (m.x, m.w):
+                if nm not in self.tens:
+                    self.tens[nm] = _i8(inp[nm], dev)
+        self.ch = _Challenges(ch, dev)
+        T = cfg.T
+        self.E_t = _f(1 << cfg.n_t, dev)
+        self.mm = []
+        nb = cfg.batched_n if self.mode == "batched" else None
+        xf = {}
+        for m in cfg.matmuls:
+            n = nb if nb is not None else m.n
+            key = (m.x, n)
+            if key not in xf:
+                xf[key] = _f(1 << n, dev)
+            d = {"m": m, "n": n, "xf": xf[key], "wf": _f(1 << n, dev), "E_o": _f(1 << m.n_o, dev),
+                 "Z": torch.empty((T, m.d_out), dtype=torch.int32, device=dev),
+                 "Y": torch.empty((T, m.d_out), dtype=torch.int8, device=dev),
+                 "R": torch.empty((T, m.d_out), dtype=torch.int8, device=dev), "c0": _f(1, dev)}
+            if self.mode == "rlc_out":
+                d.update(rounds=torch.empty((n, 3), dtype=torch.int64, device=dev),
+                         finals=torch.empty((1, 2), dtype=torch.int64, device=dev), claim0=_f(1, dev))
+            self.mm.append(d)
+        self.x_jobs = [(self.tens[x], None, 1 << n, buf) for (x, n), buf in xf.items()]
+        if self.mode == "rlc_out":
+            self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
+            self.rlc = _f(1, dev)
+        else:
+            self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
+            self.c0_batch = _f(1, dev)
+            self.rounds = torch.empty((nb, 3), dtype=torch.int64, device=dev)
+            self.finals = torch.empty((len(cfg.matmuls), 2), dtype=torch.int64, device=dev)
+            self.claim0 = _f(1, dev)
+
+    def run(self, mark=_nomark):
+        mark("witness")
+        for d in self.mm:
+            m = d["m"]
+            witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
+        mark("eq")
+        eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
+                         [self.E_t] + [d["E_o"] for d in self.mm])
+        mark("fold")
+        jobs = [(M, self.E_t, cp, out) for (M, _, cp, out) in self.x_jobs]
+        jobs += [(self.tens[d["m"].w], d["E_o"], 1 << d["n"], d["wf"]) for d in self.mm]
+        fold_matrix_batched(jobs)
+        mark("claim")
+        claim_eval_batched([(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm])
+        mark("sumcheck")
+        if self.mode == "rlc_out":
+            for d in self.mm:
+                sumcheck_prove([d["xf"]], [d["wf"]], self.ch["rounds/" + d["m"].name], rounds=d["rounds"],
+                               finals=d["finals"], claim0=d["claim0"])
+            mark("merge")
+            combine_claims([d["rounds"][-1] for d in self.mm],
+                           [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
+        else:
+            linear_combine([d["c0"] for d in self.mm], self.rho, out=self.c0_batch)
+            sumcheck_prove([d["xf"] for d in self.mm], [d["wf"] for d in self.mm], self.ch["rounds"], rho=self.rho,
+                           rounds=self.rounds, finals=self.finals, claim0=self.claim0)
+        mark("end")
+
+    def results(self) -> dict:
+        out = {"E_t": field_numpy(self.E_t)}
+        for d in self.mm:
+            r = {"Z": d["Z"].cpu().numpy(), "Y": d["Y"].cpu().numpy(), "R": d["R"].cpu().numpy(),
+                 "E_o": field_numpy(d["E_o"]), "x_fold": field_numpy(d["xf"]), "w_fold": field_numpy(d["wf"]),
+                 "c0": int(field_numpy(d["c0"])[0])}
+            if self.mode == "rlc_out":
+                r.update(rounds=field_numpy(d["rounds"]), finals=field_numpy(d["finals"]),
+                         claim0=int(field_numpy(d["claim0"])[0]))
+            out[d["m"].name] = r
+        if self.mode == "rlc_out":
+            out["rlc"] = int(field_numpy(self.rlc)[0])
+        else:
+            out["batch"] = {"rounds": field_numpy(self.rounds), "finals": field_numpy(self.finals),
+                            "claim0": int(field_numpy(self.claim0)[0]), "c0": int(field_numpy(self.c0_batch)[0])}
+        return out
+
+
+class MoEBlockProver:
+    """MoE block: top-1 routed tokens grouped by expert (stable, ascending
+    token order), one grouped witness launch per projection, and an
+    independent claim + sum-check per expert and projection. A group of T_e
+    tokens is logically padded with zero rows to 2^ceil(log2 T_e)."""
+
+    def __init__(self, cfg, inp: dict, ch: dict, dev=None):
+        dev = dev or torch.device("cuda")
+        self.cfg = cfg
+        s, d, dff = cfg.s, cfg.d_model, cfg.d_ff
+        self.s = s
+        route = np.asarray(inp["route"], np.int32)
+        counts, offsets, perm = moe_plan(route, cfg.n_experts)
+        self.counts, self.offsets = counts, offsets
+        self.experts = [e for e in range(cfg.n_experts) if counts[e] > 0]
+        ne = len(self.experts)
+        self.perm = torch.from_numpy(perm.astype(np.int32)).to(dev)
+        self.X, self.H = _i8(inp["X"], dev), _i8(inp["H"], dev)
+        self.W1 = [_i8(inp["W1_%d" % e], dev) for e in self.experts]
+        self.W2 = [_i8(inp["W2_%d" % e], dev) for e in self.experts]
+        T = len(route)
+        self.Xg = torch.empty((T, d), dtype=torch.int8, device=dev)
+        self.Hg = torch.empty((T, dff), dtype=torch.int8, device=dev)
+        self.row_off = [0] + [int(offsets[e + 1]) for e in self.experts]
+        self.n_up, self.n_dn = log2ceil(d), log2ceil(dff)   # sum-check rounds over each d_in
+        self.Zu = torch.empty((T, dff), dtype=torch.int32, device=dev)
+        self.Yu = torch.empty((T, dff), dtype=torch.int8, device=dev)
+        self.Ru = torch.empty((T, dff), dtype=torch.int8, device=dev)
+        self.Zd = torch.empty((T, d), dtype=torch.int32, device=dev)
+        self.Yd = torch.empty((T, d), dtype=torch.int8, device=dev)
+        self.Rd = torch.empty((T, d), dtype=torch.int8, device=dev)
+        # challenges rearranged per kind (host-side marshalling, once)
+        rt = [np.asarray(ch["r_t/%d" % e], np.uint64) for e in self.experts]
+        self.nt = [len(v) for v in rt]
+        self.ch = _Challenges({"r_t": np.concatenate(rt) if sum(self.nt) else np.zeros(0, np.uint64),
+                               "r_o_up": np.concatenate([ch["r_o_up/%d" % e] for e in self.experts]),
+                               "r_o_down": np.concatenate([ch["r_o_down/%d" % e] for e in self.experts]),
+                               "rounds": np.concatenate([ch["rounds_up/%d" % e] for e in self.experts] +
+                                                        [ch["rounds_down/%d" % e] for e in self.experts])}, dev)
+        nu, nd = self.n_up, self.n_dn
+        self.r_up = self.ch["rounds"][:ne * nu].view(ne, nu)
+        self.r_dn = self.ch["rounds"][ne * nu:].view(ne, nd)
+        no_up, no_dn = log2ceil(dff), log2ceil(d)
+        self.E_t = [_f(1 << k, dev) for k in self.nt]
+        self.E_ou = _f(ne << no_up, dev).view(ne, 1 << no_up)
+        self.E_od = _f(ne << no_dn, dev).view(ne, 1 << no_dn)
+        # x' and w' tables of the up and down claims, one row per expert
+        self.Au, self.Bu = _f(ne << nu, dev).view(ne, 1 << nu), _f(ne << nu, dev).view(ne, 1 << nu)
+        self.Ad, self.Bd = _f(ne << nd, dev).view(ne, 1 << nd), _f(ne << nd, dev).view(ne, 1 << nd)
+        self.c0 = _f(2 * ne, dev)
+        self.rounds_u = torch.empty((ne, nu, 3), dtype=torch.int64, device=dev)
+        self.rounds_d = torch.empty((ne, nd, 3), dtype=torch.int64, device=dev)
+        self.finals = torch.empty((2 * ne, 2), dtype=torch.int64, device=dev)
+        self.claim0 = _f(2 * ne, dev)
+        # eq descriptor lists
+        pos = 0
+        self.rt_views = []
+        for k in self.nt:
+            self.rt_views.append(self.ch["r_t"][pos:pos + k])
+            pos += k
+        ru = self.ch["r_o_up"].view(ne, no_up)
+        rd = self.ch["r_o_down"].view(ne, no_dn)
+        self.eq_r = self.rt_views + [ru[i] for i in range(ne)] + [rd[i] for i in range(ne)]
+        self.eq_E = self.E_t + [self.E_ou[i] for i in range(ne)] + [self.E_od[i] for i in range(ne)]
+        self.fold_jobs = []
+        self.claim_jobs = []
+        for i in range(ne):
+            a, b = self.row_off[i], self.row_off[i + 1]
+            self.fold_jobs.append((self.Xg[a:b], self.E_t[i], 1 << nu, self.Au[i]))
+            self.fold_jobs.append((self.W1[i], self.E_ou[i], 1 << nu, self.Bu[i]))
+            self.fold_jobs.append((self.Hg[a:b], self.E_t[i], 1 << nd, self.Ad[i]))
+            self.fold_jobs.append((self.W2[i], self.E_od[i], 1 << nd, self.Bd[i]))
+            self.claim_jobs.append((self.Zu[a:b], self.E_t[i], self.E_ou[i], self.c0[i:i + 1]))
+            self.claim_jobs.append((self.Zd[a:b], self.E_t[i], self.E_od[i], self.c0[ne + i:ne + i + 1]))
+
+    def run(self, mark=_nomark):
+        mark("group")
+        gather_rows(self.X, self.perm, self.Xg)
+        gather_rows(self.H, self.perm, self.Hg)
+        mark("witness")
+        witness_linear_grouped(self.Xg, self.W1, self.row_off, self.s, self.Zu, self.Yu, self.Ru)
+        witness_linear_grouped(self.Hg, self.W2, self.row_off, self.s, self.Zd, self.Yd, self.Rd)
+        mark("eq")
+        eq_table_batched(self.eq_r, self.eq_E)
+        mark("fold")
+        fold_matrix_batched(self.fold_jobs)
+        mark("claim")
+        claim_eval_batched(self.claim_jobs)
+        mark("sumcheck")
+        ne = len(self.experts)
+        sumcheck_prove_multi(self.Au, self.Bu, self.r_up, rounds=self.rounds_u, finals=self.finals[:ne],
+                             claim0=self.claim0[:ne])
+        sumcheck_prove_multi(self.Ad, self.Bd, self.r_dn, rounds=self.rounds_d, finals=self.finals[ne:],
+                             claim0=self.claim0[ne:])
+        mark("end")
+
+    def results(self) -> dict:
+        ne = len(self.experts)
+        Au, Bu, Ad, Bd = (field_numpy(t) for t in (self.Au, self.Bu, self.Ad, self.Bd))
+        ru, rd, finals = field_numpy(self.rounds_u), field_numpy(self.rounds_d), field_numpy(self.finals)
+        c0, cl = field_numpy(self.c0), field_numpy(self.claim0)
+        Zu, Yu, Ru = self.Zu.cpu().numpy(), self.Yu.cpu().numpy(), self.Ru.cpu().numpy()
+        Zd, Yd, Rd = self.Zd.cpu().numpy(), self.Yd.cpu().numpy(), self.Rd.cpu().numpy()
+        out = {}
+        for i, e in enumerate(self.experts):
+            a, b = self.row_off[i], self.row_off[i + 1]
+            toks = self.perm[a:b].cpu().numpy()
+            out[e] = {"tokens": toks,
+                      "up": {"Z": Zu[a:b], "Y": Yu[a:b], "R": Ru[a:b], "x_fold": Au[i], "w_fold": Bu[i],
+                             "c0": int(c0[i]), "rounds": ru[i], "finals": finals[i:i + 1],
+                             "claim0": int(cl[i])},
+                      "down": {"Z": Zd[a:b], "Y": Yd[a:b], "R": Rd[a:b], "x_fold": Ad[i], "w_fold": Bd[i],
+                               "c0": int(c0[ne + i]), "rounds": rd[i], "finals": finals[ne + i:ne + i + 1],
+                               "claim0": int(cl[ne + i])}}
+        return out
+
+
+def make_prover(cfg, inp: dict, ch: dict, dev=None):
+    if cfg.kind == "single":
+        m = cfg.matmuls[0]
+        return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev)
+    if cfg.kind in ("rlc_out", "batched"):
+        return MultiMatmulProver(cfg, inp, ch, dev)
+    if cfg.kind == "moe":
+        return MoEBlockProver(cfg, inp, ch, dev)
+    raise ValueError(cfg.kind)
