@@ -111,20 +111,16 @@ def main():
         prover.run()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, with per-step-phase HIP events on the same stream
-    marks = []
-
-    def mark(name):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record(stream)
-        marks.append((name, ev))
-
+    # the whole step as one HIP graph; timed region = K replays on this stream
+    prover.capture()
+    for _ in range(args.warmup):
+        prover.replay()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        prover.run(mark=mark)
+        prover.replay()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -132,15 +128,22 @@ def main():
     tokens = cfg.T
     value = tokens / (ms * 1e-3)
 
-    # per-phase averages: a phase runs from its mark to the next mark of the step
+    # per-phase launch durations: each phase captured alone and replayed K times
+    # back to back between two events on the same stream
     phase_ms = {}
-    for i in range(len(marks) - 1):
-        name, ev = marks[i]
-        if name == "end":
-            continue
-        phase_ms[name] = phase_ms.get(name, 0.0) + ev.elapsed_time(marks[i + 1][1])
-    for k in phase_ms:
-        phase_ms[k] /= args.steps
+    for name, fn in prover.phases():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        phase_ms[name] = e0.elapsed_time(e1) / args.steps
     dom = max(phase_ms, key=lambda k: phase_ms[k])
     b, ops = kernel_work(cfg, dom, prover)
     t = phase_ms[dom] * 1e-3

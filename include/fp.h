@@ -30,7 +30,8 @@
  * row-major with an explicit leading dimension in elements. Calls only enqueue
  * work on `stream` and return; none synchronizes or allocates device memory.
  * Scratch space comes from a caller workspace sized by the matching
- * *_workspace() query. Arguments are validated before any launch; a failing
+ * *_workspace() query (its contents need no initialization). Calls that
+ * overlap in time must not share a workspace. Arguments are validated before any launch; a failing
  * call returns a nonzero FP_E* code, launches nothing, and sets a thread-local
  * message readable with fp_last_error(). Faults inside kernels surface at the
  * caller's next stream synchronization. The library keeps no state between
@@ -114,9 +115,10 @@ typedef struct {
   fp_elem* E;       /* device, 2^n elements */
 } fp_eq_desc;
 
-/* Several eq tables in one launch. descs is a HOST array of `count`
- * descriptors; it is copied into the workspace on `stream` (the host array may
- * be reused once the call returns). Workspace: fp_eq_table_batched_workspace. */
+/* Several eq tables in as few launches as possible. descs is a HOST array of
+ * `count` descriptors, read during the call only; they travel in the kernel
+ * arguments, so the call needs no workspace (ws may be NULL; the size query
+ * returns 0). */
 int fp_eq_table_batched(int32_t count, const fp_eq_desc* descs, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t fp_eq_table_batched_workspace(int32_t count);
 
@@ -140,8 +142,8 @@ typedef struct {
   fp_elem* out;     /* device, cols_pad */
 } fp_fold_desc;
 
-/* Several folds of one dtype in one pair of launches (descs: HOST array,
- * copied into the workspace on `stream`). */
+/* Several folds of one dtype (descs: HOST array read during the call; the
+ * descriptors travel in kernel arguments, a dozen per launch). */
 int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* descs, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* descs);
@@ -168,7 +170,7 @@ typedef struct {
 /* Several matmul claims from precomputed eq tables in one pair of launches:
  * out_j = sum_t sum_c E_rows_j[t] E_cols_j[c] M_j[t, c], i.e. M_j~(r_cols ||
  * r_rows) when the tables are eq(r_rows, .) and eq(r_cols, .). descs is a
- * HOST array copied into the workspace on `stream`. */
+ * HOST array read during the call (descriptors travel in kernel arguments). */
 int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* descs, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* descs);

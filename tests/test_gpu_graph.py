@@ -1,0 +1,44 @@
+"""A whole layer step recorded as one HIP graph gives, on every replay, the
+same bytes as the eager step, with eager work and synchronizations between
+replays (outputs are cleared by a fill kernel before each replay)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from zero_knowledge_proof_amd.prover import make_prover
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(a, b, path=""):
+    if isinstance(a, dict):
+        assert a.keys() == b.keys(), path
+        for k in a:
+            _same(a[k], b[k], path + "/" + str(k))
+    else:
+        assert np.array_equal(np.asarray(a), np.asarray(b)), path
+
+
+@pytest.mark.parametrize("cid,shape", [(1, {}), (2, dict(T=100, d_in=1000, d_out=700)),
+                                       (3, dict(T=40, d=320, d_ff=600)),
+                                       (5, dict(T=24, d=96, d_kv=40, d_ff=300)),
+                                       (4, dict(T=200, d=96, d_ff=128, n_experts=12))])
+def test_graph_replays_match_eager(fp, cid, shape):
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch)
+    prover.run()
+    torch.cuda.synchronize()
+    want = prover.results()
+    prover.capture()
+    for rep in range(3):
+        for t in prover.output_tensors():
+            t.zero_()             # a fill kernel, outside the graph
+        torch.cuda.synchronize()
+        prover.replay()
+        torch.cuda.synchronize()
+        _same(prover.results(), want, "replay%d" % rep)
+        prover.run()              # eager work between replays
+        torch.cuda.synchronize()

@@ -112,12 +112,14 @@ def _check_full_matmul(X, W, s, got, r_t, r_o, r_rounds, x_fold=None):
     wf = O.fold_rows(W, E_o, 1 << n)
     assert np.array_equal(got["x_fold"], xf) and np.array_equal(got["w_fold"], wf)
     rounds, finals, claim0 = O.sumcheck([xf], [wf], r_rounds)
+    _sampled_witness(X, W, got, s)
+    # the claim kernel on the GPU's own Z, against the oracle's MLE of that Z
+    assert got["c0"] == O.mle_matrix(got["Z"], r_t, r_o)
     # the claim of Z equals the sum-check's initial claim (Z = X W^T)
     assert got["c0"] == claim0
     if "rounds" in got:
         assert np.array_equal(got["rounds"], rounds) and np.array_equal(np.asarray(got["finals"]).reshape(-1, 2), finals)
         assert got["claim0"] == claim0
-    _sampled_witness(X, W, got, s)
     return xf, wf
 
 

@@ -119,7 +119,8 @@ def _dev():
 
 
 class Workspace:
-    """A growable device scratch buffer (one per stream use; not thread-shared)."""
+    """A growable device scratch buffer; each entry-point family keeps its own
+    (calls on one stream run in order, so a family may reuse its buffer)."""
 
     def __init__(self):
         self.buf = None
@@ -132,7 +133,7 @@ class Workspace:
         return self.buf.data_ptr(), self.buf.numel()
 
 
-_ws = Workspace()
+_ws_fold, _ws_claim, _ws_mle, _ws_sc = Workspace(), Workspace(), Workspace(), Workspace()
 
 
 def to_field_tensor(vals, device=None) -> torch.Tensor:
@@ -216,9 +217,7 @@ def eq_table_batched(rs, Es=None):
         Es = [torch.empty(1 << r.numel(), dtype=torch.int64, device=_dev()) for r in rs]
     descs = (_EqDesc * k)(*[_EqDesc(r.data_ptr() if r.numel() else None, r.numel(), E.data_ptr())
                             for r, E in zip(rs, Es)])
-    need = lib().fp_eq_table_batched_workspace(k)
-    p, nb = _ws.get(need)
-    _check(lib().fp_eq_table_batched(k, descs, p, nb, _stream()), "fp_eq_table_batched")
+    _check(lib().fp_eq_table_batched(k, descs, None, 0, _stream()), "fp_eq_table_batched")
     return Es
 
 
@@ -237,7 +236,7 @@ def fold_matrix(M, E, cols_pad: int | None = None, rows: int | None = None, out=
     cols_pad = cols if cols_pad is None else cols_pad
     out = torch.empty(cols_pad, dtype=torch.int64, device=M.device) if out is None else out
     need = lib().fp_fold_matrix_workspace(_dt(M), rows, cols)
-    p, nb = _ws.get(need)
+    p, nb = _ws_fold.get(need)
     _check(lib().fp_fold_matrix(_dt(M), _ptr(M), _ld(M), rows, cols, _ptr(E), _ptr(out), cols_pad, p, nb,
                                 _stream()), "fp_fold_matrix")
     return out
@@ -250,7 +249,7 @@ def fold_matrix_batched(jobs):
     descs = (_FoldDesc * k)(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
                                         out.data_ptr()) for (M, E, cp, out) in jobs])
     need = lib().fp_fold_matrix_batched_workspace(dt, k, descs)
-    p, nb = _ws.get(need)
+    p, nb = _ws_fold.get(need)
     _check(lib().fp_fold_matrix_batched(dt, k, descs, p, nb, _stream()), "fp_fold_matrix_batched")
     return [j[3] for j in jobs]
 
@@ -260,7 +259,7 @@ def mle_eval(M, r_rows, r_cols, out=None):
     out = torch.empty(1, dtype=torch.int64, device=M.device) if out is None else out
     nr, nc = r_rows.numel(), r_cols.numel()
     need = lib().fp_mle_eval_workspace(_dt(M), rows, cols, nr, nc)
-    p, nb = _ws.get(need)
+    p, nb = _ws_mle.get(need)
     _check(lib().fp_mle_eval(_dt(M), _ptr(M), _ld(M), rows, cols, _ptr(r_rows) if nr else None, nr,
                              _ptr(r_cols) if nc else None, nc, _ptr(out), p, nb, _stream()), "fp_mle_eval")
     return out
@@ -277,7 +276,7 @@ def sumcheck_prove(As, Bs, r, rho=None, rounds=None, finals=None, claim0=None):
     pa = (ctypes.c_void_p * k)(*[a.data_ptr() for a in As])
     pb = (ctypes.c_void_p * k)(*[b.data_ptr() for b in Bs])
     need = lib().fp_sumcheck_workspace(k, n)
-    p, nb = _ws.get(need)
+    p, nb = _ws_sc.get(need)
     _check(lib().fp_sumcheck_prove(k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds), _ptr(finals), _ptr(claim0),
                                    p, nb, _stream()), "fp_sumcheck_prove")
     return rounds, finals, claim0
@@ -313,7 +312,7 @@ def claim_eval_batched(jobs):
     descs = (_ClaimDesc * k)(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
                                           Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in jobs])
     need = lib().fp_claim_eval_batched_workspace(dt, k, descs)
-    p, nb = _ws.get(need)
+    p, nb = _ws_claim.get(need)
     _check(lib().fp_claim_eval_batched(dt, k, descs, p, nb, _stream()), "fp_claim_eval_batched")
     return [j[3] for j in jobs]
 

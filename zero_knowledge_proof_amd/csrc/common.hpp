@@ -27,7 +27,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 
 // --- launchers implemented in the .hip files (no validation inside) -------
 int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st);
-int launch_eq_batched(int32_t count, const fp_eq_desc* descs_host, void* ws, size_t ws_bytes, hipStream_t st);
+int launch_eq_list(int32_t count, const fp_eq_desc* descs_host, hipStream_t st);
 size_t eq_batched_ws(int32_t count);
 
 }  // namespace fpi

@@ -6,8 +6,6 @@
 // round) and multiplies it by the product over the high variables, which is
 // the same for the whole block. Two multiplies per entry overall beyond the
 // doubling, instead of n in the product form.
-#include <vector>
-
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -18,6 +16,11 @@ struct EqJob {
   fp_elem* E;
   int32_t n;
   int32_t block_start;
+};
+constexpr int EQ_INLINE = 48;  // descriptors carried in one launch's arguments
+struct EqList {
+  EqJob j[EQ_INLINE];
+  int32_t count;
 };
 
 __device__ __forceinline__ void eq_block(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E,
@@ -52,20 +55,13 @@ __device__ __forceinline__ void eq_block(const fp_elem* __restrict__ r, int n, f
   if (tid < (1 << nl)) E[base + tid] = (n > 8) ? gl::mul(L[tid], hp) : L[tid];
 }
 
-__global__ __launch_bounds__(256) void eq_kernel(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E) {
-  eq_block(r, n, E, blockIdx.x);
-}
-
-__global__ __launch_bounds__(256) void eq_batched_kernel(const EqJob* __restrict__ jobs, int count) {
-  // the job whose block range holds this block (jobs sorted by block_start)
-  int lo = 0, hi = count - 1;
-  const int b = blockIdx.x;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (jobs[mid].block_start <= b) lo = mid; else hi = mid - 1;
-  }
-  const EqJob j = jobs[lo];
-  eq_block(j.r, j.n, j.E, b - j.block_start);
+__global__ __launch_bounds__(256) void eq_kernel(EqList jl) {
+  int k = 0;
+#pragma unroll 1
+  for (int q = 1; q < jl.count; ++q)
+    if (jl.j[q].block_start <= (int)blockIdx.x) k = q;
+  const EqJob& j = jl.j[k];
+  eq_block(j.r, j.n, j.E, (int)blockIdx.x - j.block_start);
 }
 
 inline int64_t eq_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8); }
@@ -74,26 +70,33 @@ inline int64_t eq_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8); }
 
 namespace fpi {
 
-int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st) {
-  hipLaunchKernelGGL(eq_kernel, dim3((unsigned)eq_blocks(n)), dim3(256), 0, st, r, (int)n, E);
-  return check_launch("eq_kernel");
-}
-
-size_t eq_batched_ws(int32_t count) { return align_up(sizeof(EqJob) * (size_t)(count > 0 ? count : 0), 256); }
-
-int launch_eq_batched(int32_t count, const fp_eq_desc* d, void* ws, size_t ws_bytes, hipStream_t st) {
-  std::vector<EqJob> jobs((size_t)count);
+int launch_eq_list(int32_t count, const fp_eq_desc* d, hipStream_t st) {
+  EqList jl{};
   int64_t blocks = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    jobs[i] = EqJob{d[i].r, d[i].E, d[i].n, (int32_t)blocks};
+  for (int32_t i = 0; i <= count; ++i) {
+    const bool flush = (i == count) || jl.count == EQ_INLINE || blocks + eq_blocks(d[i].n) > 0x7FFFFFFF;
+    if (flush && jl.count > 0) {
+      hipLaunchKernelGGL(eq_kernel, dim3((unsigned)blocks), dim3(256), 0, st, jl);
+      int rc = check_launch("eq_kernel");
+      if (rc) return rc;
+      jl = EqList{};
+      blocks = 0;
+    }
+    if (i == count) break;
+    jl.j[jl.count++] = EqJob{d[i].r, d[i].E, d[i].n, (int32_t)blocks};
     blocks += eq_blocks(d[i].n);
   }
-  if (blocks > 0x7FFFFFFF) return fail(FP_ESHAPE, "fp_eq_table_batched: too many blocks");
-  (void)ws_bytes;
-  hipError_t e = hipMemcpyAsync(ws, jobs.data(), sizeof(EqJob) * jobs.size(), hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return fail(FP_EHIP, "fp_eq_table_batched: descriptor copy: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(eq_batched_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const EqJob*)ws, (int)count);
-  return check_launch("eq_batched_kernel");
+  return FP_OK;
+}
+
+int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st) {
+  fp_eq_desc d{r, n, E};
+  return launch_eq_list(1, &d, st);
+}
+
+size_t eq_batched_ws(int32_t count) {
+  (void)count;
+  return 0;
 }
 
 }  // namespace fpi
@@ -109,16 +112,17 @@ extern "C" size_t fp_eq_table_batched_workspace(int32_t count) { return fpi::eq_
 
 extern "C" int fp_eq_table_batched(int32_t count, const fp_eq_desc* descs, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
   if (count < 0) return fpi::fail(FP_EARG, "fp_eq_table_batched: count < 0");
   if (count == 0) return fpi::ok();
-  if (!descs || !ws) return fpi::fail(FP_EARG, "fp_eq_table_batched: null pointer");
-  if (ws_bytes < fpi::eq_batched_ws(count)) return fpi::fail(FP_EWORKSPACE, "fp_eq_table_batched: workspace too small");
+  if (!descs) return fpi::fail(FP_EARG, "fp_eq_table_batched: null descs");
   for (int32_t i = 0; i < count; ++i) {
-    if (descs[i].n < 0 || descs[i].n > 24)
-      return fpi::fail(FP_ESHAPE, "fp_eq_table_batched: desc %d has n=%d outside [0, 24]", i, descs[i].n);
+    if (descs[i].n < 0 || descs[i].n > FP_MAX_N)
+      return fpi::fail(FP_ESHAPE, "fp_eq_table_batched: desc %d has n=%d outside [0, %d]", i, descs[i].n, FP_MAX_N);
     if (!descs[i].E || (descs[i].n > 0 && !descs[i].r))
       return fpi::fail(FP_EARG, "fp_eq_table_batched: desc %d has a null pointer", i);
   }
-  int rc = fpi::launch_eq_batched(count, descs, ws, ws_bytes, stream);
+  int rc = fpi::launch_eq_list(count, descs, stream);
   return rc ? rc : fpi::ok();
 }

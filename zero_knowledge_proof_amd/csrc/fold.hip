@@ -1,64 +1,58 @@
-// fold.hip - folded rows of integer matrices and MLE evaluation.
+// fold.hip - folded rows of integer matrices, and matmul claims.
 //
 // out[k] = sum_t E[t] M[t, k] ("How fast can FlashProve go", §2: the folded
 // row is the eq-weighted sum of all of a table's rows; §4 counts this as one of
 // the three passes over the weights, the one "for the matmuls' sum-checks").
 //
 // The pass is bound by HBM bandwidth only if the inner loop stays within a few
-// vector ops per byte, so no Goldilocks multiply runs per matrix entry. Instead
-// the field weight E[t] (< 2^64) is split into 8 unsigned bytes e_l[t] and the
-// entry is offset to an unsigned byte u = m + 128 (int8) or to four unsigned
-// bytes of m + 2^31 (int32). Then
+// vector ops per byte, so no Goldilocks multiply runs per matrix entry. The
+// field weight E[t] (< 2^64) is split into 8 unsigned bytes e_l[t] and each
+// entry is offset to unsigned bytes: u = m + 128 (int8) or the four bytes of
+// m + 2^31 (int32). Then
 //     sum_t E[t] m[t,k] = sum_l 2^(8l) sum_t e_l[t] u[t,k]  -  off * sum_t E[t]
 // where every inner sum is an exact integer built with v_dot4_u32_u8 over four
-// rows at a time (each product of two bytes, four per instruction). A thread
-// reads one dword (int8: 4 columns) or one dwordx4 (int32: 4 columns) per row,
-// transposes 4 rows x 4 bytes with v_perm_b32 so that each dword holds one
-// column's 4 rows, and accumulates into u32 limb sums. The field reduction
-// happens once per column per block. Rows are split over row-chunk blocks whose
-// per-column partial field values are summed by a second, small kernel (or,
-// for an MLE, weighted by the column eq table and summed per block).
-#include <vector>
-
+// rows at a time. A thread reads one dword (int8: 4 columns) or one dwordx4
+// (int32: 4 columns) per row, transposes 4 rows x 4 bytes with v_perm_b32 so
+// that each dword holds one column's 4 rows, and accumulates u32 limb sums
+// (exact: a workgroup covers at most 1024 rows). The field reduction happens
+// once per column per workgroup.
+//
+// Rows are split into chunks, one workgroup per (chunk, 256-column strip).
+// Each workgroup stores its per-column field values, and a second small kernel
+// adds the chunks per column (16 chunk lanes per column, so the adds are not
+// one long dependent chain). For a claim, each workgroup weights its columns
+// with the column eq table and stores one value; one workgroup per claim then
+// adds them. The two kernels need no atomics and no cross-XCD fences.
 #include "common.hpp"
 #include "gl.hpp"
 
 namespace {
 
-constexpr int FT = 256;        // threads per block
-constexpr int FCT = 64;        // column threads (one wave wide)
-constexpr int FRG = FT / FCT;  // row groups (waves)
-constexpr int FCOLS = FCT * 4; // columns per block
+constexpr int FT = 256;         // threads per workgroup
+constexpr int FCT = 64;         // column threads (one wave wide)
+constexpr int FRG = FT / FCT;   // row groups (waves)
+constexpr int FCOLS = FCT * 4;  // columns per workgroup
 constexpr int FMAX_CHUNK = 1024;
+constexpr int INLINE = 12;      // jobs carried in one launch's arguments
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct FoldJob {
   const void* M;
   int64_t ld;
-  fp_elem* dst;         // partials [n_chunks][cols] (or out when n_chunks == 1 and not MLE)
   const fp_elem* E;     // row weights
-  const fp_elem* Ecol;  // MLE column weights (nullptr for a plain fold)
+  const fp_elem* Ecol;  // claim: column weights; nullptr for a folded row
+  fp_elem* out;         // folded row (cols_pad) or the claim (1)
+  fp_elem* part;        // per-chunk column values [n_chunks][cols] or per-workgroup values
   int32_t rows, cols, cols_pad;
-  int32_t chunk_rows, n_chunks, n_colblk;
+  int32_t chunk_rows, n_chunks, n_strips;  // strips holding data columns
+  int32_t n_pad_strips;                    // strips wholly inside [cols, cols_pad)
   int32_t block_start;
-  int32_t direct;       // 1: single chunk, write out[] directly incl. zero tail
 };
 
 struct JobList {
-  const FoldJob* dev;  // device array (batched) or nullptr
+  FoldJob j[INLINE];
   int32_t count;
-  FoldJob one;
 };
-
-__device__ __forceinline__ FoldJob find_job(const JobList& jl, int b) {
-  if (!jl.dev) return jl.one;
-  int lo = 0, hi = jl.count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (jl.dev[mid].block_start <= b) lo = mid; else hi = mid - 1;
-  }
-  return jl.dev[lo];
-}
 
 // 4x4 byte transpose: w[c] byte i = v[i] byte c.
 __device__ __forceinline__ void transpose4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, uint32_t& w0,
@@ -90,29 +84,44 @@ __device__ __forceinline__ void acc128(uint64_t& lo, uint64_t& hi, uint32_t v, i
   lo = nlo;
 }
 
-// Row-chunk x column-block kernel. EB = element bytes (1: int8, 4: int32).
+__device__ __forceinline__ uint64_t wave_sum(uint64_t s) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s = gl::add(s, fpi::shfl_xor_u64(s, m));
+  return s;
+}
+
 template <int EB>
 __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
   constexpr int NL = (EB == 1) ? 8 : 11;  // limb accumulators per column
-  // LDS: E digits for the chunk (8 dwords per 4-row group), reused for the
-  // cross-wave reduction (3 waves x 64 threads x 4 cols x NL u32).
+  constexpr int U = (EB == 1) ? 4 : 2;    // row groups of 4 rows in flight per thread
   constexpr int DIG_WORDS = FMAX_CHUNK / 4 * 8;
   constexpr int RED_WORDS = (FRG - 1) * FCT * 4 * NL;
   constexpr int LDS_WORDS = DIG_WORDS > RED_WORDS ? DIG_WORDS : RED_WORDS;
   __shared__ __align__(16) uint32_t lds[LDS_WORDS];
-  __shared__ uint64_t esum_part[FT / 64];
+  __shared__ uint64_t wpart[FT / 64];
 
-  const FoldJob job = find_job(jl, blockIdx.x);
+  int ji = 0;
+#pragma unroll 1
+  for (int k = 1; k < jl.count; ++k)
+    if (jl.j[k].block_start <= (int)blockIdx.x) ji = k;
+  const FoldJob& job = jl.j[ji];
   const int lb = blockIdx.x - job.block_start;
-  const int chunk = lb / job.n_colblk;
-  const int colblk = lb - chunk * job.n_colblk;
   const int tid = threadIdx.x;
   const int ct = tid % FCT, rg = tid / FCT;
+
+  // strips wholly in the padding: write zeros and leave
+  if (lb >= job.n_chunks * job.n_strips) {
+    const int strip = job.n_strips + (lb - job.n_chunks * job.n_strips);
+    for (int c = strip * FCOLS + tid; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) job.out[c] = 0;
+    return;
+  }
+  const int chunk = lb / job.n_strips;
+  const int strip = lb - chunk * job.n_strips;
   const int row0 = chunk * job.chunk_rows;
   const int nrows = min(job.chunk_rows, job.rows - row0);
   const int ngroups = (nrows + 3) >> 2;
 
-  // ---- prologue: digits of E for this chunk and the chunk's sum of E ----
+  // ---- digits of E for this chunk, and the chunk's sum of E ----
   uint64_t esum = 0;
   for (int g = tid; g < ngroups; g += FT) {
     uint32_t dg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -124,18 +133,15 @@ __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
 #pragma unroll
       for (int l = 0; l < 8; ++l) dg[l] |= (uint32_t)((e >> (8 * l)) & 0xFF) << (8 * i);
     }
-#pragma unroll
-    for (int l = 0; l < 8; ++l) lds[g * 8 + l] = dg[l];
+    *(u32x4*)&lds[g * 8] = u32x4{dg[0], dg[1], dg[2], dg[3]};
+    *(u32x4*)&lds[g * 8 + 4] = u32x4{dg[4], dg[5], dg[6], dg[7]};
   }
-  // block sum of esum
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) esum = gl::add(esum, fpi::shfl_xor_u64(esum, m));
-  if ((tid & 63) == 0) esum_part[tid >> 6] = esum;
+  esum = wave_sum(esum);
+  if ((tid & 63) == 0) wpart[tid >> 6] = esum;
   __syncthreads();
 
-  // ---- main loop ----
-  const int c0 = colblk * FCOLS + 4 * ct;
-  const bool full_cols = (c0 + 4 <= job.cols);
+  // ---- main loop: 4-row groups g = rg, rg + FRG, ... ----
+  const int c0 = strip * FCOLS + 4 * ct;
   uint32_t acc[4][NL];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -143,73 +149,88 @@ __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
     for (int l = 0; l < NL; ++l) acc[c][l] = 0;
 
   if (c0 < job.cols) {
+    const bool full_cols = (c0 + 4 <= job.cols);
     if constexpr (EB == 1) {
       const int8_t* base = (const int8_t*)job.M + (int64_t)row0 * job.ld + c0;
       const bool vec = full_cols && ((job.ld & 3) == 0) && ((((uintptr_t)job.M) & 3) == 0);
-      for (int g = rg; g < ngroups; g += FRG) {
-        uint32_t v[4];
+      for (int g0 = rg; g0 < ngroups; g0 += FRG * U) {
+        uint32_t v[U][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * g + i;
-          const int8_t* p = base + (int64_t)t * job.ld;
-          if (t < nrows && vec) {
-            v[i] = __builtin_nontemporal_load((const uint32_t*)p);
-          } else if (t < nrows) {
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * (g0 + FRG * u) + i;
+            const int8_t* p = base + (int64_t)t * job.ld;
             uint32_t w = 0;
-            for (int c = 0; c < 4; ++c)
-              if (c0 + c < job.cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
-            v[i] = w;
-          } else {
-            v[i] = 0;
+            if (t < nrows) {
+              if (vec) {
+                w = __builtin_nontemporal_load((const uint32_t*)p);
+              } else {
+                for (int c = 0; c < 4; ++c)
+                  if (c0 + c < job.cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
+              }
+            }
+            v[u][i] = w;
           }
-        }
-        uint32_t w[4];
-        transpose4(v[0], v[1], v[2], v[3], w[0], w[1], w[2], w[3]);
-        const uint4 d0 = *(const uint4*)&lds[g * 8];
-        const uint4 d1 = *(const uint4*)&lds[g * 8 + 4];
-        const uint32_t dg[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t u = w[c] ^ 0x80808080u;  // m + 128 per byte
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + FRG * u;
+          if (g >= ngroups) break;
+          uint32_t w[4];
+          transpose4(v[u][0], v[u][1], v[u][2], v[u][3], w[0], w[1], w[2], w[3]);
+          const u32x4 d0 = *(const u32x4*)&lds[g * 8];
+          const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
+          const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-          for (int l = 0; l < 8; ++l) acc[c][l] = udot4(u, dg[l], acc[c][l]);
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t uu = w[c] ^ 0x80808080u;  // m + 128 per byte
+#pragma unroll
+            for (int l = 0; l < 8; ++l) acc[c][l] = udot4(uu, dg[l], acc[c][l]);
+          }
         }
       }
     } else {
       const int32_t* base = (const int32_t*)job.M + (int64_t)row0 * job.ld + c0;
       const bool vec = full_cols && ((job.ld & 3) == 0) && ((((uintptr_t)job.M) & 15) == 0);
-      for (int g = rg; g < ngroups; g += FRG) {
-        uint32_t v[4][4];  // [row][col]
+      for (int g0 = rg; g0 < ngroups; g0 += FRG * U) {
+        uint32_t v[U][4][4];  // [group][row][col]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * g + i;
-          const int32_t* p = base + (int64_t)t * job.ld;
-          if (t < nrows && vec) {
-            const u32x4 q = __builtin_nontemporal_load((const u32x4*)p);
-            v[i][0] = q[0]; v[i][1] = q[1]; v[i][2] = q[2]; v[i][3] = q[3];
-          } else {
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[i][c] = (t < nrows && c0 + c < job.cols) ? (uint32_t)p[c] : 0x80000000u;
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * (g0 + FRG * u) + i;
+            const int32_t* p = base + (int64_t)t * job.ld;
+            if (t < nrows && vec) {
+              const u32x4 q = __builtin_nontemporal_load((const u32x4*)p);
+              v[u][i][0] = q[0]; v[u][i][1] = q[1]; v[u][i][2] = q[2]; v[u][i][3] = q[3];
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) v[u][i][c] = (t < nrows && c0 + c < job.cols) ? (uint32_t)p[c] : 0u;
+            }
           }
-        }
-        const uint4 d0 = *(const uint4*)&lds[g * 8];
-        const uint4 d1 = *(const uint4*)&lds[g * 8 + 4];
-        const uint32_t dg[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t pl[4];  // byte planes of this column's 4 rows
-          transpose4(v[0][c], v[1][c], v[2][c], v[3][c], pl[0], pl[1], pl[2], pl[3]);
-          pl[3] ^= 0x80808080u;  // m + 2^31 as an unsigned 32-bit value
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + FRG * u;
+          if (g >= ngroups) break;
+          const u32x4 d0 = *(const u32x4*)&lds[g * 8];
+          const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
+          const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+          for (int c = 0; c < 4; ++c) {
+            uint32_t pl[4];  // byte planes of this column's 4 rows
+            transpose4(v[u][0][c], v[u][1][c], v[u][2][c], v[u][3][c], pl[0], pl[1], pl[2], pl[3]);
+            pl[3] ^= 0x80808080u;  // m + 2^31 as an unsigned 32-bit value
 #pragma unroll
-            for (int l = 0; l < 8; ++l) acc[c][b + l] = udot4(pl[b], dg[l], acc[c][b + l]);
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+              for (int l = 0; l < 8; ++l) acc[c][b + l] = udot4(pl[b], dg[l], acc[c][b + l]);
+          }
         }
       }
     }
   }
 
-  // ---- cross-wave reduction (exact u32 sums: chunk_rows <= 1024) ----
+  // ---- cross-wave reduction of the limb sums (exact in u32) ----
   __syncthreads();  // digits no longer needed
   if (rg > 0) {
     uint32_t* dst = &lds[((rg - 1) * FCT + ct) * 4 * NL];
@@ -219,147 +240,189 @@ __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
       for (int l = 0; l < NL; ++l) dst[c * NL + l] = acc[c][l];
   }
   __syncthreads();
-  if (rg != 0) return;
+  uint64_t vals[4] = {0, 0, 0, 0};
+  if (rg == 0) {
 #pragma unroll
-  for (int w = 0; w < FRG - 1; ++w) {
-    const uint32_t* src = &lds[(w * FCT + ct) * 4 * NL];
+    for (int w = 0; w < FRG - 1; ++w) {
+      const uint32_t* src = &lds[(w * FCT + ct) * 4 * NL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int l = 0; l < NL; ++l) acc[c][l] += src[c * NL + l];
-  }
-  uint64_t es = 0;
+        for (int l = 0; l < NL; ++l) acc[c][l] += src[c * NL + l];
+    }
+    uint64_t es = 0;
 #pragma unroll
-  for (int w = 0; w < FT / 64; ++w) es = gl::add(es, esum_part[w]);
-  // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
-  const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
-
-  uint64_t vals[4];
+    for (int w = 0; w < FT / 64; ++w) es = gl::add(es, wpart[w]);
+    // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
+    const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint64_t lo = 0, hi = 0;
+    for (int c = 0; c < 4; ++c) {
+      uint64_t lo = 0, hi = 0;
 #pragma unroll
-    for (int l = 0; l < NL; ++l) acc128(lo, hi, acc[c][l], 8 * l);
-    vals[c] = gl::sub(gl::reduce128(lo, hi), corr);
+      for (int l = 0; l < NL; ++l) acc128(lo, hi, acc[c][l], 8 * l);
+      vals[c] = gl::sub(gl::reduce128(lo, hi), corr);
+    }
   }
 
   if (job.Ecol) {
-    // MLE: weight each column by its eq value, one field sum per block.
-    uint64_t s = 0;
+    // claim: weight each column by its eq value; one value per workgroup
+    if (rg == 0) {
+      uint64_t s = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (c0 + c < job.cols) s = gl::add(s, gl::mul(vals[c], job.Ecol[c0 + c]));
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) s = gl::add(s, fpi::shfl_xor_u64(s, m));
-    if (ct == 0) job.dst[lb] = s;
+      for (int c = 0; c < 4; ++c)
+        if (c0 + c < job.cols) s = gl::add(s, gl::mul(vals[c], job.Ecol[c0 + c]));
+      s = wave_sum(s);
+      if (ct == 0) job.part[lb] = s;
+    }
     return;
   }
-  if (job.direct) {
+
+  if (job.n_chunks == 1) {
+    if (rg == 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int col = c0 + c;
-      if (col < job.cols) job.dst[col] = vals[c];
-      else if (col < job.cols_pad) job.dst[col] = 0;
+      for (int c = 0; c < 4; ++c) {
+        const int col = c0 + c;
+        if (col < job.cols) job.out[col] = vals[c];
+        else if (col < job.cols_pad) job.out[col] = 0;
+      }
     }
-  } else {
-    fp_elem* dst = job.dst + (int64_t)chunk * job.cols;
+    return;
+  }
+  if (rg == 0) {
+    fp_elem* dst = job.part + (int64_t)chunk * job.cols;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if (c0 + c < job.cols) dst[c0 + c] = vals[c];
   }
 }
 
-// Sum of the row-chunk partials per column, zero tail up to cols_pad.
+// ---- cross-chunk sums ----------------------------------------------------------
+// fold: out[c] = sum_chunk part[chunk][c] for c < cols, 0 up to cols_pad.
+//   A workgroup covers 16 columns with 16 chunk lanes each.
+// claim: out[0] = sum_i part[i] over the claim's workgroup values.
 struct SumJob {
   const fp_elem* part;
   fp_elem* out;
-  int32_t cols, cols_pad, n_chunks;
+  int32_t cols, cols_pad, n_chunks;  // claim: cols = 0, n_chunks = number of values
+  int32_t claim;
   int32_t block_start;
 };
 struct SumList {
-  const SumJob* dev;
+  SumJob j[INLINE];
   int32_t count;
-  SumJob one;
 };
 
 __global__ __launch_bounds__(256) void fold_sum_kernel(SumList sl) {
-  SumJob j;
-  if (!sl.dev) {
-    j = sl.one;
-  } else {
-    int lo = 0, hi = sl.count - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sl.dev[mid].block_start <= (int)blockIdx.x) lo = mid; else hi = mid - 1;
+  __shared__ uint64_t red[256];
+  int ji = 0;
+#pragma unroll 1
+  for (int k = 1; k < sl.count; ++k)
+    if (sl.j[k].block_start <= (int)blockIdx.x) ji = k;
+  const SumJob& j = sl.j[ji];
+  const int lb = blockIdx.x - j.block_start;
+  const int tid = threadIdx.x;
+  uint64_t s = 0;
+  if (j.claim) {
+    for (int i = tid; i < j.n_chunks; i += 256) s = gl::add(s, j.part[i]);
+    red[tid] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] = gl::add(red[tid], red[tid + w]);
+      __syncthreads();
     }
-    j = sl.dev[lo];
+    if (tid == 0) j.out[0] = red[0];
+    return;
   }
-  const int col = (blockIdx.x - j.block_start) * 256 + threadIdx.x;
-  if (col >= j.cols_pad) return;
-  uint64_t s = 0;
-  if (col < j.cols)
-    for (int c = 0; c < j.n_chunks; ++c) s = gl::add(s, j.part[(int64_t)c * j.cols + col]);
-  j.out[col] = s;
-}
-
-// Final sum of per-block MLE partials (one block).
-__global__ __launch_bounds__(1024) void sum_partials_kernel(const fp_elem* __restrict__ part, int n,
-                                                            fp_elem* __restrict__ out) {
-  __shared__ uint64_t wsum[16];
-  uint64_t s = 0;
-  for (int i = threadIdx.x; i < n; i += 1024) s = gl::add(s, part[i]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s = gl::add(s, fpi::shfl_xor_u64(s, m));
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  const int cl = tid & 15, lane_ch = tid >> 4;
+  const int col = lb * 16 + cl;
+  if (col < j.cols) {
+    for (int ch = lane_ch; ch < j.n_chunks; ch += 16) s = gl::add(s, j.part[(int64_t)ch * j.cols + col]);
+  }
+  red[tid] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t t = 0;
-    for (int w = 0; w < 16; ++w) t = gl::add(t, wsum[w]);
-    out[0] = t;
+  for (int w = 128; w >= 16; w >>= 1) {
+    if (tid < w) red[tid] = gl::add(red[tid], red[tid + w]);
+    __syncthreads();
   }
+  if (tid < 16 && col < j.cols_pad) j.out[col] = red[tid];
 }
 
 // ---- planning ------------------------------------------------------------
 struct Plan {
-  int32_t chunk_rows, n_chunks, n_colblk;
+  int32_t chunk_rows, n_chunks, n_strips, n_pad_strips;
+  size_t part_bytes;
+  int64_t blocks, sum_blocks;  // fold workgroups; cross-chunk sum workgroups (0: none)
 };
 
-Plan plan_fold(int32_t rows, int32_t cols, bool mle) {
-  Plan p;
-  p.n_colblk = (cols + FCOLS - 1) / FCOLS;
+Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, bool claim) {
+  Plan p{};
+  p.n_strips = (cols + FCOLS - 1) / FCOLS;
+  const int pad_total = (cols_pad + FCOLS - 1) / FCOLS;
+  p.n_pad_strips = claim ? 0 : (pad_total - p.n_strips);
   const int target_blocks = 2048;
-  int want_chunks = (target_blocks + p.n_colblk - 1) / p.n_colblk;
+  const int want_chunks = (target_blocks + p.n_strips - 1) / p.n_strips;
   int cr = (rows + want_chunks - 1) / want_chunks;
   cr = (cr + 15) / 16 * 16;
-  const int min_cr = mle ? 32 : 256;
+  const int min_cr = claim ? 32 : 256;
   if (cr < min_cr) cr = min_cr;
   if (cr > FMAX_CHUNK) cr = FMAX_CHUNK;
   if (cr >= rows) cr = (rows + 3) / 4 * 4;
   if (cr < 4) cr = 4;
   p.chunk_rows = cr;
   p.n_chunks = (rows + cr - 1) / cr;
-  if (p.n_chunks < 1) p.n_chunks = 1;
+  if (claim) {
+    p.part_bytes = fpi::align_up((size_t)p.n_chunks * p.n_strips * 8, 256);
+    p.sum_blocks = 1;
+  } else if (p.n_chunks > 1) {
+    p.part_bytes = fpi::align_up((size_t)p.n_chunks * (size_t)cols * 8, 256);
+    p.sum_blocks = (cols_pad + 15) / 16;
+  }
+  // a single chunk writes the folded row (and its zero tail) directly
+  p.blocks = (int64_t)p.n_chunks * p.n_strips + (p.n_chunks == 1 ? p.n_pad_strips : 0);
+  if (p.n_chunks > 1) p.n_pad_strips = 0;  // the sum kernel writes the tail
   return p;
 }
 
-size_t fold_ws_one(int32_t rows, int32_t cols) {
-  if (rows <= 0) return 0;
-  const Plan p = plan_fold(rows, cols, false);
-  return p.n_chunks > 1 ? fpi::align_up((size_t)p.n_chunks * (size_t)cols * 8, 256) : 0;
+// Workspace: the partials of every job, back to back.
+template <typename Desc>
+size_t layout(int32_t count, const Desc* d, bool claim, int32_t (*rows)(const Desc&), int32_t (*cols)(const Desc&),
+              int32_t (*pad)(const Desc&)) {
+  size_t parts = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (rows(d[i]) <= 0 || cols(d[i]) <= 0) continue;
+    parts += plan_job(rows(d[i]), cols(d[i]), pad(d[i]), claim).part_bytes;
+  }
+  return parts;
 }
 
-int launch_fold_rows(int eb, const JobList& jl, int64_t blocks, hipStream_t st) {
+int32_t f_rows(const fp_fold_desc& d) { return d.rows; }
+int32_t f_cols(const fp_fold_desc& d) { return d.cols; }
+int32_t f_pad(const fp_fold_desc& d) { return d.cols_pad; }
+int32_t c_rows(const fp_claim_desc& d) { return d.rows; }
+int32_t c_cols(const fp_claim_desc& d) { return d.cols; }
+int32_t c_pad(const fp_claim_desc& d) { return d.cols; }
+
+int launch_list(int eb, const JobList& jl, int64_t blocks, hipStream_t st) {
   if (blocks <= 0) return FP_OK;
+  if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "fold: too many workgroups");
   if (eb == 1) hipLaunchKernelGGL(fold_rows_kernel<1>, dim3((unsigned)blocks), dim3(FT), 0, st, jl);
   else hipLaunchKernelGGL(fold_rows_kernel<4>, dim3((unsigned)blocks), dim3(FT), 0, st, jl);
   return fpi::check_launch("fold_rows_kernel");
 }
 
-int zero_fill(fp_elem* out, int32_t n, hipStream_t st) {
+// Zero-fill of an output without data (empty matrix): padding strips only.
+int zero_only(fp_elem* out, int32_t n, hipStream_t st) {
   if (n <= 0) return FP_OK;
-  SumList sl{nullptr, 1, SumJob{nullptr, out, 0, n, 0, 0}};
-  hipLaunchKernelGGL(fold_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sl);
-  return fpi::check_launch("fold_sum_kernel");
+  JobList jl{};
+  FoldJob& j = jl.j[0];
+  j.out = out;
+  j.cols = 0;
+  j.cols_pad = n;
+  j.n_chunks = 1;
+  j.n_strips = 0;
+  j.n_pad_strips = (n + FCOLS - 1) / FCOLS;
+  jl.count = 1;
+  return launch_list(1, jl, j.n_pad_strips, st);
 }
 
 int validate_fold(const char* fn, fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols,
@@ -372,50 +435,85 @@ int validate_fold(const char* fn, fp_dtype dt, const void* M, int64_t ld, int32_
   return FP_OK;
 }
 
+// Enqueue a list of fold or claim jobs, INLINE at a time: one fold launch and
+// (when needed) one cross-chunk sum launch per INLINE jobs.
+template <typename Desc, typename Fill>
+int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fill, hipStream_t st) {
+  char* parts = ws;
+  JobList jl{};
+  SumList sl{};
+  int64_t blocks = 0, sblocks = 0;
+  auto flush = [&]() -> int {
+    int rc = launch_list(eb, jl, blocks, st);
+    if (!rc && sblocks > 0) {
+      hipLaunchKernelGGL(fold_sum_kernel, dim3((unsigned)sblocks), dim3(256), 0, st, sl);
+      rc = fpi::check_launch("fold_sum_kernel");
+    }
+    jl = JobList{};
+    sl = SumList{};
+    blocks = sblocks = 0;
+    return rc;
+  };
+  for (int32_t i = 0; i < count; ++i) {
+    FoldJob j{};
+    fill(d[i], j);
+    if (j.rows <= 0 || j.cols <= 0) {
+      // empty matrix: zero output
+      int rc = claim ? zero_only(j.out, 1, st) : zero_only(j.out, j.cols_pad, st);
+      if (rc) return rc;
+      continue;
+    }
+    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, claim);
+    j.chunk_rows = p.chunk_rows;
+    j.n_chunks = p.n_chunks;
+    j.n_strips = p.n_strips;
+    j.n_pad_strips = p.n_pad_strips;
+    j.part = p.part_bytes ? (fp_elem*)parts : nullptr;
+    parts += p.part_bytes;
+    if (jl.count == INLINE || blocks + p.blocks > 0x7FFFFFFF) {
+      int rc = flush();
+      if (rc) return rc;
+    }
+    j.block_start = (int32_t)blocks;
+    jl.j[jl.count++] = j;
+    blocks += p.blocks;
+    if (p.sum_blocks) {
+      SumJob sj{};
+      sj.part = j.part;
+      sj.out = j.out;
+      sj.claim = claim ? 1 : 0;
+      sj.cols = claim ? 0 : j.cols;
+      sj.cols_pad = claim ? 1 : j.cols_pad;
+      sj.n_chunks = claim ? (int32_t)(p.n_chunks * p.n_strips) : p.n_chunks;
+      sj.block_start = (int32_t)sblocks;
+      sl.j[sl.count++] = sj;
+      sblocks += p.sum_blocks;
+    }
+  }
+  return jl.count ? flush() : FP_OK;
+}
+
+size_t fold_ws(int32_t count, const fp_fold_desc* d) { return layout(count, d, false, f_rows, f_cols, f_pad); }
+size_t claim_ws(int32_t count, const fp_claim_desc* d) { return layout(count, d, true, c_rows, c_cols, c_pad); }
+
 }  // namespace
 
 extern "C" size_t fp_fold_matrix_workspace(fp_dtype dt, int32_t rows, int32_t cols) {
   (void)dt;
-  return fold_ws_one(rows, cols);
+  fp_fold_desc d{nullptr, cols, rows, cols, cols, nullptr, nullptr};
+  return fold_ws(1, &d);
 }
 
 extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* E,
                               fp_elem* out, int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = validate_fold("fp_fold_matrix", dt, M, ld, rows, cols, E, out, cols_pad);
-  if (rc) return rc;
-  if (rows == 0 || cols == 0) {
-    rc = zero_fill(out, cols_pad, stream);
-    return rc ? rc : fpi::ok();
-  }
-  const size_t need = fold_ws_one(rows, cols);
-  if (ws_bytes < need || (need && !ws)) return fpi::fail(FP_EWORKSPACE, "fp_fold_matrix: workspace %zu < %zu", ws_bytes, need);
-  const Plan p = plan_fold(rows, cols, false);
-  FoldJob j{};
-  j.M = M; j.ld = ld; j.E = E; j.Ecol = nullptr;
-  j.rows = rows; j.cols = cols; j.cols_pad = cols_pad;
-  j.chunk_rows = p.chunk_rows; j.n_chunks = p.n_chunks; j.block_start = 0;
-  if (p.n_chunks == 1) {
-    j.direct = 1; j.dst = out;
-    j.n_colblk = (cols_pad + FCOLS - 1) / FCOLS;
-    rc = launch_fold_rows(dt == FP_I8 ? 1 : 4, JobList{nullptr, 1, j}, j.n_colblk, stream);
-    return rc ? rc : fpi::ok();
-  }
-  j.direct = 0; j.dst = (fp_elem*)ws; j.n_colblk = p.n_colblk;
-  rc = launch_fold_rows(dt == FP_I8 ? 1 : 4, JobList{nullptr, 1, j}, (int64_t)p.n_chunks * p.n_colblk, stream);
-  if (rc) return rc;
-  SumList sl{nullptr, 1, SumJob{(const fp_elem*)ws, out, cols, cols_pad, p.n_chunks, 0}};
-  hipLaunchKernelGGL(fold_sum_kernel, dim3((unsigned)((cols_pad + 255) / 256)), dim3(256), 0, stream, sl);
-  rc = fpi::check_launch("fold_sum_kernel");
-  return rc ? rc : fpi::ok();
+  fp_fold_desc d{M, ld, rows, cols, cols_pad, E, out};
+  return fp_fold_matrix_batched(dt, 1, &d, ws, ws_bytes, stream);
 }
 
-// ---- batched folds ---------------------------------------------------------
-// Workspace layout: [FoldJob x count][SumJob x count][partials...]
 extern "C" size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* d) {
   (void)dt;
-  size_t s = fpi::align_up(sizeof(FoldJob) * (size_t)count, 256) + fpi::align_up(sizeof(SumJob) * (size_t)count, 256);
-  for (int32_t i = 0; i < count; ++i) s += fold_ws_one(d[i].rows, d[i].cols);
-  return s;
+  if (count <= 0 || !d) return 0;
+  return fold_ws(count, d);
 }
 
 extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* d, void* ws, size_t ws_bytes,
@@ -424,71 +522,57 @@ extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_
   if (count == 0) return fpi::ok();
   if (!d) return fpi::fail(FP_EARG, "fp_fold_matrix_batched: null descs");
   for (int32_t i = 0; i < count; ++i) {
-    int rc = validate_fold("fp_fold_matrix_batched", dt, d[i].M, d[i].ld, d[i].rows, d[i].cols, d[i].E, d[i].out,
+    int rc = validate_fold("fp_fold_matrix", dt, d[i].M, d[i].ld, d[i].rows, d[i].cols, d[i].E, d[i].out,
                            d[i].cols_pad);
     if (rc) return rc;
   }
-  const size_t need = fp_fold_matrix_batched_workspace(dt, count, d);
-  if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "fp_fold_matrix_batched: workspace %zu < %zu", ws_bytes, need);
-  char* w = (char*)ws;
-  FoldJob* djobs = (FoldJob*)w;
-  w += fpi::align_up(sizeof(FoldJob) * (size_t)count, 256);
-  SumJob* dsums = (SumJob*)w;
-  w += fpi::align_up(sizeof(SumJob) * (size_t)count, 256);
-  std::vector<FoldJob> jobs;
-  std::vector<SumJob> sums;
-  int64_t blocks = 0, sblocks = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    if (d[i].rows == 0 || d[i].cols == 0) {
-      if (d[i].cols_pad > 0) {
-        sums.push_back(SumJob{nullptr, d[i].out, 0, d[i].cols_pad, 0, (int32_t)sblocks});
-        sblocks += (d[i].cols_pad + 255) / 256;
-      }
-      continue;
-    }
-    const Plan p = plan_fold(d[i].rows, d[i].cols, false);
-    FoldJob j{};
-    j.M = d[i].M; j.ld = d[i].ld; j.E = d[i].E; j.Ecol = nullptr;
-    j.rows = d[i].rows; j.cols = d[i].cols; j.cols_pad = d[i].cols_pad;
-    j.chunk_rows = p.chunk_rows; j.n_chunks = p.n_chunks; j.block_start = (int32_t)blocks;
-    if (p.n_chunks == 1) {
-      j.direct = 1; j.dst = d[i].out; j.n_colblk = (d[i].cols_pad + FCOLS - 1) / FCOLS;
-    } else {
-      j.direct = 0; j.dst = (fp_elem*)w; j.n_colblk = p.n_colblk;
-      sums.push_back(SumJob{(const fp_elem*)w, d[i].out, d[i].cols, d[i].cols_pad, p.n_chunks, (int32_t)sblocks});
-      sblocks += (d[i].cols_pad + 255) / 256;
-      w += fold_ws_one(d[i].rows, d[i].cols);
-    }
-    blocks += (int64_t)j.n_chunks * j.n_colblk;
-    jobs.push_back(j);
-  }
-  if (blocks > 0x7FFFFFFF || sblocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "fp_fold_matrix_batched: too many blocks");
-  hipError_t e;
-  if (!jobs.empty()) {
-    e = hipMemcpyAsync(djobs, jobs.data(), sizeof(FoldJob) * jobs.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fpi::fail(FP_EHIP, "fp_fold_matrix_batched: copy: %s", hipGetErrorString(e));
-    int rc = launch_fold_rows(dt == FP_I8 ? 1 : 4, JobList{djobs, (int32_t)jobs.size(), FoldJob{}}, blocks, stream);
-    if (rc) return rc;
-  }
-  if (!sums.empty()) {
-    e = hipMemcpyAsync(dsums, sums.data(), sizeof(SumJob) * sums.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fpi::fail(FP_EHIP, "fp_fold_matrix_batched: copy: %s", hipGetErrorString(e));
-    hipLaunchKernelGGL(fold_sum_kernel, dim3((unsigned)sblocks), dim3(256), 0, stream,
-                       SumList{dsums, (int32_t)sums.size(), SumJob{}});
-    int rc = fpi::check_launch("fold_sum_kernel");
-    if (rc) return rc;
-  }
-  return fpi::ok();
+  const size_t need = layout(count, d, false, f_rows, f_cols, f_pad);
+  if (need && (!ws || ws_bytes < need))
+    return fpi::fail(FP_EWORKSPACE, "fp_fold_matrix: workspace %zu < %zu", ws_bytes, need);
+  auto fill = [](const fp_fold_desc& s, FoldJob& j) {
+    j.M = s.M; j.ld = s.ld; j.E = s.E; j.Ecol = nullptr; j.out = s.out;
+    j.rows = s.rows; j.cols = s.cols; j.cols_pad = s.cols_pad;
+  };
+  int rc = run_jobs(dt == FP_I8 ? 1 : 4, count, d, false, (char*)ws, fill, stream);
+  return rc ? rc : fpi::ok();
 }
 
-// ---- MLE -------------------------------------------------------------------
-// Workspace: [E_rows: 2^n_rows][E_cols: 2^n_cols][block partials]
-extern "C" size_t fp_mle_eval_workspace(fp_dtype dt, int32_t rows, int32_t cols, int32_t n_rows, int32_t n_cols) {
+extern "C" size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* d) {
   (void)dt;
-  if (n_rows < 0 || n_cols < 0 || n_rows > FP_MAX_N || n_cols > FP_MAX_N) return 0;
-  const Plan p = plan_fold(rows > 0 ? rows : 1, cols > 0 ? cols : 1, true);
-  return fpi::align_up(((size_t)8) << n_rows, 256) + fpi::align_up(((size_t)8) << n_cols, 256) +
-         fpi::align_up((size_t)p.n_chunks * p.n_colblk * 8, 256);
+  if (count <= 0 || !d) return 0;
+  return claim_ws(count, d);
+}
+
+extern "C" int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* d, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (dt != FP_I8 && dt != FP_I32) return fpi::fail(FP_EARG, "fp_claim_eval_batched: unknown dtype %d", (int)dt);
+  if (count < 0) return fpi::fail(FP_EARG, "fp_claim_eval_batched: count < 0");
+  if (count == 0) return fpi::ok();
+  if (!d) return fpi::fail(FP_EARG, "fp_claim_eval_batched: null descs");
+  for (int32_t i = 0; i < count; ++i) {
+    if (d[i].rows < 0 || d[i].cols < 0 || d[i].ld < d[i].cols)
+      return fpi::fail(FP_ESHAPE, "fp_claim_eval_batched: desc %d has bad sizes", i);
+    if (!d[i].out || (d[i].rows > 0 && d[i].cols > 0 && (!d[i].M || !d[i].E_rows || !d[i].E_cols)))
+      return fpi::fail(FP_EARG, "fp_claim_eval_batched: desc %d has a null pointer", i);
+  }
+  const size_t need = layout(count, d, true, c_rows, c_cols, c_pad);
+  if (need && (!ws || ws_bytes < need))
+    return fpi::fail(FP_EWORKSPACE, "fp_claim_eval_batched: workspace %zu < %zu", ws_bytes, need);
+  auto fill = [](const fp_claim_desc& s, FoldJob& j) {
+    j.M = s.M; j.ld = s.ld; j.E = s.E_rows; j.Ecol = s.E_cols; j.out = s.out;
+    j.rows = s.rows; j.cols = s.cols; j.cols_pad = s.cols;
+  };
+  int rc = run_jobs(dt == FP_I8 ? 1 : 4, count, d, true, (char*)ws, fill, stream);
+  return rc ? rc : fpi::ok();
+}
+
+// ---- MLE at a point ------------------------------------------------------
+// Workspace: [claim workspace][E_rows: 2^n_rows][E_cols: 2^n_cols]
+extern "C" size_t fp_mle_eval_workspace(fp_dtype dt, int32_t rows, int32_t cols, int32_t n_rows, int32_t n_cols) {
+  if (n_rows < 0 || n_cols < 0 || n_rows > 24 || n_cols > 24) return 0;
+  fp_claim_desc d{nullptr, cols, rows, cols, nullptr, nullptr, nullptr};
+  return fpi::align_up(fp_claim_eval_batched_workspace(dt, 1, &d), 256) + fpi::align_up(((size_t)8) << n_rows, 256) +
+         fpi::align_up(((size_t)8) << n_cols, 256);
 }
 
 extern "C" int fp_mle_eval(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* r_rows,
@@ -504,128 +588,16 @@ extern "C" int fp_mle_eval(fp_dtype dt, const void* M, int64_t ld, int32_t rows,
     return fpi::fail(FP_EARG, "fp_mle_eval: null pointer");
   const size_t need = fp_mle_eval_workspace(dt, rows, cols, n_rows, n_cols);
   if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "fp_mle_eval: workspace %zu < %zu", ws_bytes, need);
-  if (rows == 0 || cols == 0) {
-    int rc = zero_fill(out, 1, stream);
-    return rc ? rc : fpi::ok();
-  }
-  char* w = (char*)ws;
+  fp_claim_desc d0{nullptr, cols, rows, cols, nullptr, nullptr, nullptr};
+  const size_t cw = fpi::align_up(fp_claim_eval_batched_workspace(dt, 1, &d0), 256);
+  char* w = (char*)ws + cw;
   fp_elem* Er = (fp_elem*)w;
   w += fpi::align_up(((size_t)8) << n_rows, 256);
   fp_elem* Ec = (fp_elem*)w;
-  w += fpi::align_up(((size_t)8) << n_cols, 256);
-  fp_elem* part = (fp_elem*)w;
   int rc = fpi::launch_eq(r_rows, n_rows, Er, stream);
   if (rc) return rc;
   rc = fpi::launch_eq(r_cols, n_cols, Ec, stream);
   if (rc) return rc;
-  const Plan p = plan_fold(rows, cols, true);
-  FoldJob j{};
-  j.M = M; j.ld = ld; j.E = Er; j.Ecol = Ec; j.dst = part;
-  j.rows = rows; j.cols = cols; j.cols_pad = cols;
-  j.chunk_rows = p.chunk_rows; j.n_chunks = p.n_chunks; j.n_colblk = p.n_colblk; j.block_start = 0; j.direct = 0;
-  const int64_t blocks = (int64_t)p.n_chunks * p.n_colblk;
-  rc = launch_fold_rows(dt == FP_I8 ? 1 : 4, JobList{nullptr, 1, j}, blocks, stream);
-  if (rc) return rc;
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(1024), 0, stream, (const fp_elem*)part, (int)blocks, out);
-  rc = fpi::check_launch("sum_partials_kernel");
-  return rc ? rc : fpi::ok();
-}
-
-// ---- batched claims from eq tables -------------------------------------------
-// out_j = sum_t sum_c E_rows_j[t] E_cols_j[c] M_j[t, c]: the fold kernel in MLE
-// mode gives one partial per workgroup; one workgroup per claim sums them.
-namespace {
-struct ClaimSum {
-  const fp_elem* part;
-  fp_elem* out;
-  int32_t n;
-};
-
-__global__ __launch_bounds__(1024) void claim_sum_kernel(const ClaimSum* __restrict__ jobs) {
-  const ClaimSum j = jobs[blockIdx.x];
-  __shared__ uint64_t wsum[16];
-  uint64_t s = 0;
-  for (int i = threadIdx.x; i < j.n; i += 1024) s = gl::add(s, j.part[i]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s = gl::add(s, fpi::shfl_xor_u64(s, m));
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t t = 0;
-    for (int w = 0; w < 16; ++w) t = gl::add(t, wsum[w]);
-    j.out[0] = t;
-  }
-}
-
-size_t claim_ws(int32_t count, const fp_claim_desc* d) {
-  size_t s = fpi::align_up(sizeof(FoldJob) * (size_t)count, 256) + fpi::align_up(sizeof(ClaimSum) * (size_t)count, 256);
-  size_t parts = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    if (d[i].rows <= 0 || d[i].cols <= 0) continue;
-    const Plan p = plan_fold(d[i].rows, d[i].cols, true);
-    parts += (size_t)p.n_chunks * p.n_colblk;
-  }
-  return s + fpi::align_up(parts * 8, 256);
-}
-}  // namespace
-
-extern "C" size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* descs) {
-  (void)dt;
-  if (count <= 0 || !descs) return 0;
-  return claim_ws(count, descs);
-}
-
-extern "C" int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* d, void* ws, size_t ws_bytes,
-                                     hipStream_t stream) {
-  if (dt != FP_I8 && dt != FP_I32) return fpi::fail(FP_EARG, "fp_claim_eval_batched: unknown dtype %d", (int)dt);
-  if (count < 0) return fpi::fail(FP_EARG, "fp_claim_eval_batched: count < 0");
-  if (count == 0) return fpi::ok();
-  if (!d) return fpi::fail(FP_EARG, "fp_claim_eval_batched: null descs");
-  for (int32_t i = 0; i < count; ++i) {
-    if (d[i].rows < 0 || d[i].cols < 0 || d[i].ld < d[i].cols)
-      return fpi::fail(FP_ESHAPE, "fp_claim_eval_batched: desc %d has bad sizes", i);
-    if (!d[i].out || (d[i].rows > 0 && d[i].cols > 0 && (!d[i].M || !d[i].E_rows || !d[i].E_cols)))
-      return fpi::fail(FP_EARG, "fp_claim_eval_batched: desc %d has a null pointer", i);
-  }
-  const size_t need = claim_ws(count, d);
-  if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "fp_claim_eval_batched: workspace %zu < %zu", ws_bytes, need);
-  char* w = (char*)ws;
-  FoldJob* djobs = (FoldJob*)w;
-  w += fpi::align_up(sizeof(FoldJob) * (size_t)count, 256);
-  ClaimSum* dsums = (ClaimSum*)w;
-  w += fpi::align_up(sizeof(ClaimSum) * (size_t)count, 256);
-  fp_elem* part = (fp_elem*)w;
-  std::vector<FoldJob> jobs;
-  std::vector<ClaimSum> sums;
-  int64_t blocks = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    if (d[i].rows == 0 || d[i].cols == 0) {
-      sums.push_back(ClaimSum{part, d[i].out, 0});
-      continue;
-    }
-    const Plan p = plan_fold(d[i].rows, d[i].cols, true);
-    FoldJob j{};
-    j.M = d[i].M; j.ld = d[i].ld; j.E = d[i].E_rows; j.Ecol = d[i].E_cols;
-    j.dst = part + blocks;
-    j.rows = d[i].rows; j.cols = d[i].cols; j.cols_pad = d[i].cols;
-    j.chunk_rows = p.chunk_rows; j.n_chunks = p.n_chunks; j.n_colblk = p.n_colblk;
-    j.block_start = (int32_t)blocks; j.direct = 0;
-    const int64_t nb = (int64_t)p.n_chunks * p.n_colblk;
-    sums.push_back(ClaimSum{part + blocks, d[i].out, (int32_t)nb});
-    blocks += nb;
-    jobs.push_back(j);
-  }
-  if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "fp_claim_eval_batched: too many blocks");
-  hipError_t e;
-  if (!jobs.empty()) {
-    e = hipMemcpyAsync(djobs, jobs.data(), sizeof(FoldJob) * jobs.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fpi::fail(FP_EHIP, "fp_claim_eval_batched: copy: %s", hipGetErrorString(e));
-    int rc = launch_fold_rows(dt == FP_I8 ? 1 : 4, JobList{djobs, (int32_t)jobs.size(), FoldJob{}}, blocks, stream);
-    if (rc) return rc;
-  }
-  e = hipMemcpyAsync(dsums, sums.data(), sizeof(ClaimSum) * sums.size(), hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return fpi::fail(FP_EHIP, "fp_claim_eval_batched: copy: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(claim_sum_kernel, dim3((unsigned)sums.size()), dim3(1024), 0, stream, (const ClaimSum*)dsums);
-  int rc = fpi::check_launch("claim_sum_kernel");
-  return rc ? rc : fpi::ok();
+  fp_claim_desc d{M, ld, rows, cols, Er, Ec, out};
+  return fp_claim_eval_batched(dt, 1, &d, ws, cw, stream);
 }

@@ -25,8 +25,6 @@ namespace {
 
 constexpr int SC_SLICE = 2048;      // table entries per workgroup in a wide round
 constexpr int SC_RT = 256;          // threads of a wide-round workgroup
-constexpr int SC_TT = 1024;         // threads of the LDS tail workgroup
-constexpr int SC_TAIL_CAP = 8192;   // LDS entries per side (sum over pairs)
 constexpr int SC_MAX_PAIRS = 16;
 
 struct Tabs {
@@ -151,13 +149,23 @@ __global__ __launch_bounds__(SC_RT) void sc_round_kernel(RoundArgs a) {
   }
 }
 
-// ---- LDS tail --------------------------------------------------------------
-// One workgroup finishes rounds i0..n-1 of one instance in LDS.
-//   i0 == 0: load T_0 (tables of m = 2^n entries) into LDS.
-//   i0 > 0 : reduce the partials of g_{i0-1}, fold T_{i0-1} with r_{i0-1}
-//            into LDS.
-// Multi-instance mode (inst_stride > 0): instance b uses A + b*2^n, B + b*2^n,
-// r + b*n, rounds + b*3n, finals + 2b, claim0 + b.
+// ---- tail ------------------------------------------------------------------
+// One 512-thread workgroup finishes rounds i0..n-1 of one instance.
+//   i0 == 0: start from the caller's tables (2^n entries per pair).
+//   i0 > 0 : reduce the partials of g_{i0-1}, then fold T_{i0-1} with r_{i0-1}
+//            while loading.
+// Pairs are padded to a power of two VP of "virtual" pairs (zero tables,
+// weight 0) so that every thread's slice lies inside one pair. Phase 1: thread
+// t holds entries [t L, (t+1) L) of A and B in registers; as long as L >= 2
+// the pairs (2q, 2q+1) of a round are inside the slice, so binding a variable
+// moves no data and only the three round sums cross threads. Phase 2: at 512
+// entries the table passes through LDS to wave 0, which finishes alone (no
+// barriers): first with slices of L' >= 2 entries per lane, then one entry per
+// lane with partners at lane distance 1, 2, 4, ...
+// Multi-instance mode: instance b (= workgroup) uses A + b 2^n, B + b 2^n,
+// r + b n, rounds + 3 b n, finals + 2 b, claim0 + b.
+constexpr int ST = 512;     // tail threads
+constexpr int SLMAX = 16;   // register entries per thread and table
 struct TailArgs {
   Tabs user;
   const fp_elem* src;  // ws buffer with T_{i0-1} when i0 >= 2
@@ -168,110 +176,191 @@ struct TailArgs {
   fp_elem* finals;
   fp_elem* claim0;
   int32_t i0, n, n_pairs, nprev;
-  int32_t multi;  // 1: one instance per workgroup, single pair each
+  int32_t multi;
 };
 
-__global__ __launch_bounds__(SC_TT) void sc_tail_kernel(TailArgs a) {
-  __shared__ uint64_t tA[SC_TAIL_CAP];
-  __shared__ uint64_t tB[SC_TAIL_CAP];
-  __shared__ uint64_t red[3 * (SC_TT / 64)];
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void wave_sum3(uint64_t& a, uint64_t& b, uint64_t& c) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    a = gl::add(a, fpi::shfl_xor_u64(a, m));
+    b = gl::add(b, fpi::shfl_xor_u64(b, m));
+    c = gl::add(c, fpi::shfl_xor_u64(c, m));
+  }
+}
+
+__global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
+  __shared__ uint64_t lA[ST], lB[ST];
+  __shared__ uint64_t red[3 * (ST / 64)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int np = a.n_pairs;
   const fp_elem* r = a.r;
   fp_elem* rounds = a.rounds;
   fp_elem* finals = a.finals;
   fp_elem* claim0 = a.claim0;
-  const fp_elem* uA0 = a.user.A[0];
-  const fp_elem* uB0 = a.user.B[0];
+  const fp_elem* uA[SC_MAX_PAIRS];
+  const fp_elem* uB[SC_MAX_PAIRS];
   if (a.multi) {
     const int64_t b = blockIdx.x;
-    uA0 += b << a.n;
-    uB0 += b << a.n;
+    uA[0] = a.user.A[0] + (b << a.n);
+    uB[0] = a.user.B[0] + (b << a.n);
     r += b * a.n;
     rounds += b * 3 * a.n;
     finals += 2 * b;
     if (claim0) claim0 += b;
-  }
-  int m = 1 << (a.n - a.i0);  // per-pair table size held in LDS
-  if (a.i0 == 0) {
-    for (int j = 0; j < np; ++j) {
-      const fp_elem* A = a.multi ? uA0 : a.user.A[j];
-      const fp_elem* B = a.multi ? uB0 : a.user.B[j];
-      for (int q = tid; q < m; q += SC_TT) {
-        tA[j * m + q] = A[q];
-        tB[j * m + q] = B[q];
-      }
-    }
   } else {
-    if (tid == 0) finish_prev(a.prev_part, a.nprev, rounds, a.i0 - 1, claim0);
-    const uint64_t rr = r[a.i0 - 1];
-    const int mp = 2 * m;
     for (int j = 0; j < np; ++j) {
-      const fp_elem* A = (a.i0 == 1) ? a.user.A[j] : a.src + (int64_t)j * mp;
-      const fp_elem* B = (a.i0 == 1) ? a.user.B[j] : a.src + (int64_t)(np + j) * mp;
-      for (int q = tid; q < m; q += SC_TT) {
-        const uint64_t x0 = A[2 * q], x1 = A[2 * q + 1];
-        const uint64_t y0 = B[2 * q], y1 = B[2 * q + 1];
-        tA[j * m + q] = gl::add(x0, gl::mul(rr, gl::sub(x1, x0)));
-        tB[j * m + q] = gl::add(y0, gl::mul(rr, gl::sub(y1, y0)));
+      uA[j] = a.user.A[j];
+      uB[j] = a.user.B[j];
+    }
+  }
+  int vp = 1;
+  while (vp < np) vp <<= 1;
+  int m = 1 << (a.n - a.i0);  // per-pair entries after the entry fold
+  int i = a.i0;
+  if (i > 0 && tid == 0) finish_prev(a.prev_part, a.nprev, rounds, i - 1, claim0);
+  const uint64_t r_entry = (i > 0) ? r[i - 1] : 0;
+  const int mp = 2 * m;
+  // entry q of pair j at the start of the tail
+  auto load_entry = [&](int j, int q, uint64_t& x, uint64_t& y) {
+    if (j >= np) { x = 0; y = 0; return; }
+    if (i == 0) { x = uA[j][q]; y = uB[j][q]; return; }
+    const fp_elem* A = (a.i0 == 1) ? uA[j] : a.src + (int64_t)j * mp;
+    const fp_elem* B = (a.i0 == 1) ? uB[j] : a.src + (int64_t)(np + j) * mp;
+    const uint64_t x0 = A[2 * q], x1 = A[2 * q + 1], y0 = B[2 * q], y1 = B[2 * q + 1];
+    x = gl::add(x0, gl::mul(r_entry, gl::sub(x1, x0)));
+    y = gl::add(y0, gl::mul(r_entry, gl::sub(y1, y0)));
+  };
+  auto weight = [&](int j) -> uint64_t { return j < np ? (a.rho ? a.rho[j] : 1ull) : 0ull; };
+  const bool weighted = (a.rho != nullptr) || (vp != np);
+
+  int mt = vp * m;
+  if (mt >= 2 * ST) {
+    // ---- phase 1: register slices --------------------------------------
+    int L = mt / ST;
+    const int e0 = tid * L;
+    const int j = e0 / m;
+    const int q0 = e0 - j * m;
+    uint64_t xa[SLMAX], xb[SLMAX];
+#pragma unroll
+    for (int k = 0; k < SLMAX; ++k)
+      if (k < L) load_entry(j, q0 + k, xa[k], xb[k]);
+    const uint64_t wj = weight(j);
+    while (L >= 2) {
+      uint64_t g0 = 0, g1 = 0, g2 = 0;
+#pragma unroll
+      for (int q = 0; q < SLMAX / 2; ++q)
+        if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
+      if (weighted) { g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj); }
+      wave_sum3(g0, g1, g2);
+      if (lane == 0) { red[3 * wave] = g0; red[3 * wave + 1] = g1; red[3 * wave + 2] = g2; }
+      __syncthreads();
+      if (wave == 0) {
+        uint64_t s0 = 0, s1 = 0, s2 = 0;
+        if (lane < ST / 64) { s0 = red[3 * lane]; s1 = red[3 * lane + 1]; s2 = red[3 * lane + 2]; }
+#pragma unroll
+        for (int d = 1; d < ST / 64; d <<= 1) {
+          s0 = gl::add(s0, fpi::shfl_xor_u64(s0, d));
+          s1 = gl::add(s1, fpi::shfl_xor_u64(s1, d));
+          s2 = gl::add(s2, fpi::shfl_xor_u64(s2, d));
+        }
+        if (lane == 0) {
+          rounds[3 * i] = s0; rounds[3 * i + 1] = s1; rounds[3 * i + 2] = s2;
+          if (i == 0 && claim0) claim0[0] = gl::add(s0, s1);
+        }
       }
+      __syncthreads();  // g_i is complete before r_i is read
+      const uint64_t ri = r[i];
+#pragma unroll
+      for (int q = 0; q < SLMAX / 2; ++q)
+        if (2 * q < L) {
+          xa[q] = gl::add(xa[2 * q], gl::mul(ri, gl::sub(xa[2 * q + 1], xa[2 * q])));
+          xb[q] = gl::add(xb[2 * q], gl::mul(ri, gl::sub(xb[2 * q + 1], xb[2 * q])));
+        }
+      L >>= 1;
+      m >>= 1;
+      ++i;
+    }
+    lA[tid] = xa[0];
+    lB[tid] = xb[0];
+    mt = ST;
+  } else {
+    for (int e = tid; e < mt; e += ST) {
+      const int j = e / m;
+      load_entry(j, e - j * m, lA[e], lB[e]);
     }
   }
   __syncthreads();
+  if (wave != 0) return;
 
-  for (int i = a.i0; i < a.n; ++i) {
-    // g_i over all pairs
-    const int h = m >> 1;
-    uint64_t g0 = 0, g1 = 0, g2 = 0;
-    for (int P = tid; P < np * h; P += SC_TT) {
-      const int j = P / h;
-      const int q = P - j * h;
-      const int e = j * m + 2 * q;
-      uint64_t t0 = 0, t1 = 0, t2 = 0;
-      round_terms(tA[e], tA[e + 1], tB[e], tB[e + 1], t0, t1, t2);
-      if (a.rho) {
-        const uint64_t rj = a.rho[j];
-        t0 = gl::mul(t0, rj); t1 = gl::mul(t1, rj); t2 = gl::mul(t2, rj);
+  // ---- phase 2: wave 0 alone ------------------------------------------------
+  uint64_t xa[8], xb[8];
+  int Lw = mt >= 64 ? mt / 64 : 1;
+  {
+    const int e0 = lane * Lw;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < Lw) {
+        const bool in = e0 + k < mt;
+        xa[k] = in ? lA[e0 + k] : 0;
+        xb[k] = in ? lB[e0 + k] : 0;
       }
-      g0 = gl::add(g0, t0); g1 = gl::add(g1, t1); g2 = gl::add(g2, t2);
+  }
+  while (Lw >= 2) {
+    const int j = (lane * Lw) / m;
+    uint64_t g0 = 0, g1 = 0, g2 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (2 * q < Lw) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
+    if (weighted) {
+      const uint64_t wj = weight(j);
+      g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
     }
-    block_sum3<SC_TT>(g0, g1, g2, red);
-    if (tid == 0) {
-      rounds[3 * i] = g0;
-      rounds[3 * i + 1] = g1;
-      rounds[3 * i + 2] = g2;
+    wave_sum3(g0, g1, g2);
+    if (lane == 0) {
+      rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
       if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
     }
-    // bind variable i with r_i (read only after g_i is complete: the block
-    // reduction above ends with a barrier)
-    const uint64_t rr = r[i];
-    constexpr int PER = SC_TAIL_CAP / 2 / SC_TT;  // np * h <= SC_TAIL_CAP / 2
-    uint64_t na[PER], nb[PER];
+    const uint64_t ri = r[i];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int P = tid + k * SC_TT;
-      if (P < np * h) {
-        const int j = P / h;
-        const int e = j * m + 2 * (P - j * h);
-        na[k] = gl::add(tA[e], gl::mul(rr, gl::sub(tA[e + 1], tA[e])));
-        nb[k] = gl::add(tB[e], gl::mul(rr, gl::sub(tB[e + 1], tB[e])));
+    for (int q = 0; q < 4; ++q)
+      if (2 * q < Lw) {
+        xa[q] = gl::add(xa[2 * q], gl::mul(ri, gl::sub(xa[2 * q + 1], xa[2 * q])));
+        xb[q] = gl::add(xb[2 * q], gl::mul(ri, gl::sub(xb[2 * q + 1], xb[2 * q])));
       }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int P = tid + k * SC_TT;
-      if (P < np * h) {
-        tA[P] = na[k];  // entry q of pair j lands at j * h + q = P
-        tB[P] = nb[k];
-      }
-    }
-    __syncthreads();
-    m = h;
+    Lw >>= 1;
+    m >>= 1;
+    ++i;
   }
-  for (int j = tid; j < np; j += SC_TT) {
-    finals[2 * j] = tA[j];
-    finals[2 * j + 1] = tB[j];
+  // one entry per lane (lanes < mt / (Lw == 1 ? 1 : 1)); pair j spans lanes [j m, (j+1) m)
+  uint64_t x = xa[0], y = xb[0];
+  const int m0 = m;
+  const int jl = lane / (m0 > 0 ? m0 : 1);
+  const bool live = lane < vp * m0;
+  for (int d = 1; d < m0; d <<= 1) {
+    const uint64_t x1 = fpi::shfl_xor_u64(x, d);
+    const uint64_t y1 = fpi::shfl_xor_u64(y, d);
+    const bool even = live && ((lane & (2 * d - 1)) == 0);
+    uint64_t g0 = 0, g1 = 0, g2 = 0;
+    if (even) round_terms(x, x1, y, y1, g0, g1, g2);
+    if (weighted) {
+      const uint64_t wj = even ? weight(jl) : 0;
+      g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
+    }
+    wave_sum3(g0, g1, g2);
+    if (lane == 0) {
+      rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
+      if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
+    }
+    const uint64_t ri = r[i];
+    if (even) {
+      x = gl::add(x, gl::mul(ri, gl::sub(x1, x)));
+      y = gl::add(y, gl::mul(ri, gl::sub(y1, y)));
+    }
+    ++i;
+  }
+  if (live && (lane % m0) == 0 && jl < np) {
+    finals[2 * jl] = x;
+    finals[2 * jl + 1] = y;
   }
 }
 
@@ -282,7 +371,10 @@ struct Sched {
 
 Sched schedule(int n_pairs, int n) {
   Sched s{0, 0};
-  while (((int64_t)n_pairs << (n - s.i0)) > SC_TAIL_CAP) ++s.i0;
+  int vp = 1;
+  while (vp < n_pairs) vp <<= 1;
+  // the tail holds at most ST * SLMAX virtual entries (VP * 2^(n - i0))
+  while (((int64_t)vp << (n - s.i0)) > (int64_t)ST * SLMAX) ++s.i0;
   for (int i = 0; i < s.i0; ++i) {
     const int m = 1 << (n - i);
     const int blocks = n_pairs * ((m + SC_SLICE - 1) / SC_SLICE);
@@ -356,7 +448,7 @@ extern "C" int fp_sumcheck_prove(int32_t n_pairs, const fp_elem* const* A, const
   ta.prev_part = (s.i0 >= 1) ? part[(s.i0 - 1) & 1] : nullptr;
   ta.rounds = rounds; ta.finals = finals; ta.claim0 = claim0;
   ta.i0 = s.i0; ta.n = n; ta.n_pairs = n_pairs; ta.nprev = nprev; ta.multi = 0;
-  hipLaunchKernelGGL(sc_tail_kernel, dim3(1), dim3(SC_TT), 0, stream, ta);
+  hipLaunchKernelGGL(sc_tail_kernel, dim3(1), dim3(ST), 0, stream, ta);
   int rc = fpi::check_launch("sc_tail_kernel");
   return rc ? rc : fpi::ok();
 }
@@ -372,7 +464,7 @@ extern "C" int fp_sumcheck_prove_multi(int32_t n_inst, int32_t n, const fp_elem*
   ta.user.B[0] = B;
   ta.r = r; ta.rounds = rounds; ta.finals = finals; ta.claim0 = claim0;
   ta.i0 = 0; ta.n = n; ta.n_pairs = 1; ta.nprev = 0; ta.multi = 1;
-  hipLaunchKernelGGL(sc_tail_kernel, dim3(n_inst), dim3(SC_TT), 0, stream, ta);
+  hipLaunchKernelGGL(sc_tail_kernel, dim3(n_inst), dim3(ST), 0, stream, ta);
   int rc = fpi::check_launch("sc_tail_kernel");
   return rc ? rc : fpi::ok();
 }

@@ -11,15 +11,20 @@
 //   Y = clamp(Q, -128, 127)
 // The bit form never forms Z + 2^(s-1) or 2^s Q, so it cannot overflow int32.
 //
-// Kernel: X [M=T, K=d_in] and W [N=d_out, K] are both K-contiguous, which is
-// the operand order of v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with the
-// 16 bytes at k = 16*(l/32) of a 32-wide K slice for both operands, so the
-// products pair equal k. Workgroup tiles are BM x BN with a wave tile of
-// WM x WN (32x32 MFMA blocks), K steps of 64 bytes double-buffered through
-// LDS (rows padded to 80 bytes so the 16-byte reads of 16 consecutive rows
-// hit distinct bank groups). Workgroup ids are remapped so that each XCD
-// (workgroups are dealt round-robin to the 8 XCDs) works on a contiguous run
-// of tiles, which share W and X panels in that XCD's L2.
+// Kernel. X [T, K] and W [d_out, K] are both K-contiguous, the operand order
+// of v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with the 16 bytes at
+// k = 16*(l/32) of a 32-wide K slice, for both operands, so the products pair
+// equal k. W rows are the MFMA rows and X rows its columns: a lane's 16
+// accumulators then hold one token t and output columns o = 8g + 4h + (0..3)
+// (g = 0..3, h = l/32). Two v_permlane32_swap per 4 accumulators exchange the
+// g = 1,3 halves between lanes l and l+32, after which each lane holds 16
+// consecutive o of one t: Z leaves as four 16-byte stores and Y, R as one
+// 16-byte store each. Workgroup tiles are BO x BT (outputs x tokens), wave
+// tiles WO x WT; K steps of 64 bytes are double-buffered through LDS, rows
+// padded to 80 bytes so the 16-byte reads of 16 consecutive rows hit distinct
+// bank groups. Workgroup ids are remapped so that each XCD (ids are dealt to
+// the 8 XCDs round-robin) works on a contiguous run of tiles; tokens vary
+// fastest, so one W panel is shared by the XCD's tiles in its L2.
 #include "common.hpp"
 
 namespace {
@@ -36,18 +41,18 @@ struct WitArgs {
   int64_t ldx;
   const int8_t* W;
   int64_t ldw;
-  int32_t M, N, K, s;
+  int32_t T, N, K, s;  // tokens, outputs (d_out), reduction (d_in), shift
   int32_t* Z;
   int8_t* Y;
   int8_t* R;
-  int32_t tiles_m, tiles_n;
-  int32_t vecX, vecW;
+  int32_t tiles_t, tiles_o;
+  int32_t vecX, vecW, vecZ, vecYR;
 };
 
 struct GroupTab {
   const int8_t* W[MAXG];
-  int32_t row_off[MAXG + 1];   // output / X rows of each group
-  int32_t tile_off[MAXG + 1];  // first M tile of each group
+  int32_t row_off[MAXG + 1];   // token rows of each group
+  int32_t tile_off[MAXG + 1];  // first token tile of each group
   int32_t G;
 };
 
@@ -71,46 +76,53 @@ __device__ __forceinline__ int xcd_tile(int bid, int nb) {
   return start + li;
 }
 
-template <int BM, int BN, int WM, int WN, bool GROUPED>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
-  constexpr int WAVES_N = BN / WN;
-  constexpr int NT = (BM / WM) * WAVES_N * 64;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int NCA = BM * (BK / 16), NCB = BN * (BK / 16);  // 16-byte chunks per K step
-  constexpr int CA = (NCA + NT - 1) / NT;                      // chunks per thread
+__device__ __forceinline__ void rescale(int32_t z, int s, int32_t lowmask, uint32_t& y, uint32_t& r) {
+  const int32_t bit = (z >> (s - 1)) & 1;
+  const int32_t q = (z >> s) + bit;
+  const int32_t rr = (z & lowmask) - (bit << s);
+  const int32_t yy = q < -128 ? -128 : (q > 127 ? 127 : q);
+  y = (uint32_t)(uint8_t)(int8_t)yy;
+  r = (uint32_t)(uint8_t)(int8_t)rr;
+}
+
+template <int BO, int BT, int WO, int WT, bool GROUPED>
+__global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
+  constexpr int WAVES_T = BT / WT;
+  constexpr int NT = (BO / WO) * WAVES_T * 64;
+  constexpr int TM = WO / 32, TN = WT / 32;
+  constexpr int NCA = BO * (BK / 16), NCB = BT * (BK / 16);  // 16-byte chunks per K step
+  constexpr int CA = (NCA + NT - 1) / NT;
   constexpr int CB = (NCB + NT - 1) / NT;
-  __shared__ __align__(16) int8_t sA[2][BM * PITCH];
-  __shared__ __align__(16) int8_t sB[2][BN * PITCH];
+  __shared__ __align__(16) int8_t sA[2][BO * PITCH];  // W rows
+  __shared__ __align__(16) int8_t sB[2][BT * PITCH];  // X rows
 
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  int tm = tile % a.tiles_m;
-  const int tn = tile / a.tiles_m;
+  const int tt = tile % a.tiles_t;
+  const int to = tile / a.tiles_t;
 
-  const int8_t* Xb = a.X;
   const int8_t* Wb = a.W;
-  int row_base = 0;       // first X / output row of this tile
-  int row_lim = a.M;      // rows valid in this tile's group: [row_base, row_lim)
+  int t_base, t_lim;  // token rows [t_base, t_lim) valid for this tile's group
   if constexpr (GROUPED) {
     int lo = 0, hi = gt.G - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (gt.tile_off[mid] <= tm) lo = mid; else hi = mid - 1;
+      if (gt.tile_off[mid] <= tt) lo = mid; else hi = mid - 1;
     }
     Wb = gt.W[lo];
-    row_base = gt.row_off[lo] + (tm - gt.tile_off[lo]) * BM;
-    row_lim = gt.row_off[lo + 1];
+    t_base = gt.row_off[lo] + (tt - gt.tile_off[lo]) * BT;
+    t_lim = gt.row_off[lo + 1];
   } else {
-    row_base = tm * BM;
+    t_base = tt * BT;
+    t_lim = a.T;
   }
-  const int col_base = tn * BN;
+  const int o_base = to * BO;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm0 = (wave / WAVES_N) * WM;
-  const int wn0 = (wave % WAVES_N) * WN;
+  const int wo0 = (wave / WAVES_T) * WO;
+  const int wt0 = (wave % WAVES_T) * WT;
 
-  // global -> register staging
   const int8_t* pa[CA];
   const int8_t* pb[CB];
   int sa_off[CA], sb_off[CB], ka[CA], kb[CB];
@@ -118,8 +130,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(Wit
   for (int c = 0; c < CA; ++c) {
     const int ch = tid + c * NT;
     const int row = ch >> 2, kc = (ch & 3) * 16;
-    const int g = row_base + row;
-    pa[c] = (ch < NCA && g < row_lim) ? Xb + (int64_t)g * a.ldx : nullptr;
+    const int g = o_base + row;
+    pa[c] = (ch < NCA && g < a.N) ? Wb + (int64_t)g * a.ldw : nullptr;
     ka[c] = kc;
     sa_off[c] = (ch < NCA) ? row * PITCH + kc : -1;
   }
@@ -127,8 +139,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(Wit
   for (int c = 0; c < CB; ++c) {
     const int ch = tid + c * NT;
     const int row = ch >> 2, kc = (ch & 3) * 16;
-    const int g = col_base + row;
-    pb[c] = (ch < NCB && g < a.N) ? Wb + (int64_t)g * a.ldw : nullptr;
+    const int g = t_base + row;
+    pb[c] = (ch < NCB && g < t_lim) ? a.X + (int64_t)g * a.ldx : nullptr;
     kb[c] = kc;
     sb_off[c] = (ch < NCB) ? row * PITCH + kc : -1;
   }
@@ -138,12 +150,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(Wit
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
       v4i z = {0, 0, 0, 0};
-      ra[c] = pa[c] ? load16(pa[c], k0 + ka[c], a.K, vx) : z;
+      ra[c] = pa[c] ? load16(pa[c], k0 + ka[c], a.K, vw) : z;
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       v4i z = {0, 0, 0, 0};
-      rb[c] = pb[c] ? load16(pb[c], k0 + kb[c], a.K, vw) : z;
+      rb[c] = pb[c] ? load16(pb[c], k0 + kb[c], a.K, vx) : z;
     }
   };
   auto sstore = [&](int buf) {
@@ -175,9 +187,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(Wit
     for (int kk = 0; kk < BK / 32; ++kk) {
       v4i fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = *(const v4i*)&sA[buf][(wm0 + 32 * i + lrow) * PITCH + kk * 32 + lk];
+      for (int i = 0; i < TM; ++i) fa[i] = *(const v4i*)&sA[buf][(wo0 + 32 * i + lrow) * PITCH + kk * 32 + lk];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = *(const v4i*)&sB[buf][(wn0 + 32 * j + lrow) * PITCH + kk * 32 + lk];
+      for (int j = 0; j < TN; ++j) fb[j] = *(const v4i*)&sB[buf][(wt0 + 32 * j + lrow) * PITCH + kk * 32 + lk];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -187,43 +199,93 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void witness_kernel(Wit
     __syncthreads();
   }
 
-  // epilogue: rescale, clamp, remainder
+  // ---- epilogue: 16 consecutive outputs per lane, rescale, clamp, remainder
   const int s = a.s;
   const int32_t lowmask = (1 << s) - 1;
+  const int h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = col_base + wn0 + 32 * j + (lane & 31);
-      if (col >= a.N) continue;
+      int32_t v[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row_base + wm0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row >= row_lim) continue;
-        const int32_t z = acc[i][j][v];
-        const int32_t bit = (z >> (s - 1)) & 1;
-        const int32_t q = (z >> s) + bit;
-        const int32_t rr = (z & lowmask) - (bit << s);
-        const int32_t y = q < -128 ? -128 : (q > 127 ? 127 : q);
-        const int64_t idx = (int64_t)row * a.N + col;
-        if (a.Z) a.Z[idx] = z;
-        a.Y[idx] = (int8_t)y;
-        a.R[idx] = (int8_t)rr;
+      for (int k = 0; k < 16; ++k) v[k] = acc[i][j][k];
+      // lanes 0-31 keep o = 0..15 of the 32-block, lanes 32-63 take o = 16..31
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v[k], (unsigned)v[k + 8], false, false);
+        v[k] = (int32_t)sw[0];
+        v[k + 8] = (int32_t)sw[1];
+      }
+      // order of o offsets: regs 0-3, 8-11, 4-7, 12-15
+      int32_t z[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        z[q] = v[q];
+        z[4 + q] = v[8 + q];
+        z[8 + q] = v[4 + q];
+        z[12 + q] = v[12 + q];
+      }
+      const int t = t_base + wt0 + 32 * j + (lane & 31);
+      const int o0 = o_base + wo0 + 32 * i + 16 * h;
+      if (t >= t_lim || o0 >= a.N) continue;
+      uint32_t yw[4] = {0, 0, 0, 0}, rw[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        uint32_t y, r;
+        rescale(z[q], s, lowmask, y, r);
+        yw[q >> 2] |= y << (8 * (q & 3));
+        rw[q >> 2] |= r << (8 * (q & 3));
+      }
+      const int64_t idx = (int64_t)t * a.N + o0;
+      if (o0 + 16 <= a.N) {
+        if (a.Z) {
+          if (a.vecZ) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *(v4i*)(a.Z + idx + 4 * q) = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) a.Z[idx + q] = z[q];
+          }
+        }
+        if (a.vecYR) {
+          *(v4i*)(a.Y + idx) = v4i{(int)yw[0], (int)yw[1], (int)yw[2], (int)yw[3]};
+          *(v4i*)(a.R + idx) = v4i{(int)rw[0], (int)rw[1], (int)rw[2], (int)rw[3]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
+            a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (o0 + q < a.N) {
+            if (a.Z) a.Z[idx + q] = z[q];
+            a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
+            a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
+          }
+        }
       }
     }
   }
 }
 
-// Tile configurations: (BM, BN, WM, WN)
-#define WIT_BIG 128, 128, 64, 64
-#define WIT_SMALL 32, 128, 32, 32
+// Tile configurations (BO, BT, WO, WT): 4 waves each.
+#define WIT_L 256, 128, 128, 64
+#define WIT_M 128, 128, 64, 64
+#define WIT_S 256, 32, 64, 32
 
-template <int BM, int BN, int WM, int WN, bool GROUPED>
-int launch(const WitArgs& a, const GroupTab& gt, int64_t blocks, hipStream_t st) {
+template <int BO, int BT, int WO, int WT, bool GROUPED>
+int launch(WitArgs a, const GroupTab& gt, hipStream_t st) {
+  if (!GROUPED) a.tiles_t = (a.T + BT - 1) / BT;
+  a.tiles_o = (a.N + BO - 1) / BO;
+  const int64_t blocks = (int64_t)a.tiles_t * a.tiles_o;
   if (blocks <= 0) return FP_OK;
   if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
-  hipLaunchKernelGGL((witness_kernel<BM, BN, WM, WN, GROUPED>), dim3((unsigned)blocks),
-                     dim3((BM / WM) * (BN / WN) * 64), 0, st, a, gt);
+  hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED>), dim3((unsigned)blocks),
+                     dim3((BO / WO) * (BT / WT) * 64), 0, st, a, gt);
   return fpi::check_launch("witness_kernel");
 }
 
@@ -237,6 +299,12 @@ int validate(const char* fn, int64_t ldx, int64_t ldw, int32_t T, int32_t d_in, 
   return FP_OK;
 }
 
+void vec_flags(WitArgs& a) {
+  a.vecX = ((a.ldx & 15) == 0) && ((((uintptr_t)a.X) & 15) == 0);
+  a.vecZ = ((a.N & 3) == 0) && ((((uintptr_t)a.Z) & 15) == 0);
+  a.vecYR = ((a.N & 15) == 0) && ((((uintptr_t)a.Y) & 15) == 0) && ((((uintptr_t)a.R) & 15) == 0);
+}
+
 }  // namespace
 
 extern "C" int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T, int32_t d_in,
@@ -247,20 +315,15 @@ extern "C" int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, 
   if (d_in > 0 && (!X || !W)) return fpi::fail(FP_EARG, "fp_witness_linear: null X or W");
   WitArgs a{};
   a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
-  a.M = T; a.N = d_out; a.K = d_in; a.s = s;
+  a.T = T; a.N = d_out; a.K = d_in; a.s = s;
   a.Z = Z; a.Y = Y; a.R = R;
-  a.vecX = ((ldx & 15) == 0) && ((((uintptr_t)X) & 15) == 0);
+  vec_flags(a);
   a.vecW = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
   GroupTab gt{};
-  if (T <= 32) {
-    a.tiles_m = (T + 31) / 32;
-    a.tiles_n = (d_out + 127) / 128;
-    rc = launch<WIT_SMALL, false>(a, gt, (int64_t)a.tiles_m * a.tiles_n, stream);
-  } else {
-    a.tiles_m = (T + 127) / 128;
-    a.tiles_n = (d_out + 127) / 128;
-    rc = launch<WIT_BIG, false>(a, gt, (int64_t)a.tiles_m * a.tiles_n, stream);
-  }
+  const int64_t big = (int64_t)((d_out + 255) / 256) * ((T + 127) / 128);
+  if (T <= 32) rc = launch<WIT_S, false>(a, gt, stream);
+  else if (T >= 128 && big >= 200) rc = launch<WIT_L, false>(a, gt, stream);
+  else rc = launch<WIT_M, false>(a, gt, stream);
   return rc ? rc : fpi::ok();
 }
 
@@ -283,14 +346,13 @@ extern "C" int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int
       return fpi::fail(FP_EARG, "fp_witness_linear_grouped: null W for non-empty group %d", g);
   WitArgs a{};
   a.X = X; a.ldx = ldx; a.W = nullptr; a.ldw = ldw;
-  a.M = total; a.N = d_out; a.K = d_in; a.s = s;
+  a.T = total; a.N = d_out; a.K = d_in; a.s = s;
   a.Z = Z; a.Y = Y; a.R = R;
-  a.vecX = ((ldx & 15) == 0) && ((((uintptr_t)X) & 15) == 0);
+  vec_flags(a);
   bool vw = (ldw & 15) == 0;
   for (int g = 0; g < G; ++g) vw = vw && ((((uintptr_t)W_ptrs[g]) & 15) == 0);
   a.vecW = vw;
-  a.tiles_n = (d_out + 127) / 128;
-  constexpr int GBM = 32;
+  constexpr int GBT = 32;  // token tile of the grouped launch
   for (int g0 = 0; g0 < G; g0 += MAXG) {
     const int gc = (G - g0) < MAXG ? (G - g0) : MAXG;
     GroupTab gt{};
@@ -302,14 +364,14 @@ extern "C" int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int
       gt.row_off[ng] = row_off[g];
       gt.row_off[ng + 1] = row_off[g + 1];
       gt.tile_off[ng] = tiles;
-      tiles += (rows + GBM - 1) / GBM;
+      tiles += (rows + GBT - 1) / GBT;
       ++ng;
     }
     if (ng == 0) continue;
     gt.tile_off[ng] = tiles;
     gt.G = ng;
-    a.tiles_m = tiles;
-    rc = launch<WIT_SMALL, true>(a, gt, (int64_t)tiles * a.tiles_n, stream);
+    a.tiles_t = tiles;
+    rc = launch<WIT_S, true>(a, gt, stream);
     if (rc) return rc;
   }
   return fpi::ok();

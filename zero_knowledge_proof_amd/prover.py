@@ -43,6 +43,47 @@ def _f(n, dev):
     return torch.empty(n, dtype=torch.int64, device=dev)
 
 
+class _Prover:
+    """Common driver: ``phases()`` lists the protocol steps in order; ``run``
+    enqueues them eagerly; ``capture`` records them into one HIP graph."""
+
+    graph = None
+
+    def phases(self):
+        raise NotImplementedError
+
+    def run(self, mark=_nomark):
+        for name, fn in self.phases():
+            mark(name)
+            fn()
+        mark("end")
+
+    def capture(self):
+        """Record one whole step into a HIP graph (run once eagerly first so
+        that every workspace has its final size)."""
+        self.run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
+    # tensors the step writes (for tests that clear them between runs)
+    OUTPUTS = ()
+
+    def output_tensors(self):
+        out = []
+        for name in self.OUTPUTS:
+            v = getattr(self, name)
+            out.extend(v if isinstance(v, list) else [v])
+        return out
+
+
 class _Challenges:
     """All challenges of a workload in one device buffer, with named views."""
 
@@ -60,8 +101,10 @@ class _Challenges:
         return self.views[k]
 
 
-class SingleLayerProver:
+class SingleLayerProver(_Prover):
     """One linear map: witness, claim and sum-check over d_in."""
+
+    OUTPUTS = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0")
 
     def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None, with_z: bool = True):
         dev = dev or torch.device("cuda")
@@ -81,19 +124,17 @@ class SingleLayerProver:
         self.finals = torch.empty((1, 2), dtype=torch.int64, device=dev)
         self.claim0 = _f(1, dev)
 
-    def run(self, mark=_nomark):
-        mark("witness")
-        witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)
-        mark("eq")
-        eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o])
-        mark("fold")
-        fold_matrix_batched([(self.X, self.E_t, 1 << self.n, self.xf), (self.W, self.E_o, 1 << self.n, self.wf)])
-        mark("claim")
-        claim_eval_batched([(self.Z, self.E_t, self.E_o, self.c0)])
-        mark("sumcheck")
-        sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                       claim0=self.claim0)
-        mark("end")
+    def phases(self):
+        n = self.n
+        return [
+            ("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)),
+            ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o])),
+            ("fold", lambda: fold_matrix_batched([(self.X, self.E_t, 1 << n, self.xf),
+                                                  (self.W, self.E_o, 1 << n, self.wf)])),
+            ("claim", lambda: claim_eval_batched([(self.Z, self.E_t, self.E_o, self.c0)])),
+            ("sumcheck", lambda: sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds,
+                                                finals=self.finals, claim0=self.claim0)),
+        ]
 
     def results(self) -> dict:
         return {"Z": self.Z.cpu().numpy(), "Y": self.Y.cpu().numpy(), "R": self.R.cpu().numpy(),
@@ -103,7 +144,7 @@ class SingleLayerProver:
                 "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
 
 
-class MultiMatmulProver:
+class MultiMatmulProver(_Prover):
     """Several linear maps of one layer sharing the token axis (one r_t).
 
     mode "rlc_out": each claim gets its own sum-check; the finished claims are
@@ -111,6 +152,15 @@ class MultiMatmulProver:
     mode "batched": the claims are merged first (rho-weighted) and proved by
     one batched sum-check over tables padded to 2^batched_n (all seven maps of
     a transformer layer)."""
+
+    def output_tensors(self):
+        out = [self.E_t]
+        for d in self.mm:
+            out += [d[k] for k in ("Z", "Y", "R", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0") if k in d]
+        for k in ("rlc", "c0_batch", "rounds", "finals", "claim0"):
+            if hasattr(self, k):
+                out.append(getattr(self, k))
+        return out
 
     def __init__(self, cfg, inp: dict, ch: dict, dev=None):
         dev = dev or torch.device("cuda")
@@ -153,33 +203,43 @@ class MultiMatmulProver:
             self.finals = torch.empty((len(cfg.matmuls), 2), dtype=torch.int64, device=dev)
             self.claim0 = _f(1, dev)
 
-    def run(self, mark=_nomark):
-        mark("witness")
+    def _witness(self):
         for d in self.mm:
             m = d["m"]
             witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
-        mark("eq")
+
+    def _eq(self):
         eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
                          [self.E_t] + [d["E_o"] for d in self.mm])
-        mark("fold")
+
+    def _fold(self):
         jobs = [(M, self.E_t, cp, out) for (M, _, cp, out) in self.x_jobs]
         jobs += [(self.tens[d["m"].w], d["E_o"], 1 << d["n"], d["wf"]) for d in self.mm]
         fold_matrix_batched(jobs)
-        mark("claim")
+
+    def _claim(self):
         claim_eval_batched([(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm])
-        mark("sumcheck")
+
+    def _sumcheck(self):
         if self.mode == "rlc_out":
             for d in self.mm:
                 sumcheck_prove([d["xf"]], [d["wf"]], self.ch["rounds/" + d["m"].name], rounds=d["rounds"],
                                finals=d["finals"], claim0=d["claim0"])
-            mark("merge")
-            combine_claims([d["rounds"][-1] for d in self.mm],
-                           [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
         else:
             linear_combine([d["c0"] for d in self.mm], self.rho, out=self.c0_batch)
             sumcheck_prove([d["xf"] for d in self.mm], [d["wf"] for d in self.mm], self.ch["rounds"], rho=self.rho,
                            rounds=self.rounds, finals=self.finals, claim0=self.claim0)
-        mark("end")
+
+    def _merge(self):
+        combine_claims([d["rounds"][-1] for d in self.mm],
+                       [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
+
+    def phases(self):
+        ph = [("witness", self._witness), ("eq", self._eq), ("fold", self._fold), ("claim", self._claim),
+              ("sumcheck", self._sumcheck)]
+        if self.mode == "rlc_out":
+            ph.append(("merge", self._merge))
+        return ph
 
     def results(self) -> dict:
         out = {"E_t": field_numpy(self.E_t)}
@@ -199,11 +259,14 @@ class MultiMatmulProver:
         return out
 
 
-class MoEBlockProver:
+class MoEBlockProver(_Prover):
     """MoE block: top-1 routed tokens grouped by expert (stable, ascending
     token order), one grouped witness launch per projection, and an
     independent claim + sum-check per expert and projection. A group of T_e
     tokens is logically padded with zero rows to 2^ceil(log2 T_e)."""
+
+    OUTPUTS = ("Xg", "Hg", "Zu", "Yu", "Ru", "Zd", "Yd", "Rd", "E_t", "E_ou", "E_od", "Au", "Bu", "Ad", "Bd", "c0",
+               "rounds_u", "rounds_d", "finals", "claim0")
 
     def __init__(self, cfg, inp: dict, ch: dict, dev=None):
         dev = dev or torch.device("cuda")
@@ -274,26 +337,27 @@ class MoEBlockProver:
             self.claim_jobs.append((self.Zu[a:b], self.E_t[i], self.E_ou[i], self.c0[i:i + 1]))
             self.claim_jobs.append((self.Zd[a:b], self.E_t[i], self.E_od[i], self.c0[ne + i:ne + i + 1]))
 
-    def run(self, mark=_nomark):
-        mark("group")
+    def _group(self):
         gather_rows(self.X, self.perm, self.Xg)
         gather_rows(self.H, self.perm, self.Hg)
-        mark("witness")
+
+    def _witness(self):
         witness_linear_grouped(self.Xg, self.W1, self.row_off, self.s, self.Zu, self.Yu, self.Ru)
         witness_linear_grouped(self.Hg, self.W2, self.row_off, self.s, self.Zd, self.Yd, self.Rd)
-        mark("eq")
-        eq_table_batched(self.eq_r, self.eq_E)
-        mark("fold")
-        fold_matrix_batched(self.fold_jobs)
-        mark("claim")
-        claim_eval_batched(self.claim_jobs)
-        mark("sumcheck")
+
+    def _sumcheck(self):
         ne = len(self.experts)
         sumcheck_prove_multi(self.Au, self.Bu, self.r_up, rounds=self.rounds_u, finals=self.finals[:ne],
                              claim0=self.claim0[:ne])
         sumcheck_prove_multi(self.Ad, self.Bd, self.r_dn, rounds=self.rounds_d, finals=self.finals[ne:],
                              claim0=self.claim0[ne:])
-        mark("end")
+
+    def phases(self):
+        return [("group", self._group), ("witness", self._witness),
+                ("eq", lambda: eq_table_batched(self.eq_r, self.eq_E)),
+                ("fold", lambda: fold_matrix_batched(self.fold_jobs)),
+                ("claim", lambda: claim_eval_batched(self.claim_jobs)),
+                ("sumcheck", self._sumcheck)]
 
     def results(self) -> dict:
         ne = len(self.experts)
