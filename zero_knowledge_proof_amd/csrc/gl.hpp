@@ -37,7 +37,7 @@ __device__ __forceinline__ uint64_t reduce128(uint64_t lo, uint64_t hi) {
   uint32_t h0 = (uint32_t)hi, h1 = (uint32_t)(hi >> 32);
   uint64_t t = lo - h1;
   t -= (lo < h1) ? EPS : 0;
-  uint64_t u = (uint64_t)h0 * EPS;  // < 2^64
+  uint64_t u = ((uint64_t)h0 << 32) - h0;  // h0 * (2^32 - 1) < 2^64
   uint64_t s = t + u;
   s += (s < t) ? EPS : 0;
   return canon(s);

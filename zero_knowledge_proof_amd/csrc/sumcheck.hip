@@ -155,17 +155,22 @@ __global__ __launch_bounds__(SC_RT) void sc_round_kernel(RoundArgs a) {
 //   i0 > 0 : reduce the partials of g_{i0-1}, then fold T_{i0-1} with r_{i0-1}
 //            while loading.
 // Pairs are padded to a power of two VP of "virtual" pairs (zero tables,
-// weight 0) so that every thread's slice lies inside one pair. Phase 1: thread
-// t holds entries [t L, (t+1) L) of A and B in registers; as long as L >= 2
-// the pairs (2q, 2q+1) of a round are inside the slice, so binding a variable
-// moves no data and only the three round sums cross threads. Phase 2: at 512
-// entries the table passes through LDS to wave 0, which finishes alone (no
-// barriers): first with slices of L' >= 2 entries per lane, then one entry per
-// lane with partners at lane distance 1, 2, 4, ...
+// weight 0) so that every slice lies inside one pair.
+//   Phase 1 (tables > 512 entries): thread t holds entries [t L, (t+1) L) of A
+//     and B in registers; while L >= 2 the pairs (2q, 2q+1) of a round are in
+//     the slice, binding a variable moves no data, and only the three round
+//     sums cross threads.
+//   Phase 2 (64 < entries <= 512): the tables live in LDS; thread q handles the
+//     pair (2q, 2q+1) and writes the bound entry q back after a barrier.
+//   Phase 3 (<= 64 entries): wave 0 alone, one entry per lane, partners at lane
+//     distance 1, 2, 4, ... (no barriers).
+// Every round's sums are reduced with DPP row butterflies plus readlane of the
+// four row sums; a barrier separates a complete g_i from the read of r_i.
 // Multi-instance mode: instance b (= workgroup) uses A + b 2^n, B + b 2^n,
 // r + b n, rounds + 3 b n, finals + 2 b, claim0 + b.
 constexpr int ST = 512;     // tail threads
 constexpr int SLMAX = 16;   // register entries per thread and table
+constexpr int SW = ST / 64; // waves
 struct TailArgs {
   Tabs user;
   const fp_elem* src;  // ws buffer with T_{i0-1} when i0 >= 2
@@ -179,18 +184,55 @@ struct TailArgs {
   int32_t multi;
 };
 
-__device__ __forceinline__ void wave_sum3(uint64_t& a, uint64_t& b, uint64_t& c) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    a = gl::add(a, fpi::shfl_xor_u64(a, m));
-    b = gl::add(b, fpi::shfl_xor_u64(b, m));
-    c = gl::add(c, fpi::shfl_xor_u64(c, m));
+// Sum over the wave, returned in every lane (full wave active).
+__device__ __forceinline__ uint64_t wave_total(uint64_t v) {
+  v = gl::add(v, fpi::dpp_u64<fpi::DPP_XOR1>(v));
+  v = gl::add(v, fpi::dpp_u64<fpi::DPP_XOR2>(v));
+  v = gl::add(v, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(v));
+  v = gl::add(v, fpi::dpp_u64<fpi::DPP_MIRROR>(v));  // every lane: its row's sum
+  const uint64_t a = fpi::readlane_u64(v, 0), b = fpi::readlane_u64(v, 16);
+  const uint64_t c = fpi::readlane_u64(v, 32), d = fpi::readlane_u64(v, 48);
+  return gl::add(gl::add(a, b), gl::add(c, d));
+}
+
+// Workgroup sum of (g0, g1, g2); wave 0 lane 0 writes round i. Ends with a
+// barrier, so r_i may be read afterwards.
+__device__ __forceinline__ void block_round(uint64_t g0, uint64_t g1, uint64_t g2, uint64_t* red, fp_elem* rounds,
+                                            int i, fp_elem* claim0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  g0 = wave_total(g0);
+  g1 = wave_total(g1);
+  g2 = wave_total(g2);
+  if (lane == 0) {
+    red[3 * wave] = g0;
+    red[3 * wave + 1] = g1;
+    red[3 * wave + 2] = g2;
   }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t s0 = 0, s1 = 0, s2 = 0;
+    if (lane < SW) { s0 = red[3 * lane]; s1 = red[3 * lane + 1]; s2 = red[3 * lane + 2]; }
+    // 8 values in lanes 0..7: two quad butterflies and a half-row mirror
+    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_XOR1>(s0));
+    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_XOR1>(s1));
+    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_XOR1>(s2));
+    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_XOR2>(s0));
+    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_XOR2>(s1));
+    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_XOR2>(s2));
+    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s0));
+    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s1));
+    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s2));
+    if (lane == 0) {
+      rounds[3 * i] = s0; rounds[3 * i + 1] = s1; rounds[3 * i + 2] = s2;
+      if (i == 0 && claim0) claim0[0] = gl::add(s0, s1);
+    }
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
   __shared__ uint64_t lA[ST], lB[ST];
-  __shared__ uint64_t red[3 * (ST / 64)];
+  __shared__ uint64_t red[3 * SW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int np = a.n_pairs;
   const fp_elem* r = a.r;
@@ -223,7 +265,7 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
   // entry q of pair j at the start of the tail
   auto load_entry = [&](int j, int q, uint64_t& x, uint64_t& y) {
     if (j >= np) { x = 0; y = 0; return; }
-    if (i == 0) { x = uA[j][q]; y = uB[j][q]; return; }
+    if (a.i0 == 0) { x = uA[j][q]; y = uB[j][q]; return; }
     const fp_elem* A = (a.i0 == 1) ? uA[j] : a.src + (int64_t)j * mp;
     const fp_elem* B = (a.i0 == 1) ? uB[j] : a.src + (int64_t)(np + j) * mp;
     const uint64_t x0 = A[2 * q], x1 = A[2 * q + 1], y0 = B[2 * q], y1 = B[2 * q + 1];
@@ -251,24 +293,7 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       for (int q = 0; q < SLMAX / 2; ++q)
         if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
       if (weighted) { g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj); }
-      wave_sum3(g0, g1, g2);
-      if (lane == 0) { red[3 * wave] = g0; red[3 * wave + 1] = g1; red[3 * wave + 2] = g2; }
-      __syncthreads();
-      if (wave == 0) {
-        uint64_t s0 = 0, s1 = 0, s2 = 0;
-        if (lane < ST / 64) { s0 = red[3 * lane]; s1 = red[3 * lane + 1]; s2 = red[3 * lane + 2]; }
-#pragma unroll
-        for (int d = 1; d < ST / 64; d <<= 1) {
-          s0 = gl::add(s0, fpi::shfl_xor_u64(s0, d));
-          s1 = gl::add(s1, fpi::shfl_xor_u64(s1, d));
-          s2 = gl::add(s2, fpi::shfl_xor_u64(s2, d));
-        }
-        if (lane == 0) {
-          rounds[3 * i] = s0; rounds[3 * i + 1] = s1; rounds[3 * i + 2] = s2;
-          if (i == 0 && claim0) claim0[0] = gl::add(s0, s1);
-        }
-      }
-      __syncthreads();  // g_i is complete before r_i is read
+      block_round(g0, g1, g2, red, rounds, i, claim0);
       const uint64_t ri = r[i];
 #pragma unroll
       for (int q = 0; q < SLMAX / 2; ++q)
@@ -290,52 +315,42 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
     }
   }
   __syncthreads();
-  if (wave != 0) return;
 
-  // ---- phase 2: wave 0 alone ------------------------------------------------
-  uint64_t xa[8], xb[8];
-  int Lw = mt >= 64 ? mt / 64 : 1;
-  {
-    const int e0 = lane * Lw;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < Lw) {
-        const bool in = e0 + k < mt;
-        xa[k] = in ? lA[e0 + k] : 0;
-        xb[k] = in ? lB[e0 + k] : 0;
+  // ---- phase 2: LDS rounds, one pair per thread ---------------------------
+  while (mt > 64 && m > 1) {
+    const int h = mt >> 1;
+    const bool act = tid < h;
+    const int e = 2 * tid;
+    const int j = act ? e / m : 0;
+    uint64_t x0 = 0, x1 = 0, y0 = 0, y1 = 0, g0 = 0, g1 = 0, g2 = 0;
+    if (act) {
+      x0 = lA[e]; x1 = lA[e + 1]; y0 = lB[e]; y1 = lB[e + 1];
+      round_terms(x0, x1, y0, y1, g0, g1, g2);
+      if (weighted) {
+        const uint64_t wj = weight(j);
+        g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
       }
-  }
-  while (Lw >= 2) {
-    const int j = (lane * Lw) / m;
-    uint64_t g0 = 0, g1 = 0, g2 = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (2 * q < Lw) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
-    if (weighted) {
-      const uint64_t wj = weight(j);
-      g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
     }
-    wave_sum3(g0, g1, g2);
-    if (lane == 0) {
-      rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
-      if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
-    }
+    block_round(g0, g1, g2, red, rounds, i, claim0);
     const uint64_t ri = r[i];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (2 * q < Lw) {
-        xa[q] = gl::add(xa[2 * q], gl::mul(ri, gl::sub(xa[2 * q + 1], xa[2 * q])));
-        xb[q] = gl::add(xb[2 * q], gl::mul(ri, gl::sub(xb[2 * q + 1], xb[2 * q])));
-      }
-    Lw >>= 1;
+    if (act) {
+      x0 = gl::add(x0, gl::mul(ri, gl::sub(x1, x0)));
+      y0 = gl::add(y0, gl::mul(ri, gl::sub(y1, y0)));
+    }
+    __syncthreads();  // every read of this round's table is done
+    if (act) { lA[tid] = x0; lB[tid] = y0; }
+    __syncthreads();
+    mt = h;
     m >>= 1;
     ++i;
   }
-  // one entry per lane (lanes < mt / (Lw == 1 ? 1 : 1)); pair j spans lanes [j m, (j+1) m)
-  uint64_t x = xa[0], y = xb[0];
+  if (wave != 0) return;
+
+  // ---- phase 3: wave 0, one entry per lane -------------------------------
+  const bool live = lane < mt;
+  uint64_t x = live ? lA[lane] : 0, y = live ? lB[lane] : 0;
   const int m0 = m;
-  const int jl = lane / (m0 > 0 ? m0 : 1);
-  const bool live = lane < vp * m0;
+  const int jl = lane / m0;
   for (int d = 1; d < m0; d <<= 1) {
     const uint64_t x1 = fpi::shfl_xor_u64(x, d);
     const uint64_t y1 = fpi::shfl_xor_u64(y, d);
@@ -346,7 +361,9 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       const uint64_t wj = even ? weight(jl) : 0;
       g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
     }
-    wave_sum3(g0, g1, g2);
+    g0 = wave_total(g0);
+    g1 = wave_total(g1);
+    g2 = wave_total(g2);
     if (lane == 0) {
       rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
       if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);

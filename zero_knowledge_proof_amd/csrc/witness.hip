@@ -20,9 +20,10 @@
 // g = 1,3 halves between lanes l and l+32, after which each lane holds 16
 // consecutive o of one t: Z leaves as four 16-byte stores and Y, R as one
 // 16-byte store each. Workgroup tiles are BO x BT (outputs x tokens), wave
-// tiles WO x WT; K steps of 64 bytes are double-buffered through LDS, rows
-// padded to 80 bytes so the 16-byte reads of 16 consecutive rows hit distinct
-// bank groups. Workgroup ids are remapped so that each XCD (ids are dealt to
+// tiles WO x WT; K steps of BK bytes are double-buffered through LDS with the
+// next steps' tiles staged in registers, rows padded by 16 bytes so the
+// 16-byte reads of 16 consecutive rows hit distinct bank groups (an unpadded
+// 64- or 128-byte pitch measures 3-6x slower). Workgroup ids are remapped so that each XCD (ids are dealt to
 // the 8 XCDs round-robin) works on a contiguous run of tiles; tokens vary
 // fastest, so one W panel is shared by the XCD's tiles in its L2.
 #include "common.hpp"
@@ -32,8 +33,6 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;
-constexpr int PITCH = 80;
 constexpr int MAXG = 128;  // groups per grouped launch
 
 struct WitArgs {
@@ -85,12 +84,14 @@ __device__ __forceinline__ void rescale(int32_t z, int s, int32_t lowmask, uint3
   r = (uint32_t)(uint8_t)(int8_t)rr;
 }
 
-template <int BO, int BT, int WO, int WT, bool GROUPED>
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
 __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
+  constexpr int PITCH = BK + 16;  // LDS row pitch: 16 consecutive rows start in distinct bank groups
+  constexpr int CPR = BK / 16;    // 16-byte chunks per row
   constexpr int WAVES_T = BT / WT;
   constexpr int NT = (BO / WO) * WAVES_T * 64;
   constexpr int TM = WO / 32, TN = WT / 32;
-  constexpr int NCA = BO * (BK / 16), NCB = BT * (BK / 16);  // 16-byte chunks per K step
+  constexpr int NCA = BO * CPR, NCB = BT * CPR;  // 16-byte chunks per K step
   constexpr int CA = (NCA + NT - 1) / NT;
   constexpr int CB = (NCB + NT - 1) / NT;
   __shared__ __align__(16) int8_t sA[2][BO * PITCH];  // W rows
@@ -123,48 +124,53 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
   const int wo0 = (wave / WAVES_T) * WO;
   const int wt0 = (wave % WAVES_T) * WT;
 
+  // Rows past the matrix are clamped to its last row: their products land in
+  // outputs that are never stored, and every load stays in bounds.
   const int8_t* pa[CA];
   const int8_t* pb[CB];
   int sa_off[CA], sb_off[CB], ka[CA], kb[CB];
 #pragma unroll
   for (int c = 0; c < CA; ++c) {
     const int ch = tid + c * NT;
-    const int row = ch >> 2, kc = (ch & 3) * 16;
-    const int g = o_base + row;
-    pa[c] = (ch < NCA && g < a.N) ? Wb + (int64_t)g * a.ldw : nullptr;
+    const int row = ch / CPR, kc = (ch % CPR) * 16;
+    const int g = min(o_base + row, a.N - 1);
+    pa[c] = Wb + (int64_t)g * a.ldw;
     ka[c] = kc;
     sa_off[c] = (ch < NCA) ? row * PITCH + kc : -1;
   }
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     const int ch = tid + c * NT;
-    const int row = ch >> 2, kc = (ch & 3) * 16;
-    const int g = t_base + row;
-    pb[c] = (ch < NCB && g < t_lim) ? a.X + (int64_t)g * a.ldx : nullptr;
+    const int row = ch / CPR, kc = (ch % CPR) * 16;
+    const int g = min(t_base + row, t_lim - 1);
+    pb[c] = a.X + (int64_t)g * a.ldx;
     kb[c] = kc;
     sb_off[c] = (ch < NCB) ? row * PITCH + kc : -1;
   }
-  const bool vx = a.vecX, vw = a.vecW;
-  v4i ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  // register staging for PF K steps ahead; whole 16-byte chunks when the K step
+  // lies inside the matrix and the rows are 16-byte aligned (a uniform branch)
+  const bool vec_all = a.vecX && a.vecW;
+  v4i ra[PF][CA], rb[PF][CB];
+  auto gload = [&](int slot, int k0) {
+    if (vec_all && k0 + BK <= a.K) {
 #pragma unroll
-    for (int c = 0; c < CA; ++c) {
-      v4i z = {0, 0, 0, 0};
-      ra[c] = pa[c] ? load16(pa[c], k0 + ka[c], a.K, vw) : z;
-    }
+      for (int c = 0; c < CA; ++c) ra[slot][c] = *(const v4i*)(pa[c] + k0 + ka[c]);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      v4i z = {0, 0, 0, 0};
-      rb[c] = pb[c] ? load16(pb[c], k0 + kb[c], a.K, vx) : z;
+      for (int c = 0; c < CB; ++c) rb[slot][c] = *(const v4i*)(pb[c] + k0 + kb[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CA; ++c) ra[slot][c] = load16(pa[c], k0 + ka[c], a.K, a.vecW);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) rb[slot][c] = load16(pb[c], k0 + kb[c], a.K, a.vecX);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int slot, int buf) {
 #pragma unroll
     for (int c = 0; c < CA; ++c)
-      if (NCA % NT == 0 || sa_off[c] >= 0) *(v4i*)&sA[buf][sa_off[c]] = ra[c];
+      if (NCA % NT == 0 || sa_off[c] >= 0) *(v4i*)&sA[buf][sa_off[c]] = ra[slot][c];
 #pragma unroll
     for (int c = 0; c < CB; ++c)
-      if (NCB % NT == 0 || sb_off[c] >= 0) *(v4i*)&sB[buf][sb_off[c]] = rb[c];
+      if (NCB % NT == 0 || sb_off[c] >= 0) *(v4i*)&sB[buf][sb_off[c]] = rb[slot][c];
   };
 
   v16i acc[TM][TN];
@@ -176,13 +182,8 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
   const int KT = (a.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int lrow = lane & 31, lk = (lane >> 5) * 16;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       v4i fa[TM], fb[TN];
@@ -195,8 +196,28 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
+  };
+  // Pipeline: while step s is multiplied out of LDS buffer s%2, the loads of
+  // step s+PF are in flight into register slot s%PF; step s+1's registers go
+  // to the other LDS buffer after the MFMAs, then one barrier. U = lcm(PF, 2)
+  // steps are unrolled so that slots and buffers are compile-time indices.
+  constexpr int U = (PF % 2 == 0) ? PF : 2 * PF;
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < KT) gload(p, p * BK);
+  sstore(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = kt + u;
+      if (st < KT) {
+        if (st + PF < KT) gload(u % PF, (st + PF) * BK);
+        compute(u % 2);
+        if (st + 1 < KT) sstore((u + 1) % PF, (u + 1) % 2);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue: 16 consecutive outputs per lane, rescale, clamp, remainder
@@ -272,19 +293,24 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
   }
 }
 
-// Tile configurations (BO, BT, WO, WT): 4 waves each.
-#define WIT_L 256, 128, 128, 64
-#define WIT_M 128, 128, 64, 64
-#define WIT_S 256, 32, 64, 32
+// Tile configurations (BO, BT, WO, WT, grouped, prefetch distance, K step),
+// chosen from measurements on the up-projection and layer shapes:
+//   XL: 256x256 outputs x tokens, 8 waves of 64x128, K step 64
+//   M : 128x128, 4 waves of 64x64, K step 128
+//   S : 256x32 for few tokens (and MoE groups), 4 waves of 64x32
+#define WIT_XL 256, 256, 64, 128, false, 1, 64
+#define WIT_M 128, 128, 64, 64, false, 1, 128
+#define WIT_S 256, 32, 64, 32, false, 1, 64
+#define WIT_SG 256, 32, 64, 32, true, 1, 64
 
-template <int BO, int BT, int WO, int WT, bool GROUPED>
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
 int launch(WitArgs a, const GroupTab& gt, hipStream_t st) {
   if (!GROUPED) a.tiles_t = (a.T + BT - 1) / BT;
   a.tiles_o = (a.N + BO - 1) / BO;
   const int64_t blocks = (int64_t)a.tiles_t * a.tiles_o;
   if (blocks <= 0) return FP_OK;
   if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
-  hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED, PF, BK>), dim3((unsigned)blocks),
                      dim3((BO / WO) * (BT / WT) * 64), 0, st, a, gt);
   return fpi::check_launch("witness_kernel");
 }
@@ -320,10 +346,10 @@ extern "C" int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, 
   vec_flags(a);
   a.vecW = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
   GroupTab gt{};
-  const int64_t big = (int64_t)((d_out + 255) / 256) * ((T + 127) / 128);
-  if (T <= 32) rc = launch<WIT_S, false>(a, gt, stream);
-  else if (T >= 128 && big >= 200) rc = launch<WIT_L, false>(a, gt, stream);
-  else rc = launch<WIT_M, false>(a, gt, stream);
+  const int64_t xl_tiles = (int64_t)((d_out + 255) / 256) * ((T + 255) / 256);
+  if (T <= 32) rc = launch<WIT_S>(a, gt, stream);
+  else if (xl_tiles >= 256) rc = launch<WIT_XL>(a, gt, stream);
+  else rc = launch<WIT_M>(a, gt, stream);
   return rc ? rc : fpi::ok();
 }
 
@@ -371,7 +397,7 @@ extern "C" int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int
     gt.tile_off[ng] = tiles;
     gt.G = ng;
     a.tiles_t = tiles;
-    rc = launch<WIT_S, true>(a, gt, stream);
+    rc = launch<WIT_SG>(a, gt, stream);
     if (rc) return rc;
   }
   return fpi::ok();
