@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one device-to-device copy of MIB MiB (a reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this prover runs on one GPU; --gpus %d is not supported (each box has one GPU)" % args.gpus,
@@ -101,6 +103,14 @@ def main():
     fp.require_gpu()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = synth.config(args.config)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
