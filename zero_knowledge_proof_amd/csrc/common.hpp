@@ -42,6 +42,22 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
 
+}  // namespace fpi
+#include "gl.hpp"
+namespace fpi {
+
+// Field sum over the 64 lanes of a wave (every lane active), returned to all
+// lanes: DPP butterflies inside each row of 16, then the four row sums.
+__device__ __forceinline__ uint64_t wave_total(uint64_t v) {
+  v = gl::add(v, dpp_u64<DPP_XOR1>(v));
+  v = gl::add(v, dpp_u64<DPP_XOR2>(v));
+  v = gl::add(v, dpp_u64<DPP_HALF_MIRROR>(v));
+  v = gl::add(v, dpp_u64<DPP_MIRROR>(v));  // every lane: its row's sum
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  return gl::add(gl::add(a, b), gl::add(c, d));
+}
+
 // --- launchers implemented in the .hip files (no validation inside) -------
 int launch_eq(const fp_elem* r, int32_t n, fp_elem* E, hipStream_t st);
 int launch_eq_list(int32_t count, const fp_eq_desc* descs_host, hipStream_t st);

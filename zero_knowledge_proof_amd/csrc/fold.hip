@@ -47,6 +47,7 @@ struct FoldJob {
   int32_t chunk_rows, n_chunks, n_strips;  // strips holding data columns
   int32_t n_pad_strips;                    // strips wholly inside [cols, cols_pad)
   int32_t block_start;
+  int32_t vec;  // whole aligned 4-column groups (see fold_body)
 };
 
 struct JobList {
@@ -84,216 +85,216 @@ __device__ __forceinline__ void acc128(uint64_t& lo, uint64_t& hi, uint32_t v, i
   lo = nlo;
 }
 
-__device__ __forceinline__ uint64_t wave_sum(uint64_t s) {
+// 4-row groups per wave and batch: int8 rows are 4 bytes a lane, int32 rows 16.
+template <int EB> constexpr int kU = (EB == 1) ? 2 : 1;
+template <int EB> constexpr int kStep = FRG * kU<EB>;                  // groups per batch (workgroup)
+template <int EB> constexpr int kMaxG = FMAX_CHUNK / 4 + 2 * kStep<EB>;  // digit groups incl. padding
+// rows of a chunk are a multiple of this (whole pairs of batches)
+template <int EB> constexpr int kRowQuantum = 8 * kStep<EB>;
+
+template <int EB> constexpr int kNL = (EB == 1) ? 8 : 11;  // limb accumulators per column
+template <int EB> constexpr int kLdsWords =
+    (kMaxG<EB> * 8 > 3 * FRG * FCT * kNL<EB>) ? kMaxG<EB> * 8 : 3 * FRG * FCT * kNL<EB>;
+
+// One workgroup's (chunk, strip). VEC: every lane's 4 columns are whole and
+// aligned (cols % 4 == 0, aligned rows), so a row is one dword (int8) or one
+// dwordx4 (int32) load per lane; otherwise each column is loaded alone.
+template <int EB, bool VEC>
+__device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* lds, uint64_t* gsum) {
+  constexpr int NL = kNL<EB>;
+  constexpr int U = kU<EB>;
+  constexpr int STEP = kStep<EB>;
+  constexpr int W = (EB == 1) ? 1 : 4;    // dwords per lane and row
+  const int tid = threadIdx.x;
+  const int ct = tid % FCT;
+  const int rg = __builtin_amdgcn_readfirstlane(tid / FCT);  // wave index (uniform)
+  const int chunk = lb / job.n_strips;
+  const int strip = lb - chunk * job.n_strips;
+  const int row0 = chunk * job.chunk_rows;
+  const int nrows = min(job.chunk_rows, job.rows - row0);
+  const int ngroups = (nrows + 3) >> 2;
+  const int nb = (ngroups + STEP - 1) / STEP;  // batches
+  const int nbp = (nb + 1) & ~1;               // whole pairs for the two-stage loop
+  const int gpad = nbp * STEP;                 // groups with digits (zero past the rows)
+  const int c0 = strip * FCOLS + 4 * ct;
+  const int col = c0 + rg;                     // the column this wave finishes
+
+  // Rows go through a buffer descriptor: the chunk's base in SGPRs, the lane's
+  // column byte offset as the VGPR offset and the row's byte offset (wave-
+  // uniform) as the scalar offset. Rows past the chunk are clamped to its last
+  // row (their digits are zero); columns past cols are read from inside the
+  // row and never stored.
+  const uint32_t ldb = (uint32_t)job.ld * EB;
+  const char* cbase = (const char*)job.M + (int64_t)row0 * job.ld * EB;
+  const uint32_t extent = (uint32_t)(nrows - 1) * ldb + (uint32_t)job.cols * EB;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, (int)extent, 0x00020000);
+  const int cl = VEC ? min(c0, job.cols - 4) : 0;  // idle lanes read inside the row
+  uint32_t A[U][4][W], B[U][4][W];
+  auto load = [&](uint32_t (&v)[U][4][W], int bi) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s = gl::add(s, fpi::shfl_xor_u64(s, m));
-  return s;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = min(4 * (bi * STEP + rg + FRG * u) + i, nrows - 1);
+        const int soff = (int)((uint32_t)t * ldb);
+        if constexpr (VEC && EB == 1) {
+          v[u][i][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, cl, soff, 0);
+        } else if constexpr (VEC) {
+          const u32x4 q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, cl * 4, soff, 0));
+          v[u][i][0] = q[0]; v[u][i][1] = q[1]; v[u][i][2] = q[2]; v[u][i][3] = q[3];
+        } else if constexpr (EB == 1) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int cc = min(c0 + c, job.cols - 1);
+            w |= (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, cc, soff, 0) << (8 * c);
+          }
+          v[u][i][0] = w;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int cc = min(c0 + c, job.cols - 1);
+            v[u][i][c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, cc * 4, soff, 0);
+          }
+        }
+      }
+  };
+
+  uint32_t acc[4][NL];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int l = 0; l < NL; ++l) acc[c][l] = 0;
+  auto compute = [&](const uint32_t (&v)[U][4][W], int bi) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = bi * STEP + rg + FRG * u;
+      const u32x4 d0 = *(const u32x4*)&lds[g * 8];
+      const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
+      const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      if constexpr (EB == 1) {
+        uint32_t w[4];
+        transpose4(v[u][0][0], v[u][1][0], v[u][2][0], v[u][3][0], w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t uu = w[c] ^ 0x80808080u;  // m + 128 per byte
+#pragma unroll
+          for (int l = 0; l < 8; ++l) acc[c][l] = udot4(uu, dg[l], acc[c][l]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t pl[4];  // byte planes of this column's 4 rows
+          transpose4(v[u][0][c], v[u][1][c], v[u][2][c], v[u][3][c], pl[0], pl[1], pl[2], pl[3]);
+          pl[3] ^= 0x80808080u;  // m + 2^31 as an unsigned 32-bit value
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int l = 0; l < 8; ++l) acc[c][b + l] = udot4(pl[b], dg[l], acc[c][b + l]);
+        }
+      }
+    }
+  };
+
+  // the first batch is in flight while the digits are built
+  const uint64_t ecol = (job.Ecol && col < job.cols) ? job.Ecol[col] : 0;
+  load(A, 0);
+
+  // ---- digits of E for this chunk (zero past its rows), and group sums of E ----
+  for (int g = tid; g < gpad; g += FT) {
+    uint32_t dg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint64_t es = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+      const uint64_t e = (t < nrows) ? job.E[row0 + t] : 0;
+      es = gl::add(es, e);
+#pragma unroll
+      for (int l = 0; l < 8; ++l) dg[l] |= (uint32_t)((e >> (8 * l)) & 0xFF) << (8 * i);
+    }
+    *(u32x4*)&lds[g * 8] = u32x4{dg[0], dg[1], dg[2], dg[3]};
+    *(u32x4*)&lds[g * 8 + 4] = u32x4{dg[4], dg[5], dg[6], dg[7]};
+    gsum[g] = es;
+  }
+  __syncthreads();
+
+  // ---- main loop: batch bi covers groups bi*STEP .. bi*STEP+STEP-1; two
+  // register sets so one batch's loads are in flight while the other is used ----
+  int bi = 0;
+  for (; bi + 2 < nbp; bi += 2) {
+    load(B, bi + 1);
+    compute(A, bi);
+    load(A, bi + 2);
+    compute(B, bi + 1);
+  }
+  load(B, bi + 1);
+  compute(A, bi);
+  compute(B, bi + 1);
+
+  // ---- exchange: wave v stores its other three columns (lane-contiguous), and
+  // each wave finishes column c0 + v of its lanes ----
+  __syncthreads();  // digits no longer needed
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c == rg) continue;
+    const int slot = rg * 3 + (c < rg ? c : c - 1);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) lds[(slot * NL + l) * FCT + ct] = acc[c][l];
+  }
+  __syncthreads();
+  uint32_t sl[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) sl[l] = rg == 0 ? acc[0][l] : rg == 1 ? acc[1][l] : rg == 2 ? acc[2][l] : acc[3][l];
+#pragma unroll
+  for (int v = 0; v < FRG; ++v) {
+    if (v == rg) continue;
+    const int slot = v * 3 + (rg < v ? rg : rg - 1);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) sl[l] += lds[(slot * NL + l) * FCT + ct];  // exact: < 2^32
+  }
+  uint64_t es = 0;
+  for (int g = ct; g < gpad; g += FCT) es = gl::add(es, gsum[g]);
+  es = fpi::wave_total(es);
+  // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
+  const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
+  uint64_t lo = 0, hi = 0;
+#pragma unroll
+  for (int l = 0; l < NL; ++l) acc128(lo, hi, sl[l], 8 * l);
+  const uint64_t val = gl::sub(gl::reduce128(lo, hi), corr);
+
+  if (job.Ecol) {
+    // claim: weight the column by its eq value; one value per wave
+    const uint64_t s = fpi::wave_total(gl::mul(val, ecol));
+    if (ct == 0) job.part[lb * FRG + rg] = s;
+    return;
+  }
+  if (job.n_chunks == 1) {
+    if (col < job.cols) job.out[col] = val;
+    else if (col < job.cols_pad) job.out[col] = 0;
+    return;
+  }
+  if (col < job.cols) job.part[(int64_t)chunk * job.cols + col] = val;
 }
 
 template <int EB>
 __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
-  constexpr int NL = (EB == 1) ? 8 : 11;  // limb accumulators per column
-  constexpr int U = (EB == 1) ? 4 : 2;    // row groups of 4 rows in flight per thread
-  constexpr int DIG_WORDS = FMAX_CHUNK / 4 * 8;
-  constexpr int RED_WORDS = (FRG - 1) * FCT * 4 * NL;
-  constexpr int LDS_WORDS = DIG_WORDS > RED_WORDS ? DIG_WORDS : RED_WORDS;
-  __shared__ __align__(16) uint32_t lds[LDS_WORDS];
-  __shared__ uint64_t wpart[FT / 64];
-
+  __shared__ __align__(16) uint32_t lds[kLdsWords<EB>];
+  __shared__ uint64_t gsum[kMaxG<EB>];
   int ji = 0;
 #pragma unroll 1
   for (int k = 1; k < jl.count; ++k)
     if (jl.j[k].block_start <= (int)blockIdx.x) ji = k;
   const FoldJob& job = jl.j[ji];
   const int lb = blockIdx.x - job.block_start;
-  const int tid = threadIdx.x;
-  const int ct = tid % FCT, rg = tid / FCT;
-
   // strips wholly in the padding: write zeros and leave
   if (lb >= job.n_chunks * job.n_strips) {
     const int strip = job.n_strips + (lb - job.n_chunks * job.n_strips);
-    for (int c = strip * FCOLS + tid; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) job.out[c] = 0;
+    for (int c = strip * FCOLS + (int)threadIdx.x; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) job.out[c] = 0;
     return;
   }
-  const int chunk = lb / job.n_strips;
-  const int strip = lb - chunk * job.n_strips;
-  const int row0 = chunk * job.chunk_rows;
-  const int nrows = min(job.chunk_rows, job.rows - row0);
-  const int ngroups = (nrows + 3) >> 2;
-
-  // ---- digits of E for this chunk, and the chunk's sum of E ----
-  uint64_t esum = 0;
-  for (int g = tid; g < ngroups; g += FT) {
-    uint32_t dg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      const uint64_t e = (t < nrows) ? job.E[row0 + t] : 0;
-      esum = gl::add(esum, e);
-#pragma unroll
-      for (int l = 0; l < 8; ++l) dg[l] |= (uint32_t)((e >> (8 * l)) & 0xFF) << (8 * i);
-    }
-    *(u32x4*)&lds[g * 8] = u32x4{dg[0], dg[1], dg[2], dg[3]};
-    *(u32x4*)&lds[g * 8 + 4] = u32x4{dg[4], dg[5], dg[6], dg[7]};
-  }
-  esum = wave_sum(esum);
-  if ((tid & 63) == 0) wpart[tid >> 6] = esum;
-  __syncthreads();
-
-  // ---- main loop: 4-row groups g = rg, rg + FRG, ... ----
-  const int c0 = strip * FCOLS + 4 * ct;
-  uint32_t acc[4][NL];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int l = 0; l < NL; ++l) acc[c][l] = 0;
-
-  if (c0 < job.cols) {
-    const bool full_cols = (c0 + 4 <= job.cols);
-    if constexpr (EB == 1) {
-      const int8_t* base = (const int8_t*)job.M + (int64_t)row0 * job.ld + c0;
-      const bool vec = full_cols && ((job.ld & 3) == 0) && ((((uintptr_t)job.M) & 3) == 0);
-      for (int g0 = rg; g0 < ngroups; g0 += FRG * U) {
-        uint32_t v[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 4 * (g0 + FRG * u) + i;
-            const int8_t* p = base + (int64_t)t * job.ld;
-            uint32_t w = 0;
-            if (t < nrows) {
-              if (vec) {
-                w = __builtin_nontemporal_load((const uint32_t*)p);
-              } else {
-                for (int c = 0; c < 4; ++c)
-                  if (c0 + c < job.cols) w |= (uint32_t)(uint8_t)p[c] << (8 * c);
-              }
-            }
-            v[u][i] = w;
-          }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int g = g0 + FRG * u;
-          if (g >= ngroups) break;
-          uint32_t w[4];
-          transpose4(v[u][0], v[u][1], v[u][2], v[u][3], w[0], w[1], w[2], w[3]);
-          const u32x4 d0 = *(const u32x4*)&lds[g * 8];
-          const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
-          const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t uu = w[c] ^ 0x80808080u;  // m + 128 per byte
-#pragma unroll
-            for (int l = 0; l < 8; ++l) acc[c][l] = udot4(uu, dg[l], acc[c][l]);
-          }
-        }
-      }
-    } else {
-      const int32_t* base = (const int32_t*)job.M + (int64_t)row0 * job.ld + c0;
-      const bool vec = full_cols && ((job.ld & 3) == 0) && ((((uintptr_t)job.M) & 15) == 0);
-      for (int g0 = rg; g0 < ngroups; g0 += FRG * U) {
-        uint32_t v[U][4][4];  // [group][row][col]
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 4 * (g0 + FRG * u) + i;
-            const int32_t* p = base + (int64_t)t * job.ld;
-            if (t < nrows && vec) {
-              const u32x4 q = __builtin_nontemporal_load((const u32x4*)p);
-              v[u][i][0] = q[0]; v[u][i][1] = q[1]; v[u][i][2] = q[2]; v[u][i][3] = q[3];
-            } else {
-#pragma unroll
-              for (int c = 0; c < 4; ++c) v[u][i][c] = (t < nrows && c0 + c < job.cols) ? (uint32_t)p[c] : 0u;
-            }
-          }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int g = g0 + FRG * u;
-          if (g >= ngroups) break;
-          const u32x4 d0 = *(const u32x4*)&lds[g * 8];
-          const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
-          const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            uint32_t pl[4];  // byte planes of this column's 4 rows
-            transpose4(v[u][0][c], v[u][1][c], v[u][2][c], v[u][3][c], pl[0], pl[1], pl[2], pl[3]);
-            pl[3] ^= 0x80808080u;  // m + 2^31 as an unsigned 32-bit value
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-              for (int l = 0; l < 8; ++l) acc[c][b + l] = udot4(pl[b], dg[l], acc[c][b + l]);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- cross-wave reduction of the limb sums (exact in u32) ----
-  __syncthreads();  // digits no longer needed
-  if (rg > 0) {
-    uint32_t* dst = &lds[((rg - 1) * FCT + ct) * 4 * NL];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int l = 0; l < NL; ++l) dst[c * NL + l] = acc[c][l];
-  }
-  __syncthreads();
-  uint64_t vals[4] = {0, 0, 0, 0};
-  if (rg == 0) {
-#pragma unroll
-    for (int w = 0; w < FRG - 1; ++w) {
-      const uint32_t* src = &lds[(w * FCT + ct) * 4 * NL];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int l = 0; l < NL; ++l) acc[c][l] += src[c * NL + l];
-    }
-    uint64_t es = 0;
-#pragma unroll
-    for (int w = 0; w < FT / 64; ++w) es = gl::add(es, wpart[w]);
-    // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
-    const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint64_t lo = 0, hi = 0;
-#pragma unroll
-      for (int l = 0; l < NL; ++l) acc128(lo, hi, acc[c][l], 8 * l);
-      vals[c] = gl::sub(gl::reduce128(lo, hi), corr);
-    }
-  }
-
-  if (job.Ecol) {
-    // claim: weight each column by its eq value; one value per workgroup
-    if (rg == 0) {
-      uint64_t s = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (c0 + c < job.cols) s = gl::add(s, gl::mul(vals[c], job.Ecol[c0 + c]));
-      s = wave_sum(s);
-      if (ct == 0) job.part[lb] = s;
-    }
-    return;
-  }
-
-  if (job.n_chunks == 1) {
-    if (rg == 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = c0 + c;
-        if (col < job.cols) job.out[col] = vals[c];
-        else if (col < job.cols_pad) job.out[col] = 0;
-      }
-    }
-    return;
-  }
-  if (rg == 0) {
-    fp_elem* dst = job.part + (int64_t)chunk * job.cols;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (c0 + c < job.cols) dst[c0 + c] = vals[c];
-  }
+  if (job.vec) fold_body<EB, true>(job, lb, lds, gsum);
+  else fold_body<EB, false>(job, lb, lds, gsum);
 }
 
 // ---- cross-chunk sums ----------------------------------------------------------
@@ -354,24 +355,23 @@ struct Plan {
   int64_t blocks, sum_blocks;  // fold workgroups; cross-chunk sum workgroups (0: none)
 };
 
-Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, bool claim) {
+Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool claim) {
   Plan p{};
   p.n_strips = (cols + FCOLS - 1) / FCOLS;
   const int pad_total = (cols_pad + FCOLS - 1) / FCOLS;
   p.n_pad_strips = claim ? 0 : (pad_total - p.n_strips);
-  const int target_blocks = 2048;
+  // about two workgroups per compute unit, chunks in whole pairs of batches
+  const int target_blocks = 512;
+  const int q = eb == 1 ? kRowQuantum<1> : kRowQuantum<4>;
   const int want_chunks = (target_blocks + p.n_strips - 1) / p.n_strips;
-  int cr = (rows + want_chunks - 1) / want_chunks;
-  cr = (cr + 15) / 16 * 16;
-  const int min_cr = claim ? 32 : 256;
-  if (cr < min_cr) cr = min_cr;
+  int64_t cr = (rows + want_chunks - 1) / want_chunks;
+  cr = (cr + q - 1) / q * q;
   if (cr > FMAX_CHUNK) cr = FMAX_CHUNK;
-  if (cr >= rows) cr = (rows + 3) / 4 * 4;
-  if (cr < 4) cr = 4;
-  p.chunk_rows = cr;
-  p.n_chunks = (rows + cr - 1) / cr;
+  if (cr >= rows) cr = rows;
+  p.chunk_rows = (int32_t)cr;
+  p.n_chunks = (int32_t)((rows + cr - 1) / cr);
   if (claim) {
-    p.part_bytes = fpi::align_up((size_t)p.n_chunks * p.n_strips * 8, 256);
+    p.part_bytes = fpi::align_up((size_t)p.n_chunks * p.n_strips * FRG * 8, 256);
     p.sum_blocks = 1;
   } else if (p.n_chunks > 1) {
     p.part_bytes = fpi::align_up((size_t)p.n_chunks * (size_t)cols * 8, 256);
@@ -385,12 +385,12 @@ Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, bool claim) {
 
 // Workspace: the partials of every job, back to back.
 template <typename Desc>
-size_t layout(int32_t count, const Desc* d, bool claim, int32_t (*rows)(const Desc&), int32_t (*cols)(const Desc&),
-              int32_t (*pad)(const Desc&)) {
+size_t layout(int eb, int32_t count, const Desc* d, bool claim, int32_t (*rows)(const Desc&),
+              int32_t (*cols)(const Desc&), int32_t (*pad)(const Desc&)) {
   size_t parts = 0;
   for (int32_t i = 0; i < count; ++i) {
     if (rows(d[i]) <= 0 || cols(d[i]) <= 0) continue;
-    parts += plan_job(rows(d[i]), cols(d[i]), pad(d[i]), claim).part_bytes;
+    parts += plan_job(rows(d[i]), cols(d[i]), pad(d[i]), eb, claim).part_bytes;
   }
   return parts;
 }
@@ -463,7 +463,12 @@ int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fi
       if (rc) return rc;
       continue;
     }
-    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, claim);
+    const int64_t span = (int64_t)j.ld * eb * (j.rows < FMAX_CHUNK ? j.rows : FMAX_CHUNK);
+    if (span > 0x7FFFFFFF)
+      return fpi::fail(FP_ESHAPE, "fold: row stride %lld x %d rows exceeds 2^31 bytes", (long long)j.ld, FMAX_CHUNK);
+    const uintptr_t align = eb == 1 ? 3 : 15;
+    j.vec = (j.cols % 4 == 0) && (j.ld % 4 == 0) && (((uintptr_t)j.M & align) == 0);
+    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, eb, claim);
     j.chunk_rows = p.chunk_rows;
     j.n_chunks = p.n_chunks;
     j.n_strips = p.n_strips;
@@ -484,7 +489,7 @@ int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fi
       sj.claim = claim ? 1 : 0;
       sj.cols = claim ? 0 : j.cols;
       sj.cols_pad = claim ? 1 : j.cols_pad;
-      sj.n_chunks = claim ? (int32_t)(p.n_chunks * p.n_strips) : p.n_chunks;
+      sj.n_chunks = claim ? (int32_t)(p.n_chunks * p.n_strips * FRG) : p.n_chunks;
       sj.block_start = (int32_t)sblocks;
       sl.j[sl.count++] = sj;
       sblocks += p.sum_blocks;
@@ -493,15 +498,14 @@ int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fi
   return jl.count ? flush() : FP_OK;
 }
 
-size_t fold_ws(int32_t count, const fp_fold_desc* d) { return layout(count, d, false, f_rows, f_cols, f_pad); }
-size_t claim_ws(int32_t count, const fp_claim_desc* d) { return layout(count, d, true, c_rows, c_cols, c_pad); }
+size_t fold_ws(int eb, int32_t count, const fp_fold_desc* d) { return layout(eb, count, d, false, f_rows, f_cols, f_pad); }
+size_t claim_ws(int eb, int32_t count, const fp_claim_desc* d) { return layout(eb, count, d, true, c_rows, c_cols, c_pad); }
 
 }  // namespace
 
 extern "C" size_t fp_fold_matrix_workspace(fp_dtype dt, int32_t rows, int32_t cols) {
-  (void)dt;
   fp_fold_desc d{nullptr, cols, rows, cols, cols, nullptr, nullptr};
-  return fold_ws(1, &d);
+  return fold_ws(dt == FP_I32 ? 4 : 1, 1, &d);
 }
 
 extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* E,
@@ -511,9 +515,8 @@ extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t ro
 }
 
 extern "C" size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* d) {
-  (void)dt;
   if (count <= 0 || !d) return 0;
-  return fold_ws(count, d);
+  return fold_ws(dt == FP_I32 ? 4 : 1, count, d);
 }
 
 extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* d, void* ws, size_t ws_bytes,
@@ -526,7 +529,7 @@ extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_
                            d[i].cols_pad);
     if (rc) return rc;
   }
-  const size_t need = layout(count, d, false, f_rows, f_cols, f_pad);
+  const size_t need = fold_ws(dt == FP_I8 ? 1 : 4, count, d);
   if (need && (!ws || ws_bytes < need))
     return fpi::fail(FP_EWORKSPACE, "fp_fold_matrix: workspace %zu < %zu", ws_bytes, need);
   auto fill = [](const fp_fold_desc& s, FoldJob& j) {
@@ -538,9 +541,8 @@ extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_
 }
 
 extern "C" size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* d) {
-  (void)dt;
   if (count <= 0 || !d) return 0;
-  return claim_ws(count, d);
+  return claim_ws(dt == FP_I32 ? 4 : 1, count, d);
 }
 
 extern "C" int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* d, void* ws, size_t ws_bytes,
@@ -555,7 +557,7 @@ extern "C" int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_
     if (!d[i].out || (d[i].rows > 0 && d[i].cols > 0 && (!d[i].M || !d[i].E_rows || !d[i].E_cols)))
       return fpi::fail(FP_EARG, "fp_claim_eval_batched: desc %d has a null pointer", i);
   }
-  const size_t need = layout(count, d, true, c_rows, c_cols, c_pad);
+  const size_t need = claim_ws(dt == FP_I8 ? 1 : 4, count, d);
   if (need && (!ws || ws_bytes < need))
     return fpi::fail(FP_EWORKSPACE, "fp_claim_eval_batched: workspace %zu < %zu", ws_bytes, need);
   auto fill = [](const fp_claim_desc& s, FoldJob& j) {

@@ -185,24 +185,15 @@ struct TailArgs {
 };
 
 // Sum over the wave, returned in every lane (full wave active).
-__device__ __forceinline__ uint64_t wave_total(uint64_t v) {
-  v = gl::add(v, fpi::dpp_u64<fpi::DPP_XOR1>(v));
-  v = gl::add(v, fpi::dpp_u64<fpi::DPP_XOR2>(v));
-  v = gl::add(v, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(v));
-  v = gl::add(v, fpi::dpp_u64<fpi::DPP_MIRROR>(v));  // every lane: its row's sum
-  const uint64_t a = fpi::readlane_u64(v, 0), b = fpi::readlane_u64(v, 16);
-  const uint64_t c = fpi::readlane_u64(v, 32), d = fpi::readlane_u64(v, 48);
-  return gl::add(gl::add(a, b), gl::add(c, d));
-}
 
 // Workgroup sum of (g0, g1, g2); wave 0 lane 0 writes round i. Ends with a
 // barrier, so r_i may be read afterwards.
 __device__ __forceinline__ void block_round(uint64_t g0, uint64_t g1, uint64_t g2, uint64_t* red, fp_elem* rounds,
                                             int i, fp_elem* claim0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  g0 = wave_total(g0);
-  g1 = wave_total(g1);
-  g2 = wave_total(g2);
+  g0 = fpi::wave_total(g0);
+  g1 = fpi::wave_total(g1);
+  g2 = fpi::wave_total(g2);
   if (lane == 0) {
     red[3 * wave] = g0;
     red[3 * wave + 1] = g1;
@@ -361,9 +352,9 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       const uint64_t wj = even ? weight(jl) : 0;
       g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
     }
-    g0 = wave_total(g0);
-    g1 = wave_total(g1);
-    g2 = wave_total(g2);
+    g0 = fpi::wave_total(g0);
+    g1 = fpi::wave_total(g1);
+    g2 = fpi::wave_total(g2);
     if (lane == 0) {
       rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
       if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
