@@ -175,6 +175,21 @@ int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* descs
                           hipStream_t stream);
 size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* descs);
 
+/* Folds and matmul claims of one layer in a single pass: the fold descriptors
+ * (all of dtype fold_dt) and the claim descriptors (all of dtype claim_dt) are
+ * processed by one launch of the row-fold kernel and one launch of the
+ * cross-chunk sums per dozen descriptors, so the passes over the weights and
+ * over Z share the GPU instead of running one after the other ("How fast can
+ * FlashProve go", §4 counts these as passes over the tables). Each output is
+ * exactly what fp_fold_matrix_batched / fp_claim_eval_batched writes for the
+ * same descriptor. Either count may be 0. descs are HOST arrays read during
+ * the call. ws: sized by fp_fold_claim_batched_workspace with the same
+ * arguments. */
+int fp_fold_claim_batched(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* folds, fp_dtype claim_dt,
+                          int32_t n_claim, const fp_claim_desc* claims, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t fp_fold_claim_batched_workspace(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* folds, fp_dtype claim_dt,
+                                       int32_t n_claim, const fp_claim_desc* claims);
+
 /* ----------------------------------------------------------- sum-check --- */
 /* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of
  * tables of 2^n entries ("How fast can FlashProve go", §2: sum-check reduces

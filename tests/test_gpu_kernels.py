@@ -109,6 +109,33 @@ def test_fold_batched(fp):
         assert np.array_equal(fp.field_numpy(o), w)
 
 
+
+def test_fold_claim_batched(fp):
+    """Folds (int8) and claims (int32) in one pass, more jobs than one launch
+    carries, with ragged, unaligned and empty matrices among them."""
+    rng = _rng(31)
+    folds, fwant = [], []
+    for rows, cols, cp in [(5, 7, 8), (0, 9, 16), (1500, 300, 512), (33, 1, 4), (700, 1030, 2048), (64, 256, 256)] * 2:
+        base = _i8(rng, (rows, cols + 3))
+        M = base[:, 3:]  # unaligned start, leading dim cols + 3
+        E = _field(rng, max(rows, 1))
+        Mt = _dev(base)[:, 3:]
+        folds.append((Mt, fp.to_field_tensor(E), cp, torch.empty(cp, dtype=torch.int64, device="cuda")))
+        fwant.append(O.fold_rows(np.ascontiguousarray(M), E, cp) if rows else np.zeros(cp, np.uint64))
+    claims, cwant = [], []
+    for rows, cols in [(16, 256), (7, 9), (300, 1000), (0, 5), (513, 260), (1, 1), (40, 4096)]:
+        M = rng.integers(-2**31, 2**31, size=(rows, cols), dtype=np.int64).astype(np.int32)
+        r_rows, r_cols = _field(rng, O.log2ceil(max(rows, 1)), False), _field(rng, O.log2ceil(cols), False)
+        claims.append((_dev(M), fp.to_field_tensor(O.eq_table(r_rows)), fp.to_field_tensor(O.eq_table(r_cols)),
+                       torch.empty(1, dtype=torch.int64, device="cuda")))
+        cwant.append(O.mle_matrix(M, r_rows, r_cols) if rows else 0)
+    fo, co = fp.fold_claim_batched(folds, claims)
+    torch.cuda.synchronize()
+    for o, w in zip(fo, fwant):
+        assert np.array_equal(fp.field_numpy(o), w)
+    assert [int(fp.field_numpy(o)[0]) for o in co] == cwant
+
+
 # ------------------------------------------------------------------ MLE ---
 @pytest.mark.parametrize("rows,cols", [(1, 1), (5, 6), (16, 256), (100, 300), (513, 1030)])
 @pytest.mark.parametrize("dt", [np.int8, np.int32])

@@ -24,7 +24,7 @@ EXPORTS = [
     "fp_fold_matrix", "fp_fold_matrix_workspace", "fp_fold_matrix_batched", "fp_fold_matrix_batched_workspace",
     "fp_mle_eval", "fp_mle_eval_workspace", "fp_sumcheck_prove", "fp_sumcheck_workspace",
     "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
-    "fp_linear_combine",
+    "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
 ]
 
 _lib = None
@@ -78,6 +78,8 @@ def lib():
             "fp_claim_eval_batched": (ctypes.c_int, [i32, i32, vp, vp, sz, vp]),
             "fp_claim_eval_batched_workspace": (sz, [i32, i32, vp]),
             "fp_linear_combine": (ctypes.c_int, [i32, vp, vp, vp, vp]),
+            "fp_fold_claim_batched": (ctypes.c_int, [i32, i32, vp, i32, i32, vp, vp, sz, vp]),
+            "fp_fold_claim_batched_workspace": (sz, [i32, i32, vp, i32, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -315,6 +317,23 @@ def claim_eval_batched(jobs):
     p, nb = _ws_claim.get(need)
     _check(lib().fp_claim_eval_batched(dt, k, descs, p, nb, _stream()), "fp_claim_eval_batched")
     return [j[3] for j in jobs]
+
+
+def fold_claim_batched(fold_jobs, claim_jobs):
+    """One pass over fold jobs (M, E, cols_pad, out) of one dtype and claim jobs
+    (M, E_rows, E_cols, out) of one dtype; outputs as fold_matrix_batched and
+    claim_eval_batched."""
+    nf, nc = len(fold_jobs), len(claim_jobs)
+    fdt = _dt(fold_jobs[0][0]) if nf else FP_I8
+    cdt = _dt(claim_jobs[0][0]) if nc else FP_I32
+    fd = (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
+                                              out.data_ptr()) for (M, E, cp, out) in fold_jobs])
+    cd = (_ClaimDesc * max(nc, 1))(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
+                                                Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in claim_jobs])
+    need = lib().fp_fold_claim_batched_workspace(fdt, nf, fd, cdt, nc, cd)
+    p, nb = _ws_fold.get(need)
+    _check(lib().fp_fold_claim_batched(fdt, nf, fd, cdt, nc, cd, p, nb, _stream()), "fp_fold_claim_batched")
+    return [j[3] for j in fold_jobs], [j[3] for j in claim_jobs]
 
 
 def linear_combine(vals, rho, out=None):

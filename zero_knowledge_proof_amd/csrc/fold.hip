@@ -23,6 +23,8 @@
 // one long dependent chain). For a claim, each workgroup weights its columns
 // with the column eq table and stores one value; one workgroup per claim then
 // adds them. The two kernels need no atomics and no cross-XCD fences.
+#include <vector>
+
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -48,6 +50,7 @@ struct FoldJob {
   int32_t n_pad_strips;                    // strips wholly inside [cols, cols_pad)
   int32_t block_start;
   int32_t vec;  // whole aligned 4-column groups (see fold_body)
+  int32_t eb;   // bytes per element: 1 (int8) or 4 (int32)
 };
 
 struct JobList {
@@ -277,10 +280,13 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
   if (col < job.cols) job.part[(int64_t)chunk * job.cols + col] = val;
 }
 
-template <int EB>
+constexpr int LDS_WORDS = kLdsWords<1> > kLdsWords<4> ? kLdsWords<1> : kLdsWords<4>;
+constexpr int MAXG_ALL = kMaxG<1> > kMaxG<4> ? kMaxG<1> : kMaxG<4>;
+
+// Every job of the list, int8 or int32, folds or claims, in one launch.
 __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
-  __shared__ __align__(16) uint32_t lds[kLdsWords<EB>];
-  __shared__ uint64_t gsum[kMaxG<EB>];
+  __shared__ __align__(16) uint32_t lds[LDS_WORDS];
+  __shared__ uint64_t gsum[MAXG_ALL];
   int ji = 0;
 #pragma unroll 1
   for (int k = 1; k < jl.count; ++k)
@@ -293,8 +299,13 @@ __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
     for (int c = strip * FCOLS + (int)threadIdx.x; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) job.out[c] = 0;
     return;
   }
-  if (job.vec) fold_body<EB, true>(job, lb, lds, gsum);
-  else fold_body<EB, false>(job, lb, lds, gsum);
+  if (job.eb == 1) {
+    if (job.vec) fold_body<1, true>(job, lb, lds, gsum);
+    else fold_body<1, false>(job, lb, lds, gsum);
+  } else {
+    if (job.vec) fold_body<4, true>(job, lb, lds, gsum);
+    else fold_body<4, false>(job, lb, lds, gsum);
+  }
 }
 
 // ---- cross-chunk sums ----------------------------------------------------------
@@ -383,30 +394,10 @@ Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool claim) 
   return p;
 }
 
-// Workspace: the partials of every job, back to back.
-template <typename Desc>
-size_t layout(int eb, int32_t count, const Desc* d, bool claim, int32_t (*rows)(const Desc&),
-              int32_t (*cols)(const Desc&), int32_t (*pad)(const Desc&)) {
-  size_t parts = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    if (rows(d[i]) <= 0 || cols(d[i]) <= 0) continue;
-    parts += plan_job(rows(d[i]), cols(d[i]), pad(d[i]), eb, claim).part_bytes;
-  }
-  return parts;
-}
-
-int32_t f_rows(const fp_fold_desc& d) { return d.rows; }
-int32_t f_cols(const fp_fold_desc& d) { return d.cols; }
-int32_t f_pad(const fp_fold_desc& d) { return d.cols_pad; }
-int32_t c_rows(const fp_claim_desc& d) { return d.rows; }
-int32_t c_cols(const fp_claim_desc& d) { return d.cols; }
-int32_t c_pad(const fp_claim_desc& d) { return d.cols; }
-
-int launch_list(int eb, const JobList& jl, int64_t blocks, hipStream_t st) {
+int launch_list(const JobList& jl, int64_t blocks, hipStream_t st) {
   if (blocks <= 0) return FP_OK;
   if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "fold: too many workgroups");
-  if (eb == 1) hipLaunchKernelGGL(fold_rows_kernel<1>, dim3((unsigned)blocks), dim3(FT), 0, st, jl);
-  else hipLaunchKernelGGL(fold_rows_kernel<4>, dim3((unsigned)blocks), dim3(FT), 0, st, jl);
+  hipLaunchKernelGGL(fold_rows_kernel, dim3((unsigned)blocks), dim3(FT), 0, st, jl);
   return fpi::check_launch("fold_rows_kernel");
 }
 
@@ -421,8 +412,9 @@ int zero_only(fp_elem* out, int32_t n, hipStream_t st) {
   j.n_chunks = 1;
   j.n_strips = 0;
   j.n_pad_strips = (n + FCOLS - 1) / FCOLS;
+  j.eb = 1;
   jl.count = 1;
-  return launch_list(1, jl, j.n_pad_strips, st);
+  return launch_list(jl, j.n_pad_strips, st);
 }
 
 int validate_fold(const char* fn, fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols,
@@ -435,16 +427,55 @@ int validate_fold(const char* fn, fp_dtype dt, const void* M, int64_t ld, int32_
   return FP_OK;
 }
 
-// Enqueue a list of fold or claim jobs, INLINE at a time: one fold launch and
-// (when needed) one cross-chunk sum launch per INLINE jobs.
-template <typename Desc, typename Fill>
-int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fill, hipStream_t st) {
+// A fold or claim job before planning.
+struct Item {
+  FoldJob j;
+  bool claim;
+};
+
+void add_folds(std::vector<Item>& v, fp_dtype dt, int32_t count, const fp_fold_desc* d) {
+  for (int32_t i = 0; i < count; ++i) {
+    Item it{};
+    FoldJob& j = it.j;
+    j.M = d[i].M; j.ld = d[i].ld; j.E = d[i].E; j.Ecol = nullptr; j.out = d[i].out;
+    j.rows = d[i].rows; j.cols = d[i].cols; j.cols_pad = d[i].cols_pad;
+    j.eb = dt == FP_I8 ? 1 : 4;
+    it.claim = false;
+    v.push_back(it);
+  }
+}
+
+void add_claims(std::vector<Item>& v, fp_dtype dt, int32_t count, const fp_claim_desc* d) {
+  for (int32_t i = 0; i < count; ++i) {
+    Item it{};
+    FoldJob& j = it.j;
+    j.M = d[i].M; j.ld = d[i].ld; j.E = d[i].E_rows; j.Ecol = d[i].E_cols; j.out = d[i].out;
+    j.rows = d[i].rows; j.cols = d[i].cols; j.cols_pad = d[i].cols;
+    j.eb = dt == FP_I8 ? 1 : 4;
+    it.claim = true;
+    v.push_back(it);
+  }
+}
+
+// Workspace: the partials of every job, back to back.
+size_t items_ws(const std::vector<Item>& v) {
+  size_t parts = 0;
+  for (const Item& it : v) {
+    if (it.j.rows <= 0 || it.j.cols <= 0) continue;
+    parts += plan_job(it.j.rows, it.j.cols, it.j.cols_pad, it.j.eb, it.claim).part_bytes;
+  }
+  return parts;
+}
+
+// Enqueue the jobs, INLINE at a time: one fold launch and (when needed) one
+// cross-chunk sum launch per INLINE jobs.
+int run_items(std::vector<Item>& v, char* ws, hipStream_t st) {
   char* parts = ws;
   JobList jl{};
   SumList sl{};
   int64_t blocks = 0, sblocks = 0;
   auto flush = [&]() -> int {
-    int rc = launch_list(eb, jl, blocks, st);
+    int rc = launch_list(jl, blocks, st);
     if (!rc && sblocks > 0) {
       hipLaunchKernelGGL(fold_sum_kernel, dim3((unsigned)sblocks), dim3(256), 0, st, sl);
       rc = fpi::check_launch("fold_sum_kernel");
@@ -454,9 +485,10 @@ int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fi
     blocks = sblocks = 0;
     return rc;
   };
-  for (int32_t i = 0; i < count; ++i) {
-    FoldJob j{};
-    fill(d[i], j);
+  for (Item& it : v) {
+    FoldJob j = it.j;
+    const bool claim = it.claim;
+    const int eb = j.eb;
     if (j.rows <= 0 || j.cols <= 0) {
       // empty matrix: zero output
       int rc = claim ? zero_only(j.out, 1, st) : zero_only(j.out, j.cols_pad, st);
@@ -498,14 +530,34 @@ int run_jobs(int eb, int32_t count, const Desc* d, bool claim, char* ws, Fill fi
   return jl.count ? flush() : FP_OK;
 }
 
-size_t fold_ws(int eb, int32_t count, const fp_fold_desc* d) { return layout(eb, count, d, false, f_rows, f_cols, f_pad); }
-size_t claim_ws(int eb, int32_t count, const fp_claim_desc* d) { return layout(eb, count, d, true, c_rows, c_cols, c_pad); }
+int validate_claims(const char* fn, fp_dtype dt, int32_t count, const fp_claim_desc* d) {
+  if (dt != FP_I8 && dt != FP_I32) return fpi::fail(FP_EARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (count < 0) return fpi::fail(FP_EARG, "%s: count < 0", fn);
+  if (count > 0 && !d) return fpi::fail(FP_EARG, "%s: null descs", fn);
+  for (int32_t i = 0; i < count; ++i) {
+    if (d[i].rows < 0 || d[i].cols < 0 || d[i].ld < d[i].cols)
+      return fpi::fail(FP_ESHAPE, "%s: desc %d has bad sizes", fn, i);
+    if (!d[i].out || (d[i].rows > 0 && d[i].cols > 0 && (!d[i].M || !d[i].E_rows || !d[i].E_cols)))
+      return fpi::fail(FP_EARG, "%s: desc %d has a null pointer", fn, i);
+  }
+  return FP_OK;
+}
+
+int validate_folds(const char* fn, fp_dtype dt, int32_t count, const fp_fold_desc* d) {
+  if (count < 0) return fpi::fail(FP_EARG, "%s: count < 0", fn);
+  if (count > 0 && !d) return fpi::fail(FP_EARG, "%s: null descs", fn);
+  for (int32_t i = 0; i < count; ++i) {
+    int rc = validate_fold(fn, dt, d[i].M, d[i].ld, d[i].rows, d[i].cols, d[i].E, d[i].out, d[i].cols_pad);
+    if (rc) return rc;
+  }
+  return FP_OK;
+}
 
 }  // namespace
 
 extern "C" size_t fp_fold_matrix_workspace(fp_dtype dt, int32_t rows, int32_t cols) {
   fp_fold_desc d{nullptr, cols, rows, cols, cols, nullptr, nullptr};
-  return fold_ws(dt == FP_I32 ? 4 : 1, 1, &d);
+  return fp_fold_matrix_batched_workspace(dt, 1, &d);
 }
 
 extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* E,
@@ -515,56 +567,45 @@ extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t ro
 }
 
 extern "C" size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* d) {
-  if (count <= 0 || !d) return 0;
-  return fold_ws(dt == FP_I32 ? 4 : 1, count, d);
+  return fp_fold_claim_batched_workspace(dt, count, d, FP_I32, 0, nullptr);
 }
 
 extern "C" int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* d, void* ws, size_t ws_bytes,
                                       hipStream_t stream) {
-  if (count < 0) return fpi::fail(FP_EARG, "fp_fold_matrix_batched: count < 0");
-  if (count == 0) return fpi::ok();
-  if (!d) return fpi::fail(FP_EARG, "fp_fold_matrix_batched: null descs");
-  for (int32_t i = 0; i < count; ++i) {
-    int rc = validate_fold("fp_fold_matrix", dt, d[i].M, d[i].ld, d[i].rows, d[i].cols, d[i].E, d[i].out,
-                           d[i].cols_pad);
-    if (rc) return rc;
-  }
-  const size_t need = fold_ws(dt == FP_I8 ? 1 : 4, count, d);
-  if (need && (!ws || ws_bytes < need))
-    return fpi::fail(FP_EWORKSPACE, "fp_fold_matrix: workspace %zu < %zu", ws_bytes, need);
-  auto fill = [](const fp_fold_desc& s, FoldJob& j) {
-    j.M = s.M; j.ld = s.ld; j.E = s.E; j.Ecol = nullptr; j.out = s.out;
-    j.rows = s.rows; j.cols = s.cols; j.cols_pad = s.cols_pad;
-  };
-  int rc = run_jobs(dt == FP_I8 ? 1 : 4, count, d, false, (char*)ws, fill, stream);
-  return rc ? rc : fpi::ok();
+  return fp_fold_claim_batched(dt, count, d, FP_I32, 0, nullptr, ws, ws_bytes, stream);
 }
 
 extern "C" size_t fp_claim_eval_batched_workspace(fp_dtype dt, int32_t count, const fp_claim_desc* d) {
-  if (count <= 0 || !d) return 0;
-  return claim_ws(dt == FP_I32 ? 4 : 1, count, d);
+  return fp_fold_claim_batched_workspace(FP_I8, 0, nullptr, dt, count, d);
 }
 
 extern "C" int fp_claim_eval_batched(fp_dtype dt, int32_t count, const fp_claim_desc* d, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
-  if (dt != FP_I8 && dt != FP_I32) return fpi::fail(FP_EARG, "fp_claim_eval_batched: unknown dtype %d", (int)dt);
-  if (count < 0) return fpi::fail(FP_EARG, "fp_claim_eval_batched: count < 0");
-  if (count == 0) return fpi::ok();
-  if (!d) return fpi::fail(FP_EARG, "fp_claim_eval_batched: null descs");
-  for (int32_t i = 0; i < count; ++i) {
-    if (d[i].rows < 0 || d[i].cols < 0 || d[i].ld < d[i].cols)
-      return fpi::fail(FP_ESHAPE, "fp_claim_eval_batched: desc %d has bad sizes", i);
-    if (!d[i].out || (d[i].rows > 0 && d[i].cols > 0 && (!d[i].M || !d[i].E_rows || !d[i].E_cols)))
-      return fpi::fail(FP_EARG, "fp_claim_eval_batched: desc %d has a null pointer", i);
-  }
-  const size_t need = claim_ws(dt == FP_I8 ? 1 : 4, count, d);
+  return fp_fold_claim_batched(FP_I8, 0, nullptr, dt, count, d, ws, ws_bytes, stream);
+}
+
+extern "C" size_t fp_fold_claim_batched_workspace(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* folds,
+                                                  fp_dtype claim_dt, int32_t n_claim, const fp_claim_desc* claims) {
+  std::vector<Item> v;
+  if (n_fold > 0 && folds) add_folds(v, fold_dt, n_fold, folds);
+  if (n_claim > 0 && claims) add_claims(v, claim_dt, n_claim, claims);
+  return items_ws(v);
+}
+
+extern "C" int fp_fold_claim_batched(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* folds, fp_dtype claim_dt,
+                                     int32_t n_claim, const fp_claim_desc* claims, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  int rc = validate_folds("fp_fold_matrix", fold_dt, n_fold, folds);
+  if (!rc) rc = validate_claims("fp_claim_eval_batched", claim_dt, n_claim, claims);
+  if (rc) return rc;
+  std::vector<Item> v;
+  add_folds(v, fold_dt, n_fold, folds);
+  add_claims(v, claim_dt, n_claim, claims);
+  if (v.empty()) return fpi::ok();
+  const size_t need = items_ws(v);
   if (need && (!ws || ws_bytes < need))
-    return fpi::fail(FP_EWORKSPACE, "fp_claim_eval_batched: workspace %zu < %zu", ws_bytes, need);
-  auto fill = [](const fp_claim_desc& s, FoldJob& j) {
-    j.M = s.M; j.ld = s.ld; j.E = s.E_rows; j.Ecol = s.E_cols; j.out = s.out;
-    j.rows = s.rows; j.cols = s.cols; j.cols_pad = s.cols;
-  };
-  int rc = run_jobs(dt == FP_I8 ? 1 : 4, count, d, true, (char*)ws, fill, stream);
+    return fpi::fail(FP_EWORKSPACE, "fold/claim: workspace %zu < %zu", ws_bytes, need);
+  rc = run_items(v, (char*)ws, stream);
   return rc ? rc : fpi::ok();
 }
 

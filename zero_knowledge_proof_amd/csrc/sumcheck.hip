@@ -155,17 +155,18 @@ __global__ __launch_bounds__(SC_RT) void sc_round_kernel(RoundArgs a) {
 //   i0 > 0 : reduce the partials of g_{i0-1}, then fold T_{i0-1} with r_{i0-1}
 //            while loading.
 // Pairs are padded to a power of two VP of "virtual" pairs (zero tables,
-// weight 0) so that every slice lies inside one pair.
-//   Phase 1 (tables > 512 entries): thread t holds entries [t L, (t+1) L) of A
-//     and B in registers; while L >= 2 the pairs (2q, 2q+1) of a round are in
-//     the slice, binding a variable moves no data, and only the three round
-//     sums cross threads.
-//   Phase 2 (64 < entries <= 512): the tables live in LDS; thread q handles the
-//     pair (2q, 2q+1) and writes the bound entry q back after a barrier.
-//   Phase 3 (<= 64 entries): wave 0 alone, one entry per lane, partners at lane
-//     distance 1, 2, 4, ... (no barriers).
-// Every round's sums are reduced with DPP row butterflies plus readlane of the
-// four row sums; a barrier separates a complete g_i from the read of r_i.
+// weight 0) so that every slice lies inside one pair. With mt virtual entries:
+//   Stage A (mt >= 1024, all 8 waves): thread t holds entries [t L, (t+1) L) of
+//     A and B in registers (L = mt / 512); while L >= 2 the pairs (2q, 2q+1)
+//     of a round lie in the slice, binding a variable moves no data, and only
+//     the three round sums cross threads (one barrier per round).
+//   Stage B (wave 0 alone, no barriers): the <= 512 remaining entries are
+//     re-sliced through LDS to L = mt / 64 entries per lane; rounds as in A.
+//   Stage C (wave 0, one entry per lane): partners at lane distance 1, 2, 4, ...
+// Round sums are carried as exact 96-bit integers while they cross lanes (DPP
+// row butterflies, then row broadcasts into lane 63) and reduced mod p once;
+// across waves they meet in LDS, and every wave completes g_i before it
+// applies r_i. The challenges are inputs and are staged in LDS at the start.
 // Multi-instance mode: instance b (= workgroup) uses A + b 2^n, B + b 2^n,
 // r + b n, rounds + 3 b n, finals + 2 b, claim0 + b.
 constexpr int ST = 512;     // tail threads
@@ -184,46 +185,109 @@ struct TailArgs {
   int32_t multi;
 };
 
-// Sum over the wave, returned in every lane (full wave active).
+// An exact sum of field values, w0 + 2^32 w1 + 2^64 w2 (below 2^96).
+struct S96 {
+  uint32_t w0, w1, w2;
+};
 
-// Workgroup sum of (g0, g1, g2); wave 0 lane 0 writes round i. Ends with a
-// barrier, so r_i may be read afterwards.
-__device__ __forceinline__ void block_round(uint64_t g0, uint64_t g1, uint64_t g2, uint64_t* red, fp_elem* rounds,
-                                            int i, fp_elem* claim0) {
+__device__ __forceinline__ S96 to96(uint64_t v) { return S96{(uint32_t)v, (uint32_t)(v >> 32), 0u}; }
+
+__device__ __forceinline__ S96 add96(S96 a, S96 b) {
+  unsigned int c0, c1, c2;
+  S96 r;
+  r.w0 = __builtin_addc(a.w0, b.w0, 0u, &c0);
+  r.w1 = __builtin_addc(a.w1, b.w1, c0, &c1);
+  r.w2 = __builtin_addc(a.w2, b.w2, c1, &c2);
+  return r;
+}
+
+// DPP move of all three words; lanes of rows outside RM (and lanes without a
+// source) read 0.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ S96 dpp96(S96 a) {
+  return S96{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w0, CTRL, RM, 0xF, false),
+             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w1, CTRL, RM, 0xF, false),
+             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w2, CTRL, RM, 0xF, false)};
+}
+
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// Sum over the 64 lanes (all active); the total lands in lane 63.
+__device__ __forceinline__ S96 wave_sum96(S96 v) {
+  v = add96(v, dpp96<fpi::DPP_XOR1>(v));
+  v = add96(v, dpp96<fpi::DPP_XOR2>(v));
+  v = add96(v, dpp96<fpi::DPP_HALF_MIRROR>(v));
+  v = add96(v, dpp96<fpi::DPP_MIRROR>(v));            // row sums in every lane
+  v = add96(v, dpp96<DPP_ROW_BCAST15, 0xA>(v));       // rows 1, 3 += rows 0, 2
+  v = add96(v, dpp96<DPP_ROW_BCAST31, 0xC>(v));       // rows 2, 3 += rows 0 + 1
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lane_value(S96 v, int lane) {
+  const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)v.w0, lane);
+  const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)v.w1, lane);
+  const uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)v.w2, lane);
+  return gl::reduce128(((uint64_t)w1 << 32) | w0, w2);
+}
+
+// Round sums of one wave (stages B and C): canonical g values in every lane.
+__device__ __forceinline__ void wave_round(uint64_t& g0, uint64_t& g1, uint64_t& g2) {
+  const S96 a = wave_sum96(to96(g0)), b = wave_sum96(to96(g1)), c = wave_sum96(to96(g2));
+  g0 = lane_value(a, 63);
+  g1 = lane_value(b, 63);
+  g2 = lane_value(c, 63);
+}
+
+// Round sums of the workgroup (stage A): each wave's total goes to LDS
+// (double-buffered by round parity), one barrier, and every wave adds the SW
+// wave totals itself. Canonical g values in every lane.
+__device__ __forceinline__ void block_round(uint64_t& g0, uint64_t& g1, uint64_t& g2, S96* red, int par) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  g0 = fpi::wave_total(g0);
-  g1 = fpi::wave_total(g1);
-  g2 = fpi::wave_total(g2);
-  if (lane == 0) {
-    red[3 * wave] = g0;
-    red[3 * wave + 1] = g1;
-    red[3 * wave + 2] = g2;
+  const S96 a = wave_sum96(to96(g0)), b = wave_sum96(to96(g1)), c = wave_sum96(to96(g2));
+  S96* slot = red + (par * SW) * 3;
+  if (lane == 63) {
+    slot[3 * wave] = a;
+    slot[3 * wave + 1] = b;
+    slot[3 * wave + 2] = c;
   }
   __syncthreads();
-  if (wave == 0) {
-    uint64_t s0 = 0, s1 = 0, s2 = 0;
-    if (lane < SW) { s0 = red[3 * lane]; s1 = red[3 * lane + 1]; s2 = red[3 * lane + 2]; }
-    // 8 values in lanes 0..7: two quad butterflies and a half-row mirror
-    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_XOR1>(s0));
-    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_XOR1>(s1));
-    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_XOR1>(s2));
-    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_XOR2>(s0));
-    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_XOR2>(s1));
-    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_XOR2>(s2));
-    s0 = gl::add(s0, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s0));
-    s1 = gl::add(s1, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s1));
-    s2 = gl::add(s2, fpi::dpp_u64<fpi::DPP_HALF_MIRROR>(s2));
-    if (lane == 0) {
-      rounds[3 * i] = s0; rounds[3 * i + 1] = s1; rounds[3 * i + 2] = s2;
-      if (i == 0 && claim0) claim0[0] = gl::add(s0, s1);
-    }
+  S96 x{0, 0, 0}, y{0, 0, 0}, z{0, 0, 0};
+  if (lane < SW) {
+    x = slot[3 * lane];
+    y = slot[3 * lane + 1];
+    z = slot[3 * lane + 2];
   }
-  __syncthreads();
+  // SW = 8 values in lanes 0..7: two quad butterflies and a half-row mirror
+  x = add96(x, dpp96<fpi::DPP_XOR1>(x));
+  y = add96(y, dpp96<fpi::DPP_XOR1>(y));
+  z = add96(z, dpp96<fpi::DPP_XOR1>(z));
+  x = add96(x, dpp96<fpi::DPP_XOR2>(x));
+  y = add96(y, dpp96<fpi::DPP_XOR2>(y));
+  z = add96(z, dpp96<fpi::DPP_XOR2>(z));
+  x = add96(x, dpp96<fpi::DPP_HALF_MIRROR>(x));
+  y = add96(y, dpp96<fpi::DPP_HALF_MIRROR>(y));
+  z = add96(z, dpp96<fpi::DPP_HALF_MIRROR>(z));
+  g0 = lane_value(x, 0);
+  g1 = lane_value(y, 0);
+  g2 = lane_value(z, 0);
+}
+
+__device__ __forceinline__ void emit_round(fp_elem* rounds, fp_elem* claim0, int i, uint64_t g0, uint64_t g1,
+                                           uint64_t g2) {
+  rounds[3 * i] = g0;
+  rounds[3 * i + 1] = g1;
+  rounds[3 * i + 2] = g2;
+  if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
+}
+
+__device__ __forceinline__ uint64_t bind(uint64_t x0, uint64_t x1, uint64_t r) {
+  return gl::add(x0, gl::mul(r, gl::sub(x1, x0)));
 }
 
 __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
   __shared__ uint64_t lA[ST], lB[ST];
-  __shared__ uint64_t red[3 * SW];
+  __shared__ S96 red[2 * SW * 3];
+  __shared__ uint64_t rl[FP_MAX_N];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int np = a.n_pairs;
   const fp_elem* r = a.r;
@@ -246,6 +310,7 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       uB[j] = a.user.B[j];
     }
   }
+  if (tid >= a.i0 && tid < a.n) rl[tid] = r[tid];
   int vp = 1;
   while (vp < np) vp <<= 1;
   int m = 1 << (a.n - a.i0);  // per-pair entries after the entry fold
@@ -259,16 +324,16 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
     if (a.i0 == 0) { x = uA[j][q]; y = uB[j][q]; return; }
     const fp_elem* A = (a.i0 == 1) ? uA[j] : a.src + (int64_t)j * mp;
     const fp_elem* B = (a.i0 == 1) ? uB[j] : a.src + (int64_t)(np + j) * mp;
-    const uint64_t x0 = A[2 * q], x1 = A[2 * q + 1], y0 = B[2 * q], y1 = B[2 * q + 1];
-    x = gl::add(x0, gl::mul(r_entry, gl::sub(x1, x0)));
-    y = gl::add(y0, gl::mul(r_entry, gl::sub(y1, y0)));
+    x = bind(A[2 * q], A[2 * q + 1], r_entry);
+    y = bind(B[2 * q], B[2 * q + 1], r_entry);
   };
   auto weight = [&](int j) -> uint64_t { return j < np ? (a.rho ? a.rho[j] : 1ull) : 0ull; };
   const bool weighted = (a.rho != nullptr) || (vp != np);
 
   int mt = vp * m;
+  int par = 0;
   if (mt >= 2 * ST) {
-    // ---- phase 1: register slices --------------------------------------
+    // ---- stage A: register slices over all waves --------------------------
     int L = mt / ST;
     const int e0 = tid * L;
     const int j = e0 / m;
@@ -284,17 +349,19 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       for (int q = 0; q < SLMAX / 2; ++q)
         if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
       if (weighted) { g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj); }
-      block_round(g0, g1, g2, red, rounds, i, claim0);
-      const uint64_t ri = r[i];
+      block_round(g0, g1, g2, red, par);
+      if (tid == 0) emit_round(rounds, claim0, i, g0, g1, g2);
+      const uint64_t ri = rl[i];
 #pragma unroll
       for (int q = 0; q < SLMAX / 2; ++q)
         if (2 * q < L) {
-          xa[q] = gl::add(xa[2 * q], gl::mul(ri, gl::sub(xa[2 * q + 1], xa[2 * q])));
-          xb[q] = gl::add(xb[2 * q], gl::mul(ri, gl::sub(xb[2 * q + 1], xb[2 * q])));
+          xa[q] = bind(xa[2 * q], xa[2 * q + 1], ri);
+          xb[q] = bind(xb[2 * q], xb[2 * q + 1], ri);
         }
       L >>= 1;
       m >>= 1;
       ++i;
+      par ^= 1;
     }
     lA[tid] = xa[0];
     lB[tid] = xb[0];
@@ -306,67 +373,67 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
     }
   }
   __syncthreads();
-
-  // ---- phase 2: LDS rounds, one pair per thread ---------------------------
-  while (mt > 64 && m > 1) {
-    const int h = mt >> 1;
-    const bool act = tid < h;
-    const int e = 2 * tid;
-    const int j = act ? e / m : 0;
-    uint64_t x0 = 0, x1 = 0, y0 = 0, y1 = 0, g0 = 0, g1 = 0, g2 = 0;
-    if (act) {
-      x0 = lA[e]; x1 = lA[e + 1]; y0 = lB[e]; y1 = lB[e + 1];
-      round_terms(x0, x1, y0, y1, g0, g1, g2);
-      if (weighted) {
-        const uint64_t wj = weight(j);
-        g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
-      }
-    }
-    block_round(g0, g1, g2, red, rounds, i, claim0);
-    const uint64_t ri = r[i];
-    if (act) {
-      x0 = gl::add(x0, gl::mul(ri, gl::sub(x1, x0)));
-      y0 = gl::add(y0, gl::mul(ri, gl::sub(y1, y0)));
-    }
-    __syncthreads();  // every read of this round's table is done
-    if (act) { lA[tid] = x0; lB[tid] = y0; }
-    __syncthreads();
-    mt = h;
-    m >>= 1;
-    ++i;
-  }
   if (wave != 0) return;
 
-  // ---- phase 3: wave 0, one entry per lane -------------------------------
-  const bool live = lane < mt;
-  uint64_t x = live ? lA[lane] : 0, y = live ? lB[lane] : 0;
+  // ---- stage B: wave 0, L = mt / 64 entries per lane ----------------------
+  constexpr int BL = ST / 64;
+  int L = mt >= 64 ? mt / 64 : 1;
+  const bool live = lane * L < mt;
+  const int jb = live ? (lane * L) / m : 0;
+  uint64_t xa[BL], xb[BL];
+#pragma unroll
+  for (int k = 0; k < BL; ++k) {
+    xa[k] = (k < L && live) ? lA[lane * L + k] : 0;
+    xb[k] = (k < L && live) ? lB[lane * L + k] : 0;
+  }
+  const uint64_t wb = live ? weight(jb) : 0;
+  while (L >= 2) {
+    uint64_t g0 = 0, g1 = 0, g2 = 0;
+#pragma unroll
+    for (int q = 0; q < BL / 2; ++q)
+      if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
+    if (weighted) { g0 = gl::mul(g0, wb); g1 = gl::mul(g1, wb); g2 = gl::mul(g2, wb); }
+    wave_round(g0, g1, g2);
+    if (lane == 0) emit_round(rounds, claim0, i, g0, g1, g2);
+    const uint64_t ri = rl[i];
+#pragma unroll
+    for (int q = 0; q < BL / 2; ++q)
+      if (2 * q < L) {
+        xa[q] = bind(xa[2 * q], xa[2 * q + 1], ri);
+        xb[q] = bind(xb[2 * q], xb[2 * q + 1], ri);
+      }
+    L >>= 1;
+    m >>= 1;
+    mt >>= 1;
+    ++i;
+  }
+
+  // ---- stage C: wave 0, one entry per lane --------------------------------
+  const bool on = lane < mt;
+  uint64_t x = on ? xa[0] : 0, y = on ? xb[0] : 0;
   const int m0 = m;
   const int jl = lane / m0;
+  const uint64_t wl = on ? weight(jl) : 0;
   for (int d = 1; d < m0; d <<= 1) {
     const uint64_t x1 = fpi::shfl_xor_u64(x, d);
     const uint64_t y1 = fpi::shfl_xor_u64(y, d);
-    const bool even = live && ((lane & (2 * d - 1)) == 0);
+    const bool even = on && ((lane & (2 * d - 1)) == 0);
     uint64_t g0 = 0, g1 = 0, g2 = 0;
     if (even) round_terms(x, x1, y, y1, g0, g1, g2);
     if (weighted) {
-      const uint64_t wj = even ? weight(jl) : 0;
+      const uint64_t wj = even ? wl : 0;
       g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
     }
-    g0 = fpi::wave_total(g0);
-    g1 = fpi::wave_total(g1);
-    g2 = fpi::wave_total(g2);
-    if (lane == 0) {
-      rounds[3 * i] = g0; rounds[3 * i + 1] = g1; rounds[3 * i + 2] = g2;
-      if (i == 0 && claim0) claim0[0] = gl::add(g0, g1);
-    }
-    const uint64_t ri = r[i];
+    wave_round(g0, g1, g2);
+    if (lane == 0) emit_round(rounds, claim0, i, g0, g1, g2);
+    const uint64_t ri = rl[i];
     if (even) {
-      x = gl::add(x, gl::mul(ri, gl::sub(x1, x)));
-      y = gl::add(y, gl::mul(ri, gl::sub(y1, y)));
+      x = bind(x, x1, ri);
+      y = bind(y, y1, ri);
     }
     ++i;
   }
-  if (live && (lane % m0) == 0 && jl < np) {
+  if (on && (lane % m0) == 0 && jl < np) {
     finals[2 * jl] = x;
     finals[2 * jl + 1] = y;
   }

@@ -7,8 +7,8 @@ claim about Z to claims about the committed activations and the weights. One
 
   witness  Z = X W^T, Y, R                     (fp_witness_linear[_grouped])
   eq       E_t = eq(r_t, .), E_o = eq(r_o, .)  (fp_eq_table_batched)
-  folds    x' = X~(. || r_t), w' = W~(. || r_o) (fp_fold_matrix_batched)
-  claim    c0 = Z~(r_o || r_t)                  (fp_claim_eval_batched)
+  folds    x' = X~(. || r_t), w' = W~(. || r_o) (fp_fold_claim_batched: the
+  claim    c0 = Z~(r_o || r_t)                   folds and the claims in one pass)
   rounds   sum-check over k on (x', w')         (fp_sumcheck_prove[_multi])
   merge    random linear combinations           (fp_combine_claims, fp_linear_combine)
 
@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (claim_eval_batched, combine_claims, eq_table_batched, fold_matrix_batched, gather_rows,
+from . import (combine_claims, eq_table_batched, fold_claim_batched, gather_rows,
                linear_combine, moe_plan, sumcheck_prove, sumcheck_prove_multi, to_field_tensor, field_numpy,
                witness_linear, witness_linear_grouped)
 
@@ -129,9 +129,9 @@ class SingleLayerProver(_Prover):
         return [
             ("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)),
             ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o])),
-            ("fold", lambda: fold_matrix_batched([(self.X, self.E_t, 1 << n, self.xf),
-                                                  (self.W, self.E_o, 1 << n, self.wf)])),
-            ("claim", lambda: claim_eval_batched([(self.Z, self.E_t, self.E_o, self.c0)])),
+            ("fold+claim", lambda: fold_claim_batched([(self.X, self.E_t, 1 << n, self.xf),
+                                                       (self.W, self.E_o, 1 << n, self.wf)],
+                                                      [(self.Z, self.E_t, self.E_o, self.c0)])),
             ("sumcheck", lambda: sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds,
                                                 finals=self.finals, claim0=self.claim0)),
         ]
@@ -212,13 +212,10 @@ class MultiMatmulProver(_Prover):
         eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
                          [self.E_t] + [d["E_o"] for d in self.mm])
 
-    def _fold(self):
+    def _fold_claim(self):
         jobs = [(M, self.E_t, cp, out) for (M, _, cp, out) in self.x_jobs]
         jobs += [(self.tens[d["m"].w], d["E_o"], 1 << d["n"], d["wf"]) for d in self.mm]
-        fold_matrix_batched(jobs)
-
-    def _claim(self):
-        claim_eval_batched([(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm])
+        fold_claim_batched(jobs, [(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm])
 
     def _sumcheck(self):
         if self.mode == "rlc_out":
@@ -235,7 +232,7 @@ class MultiMatmulProver(_Prover):
                        [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
 
     def phases(self):
-        ph = [("witness", self._witness), ("eq", self._eq), ("fold", self._fold), ("claim", self._claim),
+        ph = [("witness", self._witness), ("eq", self._eq), ("fold+claim", self._fold_claim),
               ("sumcheck", self._sumcheck)]
         if self.mode == "rlc_out":
             ph.append(("merge", self._merge))
@@ -355,8 +352,7 @@ class MoEBlockProver(_Prover):
     def phases(self):
         return [("group", self._group), ("witness", self._witness),
                 ("eq", lambda: eq_table_batched(self.eq_r, self.eq_E)),
-                ("fold", lambda: fold_matrix_batched(self.fold_jobs)),
-                ("claim", lambda: claim_eval_batched(self.claim_jobs)),
+                ("fold+claim", lambda: fold_claim_batched(self.fold_jobs, self.claim_jobs)),
                 ("sumcheck", self._sumcheck)]
 
     def results(self) -> dict:
