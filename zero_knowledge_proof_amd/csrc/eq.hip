@@ -1,11 +1,11 @@
 // eq.hip - eq-table expansion: E[k] = eq(r, k) = prod_j (k_j ? r_j : 1 - r_j).
 //
 // "How fast can FlashProve go", §2: a table's folded row is the weighted sum
-// of its rows; these are the weights. Each 256-entry block builds the table of
-// its low 8 variables by doubling in LDS (8 rounds, one multiply per entry per
-// round) and multiplies it by the product over the high variables, which is
-// the same for the whole block. Two multiplies per entry overall beyond the
-// doubling, instead of n in the product form.
+// of its rows; these are the weights. A workgroup writes 256 entries: the
+// challenges and their complements are staged in LDS once, each thread takes
+// the product over its entry's low 8 variables as a balanced tree (depth 3, no
+// barriers), and multiplies it by the product over the high variables, which
+// is the same for the whole workgroup.
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -25,34 +25,31 @@ struct EqList {
 
 __device__ __forceinline__ void eq_block(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E,
                                          int64_t blk) {
-  __shared__ uint64_t L[256];
+  __shared__ uint64_t f[2][FP_MAX_N];  // f[1][j] = r_j, f[0][j] = 1 - r_j
   const int tid = threadIdx.x;
   const int nl = n < 8 ? n : 8;
-  if (tid == 0) L[0] = 1;
+  if (tid < n) {
+    const uint64_t rj = r[tid];
+    f[1][tid] = rj;
+    f[0][tid] = gl::sub(1, rj);
+  }
   __syncthreads();
-  for (int j = 0; j < nl; ++j) {
-    const int h = 1 << j;
-    const uint64_t rj = r[j];
-    uint64_t v0 = 0, v1 = 0;
-    if (tid < h) {
-      const uint64_t e = L[tid];
-      v0 = gl::mul(e, gl::sub(1, rj));
-      v1 = gl::mul(e, rj);
-    }
-    __syncthreads();
-    if (tid < h) {
-      L[tid] = v0;
-      L[tid + h] = v1;
-    }
-    __syncthreads();
-  }
   const int64_t base = blk << 8;
-  uint64_t hp = 1;
-  for (int j = 8; j < n; ++j) {
-    const uint64_t rj = r[j];
-    hp = gl::mul(hp, ((base >> j) & 1) ? rj : gl::sub(1, rj));
-  }
-  if (tid < (1 << nl)) E[base + tid] = (n > 8) ? gl::mul(L[tid], hp) : L[tid];
+  // entry base + tid: the product over its low variables as a balanced tree
+  // (factors of absent variables are 1) ...
+  uint64_t lf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lf[j] = (j < nl) ? f[(tid >> j) & 1][j] : 1;
+  const uint64_t low = gl::mul(gl::mul(gl::mul(lf[0], lf[1]), gl::mul(lf[2], lf[3])),
+                               gl::mul(gl::mul(lf[4], lf[5]), gl::mul(lf[6], lf[7])));
+  // ... times the product over the high variables, the same for the whole
+  // block (four interleaved partial products keep the chains short)
+  uint64_t hpart[4] = {1, 1, 1, 1};
+#pragma unroll
+  for (int j = 8; j < FP_MAX_N; ++j)
+    if (j < n) hpart[j & 3] = gl::mul(hpart[j & 3], f[(base >> j) & 1][j]);
+  if (tid < (1 << nl))
+    E[base + tid] = (n > 8) ? gl::mul(low, gl::mul(gl::mul(hpart[0], hpart[1]), gl::mul(hpart[2], hpart[3]))) : low;
 }
 
 __global__ __launch_bounds__(256) void eq_kernel(EqList jl) {
