@@ -32,30 +32,34 @@ __device__ __forceinline__ uint64_t sub(uint64_t a, uint64_t b) {
 }
 
 // 128-bit value (hi:lo) reduced mod p. hi = h0 + 2^32 h1:
-// x = lo + 2^64 h0 + 2^96 h1 = lo + EPS*h0 - h1 (mod p).
+// x = lo + 2^64 h0 + 2^96 h1 = lo + EPS*h0 - h1 (mod p). The corrections take
+// the carry and borrow flags of the 64-bit adds; h0 * EPS = h0 2^32 - h0 is
+// formed with 32-bit subtracts rather than a multiply.
 __device__ __forceinline__ uint64_t reduce128(uint64_t lo, uint64_t hi) {
-  uint32_t h0 = (uint32_t)hi, h1 = (uint32_t)(hi >> 32);
-  uint64_t t = lo - h1;
-  t -= (lo < h1) ? EPS : 0;
-  uint64_t u = ((uint64_t)h0 << 32) - h0;  // h0 * (2^32 - 1) < 2^64
-  uint64_t s = t + u;
-  s += (s < t) ? EPS : 0;
-  return canon(s);
+  const uint32_t h0 = (uint32_t)hi, h1 = (uint32_t)(hi >> 32);
+  unsigned long long bor, carry, b2;
+  uint64_t t = __builtin_subcll(lo, (uint64_t)h1, 0ull, &bor);
+  t -= bor ? EPS : 0;  // lo - h1 + p after a borrow; t >= 2^64 - 2^32 then, so no new borrow
+  unsigned int b0;
+  const uint32_t ulo = __builtin_subc(0u, h0, 0u, &b0);
+  const uint64_t u = ((uint64_t)(h0 - b0) << 32) | ulo;  // h0 * (2^32 - 1)
+  uint64_t s = __builtin_addcll(t, u, 0ull, &carry);
+  s += carry ? EPS : 0;  // after a carry s < u < 2^64 - 2^32, so s + EPS fits
+  const uint64_t d = __builtin_subcll(s, P, 0ull, &b2);
+  return b2 ? s : d;
 }
 
+// Schoolbook product of the 32-bit halves; every partial sum below fits in
+// 64 bits (a0 b1 + (a0 b0 >> 32) <= (2^32 - 1) 2^32, likewise for the others),
+// so no carry has to be tracked.
 __device__ __forceinline__ uint64_t mul(uint64_t a, uint64_t b) {
-  uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
-  uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
-  uint64_t p00 = (uint64_t)a0 * b0;
-  uint64_t p01 = (uint64_t)a0 * b1;
-  uint64_t p10 = (uint64_t)a1 * b0;
-  uint64_t p11 = (uint64_t)a1 * b1;
-  // middle = p01 + p10 + (p00 >> 32) fits in 65 bits; keep its carry.
-  uint64_t mid = p01 + (p00 >> 32);          // < 2^64 (p01 <= (2^32-1)^2)
-  uint64_t mid2 = mid + p10;
-  uint64_t carry = (mid2 < mid) ? (1ull << 32) : 0;
-  uint64_t lo = (mid2 << 32) | (uint32_t)p00;
-  uint64_t hi = p11 + (mid2 >> 32) + carry;
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t t1 = (uint64_t)a0 * b1 + (p00 >> 32);
+  const uint64_t t2 = (uint64_t)a1 * b0 + (uint32_t)t1;
+  const uint64_t hi = (uint64_t)a1 * b1 + (t1 >> 32) + (t2 >> 32);
+  const uint64_t lo = (t2 << 32) | (uint32_t)p00;
   return reduce128(lo, hi);
 }
 

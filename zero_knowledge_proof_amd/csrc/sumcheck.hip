@@ -58,6 +58,47 @@ __device__ __forceinline__ void block_sum3(uint64_t& a, uint64_t& b, uint64_t& c
   __syncthreads();
 }
 
+// An exact sum of field values, w0 + 2^32 w1 + 2^64 w2 (below 2^96).
+struct S96 {
+  uint32_t w0, w1, w2;
+};
+
+__device__ __forceinline__ S96 to96(uint64_t v) { return S96{(uint32_t)v, (uint32_t)(v >> 32), 0u}; }
+
+__device__ __forceinline__ S96 add96(S96 a, S96 b) {
+  unsigned int c0, c1, c2;
+  S96 r;
+  r.w0 = __builtin_addc(a.w0, b.w0, 0u, &c0);
+  r.w1 = __builtin_addc(a.w1, b.w1, c0, &c1);
+  r.w2 = __builtin_addc(a.w2, b.w2, c1, &c2);
+  return r;
+}
+
+// DPP move of all three words; lanes of rows outside RM (and lanes without a
+// source) read 0.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ S96 dpp96(S96 a) {
+  return S96{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w0, CTRL, RM, 0xF, false),
+             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w1, CTRL, RM, 0xF, false),
+             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w2, CTRL, RM, 0xF, false)};
+}
+
+__device__ __forceinline__ uint64_t reduce96(S96 v) {
+  return gl::reduce128(((uint64_t)v.w1 << 32) | v.w0, v.w2);
+}
+
+// Terms of g(0), g(1), g(2) for one pair of entries, added exactly into 96-bit
+// sums. Returns the differences A1 - A0 and B1 - B0, which binding reuses:
+// A(r) = A0 + r (A1 - A0), and A at 2 is A1 + (A1 - A0).
+__device__ __forceinline__ void round_terms96(uint64_t a0, uint64_t a1, uint64_t b0, uint64_t b1, S96& g0, S96& g1,
+                                              S96& g2, uint64_t& da, uint64_t& db) {
+  da = gl::sub(a1, a0);
+  db = gl::sub(b1, b0);
+  g0 = add96(g0, to96(gl::mul(a0, b0)));
+  g1 = add96(g1, to96(gl::mul(a1, b1)));
+  g2 = add96(g2, to96(gl::mul(gl::add(a1, da), gl::add(b1, db))));
+}
+
 // Terms of g(0), g(1), g(2) for one pair of entries.
 __device__ __forceinline__ void round_terms(uint64_t a0, uint64_t a1, uint64_t b0, uint64_t b1, uint64_t& g0,
                                             uint64_t& g1, uint64_t& g2) {
@@ -185,31 +226,6 @@ struct TailArgs {
   int32_t multi;
 };
 
-// An exact sum of field values, w0 + 2^32 w1 + 2^64 w2 (below 2^96).
-struct S96 {
-  uint32_t w0, w1, w2;
-};
-
-__device__ __forceinline__ S96 to96(uint64_t v) { return S96{(uint32_t)v, (uint32_t)(v >> 32), 0u}; }
-
-__device__ __forceinline__ S96 add96(S96 a, S96 b) {
-  unsigned int c0, c1, c2;
-  S96 r;
-  r.w0 = __builtin_addc(a.w0, b.w0, 0u, &c0);
-  r.w1 = __builtin_addc(a.w1, b.w1, c0, &c1);
-  r.w2 = __builtin_addc(a.w2, b.w2, c1, &c2);
-  return r;
-}
-
-// DPP move of all three words; lanes of rows outside RM (and lanes without a
-// source) read 0.
-template <int CTRL, int RM = 0xF>
-__device__ __forceinline__ S96 dpp96(S96 a) {
-  return S96{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w0, CTRL, RM, 0xF, false),
-             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w1, CTRL, RM, 0xF, false),
-             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w2, CTRL, RM, 0xF, false)};
-}
-
 constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
 
 // Sum over the 64 lanes (all active); the total lands in lane 63.
@@ -231,8 +247,8 @@ __device__ __forceinline__ uint64_t lane_value(S96 v, int lane) {
 }
 
 // Round sums of one wave (stages B and C): canonical g values in every lane.
-__device__ __forceinline__ void wave_round(uint64_t& g0, uint64_t& g1, uint64_t& g2) {
-  const S96 a = wave_sum96(to96(g0)), b = wave_sum96(to96(g1)), c = wave_sum96(to96(g2));
+__device__ __forceinline__ void wave_round(S96 s0, S96 s1, S96 s2, uint64_t& g0, uint64_t& g1, uint64_t& g2) {
+  const S96 a = wave_sum96(s0), b = wave_sum96(s1), c = wave_sum96(s2);
   g0 = lane_value(a, 63);
   g1 = lane_value(b, 63);
   g2 = lane_value(c, 63);
@@ -241,9 +257,10 @@ __device__ __forceinline__ void wave_round(uint64_t& g0, uint64_t& g1, uint64_t&
 // Round sums of the workgroup (stage A): each wave's total goes to LDS
 // (double-buffered by round parity), one barrier, and every wave adds the SW
 // wave totals itself. Canonical g values in every lane.
-__device__ __forceinline__ void block_round(uint64_t& g0, uint64_t& g1, uint64_t& g2, S96* red, int par) {
+__device__ __forceinline__ void block_round(S96 s0, S96 s1, S96 s2, uint64_t& g0, uint64_t& g1, uint64_t& g2, S96* red,
+                                            int par) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const S96 a = wave_sum96(to96(g0)), b = wave_sum96(to96(g1)), c = wave_sum96(to96(g2));
+  const S96 a = wave_sum96(s0), b = wave_sum96(s1), c = wave_sum96(s2);
   S96* slot = red + (par * SW) * 3;
   if (lane == 63) {
     slot[3 * wave] = a;
@@ -282,6 +299,13 @@ __device__ __forceinline__ void emit_round(fp_elem* rounds, fp_elem* claim0, int
 
 __device__ __forceinline__ uint64_t bind(uint64_t x0, uint64_t x1, uint64_t r) {
   return gl::add(x0, gl::mul(r, gl::sub(x1, x0)));
+}
+
+// Weight three exact sums by a field element.
+__device__ __forceinline__ void weigh(S96& a, S96& b, S96& c, uint64_t w) {
+  a = to96(gl::mul(reduce96(a), w));
+  b = to96(gl::mul(reduce96(b), w));
+  c = to96(gl::mul(reduce96(c), w));
 }
 
 __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
@@ -344,19 +368,21 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
       if (k < L) load_entry(j, q0 + k, xa[k], xb[k]);
     const uint64_t wj = weight(j);
     while (L >= 2) {
-      uint64_t g0 = 0, g1 = 0, g2 = 0;
+      S96 s0{0, 0, 0}, s1{0, 0, 0}, s2{0, 0, 0};
 #pragma unroll
       for (int q = 0; q < SLMAX / 2; ++q)
-        if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
-      if (weighted) { g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj); }
-      block_round(g0, g1, g2, red, par);
+        if (2 * q < L)  // the odd entry becomes the pair's difference
+          round_terms96(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], s0, s1, s2, xa[2 * q + 1], xb[2 * q + 1]);
+      if (weighted) weigh(s0, s1, s2, wj);
+      uint64_t g0, g1, g2;
+      block_round(s0, s1, s2, g0, g1, g2, red, par);
       if (tid == 0) emit_round(rounds, claim0, i, g0, g1, g2);
       const uint64_t ri = rl[i];
 #pragma unroll
       for (int q = 0; q < SLMAX / 2; ++q)
         if (2 * q < L) {
-          xa[q] = bind(xa[2 * q], xa[2 * q + 1], ri);
-          xb[q] = bind(xb[2 * q], xb[2 * q + 1], ri);
+          xa[q] = gl::add(xa[2 * q], gl::mul(ri, xa[2 * q + 1]));
+          xb[q] = gl::add(xb[2 * q], gl::mul(ri, xb[2 * q + 1]));
         }
       L >>= 1;
       m >>= 1;
@@ -388,19 +414,21 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
   }
   const uint64_t wb = live ? weight(jb) : 0;
   while (L >= 2) {
-    uint64_t g0 = 0, g1 = 0, g2 = 0;
+    S96 s0{0, 0, 0}, s1{0, 0, 0}, s2{0, 0, 0};
 #pragma unroll
     for (int q = 0; q < BL / 2; ++q)
-      if (2 * q < L) round_terms(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], g0, g1, g2);
-    if (weighted) { g0 = gl::mul(g0, wb); g1 = gl::mul(g1, wb); g2 = gl::mul(g2, wb); }
-    wave_round(g0, g1, g2);
+      if (2 * q < L)
+        round_terms96(xa[2 * q], xa[2 * q + 1], xb[2 * q], xb[2 * q + 1], s0, s1, s2, xa[2 * q + 1], xb[2 * q + 1]);
+    if (weighted) weigh(s0, s1, s2, wb);
+    uint64_t g0, g1, g2;
+    wave_round(s0, s1, s2, g0, g1, g2);
     if (lane == 0) emit_round(rounds, claim0, i, g0, g1, g2);
     const uint64_t ri = rl[i];
 #pragma unroll
     for (int q = 0; q < BL / 2; ++q)
       if (2 * q < L) {
-        xa[q] = bind(xa[2 * q], xa[2 * q + 1], ri);
-        xb[q] = bind(xb[2 * q], xb[2 * q + 1], ri);
+        xa[q] = gl::add(xa[2 * q], gl::mul(ri, xa[2 * q + 1]));
+        xb[q] = gl::add(xb[2 * q], gl::mul(ri, xb[2 * q + 1]));
       }
     L >>= 1;
     m >>= 1;
@@ -418,18 +446,17 @@ __global__ __launch_bounds__(ST) void sc_tail_kernel(TailArgs a) {
     const uint64_t x1 = fpi::shfl_xor_u64(x, d);
     const uint64_t y1 = fpi::shfl_xor_u64(y, d);
     const bool even = on && ((lane & (2 * d - 1)) == 0);
-    uint64_t g0 = 0, g1 = 0, g2 = 0;
-    if (even) round_terms(x, x1, y, y1, g0, g1, g2);
-    if (weighted) {
-      const uint64_t wj = even ? wl : 0;
-      g0 = gl::mul(g0, wj); g1 = gl::mul(g1, wj); g2 = gl::mul(g2, wj);
-    }
-    wave_round(g0, g1, g2);
+    S96 s0{0, 0, 0}, s1{0, 0, 0}, s2{0, 0, 0};
+    uint64_t dx = 0, dy = 0;
+    if (even) round_terms96(x, x1, y, y1, s0, s1, s2, dx, dy);
+    if (weighted) weigh(s0, s1, s2, even ? wl : 0);
+    uint64_t g0, g1, g2;
+    wave_round(s0, s1, s2, g0, g1, g2);
     if (lane == 0) emit_round(rounds, claim0, i, g0, g1, g2);
     const uint64_t ri = rl[i];
     if (even) {
-      x = bind(x, x1, ri);
-      y = bind(y, y1, ri);
+      x = gl::add(x, gl::mul(ri, dx));
+      y = gl::add(y, gl::mul(ri, dy));
     }
     ++i;
   }
