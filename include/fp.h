@@ -207,6 +207,23 @@ int fp_sumcheck_prove(int32_t n_pairs, const fp_elem* const* A, const fp_elem* c
                       size_t ws_bytes, hipStream_t stream);
 size_t fp_sumcheck_workspace(int32_t n_pairs, int32_t n);
 
+/* The witness of one linear layer (exactly fp_witness_linear(X, ..., R)) and,
+ * in the same launch, the sum-check of another claim (exactly
+ * fp_sumcheck_prove(n_pairs, A, B, rho, n, r, rounds, finals, claim0)). For a
+ * stream of layer proofs: the sum-check of proof k, a chain of dependent
+ * rounds that keeps one compute unit busy, runs beside the GEMM of proof k+1,
+ * which has no data in common with it ("How fast can FlashProve go", §2: the
+ * witness of every layer, then each matmul's sum-check). The sum-check must fit
+ * one workgroup: VP * 2^n <= 4096 (8192 when T > 32 and the output has at
+ * least 256 tiles of 256 x 256), VP = n_pairs rounded up to a power of two;
+ * FP_ESHAPE otherwise. The sum-check tables must not be written by the
+ * witness (they are read while it runs). No workspace. */
+int fp_witness_linear_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T,
+                                    int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R,
+                                    int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B,
+                                    const fp_elem* rho, int32_t n, const fp_elem* r, fp_elem* rounds,
+                                    fp_elem* finals, fp_elem* claim0, hipStream_t stream);
+
 /* n_inst independent single-pair sum-checks of 2^n entries in one launch
  * (one MoE expert's claim each). A, B: device [n_inst][2^n]; r: [n_inst][n];
  * rounds: [n_inst][n][3]; finals: [n_inst][2]; claim0: [n_inst] or NULL.

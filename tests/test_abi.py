@@ -54,6 +54,13 @@ def test_argument_errors_without_gpu():
     ro = (ctypes.c_int32 * 3)(1, 2, 3)
     wp = (ctypes.c_void_p * 2)(16, 16)
     assert L.fp_witness_linear_grouped(dummy, 16, wp, 16, ro, 2, 16, 16, 8, None, dummy, dummy, None) == 1
+    # witness + sum-check in one launch: pair count, and tables too large for one workgroup
+    pa = (ctypes.c_void_p * 1)(16)
+    assert L.fp_witness_linear_with_sumcheck(None, 16, None, 16, 0, 16, 4, 8, None, None, None, 0, pa, pa, None, 4,
+                                             dummy, dummy, dummy, None, None) == 1
+    assert L.fp_witness_linear_with_sumcheck(None, 16, None, 16, 0, 16, 4, 8, None, None, None, 1, pa, pa, None, 13,
+                                             dummy, dummy, dummy, None, None) == 2
+    assert b"exceed one" in L.fp_last_error()
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)

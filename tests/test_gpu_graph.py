@@ -42,3 +42,29 @@ def test_graph_replays_match_eager(fp, cid, shape):
         _same(prover.results(), want, "replay%d" % rep)
         prover.run()              # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cid,shape", [(1, {}), (2, dict(T=100, d_in=1000, d_out=700))])
+def test_pipelined_graph_replays(fp, cid, shape):
+    """Pipelined proofs recorded as a graph: replays followed by the drain give
+    the eager pipelined outputs, with outputs cleared between replays."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch, pipelined=True)
+    prover.run()
+    prover.drain()
+    torch.cuda.synchronize()
+    want = prover.results()
+    prover.capture()
+    for rep in range(3):
+        for t in prover.output_tensors():
+            t.zero_()
+        torch.cuda.synchronize()
+        prover.replay()           # witness + sum-check of the zeroed tables
+        prover.replay()           # witness + sum-check of the previous replay's tables
+        prover.drain()
+        torch.cuda.synchronize()
+        _same(prover.results(), want, "replay%d" % rep)
+        prover.run()              # eager work between replays
+        torch.cuda.synchronize()

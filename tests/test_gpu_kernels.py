@@ -213,6 +213,46 @@ def test_sumcheck_multi(fp, n_inst, n):
         assert np.array_equal(R[i], wr) and np.array_equal(F[i], wf[0]) and int(C[i]) == wc
 
 
+
+@pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 300, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
+                                             (0, 64, 64, 2, 10), (40, 96, 0, 1, 5)])
+def test_witness_with_sumcheck(fp, T, d_in, d_out, k, n):
+    """One launch: a witness and an unrelated sum-check, each against the oracle."""
+    rng = _rng(500 + T + n + k)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    As = [_field(rng, 1 << n, False) for _ in range(k)]
+    Bs = [_field(rng, 1 << n, False) for _ in range(k)]
+    r = _field(rng, n, specials=(n >= 4))
+    rho = _field(rng, k, False) if k > 1 else None
+    Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda")
+    Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    _, (rounds, finals, c0) = fp.witness_linear_with_sumcheck(
+        _dev(X), _dev(W), 8, Z, Y, R, [fp.to_field_tensor(a) for a in As], [fp.to_field_tensor(b) for b in Bs],
+        fp.to_field_tensor(r), rho=None if rho is None else fp.to_field_tensor(rho))
+    torch.cuda.synchronize()
+    if T and d_out:
+        wz, wy, wr = O.witness(X, W, 8)
+        assert np.array_equal(Z.cpu().numpy(), wz)
+        assert np.array_equal(Y.cpu().numpy(), wy)
+        assert np.array_equal(R.cpu().numpy(), wr)
+    grs, gfs, gc = O.sumcheck(As, Bs, r, rho=rho)
+    assert np.array_equal(fp.field_numpy(rounds), grs)
+    assert np.array_equal(fp.field_numpy(finals), gfs)
+    assert int(fp.field_numpy(c0)[0]) == gc
+
+
+def test_witness_with_sumcheck_too_large(fp):
+    X = torch.zeros((16, 64), dtype=torch.int8, device="cuda")
+    W = torch.zeros((64, 64), dtype=torch.int8, device="cuda")
+    A = torch.zeros(1 << 13, dtype=torch.int64, device="cuda")
+    r = torch.zeros(13, dtype=torch.int64, device="cuda")
+    Z = torch.empty((16, 64), dtype=torch.int32, device="cuda")
+    Y = torch.empty((16, 64), dtype=torch.int8, device="cuda")
+    with pytest.raises(fp.FPError, match="exceed one"):
+        fp.witness_linear_with_sumcheck(X, W, 8, Z, Y, Y.clone(), [A], [A], r)
+
+
 def test_combine_and_linear_combine(fp):
     rng = _rng(13)
     g = [_field(rng, 3, False) for _ in range(3)]

@@ -91,6 +91,26 @@ def test_layer_moe_reduced(fp):
         _cmp_matmul(got[e]["down"], want[e]["down"])
 
 
+
+@pytest.mark.parametrize("cid,shape", [(1, {}), (2, dict(T=100, d_in=1000, d_out=700))])
+def test_layer_pipelined(fp, cid, shape):
+    """Consecutive proofs overlapped (each run launches this proof's witness
+    with the previous proof's sum-check): after two runs and the drain, every
+    output is the oracle's."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch, pipelined=True)
+    prover.run()
+    prover.run()
+    prover.drain()
+    torch.cuda.synchronize()
+    got = prover.results()
+    want = O.prove_config(cfg, inp, ch)["main" if cid == 1 else "up"]
+    _cmp_matmul(got, want)
+    assert got["c0"] == got["claim0"]
+
+
 # ------------------------------------------------------- full-size checks --
 def _sampled_witness(X, W, got, s, n=2048, seed=0):
     rng = np.random.default_rng(seed)

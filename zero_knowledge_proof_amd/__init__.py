@@ -25,6 +25,7 @@ EXPORTS = [
     "fp_mle_eval", "fp_mle_eval_workspace", "fp_sumcheck_prove", "fp_sumcheck_workspace",
     "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
     "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
+    "fp_witness_linear_with_sumcheck",
 ]
 
 _lib = None
@@ -80,6 +81,8 @@ def lib():
             "fp_linear_combine": (ctypes.c_int, [i32, vp, vp, vp, vp]),
             "fp_fold_claim_batched": (ctypes.c_int, [i32, i32, vp, i32, i32, vp, vp, sz, vp]),
             "fp_fold_claim_batched_workspace": (sz, [i32, i32, vp, i32, i32, vp]),
+            "fp_witness_linear_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp,
+                                                               i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -154,7 +157,8 @@ def field_numpy(t: torch.Tensor):
 def witness_linear(X, W, s: int, Z=None, Y=None, R=None, with_z: bool = True):
     T, d_in = X.shape
     d_out = W.shape[0]
-    assert X.dtype == torch.int8 and W.dtype == torch.int8 and X.stride(1) == 1 and W.stride(1) == 1
+    assert X.dtype == torch.int8 and W.dtype == torch.int8
+    assert (X.numel() == 0 or X.stride(1) == 1) and (W.numel() == 0 or W.stride(1) == 1), "rows must be contiguous"
     if with_z and Z is None:
         Z = torch.empty((T, d_out), dtype=torch.int32, device=X.device)
     Y = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if Y is None else Y
@@ -163,6 +167,27 @@ def witness_linear(X, W, s: int, Z=None, Y=None, R=None, with_z: bool = True):
                                    _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), _stream()),
            "fp_witness_linear")
     return Z, Y, R
+
+
+def witness_linear_with_sumcheck(X, W, s: int, Z, Y, R, As, Bs, r, rho=None, rounds=None, finals=None, claim0=None):
+    """witness_linear(X, W, s, Z, Y, R) and sumcheck_prove(As, Bs, r, rho, ...) in one launch."""
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    assert X.dtype == torch.int8 and W.dtype == torch.int8
+    assert (X.numel() == 0 or X.stride(1) == 1) and (W.numel() == 0 or W.stride(1) == 1), "rows must be contiguous"
+    k = len(As)
+    n = r.numel()
+    dev = r.device
+    rounds = torch.empty((n, 3), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty((k, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    claim0 = torch.empty(1, dtype=torch.int64, device=dev) if claim0 is None else claim0
+    pa = (ctypes.c_void_p * k)(*[a.data_ptr() for a in As])
+    pb = (ctypes.c_void_p * k)(*[b.data_ptr() for b in Bs])
+    _check(lib().fp_witness_linear_with_sumcheck(_ptr(X), _ld(X), _ptr(W), _ld(W), T, d_in, d_out, s, _ptr(Z),
+                                                 _ptr(Y), _ptr(R), k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds),
+                                                 _ptr(finals), _ptr(claim0), _stream()),
+           "fp_witness_linear_with_sumcheck")
+    return (Z, Y, R), (rounds, finals, claim0)
 
 
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):

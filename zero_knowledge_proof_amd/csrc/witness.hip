@@ -27,6 +27,7 @@
 // the 8 XCDs round-robin) works on a contiguous run of tiles; tokens vary
 // fastest, so one W panel is shared by the XCD's tiles in its L2.
 #include "common.hpp"
+#include "sc_tail.hpp"
 
 namespace {
 
@@ -84,8 +85,17 @@ __device__ __forceinline__ void rescale(int32_t z, int s, int32_t lowmask, uint3
   r = (uint32_t)(uint8_t)(int8_t)rr;
 }
 
-template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
-__global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
+// LDS of one GEMM workgroup: double-buffered W and X tiles.
+template <int BO, int BT, int BK>
+struct WitLds {
+  __align__(16) int8_t sA[2][BO * (BK + 16)];  // W rows
+  __align__(16) int8_t sB[2][BT * (BK + 16)];  // X rows
+};
+
+// Tile `bid` of `nblocks` GEMM workgroups.
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF, int BK>
+__device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& gt, int bid, int nblocks,
+                                             WitLds<BO, BT, BK>& sh) {
   constexpr int PITCH = BK + 16;  // LDS row pitch: 16 consecutive rows start in distinct bank groups
   constexpr int CPR = BK / 16;    // 16-byte chunks per row
   constexpr int WAVES_T = BT / WT;
@@ -94,10 +104,10 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
   constexpr int NCA = BO * CPR, NCB = BT * CPR;  // 16-byte chunks per K step
   constexpr int CA = (NCA + NT - 1) / NT;
   constexpr int CB = (NCB + NT - 1) / NT;
-  __shared__ __align__(16) int8_t sA[2][BO * PITCH];  // W rows
-  __shared__ __align__(16) int8_t sB[2][BT * PITCH];  // X rows
+  auto& sA = sh.sA;
+  auto& sB = sh.sB;
 
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = xcd_tile(bid, nblocks);
   const int tt = tile % a.tiles_t;
   const int to = tile / a.tiles_t;
 
@@ -293,6 +303,28 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(Wit
   }
 }
 
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
+__global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
+  __shared__ WitLds<BO, BT, BK> sh;
+  witness_body<BO, BT, WO, WT, GROUPED, PF, BK>(a, gt, blockIdx.x, gridDim.x, sh);
+}
+
+// The GEMM together with sum-check tails: workgroups [0, n_tail) each run one
+// tail instance (they are dispatched first, so the latency-bound tail overlaps
+// the GEMM), the rest are GEMM tiles. The tail's LDS is carved from the GEMM's.
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
+__global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(WitArgs a, GroupTab gt,
+                                                                               sct::TailArgs ta, int n_tail) {
+  constexpr int NT = (BO / WO) * (BT / WT) * 64;
+  __shared__ WitLds<BO, BT, BK> sh;
+  static_assert(sizeof(sct::TailLds<NT>) <= sizeof(WitLds<BO, BT, BK>), "tail LDS must fit the GEMM's");
+  if ((int)blockIdx.x < n_tail) {
+    sct::tail_body<NT>(ta, blockIdx.x, *reinterpret_cast<sct::TailLds<NT>*>(&sh));
+    return;
+  }
+  witness_body<BO, BT, WO, WT, GROUPED, PF, BK>(a, gt, blockIdx.x - n_tail, gridDim.x - n_tail, sh);
+}
+
 // Tile configurations (BO, BT, WO, WT, grouped, prefetch distance, K step),
 // chosen from measurements on the up-projection and layer shapes:
 //   XL: 256x256 outputs x tokens, 8 waves of 64x128, K step 64
@@ -313,6 +345,25 @@ int launch(WitArgs a, const GroupTab& gt, hipStream_t st) {
   hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED, PF, BK>), dim3((unsigned)blocks),
                      dim3((BO / WO) * (BT / WT) * 64), 0, st, a, gt);
   return fpi::check_launch("witness_kernel");
+}
+
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
+int launch_with_tail(WitArgs a, const GroupTab& gt, const sct::TailArgs& ta, int n_tail, hipStream_t st) {
+  constexpr int NT = (BO / WO) * (BT / WT) * 64;
+  if (!GROUPED) a.tiles_t = (a.T + BT - 1) / BT;
+  a.tiles_o = (a.N + BO - 1) / BO;
+  const int64_t tiles = (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o : 0;
+  if (tiles + n_tail > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
+  hipLaunchKernelGGL((witness_sc_kernel<BO, BT, WO, WT, GROUPED, PF, BK>), dim3((unsigned)(tiles + n_tail)), dim3(NT),
+                     0, st, a, gt, ta, n_tail);
+  return fpi::check_launch("witness_sc_kernel");
+}
+
+// Threads of the workgroups the witness launch uses for a shape.
+int witness_threads(int32_t T, int32_t d_out) {
+  const int64_t xl_tiles = (int64_t)((d_out + 255) / 256) * ((T + 255) / 256);
+  if (T <= 32) return 256;
+  return xl_tiles >= 256 ? 512 : 256;
 }
 
 int validate(const char* fn, int64_t ldx, int64_t ldw, int32_t T, int32_t d_in, int32_t d_out, int32_t s,
@@ -401,4 +452,47 @@ extern "C" int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int
     if (rc) return rc;
   }
   return fpi::ok();
+}
+
+extern "C" int fp_witness_linear_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T,
+                                               int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
+                                               int8_t* R, int32_t n_pairs, const fp_elem* const* A,
+                                               const fp_elem* const* B, const fp_elem* rho, int32_t n,
+                                               const fp_elem* r, fp_elem* rounds, fp_elem* finals, fp_elem* claim0,
+                                               hipStream_t stream) {
+  const char* fn = "fp_witness_linear_with_sumcheck";
+  int rc = validate(fn, ldx, ldw, T, d_in, d_out, s, Y, R);
+  if (rc) return rc;
+  if (T > 0 && d_out > 0 && d_in > 0 && (!X || !W)) return fpi::fail(FP_EARG, "%s: null X or W", fn);
+  if (n_pairs < 1 || n_pairs > sct::SC_MAX_PAIRS)
+    return fpi::fail(FP_EARG, "%s: n_pairs=%d outside [1, %d]", fn, n_pairs, sct::SC_MAX_PAIRS);
+  if (n < 1 || n > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [1, %d]", fn, n, FP_MAX_N);
+  if (!A || !B || !r || !rounds || !finals) return fpi::fail(FP_EARG, "%s: null sum-check pointer", fn);
+  for (int j = 0; j < n_pairs; ++j)
+    if (!A[j] || !B[j]) return fpi::fail(FP_EARG, "%s: null table %d", fn, j);
+  int vp = 1;
+  while (vp < n_pairs) vp <<= 1;
+  const int nt = witness_threads(T, d_out);
+  if (((int64_t)vp << n) > (int64_t)nt * sct::SLMAX)
+    return fpi::fail(FP_ESHAPE, "%s: %d x 2^%d table entries exceed one %d-thread workgroup (%d)", fn, vp, n, nt,
+                     nt * sct::SLMAX);
+  WitArgs a{};
+  a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
+  a.T = T; a.N = d_out; a.K = d_in; a.s = s;
+  a.Z = Z; a.Y = Y; a.R = R;
+  vec_flags(a);
+  a.vecW = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
+  sct::TailArgs ta{};
+  for (int j = 0; j < n_pairs; ++j) {
+    ta.user.A[j] = A[j];
+    ta.user.B[j] = B[j];
+  }
+  ta.rho = rho; ta.r = r; ta.rounds = rounds; ta.finals = finals; ta.claim0 = claim0;
+  ta.i0 = 0; ta.n = n; ta.n_pairs = n_pairs; ta.nprev = 0; ta.multi = 0;
+  GroupTab gt{};
+  const int64_t xl_tiles = (int64_t)((d_out + 255) / 256) * ((T + 255) / 256);
+  if (T <= 32) rc = launch_with_tail<WIT_S>(a, gt, ta, 1, stream);
+  else if (xl_tiles >= 256) rc = launch_with_tail<WIT_XL>(a, gt, ta, 1, stream);
+  else rc = launch_with_tail<WIT_M>(a, gt, ta, 1, stream);
+  return rc ? rc : fpi::ok();
 }

@@ -24,7 +24,7 @@ import torch
 
 from . import (combine_claims, eq_table_batched, fold_claim_batched, gather_rows,
                linear_combine, moe_plan, sumcheck_prove, sumcheck_prove_multi, to_field_tensor, field_numpy,
-               witness_linear, witness_linear_grouped)
+               witness_linear, witness_linear_grouped, witness_linear_with_sumcheck)
 
 
 def _nomark(name):
@@ -73,6 +73,9 @@ class _Prover:
     def replay(self):
         self.graph.replay()
 
+    def drain(self):
+        """Finish work a pipelined prover leaves for the next run (none here)."""
+
     # tensors the step writes (for tests that clear them between runs)
     OUTPUTS = ()
 
@@ -101,13 +104,26 @@ class _Challenges:
         return self.views[k]
 
 
+# tables of at most this many entries fit the sum-check workgroup that runs
+# inside a witness launch
+OVERLAP_ENTRIES = 4096
+
+
 class SingleLayerProver(_Prover):
-    """One linear map: witness, claim and sum-check over d_in."""
+    """One linear map: witness, claim and sum-check over d_in.
+
+    pipelined: for a stream of proofs of the layer. ``run()`` then launches the
+    witness of this proof together with the sum-check of the previous one
+    (fp_witness_linear_with_sumcheck), followed by this proof's eq tables,
+    folds and claim; ``drain()`` runs the sum-check of the last proof. The
+    outputs of a proof are complete after the next ``run()`` or ``drain()``."""
 
     OUTPUTS = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0")
 
-    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None, with_z: bool = True):
+    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None, with_z: bool = True,
+                 pipelined: bool = False):
         dev = dev or torch.device("cuda")
+        self.pipelined = pipelined
         self.s = s
         self.X, self.W = _i8(X, dev), _i8(W, dev)
         T, d_in = X.shape
@@ -118,23 +134,39 @@ class SingleLayerProver(_Prover):
         self.Y = torch.empty((T, d_out), dtype=torch.int8, device=dev)
         self.R = torch.empty((T, d_out), dtype=torch.int8, device=dev)
         self.E_t, self.E_o = _f(1 << log2ceil(T), dev), _f(1 << log2ceil(d_out), dev)
-        self.xf, self.wf = _f(1 << self.n, dev), _f(1 << self.n, dev)
+        if pipelined and (1 << self.n) > OVERLAP_ENTRIES:
+            raise ValueError("pipelined proofs need d_in <= %d" % OVERLAP_ENTRIES)
+        # zeros: the first pipelined run proves the all-zero claim of no layer
+        self.xf = torch.zeros(1 << self.n, dtype=torch.int64, device=dev)
+        self.wf = torch.zeros(1 << self.n, dtype=torch.int64, device=dev)
         self.c0 = _f(1, dev)
         self.rounds = torch.empty((self.n, 3), dtype=torch.int64, device=dev)
         self.finals = torch.empty((1, 2), dtype=torch.int64, device=dev)
         self.claim0 = _f(1, dev)
 
+    def _sumcheck(self):
+        sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                       claim0=self.claim0)
+
+    def _witness_and_previous_sumcheck(self):
+        witness_linear_with_sumcheck(self.X, self.W, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
+                                     self.ch["rounds"], rounds=self.rounds, finals=self.finals, claim0=self.claim0)
+
+    def drain(self):
+        """Pipelined mode: the sum-check of the last proof."""
+        if self.pipelined:
+            self._sumcheck()
+
     def phases(self):
         n = self.n
-        return [
-            ("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)),
-            ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o])),
-            ("fold+claim", lambda: fold_claim_batched([(self.X, self.E_t, 1 << n, self.xf),
-                                                       (self.W, self.E_o, 1 << n, self.wf)],
-                                                      [(self.Z, self.E_t, self.E_o, self.c0)])),
-            ("sumcheck", lambda: sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds,
-                                                finals=self.finals, claim0=self.claim0)),
-        ]
+        fold = ("fold+claim", lambda: fold_claim_batched([(self.X, self.E_t, 1 << n, self.xf),
+                                                          (self.W, self.E_o, 1 << n, self.wf)],
+                                                         [(self.Z, self.E_t, self.E_o, self.c0)]))
+        eq = ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o]))
+        if self.pipelined:
+            return [("witness+sumcheck", self._witness_and_previous_sumcheck), eq, fold]
+        return [("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)), eq, fold,
+                ("sumcheck", self._sumcheck)]
 
     def results(self) -> dict:
         return {"Z": self.Z.cpu().numpy(), "Y": self.Y.cpu().numpy(), "R": self.R.cpu().numpy(),
@@ -376,10 +408,18 @@ class MoEBlockProver(_Prover):
         return out
 
 
-def make_prover(cfg, inp: dict, ch: dict, dev=None):
+def can_pipeline(cfg) -> bool:
+    """Whether proofs of this workload can overlap (one sum-check that fits the
+    workgroup inside the witness launch)."""
+    return cfg.kind == "single" and (1 << cfg.matmuls[0].n) <= OVERLAP_ENTRIES
+
+
+def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False):
     if cfg.kind == "single":
         m = cfg.matmuls[0]
-        return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev)
+        return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, pipelined=pipelined)
+    if pipelined:
+        raise ValueError("pipelined proofs are implemented for single-matmul layers")
     if cfg.kind in ("rlc_out", "batched"):
         return MultiMatmulProver(cfg, inp, ch, dev)
     if cfg.kind == "moe":
