@@ -69,6 +69,33 @@ def kernel_work(cfg, name: str, prover) -> tuple:
     return 0, 0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "witness_sc_T512_traffic.txt")
+
+
+def measured_traffic(cfg, kernel_phase: str):
+    """HBM bytes per launch of the dominant launch, from the committed counter
+    summary, or None when there is none for this workload and launch or its
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE) or kernel_phase != "witness+sumcheck":
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    if int(kv.get("workload", -1)) != cfg.cid:
+        return None
+    h = hashlib.sha256()
+    for src in kv["sources"].split():
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != kv["sha256"]:
+        return None
+    return int(round((float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                      float(kv["write_kib"]) * float(kv["write_scale"])) * 1024))
+
+
 def cpu_baseline(cfg, inp, ch) -> dict:
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -172,7 +199,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": b / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg, dom)  # HBM bytes per launch (counters), None if stale
+    roof["algorithmic_bytes"] = b
     roof["kernel"] = dom
     extras = {}
     for k, v in phase_ms.items():
