@@ -56,13 +56,12 @@ def test_pipelined_graph_replays(fp, cid, shape):
     prover.drain()
     torch.cuda.synchronize()
     want = prover.results()
-    prover.capture()
+    prover.capture(steps=2)       # two consecutive proofs per graph
     for rep in range(3):
         for t in prover.output_tensors():
             t.zero_()
         torch.cuda.synchronize()
-        prover.replay()           # witness + sum-check of the zeroed tables
-        prover.replay()           # witness + sum-check of the previous replay's tables
+        prover.replay()           # proofs 1 and 2 (proof 1's sum-check runs inside proof 2's witness launch)
         prover.drain()
         torch.cuda.synchronize()
         _same(prover.results(), want, "replay%d" % rep)

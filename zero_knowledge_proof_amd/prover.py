@@ -58,16 +58,19 @@ class _Prover:
             fn()
         mark("end")
 
-    def capture(self):
-        """Record one whole step into a HIP graph (run once eagerly first so
-        that every workspace has its final size)."""
+    def capture(self, steps: int = 1):
+        """Record `steps` consecutive whole steps into one HIP graph (run once
+        eagerly first so that every workspace has its final size). Several
+        steps per graph spread the fixed cost of a graph launch."""
         self.run()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.run()
+            for _ in range(steps):
+                self.run()
         torch.cuda.synchronize()
         self.graph = g
+        self.graph_steps = steps
         return g
 
     def replay(self):
