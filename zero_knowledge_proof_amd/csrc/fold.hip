@@ -35,7 +35,7 @@ constexpr int FCT = 64;         // column threads (one wave wide)
 constexpr int FRG = FT / FCT;   // row groups (waves)
 constexpr int FCOLS = FCT * 4;  // columns per workgroup
 constexpr int FMAX_CHUNK = 1024;
-constexpr int INLINE = 12;      // jobs carried in one launch's arguments
+constexpr int INLINE = 32;      // jobs carried in one launch's arguments (kernel arguments <= 4 KB)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct FoldJob {
@@ -57,6 +57,19 @@ struct JobList {
   FoldJob j[INLINE];
   int32_t count;
 };
+static_assert(sizeof(JobList) <= 4096, "a job list travels in the kernel arguments");
+
+// The last job whose first workgroup is <= b (block_start ascends; job 0 starts at 0).
+template <typename Job>
+__device__ __forceinline__ int find_job(const Job* j, int count, int b) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (j[mid].block_start <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 
 // 4x4 byte transpose: w[c] byte i = v[i] byte c.
 __device__ __forceinline__ void transpose4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, uint32_t& w0,
@@ -287,11 +300,7 @@ constexpr int MAXG_ALL = kMaxG<1> > kMaxG<4> ? kMaxG<1> : kMaxG<4>;
 __global__ __launch_bounds__(FT) void fold_rows_kernel(JobList jl) {
   __shared__ __align__(16) uint32_t lds[LDS_WORDS];
   __shared__ uint64_t gsum[MAXG_ALL];
-  int ji = 0;
-#pragma unroll 1
-  for (int k = 1; k < jl.count; ++k)
-    if (jl.j[k].block_start <= (int)blockIdx.x) ji = k;
-  const FoldJob& job = jl.j[ji];
+  const FoldJob& job = jl.j[find_job(jl.j, jl.count, blockIdx.x)];
   const int lb = blockIdx.x - job.block_start;
   // strips wholly in the padding: write zeros and leave
   if (lb >= job.n_chunks * job.n_strips) {
@@ -326,11 +335,7 @@ struct SumList {
 
 __global__ __launch_bounds__(256) void fold_sum_kernel(SumList sl) {
   __shared__ uint64_t red[256];
-  int ji = 0;
-#pragma unroll 1
-  for (int k = 1; k < sl.count; ++k)
-    if (sl.j[k].block_start <= (int)blockIdx.x) ji = k;
-  const SumJob& j = sl.j[ji];
+  const SumJob& j = sl.j[find_job(sl.j, sl.count, blockIdx.x)];
   const int lb = blockIdx.x - j.block_start;
   const int tid = threadIdx.x;
   uint64_t s = 0;
