@@ -149,6 +149,22 @@ def test_full_cfg2(fp):
     _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
 
 
+def test_full_cfg2_pipelined(fp):
+    """The benchmark's launch configuration: pipelined proofs, several per graph
+    replay (each proof's sum-check inside the next proof's witness launch), the
+    last sum-check drained after the replays."""
+    cfg = synth.config(2)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg)
+    prover = make_prover(cfg, inp, ch, pipelined=True)
+    prover.capture(steps=3)
+    prover.replay()
+    prover.drain()
+    torch.cuda.synchronize()
+    got = prover.results()
+    _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
+
+
 def test_full_cfg3(fp):
     cfg = synth.config(3)
     inp, ch, got = _run(cfg)
