@@ -198,8 +198,9 @@ size_t fp_fold_claim_batched_workspace(fp_dtype fold_dt, int32_t n_fold, const f
  * NULL (all ones). r (device, n) are the round challenges. For each round i
  * the prover sends g_i(0), g_i(1), g_i(2) with
  *   g_i(c) = sum_j rho_j sum_q A_j,c[q] B_j,c[q],  A_c[q] = A[2q] + c (A[2q+1] - A[2q]),
- * then binds A[q] <- A[2q] + r_i (A[2q+1] - A[2q]) (B likewise); round i
- * reads r_i only after g_i is fully reduced. Outputs (device): rounds [n][3],
+ * then binds A[q] <- A[2q] + r_i (A[2q+1] - A[2q]) (B likewise); r_i is
+ * applied only after g_i is complete across all of the call's threads (the
+ * challenges are inputs and may be loaded earlier). Outputs (device): rounds [n][3],
  * finals [n_pairs][2] = (A_j~(r), B_j~(r)), claim0 (1 element, may be NULL) =
  * the initial claim. Tables are not modified. n in [1, 30]. */
 int fp_sumcheck_prove(int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B, const fp_elem* rho,

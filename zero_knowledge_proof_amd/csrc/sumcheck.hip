@@ -12,10 +12,10 @@
 // r_{i-1}, stores the new slice and emits its share of g_i. A launch boundary
 // separates the last partial of g_{i-1} from any read of r_{i-1}, so no
 // challenge is used before its round polynomial is complete. Once all of an
-// instance's tables fit in LDS (<= 8192 entries per side), one 1024-thread
-// workgroup per instance finishes the remaining rounds in LDS with wave64
-// shuffles and an LDS tree for each round's reduction. Independent instances
-// (one per MoE expert) run as one workgroup each in a single launch.
+// instance's tables fit one workgroup (<= 8192 entries per side), one 512-thread
+// workgroup per instance finishes the remaining rounds (sc_tail.hpp: register
+// slices, then a single wave). Independent instances (one per MoE expert) run
+// as one workgroup each in a single launch.
 #include <vector>
 
 #include "common.hpp"

@@ -13,8 +13,8 @@ claim about Z to claims about the committed activations and the weights. One
   merge    random linear combinations           (fp_combine_claims, fp_linear_combine)
 
 The challenges (drawn before the run and passed in) follow the witness in the
-stream order; each round challenge is read on the device only after its round
-polynomial is complete. Every buffer is allocated at construction, so ``run``
+stream order; each round challenge is applied on the device only after its
+round polynomial is complete. Every buffer is allocated at construction, so ``run``
 only enqueues kernels. Inputs are host numpy arrays uploaded once.
 """
 from __future__ import annotations
