@@ -96,16 +96,54 @@ def measured_traffic(cfg, kernel_phase: str):
                       float(kv["write_kib"]) * float(kv["write_scale"])) * 1024))
 
 
-def cpu_baseline(cfg, inp, ch) -> dict:
+def _host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_ONE_CORE = """
+import sys, time
+sys.path.insert(0, %r)
+import oracle, synth
+cfg = synth.config(%d)
+inp = synth.make_inputs(cfg)
+ch = synth.draw_challenges(cfg, inp.get("route"))
+oracle.lib()
+t0 = time.perf_counter()
+oracle.prove_config(cfg, inp, ch)
+print(time.perf_counter() - t0)
+"""
+
+
+def cpu_baseline(cfg, inp, ch, one_core: bool = True) -> dict:
+    """The oracle's whole layer proof of the workload on the host cores (all
+    OpenMP threads, and once more on one core in a child process)."""
+    import subprocess
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    if cfg.cid in (1, 2):
-        t0 = time.perf_counter()
-        oracle.prove_config(cfg, inp, ch)
-        dt = time.perf_counter() - t0
-        return {"value": cfg.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": "the whole layer proof of this workload (all %d tokens), one pass, %.1f s" % (cfg.T, dt)}
-    return None
+    if cfg.cid not in (1, 2):
+        return None
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.prove_config(cfg, inp, ch)
+    dt = time.perf_counter() - t0
+    out = {"value": cfg.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "the whole layer proof of this workload (all %d tokens), one pass, %.2f s" % (cfg.T, dt),
+           "host_cpu": _host_cpu(), "nproc": os.cpu_count()}
+    if one_core:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", _ONE_CORE % (ROOT, cfg.cid)], env=env, capture_output=True,
+                           text=True, timeout=600)
+        if r.returncode == 0:
+            d1 = float(r.stdout.strip().splitlines()[-1])
+            out["value_1core"] = cfg.T / d1
+            out["sample_1core"] = "the same proof with OMP_NUM_THREADS=1, %.2f s" % d1
+    return out
 
 
 def main():
@@ -165,29 +203,36 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps // per_graph + 1)]
     start.record(stream)
-    for _ in range(args.steps // per_graph):
+    marks[0].record(stream)
+    for i in range(args.steps // per_graph):
         prover.replay()
+        marks[i + 1].record(stream)
     prover.drain()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
+    # per-replay spread (each replay holds per_graph steps; the drain is not in these)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) / per_graph for i in range(len(marks) - 1))
     tokens = cfg.T
     value = tokens / (ms * 1e-3)
 
-    # per-phase launch durations: each phase captured alone and replayed K times
-    # back to back between two events on the same stream
+    # per-phase launch durations: each phase captured alone, per_graph times in one
+    # graph (so the graph-launch cost is spread as in the step graph), K launches
+    # back to back between two events on the stream the kernels run on
     phase_ms = {}
     for name, fn in prover.phases():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn()
+            for _ in range(per_graph):
+                fn()
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(args.steps // per_graph):
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
@@ -213,7 +258,9 @@ def main():
     wkey = "witness+sumcheck" if pipelined else "witness"
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "ms_per_step_replays": {"median": round(per_step[len(per_step) // 2], 5), "min": round(per_step[0], 5),
+                                "max": round(per_step[-1], 5), "replays": len(per_step)}, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8->int32 witness; u64 Goldilocks field", "data": "synthetic",
         "config": {"workload": WORKLOADS[cfg.cid], "T": cfg.T, "seed": cfg.seed, "s": cfg.s,
                    "matmuls": [[m.name, m.d_in, m.d_out] for m in cfg.matmuls] if cfg.matmuls else None,
