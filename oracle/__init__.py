@@ -155,6 +155,14 @@ def fold_rows(M: np.ndarray, E, cols_pad: int | None = None) -> np.ndarray:
     return out
 
 
+def request_vectors(M: np.ndarray, Es, cols_pad: int | None = None) -> np.ndarray:
+    """Folded rows of one weight table for a batch of requests ("How fast can
+    FlashProve go", §2.1: each request commits the weight table's folded row,
+    its request vector): row j is fold_rows(M, Es[j]). Returns [R, cols_pad]."""
+    cols_pad = M.shape[1] if cols_pad is None else cols_pad
+    return np.stack([fold_rows(M, E, cols_pad) for E in Es]) if len(Es) else np.zeros((0, cols_pad), np.uint64)
+
+
 def fold_cols(M: np.ndarray, E, ks) -> np.ndarray:
     M = np.ascontiguousarray(M)
     rows, cols = M.shape

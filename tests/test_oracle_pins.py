@@ -198,6 +198,29 @@ def test_fold_boolean_point_selects_row_and_linearity():
     assert np.array_equal(O.fold_cols(A, E, [0, 5, 36]), fa[[0, 5, 36]])
 
 
+def test_request_vectors_open_the_weight_table():
+    # A request vector is the weight table's folded row at the request's point
+    # r_o: its MLE over the columns at r_k is W~(r_k || r_o) (the opening the
+    # batch shares), and at a Boolean r_o it is that row of W itself.
+    rng = np.random.default_rng(11)
+    W = rng.integers(-128, 128, size=(6, 5), dtype=np.int8)
+    pts = [[int(v) for v in synth.challenges(40 + j, 3)] for j in range(3)]
+    Es = [O.eq_table(r) for r in pts] + [O.eq_table([1, 0, 1])]
+    V = O.request_vectors(W, Es, 8)
+    assert V.shape == (4, 8) and np.all(V[:, 5:] == 0)
+    r_k = [int(v) for v in synth.challenges(50, 3)]
+    for j, r in enumerate(pts):
+        assert O.mle_seq(V[j], r_k) == O.mle_matrix(W, r, r_k)
+    assert [int(v) for v in V[3, :5]] == [O.from_int(int(v)) for v in W[5]]
+    # Freivalds' view of the same projection: <v_j, x> = <E_j, W x> for any x
+    x = [int(v) for v in synth.challenges(51, 5)]
+    Wx = [sum(O.from_int(int(W[t, k])) * x[k] for k in range(5)) % P for t in range(6)]
+    for j in range(3):
+        lhs = sum(int(V[j, k]) * x[k] for k in range(5)) % P
+        assert lhs == sum(int(Es[j][t]) * Wx[t] for t in range(6)) % P
+    assert O.request_vectors(W, [], 8).shape == (0, 8)
+
+
 def test_mle_two_routes_and_boolean_points():
     rng = random.Random(8)
     for n in range(0, 9):
