@@ -10,6 +10,9 @@ s=8); ``--config N`` selects another workload description (1..5).
 Prints one JSON line. ``roofline`` describes the kernel with the largest
 average launch time, timed with HIP events on the stream the kernels run on;
 ``cpu_baseline`` times the CPU oracle on the same workload (rank 0, N=1).
+``request_vectors`` measures the batch fold of the workload's first weight
+matrix by 64 requests' eq vectors (one pass over the weights) beside 64
+one-pass folds, with its own roofline and oracle time.
 """
 from __future__ import annotations
 
@@ -146,6 +149,84 @@ def cpu_baseline(cfg, inp, ch, one_core: bool = True) -> dict:
     return out
 
 
+def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, R: int = 64) -> dict:
+    """Request vectors of a batch: the first weight matrix of the workload
+    folded by R requests' eq vectors (points drawn like the layer's r_o) in one
+    fp_fold_matrix_multi call, against the same R folds done one matrix pass
+    each (fp_fold_matrix_batched). Inputs and the prepared transpose are
+    resident before timing; each is timed as per_graph calls in one HIP graph."""
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+    if not cfg.matmuls:
+        return None
+    m = cfg.matmuls[0]
+    rows, cols = m.d_out, m.d_in
+    W = torch.from_numpy(np.ascontiguousarray(inp[m.w])).to(dev)
+    n = synth.log2ceil(rows)
+    pts = [synth.challenges(synth.data_seed(cfg.seed, 1 << 20 | j), n) for j in range(R)]
+    Es = fp.eq_table_batched([fp.to_field_tensor(p) for p in pts])
+    E = torch.stack([e[:rows] for e in Es]).contiguous()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    Mt, c = fp.fold_weights_prepare(W)
+    t1.record(stream)
+    out = torch.empty((R, cols), dtype=torch.int64, device=dev)
+    outs1 = [torch.empty(cols, dtype=torch.int64, device=dev) for _ in range(R)]
+    jobs = [(W, E[j], cols, outs1[j]) for j in range(R)]
+
+    def timed(fn):
+        fn()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // per_graph)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph) * 1e-3
+
+    t_multi = timed(lambda: fp.fold_matrix_multi(Mt, c, rows, E, cols, out=out))
+    t_single = timed(lambda: fp.fold_matrix_batched(jobs))
+    same = all(torch.equal(outs1[j], out[j]) for j in range(R))
+    ops = 2 * 8 * R * rows * cols
+    res = {
+        "workload": "%s weights [%d x %d] (int8), %d requests' eq vectors over its %d rows" % (m.name, rows, cols, R,
+                                                                                               rows),
+        "R": R, "ms": round(t_multi * 1e3, 5), "requests_per_s": round(R / t_multi, 1),
+        "one_pass_per_request_ms": round(t_single * 1e3, 5), "speedup": round(t_single / t_multi, 2),
+        "outputs_equal_one_pass_per_request": bool(same),
+        "prepare_ms_once_per_matrix": round(t0.elapsed_time(t1), 4),
+        "roofline": {"bound": "mfma", "achieved": round(ops / t_multi / 1e12, 1), "peak": MFMA_I8_PEAK / 1e12,
+                     "unit": "TFLOP/s", "frac": round(ops / t_multi / MFMA_I8_PEAK, 4),
+                     "traffic": None, "algorithmic_ops": ops,
+                     "note": "the whole call (digits, limb GEMM, chunk sum) timed; int8 ops of the limb GEMM"},
+    }
+    if with_cpu:
+        import oracle
+        k = 8
+        Wn = np.ascontiguousarray(inp[m.w])
+        Esn = [fp.field_numpy(E[j]) for j in range(k)]
+        oracle.lib()
+        c0 = time.perf_counter()
+        oracle.request_vectors(Wn, Esn, cols)
+        dt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(k / dt, 3), "unit": "requests/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                               "kind": "oracle", "sample": "%d of the %d requests, %.2f s" % (k, R, dt)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +237,9 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="prove steps one after another instead of overlapping each step's sum-check with the "
                          "next step's witness GEMM")
+    ap.add_argument("--no-request-vectors", action="store_true",
+                    help="skip the batch request-vector measurement (64 eq vectors folded against the first weight "
+                         "matrix in one pass)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of MIB MiB (a reference for HBM byte counters)")
     args = ap.parse_args()
@@ -272,6 +356,8 @@ def main():
         "phases": extras,
         "wall_s": round(wall, 3),
     }
+    if not args.no_request_vectors:
+        out["request_vectors"] = request_vectors_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, inp, ch)
     print(json.dumps(out))
 

@@ -64,6 +64,8 @@ enum {
 #define FP_MAX_DIN 131072 /* 127^2 * d_in < 2^31 keeps Z exact in int32 */
 #define FP_MAX_N 30       /* largest table: 2^30 entries */
 #define FP_MAX_GROUPS 256 /* groups in one grouped witness launch */
+#define FP_MAX_REQUESTS 4096          /* eq vectors in one multi-request fold */
+#define FP_MAX_FOLD_ROWS (1 << 30)    /* rows of a multi-request fold's matrix */
 
 /* Thread-local message of the last failing call ("" after success). */
 const char* fp_last_error(void);
@@ -147,6 +149,32 @@ typedef struct {
 int fp_fold_matrix_batched(fp_dtype dt, int32_t count, const fp_fold_desc* descs, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 size_t fp_fold_matrix_batched_workspace(fp_dtype dt, int32_t count, const fp_fold_desc* descs);
+
+/* ------------------------------------------------- multi-request folds --- */
+/* Request vectors of a batch ("How fast can FlashProve go", §2.1: each request
+ * commits the folded row of the weight table before one shared opening):
+ * the folds of ONE int8 matrix M [rows, cols] by R eq vectors, with M read once.
+ *
+ * fp_fold_weights_prepare writes what depends on M alone, once per matrix:
+ * Mt [cols, rows] int8 with leading dim ldt (>= rows, a multiple of 16; Mt
+ * 16-byte aligned), Mt[k, t] = M[t, k], and colsum [cols] int32,
+ * colsum[k] = sum_t M[t, k]. M has leading dim ld >= cols. Bytes of Mt past
+ * `rows` in each row are not written. */
+int fp_fold_weights_prepare(const int8_t* M, int64_t ld, int32_t rows, int32_t cols, int8_t* Mt, int64_t ldt,
+                            int32_t* colsum, hipStream_t stream);
+
+/* out[j*ldo + k] = sum_{t<rows} E[j*lde + t] M[t, k] for j < R, k < cols, and
+ * 0 for cols <= k < cols_pad, given Mt and colsum from fp_fold_weights_prepare.
+ * Every E entry must be a canonical field element (< p). Each output equals
+ * fp_fold_matrix of M by the j-th vector. The eq weights are split into bytes
+ * and the sums over t run as one int8 matrix product on the matrix cores
+ * (R <= FP_MAX_REQUESTS, rows <= FP_MAX_FOLD_ROWS, lde >= rows, ldo >= cols_pad).
+ * ws: fp_fold_matrix_multi_workspace(rows, cols, R) bytes, 256-byte aligned;
+ * its contents on entry do not matter. */
+int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t* colsum, int32_t rows, int32_t cols, int32_t R,
+                         const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo, int32_t cols_pad, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+size_t fp_fold_matrix_multi_workspace(int32_t rows, int32_t cols, int32_t R);
 
 /* ----------------------------------------------------------------- MLE --- */
 /* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading

@@ -61,6 +61,14 @@ def test_argument_errors_without_gpu():
     assert L.fp_witness_linear_with_sumcheck(None, 16, None, 16, 0, 16, 4, 8, None, None, None, 1, pa, pa, None, 13,
                                              dummy, dummy, dummy, None, None) == 2
     assert b"exceed one" in L.fp_last_error()
+    # multi-request fold: Mt's leading dim must be a multiple of 16, R bounded, workspace checked
+    assert L.fp_fold_weights_prepare(dummy, 64, 100, 64, dummy, 104, dummy, None) == 2
+    assert L.fp_fold_matrix_multi(dummy, 112, dummy, 100, 64, 5000, dummy, 100, dummy, 64, 64, dummy, 0, None) == 2
+    need = L.fp_fold_matrix_multi_workspace(14336, 4096, 64)
+    assert need >= 8 * 64 * 14336  # the digit rows at least
+    assert L.fp_fold_matrix_multi_workspace(14336, 4096, 1) < need
+    assert L.fp_fold_matrix_multi(dummy, 14336, dummy, 14336, 4096, 64, dummy, 14336, dummy, 4096, 4096, dummy,
+                                  need - 1, None) == 4
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)

@@ -25,7 +25,8 @@ EXPORTS = [
     "fp_mle_eval", "fp_mle_eval_workspace", "fp_sumcheck_prove", "fp_sumcheck_workspace",
     "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
     "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
-    "fp_witness_linear_with_sumcheck",
+    "fp_witness_linear_with_sumcheck", "fp_fold_weights_prepare", "fp_fold_matrix_multi",
+    "fp_fold_matrix_multi_workspace",
 ]
 
 _lib = None
@@ -83,6 +84,9 @@ def lib():
             "fp_fold_claim_batched_workspace": (sz, [i32, i32, vp, i32, i32, vp]),
             "fp_witness_linear_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp,
                                                                i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_fold_weights_prepare": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, vp]),
+            "fp_fold_matrix_multi": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, vp, i64, vp, i64, i32, vp, sz, vp]),
+            "fp_fold_matrix_multi_workspace": (sz, [i32, i32, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -139,6 +143,7 @@ class Workspace:
 
 
 _ws_fold, _ws_claim, _ws_mle, _ws_sc = Workspace(), Workspace(), Workspace(), Workspace()
+_ws_multi = Workspace()
 
 
 def to_field_tensor(vals, device=None) -> torch.Tensor:
@@ -279,6 +284,38 @@ def fold_matrix_batched(jobs):
     p, nb = _ws_fold.get(need)
     _check(lib().fp_fold_matrix_batched(dt, k, descs, p, nb, _stream()), "fp_fold_matrix_batched")
     return [j[3] for j in jobs]
+
+
+def fold_weights_prepare(M, Mt=None, colsum=None):
+    """Transposed copy Mt [cols, ldt] (ldt = rows rounded up to 16) and column
+    sums [cols] int32 of an int8 matrix M [rows, cols], for fold_matrix_multi."""
+    rows, cols = M.shape
+    ldt = max(16, (rows + 15) // 16 * 16)
+    Mt = torch.empty((cols, ldt), dtype=torch.int8, device=M.device) if Mt is None else Mt
+    colsum = torch.empty(cols, dtype=torch.int32, device=M.device) if colsum is None else colsum
+    assert Mt.dtype == torch.int8 and Mt.shape[0] == cols and Mt.stride(1) == 1
+    _check(lib().fp_fold_weights_prepare(_ptr(M) if M.numel() else None, _ld(M), rows, cols,
+                                         _ptr(Mt) if Mt.numel() else None, Mt.stride(0), _ptr(colsum), _stream()),
+           "fp_fold_weights_prepare")
+    return Mt, colsum
+
+
+def fold_matrix_multi(Mt, colsum, rows: int, E, cols_pad: int | None = None, out=None):
+    """out[j, k] = sum_t E[j, t] M[t, k] for every row j of E [R, >= rows]
+    (int64 field tensor), from fold_weights_prepare's Mt and colsum."""
+    cols = Mt.shape[0]
+    R = E.shape[0]
+    cols_pad = cols if cols_pad is None else cols_pad
+    out = torch.empty((R, cols_pad), dtype=torch.int64, device=Mt.device) if out is None else out
+    assert E.dtype == torch.int64 and E.stride(1) == 1 and out.stride(1) == 1
+    lde = E.stride(0) if R > 1 else max(E.stride(0), rows)
+    ldo = out.stride(0) if R > 1 else max(out.stride(0), cols_pad)
+    need = lib().fp_fold_matrix_multi_workspace(rows, cols, R)
+    p, nb = _ws_multi.get(need)
+    _check(lib().fp_fold_matrix_multi(_ptr(Mt) if Mt.numel() else None, Mt.stride(0), _ptr(colsum), rows, cols, R,
+                                      _ptr(E) if E.numel() else None, lde, _ptr(out) if out.numel() else None, ldo,
+                                      cols_pad, p, nb, _stream()), "fp_fold_matrix_multi")
+    return out
 
 
 def mle_eval(M, r_rows, r_cols, out=None):

@@ -18,6 +18,24 @@ int check_launch(const char* what);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Limb folds on the matrix cores. With digit rows D [N, K] (N = 8 R: row
+// 8 j + l holds the signed byte digits of request j's weights, limb l) and a
+// transposed int8 matrix Xt [T, K], writes for every request j and column t
+//   part[s psplit + j ldp + t] = sum_l 2^(8l) sum_{k in chunk s} D[8j+l, k] Xt[t, k]
+//                                (+ 128 colsum[t] sum_l 2^(8l) in chunk 0)   mod p,
+// the reduction over [0, K) cut into ksplit chunks of kchunk (a multiple of the
+// tile's K step; at most 2^16, which keeps each int32 limb sum exact).
+constexpr int32_t SPLITK_MAX_CHUNK = 65536;
+struct SplitK {
+  int32_t ksplit;  // chunks
+  int32_t kchunk;  // reduction length per chunk
+};
+// Split for T tokens, reduction length K and N digit rows.
+SplitK splitk_plan(int32_t T, int32_t K, int32_t N);
+int witness_fold_splitk(const int8_t* Xt, int64_t ldx, const int8_t* D, int64_t ldd, int32_t T, int32_t K, int32_t N,
+                        const int32_t* colsum, const SplitK& p, uint64_t* part, int64_t ldp, int64_t psplit,
+                        hipStream_t st);
+
 // Wave64 reductions of a 64-bit value held as two 32-bit halves.
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64);

@@ -47,6 +47,14 @@ struct WitArgs {
   int8_t* R;
   int32_t tiles_t, tiles_o;
   int32_t vecX, vecW, vecZ, vecYR;
+  // split K: each tile is computed by ksplit workgroups, workgroup j reducing
+  // over [j kchunk, (j+1) kchunk) (0 or 1: no split)
+  int32_t ksplit, kchunk;
+  // limb-fold epilogue: field value of each group of 8 output rows at token t
+  // into part[j psplit + (o / 8) ldp + t], plus the column-sum term in split 0
+  const int32_t* colsum;
+  uint64_t* part;
+  int64_t ldp, psplit;
 };
 
 struct GroupTab {
@@ -93,7 +101,7 @@ struct WitLds {
 };
 
 // Tile `bid` of `nblocks` GEMM workgroups.
-template <int BO, int BT, int WO, int WT, bool GROUPED, int PF, int BK>
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF, int BK, int EPI>
 __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& gt, int bid, int nblocks,
                                              WitLds<BO, BT, BK>& sh) {
   constexpr int PITCH = BK + 16;  // LDS row pitch: 16 consecutive rows start in distinct bank groups
@@ -107,9 +115,17 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
   auto& sA = sh.sA;
   auto& sB = sh.sB;
 
-  const int tile = xcd_tile(bid, nblocks);
+  int tile = xcd_tile(bid, nblocks);
+  int ks = 0;
+  if (a.ksplit > 1) {
+    const int per = a.tiles_t * a.tiles_o;
+    ks = tile / per;
+    tile -= ks * per;
+  }
   const int tt = tile % a.tiles_t;
   const int to = tile / a.tiles_t;
+  const int kb = ks * a.kchunk;                                   // this workgroup's K range
+  const int klen = (a.ksplit > 1) ? min(a.kchunk, a.K - kb) : a.K;
 
   const int8_t* Wb = a.W;
   int t_base, t_lim;  // token rows [t_base, t_lim) valid for this tile's group
@@ -138,13 +154,13 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
   // outputs that are never stored, and every load stays in bounds.
   const int8_t* pa[CA];
   const int8_t* pb[CB];
-  int sa_off[CA], sb_off[CB], ka[CA], kb[CB];
+  int sa_off[CA], sb_off[CB], ka[CA], kb_[CB];
 #pragma unroll
   for (int c = 0; c < CA; ++c) {
     const int ch = tid + c * NT;
     const int row = ch / CPR, kc = (ch % CPR) * 16;
     const int g = min(o_base + row, a.N - 1);
-    pa[c] = Wb + (int64_t)g * a.ldw;
+    pa[c] = Wb + (int64_t)g * a.ldw + kb;
     ka[c] = kc;
     sa_off[c] = (ch < NCA) ? row * PITCH + kc : -1;
   }
@@ -153,8 +169,8 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
     const int ch = tid + c * NT;
     const int row = ch / CPR, kc = (ch % CPR) * 16;
     const int g = min(t_base + row, t_lim - 1);
-    pb[c] = a.X + (int64_t)g * a.ldx;
-    kb[c] = kc;
+    pb[c] = a.X + (int64_t)g * a.ldx + kb;
+    kb_[c] = kc;
     sb_off[c] = (ch < NCB) ? row * PITCH + kc : -1;
   }
   // register staging for PF K steps ahead; whole 16-byte chunks when the K step
@@ -162,16 +178,16 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
   const bool vec_all = a.vecX && a.vecW;
   v4i ra[PF][CA], rb[PF][CB];
   auto gload = [&](int slot, int k0) {
-    if (vec_all && k0 + BK <= a.K) {
+    if (vec_all && k0 + BK <= klen) {
 #pragma unroll
       for (int c = 0; c < CA; ++c) ra[slot][c] = *(const v4i*)(pa[c] + k0 + ka[c]);
 #pragma unroll
-      for (int c = 0; c < CB; ++c) rb[slot][c] = *(const v4i*)(pb[c] + k0 + kb[c]);
+      for (int c = 0; c < CB; ++c) rb[slot][c] = *(const v4i*)(pb[c] + k0 + kb_[c]);
     } else {
 #pragma unroll
-      for (int c = 0; c < CA; ++c) ra[slot][c] = load16(pa[c], k0 + ka[c], a.K, a.vecW);
+      for (int c = 0; c < CA; ++c) ra[slot][c] = load16(pa[c], k0 + ka[c], klen, a.vecW);
 #pragma unroll
-      for (int c = 0; c < CB; ++c) rb[slot][c] = load16(pb[c], k0 + kb[c], a.K, a.vecX);
+      for (int c = 0; c < CB; ++c) rb[slot][c] = load16(pb[c], k0 + kb_[c], klen, a.vecX);
     }
   };
   auto sstore = [&](int slot, int buf) {
@@ -191,7 +207,7 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  const int KT = (a.K + BK - 1) / BK;
+  const int KT = (klen + BK - 1) / BK;
   const int lrow = lane & 31, lk = (lane >> 5) * 16;
   auto compute = [&](int buf) {
 #pragma unroll
@@ -260,6 +276,25 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
       const int t = t_base + wt0 + 32 * j + (lane & 31);
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
       if (t >= t_lim || o0 >= a.N) continue;
+      if constexpr (EPI == 1) {
+        // z[0..7] are the byte limbs l = 0..7 of output group o0 / 8 at token t,
+        // z[8..15] those of the next group: value = sum_l 2^(8l) z[l], exact as
+        // L + 2^32 H with |L|, |H| < 2^55, then reduced.
+        uint64_t cterm = 0;
+        if (ks == 0) cterm = gl::mul(gl::from_i64(128 * (int64_t)a.colsum[t]), 0x0101010101010101ull);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int o = o0 + 8 * g;
+          if (o >= a.N) break;
+          const int32_t* zz = z + 8 * g;
+          const int64_t L = (int64_t)zz[0] + (int64_t)zz[1] * 256 + (int64_t)zz[2] * 65536 + (int64_t)zz[3] * 16777216;
+          const int64_t H = (int64_t)zz[4] + (int64_t)zz[5] * 256 + (int64_t)zz[6] * 65536 + (int64_t)zz[7] * 16777216;
+          uint64_t v = gl::add(gl::from_i64(L), gl::mul(gl::from_i64(H), 1ull << 32));
+          a.part[(int64_t)ks * a.psplit + (int64_t)(o >> 3) * a.ldp + t] = gl::add(v, cterm);
+        }
+        continue;
+      }
+      const int64_t idx = (int64_t)t * a.N + o0;
       uint32_t yw[4] = {0, 0, 0, 0}, rw[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -268,7 +303,6 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
         yw[q >> 2] |= y << (8 * (q & 3));
         rw[q >> 2] |= r << (8 * (q & 3));
       }
-      const int64_t idx = (int64_t)t * a.N + o0;
       if (o0 + 16 <= a.N) {
         if (a.Z) {
           if (a.vecZ) {
@@ -303,10 +337,10 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
   }
 }
 
-template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64, int EPI = 0>
 __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_kernel(WitArgs a, GroupTab gt) {
   __shared__ WitLds<BO, BT, BK> sh;
-  witness_body<BO, BT, WO, WT, GROUPED, PF, BK>(a, gt, blockIdx.x, gridDim.x, sh);
+  witness_body<BO, BT, WO, WT, GROUPED, PF, BK, EPI>(a, gt, blockIdx.x, gridDim.x, sh);
 }
 
 // The GEMM together with sum-check tails: workgroups [0, n_tail) each run one
@@ -322,7 +356,7 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(
     sct::tail_body<NT>(ta, blockIdx.x, *reinterpret_cast<sct::TailLds<NT>*>(&sh));
     return;
   }
-  witness_body<BO, BT, WO, WT, GROUPED, PF, BK>(a, gt, blockIdx.x - n_tail, gridDim.x - n_tail, sh);
+  witness_body<BO, BT, WO, WT, GROUPED, PF, BK, 0>(a, gt, blockIdx.x - n_tail, gridDim.x - n_tail, sh);
 }
 
 // Tile configurations (BO, BT, WO, WT, grouped, prefetch distance, K step),
@@ -335,14 +369,14 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(
 #define WIT_S 256, 32, 64, 32, false, 1, 64
 #define WIT_SG 256, 32, 64, 32, true, 1, 64
 
-template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64>
+template <int BO, int BT, int WO, int WT, bool GROUPED, int PF = 1, int BK = 64, int EPI = 0>
 int launch(WitArgs a, const GroupTab& gt, hipStream_t st) {
   if (!GROUPED) a.tiles_t = (a.T + BT - 1) / BT;
   a.tiles_o = (a.N + BO - 1) / BO;
-  const int64_t blocks = (int64_t)a.tiles_t * a.tiles_o;
+  const int64_t blocks = (int64_t)a.tiles_t * a.tiles_o * (a.ksplit > 1 ? a.ksplit : 1);
   if (blocks <= 0) return FP_OK;
   if (blocks > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
-  hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED, PF, BK>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((witness_kernel<BO, BT, WO, WT, GROUPED, PF, BK, EPI>), dim3((unsigned)blocks),
                      dim3((BO / WO) * (BT / WT) * 64), 0, st, a, gt);
   return fpi::check_launch("witness_kernel");
 }
@@ -496,3 +530,41 @@ extern "C" int fp_witness_linear_with_sumcheck(const int8_t* X, int64_t ldx, con
   else rc = launch_with_tail<WIT_M>(a, gt, ta, 1, stream);
   return rc ? rc : fpi::ok();
 }
+
+// ---- limb folds: the int8 product of a weight matrix's transpose (as the
+// token operand) with byte-digit rows (as the weight operand), reduced per
+// group of 8 digit rows to a field value in the epilogue. One tile shape, the
+// 128 x 128 one, measured best or within 2% of best from 1 to 128 requests on
+// the up-projection's weights, with the split picked for about two workgroups
+// per CU.
+namespace fpi {
+
+SplitK splitk_plan(int32_t T, int32_t K, int32_t N) {
+  constexpr int BO = 128, BT = 128, BK = 128;  // WIT_M
+  SplitK p{};
+  const int64_t tiles = (int64_t)((T + BT - 1) / BT) * ((N + BO - 1) / BO);
+  int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+  const int64_t kb = ((int64_t)K + BK - 1) / BK;  // K steps
+  if (want > kb) want = kb > 0 ? kb : 1;
+  int64_t chunk = (kb + want - 1) / want * BK;
+  if (chunk > SPLITK_MAX_CHUNK) chunk = SPLITK_MAX_CHUNK;
+  p.kchunk = (int32_t)chunk;
+  p.ksplit = (int32_t)(K > 0 ? ((int64_t)K + chunk - 1) / chunk : 1);
+  return p;
+}
+
+int witness_fold_splitk(const int8_t* Xt, int64_t ldx, const int8_t* D, int64_t ldd, int32_t T, int32_t K, int32_t N,
+                        const int32_t* colsum, const SplitK& p, uint64_t* part, int64_t ldp, int64_t psplit,
+                        hipStream_t st) {
+  WitArgs a{};
+  a.X = Xt; a.ldx = ldx; a.W = D; a.ldw = ldd;
+  a.T = T; a.N = N; a.K = K; a.s = 1;
+  a.ksplit = p.ksplit; a.kchunk = p.kchunk;
+  a.colsum = colsum; a.part = part; a.ldp = ldp; a.psplit = psplit;
+  vec_flags(a);
+  a.vecW = ((ldd & 15) == 0) && ((((uintptr_t)D) & 15) == 0);
+  GroupTab gt{};
+  return launch<WIT_M, 1>(a, gt, st);
+}
+
+}  // namespace fpi
