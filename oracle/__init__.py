@@ -10,11 +10,15 @@ arrays into it and strings the steps of a layer proof together in the order of
 "How fast can FlashProve go", §2 (witness, then sum-check claims about the
 committed tables and weights) and §3.1 (the remainder of each rescale is
 committed beside the rescaled output). Small scalar field arithmetic here uses
-Python integers with ``% P``.
+Python integers with ``% P``. The commitment of Y and R (§3.1: limbs packed
+three to a field element, each row Reed-Solomon encoded by an NTT, each column
+a salted BLAKE2b Merkle leaf) uses the C code for packing and encoding and the
+host's ``hashlib.blake2b`` for every hash.
 """
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
 
@@ -63,6 +67,10 @@ def lib():
             "or_check_sumcheck": (ctypes.c_int, [i32, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
             "or_check_rescale": (ctypes.c_int, [vp, vp, vp, i64, i32, vp]),
             "or_check_witness": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, vp, vp]),
+            "or_pack_limbs": (None, [vp, i64, vp, i64, i64, i32, vp]),
+            "or_root_of_unity": (u64, [i32]),
+            "or_rs_encode": (None, [vp, i32, vp]),
+            "or_rs_eval": (u64, [vp, i32, i64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -252,6 +260,92 @@ def check_witness(X, W, Z):
     rc = lib().or_check_witness(_p(X), X.shape[1], _p(W), W.shape[1], X.shape[0], X.shape[1], W.shape[0],
                                 _p(Z), ctypes.byref(where))
     return REASONS[rc], int(where.value)
+
+
+# ------------------------------------------------------------- commitment --
+# "How fast can FlashProve go", §3.1: a committed table is Reed-Solomon encoded
+# row by row (an NTT) and Merkle-hashed column by column (BLAKE2b); values are
+# cut into 8-bit limbs packed three to a field element in 20-bit slots.
+SALT_BYTES = 16
+DIGEST_BYTES = 32
+
+
+def pack_limbs(A: np.ndarray, B: np.ndarray, logn: int) -> np.ndarray:
+    """The limbs of A then B (int8 values, one limb each: the byte 0..255),
+    three per element in 20-bit slots, filling rows of 2^logn elements (as
+    many rows as needed, zero beyond). Returns [rows, 2^logn] uint64."""
+    A = np.ascontiguousarray(A, np.int8).reshape(-1)
+    B = np.ascontiguousarray(B, np.int8).reshape(-1)
+    n = 1 << logn
+    elems = (A.size + B.size + 2) // 3
+    rows = max(1, (elems + n - 1) // n)
+    out = np.empty((rows, n), np.uint64)
+    lib().or_pack_limbs(_p(A), A.size, _p(B), B.size, n, rows, _p(out))
+    return out
+
+
+def root_of_unity(k: int) -> int:
+    return int(lib().or_root_of_unity(k))
+
+
+def rs_encode(msg: np.ndarray) -> np.ndarray:
+    """Rate-1/2 Reed-Solomon codewords of each row of msg [rows, n], n = 2^logn:
+    code[i, j] = sum_k msg[i, k] w^(jk) for j < 2n, w a primitive 2n-th root of
+    unity (root_of_unity(logn + 1))."""
+    msg = np.ascontiguousarray(msg, np.uint64)
+    rows, n = msg.shape
+    logn = log2ceil(n)
+    assert 1 << logn == n
+    code = np.empty((rows, 2 * n), np.uint64)
+    for i in range(rows):
+        lib().or_rs_encode(_p(msg[i]), logn, _p(code[i]))
+    return code
+
+
+def rs_eval(row: np.ndarray, j: int) -> int:
+    """One codeword entry of a message row by Horner's rule at w^j."""
+    row = np.ascontiguousarray(row, np.uint64)
+    return int(lib().or_rs_eval(_p(row), log2ceil(row.size), j))
+
+
+def blake2b(data: bytes) -> bytes:
+    return hashlib.blake2b(data, digest_size=DIGEST_BYTES).digest()
+
+
+def merkle_leaf(code: np.ndarray, salts: np.ndarray, j: int) -> bytes:
+    """Leaf of column j: BLAKE2b-256(salt_j || code[0, j] || ... || code[rows-1, j]),
+    field elements as 8 little-endian bytes."""
+    col = np.ascontiguousarray(code[:, j], np.uint64)
+    return blake2b(bytes(salts[j]) + col.astype("<u8").tobytes())
+
+
+def merkle_tree(code: np.ndarray, salts: np.ndarray) -> list:
+    """All levels of the Merkle tree over the columns of code: level 0 holds the
+    leaves, level d+1 holds BLAKE2b-256(left || right) of level d's pairs, the
+    last level the root. Returns a list of lists of 32-byte digests."""
+    width = code.shape[1]
+    levels = [[merkle_leaf(code, salts, j) for j in range(width)]]
+    while len(levels[-1]) > 1:
+        prev = levels[-1]
+        levels.append([blake2b(prev[2 * i] + prev[2 * i + 1]) for i in range(len(prev) // 2)])
+    return levels
+
+
+def merkle_path(levels: list, j: int) -> list:
+    """Sibling digests from leaf j up to (not including) the root."""
+    path = []
+    for lev in levels[:-1]:
+        path.append(lev[j ^ 1])
+        j >>= 1
+    return path
+
+
+def merkle_verify(root: bytes, leaf: bytes, j: int, path: list) -> bool:
+    h = leaf
+    for sib in path:
+        h = blake2b(h + sib) if j % 2 == 0 else blake2b(sib + h)
+        j >>= 1
+    return h == root
 
 
 # ----------------------------------------------------------- layer proofs --

@@ -367,3 +367,71 @@ int or_check_witness(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw,
   *where = first;
   return first >= 0 ? OR_WITNESS_MISMATCH : OR_OK;
 }
+
+/* ------------------------------------------------------------ commitment --
+ * [HF] §3.1: committing a table Reed-Solomon encodes each row with an NTT and
+ * Merkle-hashes each column; values are split into 8-bit limbs packed three to
+ * a field element in 20-bit slots. Readings where the page is silent: an int8
+ * value is one limb, its byte 0..255; the limbs of A then B fill the rows in
+ * order, zero beyond; a row c_0..c_{n-1} is the coefficient vector of a
+ * polynomial evaluated at w^j, j < 2n, w = 7^((p-1)/2n) (rate 1/2, natural
+ * order). Hashing is done with the host's BLAKE2b in oracle/__init__.py. */
+
+/* msg[e] = l_{3e} + 2^20 l_{3e+1} + 2^40 l_{3e+2} over rows * n_row elements. */
+void or_pack_limbs(const int8_t* A, int64_t na, const int8_t* B, int64_t nb, int64_t n_row, int32_t rows,
+                   uint64_t* msg) {
+  const int64_t total = (int64_t)rows * n_row;
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < total; ++e) {
+    uint64_t v = 0;
+    for (int q = 0; q < 3; ++q) {
+      const int64_t l = 3 * e + q;
+      uint64_t limb = 0;
+      if (l < na) limb = (uint8_t)A[l];
+      else if (l - na < nb) limb = (uint8_t)B[l - na];
+      v |= limb << (20 * q);
+    }
+    msg[e] = v;
+  }
+}
+
+/* A primitive 2^k-th root of unity: 7^((p-1)/2^k) (7 generates the whole group). */
+uint64_t or_root_of_unity(int32_t k) { return or_pow(7, (OR_P - 1) >> k); }
+
+/* code[j] = sum_{i<n} msg[i] w^{ij}, j < 2n, w = or_root_of_unity(logn + 1):
+ * the row zero-padded to 2n and transformed by textbook iterative radix-2
+ * Cooley-Tukey (bit-reversal permutation, then log2(2n) butterfly stages). */
+void or_rs_encode(const uint64_t* msg, int32_t logn, uint64_t* code) {
+  const int32_t L = logn + 1;
+  const int64_t N = (int64_t)1 << L, n = N / 2;
+  for (int64_t j = 0; j < N; ++j) {
+    int64_t r = 0;
+    for (int b = 0; b < L; ++b) r |= ((j >> b) & 1) << (L - 1 - b);
+    code[r] = j < n ? msg[j] % OR_P : 0;
+  }
+  for (int32_t s = 1; s <= L; ++s) {
+    const int64_t m = (int64_t)1 << s, h = m / 2;
+    const uint64_t wm = or_root_of_unity(s);
+    uint64_t* tw = (uint64_t*)malloc(sizeof(uint64_t) * h);
+    tw[0] = 1;
+    for (int64_t t = 1; t < h; ++t) tw[t] = or_mul(tw[t - 1], wm);
+#pragma omp parallel for schedule(static)
+    for (int64_t base = 0; base < N; base += m) {
+      for (int64_t t = 0; t < h; ++t) {
+        const uint64_t u = code[base + t], v = or_mul(code[base + t + h], tw[t]);
+        code[base + t] = or_add(u, v);
+        code[base + t + h] = or_sub(u, v);
+      }
+    }
+    free(tw);
+  }
+}
+
+/* One codeword entry by its definition: the row's polynomial at w^j (Horner). */
+uint64_t or_rs_eval(const uint64_t* msg, int32_t logn, int64_t j) {
+  const int64_t n = (int64_t)1 << logn;
+  const uint64_t x = or_pow(or_root_of_unity(logn + 1), (uint64_t)j);
+  uint64_t acc = 0;
+  for (int64_t i = n - 1; i >= 0; --i) acc = or_add(or_mul(acc, x), msg[i] % OR_P);
+  return acc;
+}

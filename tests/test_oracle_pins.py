@@ -378,3 +378,113 @@ def test_negative_controls_witness():
     r_t = [int(v) for v in synth.challenges(1, 4)]
     r_o = [int(v) for v in synth.challenges(2, 4)]
     assert O.mle_matrix(Z, r_t, r_o) != O.mle_matrix(Z2, r_t, r_o)
+
+
+# ------------------------------------------------------------- commitment --
+def test_pack_limbs_worked_example_and_unpacking():
+    A = np.array([1, -1, 127, -128], np.int8)
+    B = np.array([5], np.int8)
+    msg = O.pack_limbs(A, B, 2)  # rows of 4 elements
+    # limbs 1, 255, 127 | 128, 5 (then zeros), 20-bit slots
+    assert msg.shape == (1, 4)
+    assert [int(v) for v in msg[0]] == [1 + 255 * 2**20 + 127 * 2**40, 128 + 5 * 2**20, 0, 0]
+    rng = np.random.default_rng(1)
+    A = rng.integers(-128, 128, 1000).astype(np.int8)
+    B = rng.integers(-128, 128, 777).astype(np.int8)
+    msg = O.pack_limbs(A, B, 6)
+    assert msg.shape == (10, 64)  # ceil(ceil(1777 / 3) / 64) rows
+    limbs = [(int(v) >> (20 * q)) & 0xFFFFF for v in msg.reshape(-1) for q in range(3)]
+    want = [int(x) & 0xFF for x in np.concatenate([A, B])]
+    assert limbs[:len(want)] == want and not any(limbs[len(want):])
+    assert all(int(v) < 2**60 for v in msg.reshape(-1))  # three slots fit below p
+
+
+def test_roots_of_unity():
+    for k in (1, 2, 5, 12, 23, 32):
+        w = O.root_of_unity(k)
+        assert O.power(w, 2**k) == 1 and O.power(w, 2**(k - 1)) == P - 1
+    # 2 has order 192, so the primitive 64th roots are the powers 2^(3u), u odd;
+    # the one this generator gives is 2^39 (small-radix twiddles become shifts)
+    assert O.root_of_unity(6) == pow(2, 39, P)
+    assert O.power(O.root_of_unity(23), 2**17) == O.root_of_unity(6)
+
+
+def test_rs_encode_is_the_polynomial_on_the_subgroup():
+    rng = random.Random(21)
+    for logn in range(0, 6):
+        n = 1 << logn
+        msg = np.array([[rng.randrange(P) for _ in range(n)] for _ in range(2)], np.uint64)
+        msg[0, 0] = P - 1
+        code = O.rs_encode(msg)
+        w = O.root_of_unity(logn + 1)
+        for i in range(2):
+            want = [sum(int(msg[i, k]) * pow(w, j * k, P) for k in range(n)) % P for j in range(2 * n)]
+            assert [int(v) for v in code[i]] == want
+    # larger rows: entries by Horner's rule at sampled points
+    logn = 12
+    n = 1 << logn
+    msg = np.array([[rng.randrange(P) for _ in range(n)]], np.uint64)
+    code = O.rs_encode(msg)
+    for j in [0, 1, 2, 777, 4096, 8191]:
+        assert int(code[0, j]) == O.rs_eval(msg[0], j)
+    # folding: with P = Lo + x^(n/2) Hi, at the n-th roots x^(n/2) = (-1)^j, so
+    # code[4j] and code[4j + 2] come from the half-length rows Lo + Hi and Lo - Hi
+    lo, hi = msg[0, : n // 2].astype(object), msg[0, n // 2:].astype(object)
+    plus = np.array([[(a + b) % P for a, b in zip(lo, hi)]], np.uint64)
+    minus = np.array([[(a - b) % P for a, b in zip(lo, hi)]], np.uint64)
+    cp, cm = O.rs_encode(plus)[0], O.rs_encode(minus)[0]
+    assert np.array_equal(code[0, 0::4], cp[0::2]) and np.array_equal(code[0, 2::4], cm[1::2])
+    # a constant row gives a constant codeword; the row (0, 1, 0, ...) gives w^j
+    c = O.rs_encode(np.array([[9] + [0] * 7], np.uint64))
+    assert np.all(c == 9)
+    x = O.rs_encode(np.array([[0, 1] + [0] * 6], np.uint64))
+    w = O.root_of_unity(4)
+    assert [int(v) for v in x[0]] == [pow(w, j, P) for j in range(16)]
+
+
+def test_rs_encode_convolution_theorem():
+    # codewords multiply pointwise: the product of two rows' polynomials
+    # (schoolbook, degree < 2n - 1) evaluated on the same 2n points
+    rng = random.Random(22)
+    n = 32
+    a = [rng.randrange(P) for _ in range(n)]
+    b = [rng.randrange(P) for _ in range(n)]
+    c = [0] * (2 * n)
+    for i in range(n):
+        for j in range(n):
+            c[i + j] = (c[i + j] + a[i] * b[j]) % P
+    ca, cb = O.rs_encode(np.array([a, b], np.uint64))
+    cc = O.rs_encode(np.array([c], np.uint64))[0]  # evaluations on 4n points
+    assert all(int(x) * int(y) % P == int(z) for x, y, z in zip(ca, cb, cc[::2]))
+
+
+def test_blake2b_published_vector():
+    import hashlib
+    for line in open(os.path.join(HERE, "golden", "blake2b.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        msg, nbytes, hexd = line.split()
+        assert hashlib.blake2b(msg.encode(), digest_size=int(nbytes)).hexdigest() == hexd
+
+
+def test_merkle_tree_by_hand_and_paths():
+    import hashlib
+    rng = np.random.default_rng(23)
+    code = rng.integers(0, 2**63, size=(3, 2), dtype=np.uint64)
+    salts = rng.integers(0, 256, size=(2, O.SALT_BYTES), dtype=np.uint8)
+    lv = O.merkle_tree(code, salts)
+    leaf = [hashlib.blake2b(bytes(salts[j]) + b"".join(int(code[i, j]).to_bytes(8, "little") for i in range(3)),
+                            digest_size=32).digest() for j in range(2)]
+    assert lv[0] == leaf and lv[1] == [hashlib.blake2b(leaf[0] + leaf[1], digest_size=32).digest()]
+    code = rng.integers(0, 2**63, size=(2, 16), dtype=np.uint64)
+    salts = rng.integers(0, 256, size=(16, O.SALT_BYTES), dtype=np.uint8)
+    lv = O.merkle_tree(code, salts)
+    assert [len(x) for x in lv] == [16, 8, 4, 2, 1]
+    root = lv[-1][0]
+    for j in range(16):
+        assert O.merkle_verify(root, lv[0][j], j, O.merkle_path(lv, j))
+        assert not O.merkle_verify(root, lv[0][j], j ^ 1, O.merkle_path(lv, j))
+    code2 = code.copy()
+    code2[1, 5] ^= np.uint64(1)
+    lv2 = O.merkle_tree(code2, salts)
+    assert lv2[0][5] != lv[0][5] and lv2[-1][0] != root and lv2[0][4] == lv[0][4]
