@@ -66,6 +66,8 @@ enum {
 #define FP_MAX_GROUPS 256 /* groups in one grouped witness launch */
 #define FP_MAX_REQUESTS 4096          /* eq vectors in one multi-request fold */
 #define FP_MAX_FOLD_ROWS (1 << 30)    /* rows of a multi-request fold's matrix */
+#define FP_MAX_RS_LOGN 23             /* Reed-Solomon rows of up to 2^23 elements (codewords 2^24) */
+#define FP_MAX_MERKLE_ROWS (1 << 20)  /* rows hashed into one Merkle leaf */
 
 /* Thread-local message of the last failing call ("" after success). */
 const char* fp_last_error(void);
@@ -175,6 +177,41 @@ int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t* colsum, i
                          const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo, int32_t cols_pad, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 size_t fp_fold_matrix_multi_workspace(int32_t rows, int32_t cols, int32_t R);
+
+/* ---------------------------------------------------------- commitment --- */
+/* Commitment of committed tables such as Y and R ("How fast can FlashProve
+ * go", §3.1: values are cut into 8-bit limbs packed three to a field element in
+ * 20-bit slots; each row of the table is Reed-Solomon encoded by an NTT, a row
+ * of 2^22 elements into 2^23; each column becomes a salted Merkle leaf hashed
+ * with BLAKE2b).
+ *
+ * fp_commit_pack: msg[e] = l_{3e} + 2^20 l_{3e+1} + 2^40 l_{3e+2} for
+ * e < rows * 2^logn, where the limb stream l is the na bytes of A followed by
+ * the nb bytes of B (each int8 value is one limb, its byte 0..255) and 0 past
+ * them. msg is dense [rows, 2^logn]; rows must hold every limb
+ * (FP_ESHAPE otherwise). logn <= FP_MAX_RS_LOGN. */
+int fp_commit_pack(const int8_t* A, int64_t na, const int8_t* B, int64_t nb, int32_t logn, int32_t rows,
+                   fp_elem* msg, hipStream_t stream);
+
+/* Rate-1/2 Reed-Solomon encoding of each row: for n = 2^logn,
+ * code[i*ld_code + j] = sum_{k<n} msg[i*ld_msg + k] w^(jk) for j < 2n, with
+ * w = 7^((p-1)/2n) (a primitive 2n-th root of unity; 7 generates the
+ * multiplicative group). Natural order. msg entries must be canonical.
+ * ws: fp_rs_encode_workspace(rows, logn) bytes, 256-byte aligned (twiddle
+ * tables and, for 2n > 256, one intermediate copy of the codewords). */
+int fp_rs_encode(const fp_elem* msg, int64_t ld_msg, int32_t rows, int32_t logn, fp_elem* code, int64_t ld_code,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+size_t fp_rs_encode_workspace(int32_t rows, int32_t logn);
+
+/* Salted Merkle tree over the 2^log_width columns of code [rows, ld_code]:
+ * leaf j = BLAKE2b-256(salt_j || code[0][j] || ... || code[rows-1][j]) with
+ * 16-byte salts (salts: 2^log_width x 16 bytes) and elements as 8 little-endian
+ * bytes; a parent is BLAKE2b-256(left || right) (RFC 7693, unkeyed, 32-byte
+ * digest). tree receives 2^(log_width+1) - 1 digests of 32 bytes: the leaves in
+ * column order, then each level above, the root last. salts and tree 8-byte
+ * aligned; rows <= FP_MAX_MERKLE_ROWS (rows = 0 hashes the salts alone). */
+int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t log_width, const uint8_t* salts,
+                     uint8_t* tree, hipStream_t stream);
 
 /* ----------------------------------------------------------------- MLE --- */
 /* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading

@@ -69,6 +69,15 @@ def test_argument_errors_without_gpu():
     assert L.fp_fold_matrix_multi_workspace(14336, 4096, 1) < need
     assert L.fp_fold_matrix_multi(dummy, 14336, dummy, 14336, 4096, 64, dummy, 14336, dummy, 4096, 4096, dummy,
                                   need - 1, None) == 4
+    # commitment: sizes, limbs that do not fit, workspace, null salts
+    assert L.fp_commit_pack(dummy, 10, dummy, 0, 24, 1, dummy, None) == 2
+    assert L.fp_commit_pack(dummy, 100, dummy, 0, 2, 2, dummy, None) == 2  # 34 elements > 2 rows of 4
+    assert L.fp_rs_encode(dummy, 1 << 24, 1, 24, dummy, 1 << 25, dummy, 1 << 30, None) == 2
+    need = L.fp_rs_encode_workspace(2, 22)
+    assert need >= 2 * (1 << 23) * 8
+    assert L.fp_rs_encode(dummy, 1 << 22, 2, 22, dummy, 1 << 23, dummy, need - 1, None) == 4
+    assert L.fp_merkle_commit(dummy, 1 << 26, 1, 26, dummy, dummy, None) == 2
+    assert L.fp_merkle_commit(dummy, 16, 1, 4, None, dummy, None) == 1
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)

@@ -26,7 +26,8 @@ EXPORTS = [
     "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
     "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
     "fp_witness_linear_with_sumcheck", "fp_fold_weights_prepare", "fp_fold_matrix_multi",
-    "fp_fold_matrix_multi_workspace",
+    "fp_fold_matrix_multi_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
+    "fp_merkle_commit",
 ]
 
 _lib = None
@@ -87,6 +88,10 @@ def lib():
             "fp_fold_weights_prepare": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, vp]),
             "fp_fold_matrix_multi": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, vp, i64, vp, i64, i32, vp, sz, vp]),
             "fp_fold_matrix_multi_workspace": (sz, [i32, i32, i32]),
+            "fp_commit_pack": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, vp, vp]),
+            "fp_rs_encode": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, sz, vp]),
+            "fp_rs_encode_workspace": (sz, [i32, i32]),
+            "fp_merkle_commit": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -143,7 +148,7 @@ class Workspace:
 
 
 _ws_fold, _ws_claim, _ws_mle, _ws_sc = Workspace(), Workspace(), Workspace(), Workspace()
-_ws_multi = Workspace()
+_ws_multi, _ws_rs = Workspace(), Workspace()
 
 
 def to_field_tensor(vals, device=None) -> torch.Tensor:
@@ -316,6 +321,55 @@ def fold_matrix_multi(Mt, colsum, rows: int, E, cols_pad: int | None = None, out
                                       _ptr(E) if E.numel() else None, lde, _ptr(out) if out.numel() else None, ldo,
                                       cols_pad, p, nb, _stream()), "fp_fold_matrix_multi")
     return out
+
+
+# --------------------------------------------------------------- commitment --
+SALT_BYTES, DIGEST_BYTES = 16, 32
+
+
+def commit_rows(na: int, nb: int, logn: int) -> int:
+    """Rows of 2^logn elements that hold na + nb limbs, three per element."""
+    elems = (na + nb + 2) // 3
+    return max(1, (elems + (1 << logn) - 1) >> logn)
+
+
+def commit_pack(A, B, logn: int, rows: int | None = None, out=None):
+    """Limbs of the int8 tensors A then B, three per field element in 20-bit
+    slots, as [rows, 2^logn] (zero past the limbs)."""
+    na, nb = A.numel(), B.numel()
+    rows = commit_rows(na, nb, logn) if rows is None else rows
+    dev = A.device if na else B.device
+    out = torch.empty((rows, 1 << logn), dtype=torch.int64, device=dev) if out is None else out
+    assert out.is_contiguous() and A.is_contiguous() and B.is_contiguous()
+    _check(lib().fp_commit_pack(_ptr(A) if na else None, na, _ptr(B) if nb else None, nb, logn, rows, _ptr(out),
+                                _stream()), "fp_commit_pack")
+    return out
+
+
+def rs_encode(msg, code=None):
+    """Rate-1/2 Reed-Solomon codewords [rows, 2n] of the rows of msg [rows, n]."""
+    rows, n = msg.shape
+    logn = n.bit_length() - 1
+    assert 1 << logn == n and msg.stride(1) == 1
+    code = torch.empty((rows, 2 * n), dtype=torch.int64, device=msg.device) if code is None else code
+    need = lib().fp_rs_encode_workspace(rows, logn)
+    p, nbytes = _ws_rs.get(need)
+    _check(lib().fp_rs_encode(_ptr(msg), msg.stride(0) if rows > 1 else n, rows, logn, _ptr(code),
+                              code.stride(0) if rows > 1 else 2 * n, p, nbytes, _stream()), "fp_rs_encode")
+    return code
+
+
+def merkle_commit(code, salts, tree=None):
+    """Salted BLAKE2b-256 Merkle tree over the columns of code [rows, W]
+    (W a power of 2); salts: uint8 [W, 16]. Returns the tree as uint8
+    [2W - 1, 32]: the W leaves, then each level up, the root last."""
+    rows, W = code.shape
+    logw = W.bit_length() - 1
+    assert 1 << logw == W and salts.shape == (W, SALT_BYTES) and salts.is_contiguous()
+    tree = torch.empty((2 * W - 1, DIGEST_BYTES), dtype=torch.uint8, device=code.device) if tree is None else tree
+    _check(lib().fp_merkle_commit(_ptr(code), code.stride(0) if rows > 1 else W, rows, logw, _ptr(salts),
+                                  _ptr(tree), _stream()), "fp_merkle_commit")
+    return tree
 
 
 def mle_eval(M, r_rows, r_cols, out=None):

@@ -1,0 +1,546 @@
+// commit.hip - commitment of committed tables: limb packing, Reed-Solomon
+// encoding by NTT, and a salted BLAKE2b Merkle tree over the columns.
+//
+// "How fast can FlashProve go", §3.1: to commit a table, each row is
+// Reed-Solomon encoded (an NTT; a row of 2^22 elements becomes 2^23) and each
+// column is Merkle hashed with BLAKE2b; values are cut into 8-bit limbs and
+// three limbs share a field element in 20-bit slots. Here a row c_0..c_{n-1} is
+// the coefficient vector of a polynomial evaluated at w^j, j < 2n, with w =
+// 7^((p-1)/2n); column j's leaf is BLAKE2b-256(salt_j || code[0][j] || ... ||
+// code[rows-1][j]) and a parent is BLAKE2b-256(left || right). BLAKE2b follows
+// RFC 7693 (Saarinen and Aumasson, 2015).
+//
+// NTT of N = 2^L points (L <= 24) in P = ceil(L/8) passes over HBM. With
+// N = N_1 ... N_P, n = sum_p n_p S_p (S_p = N_{p+1} ... N_P) and
+// k = sum_p k_p T_p (T_p = N_1 ... N_{p-1}), n k = sum_p n_p S_p (k_p T_p + K_{p-1})
+// (mod N) with K_{p-1} = sum_{q<p} k_q T_q, so pass p multiplies each element by
+// w^(n_p S_p K_{p-1}) and transforms along n_p (N_p <= 256 points, inside LDS);
+// k_p takes n_p's place in memory, and the last pass writes X[K_P] in natural
+// order. A pass works on a [N_p x 32] tile: 32 neighbouring columns (or, in the
+// last pass, 32 neighbouring K) so that every global access is a 256-byte run.
+// Inside the tile an N_p-point transform is two register transforms of at most
+// 16 points, whose twiddles are powers of w_16 = 2^156 (w_64 = 2^39 for this
+// generator, and 2^96 = -1), i.e. shifts.
+#include "common.hpp"
+#include "gl.hpp"
+
+namespace {
+
+// ----------------------------------------------------------------- packing
+// msg[e] = l_{3e} + 2^20 l_{3e+1} + 2^40 l_{3e+2}: limb l is byte l of the
+// stream A (na bytes) followed by B (nb bytes), 0 past both.
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ A, int64_t na,
+                                                   const int8_t* __restrict__ B, int64_t nb, int64_t total,
+                                                   uint64_t* __restrict__ msg) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  uint64_t v = 0;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int64_t l = 3 * e + q;
+    uint32_t limb = 0;
+    if (l < na) limb = (uint8_t)A[l];
+    else if (l - na < nb) limb = (uint8_t)B[l - na];
+    v |= (uint64_t)limb << (20 * q);
+  }
+  msg[e] = v;
+}
+
+// --------------------------------------------------------------------- NTT
+constexpr int NTT_MAXP = 3;   // passes (N <= 2^24)
+constexpr int TILE_C = 32;    // columns (or transforms) per workgroup
+constexpr int NTT_T = 256;    // threads
+constexpr int TW_BITS = 12;   // w^e = hi[e >> 12] * lo[e & 4095]
+
+// x * 2^e mod p for 0 <= e < 192 (e is a compile-time constant after unrolling):
+// 2^96 = -1 and 2^64 = 2^32 - 1.
+__device__ __forceinline__ uint64_t mul_pow2(uint64_t x, int e) {
+  const bool neg = e >= 96;
+  if (neg) e -= 96;
+  if (e >= 64) {
+    x = gl::sub(gl::reduce128(x << 32, x >> 32), x);  // x (2^32 - 1)
+    e -= 64;
+  }
+  if (e > 0) x = gl::reduce128(x << e, x >> (64 - e));
+  return neg ? gl::sub(0, x) : x;
+}
+
+// exponent of w_m as a power of 2, for m | 64: w_64 = 2^39
+constexpr int root_exp(int m) { return (39 * (64 / m)) % 192; }
+
+// In-register DFT of R <= 16 points, natural order in and out:
+// v[k] <- sum_n v[n] w_R^(nk). Radix-2 decimation in frequency, then the
+// bit-reversal permutation as a register renaming.
+template <int R>
+__device__ __forceinline__ void dft_small(uint64_t (&v)[16]) {
+  if constexpr (R == 1) return;
+#pragma unroll
+  for (int half = R / 2; half >= 1; half >>= 1) {
+#pragma unroll
+    for (int g = 0; g < R; g += 2 * half) {
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const uint64_t a = v[g + j], b = v[g + j + half];
+        v[g + j] = gl::add(a, b);
+        v[g + j + half] = mul_pow2(gl::sub(a, b), (root_exp(2 * half) * j) % 192);
+      }
+    }
+  }
+  uint64_t t[16];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    int r = 0;
+#pragma unroll
+    for (int b = 1, kk = k; b < R; b <<= 1, kk >>= 1) r = (r << 1) | (kk & 1);
+    t[k] = v[r];
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) v[k] = t[k];
+}
+
+
+struct NttArgs {
+  const uint64_t* src;
+  uint64_t* dst;
+  int64_t src_rs, dst_rs;    // row strides (elements)
+  const uint64_t* tw_lo;     // w_N^i, i < 4096
+  const uint64_t* tw_hi;     // w_N^(4096 i)
+  int32_t L;                 // log2 N
+  int32_t P, p;              // passes, this pass (0-based)
+  int32_t lN[NTT_MAXP];      // log2 N_q
+  int32_t first, last;
+  int32_t blocks_per_row;
+  int32_t lS, lT;            // log2 S_p, log2 T_p of this pass
+  // base(K) = sum_{q<p} k_q S_q with k_q = (K >> dT[q]) & dM[q], S_q = 2^dS[q]
+  int32_t dT[NTT_MAXP - 1], dM[NTT_MAXP - 1], dS[NTT_MAXP - 1];
+};
+
+__device__ __forceinline__ uint64_t w_pow(const NttArgs& a, int64_t e) {
+  const uint64_t lo = a.tw_lo[e & ((1 << TW_BITS) - 1)];
+  if (a.L <= TW_BITS) return lo;
+  return gl::mul(a.tw_hi[e >> TW_BITS], lo);
+}
+
+// One pass of N_p = 2^LP points: see the file comment. LDS tile [N_p][TILE_C]
+// plus the pass's in-tile twiddles w_{N_p}^i.
+template <int LP>
+__global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
+  __shared__ uint64_t tile[256 * TILE_C];
+  __shared__ uint64_t twp[256];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x / a.blocks_per_row;
+  const int blk = blockIdx.x % a.blocks_per_row;
+  const int p = a.p;
+  constexpr int lp = LP;
+  constexpr int Np = 1 << LP;
+  const int lS = a.lS, lT = a.lT;
+  const uint64_t* src = a.src + (int64_t)row * a.src_rs;
+  uint64_t* dst = a.dst + (int64_t)row * a.dst_rs;
+
+  // which transforms: not last -> K = kidx, columns c0 + c; last -> K = kidx0 + c
+  int64_t kidx = 0, c0 = 0;
+  int ncols;  // valid columns of the tile
+  if (!a.last) {
+    const int64_t S = (int64_t)1 << lS;
+    const int64_t cblocks = (S + TILE_C - 1) / TILE_C;
+    kidx = blk / cblocks;
+    c0 = (blk % cblocks) * TILE_C;
+    ncols = (int)min<int64_t>(TILE_C, S - c0);
+  } else {
+    c0 = (int64_t)blk * TILE_C;  // first K of the tile
+    ncols = (int)min<int64_t>(TILE_C, ((int64_t)1 << lT) - c0);
+  }
+  // base(K) = sum_{q<p} k_q S_q for K = sum_{q<p} k_q T_q
+  auto base_of = [&](int64_t K) {
+    int64_t b = 0;
+#pragma unroll
+    for (int q = 0; q < NTT_MAXP - 1; ++q)
+      if (q < p) b += ((K >> a.dT[q]) & a.dM[q]) << a.dS[q];
+    return b;
+  };
+
+  // in-tile twiddles w_{N_p}^i = w_N^(i N / N_p)
+  for (int i = tid; i < Np; i += NTT_T) twp[i] = w_pow(a, (int64_t)i << (a.L - lp));
+
+  // ---- load (with the pass twiddle w^(n_p S_p K))
+  const int total = Np * TILE_C;
+  if (!a.last) {
+    const int64_t b0 = base_of(kidx);
+    for (int idx = tid; idx < total; idx += NTT_T) {
+      const int n = idx / TILE_C, c = idx % TILE_C;
+      uint64_t v = 0;
+      if (c < ncols && !(a.first && n >= Np / 2)) {
+        v = src[b0 + ((int64_t)n << lS) + c0 + c];
+        if (p > 0 && kidx != 0) v = gl::mul(v, w_pow(a, ((int64_t)n << lS) * kidx));
+      }
+      tile[n * TILE_C + c] = v;
+    }
+  } else {
+    for (int idx = tid; idx < total; idx += NTT_T) {
+      const int c = idx / Np, n = idx % Np;
+      uint64_t v = 0;
+      const int64_t K = c0 + c;
+      if (c < ncols && !(a.first && n >= Np / 2)) {
+        v = src[base_of(K) + n];
+        if (p > 0 && K != 0) v = gl::mul(v, w_pow(a, (int64_t)n * K));
+      }
+      tile[n * TILE_C + c] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- N_p = R_a R_b: stage A over n_a (stride R_b), twiddle w_{N_p}^(n_b k_a)
+  constexpr int la = (LP + 1) / 2, lb = LP / 2;
+  constexpr int Ra = 1 << la, Rb = 1 << lb;
+  const int c = tid % TILE_C, g = tid / TILE_C, G = NTT_T / TILE_C;
+  uint64_t v[16];
+  for (int nb = g; nb < Rb; nb += G) {
+#pragma unroll
+    for (int i = 0; i < Ra; ++i) v[i] = tile[(i * Rb + nb) * TILE_C + c];
+    dft_small<Ra>(v);
+#pragma unroll
+    for (int ka = 0; ka < Ra; ++ka) {
+      const uint64_t x = (nb * ka) ? gl::mul(v[ka], twp[nb * ka]) : v[ka];
+      tile[(ka * Rb + nb) * TILE_C + c] = x;
+    }
+  }
+  __syncthreads();
+  // stage B over n_b (contiguous), k_p = k_a + R_a k_b
+  for (int ka = g; ka < Ra; ka += G) {
+#pragma unroll
+    for (int i = 0; i < Rb; ++i) v[i] = tile[(ka * Rb + i) * TILE_C + c];
+    dft_small<Rb>(v);
+    if (c < ncols) {
+      if (!a.last) {
+        const int64_t b0 = base_of(kidx);
+#pragma unroll
+        for (int kb = 0; kb < Rb; ++kb) dst[b0 + ((int64_t)(ka + Ra * kb) << lS) + c0 + c] = v[kb];
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < Rb; ++kb) dst[c0 + c + ((int64_t)(ka + Ra * kb) << lT)] = v[kb];
+      }
+    }
+  }
+}
+
+// tw_lo[i] = w^i (i < 4096), tw_hi[i] = w^(4096 i) (i < N / 4096)
+__global__ __launch_bounds__(256) void twiddle_kernel(uint64_t w, int32_t L, uint64_t* tw_lo, uint64_t* tw_hi) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int nlo = 1 << min(L, TW_BITS);
+  const int nhi = L > TW_BITS ? 1 << (L - TW_BITS) : 0;
+  if (i >= nlo + nhi) return;
+  uint64_t base = w;
+  int64_t e = i;
+  uint64_t* out = tw_lo + i;
+  if (i >= nlo) {
+    e = i - nlo;
+    for (int s = 0; s < TW_BITS; ++s) base = gl::mul(base, base);
+    out = tw_hi + e;
+  }
+  uint64_t r = 1;
+  while (e) {
+    if (e & 1) r = gl::mul(r, base);
+    base = gl::mul(base, base);
+    e >>= 1;
+  }
+  *out = r;
+}
+
+// ------------------------------------------------------------------ BLAKE2b
+// RFC 7693: 12 rounds of the G mixing function over a 16-word state.
+constexpr uint64_t B2_IV_H[8] = {0x6a09e667f3bcc908ull, 0xbb67ae8584caa73bull, 0x3c6ef372fe94f82bull,
+                                 0xa54ff53a5f1d36f1ull, 0x510e527fade682d1ull, 0x9b05688c2b3e6c1full,
+                                 0x1f83d9abfb41bd6bull, 0x5be0cd19137e2179ull};
+constexpr unsigned char B2_SIGMA[12][16] = {
+    {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15}, {14, 10, 4, 8, 9, 15, 13, 6, 1, 12, 0, 2, 11, 7, 5, 3},
+    {11, 8, 12, 0, 5, 2, 15, 13, 10, 14, 3, 6, 7, 1, 9, 4}, {7, 9, 3, 1, 13, 12, 11, 14, 2, 6, 5, 10, 4, 0, 15, 8},
+    {9, 0, 5, 7, 2, 4, 10, 15, 14, 1, 11, 12, 6, 8, 3, 13}, {2, 12, 6, 10, 0, 11, 8, 3, 4, 13, 7, 5, 15, 14, 1, 9},
+    {12, 5, 1, 15, 14, 13, 4, 10, 0, 7, 6, 3, 9, 2, 8, 11}, {13, 11, 7, 14, 12, 1, 3, 9, 5, 0, 15, 4, 8, 6, 2, 10},
+    {6, 15, 14, 9, 11, 3, 0, 8, 12, 2, 13, 7, 1, 4, 10, 5}, {10, 2, 8, 4, 7, 6, 1, 5, 15, 11, 9, 14, 3, 12, 13, 0},
+    {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15}, {14, 10, 4, 8, 9, 15, 13, 6, 1, 12, 0, 2, 11, 7, 5, 3}};
+
+__device__ __forceinline__ uint64_t rotr64(uint64_t x, int n) { return (x >> n) | (x << (64 - n)); }
+
+__device__ __forceinline__ void b2_g(uint64_t& a, uint64_t& b, uint64_t& c, uint64_t& d, uint64_t x, uint64_t y) {
+  a = a + b + x;
+  d = rotr64(d ^ a, 32);
+  c = c + d;
+  b = rotr64(b ^ c, 24);
+  a = a + b + y;
+  d = rotr64(d ^ a, 16);
+  c = c + d;
+  b = rotr64(b ^ c, 63);
+}
+
+// h <- compress(h, m, t, last)
+__device__ __forceinline__ void b2_compress(uint64_t (&h)[8], const uint64_t (&m)[16], uint64_t t, bool last) {
+  uint64_t v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = h[i];
+    v[i + 8] = B2_IV_H[i];
+  }
+  v[12] ^= t;  // byte counter (messages here are far below 2^64 bytes)
+  if (last) v[14] = ~v[14];
+#pragma unroll
+  for (int r = 0; r < 12; ++r) {
+    const unsigned char* s = B2_SIGMA[r];
+    b2_g(v[0], v[4], v[8], v[12], m[s[0]], m[s[1]]);
+    b2_g(v[1], v[5], v[9], v[13], m[s[2]], m[s[3]]);
+    b2_g(v[2], v[6], v[10], v[14], m[s[4]], m[s[5]]);
+    b2_g(v[3], v[7], v[11], v[15], m[s[6]], m[s[7]]);
+    b2_g(v[0], v[5], v[10], v[15], m[s[8]], m[s[9]]);
+    b2_g(v[1], v[6], v[11], v[12], m[s[10]], m[s[11]]);
+    b2_g(v[2], v[7], v[8], v[13], m[s[12]], m[s[13]]);
+    b2_g(v[3], v[4], v[9], v[14], m[s[14]], m[s[15]]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] ^= v[i] ^ v[i + 8];
+}
+
+// parameter block of an unkeyed 32-byte digest: h0 ^= 0x01010000 | 32
+__device__ __forceinline__ void b2_init32(uint64_t (&h)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = B2_IV_H[i];
+  h[0] ^= 0x01010020ull;
+}
+
+constexpr int SALT_WORDS = 2;  // 16-byte salts
+
+// leaf j = BLAKE2b-256(salt_j || code[0][j] || ... || code[rows-1][j]); the
+// message is SALT_WORDS + rows 8-byte words, in 16-word blocks.
+__global__ __launch_bounds__(256) void leaf_kernel(const uint64_t* __restrict__ code, int64_t ld, int32_t rows,
+                                                   int64_t width, const uint64_t* __restrict__ salts,
+                                                   uint64_t* __restrict__ leaves) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= width) return;
+  uint64_t h[8];
+  b2_init32(h);
+  const int words = SALT_WORDS + rows;
+  const int64_t bytes = 8 * (int64_t)words;
+  for (int w0 = 0; w0 < words; w0 += 16) {
+    uint64_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int w = w0 + i;
+      uint64_t x = 0;
+      if (w < SALT_WORDS) x = salts[j * SALT_WORDS + w];
+      else if (w < words) x = code[(int64_t)(w - SALT_WORDS) * ld + j];
+      m[i] = x;
+    }
+    const bool last = w0 + 16 >= words;
+    b2_compress(h, m, last ? (uint64_t)bytes : (uint64_t)(8 * (w0 + 16)), last);
+  }
+  uint64_t* out = leaves + 4 * j;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = h[i];
+}
+
+// Parents of `levels` consecutive levels: a workgroup hashes 2 * 256 children
+// (level `in`) into 256 parents, then 128, ... down to 512 >> levels, writing
+// each level to its place in the tree. n_in children in all (a power of 2).
+__global__ __launch_bounds__(256) void tree_kernel(const uint64_t* __restrict__ in, int64_t n_in,
+                                                   uint64_t* __restrict__ out, int32_t levels) {
+  __shared__ uint64_t nodes[256 * 4];
+  const int tid = threadIdx.x;
+  const int64_t first = (int64_t)blockIdx.x * 512;  // first child of this workgroup
+  int64_t n_level = n_in;                           // children at the current level (whole tree)
+  uint64_t* level_out = out;
+  int cnt = (int)min<int64_t>(512, n_in);            // this workgroup's children at the current level
+  for (int d = 0; d < levels; ++d) {
+    const int parents = cnt / 2;
+    uint64_t h[8];
+    const bool act = tid < parents;
+    if (act) {
+      uint64_t m[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = d == 0 ? in[(first + 2 * tid) * 4 + i] : nodes[2 * tid * 4 + i];
+#pragma unroll
+      for (int i = 8; i < 16; ++i) m[i] = 0;
+      b2_init32(h);
+      b2_compress(h, m, 64, true);
+    }
+    __syncthreads();
+    const int64_t pfirst = (first >> (d + 1));  // this workgroup's first parent at level d + 1
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nodes[tid * 4 + i] = h[i];
+        level_out[(pfirst + tid) * 4 + i] = h[i];
+      }
+    }
+    __syncthreads();
+    level_out += (n_level / 2) * 4;
+    n_level /= 2;
+    cnt = parents;
+  }
+}
+
+int plan_passes(int L, int (&lN)[NTT_MAXP]) {
+  const int P = (L + 7) / 8;
+  for (int q = 0; q < P; ++q) lN[q] = L / P + (q < L % P ? 1 : 0);
+  for (int q = P; q < NTT_MAXP; ++q) lN[q] = 0;
+  return P;
+}
+
+uint64_t host_mul(uint64_t a, uint64_t b) { return (uint64_t)(((unsigned __int128)a * b) % gl::P); }
+uint64_t host_pow(uint64_t a, uint64_t e) {
+  uint64_t r = 1;
+  while (e) {
+    if (e & 1) r = host_mul(r, a);
+    a = host_mul(a, a);
+    e >>= 1;
+  }
+  return r;
+}
+
+struct EncLayout {
+  int P;
+  size_t tw_bytes, tmp_bytes;
+};
+
+EncLayout enc_layout(int32_t rows, int32_t logn) {
+  EncLayout e{};
+  const int L = logn + 1;
+  int lN[NTT_MAXP];
+  e.P = plan_passes(L, lN);
+  const size_t nlo = (size_t)1 << (L < TW_BITS ? L : TW_BITS);
+  const size_t nhi = L > TW_BITS ? (size_t)1 << (L - TW_BITS) : 1;
+  e.tw_bytes = fpi::align_up((nlo + nhi) * 8, 256);
+  e.tmp_bytes = e.P > 1 ? fpi::align_up((size_t)rows << L, 32) * 8 : 0;
+  return e;
+}
+
+}  // namespace
+
+extern "C" int fp_commit_pack(const int8_t* A, int64_t na, const int8_t* B, int64_t nb, int32_t logn, int32_t rows,
+                              fp_elem* msg, hipStream_t stream) {
+  const char* fn = "fp_commit_pack";
+  if (na < 0 || nb < 0 || rows < 0) return fpi::fail(FP_EARG, "%s: negative size", fn);
+  if (logn < 0 || logn > FP_MAX_RS_LOGN) return fpi::fail(FP_ESHAPE, "%s: logn=%d outside [0, %d]", fn, logn, FP_MAX_RS_LOGN);
+  const int64_t total = (int64_t)rows << logn;
+  if ((na + nb + 2) / 3 > total) return fpi::fail(FP_ESHAPE, "%s: %lld limbs do not fit %d rows of 2^%d", fn,
+                                                 (long long)(na + nb), rows, logn);
+  if (total == 0) return fpi::ok();
+  if (!msg || (na > 0 && !A) || (nb > 0 && !B)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, A, na, B, nb, total,
+                     msg);
+  const int rc = fpi::check_launch("pack_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" size_t fp_rs_encode_workspace(int32_t rows, int32_t logn) {
+  if (rows <= 0 || logn < 0 || logn > FP_MAX_RS_LOGN) return 0;
+  const EncLayout e = enc_layout(rows, logn);
+  return e.tw_bytes + e.tmp_bytes;
+}
+
+extern "C" int fp_rs_encode(const fp_elem* msg, int64_t ld_msg, int32_t rows, int32_t logn, fp_elem* code,
+                            int64_t ld_code, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_rs_encode";
+  if (rows < 0) return fpi::fail(FP_EARG, "%s: negative rows", fn);
+  if (logn < 0 || logn > FP_MAX_RS_LOGN) return fpi::fail(FP_ESHAPE, "%s: logn=%d outside [0, %d]", fn, logn, FP_MAX_RS_LOGN);
+  const int L = logn + 1;
+  if (ld_msg < ((int64_t)1 << logn) || ld_code < ((int64_t)1 << L))
+    return fpi::fail(FP_ESHAPE, "%s: leading dimensions below 2^logn / 2^(logn+1)", fn);
+  if (rows == 0) return fpi::ok();
+  if (!msg || !code) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const EncLayout e = enc_layout(rows, logn);
+  if (!ws || ws_bytes < e.tw_bytes + e.tmp_bytes)
+    return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, e.tw_bytes + e.tmp_bytes);
+  if (((uintptr_t)ws) & 255) return fpi::fail(FP_EARG, "%s: workspace must be 256-byte aligned", fn);
+  uint64_t* tw_lo = (uint64_t*)ws;
+  uint64_t* tw_hi = tw_lo + ((size_t)1 << (L < TW_BITS ? L : TW_BITS));
+  uint64_t* tmp = (uint64_t*)((char*)ws + e.tw_bytes);
+  const uint64_t w = host_pow(7, (gl::P - 1) >> L);
+  {
+    const int n = (1 << (L < TW_BITS ? L : TW_BITS)) + (L > TW_BITS ? 1 << (L - TW_BITS) : 0);
+    hipLaunchKernelGGL(twiddle_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, w, L, tw_lo, tw_hi);
+    const int rc = fpi::check_launch("twiddle_kernel");
+    if (rc) return rc;
+  }
+  NttArgs a{};
+  a.tw_lo = tw_lo;
+  a.tw_hi = tw_hi;
+  a.L = L;
+  a.P = plan_passes(L, a.lN);
+  const int64_t N = (int64_t)1 << L;
+  for (int p = 0; p < a.P; ++p) {
+    a.p = p;
+    a.first = p == 0;
+    a.last = p == a.P - 1;
+    a.src = p == 0 ? msg : tmp;
+    a.src_rs = p == 0 ? ld_msg : N;
+    a.dst = a.last ? code : tmp;
+    a.dst_rs = a.last ? ld_code : N;
+    int lS = 0, lT = 0;
+    for (int q = p + 1; q < a.P; ++q) lS += a.lN[q];
+    for (int q = 0; q < p; ++q) lT += a.lN[q];
+    a.lS = lS;
+    a.lT = lT;
+    for (int q = 0, t = 0; q < NTT_MAXP - 1; ++q) {
+      int sq = 0;
+      for (int r = q + 1; r < a.P; ++r) sq += a.lN[r];
+      a.dT[q] = t;
+      a.dM[q] = (1 << a.lN[q]) - 1;
+      a.dS[q] = sq;
+      t += a.lN[q];
+    }
+    int64_t bpr;
+    if (!a.last) bpr = ((int64_t)1 << lT) * ((((int64_t)1 << lS) + TILE_C - 1) / TILE_C);
+    else bpr = (((int64_t)1 << lT) + TILE_C - 1) / TILE_C;
+    if (bpr * rows > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many rows", fn);
+    a.blocks_per_row = (int32_t)bpr;
+    const dim3 grid((unsigned)(bpr * rows));
+    switch (a.lN[p]) {
+      case 1: hipLaunchKernelGGL(ntt_pass_kernel<1>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(ntt_pass_kernel<2>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(ntt_pass_kernel<3>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(ntt_pass_kernel<4>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 5: hipLaunchKernelGGL(ntt_pass_kernel<5>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 6: hipLaunchKernelGGL(ntt_pass_kernel<6>, grid, dim3(NTT_T), 0, stream, a); break;
+      case 7: hipLaunchKernelGGL(ntt_pass_kernel<7>, grid, dim3(NTT_T), 0, stream, a); break;
+      default: hipLaunchKernelGGL(ntt_pass_kernel<8>, grid, dim3(NTT_T), 0, stream, a); break;
+    }
+    const int rc = fpi::check_launch("ntt_pass_kernel");
+    if (rc) return rc;
+  }
+  return fpi::ok();
+}
+
+extern "C" int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t log_width,
+                                const uint8_t* salts, uint8_t* tree, hipStream_t stream) {
+  const char* fn = "fp_merkle_commit";
+  if (rows < 0 || rows > FP_MAX_MERKLE_ROWS) return fpi::fail(FP_EARG, "%s: rows=%d outside [0, %d]", fn, rows,
+                                                             FP_MAX_MERKLE_ROWS);
+  if (log_width < 0 || log_width > FP_MAX_RS_LOGN + 1)
+    return fpi::fail(FP_ESHAPE, "%s: log_width=%d outside [0, %d]", fn, log_width, FP_MAX_RS_LOGN + 1);
+  const int64_t width = (int64_t)1 << log_width;
+  if (rows > 0 && ld_code < width) return fpi::fail(FP_ESHAPE, "%s: ld_code < width", fn);
+  if (!salts || !tree || (rows > 0 && !code)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if ((((uintptr_t)salts) & 7) || (((uintptr_t)tree) & 7))
+    return fpi::fail(FP_EARG, "%s: salts and tree must be 8-byte aligned", fn);
+  uint64_t* nodes = (uint64_t*)tree;
+  hipLaunchKernelGGL(leaf_kernel, dim3((unsigned)((width + 255) / 256)), dim3(256), 0, stream, code, ld_code, rows,
+                     width, (const uint64_t*)salts, nodes);
+  int rc = fpi::check_launch("leaf_kernel");
+  if (rc) return rc;
+  // levels above the leaves, at most 9 per launch (512 children per workgroup)
+  int64_t n_in = width;
+  uint64_t* in = nodes;
+  while (n_in > 1) {
+    int levels = 0;
+    while (levels < 9 && (n_in >> levels) > 1) ++levels;
+    const int64_t wgs = (n_in + 511) / 512;
+    uint64_t* out = in + n_in * 4;
+    hipLaunchKernelGGL(tree_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, in, n_in, out, levels);
+    rc = fpi::check_launch("tree_kernel");
+    if (rc) return rc;
+    // the last level this launch wrote starts after the levels before it
+    uint64_t* last = out;
+    for (int d = 1; d < levels; ++d) last += (n_in >> d) * 4;
+    in = last;
+    n_in >>= levels;
+  }
+  return fpi::ok();
+}
