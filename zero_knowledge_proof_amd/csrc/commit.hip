@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ A,
 // --------------------------------------------------------------------- NTT
 constexpr int NTT_MAXP = 3;   // passes (N <= 2^24)
 constexpr int TILE_C = 32;    // columns (or transforms) per workgroup
+constexpr int TILE_P = TILE_C + 1;  // LDS row pitch: a column walk touches 32 distinct banks
 constexpr int NTT_T = 256;    // threads
 constexpr int TW_BITS = 12;   // w^e = hi[e >> 12] * lo[e & 4095]
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ uint64_t w_pow(const NttArgs& a, int64_t e) {
 // plus the pass's in-tile twiddles w_{N_p}^i.
 template <int LP>
 __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
-  __shared__ uint64_t tile[256 * TILE_C];
+  __shared__ uint64_t tile[256 * TILE_P];
   __shared__ uint64_t twp[256];
   const int tid = threadIdx.x;
   const int row = blockIdx.x / a.blocks_per_row;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
         v = src[b0 + ((int64_t)n << lS) + c0 + c];
         if (p > 0 && kidx != 0) v = gl::mul(v, w_pow(a, ((int64_t)n << lS) * kidx));
       }
-      tile[n * TILE_C + c] = v;
+      tile[n * TILE_P + c] = v;
     }
   } else {
     for (int idx = tid; idx < total; idx += NTT_T) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
         v = src[base_of(K) + n];
         if (p > 0 && K != 0) v = gl::mul(v, w_pow(a, (int64_t)n * K));
       }
-      tile[n * TILE_C + c] = v;
+      tile[n * TILE_P + c] = v;
     }
   }
   __syncthreads();
@@ -196,19 +197,19 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
   uint64_t v[16];
   for (int nb = g; nb < Rb; nb += G) {
 #pragma unroll
-    for (int i = 0; i < Ra; ++i) v[i] = tile[(i * Rb + nb) * TILE_C + c];
+    for (int i = 0; i < Ra; ++i) v[i] = tile[(i * Rb + nb) * TILE_P + c];
     dft_small<Ra>(v);
 #pragma unroll
     for (int ka = 0; ka < Ra; ++ka) {
       const uint64_t x = (nb * ka) ? gl::mul(v[ka], twp[nb * ka]) : v[ka];
-      tile[(ka * Rb + nb) * TILE_C + c] = x;
+      tile[(ka * Rb + nb) * TILE_P + c] = x;
     }
   }
   __syncthreads();
   // stage B over n_b (contiguous), k_p = k_a + R_a k_b
   for (int ka = g; ka < Ra; ka += G) {
 #pragma unroll
-    for (int i = 0; i < Rb; ++i) v[i] = tile[(ka * Rb + i) * TILE_C + c];
+    for (int i = 0; i < Rb; ++i) v[i] = tile[(ka * Rb + i) * TILE_P + c];
     dft_small<Rb>(v);
     if (c < ncols) {
       if (!a.last) {
@@ -336,43 +337,61 @@ __global__ __launch_bounds__(256) void leaf_kernel(const uint64_t* __restrict__ 
   for (int i = 0; i < 4; ++i) out[i] = h[i];
 }
 
-// Parents of `levels` consecutive levels: a workgroup hashes 2 * 256 children
-// (level `in`) into 256 parents, then 128, ... down to 512 >> levels, writing
-// each level to its place in the tree. n_in children in all (a power of 2).
-__global__ __launch_bounds__(256) void tree_kernel(const uint64_t* __restrict__ in, int64_t n_in,
-                                                   uint64_t* __restrict__ out, int32_t levels) {
-  __shared__ uint64_t nodes[256 * 4];
-  const int tid = threadIdx.x;
-  const int64_t first = (int64_t)blockIdx.x * 512;  // first child of this workgroup
-  int64_t n_level = n_in;                           // children at the current level (whole tree)
-  uint64_t* level_out = out;
-  int cnt = (int)min<int64_t>(512, n_in);            // this workgroup's children at the current level
-  for (int d = 0; d < levels; ++d) {
-    const int parents = cnt / 2;
+// K levels above level `in` (n_in digests): thread t hashes its 2^K children
+// [t 2^K, (t+1) 2^K) up to one node, writing every node of its subtree to its
+// level (out: the level above `in`, then the next, ...). Whole lanes stay busy
+// at every level, and each thread reads and writes contiguous runs.
+template <int K>
+__global__ __launch_bounds__(256) void subtree_kernel(const uint64_t* __restrict__ in, int64_t n_in,
+                                                      uint64_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (n_in >> K)) return;
+  constexpr int H = 1 << (K - 1);  // nodes of the first level above the children
+  uint64_t d[H][4];
+  int64_t n_level = n_in >> 1;     // nodes in the level being written
+  uint64_t* level = out;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    uint64_t m[16];
+    const uint64_t* c = in + (t * (2 * H) + 2 * i) * 4;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) m[w] = c[w];
+#pragma unroll
+    for (int w = 8; w < 16; ++w) m[w] = 0;
     uint64_t h[8];
-    const bool act = tid < parents;
-    if (act) {
-      uint64_t m[16];
+    b2_init32(h);
+    b2_compress(h, m, 64, true);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m[i] = d == 0 ? in[(first + 2 * tid) * 4 + i] : nodes[2 * tid * 4 + i];
+    for (int w = 0; w < 4; ++w) d[i][w] = h[w];
+  }
 #pragma unroll
-      for (int i = 8; i < 16; ++i) m[i] = 0;
-      b2_init32(h);
-      b2_compress(h, m, 64, true);
-    }
-    __syncthreads();
-    const int64_t pfirst = (first >> (d + 1));  // this workgroup's first parent at level d + 1
-    if (act) {
+  for (int lev = 0; lev < K; ++lev) {
+    const int cnt = H >> lev;  // nodes of this level in the subtree
+    if (lev > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nodes[tid * 4 + i] = h[i];
-        level_out[(pfirst + tid) * 4 + i] = h[i];
+      for (int i = 0; i < cnt; ++i) {
+        uint64_t m[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          m[w] = d[2 * i][w];
+          m[w + 4] = d[2 * i + 1][w];
+        }
+#pragma unroll
+        for (int w = 8; w < 16; ++w) m[w] = 0;
+        uint64_t h[8];
+        b2_init32(h);
+        b2_compress(h, m, 64, true);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) d[i][w] = h[w];
       }
     }
-    __syncthreads();
-    level_out += (n_level / 2) * 4;
-    n_level /= 2;
-    cnt = parents;
+    uint64_t* o = level + t * cnt * 4;
+#pragma unroll
+    for (int i = 0; i < cnt; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[i * 4 + w] = d[i][w];
+    level += n_level * 4;
+    n_level >>= 1;
   }
 }
 
@@ -525,16 +544,19 @@ extern "C" int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t ro
                      width, (const uint64_t*)salts, nodes);
   int rc = fpi::check_launch("leaf_kernel");
   if (rc) return rc;
-  // levels above the leaves, at most 9 per launch (512 children per workgroup)
+  // levels above the leaves, up to 3 per launch (a subtree of 8 children per thread)
   int64_t n_in = width;
   uint64_t* in = nodes;
   while (n_in > 1) {
     int levels = 0;
-    while (levels < 9 && (n_in >> levels) > 1) ++levels;
-    const int64_t wgs = (n_in + 511) / 512;
+    while (levels < 3 && (n_in >> levels) > 1) ++levels;
+    const int64_t threads = n_in >> levels;
     uint64_t* out = in + n_in * 4;
-    hipLaunchKernelGGL(tree_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, in, n_in, out, levels);
-    rc = fpi::check_launch("tree_kernel");
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (levels == 3) hipLaunchKernelGGL(subtree_kernel<3>, grid, dim3(256), 0, stream, in, n_in, out);
+    else if (levels == 2) hipLaunchKernelGGL(subtree_kernel<2>, grid, dim3(256), 0, stream, in, n_in, out);
+    else hipLaunchKernelGGL(subtree_kernel<1>, grid, dim3(256), 0, stream, in, n_in, out);
+    rc = fpi::check_launch("subtree_kernel");
     if (rc) return rc;
     // the last level this launch wrote starts after the levels before it
     uint64_t* last = out;
