@@ -12,7 +12,9 @@ average launch time, timed with HIP events on the stream the kernels run on;
 ``cpu_baseline`` times the CPU oracle on the same workload (rank 0, N=1).
 ``request_vectors`` measures the batch fold of the workload's first weight
 matrix by 64 requests' eq vectors (one pass over the weights) beside 64
-one-pass folds, with its own roofline and oracle time.
+one-pass folds, with its own roofline and oracle time; ``commitment`` measures
+the commitment of the layer's Y and R (limb packing, Reed-Solomon encoding of
+rows of 2^22 into 2^23 by NTT, a salted BLAKE2b Merkle tree over the columns).
 """
 from __future__ import annotations
 
@@ -227,6 +229,112 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
     return res
 
 
+B2_OPS = 12 * 8 * 26 + 16 * 2  # 32-bit VALU operations per BLAKE2b compression (see DESIGN)
+VALU_PEAK = 256 * 4 * 16 * 2.4e9  # 32-bit lane operations/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+
+
+def commitment_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, logn: int = 22) -> dict:
+    """Commitment of the layer's Y and R as the pages commit a table: limbs
+    packed three per element into rows of 2^22, each row Reed-Solomon encoded
+    into 2^23 by NTT, a salted BLAKE2b-256 Merkle tree over the 2^23 columns.
+    Y and R come from the GPU witness of this workload; the salts are seeded
+    synthetic bytes. Each step (pack, encode, tree, and all three) is timed as
+    per_graph calls in one HIP graph."""
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+    if not cfg.matmuls:
+        return None
+    m = cfg.matmuls[0]
+    X = torch.from_numpy(np.ascontiguousarray(inp[m.x])).to(dev)
+    W = torch.from_numpy(np.ascontiguousarray(inp[m.w])).to(dev)
+    _, Y, R = fp.witness_linear(X, W, cfg.s, with_z=False)
+    Y, R = Y.contiguous(), R.contiguous()
+    rows = fp.commit_rows(Y.numel(), R.numel(), logn)
+    width = 2 << logn
+    salts_np = synth.raw(synth.data_seed(cfg.seed, 1 << 21), width * fp.SALT_BYTES // 8).view(np.uint8)
+    salts = torch.from_numpy(salts_np.reshape(width, fp.SALT_BYTES)).to(dev)
+    msg = torch.empty((rows, 1 << logn), dtype=torch.int64, device=dev)
+    code = torch.empty((rows, width), dtype=torch.int64, device=dev)
+    tree = torch.empty((2 * width - 1, fp.DIGEST_BYTES), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def pack():
+        fp.commit_pack(Y, R, logn, rows, out=msg)
+
+    def encode():
+        fp.rs_encode(msg, code=code)
+
+    def merkle():
+        fp.merkle_commit(code, salts, tree=tree)
+
+    def chain():
+        pack()
+        encode()
+        merkle()
+
+    def timed(fn):
+        fn()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // per_graph)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph) * 1e-3
+
+    t = {"pack": timed(pack), "encode": timed(encode), "merkle": timed(merkle), "commit": timed(chain)}
+    N = width
+    enc_bytes = rows * (N // 2 * 8 + N * 8 + 4 * N * 8)  # pass 1 reads half, writes all; passes 2, 3 read + write
+    leaf_blocks = -(-(fp.SALT_BYTES + 8 * rows) // 128)
+    compressions = width * leaf_blocks + (width - 1)
+    res = {
+        "workload": "Y and R of %s (%d x %d int8 each): %d limbs in %d rows of 2^%d, codewords of 2^%d, "
+                    "Merkle tree over %d columns" % (m.name, cfg.T, m.d_out, Y.numel() + R.numel(), rows, logn,
+                                                    logn + 1, width),
+        "ms": round(t["commit"] * 1e3, 4), "tokens_per_s": round(cfg.T / t["commit"], 1),
+        "phases_ms": {k: round(v * 1e3, 4) for k, v in t.items() if k != "commit"},
+        "compressions": compressions,
+        "roofline": {"bound": "alu", "kernel": "merkle (leaf + tree launches)",
+                     "achieved": round(compressions * B2_OPS / t["merkle"] / 1e12, 2),
+                     "peak": VALU_PEAK / 1e12, "unit": "T int32 ops/s",
+                     "frac": round(compressions * B2_OPS / t["merkle"] / VALU_PEAK, 4), "traffic": None,
+                     "G_compressions_per_s": round(compressions / t["merkle"] / 1e9, 2)},
+        "encode_roofline": {"bound": "hbm", "achieved": round(enc_bytes / t["encode"] / 1e9, 1),
+                            "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": round(enc_bytes / t["encode"] / HBM_PEAK, 4), "algorithmic_bytes": enc_bytes},
+    }
+    if with_cpu:
+        import oracle
+        Yn, Rn = Y.cpu().numpy(), R.cpu().numpy()
+        oracle.lib()
+        c0 = time.perf_counter()
+        msg_o = oracle.pack_limbs(Yn, Rn, logn)
+        code_o = oracle.rs_encode(msg_o)
+        t_enc = time.perf_counter() - c0
+        ns = 1 << 15  # leaves of a 2^15-column subtree
+        c0 = time.perf_counter()
+        oracle.merkle_tree(code_o[:, :ns], salts_np.reshape(width, fp.SALT_BYTES)[:ns])
+        t_hash = time.perf_counter() - c0
+        total = t_enc + t_hash * compressions / (2 * ns - 1)
+        res["cpu_baseline"] = {"value": round(cfg.T / total, 2), "unit": "tokens/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                               "kind": "oracle",
+                               "sample": "packing and encoding in full (%.2f s); the hashes of a 2^15-column subtree "
+                                         "(%.2f s) scaled to all %d compressions" % (t_enc, t_hash, compressions)}
+        res["matches_oracle_code"] = bool(np.array_equal(code.cpu().numpy().view(np.uint64), code_o))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +345,8 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="prove steps one after another instead of overlapping each step's sum-check with the "
                          "next step's witness GEMM")
+    ap.add_argument("--no-commitment", action="store_true",
+                    help="skip the commitment measurement (Y and R packed, Reed-Solomon encoded, Merkle hashed)")
     ap.add_argument("--no-request-vectors", action="store_true",
                     help="skip the batch request-vector measurement (64 eq vectors folded against the first weight "
                          "matrix in one pass)")
@@ -356,6 +466,8 @@ def main():
         "phases": extras,
         "wall_s": round(wall, 3),
     }
+    if not args.no_commitment:
+        out["commitment"] = commitment_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
     if not args.no_request_vectors:
         out["request_vectors"] = request_vectors_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, inp, ch)
