@@ -123,7 +123,7 @@ __device__ __forceinline__ uint64_t w_pow(const NttArgs& a, int64_t e) {
 }
 
 // One pass of N_p = 2^LP points: see the file comment. LDS tile [N_p][TILE_C]
-// plus the pass's in-tile twiddles w_{N_p}^i.
+// (between the two register transforms) plus the pass's in-tile twiddles w_{N_p}^i.
 template <int LP>
 __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
   __shared__ uint64_t tile[256 * TILE_P];
@@ -162,58 +162,65 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
 
   // in-tile twiddles w_{N_p}^i = w_N^(i N / N_p)
   for (int i = tid; i < Np; i += NTT_T) twp[i] = w_pow(a, (int64_t)i << (a.L - lp));
-
-  // ---- load (with the pass twiddle w^(n_p S_p K))
-  const int total = Np * TILE_C;
-  if (!a.last) {
-    const int64_t b0 = base_of(kidx);
-    for (int idx = tid; idx < total; idx += NTT_T) {
-      const int n = idx / TILE_C, c = idx % TILE_C;
-      uint64_t v = 0;
-      if (c < ncols && !(a.first && n >= Np / 2)) {
-        v = src[b0 + ((int64_t)n << lS) + c0 + c];
-        if (p > 0 && kidx != 0) v = gl::mul(v, w_pow(a, ((int64_t)n << lS) * kidx));
-      }
-      tile[n * TILE_P + c] = v;
-    }
-  } else {
-    for (int idx = tid; idx < total; idx += NTT_T) {
-      const int c = idx / Np, n = idx % Np;
-      uint64_t v = 0;
-      const int64_t K = c0 + c;
-      if (c < ncols && !(a.first && n >= Np / 2)) {
-        v = src[base_of(K) + n];
-        if (p > 0 && K != 0) v = gl::mul(v, w_pow(a, (int64_t)n * K));
-      }
-      tile[n * TILE_P + c] = v;
-    }
-  }
   __syncthreads();
 
-  // ---- N_p = R_a R_b: stage A over n_a (stride R_b), twiddle w_{N_p}^(n_b k_a)
+  // ---- N_p = R_a R_b. Stage A: each task (n_b, column) loads its R_a elements
+  // n = i R_b + n_b straight from HBM, applies the pass twiddle w^(n S_p K)
+  // as x y^i (x = w^(n_b S_p K), y = w^(R_b S_p K)), transforms over i, applies
+  // w_{N_p}^(n_b k_a) and leaves the result in LDS at (k_a R_b + n_b).
   constexpr int la = (LP + 1) / 2, lb = LP / 2;
   constexpr int Ra = 1 << la, Rb = 1 << lb;
-  const int c = tid % TILE_C, g = tid / TILE_C, G = NTT_T / TILE_C;
+  constexpr int TASKS = Rb * TILE_C;
   uint64_t v[16];
-  for (int nb = g; nb < Rb; nb += G) {
+  const int64_t b0 = a.last ? 0 : base_of(kidx);
+  for (int q = tid; q < TASKS; q += NTT_T) {
+    int nb, cc;
+    int64_t rowbase, K;
+    int sh;
+    if (!a.last) {  // lanes along columns: 256-byte runs
+      cc = q % TILE_C;
+      nb = q / TILE_C;
+      K = kidx;
+      rowbase = b0 + c0 + cc;
+      sh = lS;
+    } else {  // lanes along n_b, then transforms: R_b-element runs
+      cc = q / Rb;
+      nb = q % Rb;
+      K = c0 + cc;
+      rowbase = cc < ncols ? base_of(K) : 0;
+      sh = 0;
+    }
+    const bool ok = cc < ncols;
 #pragma unroll
-    for (int i = 0; i < Ra; ++i) v[i] = tile[(i * Rb + nb) * TILE_P + c];
+    for (int i = 0; i < Ra; ++i) {
+      const int n = i * Rb + nb;
+      v[i] = (ok && !(a.first && n >= Np / 2)) ? src[rowbase + ((int64_t)n << sh)] : 0;
+    }
+    if (p > 0 && K != 0) {
+      uint64_t cur = w_pow(a, ((int64_t)nb << sh) * K);
+      const uint64_t y = w_pow(a, ((int64_t)Rb << sh) * K);
+#pragma unroll
+      for (int i = 0; i < Ra; ++i) {
+        v[i] = gl::mul(v[i], cur);
+        if (i + 1 < Ra) cur = gl::mul(cur, y);
+      }
+    }
     dft_small<Ra>(v);
 #pragma unroll
     for (int ka = 0; ka < Ra; ++ka) {
       const uint64_t x = (nb * ka) ? gl::mul(v[ka], twp[nb * ka]) : v[ka];
-      tile[(ka * Rb + nb) * TILE_P + c] = x;
+      tile[(ka * Rb + nb) * TILE_P + cc] = x;
     }
   }
   __syncthreads();
   // stage B over n_b (contiguous), k_p = k_a + R_a k_b
+  const int c = tid % TILE_C, g = tid / TILE_C, G = NTT_T / TILE_C;
   for (int ka = g; ka < Ra; ka += G) {
 #pragma unroll
     for (int i = 0; i < Rb; ++i) v[i] = tile[(ka * Rb + i) * TILE_P + c];
     dft_small<Rb>(v);
     if (c < ncols) {
       if (!a.last) {
-        const int64_t b0 = base_of(kidx);
 #pragma unroll
         for (int kb = 0; kb < Rb; ++kb) dst[b0 + ((int64_t)(ka + Ra * kb) << lS) + c0 + c] = v[kb];
       } else {
