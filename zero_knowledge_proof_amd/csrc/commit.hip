@@ -16,11 +16,12 @@
 // (mod N) with K_{p-1} = sum_{q<p} k_q T_q, so pass p multiplies each element by
 // w^(n_p S_p K_{p-1}) and transforms along n_p (N_p <= 256 points, inside LDS);
 // k_p takes n_p's place in memory, and the last pass writes X[K_P] in natural
-// order. A pass works on a [N_p x 32] tile: 32 neighbouring columns (or, in the
-// last pass, 32 neighbouring K) so that every global access is a 256-byte run.
-// Inside the tile an N_p-point transform is two register transforms of at most
-// 16 points, whose twiddles are powers of w_16 = 2^156 (w_64 = 2^39 for this
-// generator, and 2^96 = -1), i.e. shifts.
+// order. A pass works on a [N_p x 16] tile: 16 neighbouring columns (or, in the
+// last pass, 16 neighbouring K), so that global accesses are 128-byte runs. An
+// N_p-point transform is two register transforms of at most 16 points: the
+// first reads its elements straight from HBM, the second reads the first's
+// results through LDS. Their internal twiddles are powers of w_16 = 2^156
+// (w_64 = 2^39 for this generator, and 2^96 = -1), i.e. shifts.
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ A,
 
 // --------------------------------------------------------------------- NTT
 constexpr int NTT_MAXP = 3;   // passes (N <= 2^24)
-constexpr int TILE_C = 32;    // columns (or transforms) per workgroup
+constexpr int TILE_C = 16;   // columns (or transforms) per workgroup (16 measured best of 8, 16, 32)
 constexpr int TILE_P = TILE_C + 1;  // LDS row pitch: a column walk touches 32 distinct banks
 constexpr int NTT_T = 256;    // threads
 constexpr int TW_BITS = 12;   // w^e = hi[e >> 12] * lo[e & 4095]
