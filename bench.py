@@ -229,7 +229,10 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
     return res
 
 
-B2_OPS = 12 * 8 * 26 + 16 * 2  # 32-bit VALU operations per BLAKE2b compression (see DESIGN)
+# gfx950 VALU instructions per BLAKE2b compression at the least: per G, six 64-bit adds (one
+# v_lshl_add_u64 each), four 64-bit xors (two v_xor_b32), rotations by 24, 16, 63 (two v_alignbit_b32
+# each; by 32 none); 12 rounds of 8 G, then 8 words of h ^= v ^ v' (32 v_xor_b32)
+B2_OPS = 12 * 8 * (6 + 8 + 6) + 32
 VALU_PEAK = 256 * 4 * 16 * 2.4e9  # 32-bit lane operations/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 
 
@@ -306,7 +309,7 @@ def commitment_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, lo
         "compressions": compressions,
         "roofline": {"bound": "alu", "kernel": "merkle (leaf + tree launches)",
                      "achieved": round(compressions * B2_OPS / t["merkle"] / 1e12, 2),
-                     "peak": VALU_PEAK / 1e12, "unit": "T int32 ops/s",
+                     "peak": VALU_PEAK / 1e12, "unit": "T VALU instr/s",
                      "frac": round(compressions * B2_OPS / t["merkle"] / VALU_PEAK, 4), "traffic": None,
                      "G_compressions_per_s": round(compressions / t["merkle"] / 1e9, 2)},
         "encode_roofline": {"bound": "hbm", "achieved": round(enc_bytes / t["encode"] / 1e9, 1),

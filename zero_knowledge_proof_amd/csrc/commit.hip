@@ -268,17 +268,34 @@ constexpr unsigned char B2_SIGMA[12][16] = {
     {6, 15, 14, 9, 11, 3, 0, 8, 12, 2, 13, 7, 1, 4, 10, 5}, {10, 2, 8, 4, 7, 6, 1, 5, 15, 11, 9, 14, 3, 12, 13, 0},
     {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15}, {14, 10, 4, 8, 9, 15, 13, 6, 1, 12, 0, 2, 11, 7, 5, 3}};
 
-__device__ __forceinline__ uint64_t rotr64(uint64_t x, int n) { return (x >> n) | (x << (64 - n)); }
+// 64-bit rotation right by a constant, as two 32-bit funnel shifts
+// (v_alignbit_b32): the 64-bit shift-and-or form costs three to four ops.
+template <int N>
+__device__ __forceinline__ uint64_t rotr64(uint64_t x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  uint32_t rl, rh;
+  if constexpr (N == 32) {
+    rl = hi;
+    rh = lo;
+  } else if constexpr (N < 32) {
+    rl = __builtin_amdgcn_alignbit(hi, lo, N);
+    rh = __builtin_amdgcn_alignbit(lo, hi, N);
+  } else {
+    rl = __builtin_amdgcn_alignbit(lo, hi, N - 32);
+    rh = __builtin_amdgcn_alignbit(hi, lo, N - 32);
+  }
+  return ((uint64_t)rh << 32) | rl;
+}
 
 __device__ __forceinline__ void b2_g(uint64_t& a, uint64_t& b, uint64_t& c, uint64_t& d, uint64_t x, uint64_t y) {
   a = a + b + x;
-  d = rotr64(d ^ a, 32);
+  d = rotr64<32>(d ^ a);
   c = c + d;
-  b = rotr64(b ^ c, 24);
+  b = rotr64<24>(b ^ c);
   a = a + b + y;
-  d = rotr64(d ^ a, 16);
+  d = rotr64<16>(d ^ a);
   c = c + d;
-  b = rotr64(b ^ c, 63);
+  b = rotr64<63>(b ^ c);
 }
 
 // h <- compress(h, m, t, last)
