@@ -13,7 +13,10 @@ committed beside the rescaled output). Small scalar field arithmetic here uses
 Python integers with ``% P``. The commitment of Y and R (§3.1: limbs packed
 three to a field element, each row Reed-Solomon encoded by an NTT, each column
 a salted BLAKE2b Merkle leaf) uses the C code for packing and encoding and the
-host's ``hashlib.blake2b`` for every hash.
+host's ``hashlib.blake2b`` for every hash. The lookup that shows the
+remainders are small (§3.1, §4: two products, the keys' one a binary tree whose
+levels are each proved with sum-check) is a product tree, a degree-3
+sum-check per level in C, and its verifier here.
 """
 from __future__ import annotations
 
@@ -71,6 +74,10 @@ def lib():
             "or_root_of_unity": (u64, [i32]),
             "or_rs_encode": (None, [vp, i32, vp]),
             "or_rs_eval": (u64, [vp, i32, i64]),
+            "or_product_tree": (None, [vp, i64, i32, u64, vp]),
+            "or_lookup_counts": (i64, [vp, i64, i32, i32, vp]),
+            "or_sumcheck3": (None, [vp, vp, i32, vp, vp, vp]),
+            "or_eval_deg3": (u64, [vp, u64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -346,6 +353,129 @@ def merkle_verify(root: bytes, leaf: bytes, j: int, path: list) -> bool:
         h = blake2b(h + sib) if j % 2 == 0 else blake2b(sib + h)
         j >>= 1
     return h == root
+
+
+# ----------------------------------------------------------------- lookup --
+# "How fast can FlashProve go", §3.1 (a lookup checks that each rescale
+# remainder is small) and §4 (a lookup shows that two products are equal, one
+# over the keys and one over the table; the keys' product is a binary tree and
+# each level is proved with sum-check).
+LOOKUP_REASONS = {0: "OK", 1: "LEVEL_SUM", 2: "ROUND_SUM", 3: "LEVEL_FINAL", 4: "LEAF_OPENING", 5: "MULTISET"}
+
+
+def product_tree(keys: np.ndarray, L: int, gamma: int) -> list:
+    """Levels of the keys' product tree: level 0 holds the 2^L leaves
+    gamma - key (padded with gamma - 0), level d+1 entry i the product of
+    level d entries 2i and 2i+1; the last level is the root."""
+    keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
+    assert keys.size <= 1 << L
+    flat = np.empty((2 << L) - 1, np.uint64)
+    lib().or_product_tree(_p(keys), keys.size, L, gamma % P, _p(flat))
+    levels, off = [], 0
+    for d in range(L + 1):
+        w = 1 << (L - d)
+        levels.append(flat[off:off + w])
+        off += w
+    return levels
+
+
+def lookup_counts(keys: np.ndarray, L: int, s: int):
+    """(multiplicities of t = -2^(s-1) + i among the padded keys, keys outside)."""
+    keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
+    counts = np.empty(1 << s, np.int64)
+    outside = int(lib().or_lookup_counts(_p(keys), keys.size, L, s, _p(counts)))
+    return counts, outside
+
+
+def table_product(counts: np.ndarray, s: int, gamma: int) -> int:
+    """prod_t (gamma - t)^(m_t) over the table t = -2^(s-1) .. 2^(s-1) - 1."""
+    acc = 1
+    for i, m in enumerate(counts):
+        acc = acc * pow((gamma - (i - (1 << (s - 1)))) % P, int(m), P) % P
+    return acc
+
+
+def sumcheck3(E, V, r):
+    """Degree-3 sum-check of sum_x E[x] V[2x] V[2x+1]: rounds [m, 4] (values at
+    0..3), finals (E, A, B at the point r)."""
+    E, V, r = _u64(E), _u64(V), _u64(r)
+    m = len(r)
+    assert len(E) == 1 << m and len(V) == 2 << m
+    rounds = np.empty((max(m, 1), 4), np.uint64)
+    finals = np.empty(3, np.uint64)
+    lib().or_sumcheck3(_p(E), _p(V), m, _p(r), _p(rounds), _p(finals))
+    return rounds[:m], [int(x) for x in finals]
+
+
+def eval_deg3(g, x: int) -> int:
+    return int(lib().or_eval_deg3(_p(_u64(g)), x % P))
+
+
+def lookup_challenge_offset(L: int, d: int) -> int:
+    """Start of level d's challenges [lambda_d, rho_1 .. rho_(L-1-d)] in the
+    challenge array: levels are proved from d = L-1 down to 0."""
+    return (L - 1 - d) * (L - d) // 2
+
+
+def lookup_challenges_len(L: int) -> int:
+    return L * (L + 1) // 2
+
+
+def grand_product_prove(levels: list, chal) -> list:
+    """The product tree's proof, level by level from the root down: for level d
+    (2^(L-d) entries) the claim on level d+1 at z_(d+1) is reduced by a
+    degree-3 sum-check of eq(z_(d+1), x) V_d(0, x) V_d(1, x) with challenges
+    rho; z_d = (lambda_d, rho) is the next point. Returns per level (rounds,
+    finals)."""
+    L = len(levels) - 1
+    chal = _u64(chal)
+    proof = []
+    z = []  # point of the claim on level d+1
+    for d in range(L - 1, -1, -1):
+        off = lookup_challenge_offset(L, d)
+        m = L - 1 - d
+        rho = chal[off + 1: off + 1 + m]
+        E = eq_table(z) if m else np.ones(1, np.uint64)
+        rounds, finals = sumcheck3(E, levels[d], rho)
+        proof.append((rounds, finals))
+        z = [int(chal[off])] + [int(x) for x in rho]
+    return proof
+
+
+def grand_product_verify(root: int, proof: list, chal, L: int, keys: np.ndarray, gamma: int, counts=None, s=None):
+    """Verifier of the lookup: each level's round sums, the final
+    eq(z, rho) a b, the leaf claim against the keys, and (with counts) the
+    root against the table's product. Returns (reason, level)."""
+    chal = _u64(chal)
+    claim = root % P
+    z = []
+    for idx, d in enumerate(range(L - 1, -1, -1)):
+        rounds, finals = proof[idx]
+        off = lookup_challenge_offset(L, d)
+        m = L - 1 - d
+        rho = [int(x) for x in chal[off + 1: off + 1 + m]]
+        for i in range(m):
+            g = [int(x) for x in rounds[i]]
+            if (g[0] + g[1]) % P != claim:
+                return (1 if i == 0 else 2), d
+            claim = eval_deg3(g, rho[i])
+        e, a, b = finals
+        ez = 1
+        for zj, rj in zip(z, rho):
+            ez = ez * ((zj * rj + (1 - zj) * (1 - rj)) % P) % P
+        if e != ez or claim != ez * a % P * b % P:
+            return 3, d
+        lam = int(chal[off])
+        claim = (a + lam * (b - a)) % P
+        z = [lam] + rho
+    keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
+    E0 = eq_table(z)
+    leaf = (gamma - sum(int(E0[i]) * (int(keys[i]) % P) for i in range(keys.size))) % P
+    if leaf != claim:
+        return 4, 0
+    if counts is not None and table_product(counts, s, gamma) != root % P:
+        return 5, L
+    return 0, -1
 
 
 # ----------------------------------------------------------- layer proofs --

@@ -435,3 +435,97 @@ uint64_t or_rs_eval(const uint64_t* msg, int32_t logn, int64_t j) {
   for (int64_t i = n - 1; i >= 0; --i) acc = or_add(or_mul(acc, x), msg[i] % OR_P);
   return acc;
 }
+
+/* ---------------------------------------------------------------- lookup --
+ * [HF] §3.1: a lookup checks that each rescale remainder is small; §4: a lookup
+ * shows its keys are rows of a table by showing two products equal, one over
+ * the keys and one over the table, the keys' product built as a binary tree
+ * whose levels are each proved with sum-check. Readings where the page is
+ * silent: keys are int8 values; the tree has 2^L leaves gamma - key_i, padded
+ * with gamma - 0 (0 is a row of every remainder table); level d+1 entry i is
+ * the product of level d entries 2i and 2i+1; the table side is
+ * prod_t (gamma - t)^(m_t) with m_t the multiplicity of t among the padded keys. */
+
+/* tree: level 0 (2^L leaves) first, then each level up, the root last. */
+void or_product_tree(const int8_t* keys, int64_t n, int32_t L, uint64_t gamma, uint64_t* tree) {
+  const int64_t N = (int64_t)1 << L;
+  for (int64_t i = 0; i < N; ++i) tree[i] = or_sub(gamma, i < n ? or_from_int(keys[i]) : 0);
+  int64_t off = 0;
+  for (int64_t w = N; w > 1; w /= 2) {
+    for (int64_t i = 0; i < w / 2; ++i) tree[off + w + i] = or_mul(tree[off + 2 * i], tree[off + 2 * i + 1]);
+    off += w;
+  }
+}
+
+/* Multiplicities of the table values t = -2^(s-1) + i, i < 2^s, among the keys
+ * and the 2^L - n padding keys (value 0). Returns the number of keys outside
+ * the table. */
+int64_t or_lookup_counts(const int8_t* keys, int64_t n, int32_t L, int32_t s, int64_t* counts) {
+  const int64_t T = (int64_t)1 << s, lo = -((int64_t)1 << (s - 1));
+  int64_t outside = 0;
+  for (int64_t t = 0; t < T; ++t) counts[t] = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t k = keys[i] - lo;
+    if (k < 0 || k >= T) ++outside;
+    else ++counts[k];
+  }
+  counts[-lo] += ((int64_t)1 << L) - n;
+  return outside;
+}
+
+/* Degree-3 sum-check of sum_x E[x] A[x] B[x] over m variables, with
+ * A[x] = V[2x], B[x] = V[2x+1] (the two children of node x). Round i sends
+ * g_i(0), g_i(1), g_i(2), g_i(3) and binds the lowest remaining variable to
+ * r[i]; finals are E, A, B at the point. */
+void or_sumcheck3(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t* r, uint64_t* rounds,
+                  uint64_t* finals) {
+  const int64_t M = (int64_t)1 << m;
+  uint64_t* e = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)M);
+  uint64_t* a = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)M);
+  uint64_t* b = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)M);
+  for (int64_t x = 0; x < M; ++x) {
+    e[x] = E[x];
+    a[x] = V[2 * x];
+    b[x] = V[2 * x + 1];
+  }
+  for (int32_t i = 0; i < m; ++i) {
+    const int64_t h = M >> (i + 1);
+    uint64_t g[4] = {0, 0, 0, 0};
+    for (int64_t q = 0; q < h; ++q) {
+      const uint64_t de = or_sub(e[2 * q + 1], e[2 * q]), da = or_sub(a[2 * q + 1], a[2 * q]);
+      const uint64_t db = or_sub(b[2 * q + 1], b[2 * q]);
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t ec = or_add(e[2 * q], or_mul((uint64_t)c, de));
+        const uint64_t ac = or_add(a[2 * q], or_mul((uint64_t)c, da));
+        const uint64_t bc = or_add(b[2 * q], or_mul((uint64_t)c, db));
+        g[c] = or_add(g[c], or_mul(ec, or_mul(ac, bc)));
+      }
+    }
+    for (int c = 0; c < 4; ++c) rounds[4 * i + c] = g[c];
+    for (int64_t q = 0; q < h; ++q) {
+      e[q] = or_add(e[2 * q], or_mul(r[i], or_sub(e[2 * q + 1], e[2 * q])));
+      a[q] = or_add(a[2 * q], or_mul(r[i], or_sub(a[2 * q + 1], a[2 * q])));
+      b[q] = or_add(b[2 * q], or_mul(r[i], or_sub(b[2 * q + 1], b[2 * q])));
+    }
+  }
+  finals[0] = e[0];
+  finals[1] = a[0];
+  finals[2] = b[0];
+  free(e);
+  free(a);
+  free(b);
+}
+
+/* A cubic given by its values at 0, 1, 2, 3, evaluated at x (Lagrange form). */
+uint64_t or_eval_deg3(const uint64_t* g, uint64_t x) {
+  const int64_t den[4] = {-6, 2, -2, 6}; /* prod_{j != i} (i - j) */
+  uint64_t acc = 0;
+  for (int i = 0; i < 4; ++i) {
+    uint64_t num = 1;
+    for (int j = 0; j < 4; ++j)
+      if (j != i) num = or_mul(num, or_sub(x, (uint64_t)j));
+    const uint64_t inv = or_pow(or_from_int(den[i]), OR_P - 2);
+    acc = or_add(acc, or_mul(g[i], or_mul(num, inv)));
+  }
+  return acc;
+}

@@ -488,3 +488,88 @@ def test_merkle_tree_by_hand_and_paths():
     code2[1, 5] ^= np.uint64(1)
     lv2 = O.merkle_tree(code2, salts)
     assert lv2[0][5] != lv[0][5] and lv2[-1][0] != root and lv2[0][4] == lv[0][4]
+
+
+# ----------------------------------------------------------------- lookup --
+def test_product_tree_by_hand():
+    keys = np.array([3, -1, 0], np.int8)
+    g = 1000
+    lev = O.product_tree(keys, 2, g)
+    leaves = [g - 3, g + 1, g, g]  # padded with the key 0
+    assert [int(v) for v in lev[0]] == leaves
+    assert [int(v) for v in lev[1]] == [leaves[0] * leaves[1] % P, leaves[2] * leaves[3] % P]
+    assert int(lev[2][0]) == (g - 3) * (g + 1) * g * g % P
+
+
+def test_eval_deg3_interpolates_a_cubic():
+    f = lambda x: (5 * x**3 + 7 * x**2 + (P - 2) * x + 11) % P
+    g = [f(x) for x in range(4)]
+    for x in (4, 9, P - 1, 123456789):
+        assert O.eval_deg3(g, x) == f(x)
+
+
+def _brute_round_values3(E, A, B, r, i, m):
+    """g_i(c), c = 0..3, by enumerating the hypercube over the multilinear
+    extensions of E, A and B by definition."""
+    out = []
+    for c in range(4):
+        tot = 0
+        for b in itertools.product((0, 1), repeat=m - i - 1):
+            pt = list(r[:i]) + [c] + list(b)
+            tot = (tot + O.mle_brute(E, pt) * O.mle_brute(A, pt) * O.mle_brute(B, pt)) % P
+        out.append(tot)
+    return out
+
+
+@pytest.mark.parametrize("m", [0, 1, 2, 3, 4])
+def test_sumcheck3_against_hypercube_enumeration(m):
+    rng = random.Random(300 + m)
+    E = [rng.randrange(P) for _ in range(1 << m)]
+    V = [rng.randrange(P) for _ in range(2 << m)]
+    A, B = V[0::2], V[1::2]
+    r = [rng.randrange(P) for _ in range(m)]
+    rounds, finals = O.sumcheck3(E, V, r)
+    total = sum(e * a * b for e, a, b in zip(E, A, B)) % P
+    if m:
+        assert (int(rounds[0][0]) + int(rounds[0][1])) % P == total
+    for i in range(m):
+        assert [int(v) for v in rounds[i]] == _brute_round_values3(E, A, B, r, i, m)
+    assert finals == [O.mle_brute(E, r), O.mle_brute(A, r), O.mle_brute(B, r)]
+
+
+def test_lookup_proof_verifies_and_negative_controls():
+    L, s = 6, 4
+    rng = np.random.default_rng(31)
+    keys = rng.integers(-8, 8, 50).astype(np.int8)
+    keys[:2] = [-8, 7]
+    gamma = int(synth.challenges(77, 1)[0])
+    chal = synth.challenges(78, O.lookup_challenges_len(L))
+    lev = O.product_tree(keys, L, gamma)
+    root = int(lev[-1][0])
+    counts, outside = O.lookup_counts(keys, L, s)
+    assert outside == 0 and counts.sum() == 1 << L and counts[8] >= (1 << L) - 50
+    # the two products agree exactly when every key is a table row
+    assert O.table_product(counts, s, gamma) == root
+    proof = O.grand_product_prove(lev, chal)
+    assert len(proof) == L and [len(r) for r, _ in proof] == list(range(L))
+    assert O.grand_product_verify(root, proof, chal, L, keys, gamma, counts, s) == (0, -1)
+    # a changed round value, a changed final, a different key, a key off the table
+    bad = [(r.copy(), list(f)) for r, f in proof]
+    bad[3][0][1, 2] = (int(bad[3][0][1, 2]) + 1) % P
+    assert O.grand_product_verify(root, bad, chal, L, keys, gamma)[0] == 2
+    bad = [(r.copy(), list(f)) for r, f in proof]
+    bad[2][0][0, 0] = (int(bad[2][0][0, 0]) + 1) % P
+    assert O.grand_product_verify(root, bad, chal, L, keys, gamma)[0] == 1
+    bad = [(r.copy(), list(f)) for r, f in proof]
+    bad[4][1][1] = (bad[4][1][1] + 1) % P
+    assert O.grand_product_verify(root, bad, chal, L, keys, gamma)[0] == 3
+    k2 = keys.copy()
+    k2[10] ^= 1
+    assert O.grand_product_verify(root, proof, chal, L, k2, gamma)[0] == 4
+    k3 = keys.copy()
+    k3[5] = 100  # outside [-8, 8)
+    lev3 = O.product_tree(k3, L, gamma)
+    c3, out3 = O.lookup_counts(k3, L, s)
+    assert out3 == 1
+    p3 = O.grand_product_prove(lev3, chal)
+    assert O.grand_product_verify(int(lev3[-1][0]), p3, chal, L, k3, gamma, c3, s) == (5, L)
