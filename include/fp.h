@@ -213,6 +213,49 @@ size_t fp_rs_encode_workspace(int32_t rows, int32_t logn);
 int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t log_width, const uint8_t* salts,
                      uint8_t* tree, hipStream_t stream);
 
+/* -------------------------------------------------------------- lookup --- */
+/* The lookup that shows the remainders R are small ("How fast can FlashProve
+ * go", §3.1: a lookup checks that each rescale remainder is small; §4: a
+ * lookup shows two products equal, one over the keys and one over the table,
+ * the keys' product built as a binary tree whose levels are each proved with
+ * sum-check).
+ *
+ * fp_lookup_tree: tree receives 2^(L+1) - 1 field elements: level 0 = the 2^L
+ * leaves gamma - key_i (keys[i] as a field element for i < n, 0 for
+ * n <= i < 2^L), level d+1 entry i = (level d entry 2i) * (entry 2i+1), each
+ * level after the one below it, the root last. gamma: device pointer to one
+ * field element. 0 <= n <= 2^L, L <= FP_MAX_N. */
+int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp_elem* gamma, fp_elem* tree,
+                   hipStream_t stream);
+
+/* Multiplicities of the table values t = -2^(s-1) + i (i < 2^s, 1 <= s <= 8)
+ * among the n keys and the 2^L - n padding keys (value 0): counts[i]; keys
+ * outside the table are counted in counts[2^s]. counts: device, 2^s + 1
+ * entries, overwritten. */
+int fp_lookup_counts(const int8_t* keys, int64_t n, int32_t L, int32_t s, uint32_t* counts, hipStream_t stream);
+
+/* Degree-3 sum-check of sum_{x < 2^m} E[x] V[2x] V[2x+1] (0 <= m < FP_MAX_N):
+ * round i writes rounds[4i + c] = g_i(c) for c = 0..3 and then binds the
+ * lowest remaining variable to r[i] (r_i is applied only after g_i is
+ * complete); finals = E, A, B at the point r, with A[x] = V[2x],
+ * B[x] = V[2x+1]. E: 2^m, V: 2^(m+1) canonical elements. ws:
+ * fp_sumcheck3_workspace(m) bytes, 8-byte aligned. */
+int fp_sumcheck3_prove(const fp_elem* E, const fp_elem* V, int32_t m, const fp_elem* r, fp_elem* rounds,
+                       fp_elem* finals, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t fp_sumcheck3_workspace(int32_t m);
+
+/* The product tree's proof from the root down (1 <= L <= FP_MAX_N): for
+ * d = L-1 .. 0 the claim on level d+1 at z_{d+1} is reduced to level d by the
+ * degree-3 sum-check with E = eq(z_{d+1}, .) and V = level d of tree. chal holds,
+ * for d from L-1 down to 0, the block [lambda_d, rho_1 .. rho_{L-1-d}]
+ * (L(L+1)/2 elements): rho are level d's round challenges and the block is
+ * z_d (z_L is empty). Outputs in the same level order: rounds (L(L-1)/2
+ * rounds of 4 values) and finals (3 per level). ws:
+ * fp_lookup_prove_workspace(L) bytes, 256-byte aligned. */
+int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+size_t fp_lookup_prove_workspace(int32_t L);
+
 /* ----------------------------------------------------------------- MLE --- */
 /* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading
  * dim ld) zero-padded to [2^n_rows, 2^n_cols]; rows <= 2^n_rows and

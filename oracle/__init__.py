@@ -470,7 +470,8 @@ def grand_product_verify(root: int, proof: list, chal, L: int, keys: np.ndarray,
         z = [lam] + rho
     keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
     E0 = eq_table(z)
-    leaf = (gamma - sum(int(E0[i]) * (int(keys[i]) % P) for i in range(keys.size))) % P
+    dot = int(fold_rows(keys.reshape(-1, 1), E0[:keys.size])[0]) if keys.size else 0  # sum_i eq(z, i) key_i
+    leaf = (gamma - dot) % P
     if leaf != claim:
         return 4, 0
     if counts is not None and table_product(counts, s, gamma) != root % P:

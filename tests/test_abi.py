@@ -78,6 +78,14 @@ def test_argument_errors_without_gpu():
     assert L.fp_rs_encode(dummy, 1 << 22, 2, 22, dummy, 1 << 23, dummy, need - 1, None) == 4
     assert L.fp_merkle_commit(dummy, 1 << 26, 1, 26, dummy, dummy, None) == 2
     assert L.fp_merkle_commit(dummy, 16, 1, 4, None, dummy, None) == 1
+    # lookup: sizes, s, workspace
+    assert L.fp_lookup_tree(dummy, 10, 31, dummy, dummy, None) == 2
+    assert L.fp_lookup_tree(dummy, 17, 4, dummy, dummy, None) == 2  # n > 2^L
+    assert L.fp_lookup_counts(dummy, 10, 4, 9, dummy, None) == 3
+    assert L.fp_sumcheck3_prove(dummy, dummy, 30, dummy, dummy, dummy, dummy, 1 << 40, None) == 2
+    need = L.fp_lookup_prove_workspace(23)
+    assert need >= (1 << 22) * 8
+    assert L.fp_lookup_prove(dummy, 23, dummy, dummy, dummy, dummy, need - 1, None) == 4
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)

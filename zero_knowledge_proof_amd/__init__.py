@@ -27,7 +27,8 @@ EXPORTS = [
     "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
     "fp_witness_linear_with_sumcheck", "fp_fold_weights_prepare", "fp_fold_matrix_multi",
     "fp_fold_matrix_multi_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
-    "fp_merkle_commit",
+    "fp_merkle_commit", "fp_lookup_tree", "fp_lookup_counts", "fp_sumcheck3_prove", "fp_sumcheck3_workspace",
+    "fp_lookup_prove", "fp_lookup_prove_workspace",
 ]
 
 _lib = None
@@ -92,6 +93,12 @@ def lib():
             "fp_rs_encode": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, sz, vp]),
             "fp_rs_encode_workspace": (sz, [i32, i32]),
             "fp_merkle_commit": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp]),
+            "fp_lookup_tree": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+            "fp_lookup_counts": (ctypes.c_int, [vp, i64, i32, i32, vp, vp]),
+            "fp_sumcheck3_prove": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "fp_sumcheck3_workspace": (sz, [i32]),
+            "fp_lookup_prove": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, sz, vp]),
+            "fp_lookup_prove_workspace": (sz, [i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -148,7 +155,7 @@ class Workspace:
 
 
 _ws_fold, _ws_claim, _ws_mle, _ws_sc = Workspace(), Workspace(), Workspace(), Workspace()
-_ws_multi, _ws_rs = Workspace(), Workspace()
+_ws_multi, _ws_rs, _ws_lookup = Workspace(), Workspace(), Workspace()
 
 
 def to_field_tensor(vals, device=None) -> torch.Tensor:
@@ -370,6 +377,54 @@ def merkle_commit(code, salts, tree=None):
     _check(lib().fp_merkle_commit(_ptr(code), code.stride(0) if rows > 1 else W, rows, logw, _ptr(salts),
                                   _ptr(tree), _stream()), "fp_merkle_commit")
     return tree
+
+
+# ------------------------------------------------------------------- lookup --
+def lookup_tree(keys, L: int, gamma, tree=None):
+    """Product tree [2^(L+1) - 1] of the leaves gamma - key (int8 keys, padded
+    with 0 to 2^L), levels from the leaves up; gamma: device int64 [1]."""
+    n = keys.numel()
+    tree = torch.empty((2 << L) - 1, dtype=torch.int64, device=gamma.device) if tree is None else tree
+    _check(lib().fp_lookup_tree(_ptr(keys) if n else None, n, L, _ptr(gamma), _ptr(tree), _stream()),
+           "fp_lookup_tree")
+    return tree
+
+
+def lookup_counts(keys, L: int, s: int, counts=None):
+    """Multiplicities [2^s + 1] (int32 holding uint32) of the table values
+    -2^(s-1) + i among the padded keys; the last entry counts keys outside."""
+    n = keys.numel()
+    dev = keys.device if n else _dev()
+    counts = torch.empty((1 << s) + 1, dtype=torch.int32, device=dev) if counts is None else counts
+    _check(lib().fp_lookup_counts(_ptr(keys) if n else None, n, L, s, _ptr(counts), _stream()), "fp_lookup_counts")
+    return counts
+
+
+def sumcheck3_prove(E, V, r, rounds=None, finals=None):
+    """Degree-3 sum-check of sum_x E[x] V[2x] V[2x+1]: rounds [m, 4], finals [3]."""
+    m = r.numel()
+    dev = E.device
+    rounds = torch.empty((max(m, 1), 4), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty(3, dtype=torch.int64, device=dev) if finals is None else finals
+    need = lib().fp_sumcheck3_workspace(m)
+    p, nbytes = _ws_lookup.get(need)
+    _check(lib().fp_sumcheck3_prove(_ptr(E), _ptr(V), m, _ptr(r) if m else None, _ptr(rounds), _ptr(finals), p,
+                                    nbytes, _stream()), "fp_sumcheck3_prove")
+    return rounds[:m], finals
+
+
+def lookup_prove(tree, L: int, chal, rounds=None, finals=None):
+    """The product tree's proof: rounds [L(L-1)/2, 4] and finals [L, 3], levels
+    from the root down; chal: device int64 [L(L+1)/2]."""
+    dev = tree.device
+    nr = L * (L - 1) // 2
+    rounds = torch.empty((max(nr, 1), 4), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty((L, 3), dtype=torch.int64, device=dev) if finals is None else finals
+    need = lib().fp_lookup_prove_workspace(L)
+    p, nbytes = _ws_lookup.get(need)
+    _check(lib().fp_lookup_prove(_ptr(tree), L, _ptr(chal), _ptr(rounds), _ptr(finals), p, nbytes, _stream()),
+           "fp_lookup_prove")
+    return rounds[:nr], finals
 
 
 def mle_eval(M, r_rows, r_cols, out=None):

@@ -1,0 +1,436 @@
+// lookup.hip - the lookup that shows committed remainders are small.
+//
+// "How fast can FlashProve go", §3.1: every rescale commits its remainder and a
+// lookup checks that the remainder is small; §4: a lookup shows its keys are
+// rows of a table by showing two products equal, one over the keys and one
+// over the table; the keys' product is built as a binary tree and each level of
+// the tree is proved with sum-check. Here the tree has 2^L leaves gamma - key
+// (padded with gamma - 0), level d+1 entry i = level d entries 2i times 2i+1,
+// and the claim on level d+1 at a point z is reduced to level d by the
+// degree-3 sum-check of eq(z, x) V_d(2x) V_d(2x+1); the next point is
+// (lambda, rho), rho the sum-check's challenges. The table side is the
+// keys' multiplicities.
+//
+// Sum-check rounds: while the tables are large, one launch per round folds the
+// three tables by the previous challenge and emits per-workgroup partial sums
+// of the round polynomial's values at 0..3 (a second small launch adds them);
+// at most 2048 entries are finished by one workgroup in LDS (one pair per
+// thread), one round per four barriers.
+#include <algorithm>
+
+#include "common.hpp"
+#include "gl.hpp"
+
+namespace {
+
+constexpr int LK_T = 256;        // threads of the tree and wide-round launches
+constexpr int LK_K = 4;          // tree levels per launch (16 children per thread)
+constexpr int SC3_TAIL = 2048;   // entries the single-workgroup tail takes (one pair per thread)
+constexpr int SC3_TT = 1024;     // tail threads
+constexpr int SC3_MAXB = 1024;   // workgroups of a wide round
+static_assert(SC3_TAIL <= 2 * SC3_TT, "the tail folds one pair per thread");
+
+// --------------------------------------------------------------- the tree
+// Thread t takes inputs [t 2^K, (t+1) 2^K) of level `in` (or, for the leaves,
+// keys: gamma - key, 0 past n) and writes the K levels above them; with keys,
+// the leaves themselves are written first.
+template <int K, bool LEAVES>
+__global__ __launch_bounds__(LK_T) void tree_kernel(const int8_t* __restrict__ keys, int64_t n,
+                                                    const uint64_t* __restrict__ gamma, const uint64_t* __restrict__ in,
+                                                    int64_t n_in, uint64_t* __restrict__ leaves_out,
+                                                    uint64_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * LK_T + threadIdx.x;
+  if (t >= (n_in >> K)) return;
+  constexpr int W = 1 << K;
+  uint64_t v[W];
+  if constexpr (LEAVES) {
+    const uint64_t g = *gamma;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int64_t j = t * W + i;
+      const int8_t k = j < n ? keys[j] : (int8_t)0;
+      v[i] = gl::sub(g, gl::from_i64(k));
+    }
+#pragma unroll
+    for (int i = 0; i < W; ++i) leaves_out[t * W + i] = v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = in[t * W + i];
+  }
+  int64_t level_n = n_in >> 1;
+  uint64_t* level = out;
+#pragma unroll
+  for (int lev = 0; lev < K; ++lev) {
+    const int cnt = W >> (lev + 1);
+#pragma unroll
+    for (int i = 0; i < cnt; ++i) v[i] = gl::mul(v[2 * i], v[2 * i + 1]);
+#pragma unroll
+    for (int i = 0; i < cnt; ++i) level[t * cnt + i] = v[i];
+    level += level_n;
+    level_n >>= 1;
+  }
+}
+
+// ------------------------------------------------------------ multiplicities
+__global__ __launch_bounds__(256) void counts_zero_kernel(uint32_t* counts, int32_t nb) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < nb) counts[i] = 0;
+}
+
+// counts[i] += keys equal to -2^(s-1) + i; counts[2^s] += keys outside the table.
+// One LDS histogram per workgroup, then one atomic add per bin.
+__global__ __launch_bounds__(256) void counts_kernel(const int8_t* __restrict__ keys, int64_t n, int32_t s,
+                                                     uint32_t* __restrict__ counts) {
+  __shared__ uint32_t h[257];
+  const int T = 1 << s;
+  for (int i = threadIdx.x; i <= T; i += 256) h[i] = 0;
+  __syncthreads();
+  const int lo = -(1 << (s - 1));
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
+    const int k = keys[j] - lo;
+    atomicAdd(&h[(k >= 0 && k < T) ? k : T], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i <= T; i += 256)
+    if (h[i]) atomicAdd(&counts[i], h[i]);
+}
+
+__global__ void counts_pad_kernel(uint32_t* counts, int32_t s, uint32_t pad) {
+  if (threadIdx.x == 0 && pad) counts[1 << (s - 1)] += pad;
+}
+
+// --------------------------------------------------------- degree-3 sum-check
+// Sum over a workgroup of 4 field values per thread; every thread gets the totals.
+template <int NT>
+__device__ __forceinline__ void block_sum4(uint64_t (&g)[4], uint64_t* red) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) g[c] = fpi::wave_total(g[c]);
+  if (lane == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) red[w * 4 + c] = g[c];
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    uint64_t s = 0;
+    for (int i = 0; i < NW; ++i) s = gl::add(s, red[i * 4 + threadIdx.x]);
+    red[NW * 4 + threadIdx.x] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) g[c] = red[NW * 4 + c];
+}
+
+// adds E_c A_c B_c for c = 0..3 along the line between entries 0 and 1
+__device__ __forceinline__ void pair_terms(uint64_t e0, uint64_t e1, uint64_t a0, uint64_t a1, uint64_t b0,
+                                           uint64_t b1, uint64_t (&g)[4]) {
+  const uint64_t de = gl::sub(e1, e0), da = gl::sub(a1, a0), db = gl::sub(b1, b0);
+  uint64_t e = e0, a = a0, b = b0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    g[c] = gl::add(g[c], gl::mul(e, gl::mul(a, b)));
+    if (c < 3) {
+      e = gl::add(e, de);
+      a = gl::add(a, da);
+      b = gl::add(b, db);
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t lerp(uint64_t x0, uint64_t x1, uint64_t r) {
+  return gl::add(x0, gl::mul(r, gl::sub(x1, x0)));
+}
+
+struct Sc3Tables {
+  const uint64_t* E;  // E[x]
+  const uint64_t* A;  // A[x] (interleaved: V, A[x] = V[2x], B[x] = V[2x+1])
+  const uint64_t* B;
+  int32_t interleaved;
+};
+
+__device__ __forceinline__ void load3(const Sc3Tables& t, int64_t x, uint64_t& e, uint64_t& a, uint64_t& b) {
+  e = t.E[x];
+  if (t.interleaved) {
+    a = t.A[2 * x];
+    b = t.A[2 * x + 1];
+  } else {
+    a = t.A[x];
+    b = t.B[x];
+  }
+}
+
+// One wide round. fold = 0: the round polynomial of `in` (pairs q < pairs).
+// fold = 1: `in` folded by *r into `out` (out[x] = in[2x] + r (in[2x+1] - in[2x])),
+// then the round polynomial of `out`. Partial sums into part[block][4].
+__global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t* __restrict__ Eo,
+                                                         uint64_t* __restrict__ Ao, uint64_t* __restrict__ Bo,
+                                                         const uint64_t* __restrict__ r, int32_t fold, int64_t pairs,
+                                                         uint64_t* __restrict__ part) {
+  __shared__ uint64_t red[(LK_T / 64) * 4 + 4];
+  uint64_t g[4] = {0, 0, 0, 0};
+  const uint64_t rr = fold ? *r : 0;
+  for (int64_t q = (int64_t)blockIdx.x * LK_T + threadIdx.x; q < pairs; q += (int64_t)gridDim.x * LK_T) {
+    uint64_t e[2], a[2], b[2];
+    if (fold) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint64_t e0, a0, b0, e1, a1, b1;
+        load3(in, 4 * q + 2 * h, e0, a0, b0);
+        load3(in, 4 * q + 2 * h + 1, e1, a1, b1);
+        e[h] = lerp(e0, e1, rr);
+        a[h] = lerp(a0, a1, rr);
+        b[h] = lerp(b0, b1, rr);
+        Eo[2 * q + h] = e[h];
+        Ao[2 * q + h] = a[h];
+        Bo[2 * q + h] = b[h];
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) load3(in, 2 * q + h, e[h], a[h], b[h]);
+    }
+    pair_terms(e[0], e[1], a[0], a[1], b[0], b[1], g);
+  }
+  block_sum4<LK_T>(g, red);
+  if (threadIdx.x < 4) part[(int64_t)blockIdx.x * 4 + threadIdx.x] = g[threadIdx.x];
+}
+
+// rounds[c] = sum of the nb partials' value c
+__global__ __launch_bounds__(LK_T) void sc3_reduce_kernel(const uint64_t* __restrict__ part, int32_t nb,
+                                                          uint64_t* __restrict__ rounds) {
+  __shared__ uint64_t red[(LK_T / 64) * 4 + 4];
+  uint64_t g[4] = {0, 0, 0, 0};
+  for (int i = threadIdx.x; i < nb; i += LK_T)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = gl::add(g[c], part[(int64_t)i * 4 + c]);
+  block_sum4<LK_T>(g, red);
+  if (threadIdx.x < 4) rounds[threadIdx.x] = g[threadIdx.x];
+}
+
+// The last rounds in one workgroup: `in` (size_in entries, folded by r[i0-1]
+// first when fold) is loaded into LDS, then rounds i0 .. m-1; finals = E, A, B
+// at the point.
+__global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t fold, int64_t size_in,
+                                                          const uint64_t* __restrict__ r, int32_t i0, int32_t m,
+                                                          uint64_t* __restrict__ rounds, uint64_t* __restrict__ finals) {
+  __shared__ uint64_t sE[SC3_TAIL], sA[SC3_TAIL], sB[SC3_TAIL];
+  __shared__ uint64_t red[(SC3_TT / 64) * 4 + 4];
+  const int tid = threadIdx.x;
+  int64_t size = fold ? size_in / 2 : size_in;
+  const uint64_t r0 = fold ? r[i0 - 1] : 0;
+  for (int64_t x = tid; x < size; x += SC3_TT) {
+    if (fold) {
+      uint64_t e0, a0, b0, e1, a1, b1;
+      load3(in, 2 * x, e0, a0, b0);
+      load3(in, 2 * x + 1, e1, a1, b1);
+      sE[x] = lerp(e0, e1, r0);
+      sA[x] = lerp(a0, a1, r0);
+      sB[x] = lerp(b0, b1, r0);
+    } else {
+      load3(in, x, sE[x], sA[x], sB[x]);
+    }
+  }
+  __syncthreads();
+  for (int i = i0; i < m; ++i) {
+    const int64_t pairs = size / 2;
+    uint64_t g[4] = {0, 0, 0, 0};
+    for (int64_t q = tid; q < pairs; q += SC3_TT)
+      pair_terms(sE[2 * q], sE[2 * q + 1], sA[2 * q], sA[2 * q + 1], sB[2 * q], sB[2 * q + 1], g);
+    block_sum4<SC3_TT>(g, red);
+    if (tid < 4) rounds[(int64_t)i * 4 + tid] = g[tid];
+    // r_i is applied only after g_i is complete; size <= SC3_TAIL = 2 SC3_TT, so
+    // every pair has its own thread
+    const uint64_t ri = r[i];
+    uint64_t ne = 0, na = 0, nbv = 0;
+    const bool act = tid < pairs;
+    if (act) {
+      ne = lerp(sE[2 * tid], sE[2 * tid + 1], ri);
+      na = lerp(sA[2 * tid], sA[2 * tid + 1], ri);
+      nbv = lerp(sB[2 * tid], sB[2 * tid + 1], ri);
+    }
+    __syncthreads();
+    if (act) {
+      sE[tid] = ne;
+      sA[tid] = na;
+      sB[tid] = nbv;
+    }
+    __syncthreads();
+    size = pairs;
+  }
+  if (tid == 0) {
+    finals[0] = sE[0];
+    finals[1] = sA[0];
+    finals[2] = sB[0];
+  }
+}
+
+struct Sc3Layout {
+  size_t buf;  // entries of each folded table buffer
+  int nb;      // workgroups of the wide rounds
+  size_t bytes;
+};
+
+Sc3Layout sc3_layout(int32_t m) {
+  Sc3Layout l{};
+  const int64_t S = (int64_t)1 << m;
+  l.buf = S > SC3_TAIL ? (size_t)(S / 2) : 0;
+  const int64_t pairs = S / 2;
+  l.nb = (int)std::min<int64_t>(SC3_MAXB, std::max<int64_t>(1, (pairs + LK_T - 1) / LK_T));
+  l.bytes = 6 * l.buf * 8 + fpi::align_up((size_t)l.nb * 4 * 8, 256);
+  return l;
+}
+
+// Enqueues the degree-3 sum-check (m <= FP_MAX_N - 1); ws of sc3_layout(m).bytes.
+int sc3_enqueue(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t* r, uint64_t* rounds,
+                uint64_t* finals, void* ws, hipStream_t st) {
+  const Sc3Layout l = sc3_layout(m);
+  uint64_t* bufs = (uint64_t*)ws;
+  uint64_t* part = bufs + 6 * l.buf;
+  Sc3Tables in{E, V, nullptr, 1};
+  int64_t size = (int64_t)1 << m;  // entries of `in`
+  int i = 0;
+  int fold = 0;
+  int cur = 0;
+  // wide rounds while the folded tables would exceed the tail's LDS
+  while ((fold ? size / 2 : size) > SC3_TAIL) {
+    const int64_t out_size = fold ? size / 2 : size;
+    const int64_t pairs = out_size / 2;
+    uint64_t* Eo = bufs + (size_t)(3 * cur) * l.buf;
+    uint64_t* Ao = Eo + l.buf;
+    uint64_t* Bo = Ao + l.buf;
+    const int nb = (int)std::min<int64_t>(l.nb, (pairs + LK_T - 1) / LK_T);
+    hipLaunchKernelGGL(sc3_round_kernel, dim3(nb), dim3(LK_T), 0, st, in, Eo, Ao, Bo, fold ? r + (i - 1) : r,
+                       fold, pairs, part);
+    int rc = fpi::check_launch("sc3_round_kernel");
+    if (rc) return rc;
+    hipLaunchKernelGGL(sc3_reduce_kernel, dim3(1), dim3(LK_T), 0, st, part, nb, rounds + (size_t)i * 4);
+    rc = fpi::check_launch("sc3_reduce_kernel");
+    if (rc) return rc;
+    if (fold) {
+      in = Sc3Tables{Eo, Ao, Bo, 0};
+      cur ^= 1;
+      size = out_size;
+    }
+    fold = 1;
+    ++i;
+  }
+  hipLaunchKernelGGL(sc3_tail_kernel, dim3(1), dim3(SC3_TT), 0, st, in, fold, size, r, i, m, rounds, finals);
+  return fpi::check_launch("sc3_tail_kernel");
+}
+
+int64_t level_offset(int32_t L, int32_t d) { return ((int64_t)2 << L) - ((int64_t)2 << (L - d)); }
+
+}  // namespace
+
+extern "C" int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp_elem* gamma, fp_elem* tree,
+                              hipStream_t stream) {
+  const char* fn = "fp_lookup_tree";
+  if (L < 0 || L > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: L=%d outside [0, %d]", fn, L, FP_MAX_N);
+  if (n < 0 || n > ((int64_t)1 << L)) return fpi::fail(FP_ESHAPE, "%s: n=%lld outside [0, 2^L]", fn, (long long)n);
+  if (!gamma || !tree || (n > 0 && !keys)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  // leaves, with up to LK_K levels above them
+  int64_t n_in = (int64_t)1 << L;
+  int k = L < LK_K ? L : LK_K;
+  {
+    const int64_t threads = n_in >> k;
+    const dim3 grid((unsigned)((threads + LK_T - 1) / LK_T));
+    uint64_t* out = tree + n_in;
+    switch (k) {
+      case 0: hipLaunchKernelGGL((tree_kernel<0, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+      case 1: hipLaunchKernelGGL((tree_kernel<1, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+      case 2: hipLaunchKernelGGL((tree_kernel<2, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+      case 3: hipLaunchKernelGGL((tree_kernel<3, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+      default: hipLaunchKernelGGL((tree_kernel<4, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+    }
+    const int rc = fpi::check_launch("tree_kernel");
+    if (rc) return rc;
+  }
+  int32_t d = k;  // levels written so far above the leaves
+  while (d < L) {
+    k = (L - d) < LK_K ? (L - d) : LK_K;
+    const int64_t w = (int64_t)1 << (L - d);  // entries of level d
+    const uint64_t* in = tree + level_offset(L, d);
+    uint64_t* out = tree + level_offset(L, d + 1);
+    const dim3 grid((unsigned)(((w >> k) + LK_T - 1) / LK_T));
+    switch (k) {
+      case 1: hipLaunchKernelGGL((tree_kernel<1, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
+      case 2: hipLaunchKernelGGL((tree_kernel<2, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
+      case 3: hipLaunchKernelGGL((tree_kernel<3, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
+      default: hipLaunchKernelGGL((tree_kernel<4, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
+    }
+    const int rc = fpi::check_launch("tree_kernel");
+    if (rc) return rc;
+    d += k;
+  }
+  return fpi::ok();
+}
+
+extern "C" int fp_lookup_counts(const int8_t* keys, int64_t n, int32_t L, int32_t s, uint32_t* counts,
+                                hipStream_t stream) {
+  const char* fn = "fp_lookup_counts";
+  if (s < 1 || s > 8) return fpi::fail(FP_ERANGE, "%s: s=%d outside [1, 8]", fn, s);
+  if (L < 0 || L > FP_MAX_N || n < 0 || n > ((int64_t)1 << L))
+    return fpi::fail(FP_ESHAPE, "%s: n=%lld, L=%d", fn, (long long)n, L);
+  if (!counts || (n > 0 && !keys)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const int nbins = (1 << s) + 1;
+  hipLaunchKernelGGL(counts_zero_kernel, dim3((nbins + 255) / 256), dim3(256), 0, stream, counts, nbins);
+  int rc = fpi::check_launch("counts_zero_kernel");
+  if (rc) return rc;
+  if (n > 0) {
+    const int64_t blocks = std::min<int64_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(counts_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, keys, n, s, counts);
+    rc = fpi::check_launch("counts_kernel");
+    if (rc) return rc;
+  }
+  const int64_t pad = ((int64_t)1 << L) - n;
+  if (pad > 0xFFFFFFFFll) return fpi::fail(FP_ESHAPE, "%s: padding count exceeds 32 bits", fn);
+  hipLaunchKernelGGL(counts_pad_kernel, dim3(1), dim3(64), 0, stream, counts, s, (uint32_t)pad);
+  rc = fpi::check_launch("counts_pad_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" size_t fp_sumcheck3_workspace(int32_t m) {
+  if (m < 0 || m >= FP_MAX_N) return 0;
+  return sc3_layout(m).bytes;
+}
+
+extern "C" int fp_sumcheck3_prove(const fp_elem* E, const fp_elem* V, int32_t m, const fp_elem* r, fp_elem* rounds,
+                                  fp_elem* finals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_sumcheck3_prove";
+  if (m < 0 || m >= FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: m=%d outside [0, %d)", fn, m, FP_MAX_N);
+  if (!E || !V || !finals || (m > 0 && (!r || !rounds))) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const Sc3Layout l = sc3_layout(m);
+  if (!ws || ws_bytes < l.bytes) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, l.bytes);
+  const int rc = sc3_enqueue(E, V, m, r, rounds, finals, ws, stream);
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" size_t fp_lookup_prove_workspace(int32_t L) {
+  if (L < 1 || L > FP_MAX_N) return 0;
+  return fpi::align_up(((size_t)1 << (L - 1)) * 8, 256) + sc3_layout(L - 1).bytes;
+}
+
+extern "C" int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_lookup_prove";
+  if (L < 1 || L > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: L=%d outside [1, %d]", fn, L, FP_MAX_N);
+  if (!tree || !chal || !finals || (L > 1 && !rounds)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const size_t need = fp_lookup_prove_workspace(L);
+  if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (((uintptr_t)ws) & 255) return fpi::fail(FP_EARG, "%s: workspace must be 256-byte aligned", fn);
+  uint64_t* E = (uint64_t*)ws;
+  void* sc_ws = (char*)ws + fpi::align_up(((size_t)1 << (L - 1)) * 8, 256);
+  int64_t round_off = 0;
+  for (int32_t d = L - 1; d >= 0; --d) {
+    const int32_t m = L - 1 - d;
+    // the claim on level d+1 sits at z = level d+1's challenges (empty at the root)
+    const int64_t off_next = (int64_t)(L - 2 - d) * (L - 1 - d) / 2;  // start of level d+1's challenges
+    int rc = fp_eq_table(m ? chal + off_next : nullptr, m, E, stream);
+    if (rc) return rc;
+    const int64_t off = (int64_t)(L - 1 - d) * (L - d) / 2;  // [lambda_d, rho_1 .. rho_m]
+    rc = sc3_enqueue(E, tree + level_offset(L, d), m, chal + off + 1, rounds + round_off * 4,
+                     finals + (int64_t)(L - 1 - d) * 3, sc_ws, stream);
+    if (rc) return rc;
+    round_off += m;
+  }
+  return fpi::ok();
+}
