@@ -14,7 +14,9 @@ average launch time, timed with HIP events on the stream the kernels run on;
 matrix by 64 requests' eq vectors (one pass over the weights) beside 64
 one-pass folds, with its own roofline and oracle time; ``commitment`` measures
 the commitment of the layer's Y and R (limb packing, Reed-Solomon encoding of
-rows of 2^22 into 2^23 by NTT, a salted BLAKE2b Merkle tree over the columns).
+rows of 2^22 into 2^23 by NTT, a salted BLAKE2b Merkle tree over the columns);
+``lookup`` measures the lookup that shows the remainders R are small (product
+tree, multiplicities, a degree-3 sum-check per tree level).
 """
 from __future__ import annotations
 
@@ -338,6 +340,119 @@ def commitment_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, lo
     return res
 
 
+def lookup_bytes(L: int, n_keys: int, tail: int = 2048) -> int:
+    """Algorithmic HBM bytes of the remainder lookup: the tree (keys in, every
+    level out once), then per level its eq table written once and, per
+    sum-check round launch, the three tables read once (after the first round
+    also written folded), until they fit one workgroup's LDS, whose launch
+    reads them once more."""
+    b = n_keys + 8 * ((2 << L) - 1)
+    for d in range(L - 1, -1, -1):
+        size = 1 << (L - 1 - d)
+        b += 8 * size                # eq table
+        read = 24 * size             # E, and level d's 2 size entries
+        fold = False
+        while (size // 2 if fold else size) > tail:
+            b += read
+            if fold:
+                size //= 2
+                b += 24 * size       # folded E, A, B written
+                read = 24 * size
+            fold = True
+        b += read
+    return b
+
+
+def lookup_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool) -> dict:
+    """The lookup that shows the layer's remainders R are small: the product
+    tree of gamma - r over the padded 2^L remainders, the multiplicities of the
+    2^s table values, and the level-by-level proof of the tree (a degree-3
+    sum-check per level). R comes from the GPU witness of this workload; gamma
+    and the challenges are seeded streams. Timed as per_graph runs per graph."""
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+    if not cfg.matmuls:
+        return None
+    m = cfg.matmuls[0]
+    X = torch.from_numpy(np.ascontiguousarray(inp[m.x])).to(dev)
+    W = torch.from_numpy(np.ascontiguousarray(inp[m.w])).to(dev)
+    _, _, R = fp.witness_linear(X, W, cfg.s, with_z=False)
+    keys = R.contiguous().reshape(-1)
+    n = keys.numel()
+    L = max(1, synth.log2ceil(n))
+    nch = L * (L + 1) // 2
+    gamma_h = synth.challenges(synth.data_seed(cfg.seed, 1 << 22), 1)
+    chal_h = synth.challenges(synth.data_seed(cfg.seed, 1 << 22 | 1), nch)
+    gamma, chal = fp.to_field_tensor(gamma_h), fp.to_field_tensor(chal_h)
+    tree = torch.empty((2 << L) - 1, dtype=torch.int64, device=dev)
+    counts = torch.empty((1 << cfg.s) + 1, dtype=torch.int32, device=dev)
+    rounds = torch.empty((max(1, L * (L - 1) // 2), 4), dtype=torch.int64, device=dev)
+    finals = torch.empty((L, 3), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def build():
+        fp.lookup_tree(keys, L, gamma, tree=tree)
+
+    def count():
+        fp.lookup_counts(keys, L, cfg.s, counts=counts)
+
+    def prove():
+        fp.lookup_prove(tree, L, chal, rounds=rounds, finals=finals)
+
+    def chain():
+        build()
+        count()
+        prove()
+
+    def timed(fn):
+        fn()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // per_graph)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph) * 1e-3
+
+    t = {"tree": timed(build), "counts": timed(count), "prove": timed(prove), "lookup": timed(chain)}
+    nbytes = lookup_bytes(L, n)
+    res = {
+        "workload": "R of %s (%d x %d int8, s=%d): %d keys padded to 2^%d leaves, table of 2^%d values, "
+                    "%d sum-check rounds over %d levels" % (m.name, cfg.T, m.d_out, cfg.s, n, L, cfg.s,
+                                                           L * (L - 1) // 2, L),
+        "ms": round(t["lookup"] * 1e3, 4), "tokens_per_s": round(cfg.T / t["lookup"], 1),
+        "phases_ms": {k: round(v * 1e3, 4) for k, v in t.items() if k != "lookup"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / t["lookup"] / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(nbytes / t["lookup"] / HBM_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes,
+                     "note": "the whole lookup; its %d rounds are sequential (each level's point comes from the "
+                             "level above), so the small levels are latency-bound" % (L * (L - 1) // 2)},
+    }
+    if with_cpu:
+        import oracle
+        kn = keys.cpu().numpy()
+        oracle.lib()
+        c0 = time.perf_counter()
+        lev = oracle.product_tree(kn, L, int(gamma_h[0]))
+        oracle.lookup_counts(kn, L, cfg.s)
+        oracle.grand_product_prove(lev, chal_h)
+        dt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(cfg.T / dt, 2), "unit": "tokens/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                               "kind": "oracle", "sample": "the whole lookup of this layer's remainders, %.2f s" % dt}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +463,8 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="prove steps one after another instead of overlapping each step's sum-check with the "
                          "next step's witness GEMM")
+    ap.add_argument("--no-lookup", action="store_true",
+                    help="skip the remainder lookup measurement (product tree, multiplicities, proof of the tree)")
     ap.add_argument("--no-commitment", action="store_true",
                     help="skip the commitment measurement (Y and R packed, Reed-Solomon encoded, Merkle hashed)")
     ap.add_argument("--no-request-vectors", action="store_true",
@@ -469,6 +586,8 @@ def main():
         "phases": extras,
         "wall_s": round(wall, 3),
     }
+    if not args.no_lookup:
+        out["lookup"] = lookup_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
     if not args.no_commitment:
         out["commitment"] = commitment_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
     if not args.no_request_vectors:

@@ -34,7 +34,7 @@ def _dev(a):
 
 
 # ------------------------------------------------------------------- eq ---
-@pytest.mark.parametrize("n", [0, 1, 2, 7, 8, 9, 13, 16])
+@pytest.mark.parametrize("n", [0, 1, 2, 7, 8, 9, 11, 12, 13, 16, 22])
 def test_eq_table(fp, n):
     rng = _rng(100 + n)
     r = _field(rng, n, specials=(n >= 4))

@@ -1,11 +1,15 @@
 // eq.hip - eq-table expansion: E[k] = eq(r, k) = prod_j (k_j ? r_j : 1 - r_j).
 //
 // "How fast can FlashProve go", §2: a table's folded row is the weighted sum
-// of its rows; these are the weights. A workgroup writes 256 entries: the
-// challenges and their complements are staged in LDS once, each thread takes
-// the product over its entry's low 8 variables as a balanced tree (depth 3, no
-// barriers), and multiplies it by the product over the high variables, which
-// is the same for the whole workgroup.
+// of its rows; these are the weights. A workgroup writes 256 entries, or 4096
+// for tables of at least 2^16:
+// the challenges and their complements are staged in LDS once; each thread
+// takes the product over its entries' low 8 variables (its lane) as a
+// balanced tree (depth 3, no barriers); up to 16 threads form the product over
+// the variables above them (the 4 "mid" variables that differ between a
+// thread's 16 entries, times the high ones, the same for the whole workgroup),
+// and every entry is then one multiply, so large tables are written at memory
+// speed.
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -23,33 +27,50 @@ struct EqList {
   int32_t count;
 };
 
+// Mid variables of an n-variable table: 4 (4096 entries per workgroup) once
+// the table has at least 2^16 entries, none below (256 per workgroup, more
+// workgroups for the small, latency-bound tables).
+__host__ __device__ constexpr int eq_mid(int n) { return n >= 16 ? 4 : 0; }
+
 __device__ __forceinline__ void eq_block(const fp_elem* __restrict__ r, int n, fp_elem* __restrict__ E,
                                          int64_t blk) {
   __shared__ uint64_t f[2][FP_MAX_N];  // f[1][j] = r_j, f[0][j] = 1 - r_j
+  __shared__ uint64_t mh[16];          // product over variables 8 .. n-1 for mid bits k
   const int tid = threadIdx.x;
-  const int nl = n < 8 ? n : 8;
+  const int nl = n < 8 ? n : 8;  // low variables: the lane
+  const int nm = eq_mid(n);      // mid variables: k
+  const int hb = 8 + nm;         // first high variable
   if (tid < n) {
     const uint64_t rj = r[tid];
     f[1][tid] = rj;
     f[0][tid] = gl::sub(1, rj);
   }
   __syncthreads();
-  const int64_t base = blk << 8;
-  // entry base + tid: the product over its low variables as a balanced tree
-  // (factors of absent variables are 1) ...
+  const int64_t base = blk << hb;
+  if (tid < (1 << nm)) {
+    // mid variables from k = tid, high ones from the block (four interleaved
+    // partial products keep the chains short)
+    uint64_t hp[4] = {1, 1, 1, 1};
+#pragma unroll
+    for (int j = 8; j < FP_MAX_N; ++j)
+      if (j < n) hp[j & 3] = gl::mul(hp[j & 3], f[j < hb ? (tid >> (j - 8)) & 1 : (base >> j) & 1][j]);
+    mh[tid] = gl::mul(gl::mul(hp[0], hp[1]), gl::mul(hp[2], hp[3]));
+  }
+  // the product over the lane's low variables as a balanced tree (factors of
+  // absent variables are 1)
   uint64_t lf[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) lf[j] = (j < nl) ? f[(tid >> j) & 1][j] : 1;
   const uint64_t low = gl::mul(gl::mul(gl::mul(lf[0], lf[1]), gl::mul(lf[2], lf[3])),
                                gl::mul(gl::mul(lf[4], lf[5]), gl::mul(lf[6], lf[7])));
-  // ... times the product over the high variables, the same for the whole
-  // block (four interleaved partial products keep the chains short)
-  uint64_t hpart[4] = {1, 1, 1, 1};
-#pragma unroll
-  for (int j = 8; j < FP_MAX_N; ++j)
-    if (j < n) hpart[j & 3] = gl::mul(hpart[j & 3], f[(base >> j) & 1][j]);
-  if (tid < (1 << nl))
-    E[base + tid] = (n > 8) ? gl::mul(low, gl::mul(gl::mul(hpart[0], hpart[1]), gl::mul(hpart[2], hpart[3]))) : low;
+  __syncthreads();
+  if (tid < (1 << nl)) {
+    if (n <= 8) {
+      E[base + tid] = low;
+    } else {
+      for (int k = 0; k < (1 << nm); ++k) E[base + ((int64_t)k << 8) + tid] = gl::mul(low, mh[k]);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void eq_kernel(EqList jl) {
@@ -61,7 +82,7 @@ __global__ __launch_bounds__(256) void eq_kernel(EqList jl) {
   eq_block(j.r, j.n, j.E, (int)blockIdx.x - j.block_start);
 }
 
-inline int64_t eq_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8); }
+inline int64_t eq_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8 - eq_mid(n)); }
 
 }  // namespace
 

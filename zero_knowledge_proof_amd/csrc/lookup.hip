@@ -13,9 +13,9 @@
 //
 // Sum-check rounds: while the tables are large, one launch per round folds the
 // three tables by the previous challenge and emits per-workgroup partial sums
-// of the round polynomial's values at 0..3 (a second small launch adds them);
-// at most 2048 entries are finished by one workgroup in LDS (one pair per
-// thread), one round per four barriers.
+// of the round polynomial's values at 0..3 (the next launch's first workgroup
+// adds them); at most 2048 entries are finished by one workgroup, first 8 per
+// thread in registers, then in one wave with no barriers.
 #include <algorithm>
 
 #include "common.hpp"
@@ -25,10 +25,10 @@ namespace {
 
 constexpr int LK_T = 256;        // threads of the tree and wide-round launches
 constexpr int LK_K = 4;          // tree levels per launch (16 children per thread)
-constexpr int SC3_TAIL = 2048;   // entries the single-workgroup tail takes (one pair per thread)
-constexpr int SC3_TT = 1024;     // tail threads
+constexpr int SC3_TAIL = 2048;   // entries the single-workgroup tail takes
+constexpr int SC3_TT = 256;      // tail threads
 constexpr int SC3_MAXB = 1024;   // workgroups of a wide round
-static_assert(SC3_TAIL <= 2 * SC3_TT, "the tail folds one pair per thread");
+static_assert(SC3_TAIL == 8 * SC3_TT, "the tail starts with 8 entries per thread");
 
 // --------------------------------------------------------------- the tree
 // Thread t takes inputs [t 2^K, (t+1) 2^K) of level `in` (or, for the leaves,
@@ -159,15 +159,37 @@ __device__ __forceinline__ void load3(const Sc3Tables& t, int64_t x, uint64_t& e
   }
 }
 
-// One wide round. fold = 0: the round polynomial of `in` (pairs q < pairs).
-// fold = 1: `in` folded by *r into `out` (out[x] = in[2x] + r (in[2x+1] - in[2x])),
-// then the round polynomial of `out`. Partial sums into part[block][4].
+// Sum of the nb partial value-quadruples of a round (workgroup-wide; every
+// thread gets the totals).
+template <int NT>
+__device__ __forceinline__ void sum_partials(const uint64_t* __restrict__ part, int nb, uint64_t (&g)[4],
+                                             uint64_t* red) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) g[c] = 0;
+  for (int b = threadIdx.x; b < nb; b += NT)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = gl::add(g[c], part[(int64_t)b * 4 + c]);
+  block_sum4<NT>(g, red);
+}
+
+// One wide round i. fold = 0: the round polynomial of `in` (pairs q < pairs).
+// fold = 1: `in` folded by r[i-1] into `out` (out[x] = in[2x] + r (in[2x+1] -
+// in[2x])), then the round polynomial of `out`. Partial sums go to
+// part[block][4]; workgroup 0 first adds the previous round's partials
+// (prev, nb_prev > 0) into rounds[i-1].
 __global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t* __restrict__ Eo,
                                                          uint64_t* __restrict__ Ao, uint64_t* __restrict__ Bo,
                                                          const uint64_t* __restrict__ r, int32_t fold, int64_t pairs,
-                                                         uint64_t* __restrict__ part) {
+                                                         uint64_t* __restrict__ part, const uint64_t* __restrict__ prev,
+                                                         int32_t nb_prev, uint64_t* __restrict__ prev_round) {
   __shared__ uint64_t red[(LK_T / 64) * 4 + 4];
-  uint64_t g[4] = {0, 0, 0, 0};
+  uint64_t g[4];
+  if (blockIdx.x == 0 && nb_prev > 0) {
+    sum_partials<LK_T>(prev, nb_prev, g, red);
+    if (threadIdx.x < 4) prev_round[threadIdx.x] = g[threadIdx.x];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) g[c] = 0;
   const uint64_t rr = fold ? *r : 0;
   for (int64_t q = (int64_t)blockIdx.x * LK_T + threadIdx.x; q < pairs; q += (int64_t)gridDim.x * LK_T) {
     uint64_t e[2], a[2], b[2];
@@ -194,72 +216,144 @@ __global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t*
   if (threadIdx.x < 4) part[(int64_t)blockIdx.x * 4 + threadIdx.x] = g[threadIdx.x];
 }
 
-// rounds[c] = sum of the nb partials' value c
-__global__ __launch_bounds__(LK_T) void sc3_reduce_kernel(const uint64_t* __restrict__ part, int32_t nb,
-                                                          uint64_t* __restrict__ rounds) {
-  __shared__ uint64_t red[(LK_T / 64) * 4 + 4];
-  uint64_t g[4] = {0, 0, 0, 0};
-  for (int i = threadIdx.x; i < nb; i += LK_T)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[c] = gl::add(g[c], part[(int64_t)i * 4 + c]);
-  block_sum4<LK_T>(g, red);
-  if (threadIdx.x < 4) rounds[threadIdx.x] = g[threadIdx.x];
+// The last rounds in one workgroup of SC3_TT = 256 threads. The first adds the
+// previous wide round's partials (nb_prev > 0) into rounds[i0-1]. Then `in`
+// (size_in entries, folded by r[i0-1] first when fold; S <= 2048 entries after
+// that) is held as 8 consecutive entries per thread, and rounds run:
+//  - while a thread holds 2 or more entries, pairs are inside the thread and
+//    only the round sums cross threads (LDS, two barriers);
+//  - the <= 256 left go to wave 0, up to 4 per lane, pairs inside the lane,
+//    round sums by DPP within the wave, no barriers;
+//  - with one entry per lane (<= 64), partners are lane distance 1, 2, 4 ...
+//    apart (shuffles), round sums within the wave.
+// r_i is applied only after g_i is complete. finals = E, A, B at the point.
+constexpr int TQ = SC3_TAIL / SC3_TT;  // entries per thread in the first stage (8)
+
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int d) {
+  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, d, 64);
+  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// The last rounds in one workgroup: `in` (size_in entries, folded by r[i0-1]
-// first when fold) is loaded into LDS, then rounds i0 .. m-1; finals = E, A, B
-// at the point.
 __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t fold, int64_t size_in,
                                                           const uint64_t* __restrict__ r, int32_t i0, int32_t m,
-                                                          uint64_t* __restrict__ rounds, uint64_t* __restrict__ finals) {
-  __shared__ uint64_t sE[SC3_TAIL], sA[SC3_TAIL], sB[SC3_TAIL];
+                                                          uint64_t* __restrict__ rounds, uint64_t* __restrict__ finals,
+                                                          const uint64_t* __restrict__ prev, int32_t nb_prev) {
   __shared__ uint64_t red[(SC3_TT / 64) * 4 + 4];
-  const int tid = threadIdx.x;
-  int64_t size = fold ? size_in / 2 : size_in;
+  __shared__ uint64_t xE[SC3_TT], xA[SC3_TT], xB[SC3_TT];
+  __shared__ uint64_t rs[FP_MAX_N];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t g[4];
+  if (nb_prev > 0) {
+    sum_partials<SC3_TT>(prev, nb_prev, g, red);
+    if (tid < 4) rounds[(int64_t)(i0 - 1) * 4 + tid] = g[tid];
+  }
+  if (tid < m - i0) rs[tid] = r[i0 + tid];
+  const int64_t S = fold ? size_in / 2 : size_in;  // entries after the first fold
   const uint64_t r0 = fold ? r[i0 - 1] : 0;
-  for (int64_t x = tid; x < size; x += SC3_TT) {
-    if (fold) {
-      uint64_t e0, a0, b0, e1, a1, b1;
-      load3(in, 2 * x, e0, a0, b0);
-      load3(in, 2 * x + 1, e1, a1, b1);
-      sE[x] = lerp(e0, e1, r0);
-      sA[x] = lerp(a0, a1, r0);
-      sB[x] = lerp(b0, b1, r0);
-    } else {
-      load3(in, x, sE[x], sA[x], sB[x]);
+  // stage 1: thread t holds entries t q .. t q + q - 1, q = max(1, S / 256)
+  int q = S >= SC3_TT ? (int)(S / SC3_TT) : 1;
+  uint64_t e[TQ], a[TQ], b[TQ];
+#pragma unroll
+  for (int k = 0; k < TQ; ++k) {
+    e[k] = a[k] = b[k] = 0;
+    const int64_t x = (int64_t)tid * q + k;
+    if (k < q && x < S) {
+      if (fold) {
+        uint64_t e0, a0, b0, e1, a1, b1;
+        load3(in, 2 * x, e0, a0, b0);
+        load3(in, 2 * x + 1, e1, a1, b1);
+        e[k] = lerp(e0, e1, r0);
+        a[k] = lerp(a0, a1, r0);
+        b[k] = lerp(b0, b1, r0);
+      } else {
+        load3(in, x, e[k], a[k], b[k]);
+      }
     }
   }
+  __syncthreads();  // rs visible
+  int i = i0;
+#pragma unroll
+  for (int cnt = TQ; cnt >= 2; cnt >>= 1) {
+    if (q == cnt) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[c] = 0;
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) pair_terms(e[2 * p], e[2 * p + 1], a[2 * p], a[2 * p + 1], b[2 * p], b[2 * p + 1], g);
+      block_sum4<SC3_TT>(g, red);
+      if (tid < 4) rounds[(int64_t)i * 4 + tid] = g[tid];
+      const uint64_t ri = rs[i - i0];
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) {
+        e[p] = lerp(e[2 * p], e[2 * p + 1], ri);
+        a[p] = lerp(a[2 * p], a[2 * p + 1], ri);
+        b[p] = lerp(b[2 * p], b[2 * p + 1], ri);
+      }
+      ++i;
+      q = cnt / 2;
+    }
+  }
+  // stage 2: n2 = min(S, 256) entries, one per thread -> wave 0, q2 per lane
+  const int n2 = S < SC3_TT ? (int)S : SC3_TT;
+  xE[tid] = e[0];
+  xA[tid] = a[0];
+  xB[tid] = b[0];
   __syncthreads();
-  for (int i = i0; i < m; ++i) {
-    const int64_t pairs = size / 2;
-    uint64_t g[4] = {0, 0, 0, 0};
-    for (int64_t q = tid; q < pairs; q += SC3_TT)
-      pair_terms(sE[2 * q], sE[2 * q + 1], sA[2 * q], sA[2 * q + 1], sB[2 * q], sB[2 * q + 1], g);
-    block_sum4<SC3_TT>(g, red);
-    if (tid < 4) rounds[(int64_t)i * 4 + tid] = g[tid];
-    // r_i is applied only after g_i is complete; size <= SC3_TAIL = 2 SC3_TT, so
-    // every pair has its own thread
-    const uint64_t ri = r[i];
-    uint64_t ne = 0, na = 0, nbv = 0;
-    const bool act = tid < pairs;
-    if (act) {
-      ne = lerp(sE[2 * tid], sE[2 * tid + 1], ri);
-      na = lerp(sA[2 * tid], sA[2 * tid + 1], ri);
-      nbv = lerp(sB[2 * tid], sB[2 * tid + 1], ri);
-    }
-    __syncthreads();
-    if (act) {
-      sE[tid] = ne;
-      sA[tid] = na;
-      sB[tid] = nbv;
-    }
-    __syncthreads();
-    size = pairs;
+  if (wave != 0) return;
+  int q2 = n2 >= 64 ? n2 / 64 : 1;
+  uint64_t e2[4], a2[4], b2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int x = lane * q2 + k;
+    const bool ok = k < q2 && x < n2;
+    e2[k] = ok ? xE[x] : 0;
+    a2[k] = ok ? xA[x] : 0;
+    b2[k] = ok ? xB[x] : 0;
   }
-  if (tid == 0) {
-    finals[0] = sE[0];
-    finals[1] = sA[0];
-    finals[2] = sB[0];
+#pragma unroll
+  for (int cnt = 4; cnt >= 2; cnt >>= 1) {
+    if (q2 == cnt) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[c] = 0;
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p)
+        pair_terms(e2[2 * p], e2[2 * p + 1], a2[2 * p], a2[2 * p + 1], b2[2 * p], b2[2 * p + 1], g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[c] = fpi::wave_total(g[c]);
+      if (lane < 4) rounds[(int64_t)i * 4 + lane] = lane == 0 ? g[0] : lane == 1 ? g[1] : lane == 2 ? g[2] : g[3];
+      const uint64_t ri = rs[i - i0];
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) {
+        e2[p] = lerp(e2[2 * p], e2[2 * p + 1], ri);
+        a2[p] = lerp(a2[2 * p], a2[2 * p + 1], ri);
+        b2[p] = lerp(b2[2 * p], b2[2 * p + 1], ri);
+      }
+      ++i;
+      q2 = cnt / 2;
+    }
+  }
+  // stage 3: entry x at lane x * dist, pairs dist apart
+  uint64_t ev = e2[0], av = a2[0], bv = b2[0];
+  for (int dist = 1; i < m; dist <<= 1, ++i) {
+    const uint64_t e1 = shfl_down_u64(ev, dist), a1 = shfl_down_u64(av, dist), b1 = shfl_down_u64(bv, dist);
+    const bool lead = (lane & (2 * dist - 1)) == 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = 0;
+    if (lead) pair_terms(ev, e1, av, a1, bv, b1, g);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = fpi::wave_total(g[c]);
+    if (lane < 4) rounds[(int64_t)i * 4 + lane] = lane == 0 ? g[0] : lane == 1 ? g[1] : lane == 2 ? g[2] : g[3];
+    const uint64_t ri = rs[i - i0];
+    if (lead) {
+      ev = lerp(ev, e1, ri);
+      av = lerp(av, a1, ri);
+      bv = lerp(bv, b1, ri);
+    }
+  }
+  if (lane == 0) {
+    finals[0] = ev;
+    finals[1] = av;
+    finals[2] = bv;
   }
 }
 
@@ -275,7 +369,7 @@ Sc3Layout sc3_layout(int32_t m) {
   l.buf = S > SC3_TAIL ? (size_t)(S / 2) : 0;
   const int64_t pairs = S / 2;
   l.nb = (int)std::min<int64_t>(SC3_MAXB, std::max<int64_t>(1, (pairs + LK_T - 1) / LK_T));
-  l.bytes = 6 * l.buf * 8 + fpi::align_up((size_t)l.nb * 4 * 8, 256);
+  l.bytes = 6 * l.buf * 8 + 2 * fpi::align_up((size_t)l.nb * 4 * 8, 256);
   return l;
 }
 
@@ -284,13 +378,16 @@ int sc3_enqueue(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t*
                 uint64_t* finals, void* ws, hipStream_t st) {
   const Sc3Layout l = sc3_layout(m);
   uint64_t* bufs = (uint64_t*)ws;
-  uint64_t* part = bufs + 6 * l.buf;
+  uint64_t* parts[2];
+  parts[0] = bufs + 6 * l.buf;
+  parts[1] = parts[0] + fpi::align_up((size_t)l.nb * 4 * 8, 256) / 8;
   Sc3Tables in{E, V, nullptr, 1};
   int64_t size = (int64_t)1 << m;  // entries of `in`
   int i = 0;
   int fold = 0;
   int cur = 0;
-  // wide rounds while the folded tables would exceed the tail's LDS
+  int nb_prev = 0;  // partials of round i - 1 still to add
+  // wide rounds while the folded tables would exceed the tail's entries
   while ((fold ? size / 2 : size) > SC3_TAIL) {
     const int64_t out_size = fold ? size / 2 : size;
     const int64_t pairs = out_size / 2;
@@ -298,12 +395,9 @@ int sc3_enqueue(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t*
     uint64_t* Ao = Eo + l.buf;
     uint64_t* Bo = Ao + l.buf;
     const int nb = (int)std::min<int64_t>(l.nb, (pairs + LK_T - 1) / LK_T);
-    hipLaunchKernelGGL(sc3_round_kernel, dim3(nb), dim3(LK_T), 0, st, in, Eo, Ao, Bo, fold ? r + (i - 1) : r,
-                       fold, pairs, part);
-    int rc = fpi::check_launch("sc3_round_kernel");
-    if (rc) return rc;
-    hipLaunchKernelGGL(sc3_reduce_kernel, dim3(1), dim3(LK_T), 0, st, part, nb, rounds + (size_t)i * 4);
-    rc = fpi::check_launch("sc3_reduce_kernel");
+    hipLaunchKernelGGL(sc3_round_kernel, dim3(nb), dim3(LK_T), 0, st, in, Eo, Ao, Bo, fold ? r + (i - 1) : r, fold,
+                       pairs, parts[i & 1], parts[(i + 1) & 1], nb_prev, rounds + (size_t)(i - 1) * 4);
+    const int rc = fpi::check_launch("sc3_round_kernel");
     if (rc) return rc;
     if (fold) {
       in = Sc3Tables{Eo, Ao, Bo, 0};
@@ -311,9 +405,11 @@ int sc3_enqueue(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t*
       size = out_size;
     }
     fold = 1;
+    nb_prev = nb;
     ++i;
   }
-  hipLaunchKernelGGL(sc3_tail_kernel, dim3(1), dim3(SC3_TT), 0, st, in, fold, size, r, i, m, rounds, finals);
+  hipLaunchKernelGGL(sc3_tail_kernel, dim3(1), dim3(SC3_TT), 0, st, in, fold, size, r, i, m, rounds, finals,
+                     parts[(i + 1) & 1], nb_prev);
   return fpi::check_launch("sc3_tail_kernel");
 }
 
