@@ -20,6 +20,7 @@
 
 #include "common.hpp"
 #include "gl.hpp"
+#include "sc_tail.hpp"
 
 namespace {
 
@@ -135,6 +136,34 @@ __device__ __forceinline__ void pair_terms(uint64_t e0, uint64_t e1, uint64_t a0
       b = gl::add(b, db);
     }
   }
+}
+
+// The same terms as exact 96-bit sums (each product < p), for wave reductions
+// that carry no modular corrections.
+__device__ __forceinline__ void pair_terms96(uint64_t e0, uint64_t e1, uint64_t a0, uint64_t a1, uint64_t b0,
+                                             uint64_t b1, sct::S96 (&g)[4]) {
+  const uint64_t de = gl::sub(e1, e0), da = gl::sub(a1, a0), db = gl::sub(b1, b0);
+  uint64_t e = e0, a = a0, b = b0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    g[c] = sct::add96(g[c], sct::to96(gl::mul(e, gl::mul(a, b))));
+    if (c < 3) {
+      e = gl::add(e, de);
+      a = gl::add(a, da);
+      b = gl::add(b, db);
+    }
+  }
+}
+
+// Round sums of one wave: the 96-bit lane sums added across the wave (DPP),
+// reduced once; lane 0 stores them.
+__device__ __forceinline__ void wave_round(sct::S96 (&s)[4], uint64_t* rounds) {
+  uint64_t g[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) g[c] = sct::lane_value(sct::wave_sum96(s[c]), 63);
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rounds[c] = g[c];
 }
 
 __device__ __forceinline__ uint64_t lerp(uint64_t x0, uint64_t x1, uint64_t r) {
@@ -313,14 +342,11 @@ __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t 
 #pragma unroll
   for (int cnt = 4; cnt >= 2; cnt >>= 1) {
     if (q2 == cnt) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) g[c] = 0;
+      sct::S96 s96[4] = {};
 #pragma unroll
       for (int p = 0; p < cnt / 2; ++p)
-        pair_terms(e2[2 * p], e2[2 * p + 1], a2[2 * p], a2[2 * p + 1], b2[2 * p], b2[2 * p + 1], g);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) g[c] = fpi::wave_total(g[c]);
-      if (lane < 4) rounds[(int64_t)i * 4 + lane] = lane == 0 ? g[0] : lane == 1 ? g[1] : lane == 2 ? g[2] : g[3];
+        pair_terms96(e2[2 * p], e2[2 * p + 1], a2[2 * p], a2[2 * p + 1], b2[2 * p], b2[2 * p + 1], s96);
+      wave_round(s96, rounds + (int64_t)i * 4);
       const uint64_t ri = rs[i - i0];
 #pragma unroll
       for (int p = 0; p < cnt / 2; ++p) {
@@ -337,12 +363,9 @@ __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t 
   for (int dist = 1; i < m; dist <<= 1, ++i) {
     const uint64_t e1 = shfl_down_u64(ev, dist), a1 = shfl_down_u64(av, dist), b1 = shfl_down_u64(bv, dist);
     const bool lead = (lane & (2 * dist - 1)) == 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[c] = 0;
-    if (lead) pair_terms(ev, e1, av, a1, bv, b1, g);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[c] = fpi::wave_total(g[c]);
-    if (lane < 4) rounds[(int64_t)i * 4 + lane] = lane == 0 ? g[0] : lane == 1 ? g[1] : lane == 2 ? g[2] : g[3];
+    sct::S96 s96[4] = {};
+    if (lead) pair_terms96(ev, e1, av, a1, bv, b1, s96);
+    wave_round(s96, rounds + (int64_t)i * 4);
     const uint64_t ri = rs[i - i0];
     if (lead) {
       ev = lerp(ev, e1, ri);
