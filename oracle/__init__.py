@@ -590,3 +590,206 @@ def prove_config(cfg, inp: dict, ch: dict, witness_full=True, experts=None):
             res[e] = {"tokens": toks, "up": up, "down": dn}
         return res
     raise ValueError(cfg.kind)
+
+
+# ------------------------------------------- soundness-faithful challenges --
+# "How fast can FlashProve go", §2 (every challenge is a BLAKE2b hash of all
+# the prover has sent so far) and §4 footnote 20 (challenge and lookup
+# arithmetic runs in an extension of Goldilocks). Readings: the extension is
+# F_p[u]/(u^2 - 7) (7 generates F_p*, so it is not a square); the transcript
+# state is a 32-byte BLAKE2b-256 digest, s <- BLAKE2b-256(s || message) per
+# message; challenges come from s and, beyond the first two, from
+# BLAKE2b-256(s || j) for j = 1, 2, ... (32-bit little-endian j), each digest's
+# four little-endian words giving two elements (w0 mod p) + u (w1 mod p) and
+# (w2 mod p) + u (w3 mod p).
+EXT_W = 7
+FS_LABEL = b"zkp-matmul-sumcheck-fs-v1"
+
+
+def e2(a, b=0):
+    return (a % P, b % P)
+
+
+def e2_add(x, y):
+    return ((x[0] + y[0]) % P, (x[1] + y[1]) % P)
+
+
+def e2_sub(x, y):
+    return ((x[0] - y[0]) % P, (x[1] - y[1]) % P)
+
+
+def e2_mul(x, y):
+    return ((x[0] * y[0] + EXT_W * x[1] * y[1]) % P, (x[0] * y[1] + x[1] * y[0]) % P)
+
+
+def e2_inv(x):
+    n = (x[0] * x[0] - EXT_W * x[1] * x[1]) % P  # norm: x * conj(x)
+    ni = pow(n, P - 2, P)
+    return (x[0] * ni % P, (-x[1]) * ni % P)
+
+
+def e2_pow(x, e: int):
+    r = (1, 0)
+    while e:
+        if e & 1:
+            r = e2_mul(r, x)
+        x = e2_mul(x, x)
+        e >>= 1
+    return r
+
+
+def e2_words(x) -> bytes:
+    return int(x[0]).to_bytes(8, "little") + int(x[1]).to_bytes(8, "little")
+
+
+class Transcript:
+    def __init__(self, params: bytes):
+        self.s = blake2b(FS_LABEL + params)
+
+    def absorb(self, msg: bytes):
+        self.s = blake2b(self.s + msg)
+
+    def challenges(self, k: int) -> list:
+        out, j = [], 0
+        while len(out) < k:
+            d = self.s if j == 0 else blake2b(self.s + j.to_bytes(4, "little"))
+            w = [int.from_bytes(d[8 * i: 8 * i + 8], "little") for i in range(4)]
+            out += [(w[0] % P, w[1] % P), (w[2] % P, w[3] % P)]
+            j += 1
+        return out[:k]
+
+
+def layer_params(T: int, d_in: int, d_out: int, s: int) -> bytes:
+    return b"".join(int(v).to_bytes(4, "little") for v in (T, d_in, d_out, s))
+
+
+def eq_table_e2(r) -> list:
+    """eq(r, k) over the extension, k < 2^len(r), bit j of k picking r_j."""
+    E = [(1, 0)]
+    for j, rj in enumerate(r):
+        one_m = e2_sub((1, 0), rj)
+        E = [e2_mul(e, one_m) for e in E] + [e2_mul(e, rj) for e in E]
+    return E
+
+
+def e2_split(E) -> tuple:
+    return np.array([e[0] for e in E], np.uint64), np.array([e[1] for e in E], np.uint64)
+
+
+def e2_join(a, b) -> list:
+    return [(int(x), int(y)) for x, y in zip(a, b)]
+
+
+def fold_rows_e2(M: np.ndarray, E, cols_pad: int) -> list:
+    """sum_t E[t] M[t, :] with extension weights: the two base folds."""
+    E0, E1 = e2_split(E)
+    return e2_join(fold_rows(M, E0, cols_pad), fold_rows(M, E1, cols_pad))
+
+
+def sumcheck_e2(A: list, B: list, tr: Transcript):
+    """Sum-check of sum_k A[k] B[k] over the extension with the transcript:
+    round i absorbs g_i(0), g_i(1), g_i(2) and takes r_i from the transcript,
+    then binds the lowest remaining variable. Returns (rounds, r, finals)."""
+    a, b = list(A), list(B)
+    rounds, rs = [], []
+    while len(a) > 1:
+        h = len(a) // 2
+        g = [(0, 0)] * 3
+        for q in range(h):
+            da, db = e2_sub(a[2 * q + 1], a[2 * q]), e2_sub(b[2 * q + 1], b[2 * q])
+            ac, bc = a[2 * q], b[2 * q]
+            for c in range(3):
+                g[c] = e2_add(g[c], e2_mul(ac, bc))
+                ac, bc = e2_add(ac, da), e2_add(bc, db)
+        rounds.append(g)
+        tr.absorb(b"".join(e2_words(x) for x in g))
+        r = tr.challenges(1)[0]
+        rs.append(r)
+        a = [e2_add(a[2 * q], e2_mul(r, e2_sub(a[2 * q + 1], a[2 * q]))) for q in range(h)]
+        b = [e2_add(b[2 * q], e2_mul(r, e2_sub(b[2 * q + 1], b[2 * q]))) for q in range(h)]
+    return rounds, rs, (a[0], b[0])
+
+
+def e2_eval_deg2(g, x):
+    """The quadratic through (0, g0), (1, g1), (2, g2) at x (Lagrange)."""
+    inv2 = (P + 1) // 2
+    l0 = e2_mul(e2_mul(e2_sub(x, (1, 0)), e2_sub(x, (2, 0))), (inv2, 0))
+    l1 = e2_mul(e2_mul(x, e2_sub(x, (2, 0))), (P - 1, 0))
+    l2 = e2_mul(e2_mul(x, e2_sub(x, (1, 0))), (inv2, 0))
+    return e2_add(e2_add(e2_mul(g[0], l0), e2_mul(g[1], l1)), e2_mul(g[2], l2))
+
+
+def prove_layer_fs(X: np.ndarray, W: np.ndarray, s: int, root: bytes) -> dict:
+    """The layer's matmul proof with Fiat-Shamir over the extension: the
+    transcript absorbs the layer's shape and the commitment root of Y and R,
+    yields r_t and r_o, absorbs the claim c0 = Z~(r_o || r_t), then runs the
+    sum-check of sum_k x'(k) w'(k) over d_in (padded to 2^n), and absorbs the
+    finals."""
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    Z, Y, R = witness(X, W, s)
+    n_t, n_o, n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
+    tr = Transcript(layer_params(T, d_in, d_out, s))
+    tr.absorb(root)
+    ch = tr.challenges(n_t + n_o)
+    r_t, r_o = ch[:n_t], ch[n_t:]
+    Et, Eo = eq_table_e2(r_t), eq_table_e2(r_o)
+    xf = fold_rows_e2(X, Et[:T], 1 << n)
+    wf = fold_rows_e2(W, Eo[:d_out], 1 << n)
+    G = fold_rows_e2(np.ascontiguousarray(Z.T), Eo[:d_out], T)  # G[t] = sum_o Eo[o] Z[t, o]
+    c0 = (0, 0)
+    for t in range(T):
+        c0 = e2_add(c0, e2_mul(Et[t], G[t]))
+    tr.absorb(e2_words(c0))
+    rounds, rs, finals = sumcheck_e2(xf, wf, tr)
+    tr.absorb(e2_words(finals[0]) + e2_words(finals[1]))
+    return {"Z": Z, "Y": Y, "R": R, "r_t": r_t, "r_o": r_o, "c0": c0, "rounds": rounds, "r": rs,
+            "finals": finals, "state": tr.s, "x_fold": xf, "w_fold": wf}
+
+
+def verify_layer_fs(X: np.ndarray, W: np.ndarray, s: int, root: bytes, proof: dict):
+    """Replays the transcript from the root and the prover's messages, checks
+    every round sum and the finals against x~' and w~' at the point, and the
+    claim against Z = X W^T. Returns a reason from REASONS."""
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    n_t, n_o, n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
+    tr = Transcript(layer_params(T, d_in, d_out, s))
+    tr.absorb(root)
+    ch = tr.challenges(n_t + n_o)
+    r_t, r_o = ch[:n_t], ch[n_t:]
+    Et, Eo = eq_table_e2(r_t), eq_table_e2(r_o)
+    Z = witness(X, W, s)[0]
+    G = fold_rows_e2(np.ascontiguousarray(Z.T), Eo[:d_out], T)
+    c0 = (0, 0)
+    for t in range(T):
+        c0 = e2_add(c0, e2_mul(Et[t], G[t]))
+    if tuple(proof["c0"]) != c0:
+        return "INITIAL_CLAIM"
+    tr.absorb(e2_words(c0))
+    claim, rs = c0, []
+    for g in proof["rounds"]:
+        g = [tuple(x) for x in g]
+        if e2_add(g[0], g[1]) != claim:
+            return "ROUND_SUM"
+        tr.absorb(b"".join(e2_words(x) for x in g))
+        r = tr.challenges(1)[0]
+        rs.append(r)
+        claim = e2_eval_deg2(g, r)
+    a, b = (tuple(x) for x in proof["finals"])
+    if e2_mul(a, b) != claim:
+        return "FINAL_CLAIM"
+    # the finals are the folded rows' extensions at the point
+    xf = fold_rows_e2(X, Et[:T], 1 << n)
+    wf = fold_rows_e2(W, Eo[:d_out], 1 << n)
+    Er = eq_table_e2(rs)
+    xa, wa = (0, 0), (0, 0)
+    for k in range(1 << n):
+        xa = e2_add(xa, e2_mul(Er[k], xf[k]))
+        wa = e2_add(wa, e2_mul(Er[k], wf[k]))
+    if (xa, wa) != (a, b):
+        return "FINAL_OPENING"
+    tr.absorb(e2_words(a) + e2_words(b))
+    if proof.get("state") is not None and proof["state"] != tr.s:
+        return "FINAL_OPENING"
+    return "OK"

@@ -573,3 +573,91 @@ def test_lookup_proof_verifies_and_negative_controls():
     assert out3 == 1
     p3 = O.grand_product_prove(lev3, chal)
     assert O.grand_product_verify(int(lev3[-1][0]), p3, chal, L, k3, gamma, c3, s) == (5, L)
+
+
+# ------------------------------------------- soundness-faithful challenges --
+def test_extension_field():
+    # 7 is not a square mod p (Euler's criterion), so F_p[u]/(u^2 - 7) is a field
+    assert pow(7, (P - 1) // 2, P) == P - 1
+    rng = random.Random(41)
+    u = (0, 1)
+    assert O.e2_mul(u, u) == (7, 0)
+    for _ in range(50):
+        a, b, c = [(rng.randrange(P), rng.randrange(P)) for _ in range(3)]
+        assert O.e2_mul(O.e2_mul(a, b), c) == O.e2_mul(a, O.e2_mul(b, c))
+        assert O.e2_mul(a, O.e2_add(b, c)) == O.e2_add(O.e2_mul(a, b), O.e2_mul(a, c))
+        assert O.e2_mul(a, O.e2_inv(a)) == (1, 0)
+    # Frobenius: a^p is the conjugate, since u^p = u 7^((p-1)/2) = -u
+    a = (rng.randrange(P), rng.randrange(P))
+    assert O.e2_pow(a, P) == (a[0], (P - a[1]) % P)
+    # the multiplicative group has order p^2 - 1
+    assert O.e2_pow(a, P * P - 1) == (1, 0)
+
+
+def test_transcript_derivation_and_sensitivity():
+    import hashlib
+    h = lambda b: hashlib.blake2b(b, digest_size=32).digest()
+    tr = O.Transcript(b"params")
+    s0 = h(O.FS_LABEL + b"params")
+    assert tr.s == s0
+    tr.absorb(b"root")
+    s1 = h(s0 + b"root")
+    assert tr.s == s1
+    ch = tr.challenges(3)
+    w = [int.from_bytes(s1[8 * i: 8 * i + 8], "little") for i in range(4)]
+    assert ch[0] == (w[0] % P, w[1] % P) and ch[1] == (w[2] % P, w[3] % P)
+    d1 = h(s1 + (1).to_bytes(4, "little"))
+    assert ch[2] == (int.from_bytes(d1[:8], "little") % P, int.from_bytes(d1[8:16], "little") % P)
+    # any change to an absorbed byte changes every later challenge
+    tr2 = O.Transcript(b"params")
+    tr2.absorb(b"rooT")
+    assert all(a != b for a, b in zip(tr2.challenges(3), ch))
+
+
+def _mle_e2(A, pt):
+    E = O.eq_table_e2(pt)
+    acc = (0, 0)
+    for e, a in zip(E, A):
+        acc = O.e2_add(acc, O.e2_mul(e, a))
+    return acc
+
+
+def test_sumcheck_e2_against_hypercube_enumeration():
+    rng = random.Random(42)
+    n = 3
+    A = [(rng.randrange(P), rng.randrange(P)) for _ in range(1 << n)]
+    B = [(rng.randrange(P), rng.randrange(P)) for _ in range(1 << n)]
+    rounds, rs, finals = O.sumcheck_e2(A, B, O.Transcript(b"t"))
+    total = (0, 0)
+    for a, b in zip(A, B):
+        total = O.e2_add(total, O.e2_mul(a, b))
+    assert O.e2_add(rounds[0][0], rounds[0][1]) == total
+    for i in range(n):
+        for c in range(3):
+            tot = (0, 0)
+            for bits in itertools.product((0, 1), repeat=n - i - 1):
+                pt = list(rs[:i]) + [(c, 0)] + [(x, 0) for x in bits]
+                tot = O.e2_add(tot, O.e2_mul(_mle_e2(A, pt), _mle_e2(B, pt)))
+            assert rounds[i][c] == tot
+    assert finals == (_mle_e2(A, rs), _mle_e2(B, rs))
+
+
+def test_layer_fs_proof_and_negative_controls():
+    cfg = synth.config(1)
+    inp = synth.make_inputs(cfg)
+    X, W = inp["X"], inp["W"]
+    root = O.blake2b(b"commitment of Y and R")
+    pr = O.prove_layer_fs(X, W, cfg.s, root)
+    assert O.verify_layer_fs(X, W, cfg.s, root, pr) == "OK"
+    # a different commitment changes the challenges, so the claim no longer matches
+    assert O.verify_layer_fs(X, W, cfg.s, O.blake2b(b"other"), pr) == "INITIAL_CLAIM"
+    bad = dict(pr, rounds=[list(g) for g in pr["rounds"]])
+    bad["rounds"][2][1] = O.e2_add(bad["rounds"][2][1], (1, 0))
+    assert O.verify_layer_fs(X, W, cfg.s, root, bad) == "ROUND_SUM"
+    bad = dict(pr, finals=(O.e2_add(pr["finals"][0], (0, 1)), pr["finals"][1]))
+    assert O.verify_layer_fs(X, W, cfg.s, root, bad) == "FINAL_CLAIM"
+    W2 = W.copy()
+    W2[3, 7] ^= 1
+    assert O.verify_layer_fs(X, W2, cfg.s, root, pr) == "INITIAL_CLAIM"
+    # the finals are extension elements, not base ones: the challenges left F_p
+    assert any(r[1] != 0 for r in pr["r"]) and any(x[1] != 0 for x in pr["finals"])
