@@ -256,6 +256,44 @@ int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem
                     size_t ws_bytes, hipStream_t stream);
 size_t fp_lookup_prove_workspace(int32_t L);
 
+/* --------------------------------------- soundness-faithful challenges --- */
+/* Fiat-Shamir challenges over an extension of Goldilocks ("How fast can
+ * FlashProve go", §2: every challenge is a BLAKE2b hash of all the prover has
+ * sent so far; §4 footnote 20: challenge arithmetic runs in an extension
+ * field). Extension elements are pairs (a, b) = a + u b of canonical base
+ * elements with u^2 = 7, stored as two consecutive fp_elem.
+ *
+ * The transcript state is 32 bytes of device memory (8-byte aligned):
+ * fp_fs_init sets it to BLAKE2b-256 of the nbytes (<= 128) host bytes msg
+ * (they travel in the kernel arguments); fp_fs_absorb sets
+ * state <- BLAKE2b-256(state || data) for nwords device words (8 little-endian
+ * bytes each); fp_fs_challenges writes k extension elements to out [k][2]
+ * without changing the state: digest 0 is the state, digest j >= 1 is
+ * BLAKE2b-256(state || j as 4 little-endian bytes), and digest j's words
+ * w0..w3 give challenges 2j = (w0 mod p, w1 mod p) and 2j+1 = (w2 mod p,
+ * w3 mod p). */
+int fp_fs_init(uint8_t* state, const uint8_t* msg, int32_t nbytes, hipStream_t stream);
+int fp_fs_absorb(uint8_t* state, const fp_elem* data, int32_t nwords, hipStream_t stream);
+int fp_fs_challenges(const uint8_t* state, int32_t k, fp_elem* out, hipStream_t stream);
+
+/* E0[k] + u E1[k] = prod_j (bit j of k ? r_j : 1 - r_j) for k < 2^n over the
+ * extension; r: device [n][2], n <= 24. */
+int fp_eq_table_ext(const fp_elem* r, int32_t n, fp_elem* E0, fp_elem* E1, hipStream_t stream);
+
+/* c0 = (c4[0] + 7 c4[1]) + u (c4[2] + c4[3]): the extension claim from the four
+ * base claims of (E_t0, E_o0), (E_t1, E_o1), (E_t0, E_o1), (E_t1, E_o0). */
+int fp_ext_claim_combine(const fp_elem* c4, fp_elem* c0, hipStream_t stream);
+
+/* Sum-check of sum_{k < 2^n} A(k) B(k) over the extension (A = A0 + u A1,
+ * B = B0 + u B1, device arrays of 2^n canonical elements, n <= 12) with the
+ * transcript: round i writes rounds[6i .. 6i+5] = g_i(0), g_i(1), g_i(2),
+ * absorbs those 6 words, takes r_i = challenge 0 of the new state (written to
+ * r[2i], r[2i+1]) and only then binds the lowest remaining variable to r_i.
+ * At the end finals = A(r), B(r) (4 words), which are absorbed. One
+ * workgroup. */
+int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp_elem* B0, const fp_elem* B1, int32_t n,
+                       uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals, hipStream_t stream);
+
 /* ----------------------------------------------------------------- MLE --- */
 /* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading
  * dim ld) zero-padded to [2^n_rows, 2^n_cols]; rows <= 2^n_rows and

@@ -86,6 +86,11 @@ def test_argument_errors_without_gpu():
     need = L.fp_lookup_prove_workspace(23)
     assert need >= (1 << 22) * 8
     assert L.fp_lookup_prove(dummy, 23, dummy, dummy, dummy, dummy, need - 1, None) == 4
+    # transcript and extension sum-check: message size, table size, null state
+    assert L.fp_fs_init(dummy, b"x" * 200, 200, None) == 1
+    assert L.fp_sumcheck_ext_fs(dummy, dummy, dummy, dummy, 13, dummy, dummy, dummy, dummy, None) == 2
+    assert L.fp_fs_absorb(None, dummy, 4, None) == 1
+    assert L.fp_eq_table_ext(dummy, 25, dummy, dummy, None) == 2
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)

@@ -28,7 +28,8 @@ EXPORTS = [
     "fp_witness_linear_with_sumcheck", "fp_fold_weights_prepare", "fp_fold_matrix_multi",
     "fp_fold_matrix_multi_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
     "fp_merkle_commit", "fp_lookup_tree", "fp_lookup_counts", "fp_sumcheck3_prove", "fp_sumcheck3_workspace",
-    "fp_lookup_prove", "fp_lookup_prove_workspace",
+    "fp_lookup_prove", "fp_lookup_prove_workspace", "fp_fs_init", "fp_fs_absorb", "fp_fs_challenges",
+    "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs",
 ]
 
 _lib = None
@@ -99,6 +100,12 @@ def lib():
             "fp_sumcheck3_workspace": (sz, [i32]),
             "fp_lookup_prove": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, sz, vp]),
             "fp_lookup_prove_workspace": (sz, [i32]),
+            "fp_fs_init": (ctypes.c_int, [vp, ctypes.c_char_p, i32, vp]),
+            "fp_fs_absorb": (ctypes.c_int, [vp, vp, i32, vp]),
+            "fp_fs_challenges": (ctypes.c_int, [vp, i32, vp, vp]),
+            "fp_eq_table_ext": (ctypes.c_int, [vp, i32, vp, vp, vp]),
+            "fp_ext_claim_combine": (ctypes.c_int, [vp, vp, vp]),
+            "fp_sumcheck_ext_fs": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -425,6 +432,55 @@ def lookup_prove(tree, L: int, chal, rounds=None, finals=None):
     _check(lib().fp_lookup_prove(_ptr(tree), L, _ptr(chal), _ptr(rounds), _ptr(finals), p, nbytes, _stream()),
            "fp_lookup_prove")
     return rounds[:nr], finals
+
+
+# ---------------------------------------------- soundness-faithful challenges --
+def fs_init(state, msg: bytes):
+    """state (device uint8 [32], 8-byte aligned) <- BLAKE2b-256(msg), msg <= 128 bytes."""
+    _check(lib().fp_fs_init(_ptr(state), msg, len(msg), _stream()), "fp_fs_init")
+    return state
+
+
+def fs_absorb(state, data):
+    """state <- BLAKE2b-256(state || data), data a device int64 tensor of words."""
+    _check(lib().fp_fs_absorb(_ptr(state), _ptr(data) if data.numel() else None, data.numel(), _stream()),
+           "fp_fs_absorb")
+    return state
+
+
+def fs_challenges(state, k: int, out=None):
+    """k extension challenges [k, 2] read from the state."""
+    out = torch.empty((max(k, 1), 2), dtype=torch.int64, device=state.device) if out is None else out
+    _check(lib().fp_fs_challenges(_ptr(state), k, _ptr(out), _stream()), "fp_fs_challenges")
+    return out[:k]
+
+
+def eq_table_ext(r, E0=None, E1=None):
+    """(E0, E1): eq over the extension at r [n, 2]."""
+    n = r.shape[0]
+    dev = r.device
+    E0 = torch.empty(1 << n, dtype=torch.int64, device=dev) if E0 is None else E0
+    E1 = torch.empty(1 << n, dtype=torch.int64, device=dev) if E1 is None else E1
+    _check(lib().fp_eq_table_ext(_ptr(r) if n else None, n, _ptr(E0), _ptr(E1), _stream()), "fp_eq_table_ext")
+    return E0, E1
+
+
+def ext_claim_combine(c4, c0=None):
+    c0 = torch.empty(2, dtype=torch.int64, device=c4.device) if c0 is None else c0
+    _check(lib().fp_ext_claim_combine(_ptr(c4), _ptr(c0), _stream()), "fp_ext_claim_combine")
+    return c0
+
+
+def sumcheck_ext_fs(A0, A1, B0, B1, state, rounds=None, r=None, finals=None):
+    """Extension sum-check with the transcript: rounds [n, 3, 2], r [n, 2], finals [2, 2]."""
+    n = A0.numel().bit_length() - 1
+    dev = A0.device
+    rounds = torch.empty((max(n, 1), 3, 2), dtype=torch.int64, device=dev) if rounds is None else rounds
+    r = torch.empty((max(n, 1), 2), dtype=torch.int64, device=dev) if r is None else r
+    finals = torch.empty((2, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    _check(lib().fp_sumcheck_ext_fs(_ptr(A0), _ptr(A1), _ptr(B0), _ptr(B1), n, _ptr(state), _ptr(rounds), _ptr(r),
+                                    _ptr(finals), _stream()), "fp_sumcheck_ext_fs")
+    return rounds[:n], r[:n], finals
 
 
 def mle_eval(M, r_rows, r_cols, out=None):

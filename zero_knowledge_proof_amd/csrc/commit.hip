@@ -22,6 +22,7 @@
 // first reads its elements straight from HBM, the second reads the first's
 // results through LDS. Their internal twiddles are powers of w_16 = 2^156
 // (w_64 = 2^39 for this generator, and 2^96 = -1), i.e. shifts.
+#include "blake2b.hpp"
 #include "common.hpp"
 #include "gl.hpp"
 
@@ -253,82 +254,6 @@ __global__ __launch_bounds__(256) void twiddle_kernel(uint64_t w, int32_t L, uin
     e >>= 1;
   }
   *out = r;
-}
-
-// ------------------------------------------------------------------ BLAKE2b
-// RFC 7693: 12 rounds of the G mixing function over a 16-word state.
-constexpr uint64_t B2_IV_H[8] = {0x6a09e667f3bcc908ull, 0xbb67ae8584caa73bull, 0x3c6ef372fe94f82bull,
-                                 0xa54ff53a5f1d36f1ull, 0x510e527fade682d1ull, 0x9b05688c2b3e6c1full,
-                                 0x1f83d9abfb41bd6bull, 0x5be0cd19137e2179ull};
-constexpr unsigned char B2_SIGMA[12][16] = {
-    {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15}, {14, 10, 4, 8, 9, 15, 13, 6, 1, 12, 0, 2, 11, 7, 5, 3},
-    {11, 8, 12, 0, 5, 2, 15, 13, 10, 14, 3, 6, 7, 1, 9, 4}, {7, 9, 3, 1, 13, 12, 11, 14, 2, 6, 5, 10, 4, 0, 15, 8},
-    {9, 0, 5, 7, 2, 4, 10, 15, 14, 1, 11, 12, 6, 8, 3, 13}, {2, 12, 6, 10, 0, 11, 8, 3, 4, 13, 7, 5, 15, 14, 1, 9},
-    {12, 5, 1, 15, 14, 13, 4, 10, 0, 7, 6, 3, 9, 2, 8, 11}, {13, 11, 7, 14, 12, 1, 3, 9, 5, 0, 15, 4, 8, 6, 2, 10},
-    {6, 15, 14, 9, 11, 3, 0, 8, 12, 2, 13, 7, 1, 4, 10, 5}, {10, 2, 8, 4, 7, 6, 1, 5, 15, 11, 9, 14, 3, 12, 13, 0},
-    {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15}, {14, 10, 4, 8, 9, 15, 13, 6, 1, 12, 0, 2, 11, 7, 5, 3}};
-
-// 64-bit rotation right by a constant, as two 32-bit funnel shifts
-// (v_alignbit_b32): the 64-bit shift-and-or form costs three to four ops.
-template <int N>
-__device__ __forceinline__ uint64_t rotr64(uint64_t x) {
-  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-  uint32_t rl, rh;
-  if constexpr (N == 32) {
-    rl = hi;
-    rh = lo;
-  } else if constexpr (N < 32) {
-    rl = __builtin_amdgcn_alignbit(hi, lo, N);
-    rh = __builtin_amdgcn_alignbit(lo, hi, N);
-  } else {
-    rl = __builtin_amdgcn_alignbit(lo, hi, N - 32);
-    rh = __builtin_amdgcn_alignbit(hi, lo, N - 32);
-  }
-  return ((uint64_t)rh << 32) | rl;
-}
-
-__device__ __forceinline__ void b2_g(uint64_t& a, uint64_t& b, uint64_t& c, uint64_t& d, uint64_t x, uint64_t y) {
-  a = a + b + x;
-  d = rotr64<32>(d ^ a);
-  c = c + d;
-  b = rotr64<24>(b ^ c);
-  a = a + b + y;
-  d = rotr64<16>(d ^ a);
-  c = c + d;
-  b = rotr64<63>(b ^ c);
-}
-
-// h <- compress(h, m, t, last)
-__device__ __forceinline__ void b2_compress(uint64_t (&h)[8], const uint64_t (&m)[16], uint64_t t, bool last) {
-  uint64_t v[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = h[i];
-    v[i + 8] = B2_IV_H[i];
-  }
-  v[12] ^= t;  // byte counter (messages here are far below 2^64 bytes)
-  if (last) v[14] = ~v[14];
-#pragma unroll
-  for (int r = 0; r < 12; ++r) {
-    const unsigned char* s = B2_SIGMA[r];
-    b2_g(v[0], v[4], v[8], v[12], m[s[0]], m[s[1]]);
-    b2_g(v[1], v[5], v[9], v[13], m[s[2]], m[s[3]]);
-    b2_g(v[2], v[6], v[10], v[14], m[s[4]], m[s[5]]);
-    b2_g(v[3], v[7], v[11], v[15], m[s[6]], m[s[7]]);
-    b2_g(v[0], v[5], v[10], v[15], m[s[8]], m[s[9]]);
-    b2_g(v[1], v[6], v[11], v[12], m[s[10]], m[s[11]]);
-    b2_g(v[2], v[7], v[8], v[13], m[s[12]], m[s[13]]);
-    b2_g(v[3], v[4], v[9], v[14], m[s[14]], m[s[15]]);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] ^= v[i] ^ v[i + 8];
-}
-
-// parameter block of an unkeyed 32-byte digest: h0 ^= 0x01010000 | 32
-__device__ __forceinline__ void b2_init32(uint64_t (&h)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = B2_IV_H[i];
-  h[0] ^= 0x01010020ull;
 }
 
 constexpr int SALT_WORDS = 2;  // 16-byte salts

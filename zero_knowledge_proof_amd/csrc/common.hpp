@@ -51,6 +51,13 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// v of the lane d above this one (wave64 shuffle).
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int d) {
+  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, d, 64);
+  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);

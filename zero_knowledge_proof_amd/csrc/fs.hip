@@ -1,0 +1,407 @@
+// fs.hip - soundness-faithful challenges: a Fiat-Shamir transcript on the
+// device and the matmul sum-check over an extension of Goldilocks.
+//
+// "How fast can FlashProve go", §2: every challenge is a BLAKE2b hash of all
+// the prover has sent so far; §4 footnote 20: the protocol's challenge and
+// lookup arithmetic runs in an extension of Goldilocks, a product costing
+// several base products. Here the extension is F_p[u]/(u^2 - 7) (7 generates
+// F_p*, so it is not a square); the transcript state is a 32-byte BLAKE2b-256
+// digest s, absorbing a message sets s <- BLAKE2b-256(s || message), and
+// challenges are read from s and, beyond the first two, from
+// BLAKE2b-256(s || j) (j = 1, 2, ... as 32-bit little-endian), each digest's
+// four little-endian words w0..w3 giving (w0 mod p) + u (w1 mod p) and
+// (w2 mod p) + u (w3 mod p).
+//
+// The sum-check of sum_k A(k) B(k) over the extension runs in one workgroup:
+// each round's values g(0), g(1), g(2) are absorbed and r_i is read from the
+// new state before any table is bound by it, so the round chain includes one
+// BLAKE2b compression per round, computed by wave 0.
+#include "blake2b.hpp"
+#include "common.hpp"
+#include "gl.hpp"
+#include "sc_tail.hpp"
+
+namespace {
+
+// ---------------------------------------------------------------- F_{p^2}
+struct E2 {
+  uint64_t a, b;  // a + u b
+};
+__device__ __forceinline__ E2 e2_add(E2 x, E2 y) { return E2{gl::add(x.a, y.a), gl::add(x.b, y.b)}; }
+__device__ __forceinline__ E2 e2_sub(E2 x, E2 y) { return E2{gl::sub(x.a, y.a), gl::sub(x.b, y.b)}; }
+__device__ __forceinline__ E2 e2_mul(E2 x, E2 y) {
+  return E2{gl::add(gl::mul(x.a, y.a), gl::mul_small(gl::mul(x.b, y.b), 7u)),
+            gl::add(gl::mul(x.a, y.b), gl::mul(x.b, y.a))};
+}
+__device__ __forceinline__ E2 e2_lerp(E2 x0, E2 x1, E2 r) { return e2_add(x0, e2_mul(r, e2_sub(x1, x0))); }
+__device__ __forceinline__ uint64_t canon(uint64_t w) { return w >= gl::P ? w - gl::P : w; }
+
+// ----------------------------------------------------------- the transcript
+constexpr int FS_MAX_INIT_WORDS = 16;
+struct InitMsg {
+  uint64_t w[FS_MAX_INIT_WORDS];
+};
+
+// d <- BLAKE2b-256 of nbytes bytes given as little-endian words (zero past the end)
+template <typename F>
+__device__ __forceinline__ void b2_digest(F word, int nbytes, uint64_t (&d)[4]) {
+  uint64_t h[8];
+  b2_init32(h);
+  const int nw = (nbytes + 7) / 8;
+  for (int w0 = 0; w0 < nw || w0 == 0; w0 += 16) {
+    uint64_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = (w0 + i < nw) ? word(w0 + i) : 0;
+    const bool last = w0 + 16 >= nw;
+    b2_compress(h, m, last ? (uint64_t)nbytes : (uint64_t)(8 * (w0 + 16)), last);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = h[i];
+}
+
+// s <- BLAKE2b-256(s || g0 || g1 || g2): 10 words, one block
+__device__ __forceinline__ void absorb_round(uint64_t (&s)[4], const E2 (&g)[3]) {
+  uint64_t h[8], m[16];
+  b2_init32(h);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = s[i];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    m[4 + 2 * c] = g[c].a;
+    m[5 + 2 * c] = g[c].b;
+  }
+#pragma unroll
+  for (int i = 10; i < 16; ++i) m[i] = 0;
+  b2_compress(h, m, 80, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = h[i];
+}
+
+__device__ __forceinline__ E2 first_challenge(const uint64_t (&s)[4]) { return E2{canon(s[0]), canon(s[1])}; }
+
+__global__ void fs_init_kernel(InitMsg msg, int32_t nbytes, uint64_t* state) {
+  if (threadIdx.x != 0) return;
+  uint64_t d[4];
+  b2_digest([&](int i) { return msg.w[i]; }, nbytes, d);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) state[i] = d[i];
+}
+
+__global__ void fs_absorb_kernel(uint64_t* state, const uint64_t* __restrict__ data, int32_t nw) {
+  if (threadIdx.x != 0) return;
+  uint64_t d[4];
+  b2_digest([&](int i) { return i < 4 ? state[i] : data[i - 4]; }, 8 * (4 + nw), d);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) state[i] = d[i];
+}
+
+// challenge c (c < k) into out[2c], out[2c+1]; thread j reads digest j
+__global__ __launch_bounds__(64) void fs_challenges_kernel(const uint64_t* __restrict__ state, int32_t k,
+                                                           uint64_t* __restrict__ out) {
+  const int j = blockIdx.x * 64 + threadIdx.x;
+  if (2 * j >= k) return;
+  uint64_t s[4], d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = state[i];
+  if (j == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = s[i];
+  } else {  // BLAKE2b-256(s || j): 36 bytes, one block
+    uint64_t h[8], m[16];
+    b2_init32(h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = s[i];
+    m[4] = (uint32_t)j;
+#pragma unroll
+    for (int i = 5; i < 16; ++i) m[i] = 0;
+    b2_compress(h, m, 36, true);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = h[i];
+  }
+  out[4 * j] = canon(d[0]);
+  out[4 * j + 1] = canon(d[1]);
+  if (2 * j + 1 < k) {
+    out[4 * j + 2] = canon(d[2]);
+    out[4 * j + 3] = canon(d[3]);
+  }
+}
+
+// E[k] = prod_j (bit j of k ? r_j : 1 - r_j) over the extension, as E0 + u E1
+__global__ __launch_bounds__(256) void eq_ext_kernel(const uint64_t* __restrict__ r, int32_t n,
+                                                     uint64_t* __restrict__ E0, uint64_t* __restrict__ E1) {
+  __shared__ E2 f[2][FP_MAX_N];
+  if (threadIdx.x < n) {
+    const E2 rj{r[2 * threadIdx.x], r[2 * threadIdx.x + 1]};
+    f[1][threadIdx.x] = rj;
+    f[0][threadIdx.x] = e2_sub(E2{1, 0}, rj);
+  }
+  __syncthreads();
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= ((int64_t)1 << n)) return;
+  E2 e{1, 0};
+  for (int j = 0; j < n; ++j) e = e2_mul(e, f[(k >> j) & 1][j]);
+  E0[k] = e.a;
+  E1[k] = e.b;
+}
+
+// c0 = (c00 + 7 c11) + u (c01 + c10) from the four base claims c4 = [c00, c11, c01, c10]
+__global__ void ext_claim_kernel(const uint64_t* __restrict__ c4, uint64_t* __restrict__ c0) {
+  if (threadIdx.x != 0) return;
+  c0[0] = gl::add(c4[0], gl::mul_small(c4[1], 7u));
+  c0[1] = gl::add(c4[2], c4[3]);
+}
+
+// ------------------------------------------------ the extension sum-check
+constexpr int SE_T = 512;                  // threads
+constexpr int SE_Q = 8;                    // entries per thread at the start (n <= 12)
+constexpr int SE_MAXN = 12;
+
+// terms of g(0), g(1), g(2) of one pair as exact 96-bit sums per component
+__device__ __forceinline__ void pair_terms_e2(E2 a0, E2 a1, E2 b0, E2 b1, sct::S96 (&s)[6]) {
+  const E2 da = e2_sub(a1, a0), db = e2_sub(b1, b0);
+  E2 a = a0, b = b0;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const E2 p = e2_mul(a, b);
+    s[2 * c] = sct::add96(s[2 * c], sct::to96(p.a));
+    s[2 * c + 1] = sct::add96(s[2 * c + 1], sct::to96(p.b));
+    if (c < 2) {
+      a = e2_add(a, da);
+      b = e2_add(b, db);
+    }
+  }
+}
+
+// wave totals of the 6 sums, canonical, in every lane
+__device__ __forceinline__ void wave_g(sct::S96 (&s)[6], E2 (&g)[3]) {
+  uint64_t v[6];
+#pragma unroll
+  for (int c = 0; c < 6; ++c) v[c] = sct::lane_value(sct::wave_sum96(s[c]), 63);
+#pragma unroll
+  for (int c = 0; c < 3; ++c) g[c] = E2{v[2 * c], v[2 * c + 1]};
+}
+
+// the round's message out, the transcript advanced, r_i returned (wave-uniform)
+__device__ __forceinline__ E2 emit_round(uint64_t (&s)[4], const E2 (&g)[3], uint64_t* rounds, uint64_t* r_out,
+                                         int i, bool writer) {
+  absorb_round(s, g);
+  const E2 r = first_challenge(s);
+  if (writer) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      rounds[(int64_t)i * 6 + 2 * c] = g[c].a;
+      rounds[(int64_t)i * 6 + 2 * c + 1] = g[c].b;
+    }
+    r_out[2 * i] = r.a;
+    r_out[2 * i + 1] = r.b;
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restrict__ A0, const uint64_t* __restrict__ A1,
+                                                         const uint64_t* __restrict__ B0, const uint64_t* __restrict__ B1,
+                                                         int32_t n, uint64_t* __restrict__ state,
+                                                         uint64_t* __restrict__ rounds, uint64_t* __restrict__ r_out,
+                                                         uint64_t* __restrict__ finals) {
+  __shared__ sct::S96 red[SE_T / 64][6];
+  __shared__ uint64_t rsh[2];
+  __shared__ E2 xa[SE_T], xb[SE_T];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t N = (int64_t)1 << n;
+  uint64_t s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = state[i];
+  // stage 1: thread t holds entries t q .. t q + q - 1
+  int q = N >= SE_T ? (int)(N / SE_T) : 1;
+  E2 a[SE_Q], b[SE_Q];
+#pragma unroll
+  for (int k = 0; k < SE_Q; ++k) {
+    const int64_t x = (int64_t)tid * q + k;
+    const bool ok = k < q && x < N;
+    a[k] = ok ? E2{A0[x], A1[x]} : E2{0, 0};
+    b[k] = ok ? E2{B0[x], B1[x]} : E2{0, 0};
+  }
+  int i = 0;
+#pragma unroll
+  for (int cnt = SE_Q; cnt >= 2; cnt >>= 1) {
+    if (q == cnt) {
+      sct::S96 acc[6] = {};
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) pair_terms_e2(a[2 * p], a[2 * p + 1], b[2 * p], b[2 * p + 1], acc);
+#pragma unroll
+      for (int c = 0; c < 6; ++c) acc[c] = sct::wave_sum96(acc[c]);
+      if (lane == 63)
+#pragma unroll
+        for (int c = 0; c < 6; ++c) red[wave][c] = acc[c];
+      __syncthreads();
+      if (wave == 0) {
+        // every lane of wave 0 adds the wave totals and hashes the same message
+        E2 g[3];
+        uint64_t v[6];
+#pragma unroll
+        for (int c = 0; c < 6; ++c) {
+          sct::S96 t = red[0][c];
+#pragma unroll
+          for (int w = 1; w < SE_T / 64; ++w) t = sct::add96(t, red[w][c]);
+          v[c] = sct::reduce96(t);
+        }
+#pragma unroll
+        for (int c = 0; c < 3; ++c) g[c] = E2{v[2 * c], v[2 * c + 1]};
+        const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
+        if (lane == 0) {
+          rsh[0] = r.a;
+          rsh[1] = r.b;
+        }
+      }
+      __syncthreads();
+      // only wave 0 carries the transcript: the other waves stop after stage 1
+      const E2 r{rsh[0], rsh[1]};
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) {
+        a[p] = e2_lerp(a[2 * p], a[2 * p + 1], r);
+        b[p] = e2_lerp(b[2 * p], b[2 * p + 1], r);
+      }
+      ++i;
+      q = cnt / 2;
+    }
+  }
+  // stage 2: n2 = min(N, 512) entries, one per thread -> wave 0, q2 per lane
+  const int n2 = N < SE_T ? (int)N : SE_T;
+  xa[tid] = a[0];
+  xb[tid] = b[0];
+  __syncthreads();
+  if (wave != 0) return;
+  int q2 = n2 >= 64 ? n2 / 64 : 1;
+  E2 a2[8], b2[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int x = lane * q2 + k;
+    const bool ok = k < q2 && x < n2;
+    a2[k] = ok ? xa[x] : E2{0, 0};
+    b2[k] = ok ? xb[x] : E2{0, 0};
+  }
+#pragma unroll
+  for (int cnt = 8; cnt >= 2; cnt >>= 1) {
+    if (q2 == cnt) {
+      sct::S96 acc[6] = {};
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) pair_terms_e2(a2[2 * p], a2[2 * p + 1], b2[2 * p], b2[2 * p + 1], acc);
+      E2 g[3];
+      wave_g(acc, g);
+      const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
+#pragma unroll
+      for (int p = 0; p < cnt / 2; ++p) {
+        a2[p] = e2_lerp(a2[2 * p], a2[2 * p + 1], r);
+        b2[p] = e2_lerp(b2[2 * p], b2[2 * p + 1], r);
+      }
+      ++i;
+      q2 = cnt / 2;
+    }
+  }
+  // stage 3: entry x at lane x * dist, partners dist apart
+  E2 av = a2[0], bv = b2[0];
+  for (int dist = 1; i < n; dist <<= 1, ++i) {
+    const E2 a1{fpi::shfl_down_u64(av.a, dist), fpi::shfl_down_u64(av.b, dist)};
+    const E2 b1{fpi::shfl_down_u64(bv.a, dist), fpi::shfl_down_u64(bv.b, dist)};
+    const bool lead = (lane & (2 * dist - 1)) == 0;
+    sct::S96 acc[6] = {};
+    if (lead) pair_terms_e2(av, a1, bv, b1, acc);
+    E2 g[3];
+    wave_g(acc, g);
+    const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
+    if (lead) {
+      av = e2_lerp(av, a1, r);
+      bv = e2_lerp(bv, b1, r);
+    }
+  }
+  // finals: A(r), B(r), absorbed like a round message (8 words, one block)
+  const E2 fa{fpi::readlane_u64(av.a, 0), fpi::readlane_u64(av.b, 0)};
+  const E2 fb{fpi::readlane_u64(bv.a, 0), fpi::readlane_u64(bv.b, 0)};
+  uint64_t h[8], m[16];
+  b2_init32(h);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) m[k] = s[k];
+  m[4] = fa.a;
+  m[5] = fa.b;
+  m[6] = fb.a;
+  m[7] = fb.b;
+#pragma unroll
+  for (int k = 8; k < 16; ++k) m[k] = 0;
+  b2_compress(h, m, 64, true);
+  if (lane == 0) {
+    finals[0] = fa.a;
+    finals[1] = fa.b;
+    finals[2] = fb.a;
+    finals[3] = fb.b;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) state[k] = h[k];
+  }
+}
+
+}  // namespace
+
+extern "C" int fp_fs_init(uint8_t* state, const uint8_t* msg, int32_t nbytes, hipStream_t stream) {
+  const char* fn = "fp_fs_init";
+  if (nbytes < 0 || nbytes > 8 * FS_MAX_INIT_WORDS) return fpi::fail(FP_EARG, "%s: nbytes=%d outside [0, 128]", fn, nbytes);
+  if (!state || (nbytes > 0 && !msg)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if (((uintptr_t)state) & 7) return fpi::fail(FP_EARG, "%s: state must be 8-byte aligned", fn);
+  InitMsg m{};
+  for (int i = 0; i < nbytes; ++i) m.w[i / 8] |= (uint64_t)msg[i] << (8 * (i % 8));
+  hipLaunchKernelGGL(fs_init_kernel, dim3(1), dim3(64), 0, stream, m, nbytes, (uint64_t*)state);
+  const int rc = fpi::check_launch("fs_init_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_fs_absorb(uint8_t* state, const fp_elem* data, int32_t nwords, hipStream_t stream) {
+  const char* fn = "fp_fs_absorb";
+  if (nwords < 0 || nwords > (1 << 20)) return fpi::fail(FP_EARG, "%s: nwords=%d", fn, nwords);
+  if (!state || (nwords > 0 && !data)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if (((uintptr_t)state) & 7) return fpi::fail(FP_EARG, "%s: state must be 8-byte aligned", fn);
+  hipLaunchKernelGGL(fs_absorb_kernel, dim3(1), dim3(64), 0, stream, (uint64_t*)state, data, nwords);
+  const int rc = fpi::check_launch("fs_absorb_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_fs_challenges(const uint8_t* state, int32_t k, fp_elem* out, hipStream_t stream) {
+  const char* fn = "fp_fs_challenges";
+  if (k < 0 || k > (1 << 20)) return fpi::fail(FP_EARG, "%s: k=%d", fn, k);
+  if (k == 0) return fpi::ok();
+  if (!state || !out) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if (((uintptr_t)state) & 7) return fpi::fail(FP_EARG, "%s: state must be 8-byte aligned", fn);
+  const int digests = (k + 1) / 2;
+  hipLaunchKernelGGL(fs_challenges_kernel, dim3((digests + 63) / 64), dim3(64), 0, stream, (const uint64_t*)state, k,
+                     out);
+  const int rc = fpi::check_launch("fs_challenges_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_eq_table_ext(const fp_elem* r, int32_t n, fp_elem* E0, fp_elem* E1, hipStream_t stream) {
+  const char* fn = "fp_eq_table_ext";
+  if (n < 0 || n > 24) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [0, 24]", fn, n);
+  if (!E0 || !E1 || (n > 0 && !r)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const int64_t N = (int64_t)1 << n;
+  hipLaunchKernelGGL(eq_ext_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, r, n, E0, E1);
+  const int rc = fpi::check_launch("eq_ext_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_ext_claim_combine(const fp_elem* c4, fp_elem* c0, hipStream_t stream) {
+  if (!c4 || !c0) return fpi::fail(FP_EARG, "fp_ext_claim_combine: null pointer");
+  hipLaunchKernelGGL(ext_claim_kernel, dim3(1), dim3(64), 0, stream, c4, c0);
+  const int rc = fpi::check_launch("ext_claim_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp_elem* B0, const fp_elem* B1,
+                                  int32_t n, uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals,
+                                  hipStream_t stream) {
+  const char* fn = "fp_sumcheck_ext_fs";
+  if (n < 0 || n > SE_MAXN) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [0, %d]", fn, n, SE_MAXN);
+  if (!A0 || !A1 || !B0 || !B1 || !state || !finals || (n > 0 && (!rounds || !r)))
+    return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if (((uintptr_t)state) & 7) return fpi::fail(FP_EARG, "%s: state must be 8-byte aligned", fn);
+  hipLaunchKernelGGL(sc_ext_fs_kernel, dim3(1), dim3(SE_T), 0, stream, A0, A1, B0, B1, n, (uint64_t*)state, rounds,
+                     r, finals);
+  const int rc = fpi::check_launch("sc_ext_fs_kernel");
+  return rc ? rc : fpi::ok();
+}

@@ -258,12 +258,6 @@ __global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t*
 // r_i is applied only after g_i is complete. finals = E, A, B at the point.
 constexpr int TQ = SC3_TAIL / SC3_TT;  // entries per thread in the first stage (8)
 
-__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int d) {
-  const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, d, 64);
-  const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), d, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t fold, int64_t size_in,
                                                           const uint64_t* __restrict__ r, int32_t i0, int32_t m,
                                                           uint64_t* __restrict__ rounds, uint64_t* __restrict__ finals,
@@ -361,7 +355,7 @@ __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t 
   // stage 3: entry x at lane x * dist, pairs dist apart
   uint64_t ev = e2[0], av = a2[0], bv = b2[0];
   for (int dist = 1; i < m; dist <<= 1, ++i) {
-    const uint64_t e1 = shfl_down_u64(ev, dist), a1 = shfl_down_u64(av, dist), b1 = shfl_down_u64(bv, dist);
+    const uint64_t e1 = fpi::shfl_down_u64(ev, dist), a1 = fpi::shfl_down_u64(av, dist), b1 = fpi::shfl_down_u64(bv, dist);
     const bool lead = (lane & (2 * dist - 1)) == 0;
     sct::S96 s96[4] = {};
     if (lead) pair_terms96(ev, e1, av, a1, bv, b1, s96);

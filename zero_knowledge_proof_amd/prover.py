@@ -22,9 +22,10 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (combine_claims, eq_table_batched, fold_claim_batched, gather_rows,
-               linear_combine, moe_plan, sumcheck_prove, sumcheck_prove_multi, to_field_tensor, field_numpy,
-               witness_linear, witness_linear_grouped, witness_linear_with_sumcheck)
+from . import (combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext, ext_claim_combine,
+               fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows, linear_combine, merkle_commit,
+               moe_plan, rs_encode, sumcheck_ext_fs, sumcheck_prove, sumcheck_prove_multi, to_field_tensor,
+               field_numpy, witness_linear, witness_linear_grouped, witness_linear_with_sumcheck)
 
 
 def _nomark(name):
@@ -409,6 +410,101 @@ class MoEBlockProver(_Prover):
                                "c0": int(c0[ne + i]), "rounds": rd[i], "finals": finals[ne + i:ne + i + 1],
                                "claim0": int(cl[ne + i])}}
         return out
+
+
+FS_LABEL = b"zkp-matmul-sumcheck-fs-v1"
+
+
+def commit_logn(n_limbs: int) -> int:
+    """Row length 2^logn of the commitment of n_limbs limbs: 2^22 elements as on
+    the pages, or the smallest power of two holding them all."""
+    return min(22, log2ceil(max(1, (n_limbs + 2) // 3)))
+
+
+class FaithfulLayerProver(_Prover):
+    """One linear map proved with soundness-faithful challenges ("How fast can
+    FlashProve go", §2: every challenge hashes all the prover has sent so far;
+    §4 footnote 20: the challenges live in an extension field). In order:
+    the witness; the commitment of Y and R (limbs packed three per element,
+    rows Reed-Solomon encoded, salted BLAKE2b Merkle tree); the transcript
+    absorbs the layer's shape and the Merkle root and yields r_t, r_o in
+    F_p[u]/(u^2 - 7); the eq tables and the folds of X and W (two base folds
+    each) and the claim c0 (four base claims combined) follow; c0 is absorbed;
+    the sum-check over the extension absorbs each round and draws each r_i
+    from the transcript on the device; the finals are absorbed."""
+
+    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, salts: np.ndarray, dev=None):
+        dev = dev or torch.device("cuda")
+        self.s = s
+        self.X, self.W = _i8(X, dev), _i8(W, dev)
+        T, d_in = X.shape
+        d_out = W.shape[0]
+        self.T, self.d_in, self.d_out = T, d_in, d_out
+        self.n_t, self.n_o, self.n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
+        self.Z = torch.empty((T, d_out), dtype=torch.int32, device=dev)
+        self.Y = torch.empty((T, d_out), dtype=torch.int8, device=dev)
+        self.R = torch.empty((T, d_out), dtype=torch.int8, device=dev)
+        self.logn = commit_logn(2 * T * d_out)
+        self.rows = commit_rows(T * d_out, T * d_out, self.logn)
+        width = 2 << self.logn
+        assert salts.shape == (width, 16)
+        self.salts = _i8(salts.astype(np.uint8), dev)
+        self.msg = torch.empty((self.rows, 1 << self.logn), dtype=torch.int64, device=dev)
+        self.code = torch.empty((self.rows, width), dtype=torch.int64, device=dev)
+        self.tree = torch.empty((2 * width - 1, 32), dtype=torch.uint8, device=dev)
+        self.state = torch.empty(4, dtype=torch.int64, device=dev)
+        self.init_msg = FS_LABEL + b"".join(int(v).to_bytes(4, "little") for v in (T, d_in, d_out, s))
+        self.chal = torch.empty((max(1, self.n_t + self.n_o), 2), dtype=torch.int64, device=dev)
+        self.Et = [_f(1 << self.n_t, dev), _f(1 << self.n_t, dev)]
+        self.Eo = [_f(1 << self.n_o, dev), _f(1 << self.n_o, dev)]
+        self.xf = [_f(1 << self.n, dev), _f(1 << self.n, dev)]
+        self.wf = [_f(1 << self.n, dev), _f(1 << self.n, dev)]
+        self.c4 = _f(4, dev)
+        self.c0 = _f(2, dev)
+        self.rounds = torch.empty((max(1, self.n), 3, 2), dtype=torch.int64, device=dev)
+        self.r = torch.empty((max(1, self.n), 2), dtype=torch.int64, device=dev)
+        self.finals = torch.empty((2, 2), dtype=torch.int64, device=dev)
+
+    def _commit(self):
+        commit_pack(self.Y.reshape(-1), self.R.reshape(-1), self.logn, self.rows, out=self.msg)
+        rs_encode(self.msg, code=self.code)
+        merkle_commit(self.code, self.salts, tree=self.tree)
+
+    def _challenges(self):
+        fs_init(self.state, self.init_msg)
+        fs_absorb(self.state, self.tree[-1].view(torch.int64))
+        fs_challenges(self.state, self.n_t + self.n_o, out=self.chal)
+
+    def _eq(self):
+        eq_table_ext(self.chal[:self.n_t], self.Et[0], self.Et[1])
+        eq_table_ext(self.chal[self.n_t:self.n_t + self.n_o], self.Eo[0], self.Eo[1])
+
+    def _fold_claim(self):
+        N = 1 << self.n
+        Et, Eo, c4 = self.Et, self.Eo, self.c4
+        fold_claim_batched([(self.X, Et[0], N, self.xf[0]), (self.X, Et[1], N, self.xf[1]),
+                            (self.W, Eo[0], N, self.wf[0]), (self.W, Eo[1], N, self.wf[1])],
+                           [(self.Z, Et[0], Eo[0], c4[0:1]), (self.Z, Et[1], Eo[1], c4[1:2]),
+                            (self.Z, Et[0], Eo[1], c4[2:3]), (self.Z, Et[1], Eo[0], c4[3:4])])
+        ext_claim_combine(self.c4, self.c0)
+        fs_absorb(self.state, self.c0)
+
+    def _sumcheck(self):
+        sumcheck_ext_fs(self.xf[0], self.xf[1], self.wf[0], self.wf[1], self.state, rounds=self.rounds, r=self.r,
+                        finals=self.finals)
+
+    def phases(self):
+        return [("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)),
+                ("commit", self._commit), ("transcript", self._challenges), ("eq", self._eq),
+                ("fold+claim", self._fold_claim), ("sumcheck", self._sumcheck)]
+
+    def results(self) -> dict:
+        u = lambda t: [tuple(int(x) for x in row) for row in field_numpy(t.reshape(-1, 2))]
+        return {"Z": self.Z.cpu().numpy(), "Y": self.Y.cpu().numpy(), "R": self.R.cpu().numpy(),
+                "root": bytes(self.tree[-1].cpu().numpy()), "c0": u(self.c0)[0],
+                "rounds": [u(self.rounds[i]) for i in range(self.n)], "r": u(self.r[:self.n]),
+                "finals": tuple(u(self.finals)), "state": bytes(self.state.cpu().numpy().view(np.uint8)),
+                "chal": u(self.chal[:self.n_t + self.n_o])}
 
 
 def can_pipeline(cfg) -> bool:
