@@ -198,6 +198,68 @@ __device__ __forceinline__ E2 emit_round(uint64_t (&s)[4], const E2 (&g)[3], uin
   return r;
 }
 
+// Stage 1 of the extension sum-check: CNT entries per thread, pairs inside the
+// thread; the round sums meet in LDS, wave 0 absorbs them and reads r_i, which
+// every thread then applies.
+template <int CNT>
+__device__ __forceinline__ void s1_round(E2 (&a)[SE_Q], E2 (&b)[SE_Q], uint64_t (&s)[4], sct::S96 (*red)[6],
+                                         uint64_t* rsh, uint64_t* rounds, uint64_t* r_out, int i) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  sct::S96 acc[6] = {};
+#pragma unroll
+  for (int p = 0; p < CNT / 2; ++p) pair_terms_e2(a[2 * p], a[2 * p + 1], b[2 * p], b[2 * p + 1], acc);
+#pragma unroll
+  for (int c = 0; c < 6; ++c) acc[c] = sct::wave_sum96(acc[c]);
+  if (lane == 63)
+#pragma unroll
+    for (int c = 0; c < 6; ++c) red[wave][c] = acc[c];
+  __syncthreads();
+  if (wave == 0) {
+    // every lane of wave 0 adds the wave totals and hashes the same message
+    E2 g[3];
+    uint64_t v[6];
+#pragma unroll
+    for (int c = 0; c < 6; ++c) {
+      sct::S96 t = red[0][c];
+#pragma unroll
+      for (int w = 1; w < SE_T / 64; ++w) t = sct::add96(t, red[w][c]);
+      v[c] = sct::reduce96(t);
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g[c] = E2{v[2 * c], v[2 * c + 1]};
+    const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
+    if (lane == 0) {
+      rsh[0] = r.a;
+      rsh[1] = r.b;
+    }
+  }
+  __syncthreads();
+  // only wave 0 carries the transcript: the other waves stop after stage 1
+  const E2 r{rsh[0], rsh[1]};
+#pragma unroll
+  for (int p = 0; p < CNT / 2; ++p) {
+    a[p] = e2_lerp(a[2 * p], a[2 * p + 1], r);
+    b[p] = e2_lerp(b[2 * p], b[2 * p + 1], r);
+  }
+}
+
+// Stage 2: wave 0 alone, CNT entries per lane, pairs inside the lane.
+template <int CNT>
+__device__ __forceinline__ void s2_round(E2 (&a)[8], E2 (&b)[8], uint64_t (&s)[4], uint64_t* rounds, uint64_t* r_out,
+                                         int i) {
+  sct::S96 acc[6] = {};
+#pragma unroll
+  for (int p = 0; p < CNT / 2; ++p) pair_terms_e2(a[2 * p], a[2 * p + 1], b[2 * p], b[2 * p + 1], acc);
+  E2 g[3];
+  wave_g(acc, g);
+  const E2 r = emit_round(s, g, rounds, r_out, i, (threadIdx.x & 63) == 0);
+#pragma unroll
+  for (int p = 0; p < CNT / 2; ++p) {
+    a[p] = e2_lerp(a[2 * p], a[2 * p + 1], r);
+    b[p] = e2_lerp(b[2 * p], b[2 * p + 1], r);
+  }
+}
+
 __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restrict__ A0, const uint64_t* __restrict__ A1,
                                                          const uint64_t* __restrict__ B0, const uint64_t* __restrict__ B1,
                                                          int32_t n, uint64_t* __restrict__ state,
@@ -222,49 +284,9 @@ __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restr
     b[k] = ok ? E2{B0[x], B1[x]} : E2{0, 0};
   }
   int i = 0;
-#pragma unroll
-  for (int cnt = SE_Q; cnt >= 2; cnt >>= 1) {
-    if (q == cnt) {
-      sct::S96 acc[6] = {};
-#pragma unroll
-      for (int p = 0; p < cnt / 2; ++p) pair_terms_e2(a[2 * p], a[2 * p + 1], b[2 * p], b[2 * p + 1], acc);
-#pragma unroll
-      for (int c = 0; c < 6; ++c) acc[c] = sct::wave_sum96(acc[c]);
-      if (lane == 63)
-#pragma unroll
-        for (int c = 0; c < 6; ++c) red[wave][c] = acc[c];
-      __syncthreads();
-      if (wave == 0) {
-        // every lane of wave 0 adds the wave totals and hashes the same message
-        E2 g[3];
-        uint64_t v[6];
-#pragma unroll
-        for (int c = 0; c < 6; ++c) {
-          sct::S96 t = red[0][c];
-#pragma unroll
-          for (int w = 1; w < SE_T / 64; ++w) t = sct::add96(t, red[w][c]);
-          v[c] = sct::reduce96(t);
-        }
-#pragma unroll
-        for (int c = 0; c < 3; ++c) g[c] = E2{v[2 * c], v[2 * c + 1]};
-        const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
-        if (lane == 0) {
-          rsh[0] = r.a;
-          rsh[1] = r.b;
-        }
-      }
-      __syncthreads();
-      // only wave 0 carries the transcript: the other waves stop after stage 1
-      const E2 r{rsh[0], rsh[1]};
-#pragma unroll
-      for (int p = 0; p < cnt / 2; ++p) {
-        a[p] = e2_lerp(a[2 * p], a[2 * p + 1], r);
-        b[p] = e2_lerp(b[2 * p], b[2 * p + 1], r);
-      }
-      ++i;
-      q = cnt / 2;
-    }
-  }
+  if (q == 8) s1_round<8>(a, b, s, red, rsh, rounds, r_out, i++), q = 4;
+  if (q == 4) s1_round<4>(a, b, s, red, rsh, rounds, r_out, i++), q = 2;
+  if (q == 2) s1_round<2>(a, b, s, red, rsh, rounds, r_out, i++), q = 1;
   // stage 2: n2 = min(N, 512) entries, one per thread -> wave 0, q2 per lane
   const int n2 = N < SE_T ? (int)N : SE_T;
   xa[tid] = a[0];
@@ -280,24 +302,9 @@ __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restr
     a2[k] = ok ? xa[x] : E2{0, 0};
     b2[k] = ok ? xb[x] : E2{0, 0};
   }
-#pragma unroll
-  for (int cnt = 8; cnt >= 2; cnt >>= 1) {
-    if (q2 == cnt) {
-      sct::S96 acc[6] = {};
-#pragma unroll
-      for (int p = 0; p < cnt / 2; ++p) pair_terms_e2(a2[2 * p], a2[2 * p + 1], b2[2 * p], b2[2 * p + 1], acc);
-      E2 g[3];
-      wave_g(acc, g);
-      const E2 r = emit_round(s, g, rounds, r_out, i, lane == 0);
-#pragma unroll
-      for (int p = 0; p < cnt / 2; ++p) {
-        a2[p] = e2_lerp(a2[2 * p], a2[2 * p + 1], r);
-        b2[p] = e2_lerp(b2[2 * p], b2[2 * p + 1], r);
-      }
-      ++i;
-      q2 = cnt / 2;
-    }
-  }
+  if (q2 == 8) s2_round<8>(a2, b2, s, rounds, r_out, i++), q2 = 4;
+  if (q2 == 4) s2_round<4>(a2, b2, s, rounds, r_out, i++), q2 = 2;
+  if (q2 == 2) s2_round<2>(a2, b2, s, rounds, r_out, i++), q2 = 1;
   // stage 3: entry x at lane x * dist, partners dist apart
   E2 av = a2[0], bv = b2[0];
   for (int dist = 1; i < n; dist <<= 1, ++i) {
