@@ -613,6 +613,17 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         phase_ms[name] = e0.elapsed_time(e1) / args.steps
+    # one-time weight preparation (outside the timed step): the packed layout the witness reads
+    packed = None
+    if getattr(prover, "Wp", None) is not None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fp.pack_weights(prover.W)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        packed = {"ms": round(e0.elapsed_time(e1), 4), "bytes": prover.Wp.data.numel(),
+                  "note": "the layer's weights packed once for the matrix cores (fp_witness_pack_weights); "
+                          "a fixed layer is packed when it is loaded, so this is not part of a step"}
     dom = max(phase_ms, key=lambda k: phase_ms[k])
     b, ops = kernel_work(cfg, dom, prover)
     t = phase_ms[dom] * 1e-3
@@ -646,6 +657,7 @@ def main():
         "witness_int8_TOPS": extras.get(wkey, {}).get("TOPS"),
         "witness_mfma_frac": round(wops / (phase_ms[wkey] * 1e-3) / MFMA_I8_PEAK, 4),
         "phases": extras,
+        "weights_packed": packed,
         "wall_s": round(wall, 3),
     }
     if not args.no_faithful:

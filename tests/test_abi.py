@@ -38,6 +38,8 @@ def test_argument_errors_without_gpu():
     assert b"s=9" in L.fp_last_error()
     # d_in too large for an exact int32 witness
     assert L.fp_witness_linear(None, 200000, None, 200000, 1, 131073, 1, 8, None, None, None, None) == 2
+    # 128^2 * 131072 = 2^31 would overflow int32 when every product is (-128)^2
+    assert L.fp_witness_linear(None, 131072, None, 131072, 1, 131072, 1, 8, None, None, None, None) == 2
     # eq table size
     assert L.fp_eq_table(None, 31, None, None) == 2
     # sum-check sizes
@@ -60,6 +62,19 @@ def test_argument_errors_without_gpu():
                                              dummy, dummy, dummy, None, None) == 1
     assert L.fp_witness_linear_with_sumcheck(None, 16, None, 16, 0, 16, 4, 8, None, None, None, 1, pa, pa, None, 13,
                                              dummy, dummy, dummy, None, None) == 2
+    assert b"exceed one" in L.fp_last_error()
+    # packed weights: ceil(d_out / 32) * 32 rows of ceil(d_in / 64) * 64 bytes; the packed witness needs
+    # d_in % 16 == 0 and 16-byte aligned X rows
+    assert L.fp_witness_packed_weights_bytes(100, 100) == 128 * 128
+    assert L.fp_witness_packed_weights_bytes(14336, 4096) == 14336 * 4096
+    assert L.fp_witness_packed_weights_bytes(-1, 4) == 0
+    assert L.fp_witness_pack_weights(dummy, 8, 4, 16, dummy, None) == 2
+    assert L.fp_witness_linear_packed(dummy, 40, dummy, 4, 40, 4, 8, None, dummy, dummy, None) == 2
+    assert b"d_in % 16" in L.fp_last_error()
+    assert L.fp_witness_linear_packed(ctypes.c_void_p(24), 48, dummy, 4, 48, 4, 8, None, dummy, dummy, None) == 2
+    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 0, None, dummy, dummy, None) == 3
+    assert L.fp_witness_linear_packed_with_sumcheck(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 1, pa, pa, None,
+                                                    13, dummy, dummy, dummy, None, None) == 2
     assert b"exceed one" in L.fp_last_error()
     # multi-request fold: Mt's leading dim must be a multiple of 16, R bounded, workspace checked
     assert L.fp_fold_weights_prepare(dummy, 64, 100, 64, dummy, 104, dummy, None) == 2

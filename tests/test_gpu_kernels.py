@@ -317,6 +317,103 @@ def test_witness_strided_inputs(fp):
     assert np.array_equal(R.cpu().numpy(), wr)
 
 
+# ------------------------------------------------------- packed weights ---
+def _pack_ref(W):
+    """The packed layout include/fp.h documents, built in numpy: fragment (b, c, q), lane l holds
+    W[32 b + l % 32][64 c + 32 (l // 32) + 16 q + 0..15], zero past the matrix."""
+    d_out, d_in = W.shape
+    nrb, nkb = -(-d_out // 32), -(-d_in // 64)
+    Wz = np.zeros((nrb * 32, nkb * 64), np.int8)
+    Wz[:d_out, :d_in] = W
+    A = Wz.reshape(nrb, 32, nkb, 2, 2, 16)  # [b][row][c][half][q][byte]
+    return A.transpose(0, 2, 4, 3, 1, 5).reshape(-1)  # [b][c][q][lane = 32 half + row][byte]
+
+
+@pytest.mark.parametrize("d_out,d_in", [(1, 1), (7, 17), (33, 64), (100, 300), (64, 4096)])
+def test_pack_weights(fp, d_out, d_in):
+    rng = _rng(d_out * 7 + d_in)
+    W = _i8(rng, (d_out, d_in))
+    Wp = fp.pack_weights(_dev(W))
+    torch.cuda.synchronize()
+    want = _pack_ref(W)
+    assert Wp.data.numel() == max(want.size, 16)
+    assert np.array_equal(Wp.data.cpu().numpy()[:want.size], want)
+
+
+PACK_SHAPES = [(1, 16, 1, 8), (5, 48, 7, 7), (33, 64, 129, 8), (130, 304, 300, 1), (200, 1008, 260, 8),
+               (257, 128, 513, 4), (64, 4096, 256, 8), (300, 80, 70, 3), (4, 0, 9, 8)]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,s", PACK_SHAPES)
+def test_witness_packed(fp, T, d_in, d_out, s):
+    """The witness from packed weights equals the oracle's (256x64 tiles: ragged in T, d_out and d_in)."""
+    rng = _rng(T * 1000 + d_in + d_out + 7)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    Z, Y, R = fp.witness_linear_packed(_dev(X), fp.pack_weights(_dev(W)), s)
+    torch.cuda.synchronize()
+    wz, wy, wr = O.witness(X, W, s)
+    assert np.array_equal(Z.cpu().numpy(), wz)
+    assert np.array_equal(Y.cpu().numpy(), wy)
+    assert np.array_equal(R.cpu().numpy(), wr)
+
+
+def test_witness_packed_extremes_strided_and_no_z(fp):
+    # |Z| at its largest, rounding ties, X rows with a 16-byte aligned stride, and Z not stored
+    T, d_in, d_out = 40, 4096, 70
+    X = np.full((T, d_in), -128, np.int8)
+    X[1::2] = 127
+    W = np.full((d_out, d_in), -128, np.int8)
+    W[3::3] = 127
+    W[5, :] = 0
+    W[5, 0] = 1
+    X[7, :] = 0
+    X[7, :128] = 1
+    W[6, :] = 0
+    W[6, :128] = 1  # Z[7, 6] = 128: a tie at s = 8
+    Wp = fp.pack_weights(_dev(W))
+    for s in (8, 7, 1):
+        Z, Y, R = fp.witness_linear_packed(_dev(X), Wp, s)
+        torch.cuda.synchronize()
+        wz, wy, wr = O.witness(X, W, s)
+        assert np.array_equal(Z.cpu().numpy(), wz)
+        assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+    rng = _rng(22)
+    Xb, W2 = _i8(rng, (50, 352)), _i8(rng, (90, 304))
+    _, Y, R = fp.witness_linear_packed(_dev(Xb)[:, 32:336], fp.pack_weights(_dev(W2)), 8, with_z=False)
+    torch.cuda.synchronize()
+    _, wy, wr = O.witness(np.ascontiguousarray(Xb[:, 32:336]), W2, 8)
+    assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+
+
+@pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 320, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
+                                             (0, 64, 64, 2, 10), (40, 96, 0, 1, 5)])
+def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):
+    """One launch: a packed-weight witness and an unrelated sum-check, each against the oracle."""
+    rng = _rng(900 + T + n + k)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    As = [_field(rng, 1 << n, False) for _ in range(k)]
+    Bs = [_field(rng, 1 << n, False) for _ in range(k)]
+    r = _field(rng, n, specials=(n >= 4))
+    rho = _field(rng, k, False) if k > 1 else None
+    Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda")
+    Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    _, (rounds, finals, c0) = fp.witness_linear_packed_with_sumcheck(
+        _dev(X), fp.pack_weights(_dev(W)), 8, Z, Y, R, [fp.to_field_tensor(a) for a in As],
+        [fp.to_field_tensor(b) for b in Bs], fp.to_field_tensor(r),
+        rho=None if rho is None else fp.to_field_tensor(rho))
+    torch.cuda.synchronize()
+    if T and d_out:
+        wz, wy, wr = O.witness(X, W, 8)
+        assert np.array_equal(Z.cpu().numpy(), wz)
+        assert np.array_equal(Y.cpu().numpy(), wy)
+        assert np.array_equal(R.cpu().numpy(), wr)
+    grs, gfs, gc = O.sumcheck(As, Bs, r, rho=rho)
+    assert np.array_equal(fp.field_numpy(rounds), grs)
+    assert np.array_equal(fp.field_numpy(finals), gfs)
+    assert int(fp.field_numpy(c0)[0]) == gc
+
+
 def test_witness_grouped(fp):
     rng = _rng(22)
     sizes = [3, 0, 40, 1, 0, 65, 17]

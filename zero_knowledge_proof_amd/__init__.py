@@ -29,7 +29,8 @@ EXPORTS = [
     "fp_fold_matrix_multi_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
     "fp_merkle_commit", "fp_lookup_tree", "fp_lookup_counts", "fp_sumcheck3_prove", "fp_sumcheck3_workspace",
     "fp_lookup_prove", "fp_lookup_prove_workspace", "fp_fs_init", "fp_fs_absorb", "fp_fs_challenges",
-    "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs",
+    "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
+    "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
 ]
 
 _lib = None
@@ -106,6 +107,11 @@ def lib():
             "fp_eq_table_ext": (ctypes.c_int, [vp, i32, vp, vp, vp]),
             "fp_ext_claim_combine": (ctypes.c_int, [vp, vp, vp]),
             "fp_sumcheck_ext_fs": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_witness_packed_weights_bytes": (sz, [i32, i32]),
+            "fp_witness_pack_weights": (ctypes.c_int, [vp, i64, i32, i32, vp, vp]),
+            "fp_witness_linear_packed": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "fp_witness_linear_packed_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp,
+                                                                      i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -211,6 +217,61 @@ def witness_linear_with_sumcheck(X, W, s: int, Z, Y, R, As, Bs, r, rho=None, rou
                                                  _ptr(Y), _ptr(R), k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds),
                                                  _ptr(finals), _ptr(claim0), _stream()),
            "fp_witness_linear_with_sumcheck")
+    return (Z, Y, R), (rounds, finals, claim0)
+
+
+class PackedWeights:
+    """The weights of one layer packed for the matrix cores (fp_witness_pack_weights):
+    ``data`` is the packed int8 buffer, ``d_out`` and ``d_in`` the shape of W."""
+
+    def __init__(self, data: torch.Tensor, d_out: int, d_in: int):
+        self.data, self.d_out, self.d_in = data, d_out, d_in
+
+
+def pack_weights(W) -> PackedWeights:
+    d_out, d_in = W.shape
+    assert W.dtype == torch.int8 and (W.numel() == 0 or W.stride(1) == 1), "rows must be contiguous"
+    nbytes = lib().fp_witness_packed_weights_bytes(d_out, d_in)
+    Wp = torch.empty(max(nbytes, 16), dtype=torch.int8, device=W.device)
+    _check(lib().fp_witness_pack_weights(_ptr(W), _ld(W), d_out, d_in, _ptr(Wp), _stream()),
+           "fp_witness_pack_weights")
+    return PackedWeights(Wp, d_out, d_in)
+
+
+def witness_linear_packed(X, Wp: PackedWeights, s: int, Z=None, Y=None, R=None, with_z: bool = True):
+    """witness_linear(X, W, s) with W given packed (pack_weights(W))."""
+    T, d_in = X.shape
+    assert X.dtype == torch.int8 and d_in == Wp.d_in
+    assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
+    d_out = Wp.d_out
+    if with_z and Z is None:
+        Z = torch.empty((T, d_out), dtype=torch.int32, device=X.device)
+    Y = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if Y is None else Y
+    R = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if R is None else R
+    _check(lib().fp_witness_linear_packed(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, d_out, s,
+                                          _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), _stream()),
+           "fp_witness_linear_packed")
+    return Z, Y, R
+
+
+def witness_linear_packed_with_sumcheck(X, Wp: PackedWeights, s: int, Z, Y, R, As, Bs, r, rho=None, rounds=None,
+                                        finals=None, claim0=None):
+    """witness_linear_packed(X, Wp, s, Z, Y, R) and sumcheck_prove(As, Bs, r, rho, ...) in one launch."""
+    T, d_in = X.shape
+    assert X.dtype == torch.int8 and d_in == Wp.d_in
+    assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
+    k = len(As)
+    n = r.numel()
+    dev = r.device
+    rounds = torch.empty((n, 3), dtype=torch.int64, device=dev) if rounds is None else rounds
+    finals = torch.empty((k, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    claim0 = torch.empty(1, dtype=torch.int64, device=dev) if claim0 is None else claim0
+    pa = (ctypes.c_void_p * k)(*[a.data_ptr() for a in As])
+    pb = (ctypes.c_void_p * k)(*[b.data_ptr() for b in Bs])
+    _check(lib().fp_witness_linear_packed_with_sumcheck(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, Wp.d_out, s,
+                                                        _ptr(Z), _ptr(Y), _ptr(R), k, pa, pb, _ptr(rho), n, _ptr(r),
+                                                        _ptr(rounds), _ptr(finals), _ptr(claim0), _stream()),
+           "fp_witness_linear_packed_with_sumcheck")
     return (Z, Y, R), (rounds, finals, claim0)
 
 

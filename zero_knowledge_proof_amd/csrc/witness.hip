@@ -26,6 +26,8 @@
 // 64- or 128-byte pitch measures 3-6x slower). Workgroup ids are remapped so that each XCD (ids are dealt to
 // the 8 XCDs round-robin) works on a contiguous run of tiles; tokens vary
 // fastest, so one W panel is shared by the XCD's tiles in its L2.
+#include <utility>
+
 #include "common.hpp"
 #include "sc_tail.hpp"
 
@@ -55,6 +57,8 @@ struct WitArgs {
   const int32_t* colsum;
   uint64_t* part;
   int64_t ldp, psplit;
+  // packed weights (W then points at them): 32-row blocks and WP_BK-byte K blocks
+  int32_t wp_rb, wp_kb;
 };
 
 struct GroupTab {
@@ -91,6 +95,74 @@ __device__ __forceinline__ void rescale(int32_t z, int s, int32_t lowmask, uint3
   const int32_t yy = q < -128 ? -128 : (q > 127 ? 127 : q);
   y = (uint32_t)(uint8_t)(int8_t)yy;
   r = (uint32_t)(uint8_t)(int8_t)rr;
+}
+
+// One 32x32 accumulator fragment as 16 consecutive outputs per lane: lanes
+// 0-31 keep o = 0..15 of the 32-block, lanes 32-63 take o = 16..31 (two
+// v_permlane32_swap per 4 accumulators), then the o offsets are in register
+// order 0-3, 8-11, 4-7, 12-15.
+__device__ __forceinline__ void fragment_outputs(const v16i& accv, int32_t (&z)[16]) {
+  int32_t v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = accv[k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v[k], (unsigned)v[k + 8], false, false);
+    v[k] = (int32_t)sw[0];
+    v[k + 8] = (int32_t)sw[1];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    z[q] = v[q];
+    z[4 + q] = v[8 + q];
+    z[8 + q] = v[4 + q];
+    z[12 + q] = v[12 + q];
+  }
+}
+
+// Y, R (and Z unless NULL) of 16 consecutive outputs o0.. of token t, held by one
+// lane after the swap; the caller has checked t < T and o0 < N.
+__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s,
+                                               int32_t lowmask) {
+  const int64_t idx = (int64_t)t * a.N + o0;
+  uint32_t yw[4] = {0, 0, 0, 0}, rw[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    uint32_t y, r;
+    rescale(z[q], s, lowmask, y, r);
+    yw[q >> 2] |= y << (8 * (q & 3));
+    rw[q >> 2] |= r << (8 * (q & 3));
+  }
+  if (o0 + 16 <= a.N) {
+    if (a.Z) {
+      if (a.vecZ) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(v4i*)(a.Z + idx + 4 * q) = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) a.Z[idx + q] = z[q];
+      }
+    }
+    if (a.vecYR) {
+      *(v4i*)(a.Y + idx) = v4i{(int)yw[0], (int)yw[1], (int)yw[2], (int)yw[3]};
+      *(v4i*)(a.R + idx) = v4i{(int)rw[0], (int)rw[1], (int)rw[2], (int)rw[3]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
+        a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (o0 + q < a.N) {
+        if (a.Z) a.Z[idx + q] = z[q];
+        a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
+        a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
+      }
+    }
+  }
 }
 
 // LDS of one GEMM workgroup: double-buffered W and X tiles.
@@ -254,25 +326,8 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      int32_t v[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = acc[i][j][k];
-      // lanes 0-31 keep o = 0..15 of the 32-block, lanes 32-63 take o = 16..31
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v[k], (unsigned)v[k + 8], false, false);
-        v[k] = (int32_t)sw[0];
-        v[k + 8] = (int32_t)sw[1];
-      }
-      // order of o offsets: regs 0-3, 8-11, 4-7, 12-15
       int32_t z[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        z[q] = v[q];
-        z[4 + q] = v[8 + q];
-        z[8 + q] = v[4 + q];
-        z[12 + q] = v[12 + q];
-      }
+      fragment_outputs(acc[i][j], z);
       const int t = t_base + wt0 + 32 * j + (lane & 31);
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
       if (t >= t_lim || o0 >= a.N) continue;
@@ -294,45 +349,7 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
         }
         continue;
       }
-      const int64_t idx = (int64_t)t * a.N + o0;
-      uint32_t yw[4] = {0, 0, 0, 0}, rw[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        uint32_t y, r;
-        rescale(z[q], s, lowmask, y, r);
-        yw[q >> 2] |= y << (8 * (q & 3));
-        rw[q >> 2] |= r << (8 * (q & 3));
-      }
-      if (o0 + 16 <= a.N) {
-        if (a.Z) {
-          if (a.vecZ) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *(v4i*)(a.Z + idx + 4 * q) = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) a.Z[idx + q] = z[q];
-          }
-        }
-        if (a.vecYR) {
-          *(v4i*)(a.Y + idx) = v4i{(int)yw[0], (int)yw[1], (int)yw[2], (int)yw[3]};
-          *(v4i*)(a.R + idx) = v4i{(int)rw[0], (int)rw[1], (int)rw[2], (int)rw[3]};
-        } else {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
-            a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if (o0 + q < a.N) {
-            if (a.Z) a.Z[idx + q] = z[q];
-            a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
-            a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
-          }
-        }
-      }
+      store_fragment(a, z, t, o0, s, lowmask);
     }
   }
 }
@@ -357,6 +374,209 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(
     return;
   }
   witness_body<BO, BT, WO, WT, GROUPED, PF, BK, 0>(a, gt, blockIdx.x - n_tail, gridDim.x - n_tail, sh);
+}
+
+
+// ---- packed weights: W streamed straight into the MFMA registers ----------
+// The weights of a layer are fixed, so they can be laid out once in the order
+// the matrix cores read them: fragment (row block b, K block c, step q) is
+// 1 KiB, lane l holding W[32 b + l%32][WP_BK c + (l/32) WP_BK/2 + 16 q + 0..15]
+// (zero past d_out and d_in). Within a K block the two lane halves take
+// different byte ranges of the same rows; X is staged in LDS in the same
+// order, so both operands pair equal k and the sum over k is unchanged. A
+// wave's weight fragments are then single coalesced 1 KiB loads that no other
+// wave needs, and only X (shared by the workgroup's waves) passes through LDS:
+// half the LDS traffic per MFMA of the tile above, and the register copy of
+// each W byte is used against all of the workgroup's tokens.
+constexpr int WP_BK = 64;
+
+__global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restrict__ W, int64_t ldw, int32_t N,
+                                                           int32_t K, int32_t nrb, int32_t nkb, int vec,
+                                                           int8_t* __restrict__ Wp) {
+  constexpr int KS = WP_BK / 32;
+  const int64_t units = (int64_t)nrb * nkb * KS * 64;  // 16-byte units
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int l = (int)(u & 63);
+    int64_t f = u >> 6;  // (b nkb + c) KS + q
+    const int q = (int)(f % KS);
+    f /= KS;
+    const int c = (int)(f % nkb);
+    const int b = (int)(f / nkb);
+    const int row = 32 * b + (l & 31);
+    const int k = WP_BK * c + (l >> 5) * (WP_BK / 2) + 16 * q;
+    v4i val = {0, 0, 0, 0};
+    if (row < N) val = load16(W + (int64_t)row * ldw, k, K, vec != 0);
+    *(v4i*)(Wp + u * 16) = val;
+  }
+}
+
+// Tile `bid` of `nblocks`: NW waves, wave w owning weight rows
+// [o_base + 32 TM w, +32 TM) (fragments from the packed weights, PFW K blocks
+// ahead) and all BT = 32 TN tokens of the tile (X through double-buffered
+// LDS, PFX K blocks ahead in registers). Every K block issues its loads
+// unconditionally (past the end they re-read the last block), so the code
+// between barriers is straight-line and the compiler's wait counts let the
+// prefetches stay in flight. X chunks past d_in are read from column 0: they
+// meet zero weights. Requires d_in % 16 == 0 and 16-byte aligned X rows.
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+struct WsCfg {
+  static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
+  static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32, HB = BK / 2;
+  static constexpr int LDS_BYTES = 2 * BT * PITCH;
+  static_assert((BT * CPR) % NT == 0, "X chunks per thread");
+};
+
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+__device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int nblocks, int8_t* lds) {
+  using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
+  constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
+  constexpr int KS = C::KS, HB = C::HB;
+  int8_t (*sB)[BT * PITCH] = reinterpret_cast<int8_t (*)[BT * PITCH]>(lds);
+  const int tile = xcd_tile(bid, nblocks);
+  const int tt = tile % a.tiles_t, to = tile / a.tiles_t;
+  const int t_base = tt * BT, o_base = to * BO;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int wo0 = wave * 32 * TM;
+  const int64_t rb_bytes = (int64_t)a.wp_kb * BK * 32;  // one 32-row block of the packed weights
+  const int8_t* pw[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) pw[i] = a.W + (int64_t)min((o_base + wo0) / 32 + i, a.wp_rb - 1) * rb_bytes + lane * 16;
+  const int8_t* px[CB];
+  int kc[CB], so[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int ch = tid + c * NT, row = ch / CPR;
+    kc[c] = (ch % CPR) * 16;
+    px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx;
+    so[c] = row * PITCH + kc[c];
+  }
+  v4i wf[PFW][TM][KS];
+  v4i xr[PFX][CB];
+  auto wload = [&](int slot, int kblk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < KS; ++q) wf[slot][i][q] = *(const v4i*)(pw[i] + (int64_t)kblk * (BK * 32) + 1024 * q);
+  };
+  auto xload = [&](int slot, int kblk) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int k = kblk * BK + kc[c];
+      xr[slot][c] = *(const v4i*)(px[c] + (k < a.K ? k : 0));
+    }
+  };
+  auto sstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) *(v4i*)&sB[buf][so[c]] = xr[slot][c];
+  };
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+  auto compute = [&](int buf, int ws) {
+    const int8_t* B = &sB[buf][r * PITCH + HB * h];
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      v4i fb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = *(const v4i*)(B + 32 * j * PITCH + 16 * q);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ws][i][q], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // K block s: multiply out of LDS buffer s%2 with weight slot s%PFW, refill
+  // that slot with block s+PFW, store block s+1 (register slot (s+1)%PFX) into
+  // the other buffer and refill its slot with block s+1+PFX; one barrier.
+  constexpr int L1 = (PFW % 2 == 0) ? PFW : 2 * PFW;
+  constexpr int U = ((L1 % PFX == 0) ? L1 : L1 * PFX) * UNR;
+  const int KT = a.wp_kb;
+  if (KT > 0) {  // d_in = 0: every output is 0
+#pragma unroll
+    for (int p = 0; p < PFW; ++p) wload(p, min(p, KT - 1));
+#pragma unroll
+    for (int p = 0; p < PFX; ++p) xload(p, min(p, KT - 1));
+    sstore(0, 0);
+    xload(0, min(PFX, KT - 1));
+    __syncthreads();
+    auto step = [&](auto uc, int st) {
+      constexpr int u = decltype(uc)::value;
+      compute(u % 2, u % PFW);
+      wload(u % PFW, min(st + PFW, KT - 1));
+      sstore((u + 1) % PFX, (u + 1) % 2);
+      xload((u + 1) % PFX, min(st + 1 + PFX, KT - 1));
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + U <= KT; kt += U) {
+      [&]<int... I>(std::integer_sequence<int, I...>) { (step(std::integral_constant<int, I>{}, kt + I), ...); }(
+          std::make_integer_sequence<int, U>{});
+    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((kt + I < KT ? step(std::integral_constant<int, I>{}, kt + I) : void()), ...);
+    }(std::make_integer_sequence<int, U>{});
+  }
+
+  const int s = a.s;
+  const int32_t lowmask = (1 << s) - 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int32_t z[16];
+      fragment_outputs(acc[i][j], z);
+      const int t = t_base + 32 * j + r;
+      const int o0 = o_base + wo0 + 32 * i + 16 * h;
+      if (t < a.T && o0 < a.N) store_fragment(a, z, t, o0, s, lowmask);
+    }
+}
+
+// 256x64 workgroup tiles (outputs x tokens): 4 waves of 64x64, weight
+// fragments two K blocks ahead, X two blocks ahead; two workgroups per CU.
+#define WIT_WS 4, 2, 2, 2, 2, 4
+
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_kernel(WitArgs a) {
+  __shared__ __align__(16) int8_t lds[WsCfg<NW, TM, TN, PFW, PFX, UNR>::LDS_BYTES];
+  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, blockIdx.x, gridDim.x, lds);
+}
+
+// With sum-check tails in workgroups [0, n_tail), as witness_sc_kernel.
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_sc_kernel(
+    WitArgs a, sct::TailArgs ta, int n_tail) {
+  constexpr int NT = NW * 64;
+  constexpr int GEMM_LDS = WsCfg<NW, TM, TN, PFW, PFX, UNR>::LDS_BYTES;
+  constexpr int BYTES = GEMM_LDS > (int)sizeof(sct::TailLds<NT>) ? GEMM_LDS : (int)sizeof(sct::TailLds<NT>);
+  __shared__ __align__(16) int8_t lds[BYTES];
+  if ((int)blockIdx.x < n_tail) {
+    sct::tail_body<NT>(ta, blockIdx.x, *reinterpret_cast<sct::TailLds<NT>*>(lds));
+    return;
+  }
+  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, blockIdx.x - n_tail, gridDim.x - n_tail, lds);
+}
+
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, hipStream_t st) {
+  using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
+  a.tiles_t = (a.T + C::BT - 1) / C::BT;
+  a.tiles_o = (a.N + C::BO - 1) / C::BO;
+  const int64_t tiles = (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o : 0;
+  if (tiles + n_tail > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
+  if (tiles + n_tail == 0) return FP_OK;
+  if (ta) {
+    hipLaunchKernelGGL((witness_ws_sc_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)(tiles + n_tail)),
+                       dim3(C::NT), 0, st, a, *ta, n_tail);
+    return fpi::check_launch("witness_ws_sc_kernel");
+  }
+  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  return fpi::check_launch("witness_ws_kernel");
 }
 
 // Tile configurations (BO, BT, WO, WT, grouped, prefetch distance, K step),
@@ -414,6 +634,32 @@ void vec_flags(WitArgs& a) {
   a.vecX = ((a.ldx & 15) == 0) && ((((uintptr_t)a.X) & 15) == 0);
   a.vecZ = ((a.N & 3) == 0) && ((((uintptr_t)a.Z) & 15) == 0);
   a.vecYR = ((a.N & 15) == 0) && ((((uintptr_t)a.Y) & 15) == 0) && ((((uintptr_t)a.R) & 15) == 0);
+}
+
+// Checks and packs the arguments of a sum-check that runs as the tail of a
+// witness launch of nt-thread workgroups.
+int tail_args(const char* fn, int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B, const fp_elem* rho,
+              int32_t n, const fp_elem* r, fp_elem* rounds, fp_elem* finals, fp_elem* claim0, int nt,
+              sct::TailArgs& ta) {
+  if (n_pairs < 1 || n_pairs > sct::SC_MAX_PAIRS)
+    return fpi::fail(FP_EARG, "%s: n_pairs=%d outside [1, %d]", fn, n_pairs, sct::SC_MAX_PAIRS);
+  if (n < 1 || n > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [1, %d]", fn, n, FP_MAX_N);
+  if (!A || !B || !r || !rounds || !finals) return fpi::fail(FP_EARG, "%s: null sum-check pointer", fn);
+  for (int j = 0; j < n_pairs; ++j)
+    if (!A[j] || !B[j]) return fpi::fail(FP_EARG, "%s: null table %d", fn, j);
+  int vp = 1;
+  while (vp < n_pairs) vp <<= 1;
+  if (((int64_t)vp << n) > (int64_t)nt * sct::SLMAX)
+    return fpi::fail(FP_ESHAPE, "%s: %d x 2^%d table entries exceed one %d-thread workgroup (%d)", fn, vp, n, nt,
+                     nt * sct::SLMAX);
+  ta = sct::TailArgs{};
+  for (int j = 0; j < n_pairs; ++j) {
+    ta.user.A[j] = A[j];
+    ta.user.B[j] = B[j];
+  }
+  ta.rho = rho; ta.r = r; ta.rounds = rounds; ta.finals = finals; ta.claim0 = claim0;
+  ta.i0 = 0; ta.n = n; ta.n_pairs = n_pairs; ta.nprev = 0; ta.multi = 0;
+  return FP_OK;
 }
 
 }  // namespace
@@ -498,31 +744,16 @@ extern "C" int fp_witness_linear_with_sumcheck(const int8_t* X, int64_t ldx, con
   int rc = validate(fn, ldx, ldw, T, d_in, d_out, s, Y, R);
   if (rc) return rc;
   if (T > 0 && d_out > 0 && d_in > 0 && (!X || !W)) return fpi::fail(FP_EARG, "%s: null X or W", fn);
-  if (n_pairs < 1 || n_pairs > sct::SC_MAX_PAIRS)
-    return fpi::fail(FP_EARG, "%s: n_pairs=%d outside [1, %d]", fn, n_pairs, sct::SC_MAX_PAIRS);
-  if (n < 1 || n > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [1, %d]", fn, n, FP_MAX_N);
-  if (!A || !B || !r || !rounds || !finals) return fpi::fail(FP_EARG, "%s: null sum-check pointer", fn);
-  for (int j = 0; j < n_pairs; ++j)
-    if (!A[j] || !B[j]) return fpi::fail(FP_EARG, "%s: null table %d", fn, j);
-  int vp = 1;
-  while (vp < n_pairs) vp <<= 1;
   const int nt = witness_threads(T, d_out);
-  if (((int64_t)vp << n) > (int64_t)nt * sct::SLMAX)
-    return fpi::fail(FP_ESHAPE, "%s: %d x 2^%d table entries exceed one %d-thread workgroup (%d)", fn, vp, n, nt,
-                     nt * sct::SLMAX);
+  sct::TailArgs ta;
+  rc = tail_args(fn, n_pairs, A, B, rho, n, r, rounds, finals, claim0, nt, ta);
+  if (rc) return rc;
   WitArgs a{};
   a.X = X; a.ldx = ldx; a.W = W; a.ldw = ldw;
   a.T = T; a.N = d_out; a.K = d_in; a.s = s;
   a.Z = Z; a.Y = Y; a.R = R;
   vec_flags(a);
   a.vecW = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
-  sct::TailArgs ta{};
-  for (int j = 0; j < n_pairs; ++j) {
-    ta.user.A[j] = A[j];
-    ta.user.B[j] = B[j];
-  }
-  ta.rho = rho; ta.r = r; ta.rounds = rounds; ta.finals = finals; ta.claim0 = claim0;
-  ta.i0 = 0; ta.n = n; ta.n_pairs = n_pairs; ta.nprev = 0; ta.multi = 0;
   GroupTab gt{};
   const int64_t xl_tiles = (int64_t)((d_out + 255) / 256) * ((T + 255) / 256);
   if (T <= 32) rc = launch_with_tail<WIT_S>(a, gt, ta, 1, stream);
@@ -568,3 +799,93 @@ int witness_fold_splitk(const int8_t* Xt, int64_t ldx, const int8_t* D, int64_t 
 }
 
 }  // namespace fpi
+
+// ---- packed weights ------------------------------------------------------
+namespace {
+
+bool packed_dims(int32_t d_out, int32_t d_in, int32_t& nrb, int32_t& nkb) {
+  if (d_out < 0 || d_in < 0) return false;
+  nrb = (d_out + 31) / 32;
+  nkb = (d_in + WP_BK - 1) / WP_BK;
+  return true;
+}
+
+// Shared checks of the packed-weight witness entry points.
+int packed_args(const char* fn, const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
+                int32_t d_out, int32_t s, const int8_t* Y, const int8_t* R, WitArgs& a) {
+  int rc = validate(fn, ldx, d_in, T, d_in, d_out, s, Y, R);
+  if (rc) return rc;
+  if (T > 0 && d_out > 0 && d_in > 0) {
+    if (!X || !Wp) return fpi::fail(FP_EARG, "%s: null X or packed W", fn);
+    if (d_in % 16 != 0 || ldx % 16 != 0 || (((uintptr_t)X) & 15) != 0)
+      return fpi::fail(FP_ESHAPE, "%s: needs d_in %% 16 == 0 and 16-byte aligned X rows (d_in=%d, ldx=%lld)", fn, d_in,
+                       (long long)ldx);
+    if ((((uintptr_t)Wp) & 15) != 0) return fpi::fail(FP_EARG, "%s: packed W not 16-byte aligned", fn);
+  }
+  a = WitArgs{};
+  a.X = X; a.ldx = ldx; a.W = Wp; a.ldw = 0;
+  a.T = T; a.N = d_out; a.K = d_in; a.s = s;
+  packed_dims(d_out, d_in, a.wp_rb, a.wp_kb);
+  vec_flags(a);
+  a.vecW = 1;
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t fp_witness_packed_weights_bytes(int32_t d_out, int32_t d_in) {
+  int32_t nrb, nkb;
+  if (!packed_dims(d_out, d_in, nrb, nkb)) return 0;
+  return (size_t)nrb * 32 * (size_t)nkb * WP_BK;
+}
+
+extern "C" int fp_witness_pack_weights(const int8_t* W, int64_t ldw, int32_t d_out, int32_t d_in, int8_t* Wp,
+                                       hipStream_t stream) {
+  const char* fn = "fp_witness_pack_weights";
+  int32_t nrb, nkb;
+  if (!packed_dims(d_out, d_in, nrb, nkb)) return fpi::fail(FP_EARG, "%s: negative size", fn);
+  if (d_in > FP_MAX_DIN) return fpi::fail(FP_ESHAPE, "%s: d_in=%d > %d", fn, d_in, FP_MAX_DIN);
+  if (ldw < d_in) return fpi::fail(FP_ESHAPE, "%s: ldw < d_in", fn);
+  const int64_t units = (int64_t)nrb * nkb * (WP_BK / 32) * 64;
+  if (units == 0) return fpi::ok();
+  if (!Wp || (d_out > 0 && d_in > 0 && !W)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if ((((uintptr_t)Wp) & 15) != 0) return fpi::fail(FP_EARG, "%s: Wp not 16-byte aligned", fn);
+  const int vec = ((ldw & 15) == 0) && ((((uintptr_t)W) & 15) == 0);
+  const int64_t want = (units + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(256), 0, stream, W, ldw, d_out, d_in, nrb, nkb, vec, Wp);
+  int rc = fpi::check_launch("pack_weights_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_witness_linear_packed(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
+                                        int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R,
+                                        hipStream_t stream) {
+  WitArgs a;
+  int rc = packed_args("fp_witness_linear_packed", X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
+  if (rc) return rc;
+  if (T == 0 || d_out == 0) return fpi::ok();
+  a.Z = Z; a.Y = Y; a.R = R;
+  vec_flags(a);
+  rc = launch_ws<WIT_WS>(a, nullptr, 0, stream);
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T,
+                                                      int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
+                                                      int8_t* R, int32_t n_pairs, const fp_elem* const* A,
+                                                      const fp_elem* const* B, const fp_elem* rho, int32_t n,
+                                                      const fp_elem* r, fp_elem* rounds, fp_elem* finals,
+                                                      fp_elem* claim0, hipStream_t stream) {
+  const char* fn = "fp_witness_linear_packed_with_sumcheck";
+  WitArgs a;
+  int rc = packed_args(fn, X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
+  if (rc) return rc;
+  sct::TailArgs ta;
+  rc = tail_args(fn, n_pairs, A, B, rho, n, r, rounds, finals, claim0, WsCfg<WIT_WS>::NT, ta);
+  if (rc) return rc;
+  a.Z = Z; a.Y = Y; a.R = R;
+  vec_flags(a);
+  rc = launch_ws<WIT_WS>(a, &ta, 1, stream);
+  return rc ? rc : fpi::ok();
+}

@@ -5,7 +5,8 @@ rescaled output and the remainder (§3.1), and sum-check reduces the matmul
 claim about Z to claims about the committed activations and the weights. One
 ``run()`` of a layer prover performs, on one stream and in protocol order:
 
-  witness  Z = X W^T, Y, R                     (fp_witness_linear[_grouped])
+  witness  Z = X W^T, Y, R                     (fp_witness_linear_packed from weights packed once by
+                                               fp_witness_pack_weights; fp_witness_linear[_grouped])
   eq       E_t = eq(r_t, .), E_o = eq(r_o, .)  (fp_eq_table_batched)
   folds    x' = X~(. || r_t), w' = W~(. || r_o) (fp_fold_claim_batched: the
   claim    c0 = Z~(r_o || r_t)                   folds and the claims in one pass)
@@ -25,7 +26,8 @@ import torch
 from . import (combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext, ext_claim_combine,
                fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows, linear_combine, merkle_commit,
                moe_plan, rs_encode, sumcheck_ext_fs, sumcheck_prove, sumcheck_prove_multi, to_field_tensor,
-               field_numpy, witness_linear, witness_linear_grouped, witness_linear_with_sumcheck)
+               field_numpy, pack_weights, witness_linear, witness_linear_grouped, witness_linear_packed,
+               witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck)
 
 
 def _nomark(name):
@@ -42,6 +44,19 @@ def _i8(a: np.ndarray, dev) -> torch.Tensor:
 
 def _f(n, dev):
     return torch.empty(n, dtype=torch.int64, device=dev)
+
+
+def _packed(W: torch.Tensor):
+    """The weights packed for the matrix cores (fp_witness_pack_weights, once per layer) when the
+    packed witness applies to them (d_in % 16 == 0), else None."""
+    return pack_weights(W) if W.shape[1] % 16 == 0 else None
+
+
+def _witness(X, W, Wp, s, Z, Y, R):
+    if Wp is not None:
+        witness_linear_packed(X, Wp, s, Z, Y, R)
+    else:
+        witness_linear(X, W, s, Z, Y, R)
 
 
 class _Prover:
@@ -130,6 +145,7 @@ class SingleLayerProver(_Prover):
         self.pipelined = pipelined
         self.s = s
         self.X, self.W = _i8(X, dev), _i8(W, dev)
+        self.Wp = _packed(self.W)
         T, d_in = X.shape
         d_out = W.shape[0]
         self.n = log2ceil(d_in)
@@ -153,8 +169,14 @@ class SingleLayerProver(_Prover):
                        claim0=self.claim0)
 
     def _witness_and_previous_sumcheck(self):
-        witness_linear_with_sumcheck(self.X, self.W, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
-                                     self.ch["rounds"], rounds=self.rounds, finals=self.finals, claim0=self.claim0)
+        if self.Wp is not None:
+            witness_linear_packed_with_sumcheck(self.X, self.Wp, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
+                                                self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                                                claim0=self.claim0)
+        else:
+            witness_linear_with_sumcheck(self.X, self.W, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
+                                         self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                                         claim0=self.claim0)
 
     def drain(self):
         """Pipelined mode: the sum-check of the last proof."""
@@ -169,7 +191,7 @@ class SingleLayerProver(_Prover):
         eq = ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o]))
         if self.pipelined:
             return [("witness+sumcheck", self._witness_and_previous_sumcheck), eq, fold]
-        return [("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)), eq, fold,
+        return [("witness", lambda: _witness(self.X, self.W, self.Wp, self.s, self.Z, self.Y, self.R)), eq, fold,
                 ("sumcheck", self._sumcheck)]
 
     def results(self) -> dict:
@@ -229,6 +251,7 @@ class MultiMatmulProver(_Prover):
                          finals=torch.empty((1, 2), dtype=torch.int64, device=dev), claim0=_f(1, dev))
             self.mm.append(d)
         self.x_jobs = [(self.tens[x], None, 1 << n, buf) for (x, n), buf in xf.items()]
+        self.packed = {m.w: _packed(self.tens[m.w]) for m in cfg.matmuls}
         if self.mode == "rlc_out":
             self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
             self.rlc = _f(1, dev)
@@ -242,7 +265,7 @@ class MultiMatmulProver(_Prover):
     def _witness(self):
         for d in self.mm:
             m = d["m"]
-            witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
+            _witness(self.tens[m.x], self.tens[m.w], self.packed[m.w], self.s, d["Z"], d["Y"], d["R"])
 
     def _eq(self):
         eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
@@ -437,6 +460,7 @@ class FaithfulLayerProver(_Prover):
         dev = dev or torch.device("cuda")
         self.s = s
         self.X, self.W = _i8(X, dev), _i8(W, dev)
+        self.Wp = _packed(self.W)
         T, d_in = X.shape
         d_out = W.shape[0]
         self.T, self.d_in, self.d_out = T, d_in, d_out
@@ -494,7 +518,7 @@ class FaithfulLayerProver(_Prover):
                         finals=self.finals)
 
     def phases(self):
-        return [("witness", lambda: witness_linear(self.X, self.W, self.s, self.Z, self.Y, self.R)),
+        return [("witness", lambda: _witness(self.X, self.W, self.Wp, self.s, self.Z, self.Y, self.R)),
                 ("commit", self._commit), ("transcript", self._challenges), ("eq", self._eq),
                 ("fold+claim", self._fold_claim), ("sumcheck", self._sumcheck)]
 
