@@ -75,10 +75,12 @@ def kernel_work(cfg, name: str, prover) -> tuple:
     if name == "sumcheck":
         n = cfg.batched_n if cfg.kind == "batched" else None
         return sum(16 * (1 << (n if n else m.n)) for m in mms), 0
+    if name == "eq":  # the tables written (the challenges read are negligible)
+        return 8 * ((1 << cfg.n_t) + sum(1 << m.n_o for m in mms)), 0
     return 0, 0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "witness_sc_T512_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_T512_witness_traffic.txt")
 
 
 def measured_traffic(cfg, kernel_phase: str):
@@ -86,7 +88,7 @@ def measured_traffic(cfg, kernel_phase: str):
     summary, or None when there is none for this workload and launch or its
     kernel sources changed since the counters were taken."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE) or kernel_phase != "witness+sumcheck":
+    if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
@@ -94,7 +96,7 @@ def measured_traffic(cfg, kernel_phase: str):
             continue
         k, v = line.split(":", 1)
         kv[k.strip()] = v.strip()
-    if int(kv.get("workload", -1)) != cfg.cid:
+    if int(kv.get("workload", -1)) != cfg.cid or kv.get("phase") != kernel_phase:
         return None
     h = hashlib.sha256()
     for src in kv["sources"].split():
@@ -617,8 +619,9 @@ def main():
     packed = None
     if getattr(prover, "Wp", None) is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fp.pack_weights(prover.W, out=prover.Wp)
         e0.record(stream)
-        fp.pack_weights(prover.W)
+        fp.pack_weights(prover.W, out=prover.Wp)
         e1.record(stream)
         torch.cuda.synchronize()
         packed = {"ms": round(e0.elapsed_time(e1), 4), "bytes": prover.Wp.data.numel(),
@@ -642,7 +645,7 @@ def main():
         extras[k] = {"ms": round(v, 5), "GB/s": round(bb / (v * 1e-3) / 1e9, 1) if bb else None,
                      "TOPS": round(oo / (v * 1e-3) / 1e12, 1) if oo else None}
     wb, wops = kernel_work(cfg, "witness", prover)
-    wkey = "witness+sumcheck" if pipelined else "witness"
+    wkey = next(k for k in phase_ms if k.startswith("witness"))
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5),

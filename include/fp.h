@@ -93,37 +93,6 @@ int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int8_t* const*
                               const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out, int32_t s,
                               int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
 
-/* Packed weights: the weights of one layer laid out once in the order the
- * int8 matrix cores read them, for the fp_witness_linear_packed* calls (the
- * weights of a layer are fixed, so one packing serves every proof of it).
- * Fragment (b, c, q) is 1 KiB at byte ((b * nkb + c) * 2 + q) * 1024, nkb =
- * ceil(d_in / 64); its lane l (16 bytes at l * 16) holds
- * W[32 b + l % 32][64 c + 32 (l / 32) + 16 q + 0..15], zero past d_out and
- * d_in. Wp (device, 16-byte aligned) holds
- * fp_witness_packed_weights_bytes(d_out, d_in) =
- * ceil(d_out / 32) * 32 * nkb * 64 bytes; W is int8 [d_out, d_in] (ldw). */
-size_t fp_witness_packed_weights_bytes(int32_t d_out, int32_t d_in);
-int fp_witness_pack_weights(const int8_t* W, int64_t ldw, int32_t d_out, int32_t d_in, int8_t* Wp,
-                            hipStream_t stream);
-
-/* fp_witness_linear with the weights given packed (Wp from
- * fp_witness_pack_weights for this d_out, d_in): the same Z, Y, R. Each wave
- * streams its weight fragments straight into registers and only X passes
- * through LDS. Requires d_in % 16 == 0, ldx % 16 == 0 and X 16-byte aligned
- * (FP_ESHAPE otherwise). */
-int fp_witness_linear_packed(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
-                             int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
-
-/* fp_witness_linear_with_sumcheck with packed weights: the witness of
- * fp_witness_linear_packed and, in the same launch, the sum-check of another
- * claim (VP * 2^n <= 4096; the conditions of both calls apply). */
-int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T,
-                                           int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
-                                           int8_t* R, int32_t n_pairs, const fp_elem* const* A,
-                                           const fp_elem* const* B, const fp_elem* rho, int32_t n,
-                                           const fp_elem* r, fp_elem* rounds, fp_elem* finals, fp_elem* claim0,
-                                           hipStream_t stream);
-
 /* ----------------------------------------------------------- grouping --- */
 /* MoE grouping plan, host only (no device work). route (host, T entries in
  * [0, n_experts)) gives each token's expert. Writes counts[e] (host,
@@ -156,6 +125,44 @@ typedef struct {
  * returns 0). */
 int fp_eq_table_batched(int32_t count, const fp_eq_desc* descs, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t fp_eq_table_batched_workspace(int32_t count);
+
+/* ------------------------------------------------------ packed witness --- */
+/* Packed weights: the weights of one layer laid out once in the order the
+ * int8 matrix cores read them, for the fp_witness_linear_packed* calls (the
+ * weights of a layer are fixed, so one packing serves every proof of it).
+ * Fragment (b, c, q) is 1 KiB at byte ((b * nkb + c) * 2 + q) * 1024, nkb =
+ * ceil(d_in / 64); its lane l (16 bytes at l * 16) holds
+ * W[32 b + l % 32][64 c + 32 (l / 32) + 16 q + 0..15], zero past d_out and
+ * d_in. Wp (device, 16-byte aligned) holds
+ * fp_witness_packed_weights_bytes(d_out, d_in) =
+ * ceil(d_out / 32) * 32 * nkb * 64 bytes; W is int8 [d_out, d_in] (ldw). */
+size_t fp_witness_packed_weights_bytes(int32_t d_out, int32_t d_in);
+int fp_witness_pack_weights(const int8_t* W, int64_t ldw, int32_t d_out, int32_t d_in, int8_t* Wp,
+                            hipStream_t stream);
+
+/* fp_witness_linear with the weights given packed (Wp from
+ * fp_witness_pack_weights for this d_out, d_in): the same Z, Y, R. Each wave
+ * streams its weight fragments straight into registers and only X passes
+ * through LDS. Requires d_in % 16 == 0, ldx % 16 == 0 and X 16-byte aligned
+ * (FP_ESHAPE otherwise). The same launch also writes the n_eq eq tables
+ * eq[0 .. n_eq) (exactly fp_eq_table_batched(n_eq, eq)) in workgroups beside
+ * the GEMM: a proof's eq tables depend only on its challenges, so they are
+ * built while its witness runs. n_eq in [0, 8]; the tables must not overlap
+ * X, Wp or the outputs. */
+int fp_witness_linear_packed(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
+                             int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq,
+                             const fp_eq_desc* eq, hipStream_t stream);
+
+/* fp_witness_linear_with_sumcheck with packed weights: the witness and eq
+ * tables of fp_witness_linear_packed and, in the same launch, the sum-check of
+ * another claim (VP * 2^n <= 4096; the conditions of both calls apply; the
+ * eq tables must not overlap the sum-check's tables either). */
+int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T,
+                                           int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
+                                           int8_t* R, int32_t n_pairs, const fp_elem* const* A,
+                                           const fp_elem* const* B, const fp_elem* rho, int32_t n,
+                                           const fp_elem* r, fp_elem* rounds, fp_elem* finals, fp_elem* claim0,
+                                           int32_t n_eq, const fp_eq_desc* eq, hipStream_t stream);
 
 /* --------------------------------------------------------------- folds --- */
 /* Folded row of an integer matrix ("How fast can FlashProve go", §2: the

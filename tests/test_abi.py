@@ -69,13 +69,21 @@ def test_argument_errors_without_gpu():
     assert L.fp_witness_packed_weights_bytes(14336, 4096) == 14336 * 4096
     assert L.fp_witness_packed_weights_bytes(-1, 4) == 0
     assert L.fp_witness_pack_weights(dummy, 8, 4, 16, dummy, None) == 2
-    assert L.fp_witness_linear_packed(dummy, 40, dummy, 4, 40, 4, 8, None, dummy, dummy, None) == 2
+    assert L.fp_witness_linear_packed(dummy, 40, dummy, 4, 40, 4, 8, None, dummy, dummy, 0, None, None) == 2
     assert b"d_in % 16" in L.fp_last_error()
-    assert L.fp_witness_linear_packed(ctypes.c_void_p(24), 48, dummy, 4, 48, 4, 8, None, dummy, dummy, None) == 2
-    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 0, None, dummy, dummy, None) == 3
+    assert L.fp_witness_linear_packed(ctypes.c_void_p(24), 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 0, None,
+                                      None) == 2
+    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 0, None, dummy, dummy, 0, None, None) == 3
     assert L.fp_witness_linear_packed_with_sumcheck(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 1, pa, pa, None,
-                                                    13, dummy, dummy, dummy, None, None) == 2
+                                                    13, dummy, dummy, dummy, None, 0, None, None) == 2
     assert b"exceed one" in L.fp_last_error()
+    # eq tables built beside the packed witness: at most 8, each n in [0, 30] with non-null pointers
+    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 9, dummy, None) == 1
+    eqd = (fp._EqDesc * 2)(fp._EqDesc(16, 3, 16), fp._EqDesc(16, 31, 16))
+    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 2, eqd, None) == 2
+    assert b"n=31" in L.fp_last_error()
+    eqd = (fp._EqDesc * 1)(fp._EqDesc(None, 3, 16))
+    assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 1, eqd, None) == 1
     # multi-request fold: Mt's leading dim must be a multiple of 16, R bounded, workspace checked
     assert L.fp_fold_weights_prepare(dummy, 64, 100, 64, dummy, 104, dummy, None) == 2
     assert L.fp_fold_matrix_multi(dummy, 112, dummy, 100, 64, 5000, dummy, 100, dummy, 64, 64, dummy, 0, None) == 2

@@ -385,6 +385,26 @@ def test_witness_packed_extremes_strided_and_no_z(fp):
     assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
 
 
+@pytest.mark.parametrize("T,d_out", [(200, 260), (0, 64)])
+def test_witness_packed_with_eq_tables(fp, T, d_out):
+    """eq tables built by spare workgroups of the packed witness launch (one per 256 x 2^min(n - 8, 6) entries)
+    equal the oracle's, and the witness beside them is unchanged; with no tokens only the tables are built."""
+    rng = _rng(31 + T)
+    d_in = 320
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    ns = [0, 1, 8, 9, 14, 15, 20, 3]
+    rs = [_field(rng, n, specials=(n >= 4)) for n in ns]
+    rt = [fp.to_field_tensor(r) if len(r) else torch.empty(0, dtype=torch.int64, device="cuda") for r in rs]
+    Es = [torch.empty(1 << n, dtype=torch.int64, device="cuda") for n in ns]
+    Z, Y, R = fp.witness_linear_packed(_dev(X), fp.pack_weights(_dev(W)), 8, eq=list(zip(rt, Es)))
+    torch.cuda.synchronize()
+    for r, E in zip(rs, Es):
+        assert np.array_equal(fp.field_numpy(E), O.eq_table(r))
+    wz, wy, wr = O.witness(X, W, 8)
+    assert np.array_equal(Z.cpu().numpy(), wz)
+    assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+
+
 @pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 320, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
                                              (0, 64, 64, 2, 10), (40, 96, 0, 1, 5)])
 def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):
@@ -398,11 +418,14 @@ def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):
     Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda")
     Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
     R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    re = _field(rng, 11, specials=True)
+    E = torch.empty(1 << 11, dtype=torch.int64, device="cuda")
     _, (rounds, finals, c0) = fp.witness_linear_packed_with_sumcheck(
         _dev(X), fp.pack_weights(_dev(W)), 8, Z, Y, R, [fp.to_field_tensor(a) for a in As],
         [fp.to_field_tensor(b) for b in Bs], fp.to_field_tensor(r),
-        rho=None if rho is None else fp.to_field_tensor(rho))
+        rho=None if rho is None else fp.to_field_tensor(rho), eq=[(fp.to_field_tensor(re), E)])
     torch.cuda.synchronize()
+    assert np.array_equal(fp.field_numpy(E), O.eq_table(re))
     if T and d_out:
         wz, wy, wr = O.witness(X, W, 8)
         assert np.array_equal(Z.cpu().numpy(), wz)

@@ -109,9 +109,10 @@ def lib():
             "fp_sumcheck_ext_fs": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
             "fp_witness_packed_weights_bytes": (sz, [i32, i32]),
             "fp_witness_pack_weights": (ctypes.c_int, [vp, i64, i32, i32, vp, vp]),
-            "fp_witness_linear_packed": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "fp_witness_linear_packed": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]),
             "fp_witness_linear_packed_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp,
-                                                                      i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+                                                                      i32, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                                                      vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -228,18 +229,30 @@ class PackedWeights:
         self.data, self.d_out, self.d_in = data, d_out, d_in
 
 
-def pack_weights(W) -> PackedWeights:
+def pack_weights(W, out: PackedWeights | None = None) -> PackedWeights:
     d_out, d_in = W.shape
     assert W.dtype == torch.int8 and (W.numel() == 0 or W.stride(1) == 1), "rows must be contiguous"
     nbytes = lib().fp_witness_packed_weights_bytes(d_out, d_in)
-    Wp = torch.empty(max(nbytes, 16), dtype=torch.int8, device=W.device)
+    if out is not None:
+        assert (out.d_out, out.d_in) == (d_out, d_in) and out.data.numel() >= nbytes
+        Wp = out.data
+    else:
+        Wp = torch.empty(max(nbytes, 16), dtype=torch.int8, device=W.device)
     _check(lib().fp_witness_pack_weights(_ptr(W), _ld(W), d_out, d_in, _ptr(Wp), _stream()),
            "fp_witness_pack_weights")
     return PackedWeights(Wp, d_out, d_in)
 
 
-def witness_linear_packed(X, Wp: PackedWeights, s: int, Z=None, Y=None, R=None, with_z: bool = True):
-    """witness_linear(X, W, s) with W given packed (pack_weights(W))."""
+def _eq_descs(eq):
+    """fp_eq_desc array of (r, E) pairs (None: no tables)."""
+    eq = list(eq or [])
+    return len(eq), (_EqDesc * max(len(eq), 1))(*[_EqDesc(r.data_ptr() if r.numel() else None, r.numel(),
+                                                          E.data_ptr()) for r, E in eq])
+
+
+def witness_linear_packed(X, Wp: PackedWeights, s: int, Z=None, Y=None, R=None, with_z: bool = True, eq=None):
+    """witness_linear(X, W, s) with W given packed (pack_weights(W)); eq: (r, E) pairs of eq tables
+    written by the same launch (eq_table_batched of them)."""
     T, d_in = X.shape
     assert X.dtype == torch.int8 and d_in == Wp.d_in
     assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
@@ -248,15 +261,16 @@ def witness_linear_packed(X, Wp: PackedWeights, s: int, Z=None, Y=None, R=None, 
         Z = torch.empty((T, d_out), dtype=torch.int32, device=X.device)
     Y = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if Y is None else Y
     R = torch.empty((T, d_out), dtype=torch.int8, device=X.device) if R is None else R
+    ne, descs = _eq_descs(eq)
     _check(lib().fp_witness_linear_packed(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, d_out, s,
-                                          _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), _stream()),
+                                          _ptr(Z) if with_z else None, _ptr(Y), _ptr(R), ne, descs, _stream()),
            "fp_witness_linear_packed")
     return Z, Y, R
 
 
 def witness_linear_packed_with_sumcheck(X, Wp: PackedWeights, s: int, Z, Y, R, As, Bs, r, rho=None, rounds=None,
-                                        finals=None, claim0=None):
-    """witness_linear_packed(X, Wp, s, Z, Y, R) and sumcheck_prove(As, Bs, r, rho, ...) in one launch."""
+                                        finals=None, claim0=None, eq=None):
+    """witness_linear_packed(X, Wp, s, Z, Y, R, eq=eq) and sumcheck_prove(As, Bs, r, rho, ...) in one launch."""
     T, d_in = X.shape
     assert X.dtype == torch.int8 and d_in == Wp.d_in
     assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
@@ -270,7 +284,8 @@ def witness_linear_packed_with_sumcheck(X, Wp: PackedWeights, s: int, Z, Y, R, A
     pb = (ctypes.c_void_p * k)(*[b.data_ptr() for b in Bs])
     _check(lib().fp_witness_linear_packed_with_sumcheck(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, Wp.d_out, s,
                                                         _ptr(Z), _ptr(Y), _ptr(R), k, pa, pb, _ptr(rho), n, _ptr(r),
-                                                        _ptr(rounds), _ptr(finals), _ptr(claim0), _stream()),
+                                                        _ptr(rounds), _ptr(finals), _ptr(claim0), *_eq_descs(eq),
+                                                        _stream()),
            "fp_witness_linear_packed_with_sumcheck")
     return (Z, Y, R), (rounds, finals, claim0)
 

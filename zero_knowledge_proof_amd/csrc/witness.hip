@@ -29,6 +29,7 @@
 #include <utility>
 
 #include "common.hpp"
+#include "eq.hpp"
 #include "sc_tail.hpp"
 
 namespace {
@@ -541,41 +542,68 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
 // fragments two K blocks ahead, X two blocks ahead; two workgroups per CU.
 #define WIT_WS 4, 2, 2, 2, 2, 4
 
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_kernel(WitArgs a) {
-  __shared__ __align__(16) int8_t lds[WsCfg<NW, TM, TN, PFW, PFX, UNR>::LDS_BYTES];
-  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, blockIdx.x, gridDim.x, lds);
+// eq tables built by spare workgroups of a witness launch (a proof's eq
+// tables depend on its challenges only, so they can be made while its GEMM
+// runs): table i takes aux workgroups [block_start[i], block_start[i+1]),
+// each writing 2^(8 + eq_aux_mid(n)) entries.
+constexpr int WIT_MAX_EQ = 8;
+struct EqAux {
+  const fp_elem* r[WIT_MAX_EQ];
+  fp_elem* E[WIT_MAX_EQ];
+  int32_t n[WIT_MAX_EQ];
+  int32_t block_start[WIT_MAX_EQ + 1];
+  int32_t count;
+};
+__host__ __device__ inline int eq_aux_mid(int n) {
+  return n <= 8 ? 0 : (n - 8 < eqk::EQ_MAX_MID ? n - 8 : eqk::EQ_MAX_MID);
+}
+inline int64_t eq_aux_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8 - eq_aux_mid(n)); }
+
+// Aux workgroup b of the launch's eq tables.
+__device__ __forceinline__ void eq_aux_block(const EqAux& eq, int b) {
+  int k = 0;
+#pragma unroll 1
+  for (int q = 1; q < eq.count; ++q)
+    if (eq.block_start[q] <= b) k = q;
+  eqk::eq_block(eq.r[k], eq.n[k], eq.E[k], b - eq.block_start[k], eq_aux_mid(eq.n[k]));
 }
 
-// With sum-check tails in workgroups [0, n_tail), as witness_sc_kernel.
+// Workgroups [0, n_tail): sum-check tails (as witness_sc_kernel); the next
+// eq.block_start[eq.count]: eq tables; the rest: GEMM tiles.
 template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_sc_kernel(
-    WitArgs a, sct::TailArgs ta, int n_tail) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_kernel(
+    WitArgs a, sct::TailArgs ta, int n_tail, EqAux eq) {
   constexpr int NT = NW * 64;
+  static_assert(NT == 256, "the eq blocks and the tail are written for 256 threads");
   constexpr int GEMM_LDS = WsCfg<NW, TM, TN, PFW, PFX, UNR>::LDS_BYTES;
   constexpr int BYTES = GEMM_LDS > (int)sizeof(sct::TailLds<NT>) ? GEMM_LDS : (int)sizeof(sct::TailLds<NT>);
   __shared__ __align__(16) int8_t lds[BYTES];
-  if ((int)blockIdx.x < n_tail) {
-    sct::tail_body<NT>(ta, blockIdx.x, *reinterpret_cast<sct::TailLds<NT>*>(lds));
+  int b = blockIdx.x;
+  if (b < n_tail) {
+    sct::tail_body<NT>(ta, b, *reinterpret_cast<sct::TailLds<NT>*>(lds));
     return;
   }
-  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, blockIdx.x - n_tail, gridDim.x - n_tail, lds);
+  b -= n_tail;
+  const int n_eq = eq.block_start[eq.count];
+  if (b < n_eq) {
+    eq_aux_block(eq, b);
+    return;
+  }
+  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, b - n_eq, gridDim.x - n_tail - n_eq, lds);
 }
 
 template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
-int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, hipStream_t st) {
+int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, hipStream_t st) {
   using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
   a.tiles_t = (a.T + C::BT - 1) / C::BT;
   a.tiles_o = (a.N + C::BO - 1) / C::BO;
   const int64_t tiles = (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o : 0;
-  if (tiles + n_tail > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
-  if (tiles + n_tail == 0) return FP_OK;
-  if (ta) {
-    hipLaunchKernelGGL((witness_ws_sc_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)(tiles + n_tail)),
-                       dim3(C::NT), 0, st, a, *ta, n_tail);
-    return fpi::check_launch("witness_ws_sc_kernel");
-  }
-  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  const int64_t total = tiles + n_tail + eq.block_start[eq.count];
+  if (total > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
+  if (total == 0) return FP_OK;
+  sct::TailArgs none{};
+  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)total), dim3(C::NT), 0, st, a,
+                     ta ? *ta : none, n_tail, eq);
   return fpi::check_launch("witness_ws_kernel");
 }
 
@@ -810,6 +838,28 @@ bool packed_dims(int32_t d_out, int32_t d_in, int32_t& nrb, int32_t& nkb) {
   return true;
 }
 
+// The eq tables a packed witness launch builds beside its GEMM.
+int eq_aux(const char* fn, int32_t n_eq, const fp_eq_desc* eq, EqAux& aux) {
+  aux = EqAux{};
+  if (n_eq < 0 || n_eq > WIT_MAX_EQ) return fpi::fail(FP_EARG, "%s: n_eq=%d outside [0, %d]", fn, n_eq, WIT_MAX_EQ);
+  if (n_eq > 0 && !eq) return fpi::fail(FP_EARG, "%s: null eq descs", fn);
+  int64_t blocks = 0;
+  for (int32_t i = 0; i < n_eq; ++i) {
+    if (eq[i].n < 0 || eq[i].n > FP_MAX_N)
+      return fpi::fail(FP_ESHAPE, "%s: eq table %d has n=%d outside [0, %d]", fn, i, eq[i].n, FP_MAX_N);
+    if (!eq[i].E || (eq[i].n > 0 && !eq[i].r)) return fpi::fail(FP_EARG, "%s: eq table %d has a null pointer", fn, i);
+    aux.r[i] = eq[i].r;
+    aux.E[i] = eq[i].E;
+    aux.n[i] = eq[i].n;
+    aux.block_start[i] = (int32_t)blocks;
+    blocks += eq_aux_blocks(eq[i].n);
+    if (blocks > (1 << 24)) return fpi::fail(FP_ESHAPE, "%s: eq tables too large for one launch", fn);
+  }
+  aux.block_start[n_eq] = (int32_t)blocks;
+  aux.count = n_eq;
+  return FP_OK;
+}
+
 // Shared checks of the packed-weight witness entry points.
 int packed_args(const char* fn, const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
                 int32_t d_out, int32_t s, const int8_t* Y, const int8_t* R, WitArgs& a) {
@@ -859,15 +909,18 @@ extern "C" int fp_witness_pack_weights(const int8_t* W, int64_t ldw, int32_t d_o
 }
 
 extern "C" int fp_witness_linear_packed(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in,
-                                        int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R,
-                                        hipStream_t stream) {
+                                        int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq,
+                                        const fp_eq_desc* eq, hipStream_t stream) {
+  const char* fn = "fp_witness_linear_packed";
   WitArgs a;
-  int rc = packed_args("fp_witness_linear_packed", X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
+  int rc = packed_args(fn, X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
   if (rc) return rc;
-  if (T == 0 || d_out == 0) return fpi::ok();
+  EqAux aux;
+  rc = eq_aux(fn, n_eq, eq, aux);
+  if (rc) return rc;
   a.Z = Z; a.Y = Y; a.R = R;
   vec_flags(a);
-  rc = launch_ws<WIT_WS>(a, nullptr, 0, stream);
+  rc = launch_ws<WIT_WS>(a, nullptr, 0, aux, stream);
   return rc ? rc : fpi::ok();
 }
 
@@ -876,7 +929,8 @@ extern "C" int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t l
                                                       int8_t* R, int32_t n_pairs, const fp_elem* const* A,
                                                       const fp_elem* const* B, const fp_elem* rho, int32_t n,
                                                       const fp_elem* r, fp_elem* rounds, fp_elem* finals,
-                                                      fp_elem* claim0, hipStream_t stream) {
+                                                      fp_elem* claim0, int32_t n_eq, const fp_eq_desc* eq,
+                                                      hipStream_t stream) {
   const char* fn = "fp_witness_linear_packed_with_sumcheck";
   WitArgs a;
   int rc = packed_args(fn, X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
@@ -884,8 +938,11 @@ extern "C" int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t l
   sct::TailArgs ta;
   rc = tail_args(fn, n_pairs, A, B, rho, n, r, rounds, finals, claim0, WsCfg<WIT_WS>::NT, ta);
   if (rc) return rc;
+  EqAux aux;
+  rc = eq_aux(fn, n_eq, eq, aux);
+  if (rc) return rc;
   a.Z = Z; a.Y = Y; a.R = R;
   vec_flags(a);
-  rc = launch_ws<WIT_WS>(a, &ta, 1, stream);
+  rc = launch_ws<WIT_WS>(a, &ta, 1, aux, stream);
   return rc ? rc : fpi::ok();
 }

@@ -131,11 +131,14 @@ OVERLAP_ENTRIES = 4096
 class SingleLayerProver(_Prover):
     """One linear map: witness, claim and sum-check over d_in.
 
+    With packed weights (d_in % 16 == 0) the witness launch also builds the
+    proof's eq tables (they depend on its challenges only).
+
     pipelined: for a stream of proofs of the layer. ``run()`` then launches the
     witness of this proof together with the sum-check of the previous one
-    (fp_witness_linear_with_sumcheck), followed by this proof's eq tables,
-    folds and claim; ``drain()`` runs the sum-check of the last proof. The
-    outputs of a proof are complete after the next ``run()`` or ``drain()``."""
+    (fp_witness_linear[_packed]_with_sumcheck), followed by this proof's folds
+    and claim; ``drain()`` runs the sum-check of the last proof. The outputs
+    of a proof are complete after the next ``run()`` or ``drain()``."""
 
     OUTPUTS = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0")
 
@@ -168,11 +171,15 @@ class SingleLayerProver(_Prover):
         sumcheck_prove([self.xf], [self.wf], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
                        claim0=self.claim0)
 
+    def _eq_pairs(self):
+        return [(self.ch["r_t"], self.E_t), (self.ch["r_o"], self.E_o)]
+
     def _witness_and_previous_sumcheck(self):
         if self.Wp is not None:
+            # this proof's eq tables are built by the same launch
             witness_linear_packed_with_sumcheck(self.X, self.Wp, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
                                                 self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                                                claim0=self.claim0)
+                                                claim0=self.claim0, eq=self._eq_pairs())
         else:
             witness_linear_with_sumcheck(self.X, self.W, self.s, self.Z, self.Y, self.R, [self.xf], [self.wf],
                                          self.ch["rounds"], rounds=self.rounds, finals=self.finals,
@@ -189,6 +196,13 @@ class SingleLayerProver(_Prover):
                                                           (self.W, self.E_o, 1 << n, self.wf)],
                                                          [(self.Z, self.E_t, self.E_o, self.c0)]))
         eq = ("eq", lambda: eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [self.E_t, self.E_o]))
+        if self.Wp is not None:
+            # packed weights: the witness launch also builds the eq tables
+            if self.pipelined:
+                return [("witness+eq+sumcheck", self._witness_and_previous_sumcheck), fold]
+            return [("witness+eq", lambda: witness_linear_packed(self.X, self.Wp, self.s, self.Z, self.Y, self.R,
+                                                                 eq=self._eq_pairs())), fold,
+                    ("sumcheck", self._sumcheck)]
         if self.pipelined:
             return [("witness+sumcheck", self._witness_and_previous_sumcheck), eq, fold]
         return [("witness", lambda: _witness(self.X, self.W, self.Wp, self.s, self.Z, self.Y, self.R)), eq, fold,
@@ -262,10 +276,23 @@ class MultiMatmulProver(_Prover):
             self.finals = torch.empty((len(cfg.matmuls), 2), dtype=torch.int64, device=dev)
             self.claim0 = _f(1, dev)
 
-    def _witness(self):
+    def _eq_pairs(self):
+        return [(self.ch["r_t"], self.E_t)] + [(self.ch["r_o/" + d["m"].name], d["E_o"]) for d in self.mm]
+
+    def _fuse_eq(self) -> bool:
+        # the first packed witness launch can build all eq tables (at most 8 per launch)
+        return any(v is not None for v in self.packed.values()) and len(self.mm) + 1 <= 8
+
+    def _witness(self, with_eq: bool = False):
+        eq = self._eq_pairs() if with_eq else None
         for d in self.mm:
             m = d["m"]
-            _witness(self.tens[m.x], self.tens[m.w], self.packed[m.w], self.s, d["Z"], d["Y"], d["R"])
+            Wp = self.packed[m.w]
+            if Wp is not None:
+                witness_linear_packed(self.tens[m.x], Wp, self.s, d["Z"], d["Y"], d["R"], eq=eq)
+                eq = None
+            else:
+                witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
 
     def _eq(self):
         eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
@@ -291,8 +318,12 @@ class MultiMatmulProver(_Prover):
                        [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
 
     def phases(self):
-        ph = [("witness", self._witness), ("eq", self._eq), ("fold+claim", self._fold_claim),
-              ("sumcheck", self._sumcheck)]
+        if self._fuse_eq():
+            ph = [("witness+eq", lambda: self._witness(with_eq=True)), ("fold+claim", self._fold_claim),
+                  ("sumcheck", self._sumcheck)]
+        else:
+            ph = [("witness", self._witness), ("eq", self._eq), ("fold+claim", self._fold_claim),
+                  ("sumcheck", self._sumcheck)]
         if self.mode == "rlc_out":
             ph.append(("merge", self._merge))
         return ph
