@@ -136,6 +136,37 @@ def test_fold_claim_batched(fp):
     assert [int(fp.field_numpy(o)[0]) for o in co] == cwant
 
 
+def test_fold_wide_and_many_jobs(fp):
+    """Calls of different shapes on one workspace: 65536-column folds of several chunks, more jobs than one
+    launch carries, and a claim beside them, all equal to the oracle."""
+    rng = _rng(77)
+    def fold_case(rows, cols, cp):
+        M = _i8(rng, (rows, cols))
+        E = _field(rng, rows)
+        return (_dev(M), fp.to_field_tensor(E), cp, torch.empty(cp, dtype=torch.int64, device="cuda")), \
+            O.fold_rows(M, E, cp)
+    big = [fold_case(3000, 65536, 65536), fold_case(2000, 60000, 65536)]  # 256 + 235 strips of 2-3 chunks
+    small = [fold_case(900, 700, 1024) for _ in range(40)]               # > 32 jobs: several launches
+    # 17 folds of one 1025 x 65536 matrix (2 chunks, 256 strips each)
+    Mw = _i8(rng, (1025, 65536))
+    Mw_d = _dev(Mw)
+    wide = []
+    for _ in range(17):
+        E = _field(rng, 1025)
+        wide.append(((Mw_d, fp.to_field_tensor(E), 65536, torch.empty(65536, dtype=torch.int64, device="cuda")),
+                     O.fold_rows(Mw, E, 65536)))
+    M = rng.integers(-2**31, 2**31, size=(700, 3000), dtype=np.int64).astype(np.int32)
+    rr, rc = _field(rng, 10, False), _field(rng, 12, False)
+    claim = (_dev(M), fp.to_field_tensor(O.eq_table(rr)), fp.to_field_tensor(O.eq_table(rc)),
+             torch.empty(1, dtype=torch.int64, device="cuda"))
+    for jobs in (big, small, wide, big + small[:5]):
+        fo, co = fp.fold_claim_batched([j for j, _ in jobs], [claim])
+        torch.cuda.synchronize()
+        for o, (_, w) in zip(fo, jobs):
+            assert np.array_equal(fp.field_numpy(o), w)
+        assert int(fp.field_numpy(co[0])[0]) == O.mle_matrix(M, rr, rc)
+
+
 # ------------------------------------------------------------------ MLE ---
 @pytest.mark.parametrize("rows,cols", [(1, 1), (5, 6), (16, 256), (100, 300), (513, 1030)])
 @pytest.mark.parametrize("dt", [np.int8, np.int32])

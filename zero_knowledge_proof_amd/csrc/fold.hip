@@ -376,8 +376,10 @@ Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool claim) 
   p.n_strips = (cols + FCOLS - 1) / FCOLS;
   const int pad_total = (cols_pad + FCOLS - 1) / FCOLS;
   p.n_pad_strips = claim ? 0 : (pad_total - p.n_strips);
-  // about two workgroups per compute unit, chunks in whole pairs of batches
-  const int target_blocks = 512;
+  // about one workgroup per compute unit (measured against 128-1536 on the
+  // up-projection: fewer chunks also shorten the cross-chunk sums), chunks in
+  // whole pairs of batches
+  const int target_blocks = 256;
   const int q = eb == 1 ? kRowQuantum<1> : kRowQuantum<4>;
   const int want_chunks = (target_blocks + p.n_strips - 1) / p.n_strips;
   int64_t cr = (rows + want_chunks - 1) / want_chunks;
