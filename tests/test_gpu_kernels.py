@@ -372,7 +372,8 @@ def test_pack_weights(fp, d_out, d_in):
 
 
 PACK_SHAPES = [(1, 16, 1, 8), (5, 48, 7, 7), (33, 64, 129, 8), (130, 304, 300, 1), (200, 1008, 260, 8),
-               (257, 128, 513, 4), (64, 4096, 256, 8), (300, 80, 70, 3), (4, 0, 9, 8)]
+               (257, 128, 513, 4), (64, 4096, 256, 8), (300, 80, 70, 3), (4, 0, 9, 8),
+               (1000, 208, 6100, 8), (1030, 64, 6144, 5)]  # the last two: 256x128 tiles (>= 192 of them)
 
 
 @pytest.mark.parametrize("T,d_in,d_out,s", PACK_SHAPES)
@@ -437,7 +438,7 @@ def test_witness_packed_with_eq_tables(fp, T, d_out):
 
 
 @pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 320, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
-                                             (0, 64, 64, 2, 10), (40, 96, 0, 1, 5)])
+                                             (0, 64, 64, 2, 10), (40, 96, 0, 1, 5), (1000, 96, 6100, 2, 11)])
 def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):
     """One launch: a packed-weight witness and an unrelated sum-check, each against the oracle."""
     rng = _rng(900 + T + n + k)
