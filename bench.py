@@ -525,6 +525,9 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="prove steps one after another instead of overlapping each step's sum-check with the "
                          "next step's witness GEMM")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="keep two proofs in flight instead of three (the folds of the previous proof then run after "
+                         "the witness instead of beside it)")
     ap.add_argument("--no-faithful", action="store_true",
                     help="skip the soundness-faithful proof (commitment, Fiat-Shamir, extension-field challenges)")
     ap.add_argument("--no-lookup", action="store_true",
@@ -546,7 +549,7 @@ def main():
 
     import synth
     import zero_knowledge_proof_amd as fp
-    from zero_knowledge_proof_amd.prover import can_pipeline, make_prover
+    from zero_knowledge_proof_amd.prover import can_overlap, can_pipeline, make_prover
 
     fp.require_gpu()
     dev = torch.device("cuda", 0)
@@ -563,7 +566,8 @@ def main():
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
     pipelined = (not args.no_pipeline) and can_pipeline(cfg)
-    prover = make_prover(cfg, inp, ch, dev, pipelined=pipelined)
+    overlapped = pipelined and (not args.no_overlap) and can_overlap(cfg)
+    prover = make_prover(cfg, inp, ch, dev, pipelined=pipelined, overlapped=overlapped)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -654,7 +658,8 @@ def main():
         "vs_baseline": None, "dtype": "int8->int32 witness; u64 Goldilocks field", "data": "synthetic",
         "config": {"workload": WORKLOADS[cfg.cid], "T": cfg.T, "seed": cfg.seed, "s": cfg.s,
                    "matmuls": [[m.name, m.d_in, m.d_out] for m in cfg.matmuls] if cfg.matmuls else None,
-                   "pipelined": pipelined, "steps_per_graph": per_graph},
+                   "pipelined": pipelined, "proofs_in_flight": 3 if overlapped else (2 if pipelined else 1),
+                   "steps_per_graph": per_graph},
         "roofline": roof,
         "fold_claim_GBps": extras.get("fold+claim", {}).get("GB/s"),
         "witness_int8_TOPS": extras.get(wkey, {}).get("TOPS"),

@@ -67,3 +67,30 @@ def test_pipelined_graph_replays(fp, cid, shape):
         _same(prover.results(), want, "replay%d" % rep)
         prover.run()              # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cid,shape,steps", [(1, {}, 2), (2, dict(T=100, d_in=1008, d_out=700), 3)])
+def test_overlapped_graph_replays(fp, cid, shape, steps):
+    """Three proofs in flight recorded as a graph (two streams inside it): replays followed by the drain give the
+    eager outputs, with every buffer cleared between replays and eager steps in between."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
+    prover.run()
+    prover.run()
+    prover.drain()
+    torch.cuda.synchronize()
+    want = prover.results()
+    prover.capture(steps=steps)
+    for rep in range(3):
+        for t in prover.output_tensors():
+            t.zero_()
+        torch.cuda.synchronize()
+        prover.replay()
+        prover.replay()
+        prover.drain()
+        torch.cuda.synchronize()
+        _same(prover.results(), want, "replay%d" % rep)
+        prover.run()              # eager work between replays
+        torch.cuda.synchronize()

@@ -111,6 +111,25 @@ def test_layer_pipelined(fp, cid, shape):
     assert got["c0"] == got["claim0"]
 
 
+@pytest.mark.parametrize("cid,shape,runs", [(1, {}, 1), (1, {}, 4), (2, dict(T=100, d_in=1008, d_out=700), 3)])
+def test_layer_overlapped(fp, cid, shape, runs):
+    """Three proofs in flight (each step: this proof's witness and eq tables with the sum-check of the proof two
+    back, and the previous proof's folds and claim on a second stream): after the runs and the drain every output
+    is the oracle's."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg, inp.get("route"))
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
+    for _ in range(runs):
+        prover.run()
+    prover.drain()
+    torch.cuda.synchronize()
+    got = prover.results()
+    want = O.prove_config(cfg, inp, ch)["main" if cid == 1 else "up"]
+    _cmp_matmul(got, want)
+    assert got["c0"] == got["claim0"]
+
+
 # ------------------------------------------------------- full-size checks --
 def _sampled_witness(X, W, got, s, n=2048, seed=0):
     rng = np.random.default_rng(seed)
@@ -158,6 +177,22 @@ def test_full_cfg2_pipelined(fp):
     ch = synth.draw_challenges(cfg)
     prover = make_prover(cfg, inp, ch, pipelined=True)
     prover.capture(steps=3)
+    prover.replay()
+    prover.drain()
+    torch.cuda.synchronize()
+    got = prover.results()
+    _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
+
+
+def test_full_cfg2_overlapped(fp):
+    """The benchmark's launch configuration with three proofs in flight: four proofs per graph replay, the folds
+    of each beside the next proof's witness, the last two finished by the drain."""
+    cfg = synth.config(2)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg)
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
+    prover.capture(steps=4)
+    prover.replay()
     prover.replay()
     prover.drain()
     torch.cuda.synchronize()

@@ -216,6 +216,101 @@ class SingleLayerProver(_Prover):
                 "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
 
 
+class OverlappedLayerProver(SingleLayerProver):
+    """Single-layer proofs three deep, for a stream of proofs of one layer with
+    packed weights: step k runs proof k's witness and eq tables together with
+    proof k-2's sum-check (one launch, fp_witness_linear_packed_with_sumcheck)
+    on the caller's stream while proof k-1's folds and claim run on a second
+    stream beside it. Proof k-1's folds read only its own witness and eq tables
+    (finished in step k-1), and proof k-2's sum-check reads only its own folds
+    (finished in step k-1), so each proof still follows the protocol order;
+    the buffers of consecutive proofs alternate between two sets. ``drain()``
+    finishes the last two proofs; outputs are those of the last proof."""
+
+    PER_PROOF = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0")
+
+    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None):
+        super().__init__(X, W, s, ch, dev, pipelined=True)
+        if self.Wp is None:
+            raise ValueError("overlapped proofs need packed weights (d_in % 16 == 0)")
+        first = {k: getattr(self, k) for k in self.PER_PROOF}
+        second = {k: (torch.zeros_like(v) if k in ("xf", "wf") else torch.empty_like(v)) for k, v in first.items()}
+        self.bufs = [first, second]
+        self.k = 0
+        self.side = torch.cuda.Stream(device=self.X.device)
+
+    def _fold(self, b):
+        n = self.n
+        fold_claim_batched([(self.X, b["E_t"], 1 << n, b["xf"]), (self.W, b["E_o"], 1 << n, b["wf"])],
+                           [(b["Z"], b["E_t"], b["E_o"], b["c0"])])
+
+    def _sumcheck_of(self, b):
+        sumcheck_prove([b["xf"]], [b["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                       claim0=self.claim0)
+
+    def run(self, mark=_nomark):
+        main, side = torch.cuda.current_stream(), self.side
+        cur, prev = self.bufs[self.k % 2], self.bufs[(self.k + 1) % 2]
+        side.wait_stream(main)  # proof k-1's witness and eq tables are done
+        main.wait_stream(side)  # proof k-2's folds (cur xf, wf) are done
+        if self.k > 0:
+            with torch.cuda.stream(side):
+                mark("fold+claim")
+                self._fold(prev)
+        mark("witness+eq+sumcheck")
+        witness_linear_packed_with_sumcheck(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"], [cur["xf"]],
+                                            [cur["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                                            claim0=self.claim0,
+                                            eq=[(self.ch["r_t"], cur["E_t"]), (self.ch["r_o"], cur["E_o"])])
+        mark("end")
+        self.k += 1
+
+    def capture(self, steps: int = 1):
+        self.run()
+        torch.cuda.current_stream().wait_stream(self.side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                self.run()
+            torch.cuda.current_stream().wait_stream(self.side)
+        torch.cuda.synchronize()
+        self.graph = g
+        self.graph_steps = steps
+        self.k_graph = self.k
+        return g
+
+    def replay(self):
+        """The captured steps again (with their buffers); drain() then finishes
+        the replay's last two proofs."""
+        self.graph.replay()
+        self.k = self.k_graph
+
+    def drain(self):
+        """The sum-check of the next-to-last proof, then the folds, claim and
+        sum-check of the last one."""
+        torch.cuda.current_stream().wait_stream(self.side)
+        last = self.k - 1
+        if last < 0:
+            return
+        cur, prev = self.bufs[last % 2], self.bufs[(last + 1) % 2]
+        if last >= 1:
+            self._sumcheck_of(prev)
+        self._fold(cur)
+        self._sumcheck_of(cur)
+
+    def output_tensors(self):
+        return [t for b in self.bufs for t in b.values()] + [self.rounds, self.finals, self.claim0]
+
+    def results(self) -> dict:
+        b = self.bufs[(self.k - 1) % 2]
+        return {"Z": b["Z"].cpu().numpy(), "Y": b["Y"].cpu().numpy(), "R": b["R"].cpu().numpy(),
+                "E_t": field_numpy(b["E_t"]), "E_o": field_numpy(b["E_o"]),
+                "x_fold": field_numpy(b["xf"]), "w_fold": field_numpy(b["wf"]),
+                "c0": int(field_numpy(b["c0"])[0]), "rounds": field_numpy(self.rounds),
+                "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
+
+
 class MultiMatmulProver(_Prover):
     """Several linear maps of one layer sharing the token axis (one r_t).
 
@@ -568,9 +663,18 @@ def can_pipeline(cfg) -> bool:
     return cfg.kind == "single" and (1 << cfg.matmuls[0].n) <= OVERLAP_ENTRIES
 
 
-def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False):
+def can_overlap(cfg) -> bool:
+    """Whether three proofs can be in flight (pipelined, and the packed witness applies)."""
+    return can_pipeline(cfg) and cfg.matmuls[0].d_in % 16 == 0
+
+
+def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, overlapped: bool = False):
+    """overlapped: three proofs in flight (OverlappedLayerProver), for single
+    layers with packed weights; pipelined: two (SingleLayerProver)."""
     if cfg.kind == "single":
         m = cfg.matmuls[0]
+        if overlapped:
+            return OverlappedLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev)
         return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, pipelined=pipelined)
     if pipelined:
         raise ValueError("pipelined proofs are implemented for single-matmul layers")
