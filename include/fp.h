@@ -30,8 +30,10 @@
  * row-major with an explicit leading dimension in elements. Calls only enqueue
  * work on `stream` and return; none synchronizes or allocates device memory.
  * Scratch space comes from a caller workspace sized by the matching
- * *_workspace() query (its contents need no initialization). Calls that
- * overlap in time must not share a workspace. Arguments are validated before any launch; a failing
+ * *_workspace() query (its contents need no initialization, except the
+ * FP_FOLD_COUNTER_BYTES of arrival counters at the start of a fp_layer_step
+ * workspace: zero them once when the workspace is created; every call leaves
+ * them zero). Calls that overlap in time must not share a workspace. Arguments are validated before any launch; a failing
  * call returns a nonzero FP_E* code, launches nothing, and sets a thread-local
  * message readable with fp_last_error(). Faults inside kernels surface at the
  * caller's next stream synchronization. The library keeps no state between
@@ -68,6 +70,7 @@ enum {
 #define FP_MAX_FOLD_ROWS (1 << 30)    /* rows of a multi-request fold's matrix */
 #define FP_MAX_RS_LOGN 23             /* Reed-Solomon rows of up to 2^23 elements (codewords 2^24) */
 #define FP_MAX_MERKLE_ROWS (1 << 20)  /* rows hashed into one Merkle leaf */
+#define FP_FOLD_COUNTER_BYTES 16384   /* arrival counters at the start of a fp_layer_step workspace */
 
 /* Thread-local message of the last failing call ("" after success). */
 const char* fp_last_error(void);
@@ -373,6 +376,33 @@ int fp_fold_claim_batched(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* 
                           int32_t n_claim, const fp_claim_desc* claims, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t fp_fold_claim_batched_workspace(fp_dtype fold_dt, int32_t n_fold, const fp_fold_desc* folds, fp_dtype claim_dt,
                                        int32_t n_claim, const fp_claim_desc* claims);
+
+/* ----------------------------------------------------------- layer step --- */
+/* One step of a stream of proofs of one layer, in ONE launch: the witness and
+ * eq tables of proof k (exactly fp_witness_linear_packed(X, ldx, Wp, T, d_in,
+ * d_out, s, Z, Y, R, n_eq, eq)), the folds and claims of proof k-1 (exactly
+ * fp_fold_claim_batched(FP_I8, n_fold, folds, FP_I32, n_claim, claims)) and
+ * the sum-check of proof k-2 (exactly fp_sumcheck_prove(n_pairs, A, B, rho,
+ * n, r, rounds, finals, claim0); n_pairs = 0: none). The three share no data
+ * ("How fast can FlashProve go", §2: the witness of every layer, then the
+ * folds and each matmul's sum-check), so their workgroups run side by side:
+ * the GEMM on most compute units, the folds' workgroups beside it, the
+ * sum-check's chain of rounds on one. The folds' cross-chunk sums are done by
+ * the last workgroup of each column strip (or claim) to finish, through
+ * arrival counters at the start of ws: ws is fp_layer_step_workspace(n_fold,
+ * folds, n_claim, claims) bytes, 256-byte aligned, and its first
+ * FP_FOLD_COUNTER_BYTES must be zero on entry (every call leaves them zero).
+ * At most 4 folds and claims, each with rows and columns (FP_ESHAPE
+ * otherwise); the conditions of the three calls apply (VP * 2^n <= 4096).
+ * Inputs of one part must not be written by another part of the same call. */
+int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in, int32_t d_out, int32_t s,
+                  int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq, const fp_eq_desc* eq, int32_t n_fold,
+                  const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims,
+                  void* ws, size_t ws_bytes, int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B,
+                  const fp_elem* rho, int32_t n, const fp_elem* r, fp_elem* rounds, fp_elem* finals,
+                  fp_elem* claim0, hipStream_t stream);
+size_t fp_layer_step_workspace(int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
+                               const fp_claim_desc* claims);
 
 /* ----------------------------------------------------------- sum-check --- */
 /* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of

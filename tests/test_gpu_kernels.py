@@ -437,6 +437,60 @@ def test_witness_packed_with_eq_tables(fp, T, d_out):
     assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
 
 
+@pytest.mark.parametrize("T,d_in,d_out,k", [(100, 320, 700, 1), (1000, 96, 6100, 2), (16, 64, 48, 0)])
+def test_layer_step(fp, T, d_in, d_out, k):
+    """One launch with a witness and its eq tables, the folds and claim of an unrelated proof and the sum-check of
+    a third: each part equals the oracle's; the arrival counters are zero again after every call."""
+    rng = _rng(1200 + T + k)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    # another proof's tables: int8 folds of two matrices and an int32 claim, several chunks each
+    X2, W2 = _i8(rng, (700, 300)), _i8(rng, (3000, 260))
+    Z2 = rng.integers(-2**31, 2**31, size=(700, 3000), dtype=np.int64).astype(np.int32)
+    E1, E2 = _field(rng, 700), _field(rng, 3000)
+    rr, rc = _field(rng, 10, False), _field(rng, 12, False)
+    n = 9
+    As = [_field(rng, 1 << n, False) for _ in range(k)]
+    Bs = [_field(rng, 1 << n, False) for _ in range(k)]
+    r = _field(rng, n)
+    rho = _field(rng, k, False) if k > 1 else None
+    re_t, re_o = _field(rng, 10), _field(rng, 13)
+    Et = torch.empty(1 << 10, dtype=torch.int64, device="cuda")
+    Eo = torch.empty(1 << 13, dtype=torch.int64, device="cuda")
+    Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda")
+    Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    xo = torch.empty(512, dtype=torch.int64, device="cuda")
+    wo = torch.empty(512, dtype=torch.int64, device="cuda")
+    co = torch.empty(1, dtype=torch.int64, device="cuda")
+    rounds = torch.empty((n, 3), dtype=torch.int64, device="cuda")
+    finals = torch.empty((max(k, 1), 2), dtype=torch.int64, device="cuda")
+    c0 = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws = fp.StepWorkspace()
+    for rep in range(2):
+        fp.layer_step(_dev(X), fp.pack_weights(_dev(W)), 8, Z, Y, R,
+                      eq=[(fp.to_field_tensor(re_t), Et), (fp.to_field_tensor(re_o), Eo)],
+                      folds=[(_dev(X2), fp.to_field_tensor(E1), 512, xo), (_dev(W2), fp.to_field_tensor(E2), 512, wo)],
+                      claims=[(_dev(Z2), fp.to_field_tensor(O.eq_table(rr)), fp.to_field_tensor(O.eq_table(rc)), co)],
+                      As=[fp.to_field_tensor(a) for a in As], Bs=[fp.to_field_tensor(b) for b in Bs],
+                      r=fp.to_field_tensor(r), rho=None if rho is None else fp.to_field_tensor(rho),
+                      rounds=rounds, finals=finals, claim0=c0, ws=ws)
+        torch.cuda.synchronize()
+        wz, wy, wr = O.witness(X, W, 8)
+        assert np.array_equal(Z.cpu().numpy(), wz)
+        assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+        assert np.array_equal(fp.field_numpy(Et), O.eq_table(re_t))
+        assert np.array_equal(fp.field_numpy(Eo), O.eq_table(re_o))
+        assert np.array_equal(fp.field_numpy(xo), O.fold_rows(X2, E1, 512))
+        assert np.array_equal(fp.field_numpy(wo), O.fold_rows(W2, E2, 512))
+        assert int(fp.field_numpy(co)[0]) == O.mle_matrix(Z2, rr, rc)
+        if k:
+            grs, gfs, gc = O.sumcheck(As, Bs, r, rho=rho)
+            assert np.array_equal(fp.field_numpy(rounds), grs)
+            assert np.array_equal(fp.field_numpy(finals), gfs)
+            assert int(fp.field_numpy(c0)[0]) == gc
+        assert int(ws.buf[:16384].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 320, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
                                              (0, 64, 64, 2, 10), (40, 96, 0, 1, 5), (1000, 96, 6100, 2, 11)])
 def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):

@@ -31,6 +31,7 @@ EXPORTS = [
     "fp_lookup_prove", "fp_lookup_prove_workspace", "fp_fs_init", "fp_fs_absorb", "fp_fs_challenges",
     "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
     "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
+    "fp_layer_step", "fp_layer_step_workspace",
 ]
 
 _lib = None
@@ -113,6 +114,9 @@ def lib():
             "fp_witness_linear_packed_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp,
                                                                       i32, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                                                       vp]),
+            "fp_layer_step": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, i32, vp,
+                                             vp, sz, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_layer_step_workspace": (sz, [i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -288,6 +292,49 @@ def witness_linear_packed_with_sumcheck(X, Wp: PackedWeights, s: int, Z, Y, R, A
                                                         _stream()),
            "fp_witness_linear_packed_with_sumcheck")
     return (Z, Y, R), (rounds, finals, claim0)
+
+
+class StepWorkspace:
+    """Workspace of fp_layer_step: arrival counters (zeroed once, here) and the
+    folds' partial values."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=_dev())
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_ws_step = StepWorkspace()
+
+
+def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=(), As=(), Bs=(), r=None, rho=None,
+               rounds=None, finals=None, claim0=None, ws: StepWorkspace | None = None):
+    """One launch: the witness and eq tables of a proof (as witness_linear_packed), the int8 folds
+    (M, E, cols_pad, out) and int32 claims (M, E_rows, E_cols, out) of another (as fold_claim_batched), and
+    the sum-check of a third (as sumcheck_prove over As, Bs, r; none when As is empty)."""
+    T, d_in = X.shape
+    assert X.dtype == torch.int8 and d_in == Wp.d_in
+    assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
+    ne, eqd = _eq_descs(eq)
+    nf, nc = len(folds), len(claims)
+    fd = (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
+                                              out.data_ptr()) for (M, E, cp, out) in folds])
+    cd = (_ClaimDesc * max(nc, 1))(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
+                                                Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in claims])
+    ws = _ws_step if ws is None else ws
+    p, nb = ws.get(lib().fp_layer_step_workspace(nf, fd, nc, cd))
+    k = len(As)
+    pa = (ctypes.c_void_p * max(k, 1))(*[a.data_ptr() for a in As])
+    pb = (ctypes.c_void_p * max(k, 1))(*[b.data_ptr() for b in Bs])
+    n = r.numel() if r is not None else 0
+    _check(lib().fp_layer_step(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, Wp.d_out, s, _ptr(Z), _ptr(Y), _ptr(R),
+                               ne, eqd, nf, fd, nc, cd, p, nb, k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds),
+                               _ptr(finals), _ptr(claim0), _stream()), "fp_layer_step")
 
 
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):

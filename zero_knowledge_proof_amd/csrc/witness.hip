@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "eq.hpp"
+#include "fold.hpp"
 #include "sc_tail.hpp"
 
 namespace {
@@ -610,6 +611,73 @@ int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, h
   return fpi::check_launch("witness_ws_kernel");
 }
 
+// ---- one step of a stream of layer proofs in one launch ------------------
+// Proof k's witness GEMM and eq tables, proof k-1's folds and claim and proof
+// k-2's sum-check: the three touch different data, so one launch runs them
+// side by side. Workgroups: [0, n_tail) sum-check tail, then the eq tables,
+// then the GEMM tiles, then the fold and claim workgroups in arrival mode (the
+// last workgroup of each strip or claim adds the chunks), whose work hides
+// under the GEMM's on the compute units it leaves free.
+constexpr int STEP_MAX_FOLD = 4;
+struct FoldAux {
+  foldk::FoldJob j[STEP_MAX_FOLD];
+  uint32_t* ctrs;
+  int32_t count;
+  int32_t blocks;
+};
+
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void layer_step_kernel(
+    WitArgs a, sct::TailArgs ta, int n_tail, EqAux eq, FoldAux fa) {
+  constexpr int NT = NW * 64;
+  static_assert(NT == foldk::FT, "the fold, eq and tail workgroups are written for 256 threads");
+  constexpr int GEMM_LDS = WsCfg<NW, TM, TN, PFW, PFX, UNR>::LDS_BYTES;
+  constexpr int FOLD_LDS = foldk::LDS_WORDS * 4 + foldk::MAXG_ALL * 8 + 16;
+  constexpr int TAIL_LDS = (int)sizeof(sct::TailLds<NT>);
+  constexpr int B1 = GEMM_LDS > TAIL_LDS ? GEMM_LDS : TAIL_LDS;
+  constexpr int BYTES = B1 > FOLD_LDS ? B1 : FOLD_LDS;
+  __shared__ __align__(16) int8_t lds[BYTES];
+  int b = blockIdx.x;
+  if (b < n_tail) {
+    sct::tail_body<NT>(ta, b, *reinterpret_cast<sct::TailLds<NT>*>(lds));
+    return;
+  }
+  b -= n_tail;
+  const int n_eq = eq.block_start[eq.count];
+  if (b < n_eq) {
+    eq_aux_block(eq, b);
+    return;
+  }
+  b -= n_eq;
+  const int tiles = (int)gridDim.x - n_tail - n_eq - fa.blocks;
+  if (b < tiles) {
+    witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, b, tiles, lds);
+    return;
+  }
+  b -= tiles;
+  const foldk::FoldJob& job = fa.j[foldk::find_job(fa.j, fa.count, b)];
+  uint32_t* fl = reinterpret_cast<uint32_t*>(lds);
+  uint64_t* gsum = reinterpret_cast<uint64_t*>(lds + foldk::LDS_WORDS * 4);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(gsum + foldk::MAXG_ALL);
+  foldk::fold_block_arrive(job, b - job.block_start, fa.ctrs, fl, gsum, flag);
+}
+
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+int launch_step(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, const FoldAux& fa,
+                hipStream_t st) {
+  using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
+  a.tiles_t = (a.T + C::BT - 1) / C::BT;
+  a.tiles_o = (a.N + C::BO - 1) / C::BO;
+  const int64_t tiles = (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o : 0;
+  const int64_t total = tiles + n_tail + eq.block_start[eq.count] + fa.blocks;
+  if (total > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "layer step: too many workgroups");
+  if (total == 0) return FP_OK;
+  sct::TailArgs none{};
+  hipLaunchKernelGGL((layer_step_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)total), dim3(C::NT), 0, st, a,
+                     ta ? *ta : none, n_tail, eq, fa);
+  return fpi::check_launch("layer_step_kernel");
+}
+
 // Tile configurations (BO, BT, WO, WT, grouped, prefetch distance, K step),
 // chosen from measurements on the up-projection and layer shapes:
 //   XL: 256x256 outputs x tokens, 8 waves of 64x128, K step 64
@@ -957,5 +1025,109 @@ extern "C" int fp_witness_linear_packed_with_sumcheck(const int8_t* X, int64_t l
   a.Z = Z; a.Y = Y; a.R = R;
   vec_flags(a);
   rc = launch_ws_auto(a, &ta, 1, aux, stream);
+  return rc ? rc : fpi::ok();
+}
+
+// ---- one step of a stream of layer proofs ----------------------------------
+namespace {
+
+// Plans the folds (int8) and claims (int32) of the step's fold workgroups:
+// workspace = arrival counters, then every job's partial values.
+int step_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
+               const fp_claim_desc* claims, void* ws, size_t ws_bytes, bool plan_only, size_t* need, FoldAux& fa) {
+  fa = FoldAux{};
+  if (n_fold < 0 || n_claim < 0 || n_fold + n_claim > STEP_MAX_FOLD)
+    return fpi::fail(FP_EARG, "%s: %d folds and %d claims (at most %d in all)", fn, n_fold, n_claim, STEP_MAX_FOLD);
+  if ((n_fold > 0 && !folds) || (n_claim > 0 && !claims)) return fpi::fail(FP_EARG, "%s: null descs", fn);
+  size_t off = FP_FOLD_COUNTER_BYTES;
+  int64_t blocks = 0;
+  int32_t nctr = 0;
+  for (int32_t i = 0; i < n_fold + n_claim; ++i) {
+    const bool claim = i >= n_fold;
+    foldk::FoldJob j{};
+    if (!claim) {
+      const fp_fold_desc& d = folds[i];
+      if (d.rows < 0 || d.cols < 0 || d.cols_pad < d.cols || d.ld < d.cols)
+        return fpi::fail(FP_ESHAPE, "%s: fold %d has bad sizes", fn, i);
+      if ((d.cols_pad > 0 && !d.out) || (d.rows > 0 && d.cols > 0 && (!d.M || !d.E)))
+        return fpi::fail(FP_EARG, "%s: fold %d has a null pointer", fn, i);
+      j.M = d.M; j.ld = d.ld; j.E = d.E; j.Ecol = nullptr; j.out = d.out;
+      j.rows = d.rows; j.cols = d.cols; j.cols_pad = d.cols_pad; j.eb = 1;
+    } else {
+      const fp_claim_desc& d = claims[i - n_fold];
+      if (d.rows < 0 || d.cols < 0 || d.ld < d.cols) return fpi::fail(FP_ESHAPE, "%s: claim %d has bad sizes", fn, i);
+      if (!d.out || (d.rows > 0 && d.cols > 0 && (!d.M || !d.E_rows || !d.E_cols)))
+        return fpi::fail(FP_EARG, "%s: claim %d has a null pointer", fn, i);
+      j.M = d.M; j.ld = d.ld; j.E = d.E_rows; j.Ecol = d.E_cols; j.out = d.out;
+      j.rows = d.rows; j.cols = d.cols; j.cols_pad = d.cols; j.eb = 4;
+    }
+    if (j.rows == 0 || j.cols == 0)
+      return fpi::fail(FP_ESHAPE, "%s: job %d is empty (the step's folds and claims need rows and columns)", fn, i);
+    const int64_t span = (int64_t)j.ld * j.eb * (j.rows < foldk::FMAX_CHUNK ? j.rows : foldk::FMAX_CHUNK);
+    if (span > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: job %d spans more than 2^31 bytes per chunk", fn, i);
+    const foldk::Plan p = foldk::plan_job(j.rows, j.cols, j.cols_pad, j.eb, claim, true);
+    const uintptr_t align = j.eb == 1 ? 3 : 15;
+    j.vec = (j.cols % 4 == 0) && (j.ld % 4 == 0) && (((uintptr_t)j.M & align) == 0);
+    j.chunk_rows = p.chunk_rows;
+    j.n_chunks = p.n_chunks;
+    j.n_strips = p.n_strips;
+    j.n_pad_strips = p.n_pad_strips;
+    j.part = p.part_bytes ? (fp_elem*)((char*)ws + off) : nullptr;
+    off += p.part_bytes;
+    j.block_start = (int32_t)blocks;
+    j.ctr = nctr;
+    blocks += p.blocks;
+    nctr += p.ctrs;
+    fa.j[fa.count++] = j;
+  }
+  if (nctr > (int32_t)(FP_FOLD_COUNTER_BYTES / 4) || blocks > (1 << 24))
+    return fpi::fail(FP_ESHAPE, "%s: folds too large for one step", fn);
+  fa.blocks = (int32_t)blocks;
+  fa.ctrs = (uint32_t*)ws;
+  *need = (n_fold + n_claim) ? off : 0;
+  if (plan_only) return FP_OK;
+  if (*need && (!ws || ws_bytes < *need)) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, *need);
+  if (*need && (((uintptr_t)ws) & 255)) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t fp_layer_step_workspace(int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
+                                          const fp_claim_desc* claims) {
+  FoldAux fa;
+  size_t need = 0;
+  if (step_folds("fp_layer_step_workspace", n_fold, folds, n_claim, claims, nullptr, 0, true, &need, fa)) return 0;
+  return need;
+}
+
+extern "C" int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in, int32_t d_out,
+                             int32_t s, int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq, const fp_eq_desc* eq,
+                             int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims,
+                             void* ws, size_t ws_bytes, int32_t n_pairs, const fp_elem* const* A,
+                             const fp_elem* const* B, const fp_elem* rho, int32_t n, const fp_elem* r,
+                             fp_elem* rounds, fp_elem* finals, fp_elem* claim0, hipStream_t stream) {
+  const char* fn = "fp_layer_step";
+  WitArgs a;
+  int rc = packed_args(fn, X, ldx, Wp, T, d_in, d_out, s, Y, R, a);
+  if (rc) return rc;
+  EqAux aux;
+  rc = eq_aux(fn, n_eq, eq, aux);
+  if (rc) return rc;
+  FoldAux fa;
+  size_t need = 0;
+  rc = step_folds(fn, n_fold, folds, n_claim, claims, ws, ws_bytes, false, &need, fa);
+  if (rc) return rc;
+  sct::TailArgs ta;
+  const bool tail = n_pairs > 0;
+  if (tail) {
+    rc = tail_args(fn, n_pairs, A, B, rho, n, r, rounds, finals, claim0, 256, ta);
+    if (rc) return rc;
+  }
+  a.Z = Z; a.Y = Y; a.R = R;
+  vec_flags(a);
+  const int64_t large_tiles = (int64_t)((a.N + 255) / 256) * ((a.T + 127) / 128);
+  if (large_tiles >= 192) rc = launch_step<WIT_WS_L>(a, tail ? &ta : nullptr, tail ? 1 : 0, aux, fa, stream);
+  else rc = launch_step<WIT_WS>(a, tail ? &ta : nullptr, tail ? 1 : 0, aux, fa, stream);
   return rc ? rc : fpi::ok();
 }

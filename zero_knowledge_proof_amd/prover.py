@@ -23,11 +23,11 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext, ext_claim_combine,
-               fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows, linear_combine, merkle_commit,
-               moe_plan, rs_encode, sumcheck_ext_fs, sumcheck_prove, sumcheck_prove_multi, to_field_tensor,
-               field_numpy, pack_weights, witness_linear, witness_linear_grouped, witness_linear_packed,
-               witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck)
+from . import (StepWorkspace, combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
+               ext_claim_combine, field_numpy, fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows,
+               layer_step, linear_combine, merkle_commit, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs,
+               sumcheck_prove, sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped,
+               witness_linear_packed, witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck)
 
 
 def _nomark(name):
@@ -218,12 +218,11 @@ class SingleLayerProver(_Prover):
 
 class OverlappedLayerProver(SingleLayerProver):
     """Single-layer proofs three deep, for a stream of proofs of one layer with
-    packed weights: step k runs proof k's witness and eq tables together with
-    proof k-2's sum-check (one launch, fp_witness_linear_packed_with_sumcheck)
-    on the caller's stream while proof k-1's folds and claim run on a second
-    stream beside it. Proof k-1's folds read only its own witness and eq tables
-    (finished in step k-1), and proof k-2's sum-check reads only its own folds
-    (finished in step k-1), so each proof still follows the protocol order;
+    packed weights: step k is ONE launch (fp_layer_step) that runs proof k's
+    witness and eq tables, proof k-1's folds and claim and proof k-2's
+    sum-check side by side. Proof k-1's folds read only its own witness and eq
+    tables (finished by the previous launch), and proof k-2's sum-check only
+    its own folds (likewise), so each proof still follows the protocol order;
     the buffers of consecutive proofs alternate between two sets. ``drain()``
     finishes the last two proofs; outputs are those of the last proof."""
 
@@ -237,43 +236,40 @@ class OverlappedLayerProver(SingleLayerProver):
         second = {k: (torch.zeros_like(v) if k in ("xf", "wf") else torch.empty_like(v)) for k, v in first.items()}
         self.bufs = [first, second]
         self.k = 0
-        self.side = torch.cuda.Stream(device=self.X.device)
+        self.ws = StepWorkspace()
 
-    def _fold(self, b):
+    def _jobs(self, b):
         n = self.n
-        fold_claim_batched([(self.X, b["E_t"], 1 << n, b["xf"]), (self.W, b["E_o"], 1 << n, b["wf"])],
-                           [(b["Z"], b["E_t"], b["E_o"], b["c0"])])
+        return ([(self.X, b["E_t"], 1 << n, b["xf"]), (self.W, b["E_o"], 1 << n, b["wf"])],
+                [(b["Z"], b["E_t"], b["E_o"], b["c0"])])
 
-    def _sumcheck_of(self, b):
-        sumcheck_prove([b["xf"]], [b["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                       claim0=self.claim0)
+    def _step(self, cur, prev, fold: bool, tail: bool):
+        folds, claims = self._jobs(prev) if fold else ((), ())
+        layer_step(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"],
+                   eq=[(self.ch["r_t"], cur["E_t"]), (self.ch["r_o"], cur["E_o"])], folds=folds, claims=claims,
+                   As=[cur["xf"]] if tail else (), Bs=[cur["wf"]] if tail else (), r=self.ch["rounds"],
+                   rounds=self.rounds, finals=self.finals, claim0=self.claim0, ws=self.ws)
 
     def run(self, mark=_nomark):
-        main, side = torch.cuda.current_stream(), self.side
-        cur, prev = self.bufs[self.k % 2], self.bufs[(self.k + 1) % 2]
-        side.wait_stream(main)  # proof k-1's witness and eq tables are done
-        main.wait_stream(side)  # proof k-2's folds (cur xf, wf) are done
-        if self.k > 0:
-            with torch.cuda.stream(side):
-                mark("fold+claim")
-                self._fold(prev)
-        mark("witness+eq+sumcheck")
-        witness_linear_packed_with_sumcheck(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"], [cur["xf"]],
-                                            [cur["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                                            claim0=self.claim0,
-                                            eq=[(self.ch["r_t"], cur["E_t"]), (self.ch["r_o"], cur["E_o"])])
+        mark("step")
+        # proof k into `cur`; proof k-1's folds into `prev`; proof k-2's sum-check from `cur`'s tables
+        self._step(self.bufs[self.k % 2], self.bufs[(self.k + 1) % 2], self.k >= 1, self.k >= 2)
         mark("end")
         self.k += 1
 
+    def phases(self):
+        # the whole step is one launch
+        return [("witness+eq+fold+claim+sumcheck", lambda: self._step(self.bufs[0], self.bufs[1], True, True))]
+
     def capture(self, steps: int = 1):
+        while self.k < 2:  # every captured step then has all three parts
+            self.run()
         self.run()
-        torch.cuda.current_stream().wait_stream(self.side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(steps):
                 self.run()
-            torch.cuda.current_stream().wait_stream(self.side)
         torch.cuda.synchronize()
         self.graph = g
         self.graph_steps = steps
@@ -289,15 +285,16 @@ class OverlappedLayerProver(SingleLayerProver):
     def drain(self):
         """The sum-check of the next-to-last proof, then the folds, claim and
         sum-check of the last one."""
-        torch.cuda.current_stream().wait_stream(self.side)
         last = self.k - 1
         if last < 0:
             return
         cur, prev = self.bufs[last % 2], self.bufs[(last + 1) % 2]
         if last >= 1:
-            self._sumcheck_of(prev)
-        self._fold(cur)
-        self._sumcheck_of(cur)
+            sumcheck_prove([prev["xf"]], [prev["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                           claim0=self.claim0)
+        fold_claim_batched(*self._jobs(cur))
+        sumcheck_prove([cur["xf"]], [cur["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
+                       claim0=self.claim0)
 
     def output_tensors(self):
         return [t for b in self.bufs for t in b.values()] + [self.rounds, self.finals, self.claim0]
