@@ -80,7 +80,7 @@ def kernel_work(cfg, name: str, prover) -> tuple:
     return 0, 0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_T512_witness_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_T512_step_traffic.txt")
 
 
 def measured_traffic(cfg, kernel_phase: str):
