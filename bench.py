@@ -582,6 +582,8 @@ def main():
     prover.capture(per_graph)
     for _ in range(max(1, args.warmup // per_graph)):
         prover.replay()
+    # the drain path's one-time set-up (its workspace) outside the timed region
+    prover.drain()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -424,7 +424,9 @@ template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
 struct WsCfg {
   static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
   static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32, HB = BK / 2;
-  static constexpr int LDS_BYTES = 2 * BT * PITCH;
+  // the epilogue stages each wave's 32x32 int32 fragments in rows of EP words
+  static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
+  static constexpr int LDS_BYTES = 2 * BT * PITCH > STAGE_BYTES ? 2 * BT * PITCH : STAGE_BYTES;
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
 };
 
@@ -527,6 +529,14 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
 
   const int s = a.s;
   const int32_t lowmask = (1 << s) - 1;
+  // Z leaves through LDS: a lane's fragment holds 16 outputs of one token,
+  // so direct stores write 32-byte pieces of 32 rows; staged, eight lanes
+  // write a row's whole 128 bytes.
+  const bool stage = a.Z != nullptr && a.vecZ;
+  if (stage) __syncthreads();  // every wave is done with the X tiles
+  int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
+  WitArgs yr = a;
+  if (stage) yr.Z = nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -535,7 +545,21 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
       fragment_outputs(acc[i][j], z);
       const int t = t_base + 32 * j + r;
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
-      if (t < a.T && o0 < a.N) store_fragment(a, z, t, o0, s, lowmask);
+      if (t < a.T && o0 < a.N) store_fragment(yr, z, t, o0, s, lowmask);
+      if (stage) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(v4i*)&E[r * C::EP + 16 * h + 4 * q] = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int row = 8 * p + (lane >> 3), c4 = (lane & 7) * 4;
+          const v4i v = *(const v4i*)&E[row * C::EP + c4];
+          const int tz = t_base + 32 * j + row, oz = o_base + wo0 + 32 * i + c4;
+          if (tz < a.T && oz < a.N) *(v4i*)(a.Z + (int64_t)tz * a.N + oz) = v;  // N % 4 == 0
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
 }
 
