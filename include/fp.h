@@ -389,20 +389,32 @@ size_t fp_fold_claim_batched_workspace(fp_dtype fold_dt, int32_t n_fold, const f
  * the GEMM on most compute units, the folds' workgroups beside it, the
  * sum-check's chain of rounds on one. The folds' cross-chunk sums are done by
  * the last workgroup of each column strip (or claim) to finish, through
- * arrival counters at the start of ws: ws is fp_layer_step_workspace(n_fold,
- * folds, n_claim, claims) bytes, 256-byte aligned, and its first
- * FP_FOLD_COUNTER_BYTES must be zero on entry (every call leaves them zero).
- * At most 4 folds and claims, each with rows and columns (FP_ESHAPE
- * otherwise); the conditions of the three calls apply (VP * 2^n <= 4096).
- * Inputs of one part must not be written by another part of the same call. */
+ * arrival counters at the start of ws: ws is fp_layer_step_workspace(T, d_out,
+ * claim_E_t != NULL, n_fold, folds, n_claim, claims) bytes, 256-byte aligned,
+ * and its first FP_FOLD_COUNTER_BYTES must be zero on entry (every call leaves
+ * them zero). At most 4 folds and claims, each with rows and columns
+ * (FP_ESHAPE otherwise); the conditions of the three calls apply
+ * (VP * 2^n <= 4096). Inputs of one part must not be written by another part
+ * of the same call.
+ *
+ * Proof k's own claim (claim_E_t non-NULL; device tables of >= T and >= d_out
+ * entries, claim one element): *claim = sum_t sum_o E_t[t] E_o[o] Z[t, o]
+ * ("How fast can FlashProve go", §3.1: the claim about the product, the value
+ * fp_claim_eval_batched gives for Z), taken from the GEMM's accumulators, so Z
+ * need not be stored (Z may be NULL); E_t and E_o must then be complete before
+ * the call (not tables that the same call builds). Needs T, d_out > 0
+ * (FP_ESHAPE), and claim_E_o and claim with claim_E_t (FP_EARG). */
 int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in, int32_t d_out, int32_t s,
-                  int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq, const fp_eq_desc* eq, int32_t n_fold,
+                  int32_t* Z, int8_t* Y, int8_t* R, const fp_elem* claim_E_t, const fp_elem* claim_E_o,
+                  fp_elem* claim, int32_t n_eq, const fp_eq_desc* eq, int32_t n_fold,
                   const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims,
                   void* ws, size_t ws_bytes, int32_t n_pairs, const fp_elem* const* A, const fp_elem* const* B,
                   const fp_elem* rho, int32_t n, const fp_elem* r, fp_elem* rounds, fp_elem* finals,
                   fp_elem* claim0, hipStream_t stream);
-size_t fp_layer_step_workspace(int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
-                               const fp_claim_desc* claims);
+/* Bytes of fp_layer_step's ws for these folds and claims, with (own_claim != 0)
+ * one slot per GEMM wave for the claim of proof k; 0 on bad arguments. */
+size_t fp_layer_step_workspace(int32_t T, int32_t d_out, int32_t own_claim, int32_t n_fold,
+                               const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims);
 
 /* ----------------------------------------------------------- sum-check --- */
 /* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of

@@ -79,16 +79,25 @@ def test_argument_errors_without_gpu():
     assert b"exceed one" in L.fp_last_error()
     # the layer step: at most 4 folds and claims, none empty, and a large enough workspace
     fd = (fp._FoldDesc * 5)(*[fp._FoldDesc(16, 64, 10, 64, 64, 16, 16) for _ in range(5)])
-    assert L.fp_layer_step(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 0, None, 5, fd, 0, None, dummy, 1 << 20,
-                           0, None, None, None, 0, None, None, None, None, None) == 1
+    assert L.fp_layer_step(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, None, None, None, 0, None, 5, fd, 0,
+                           None, dummy, 1 << 20, 0, None, None, None, 0, None, None, None, None, None) == 1
     fd0 = (fp._FoldDesc * 1)(fp._FoldDesc(16, 64, 0, 64, 64, 16, 16))
-    assert L.fp_layer_step(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 0, None, 1, fd0, 0, None, dummy, 1 << 20,
-                           0, None, None, None, 0, None, None, None, None, None) == 2
+    assert L.fp_layer_step(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, None, None, None, 0, None, 1, fd0, 0,
+                           None, dummy, 1 << 20, 0, None, None, None, 0, None, None, None, None, None) == 2
     fd1 = (fp._FoldDesc * 1)(fp._FoldDesc(16, 64, 5000, 64, 64, 16, 16))
-    need = L.fp_layer_step_workspace(1, fd1, 0, None)
+    need = L.fp_layer_step_workspace(4, 4, 0, 1, fd1, 0, None)
     assert need > 16384
-    assert L.fp_layer_step(ctypes.c_void_p(256), 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 0, None, 1, fd1, 0, None,
-                           ctypes.c_void_p(256), need - 1, 0, None, None, None, 0, None, None, None, None, None) == 4
+    # the witness's own claim: one more slot per GEMM wave, both tables and an output, tokens and outputs
+    assert L.fp_layer_step_workspace(4, 4, 1, 1, fd1, 0, None) > need
+    assert L.fp_layer_step_workspace(4, 4, 1, 0, None, 0, None) > 16384
+    assert L.fp_layer_step_workspace(-1, 4, 1, 0, None, 0, None) == 0
+    assert L.fp_layer_step(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, dummy, None, dummy, 0, None, 0, None, 0,
+                           None, dummy, 1 << 20, 0, None, None, None, 0, None, None, None, None, None) == 1
+    assert L.fp_layer_step(dummy, 48, dummy, 0, 48, 4, 8, None, dummy, dummy, dummy, dummy, dummy, 0, None, 0, None,
+                           0, None, dummy, 1 << 20, 0, None, None, None, 0, None, None, None, None, None) == 2
+    assert L.fp_layer_step(ctypes.c_void_p(256), 48, dummy, 4, 48, 4, 8, None, dummy, dummy, None, None, None, 0,
+                           None, 1, fd1, 0, None, ctypes.c_void_p(256), need - 1, 0, None, None, None, 0, None, None,
+                           None, None, None) == 4
     # eq tables built beside the packed witness: at most 8, each n in [0, 30] with non-null pointers
     assert L.fp_witness_linear_packed(dummy, 48, dummy, 4, 48, 4, 8, None, dummy, dummy, 9, dummy, None) == 1
     eqd = (fp._EqDesc * 2)(fp._EqDesc(16, 3, 16), fp._EqDesc(16, 31, 16))

@@ -69,14 +69,17 @@ def test_pipelined_graph_replays(fp, cid, shape):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cid,shape,steps", [(1, {}, 2), (2, dict(T=100, d_in=1008, d_out=700), 3)])
-def test_overlapped_graph_replays(fp, cid, shape, steps):
-    """Three proofs in flight recorded as a graph (two streams inside it): replays followed by the drain give the
-    eager outputs, with every buffer cleared between replays and eager steps in between."""
+@pytest.mark.parametrize("cid,shape,steps,keep_z", [(1, {}, 3, False), (2, dict(T=100, d_in=1008, d_out=700), 6, True)])
+def test_overlapped_graph_replays(fp, cid, shape, steps, keep_z):
+    """Three proofs in flight recorded as a graph (one launch per step): replays followed by the drain give the
+    eager outputs, with every buffer cleared between replays and eager steps in between; a graph of a number of
+    steps that is not a multiple of three is refused."""
     cfg = synth.config(cid, **shape)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
-    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True, keep_z=keep_z)
+    with pytest.raises(ValueError):
+        prover.capture(steps=4)
     prover.run()
     prover.run()
     prover.drain()

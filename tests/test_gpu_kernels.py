@@ -491,6 +491,66 @@ def test_layer_step(fp, T, d_in, d_out, k):
         assert int(ws.buf[:16384].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("T,d_in,d_out,keep_z,tables,fold", [
+    (100, 320, 700, True, "eq", True), (1000, 96, 6100, False, "rand", True), (1000, 96, 6100, True, "eq", False),
+    (16, 64, 48, False, "rand", False), (1, 16, 1, True, "rand", True), (4, 0, 9, True, "eq", False),
+    (512, 512, 2048, False, "eq", True)])
+def test_layer_step_own_claim(fp, T, d_in, d_out, keep_z, tables, fold):
+    """The witness's own claim sum_t sum_o E_t[t] E_o[o] Z[t, o] taken from the GEMM's accumulators (both tile
+    configurations, ragged edges, Z stored or not, eq tables or arbitrary field tables with 0, 1 and p - 1),
+    beside another proof's fold: the claim, Y, R (and Z) equal the oracle's on two calls in a row, and the
+    arrival counters are zero again."""
+    rng = _rng(1300 + T + d_out + d_in)
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    if tables == "eq":
+        rt, ro = _field(rng, max(1, (T - 1).bit_length())), _field(rng, max(1, (d_out - 1).bit_length()))
+        Et_h, Eo_h = O.eq_table(rt), O.eq_table(ro)
+    else:
+        Et_h, Eo_h = _field(rng, T), _field(rng, d_out)
+    Et, Eo = fp.to_field_tensor(Et_h), fp.to_field_tensor(Eo_h)
+    X2, E1 = _i8(rng, (300, 200)), _field(rng, 300)
+    xo = torch.empty(256, dtype=torch.int64, device="cuda")
+    Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda") if keep_z else None
+    Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    c = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws = fp.StepWorkspace()
+    Wp = fp.pack_weights(_dev(W))
+    wz, wy, wr = O.witness(X, W, 8)
+    if tables == "eq":
+        want = O.mle_matrix(wz, rt, ro)
+    else:
+        u = O.fold_rows(wz, Et_h)
+        want = 0
+        for o in range(d_out):
+            want = O.add(want, O.mul(int(Eo_h[o]), int(u[o])))
+    for rep in range(2):
+        c.fill_(-1)
+        fp.layer_step(_dev(X), Wp, 8, Z, Y, R, own_claim=(Et, Eo, c),
+                      folds=[(_dev(X2), fp.to_field_tensor(E1), 256, xo)] if fold else (), ws=ws)
+        torch.cuda.synchronize()
+        assert int(fp.field_numpy(c)[0]) == want
+        assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
+        if keep_z:
+            assert np.array_equal(Z.cpu().numpy(), wz)
+        if fold:
+            assert np.array_equal(fp.field_numpy(xo), O.fold_rows(X2, E1, 256))
+        assert int(ws.buf[:16384].count_nonzero()) == 0
+
+
+def test_layer_step_own_claim_errors(fp):
+    """The own claim needs both tables and an output, and tokens and outputs."""
+    X = torch.zeros((8, 16), dtype=torch.int8, device="cuda")
+    Wp = fp.pack_weights(torch.zeros((8, 16), dtype=torch.int8, device="cuda"))
+    Y = torch.empty((8, 8), dtype=torch.int8, device="cuda")
+    R = torch.empty((8, 8), dtype=torch.int8, device="cuda")
+    E = torch.zeros(8, dtype=torch.int64, device="cuda")
+    with pytest.raises(RuntimeError):
+        fp.layer_step(X, Wp, 8, None, Y, R, own_claim=(E, None, torch.empty(1, dtype=torch.int64, device="cuda")))
+    with pytest.raises(RuntimeError):
+        fp.layer_step(X[:0], Wp, 8, None, Y[:0], R[:0], own_claim=(E, E, torch.empty(1, dtype=torch.int64, device="cuda")))
+
+
 @pytest.mark.parametrize("T,d_in,d_out,k,n", [(100, 320, 700, 1, 12), (16, 64, 48, 1, 1), (600, 256, 300, 3, 9),
                                              (0, 64, 64, 2, 10), (40, 96, 0, 1, 5), (1000, 96, 6100, 2, 11)])
 def test_witness_packed_with_sumcheck(fp, T, d_in, d_out, k, n):

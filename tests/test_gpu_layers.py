@@ -111,22 +111,26 @@ def test_layer_pipelined(fp, cid, shape):
     assert got["c0"] == got["claim0"]
 
 
-@pytest.mark.parametrize("cid,shape,runs", [(1, {}, 1), (1, {}, 4), (2, dict(T=100, d_in=1008, d_out=700), 3)])
-def test_layer_overlapped(fp, cid, shape, runs):
-    """Three proofs in flight (each step: this proof's witness and eq tables with the sum-check of the proof two
-    back, and the previous proof's folds and claim on a second stream): after the runs and the drain every output
-    is the oracle's."""
+@pytest.mark.parametrize("cid,shape,runs,keep_z", [(1, {}, 1, True), (1, {}, 4, False), (1, {}, 5, True),
+                                                   (2, dict(T=100, d_in=1008, d_out=700), 3, False),
+                                                   (2, dict(T=100, d_in=1008, d_out=700), 7, True)])
+def test_layer_overlapped(fp, cid, shape, runs, keep_z):
+    """Three proofs in flight (each step one launch: this proof's witness with its claim from the accumulators,
+    the next proof's eq tables, the previous proof's folds and the sum-check of the proof two back; buffers over
+    three sets): after the runs and the drain every output is the oracle's (Z only when it is kept)."""
     cfg = synth.config(cid, **shape)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
-    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True, keep_z=keep_z)
     for _ in range(runs):
         prover.run()
     prover.drain()
     torch.cuda.synchronize()
     got = prover.results()
     want = O.prove_config(cfg, inp, ch)["main" if cid == 1 else "up"]
-    _cmp_matmul(got, want)
+    assert ("Z" in got) == keep_z
+    _cmp_matmul(got, want, keys=[k for k in ("Z", "Y", "R", "x_fold", "w_fold", "rounds", "finals", "c0", "claim0")
+                                 if k in got])
     assert got["c0"] == got["claim0"]
 
 
@@ -184,20 +188,44 @@ def test_full_cfg2_pipelined(fp):
     _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
 
 
-def test_full_cfg2_overlapped(fp):
-    """The benchmark's launch configuration with three proofs in flight: four proofs per graph replay, the folds
-    of each beside the next proof's witness, the last two finished by the drain."""
+@pytest.mark.parametrize("keep_z", [True, False])
+def test_full_cfg2_overlapped(fp, keep_z):
+    """The benchmark's launch configuration with three proofs in flight: six proofs per graph replay, each
+    proof's claim from its GEMM's accumulators, its folds beside the next proof's witness, the last two finished
+    by the drain. With Z kept: sampled Z, Y, R and the claim against the oracle's MLE of that Z; without it (as
+    the benchmark runs): sampled Y, R against the oracle's entries, the folds and rounds against the oracle's,
+    and the claim equal to the sum-check's initial claim <x', w'> (Z = X W^T makes them equal)."""
     cfg = synth.config(2)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg)
-    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True)
-    prover.capture(steps=4)
+    prover = make_prover(cfg, inp, ch, pipelined=True, overlapped=True, keep_z=keep_z)
+    prover.capture(steps=6)
     prover.replay()
     prover.replay()
     prover.drain()
     torch.cuda.synchronize()
     got = prover.results()
-    _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
+    if keep_z:
+        _check_full_matmul(inp["X"], inp["W"], cfg.s, got, ch["r_t"], ch["r_o"], ch["rounds"])
+        return
+    assert "Z" not in got
+    X, W = inp["X"], inp["W"]
+    E_t, E_o = O.eq_table(ch["r_t"]), O.eq_table(ch["r_o"])
+    n = len(ch["rounds"])
+    xf, wf = O.fold_rows(X, E_t, 1 << n), O.fold_rows(W, E_o, 1 << n)
+    assert np.array_equal(got["x_fold"], xf) and np.array_equal(got["w_fold"], wf)
+    rounds, finals, claim0 = O.sumcheck([xf], [wf], ch["rounds"])
+    assert np.array_equal(got["rounds"], rounds) and np.array_equal(np.asarray(got["finals"]).reshape(-1, 2), finals)
+    assert got["claim0"] == claim0 and got["c0"] == claim0
+    rng = np.random.default_rng(5)
+    T, d_out = got["Y"].shape
+    ts = rng.integers(0, T, 2048).astype(np.int32)
+    os_ = rng.integers(0, d_out, 2048).astype(np.int32)
+    ts[:4] = [0, T - 1, 0, T - 1]
+    os_[:4] = [0, d_out - 1, d_out - 1, 0]
+    z = O.witness_entries(X, W, ts, os_)
+    _, r, y = O.rescale(z, cfg.s)
+    assert np.array_equal(got["Y"][ts, os_], y) and np.array_equal(got["R"][ts, os_], r)
 
 
 def test_full_cfg3(fp):

@@ -114,9 +114,9 @@ def lib():
             "fp_witness_linear_packed_with_sumcheck": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp,
                                                                       i32, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                                                       vp]),
-            "fp_layer_step": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32, vp, i32, vp,
-                                             vp, sz, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
-            "fp_layer_step_workspace": (sz, [i32, vp, i32, vp]),
+            "fp_layer_step": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp,
+                                             i32, vp, vp, sz, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -313,10 +313,12 @@ _ws_step = StepWorkspace()
 
 
 def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=(), As=(), Bs=(), r=None, rho=None,
-               rounds=None, finals=None, claim0=None, ws: StepWorkspace | None = None):
+               rounds=None, finals=None, claim0=None, ws: StepWorkspace | None = None, own_claim=None):
     """One launch: the witness and eq tables of a proof (as witness_linear_packed), the int8 folds
     (M, E, cols_pad, out) and int32 claims (M, E_rows, E_cols, out) of another (as fold_claim_batched), and
-    the sum-check of a third (as sumcheck_prove over As, Bs, r; none when As is empty)."""
+    the sum-check of a third (as sumcheck_prove over As, Bs, r; none when As is empty). own_claim =
+    (E_t, E_o, out): the witness's own claim sum E_t[t] E_o[o] Z[t, o] from the accumulators (Z may then
+    be None; E_t and E_o must be finished before the call)."""
     T, d_in = X.shape
     assert X.dtype == torch.int8 and d_in == Wp.d_in
     assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
@@ -327,12 +329,14 @@ def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=
     cd = (_ClaimDesc * max(nc, 1))(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
                                                 Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in claims])
     ws = _ws_step if ws is None else ws
-    p, nb = ws.get(lib().fp_layer_step_workspace(nf, fd, nc, cd))
+    cEt, cEo, cout = own_claim if own_claim is not None else (None, None, None)
+    p, nb = ws.get(lib().fp_layer_step_workspace(T, Wp.d_out, int(own_claim is not None), nf, fd, nc, cd))
     k = len(As)
     pa = (ctypes.c_void_p * max(k, 1))(*[a.data_ptr() for a in As])
     pb = (ctypes.c_void_p * max(k, 1))(*[b.data_ptr() for b in Bs])
     n = r.numel() if r is not None else 0
     _check(lib().fp_layer_step(_ptr(X), _ld(X), _ptr(Wp.data), T, d_in, Wp.d_out, s, _ptr(Z), _ptr(Y), _ptr(R),
+                               _ptr(cEt), _ptr(cEo), _ptr(cout),
                                ne, eqd, nf, fd, nc, cd, p, nb, k, pa, pb, _ptr(rho), n, _ptr(r), _ptr(rounds),
                                _ptr(finals), _ptr(claim0), _stream()), "fp_layer_step")
 

@@ -61,6 +61,14 @@ struct WitArgs {
   int64_t ldp, psplit;
   // packed weights (W then points at them): 32-row blocks and WP_BK-byte K blocks
   int32_t wp_rb, wp_kb;
+  // packed kernel: the claim sum_{t,o} cEt[t] cEo[o] Z[t, o] of the launch's own
+  // product, taken from the accumulators (none when cEt is NULL): one value per
+  // wave into cpart, and the last tile to arrive at *cctr writes the sum to *cout
+  const uint64_t* cEt = nullptr;
+  const uint64_t* cEo = nullptr;
+  uint64_t* cpart = nullptr;
+  uint64_t* cout = nullptr;
+  uint32_t* cctr = nullptr;
 };
 
 struct GroupTab {
@@ -412,6 +420,61 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
   }
 }
 
+// ---- the claim of a launch's own product, from the accumulators ---------
+// Each wave contracts its fragments over the outputs on the matrix cores:
+// the 7-bit limbs of E_o (CL_LIMBS per element, rows 0..9 of the A operand)
+// against the four byte planes of Z (the B operand: after the swap a lane
+// holds 16 consecutive outputs of one token, which is the operand's layout
+// with the outputs as k). Planes 0-2 are unsigned bytes, fed as b - 128 with
+// 128 times the limb sums (one more product, against ones) added back; plane
+// 3 is Z's signed top byte. Row m of the products, weighted 2^(7m + 8p), then
+// gives sum_o E_o[o] Z[t, o] for the lane's token t, which E_t[t] weights.
+constexpr int CL_LIMBS = 10;
+
+// Lane (t, h) of plane products D[p] and of the limb sums L: register v holds
+// row m = 8 (v / 4) + 4 h + v % 4; rows below CL_LIMBS carry limbs (v < 4 for
+// both halves, v = 4, 5 for h = 0). Returns sum_m 2^(7m) (sum_p 2^(8p) D_p[m]
+// + 128 (1 + 2^8 + 2^16) L[m]) mod p.
+__device__ __forceinline__ uint64_t claim_row_value(const v16i (&D)[4], const int64_t (&corr)[6], int h) {
+  // p 2^48 keeps the 128-bit sum positive (|sum| < 2^112)
+  uint64_t lo = 1ull << 48, hi = (1ull << 48) - (1ull << 16);
+#pragma unroll
+  for (int v = 0; v < 6; ++v) {
+    if (v >= 4 && h != 0) continue;
+    const int m = (v < 4 ? v : v + 4) + 4 * h;
+    const int32_t s01 = D[0][v] + (D[1][v] << 8);  // |D| < 2^21: exact in 32 bits
+    const int32_t s23 = D[2][v] + (D[3][v] << 8);
+    const int64_t sv = (int64_t)s01 + ((int64_t)s23 << 16) + corr[v];
+    const int sh = 7 * m;
+    const uint64_t plo = (uint64_t)sv << sh;
+    const uint64_t phi = sh == 0 ? (uint64_t)(sv >> 63) : (uint64_t)(sv >> (64 - sh));
+    const uint64_t nlo = lo + plo;
+    hi += phi + (nlo < lo ? 1 : 0);
+    lo = nlo;
+  }
+  return gl::reduce128(lo, hi);
+}
+
+// The wave's claim value to its slot; the last tile to arrive adds them all.
+__device__ __forceinline__ void claim_arrive(const WitArgs& a, uint64_t wsum, int bid, int nblocks, int nwaves,
+                                             uint64_t* red, uint32_t* flag) {
+  const int tid = threadIdx.x;
+  wsum = fpi::wave_total(wsum);
+  if ((tid & 63) == 0) foldk::store_part(a.cpart + (int64_t)bid * nwaves + (tid >> 6), wsum, true);
+  if (!foldk::arrive_last(a.cctr, (uint32_t)nblocks, flag)) return;
+  const int nv = nblocks * nwaves;
+  uint64_t v = 0;
+  for (int i = tid; i < nv; i += (int)blockDim.x) v = gl::add(v, foldk::load_part(a.cpart + i));
+  v = fpi::wave_total(v);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t t = 0;
+    for (int w = 0; w < nwaves; ++w) t = gl::add(t, red[w]);
+    *a.cout = t;
+  }
+}
+
 // Tile `bid` of `nblocks`: NW waves, wave w owning weight rows
 // [o_base + 32 TM w, +32 TM) (fragments from the packed weights, PFW K blocks
 // ahead) and all BT = 32 TN tokens of the tile (X through double-buffered
@@ -424,9 +487,12 @@ template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
 struct WsCfg {
   static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
   static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32, HB = BK / 2;
-  // the epilogue stages each wave's 32x32 int32 fragments in rows of EP words
+  // the epilogue stages each wave's 32x32 int32 fragments in rows of EP words;
+  // the claim's limb table [CL_LIMBS][BO] and reduction words follow
   static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
-  static constexpr int LDS_BYTES = 2 * BT * PITCH > STAGE_BYTES ? 2 * BT * PITCH : STAGE_BYTES;
+  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 16 * 8;
+  static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
+  static constexpr int LDS_BYTES = 2 * BT * PITCH > EPI_BYTES ? 2 * BT * PITCH : EPI_BYTES;
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
 };
 
@@ -533,14 +599,47 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   // so direct stores write 32-byte pieces of 32 rows; staged, eight lanes
   // write a row's whole 128 bytes.
   const bool stage = a.Z != nullptr && a.vecZ;
-  if (stage) __syncthreads();  // every wave is done with the X tiles
+  const bool claim = a.cEt != nullptr;
+  if (stage || claim) __syncthreads();  // every wave is done with the X tiles
   int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
+  uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::STAGE_BYTES;
+  uint64_t* red = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);
+  v4i Aop[TM];
+  int64_t corr[6];
+  if (claim) {
+    // limb table of the tile's outputs (zero past d_out, so rows of Z there,
+    // computed from clamped weight blocks, do not count)
+    for (int x = tid; x < BO; x += NT) {
+      const int o = o_base + x;
+      const uint64_t e = o < a.N ? a.cEo[o] : 0;
+#pragma unroll
+      for (int m = 0; m < CL_LIMBS; ++m) limbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      Aop[i] = r < CL_LIMBS ? *(const v4i*)&limbs[r * BO + wo0 + 32 * i + 16 * h] : v4i{0, 0, 0, 0};
+    v16i L;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) L[v] = 0;
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+    for (int i = 0; i < TM; ++i) L = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], ones, L, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 6; ++v) corr[v] = (int64_t)L[v] * (128 * 65793);
+  }
   WitArgs yr = a;
   if (stage) yr.Z = nullptr;
+  uint64_t wsum = 0;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < TN; ++j) {
+    v16i D[4];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) D[p][v] = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
       int32_t z[16];
       fragment_outputs(acc[i][j], z);
       const int t = t_base + 32 * j + r;
@@ -560,7 +659,28 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
         }
         __builtin_amdgcn_wave_barrier();
       }
+      if (claim) {
+        v4i P[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t w0, w1, w2, w3;
+          foldk::transpose4((uint32_t)z[4 * g], (uint32_t)z[4 * g + 1], (uint32_t)z[4 * g + 2], (uint32_t)z[4 * g + 3],
+                            w0, w1, w2, w3);
+          P[0][g] = (int)(w0 ^ 0x80808080u);
+          P[1][g] = (int)(w1 ^ 0x80808080u);
+          P[2][g] = (int)(w2 ^ 0x80808080u);
+          P[3][g] = (int)w3;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) D[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], P[p], D[p], 0, 0, 0);
+      }
     }
+    if (claim) {
+      const int t = t_base + 32 * j + r;
+      wsum = gl::add(wsum, gl::mul(claim_row_value(D, corr, h), t < a.T ? a.cEt[t] : 0));
+    }
+  }
+  if (claim) claim_arrive(a, wsum, bid, nblocks, NW, red, reinterpret_cast<uint32_t*>(red + 8));
 }
 
 // 256x64 workgroup tiles (outputs x tokens): 4 waves of 64x64, weight
@@ -1057,8 +1177,20 @@ namespace {
 
 // Plans the folds (int8) and claims (int32) of the step's fold workgroups:
 // workspace = arrival counters, then every job's partial values.
+// GEMM tiles of the layer step for a shape (256x128 once there are >= 192 of them, else 256x64).
+int64_t step_tiles(int32_t T, int32_t d_out, bool* large) {
+  const int64_t large_tiles = (int64_t)((d_out + 255) / 256) * ((T + 127) / 128);
+  *large = large_tiles >= 192;
+  return *large ? large_tiles : (int64_t)((d_out + 255) / 256) * ((T + 63) / 64);
+}
+constexpr int STEP_WAVES = 4;  // waves of both layer-step tile configurations
+
+// Workspace of a layer step: arrival counters, the folds' partial values and
+// (own_parts > 0) one slot per GEMM wave for the claim taken from the
+// accumulators, whose counter follows the folds'.
 int step_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
-               const fp_claim_desc* claims, void* ws, size_t ws_bytes, bool plan_only, size_t* need, FoldAux& fa) {
+               const fp_claim_desc* claims, int64_t own_parts, void* ws, size_t ws_bytes, bool plan_only,
+               size_t* need, FoldAux& fa, uint64_t** own_part, uint32_t** own_ctr) {
   fa = FoldAux{};
   if (n_fold < 0 || n_claim < 0 || n_fold + n_claim > STEP_MAX_FOLD)
     return fpi::fail(FP_EARG, "%s: %d folds and %d claims (at most %d in all)", fn, n_fold, n_claim, STEP_MAX_FOLD);
@@ -1104,11 +1236,19 @@ int step_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_
     nctr += p.ctrs;
     fa.j[fa.count++] = j;
   }
+  *own_part = nullptr;
+  *own_ctr = nullptr;
+  if (own_parts > 0) {
+    *own_part = (uint64_t*)((char*)ws + off);
+    off += fpi::align_up((size_t)own_parts * 8, 256);
+    *own_ctr = (uint32_t*)ws + nctr;
+    nctr += 1;
+  }
   if (nctr > (int32_t)(FP_FOLD_COUNTER_BYTES / 4) || blocks > (1 << 24))
     return fpi::fail(FP_ESHAPE, "%s: folds too large for one step", fn);
   fa.blocks = (int32_t)blocks;
   fa.ctrs = (uint32_t*)ws;
-  *need = (n_fold + n_claim) ? off : 0;
+  *need = (n_fold + n_claim || own_parts > 0) ? off : 0;
   if (plan_only) return FP_OK;
   if (*need && (!ws || ws_bytes < *need)) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, *need);
   if (*need && (((uintptr_t)ws) & 255)) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
@@ -1117,16 +1257,24 @@ int step_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_
 
 }  // namespace
 
-extern "C" size_t fp_layer_step_workspace(int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
-                                          const fp_claim_desc* claims) {
+extern "C" size_t fp_layer_step_workspace(int32_t T, int32_t d_out, int32_t own_claim, int32_t n_fold,
+                                          const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims) {
+  if (T < 0 || d_out < 0) return 0;
   FoldAux fa;
   size_t need = 0;
-  if (step_folds("fp_layer_step_workspace", n_fold, folds, n_claim, claims, nullptr, 0, true, &need, fa)) return 0;
+  bool large;
+  const int64_t own = own_claim ? step_tiles(T, d_out, &large) * STEP_WAVES : 0;
+  uint64_t* op;
+  uint32_t* oc;
+  if (step_folds("fp_layer_step_workspace", n_fold, folds, n_claim, claims, own, nullptr, 0, true, &need, fa, &op,
+                 &oc))
+    return 0;
   return need;
 }
 
 extern "C" int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int32_t d_in, int32_t d_out,
-                             int32_t s, int32_t* Z, int8_t* Y, int8_t* R, int32_t n_eq, const fp_eq_desc* eq,
+                             int32_t s, int32_t* Z, int8_t* Y, int8_t* R, const fp_elem* claim_E_t,
+                             const fp_elem* claim_E_o, fp_elem* claim, int32_t n_eq, const fp_eq_desc* eq,
                              int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims,
                              void* ws, size_t ws_bytes, int32_t n_pairs, const fp_elem* const* A,
                              const fp_elem* const* B, const fp_elem* rho, int32_t n, const fp_elem* r,
@@ -1138,9 +1286,16 @@ extern "C" int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int
   EqAux aux;
   rc = eq_aux(fn, n_eq, eq, aux);
   if (rc) return rc;
+  const bool own = claim_E_t != nullptr;
+  if (own && (!claim_E_o || !claim)) return fpi::fail(FP_EARG, "%s: the claim needs E_t, E_o and its output", fn);
+  if (own && (T == 0 || d_out == 0)) return fpi::fail(FP_ESHAPE, "%s: the claim needs tokens and outputs", fn);
+  bool large;
+  const int64_t own_parts = own ? step_tiles(T, d_out, &large) * STEP_WAVES : 0;
   FoldAux fa;
   size_t need = 0;
-  rc = step_folds(fn, n_fold, folds, n_claim, claims, ws, ws_bytes, false, &need, fa);
+  uint64_t* own_part;
+  uint32_t* own_ctr;
+  rc = step_folds(fn, n_fold, folds, n_claim, claims, own_parts, ws, ws_bytes, false, &need, fa, &own_part, &own_ctr);
   if (rc) return rc;
   sct::TailArgs ta;
   const bool tail = n_pairs > 0;
@@ -1149,9 +1304,16 @@ extern "C" int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int
     if (rc) return rc;
   }
   a.Z = Z; a.Y = Y; a.R = R;
+  if (own) {
+    a.cEt = claim_E_t;
+    a.cEo = claim_E_o;
+    a.cout = claim;
+    a.cpart = own_part;
+    a.cctr = own_ctr;
+  }
   vec_flags(a);
-  const int64_t large_tiles = (int64_t)((a.N + 255) / 256) * ((a.T + 127) / 128);
-  if (large_tiles >= 192) rc = launch_step<WIT_WS_L>(a, tail ? &ta : nullptr, tail ? 1 : 0, aux, fa, stream);
+  step_tiles(T, d_out, &large);
+  if (large) rc = launch_step<WIT_WS_L>(a, tail ? &ta : nullptr, tail ? 1 : 0, aux, fa, stream);
   else rc = launch_step<WIT_WS>(a, tail ? &ta : nullptr, tail ? 1 : 0, aux, fa, stream);
   return rc ? rc : fpi::ok();
 }

@@ -219,50 +219,73 @@ class SingleLayerProver(_Prover):
 class OverlappedLayerProver(SingleLayerProver):
     """Single-layer proofs three deep, for a stream of proofs of one layer with
     packed weights: step k is ONE launch (fp_layer_step) that runs proof k's
-    witness and eq tables, proof k-1's folds and claim and proof k-2's
-    sum-check side by side. Proof k-1's folds read only its own witness and eq
-    tables (finished by the previous launch), and proof k-2's sum-check only
-    its own folds (likewise), so each proof still follows the protocol order;
-    the buffers of consecutive proofs alternate between two sets. ``drain()``
-    finishes the last two proofs; outputs are those of the last proof."""
+    witness together with its claim c0 = Z~(r_o || r_t), taken from the GEMM's
+    accumulators (so Z never has to be stored and read back), proof k+1's eq
+    tables, proof k-1's folds and proof k-2's sum-check side by side. A proof's
+    eq tables depend on its challenges alone, so they are built one step ahead
+    and are complete when its GEMM's epilogue weights the claim with them;
+    proof k-1's folds read only its own tables (likewise finished), and proof
+    k-2's sum-check only its own folds, so each proof still follows the
+    protocol order. The buffers of a proof (Y, R, tables, folds, c0) live from
+    the step that builds its eq tables to the one that runs its sum-check, so
+    they rotate over three sets, and a captured graph holds a multiple of three
+    steps. ``drain()`` finishes the last two proofs; outputs are those of the
+    last proof. keep_z: also write Z (which the proof never reads back)."""
 
     PER_PROOF = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0")
+    SETS = 3
+    GRAPH_QUANTUM = 3  # steps per captured graph must be a multiple of this
 
-    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None):
+    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, ch: dict, dev=None, keep_z: bool = False):
         super().__init__(X, W, s, ch, dev, pipelined=True)
         if self.Wp is None:
             raise ValueError("overlapped proofs need packed weights (d_in % 16 == 0)")
+        self.keep_z = keep_z
         first = {k: getattr(self, k) for k in self.PER_PROOF}
-        second = {k: (torch.zeros_like(v) if k in ("xf", "wf") else torch.empty_like(v)) for k, v in first.items()}
-        self.bufs = [first, second]
+        if not keep_z:
+            first["Z"] = None
+        self.bufs = [first] + [
+            {k: (None if v is None else torch.zeros_like(v) if k in ("xf", "wf") else torch.empty_like(v))
+             for k, v in first.items()} for _ in range(self.SETS - 1)]
         self.k = 0
         self.ws = StepWorkspace()
 
-    def _jobs(self, b):
-        n = self.n
-        return ([(self.X, b["E_t"], 1 << n, b["xf"]), (self.W, b["E_o"], 1 << n, b["wf"])],
-                [(b["Z"], b["E_t"], b["E_o"], b["c0"])])
+    def _buf(self, k):
+        return self.bufs[k % self.SETS]
 
-    def _step(self, cur, prev, fold: bool, tail: bool):
-        folds, claims = self._jobs(prev) if fold else ((), ())
-        layer_step(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"],
-                   eq=[(self.ch["r_t"], cur["E_t"]), (self.ch["r_o"], cur["E_o"])], folds=folds, claims=claims,
-                   As=[cur["xf"]] if tail else (), Bs=[cur["wf"]] if tail else (), r=self.ch["rounds"],
+    def _eq_jobs(self, b):
+        return [(self.ch["r_t"], b["E_t"]), (self.ch["r_o"], b["E_o"])]
+
+    def _folds(self, b):
+        n = self.n
+        return [(self.X, b["E_t"], 1 << n, b["xf"]), (self.W, b["E_o"], 1 << n, b["wf"])]
+
+    def _step(self, k, fold: bool, tail: bool):
+        cur, nxt, prev, old = self._buf(k), self._buf(k + 1), self._buf(k - 1), self._buf(k - 2)
+        layer_step(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"], own_claim=(cur["E_t"], cur["E_o"], cur["c0"]),
+                   eq=self._eq_jobs(nxt), folds=self._folds(prev) if fold else (),
+                   As=[old["xf"]] if tail else (), Bs=[old["wf"]] if tail else (), r=self.ch["rounds"],
                    rounds=self.rounds, finals=self.finals, claim0=self.claim0, ws=self.ws)
 
     def run(self, mark=_nomark):
         mark("step")
-        # proof k into `cur`; proof k-1's folds into `prev`; proof k-2's sum-check from `cur`'s tables
-        self._step(self.bufs[self.k % 2], self.bufs[(self.k + 1) % 2], self.k >= 1, self.k >= 2)
+        if self.k == 0:  # the first proof's eq tables (later ones are built a step ahead)
+            b = self._buf(0)
+            eq_table_batched([self.ch["r_t"], self.ch["r_o"]], [b["E_t"], b["E_o"]])
+        # proof k's witness and claim; proof k+1's eq tables; proof k-1's folds; proof k-2's sum-check
+        self._step(self.k, self.k >= 1, self.k >= 2)
         mark("end")
         self.k += 1
 
     def phases(self):
         # the whole step is one launch
-        return [("witness+eq+fold+claim+sumcheck", lambda: self._step(self.bufs[0], self.bufs[1], True, True))]
+        wit = "witness" if self.keep_z else "witness(Y,R)"
+        return [(wit + "+claim(acc)+eq+fold+sumcheck", lambda: self._step(2, True, True))]
 
     def capture(self, steps: int = 1):
-        while self.k < 2:  # every captured step then has all three parts
+        if steps % self.GRAPH_QUANTUM:
+            raise ValueError("a captured graph holds a multiple of %d steps" % self.GRAPH_QUANTUM)
+        while self.k < 2:  # every captured step then has all its parts
             self.run()
         self.run()
         torch.cuda.synchronize()
@@ -277,35 +300,40 @@ class OverlappedLayerProver(SingleLayerProver):
         return g
 
     def replay(self):
-        """The captured steps again (with their buffers); drain() then finishes
-        the replay's last two proofs."""
+        """The captured steps again (with their buffers: a multiple of three
+        steps leaves every set where the graph expects it); drain() then
+        finishes the replay's last two proofs."""
         self.graph.replay()
         self.k = self.k_graph
 
     def drain(self):
-        """The sum-check of the next-to-last proof, then the folds, claim and
-        sum-check of the last one."""
+        """The sum-check of the next-to-last proof, then the folds and
+        sum-check of the last one (its claim came with its witness)."""
         last = self.k - 1
         if last < 0:
             return
-        cur, prev = self.bufs[last % 2], self.bufs[(last + 1) % 2]
         if last >= 1:
+            prev = self._buf(last - 1)
             sumcheck_prove([prev["xf"]], [prev["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
                            claim0=self.claim0)
-        fold_claim_batched(*self._jobs(cur))
+        cur = self._buf(last)
+        fold_claim_batched(self._folds(cur), [])
         sumcheck_prove([cur["xf"]], [cur["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
                        claim0=self.claim0)
 
     def output_tensors(self):
-        return [t for b in self.bufs for t in b.values()] + [self.rounds, self.finals, self.claim0]
+        return [t for b in self.bufs for t in b.values() if t is not None] + [self.rounds, self.finals, self.claim0]
 
     def results(self) -> dict:
-        b = self.bufs[(self.k - 1) % 2]
-        return {"Z": b["Z"].cpu().numpy(), "Y": b["Y"].cpu().numpy(), "R": b["R"].cpu().numpy(),
-                "E_t": field_numpy(b["E_t"]), "E_o": field_numpy(b["E_o"]),
-                "x_fold": field_numpy(b["xf"]), "w_fold": field_numpy(b["wf"]),
-                "c0": int(field_numpy(b["c0"])[0]), "rounds": field_numpy(self.rounds),
-                "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
+        b = self._buf(self.k - 1)
+        out = {"Y": b["Y"].cpu().numpy(), "R": b["R"].cpu().numpy(),
+               "E_t": field_numpy(b["E_t"]), "E_o": field_numpy(b["E_o"]),
+               "x_fold": field_numpy(b["xf"]), "w_fold": field_numpy(b["wf"]),
+               "c0": int(field_numpy(b["c0"])[0]), "rounds": field_numpy(self.rounds),
+               "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
+        if b["Z"] is not None:
+            out["Z"] = b["Z"].cpu().numpy()
+        return out
 
 
 class MultiMatmulProver(_Prover):
@@ -665,13 +693,15 @@ def can_overlap(cfg) -> bool:
     return can_pipeline(cfg) and cfg.matmuls[0].d_in % 16 == 0
 
 
-def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, overlapped: bool = False):
+def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, overlapped: bool = False,
+                keep_z: bool = False):
     """overlapped: three proofs in flight (OverlappedLayerProver), for single
-    layers with packed weights; pipelined: two (SingleLayerProver)."""
+    layers with packed weights (keep_z: also write Z); pipelined: two
+    (SingleLayerProver)."""
     if cfg.kind == "single":
         m = cfg.matmuls[0]
         if overlapped:
-            return OverlappedLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev)
+            return OverlappedLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, keep_z=keep_z)
         return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, pipelined=pipelined)
     if pipelined:
         raise ValueError("pipelined proofs are implemented for single-matmul layers")
