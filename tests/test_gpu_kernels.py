@@ -417,6 +417,31 @@ def test_witness_packed_extremes_strided_and_no_z(fp):
     assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr)
 
 
+def test_witness_rescale_at_the_int32_limit(fp):
+    """The rescale forms Z + 2^(s-1) in int32 before its shift: with d_in at its largest (131071 for the row-major
+    kernel, 131056 = the largest multiple of 16 for the packed one) and every product 128 * 128, |Z| is within
+    2^14 of 2^31, and every s in [1, 8] must still match the oracle's floor division."""
+    for d_in, kinds in ((131056, (True, False)), (131071, (False,))):
+        X = np.full((3, d_in), -128, np.int8)
+        X[1] = 127
+        X[2, ::2] = 5
+        W = np.full((5, d_in), -128, np.int8)
+        W[1] = 127
+        W[3, 1::3] = -7
+        Wp = fp.pack_weights(_dev(W)) if True in kinds else None
+        for s in (1, 2, 7, 8):
+            wz, wy, wr = O.witness(X, W, s)
+            assert int(np.abs(wz.astype(np.int64)).max()) == 128 * 128 * d_in
+            for packed in kinds:
+                if packed:
+                    Z, Y, R = fp.witness_linear_packed(_dev(X), Wp, s)
+                else:
+                    Z, Y, R = fp.witness_linear(_dev(X), _dev(W), s)
+                torch.cuda.synchronize()
+                assert np.array_equal(Z.cpu().numpy(), wz), (d_in, s, packed)
+                assert np.array_equal(Y.cpu().numpy(), wy) and np.array_equal(R.cpu().numpy(), wr), (d_in, s, packed)
+
+
 @pytest.mark.parametrize("T,d_out", [(200, 260), (0, 64)])
 def test_witness_packed_with_eq_tables(fp, T, d_out):
     """eq tables built by spare workgroups of the packed witness launch (one per 256 x 2^min(n - 8, 6) entries)

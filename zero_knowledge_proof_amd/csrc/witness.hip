@@ -98,13 +98,21 @@ __device__ __forceinline__ int xcd_tile(int bid, int nb) {
   return start + li;
 }
 
-__device__ __forceinline__ void rescale(int32_t z, int s, int32_t lowmask, uint32_t& y, uint32_t& r) {
-  const int32_t bit = (z >> (s - 1)) & 1;
-  const int32_t q = (z >> s) + bit;
-  const int32_t rr = (z & lowmask) - (bit << s);
-  const int32_t yy = q < -128 ? -128 : (q > 127 ? 127 : q);
-  y = (uint32_t)(uint8_t)(int8_t)yy;
-  r = (uint32_t)(uint8_t)(int8_t)rr;
+// Q = floor((z + 2^(s-1)) / 2^s) by an arithmetic shift, R = z - 2^s Q, Y = Q
+// clamped to int8. The sum cannot overflow: |z| <= 2^14 d_in <= 2^31 - 2^14
+// (d_in <= FP_MAX_DIN) and 2^(s-1) <= 128 (s in [1, 8]). Results in the low
+// byte (the packing keeps only that byte).
+__device__ __forceinline__ void rescale(int32_t z, int s, int32_t& y, int32_t& r) {
+  const int32_t q = (z + (1 << (s - 1))) >> s;
+  r = z - (q << s);
+  y = q < -128 ? -128 : (q > 127 ? 127 : q);
+}
+
+// Low bytes of a, b, c, d as one dword (byte 0 = a).
+__device__ __forceinline__ uint32_t pack_low_bytes(int32_t a, int32_t b, int32_t c, int32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);  // a0 b0 0 0
+  const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0c0c0400u);  // c0 d0 0 0
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // One 32x32 accumulator fragment as 16 consecutive outputs per lane: lanes
@@ -132,16 +140,16 @@ __device__ __forceinline__ void fragment_outputs(const v16i& accv, int32_t (&z)[
 
 // Y, R (and Z unless NULL) of 16 consecutive outputs o0.. of token t, held by one
 // lane after the swap; the caller has checked t < T and o0 < N.
-__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s,
-                                               int32_t lowmask) {
+__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s) {
   const int64_t idx = (int64_t)t * a.N + o0;
-  uint32_t yw[4] = {0, 0, 0, 0}, rw[4] = {0, 0, 0, 0};
+  uint32_t yw[4], rw[4];
+  int32_t y[16], r[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    uint32_t y, r;
-    rescale(z[q], s, lowmask, y, r);
-    yw[q >> 2] |= y << (8 * (q & 3));
-    rw[q >> 2] |= r << (8 * (q & 3));
+  for (int q = 0; q < 16; ++q) rescale(z[q], s, y[q], r[q]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    yw[g] = pack_low_bytes(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]);
+    rw[g] = pack_low_bytes(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
   }
   if (o0 + 16 <= a.N) {
     if (a.Z) {
@@ -330,7 +338,6 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
 
   // ---- epilogue: 16 consecutive outputs per lane, rescale, clamp, remainder
   const int s = a.s;
-  const int32_t lowmask = (1 << s) - 1;
   const int h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -359,7 +366,7 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
         }
         continue;
       }
-      store_fragment(a, z, t, o0, s, lowmask);
+      store_fragment(a, z, t, o0, s);
     }
   }
 }
@@ -425,34 +432,32 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
 // the 7-bit limbs of E_o (CL_LIMBS per element, rows 0..9 of the A operand)
 // against the four byte planes of Z (the B operand: after the swap a lane
 // holds 16 consecutive outputs of one token, which is the operand's layout
-// with the outputs as k). Planes 0-2 are unsigned bytes, fed as b - 128 with
-// 128 times the limb sums (one more product, against ones) added back; plane
-// 3 is Z's signed top byte. Row m of the products, weighted 2^(7m + 8p), then
-// gives sum_o E_o[o] Z[t, o] for the lane's token t, which E_t[t] weights.
+// with the outputs as k). Planes 0-2 are unsigned bytes, fed as b - 128;
+// plane 3 is Z's signed top byte. Row m of the products, weighted
+// 2^(7m + 8p), plus the offsets' share, then gives sum_o E_o[o] Z[t, o] for
+// the lane's token t, which E_t[t] weights.
 constexpr int CL_LIMBS = 10;
 
-// Lane (t, h) of plane products D[p] and of the limb sums L: register v holds
-// row m = 8 (v / 4) + 4 h + v % 4; rows below CL_LIMBS carry limbs (v < 4 for
-// both halves, v = 4, 5 for h = 0). Returns sum_m 2^(7m) (sum_p 2^(8p) D_p[m]
-// + 128 (1 + 2^8 + 2^16) L[m]) mod p.
-__device__ __forceinline__ uint64_t claim_row_value(const v16i (&D)[4], const int64_t (&corr)[6], int h) {
-  // p 2^48 keeps the 128-bit sum positive (|sum| < 2^112)
-  uint64_t lo = 1ull << 48, hi = (1ull << 48) - (1ull << 16);
-#pragma unroll
-  for (int v = 0; v < 6; ++v) {
-    if (v >= 4 && h != 0) continue;
-    const int m = (v < 4 ? v : v + 4) + 4 * h;
+// Lane (t, h) of the plane products D[p]: register v holds row m = 8 (v / 4)
+// + 4 h + v % 4; rows below CL_LIMBS carry limbs (v < 4 for both halves,
+// v = 4, 5 for h = 0). Returns sum_m 2^(7m) sum_p 2^(8p) D_p[m] mod p (the
+// offsets of planes 0-2 are added back per wave: sum_m 2^(7m) 128 (1 + 2^8 +
+// 2^16) sum_o limb_m(E_o[o]) is 128 * 65793 * sum_o E_o[o]).
+__device__ __forceinline__ uint64_t claim_row_value(const v16i (&D)[4], int h) {
+  // sum_p 2^(8p) D_p for register v, |.| < 2^46
+  auto rowsum = [&](int v) -> __int128 {
     const int32_t s01 = D[0][v] + (D[1][v] << 8);  // |D| < 2^21: exact in 32 bits
     const int32_t s23 = D[2][v] + (D[3][v] << 8);
-    const int64_t sv = (int64_t)s01 + ((int64_t)s23 << 16) + corr[v];
-    const int sh = 7 * m;
-    const uint64_t plo = (uint64_t)sv << sh;
-    const uint64_t phi = sh == 0 ? (uint64_t)(sv >> 63) : (uint64_t)(sv >> (64 - sh));
-    const uint64_t nlo = lo + plo;
-    hi += phi + (nlo < lo ? 1 : 0);
-    lo = nlo;
-  }
-  return gl::reduce128(lo, hi);
+    return (__int128)((int64_t)s01 + ((int64_t)s23 << 16));
+  };
+  // registers 0-3 hold rows v + 4h: scale by 2^(7v), then by 2^28 in the upper half
+  __int128 x = rowsum(0) + (rowsum(1) << 7) + (rowsum(2) << 14) + (rowsum(3) << 21);
+  x = h ? (x << 28) : x;
+  // registers 4, 5 hold rows 8, 9 (h = 0; rows 12, 13 of the upper half are zero)
+  x += (rowsum(4) << 56) + (rowsum(5) << 63);
+  // p 2^48 keeps the sum positive (|x| < 2^110)
+  const unsigned __int128 y = (unsigned __int128)x + ((unsigned __int128)0xFFFFFFFF00000001ull << 48);
+  return gl::reduce128((uint64_t)y, (uint64_t)(y >> 64));
 }
 
 // The wave's claim value to its slot; the last tile to arrive adds them all.
@@ -488,9 +493,9 @@ struct WsCfg {
   static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
   static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32, HB = BK / 2;
   // the epilogue stages each wave's 32x32 int32 fragments in rows of EP words;
-  // the claim's limb table [CL_LIMBS][BO] and reduction words follow
+  // the claim's limb table [CL_LIMBS][BO], the tile's E_t and reduction words follow
   static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
-  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 16 * 8;
+  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8;
   static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
   static constexpr int LDS_BYTES = 2 * BT * PITCH > EPI_BYTES ? 2 * BT * PITCH : EPI_BYTES;
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
@@ -594,7 +599,6 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   }
 
   const int s = a.s;
-  const int32_t lowmask = (1 << s) - 1;
   // Z leaves through LDS: a lane's fragment holds 16 outputs of one token,
   // so direct stores write 32-byte pieces of 32 rows; staged, eight lanes
   // write a row's whole 128 bytes.
@@ -603,30 +607,38 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   if (stage || claim) __syncthreads();  // every wave is done with the X tiles
   int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
   uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::STAGE_BYTES;
-  uint64_t* red = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);
+  uint64_t* etl = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);  // E_t of the tile's tokens
+  uint64_t* red = etl + BT;
   v4i Aop[TM];
-  int64_t corr[6];
+  uint64_t corr = 0;  // the planes' offsets, added once per token (by the h = 0 lanes)
   if (claim) {
+    for (int x = tid; x < BT; x += NT) {
+      const int t = t_base + x;
+      etl[x] = t < a.T ? a.cEt[t] : 0;
+    }
     // limb table of the tile's outputs (zero past d_out, so rows of Z there,
     // computed from clamped weight blocks, do not count)
+    uint64_t se = 0;
     for (int x = tid; x < BO; x += NT) {
       const int o = o_base + x;
       const uint64_t e = o < a.N ? a.cEo[o] : 0;
 #pragma unroll
       for (int m = 0; m < CL_LIMBS; ++m) limbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
+      if constexpr (BO == NT) se = e;  // output tid is lane tid % 64 of its wave's range
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       Aop[i] = r < CL_LIMBS ? *(const v4i*)&limbs[r * BO + wo0 + 32 * i + 16 * h] : v4i{0, 0, 0, 0};
-    v16i L;
+    if constexpr (BO != NT) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) L[v] = 0;
-    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-#pragma unroll
-    for (int i = 0; i < TM; ++i) L = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], ones, L, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 6; ++v) corr[v] = (int64_t)L[v] * (128 * 65793);
+      for (int x = lane; x < 32 * TM; x += 64) {
+        const int o = o_base + wo0 + x;
+        if (o < a.N) se = gl::add(se, a.cEo[o]);
+      }
+    }
+    se = fpi::wave_total(se);  // every lane takes part (outside the lane-dependent select below)
+    corr = h == 0 ? gl::mul_small(se, 128u * 65793u) : 0;
   }
   WitArgs yr = a;
   if (stage) yr.Z = nullptr;
@@ -635,16 +647,12 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   for (int j = 0; j < TN; ++j) {
     v16i D[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) D[p][v] = 0;
-#pragma unroll
     for (int i = 0; i < TM; ++i) {
       int32_t z[16];
       fragment_outputs(acc[i][j], z);
       const int t = t_base + 32 * j + r;
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
-      if (t < a.T && o0 < a.N) store_fragment(yr, z, t, o0, s, lowmask);
+      if (t < a.T && o0 < a.N) store_fragment(yr, z, t, o0, s);
       if (stage) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -671,14 +679,13 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
           P[2][g] = (int)(w2 ^ 0x80808080u);
           P[3][g] = (int)w3;
         }
+        const v16i zero = {};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) D[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], P[p], D[p], 0, 0, 0);
+        for (int p = 0; p < 4; ++p)
+          D[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], P[p], i == 0 ? zero : D[p], 0, 0, 0);
       }
     }
-    if (claim) {
-      const int t = t_base + 32 * j + r;
-      wsum = gl::add(wsum, gl::mul(claim_row_value(D, corr, h), t < a.T ? a.cEt[t] : 0));
-    }
+    if (claim) wsum = gl::add(wsum, gl::mul(gl::add(claim_row_value(D, h), corr), etl[32 * j + r]));
   }
   if (claim) claim_arrive(a, wsum, bid, nblocks, NW, red, reinterpret_cast<uint32_t*>(red + 8));
 }
