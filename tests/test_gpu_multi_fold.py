@@ -2,7 +2,8 @@
 fp_fold_weights_prepare against the transpose and column sums it defines,
 fp_fold_matrix_multi against the oracle's request vectors, bit-exact, over
 ragged shapes, split reductions, extreme weights and eq entries, strided
-operands, the empty cases, and the up-projection's full weight matrix."""
+operands, the empty cases, and the up-projection's full weight matrix, on both
+of its kernels (row-major digit rows below 16 requests, packed from 16 on)."""
 import numpy as np
 import pytest
 import torch
@@ -43,9 +44,10 @@ def test_fold_weights_prepare(fp, rows, cols):
     assert np.array_equal(c.cpu().numpy(), M.astype(np.int64).sum(0))
 
 
-MULTI = [  # rows, cols, cols_pad, R
+MULTI = [  # rows, cols, cols_pad, R (from 16 requests on the digit rows go through the packed-weight kernel)
     (1, 1, 1, 1), (3, 5, 8, 2), (17, 37, 64, 3), (300, 256, 256, 1), (1000, 300, 512, 8), (2500, 1030, 2048, 5),
     (1025, 257, 512, 64), (4096, 640, 1024, 64), (4097, 100, 128, 33), (70000, 64, 64, 1), (20, 2049, 4096, 70),
+    (100, 96, 128, 15), (70000, 130, 256, 16),
 ]
 
 

@@ -85,6 +85,36 @@ __global__ __launch_bounds__(256) void digits_kernel(const uint64_t* __restrict_
   }
 }
 
+// The same digits in the packed-weight layout: fragment (b, c, q) of 1 KiB at
+// ((b nkb + c) 2 + q) 1024, lane u holding row 32 b + u % 32 at k = 64 c +
+// 32 (u / 32) + 16 q + 0..15; zero past `rows` and for rows past 8 R (the
+// rest of the last 32-row block). One wave per fragment, so each wave writes
+// its 1 KiB in one piece; the 8 lanes of a request's limbs read the same 16
+// weights (from L1 after the first).
+__global__ __launch_bounds__(256) void digits_packed_kernel(const uint64_t* __restrict__ E, int64_t lde, int32_t rows,
+                                                            int32_t R, int32_t nrb, int32_t nkb,
+                                                            int8_t* __restrict__ Dp) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t f = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (f >= (int64_t)nrb * nkb * 2) return;
+  const int u = threadIdx.x & 63;
+  const int qq = (int)(f & 1);
+  const int64_t bc = f >> 1;
+  const int c = (int)(bc % nkb);
+  const int64_t row = 32 * (bc / nkb) + (u & 31);
+  const int64_t j = row >> 3;
+  const int l = (int)(row & 7);
+  const int k0 = 64 * c + 32 * (u >> 5) + 16 * qq;
+  uint32_t w[4] = {0, 0, 0, 0};
+  if (j < R) {
+    const uint64_t* e = E + j * lde;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (k0 + i < rows) w[i >> 2] |= ((((uint32_t)(e[k0 + i] >> (8 * l))) & 0xFF) ^ 0x80u) << (8 * (i & 3));  // byte - 128
+  }
+  *(u32x4*)(Dp + f * 1024 + u * 16) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // out[j, k] = sum_s part[s][j, k] for k0 <= k < cols (nothing added when
 // nsum = 0), and 0 for cols <= k < cols_pad.
 __global__ __launch_bounds__(256) void finish_kernel(const uint64_t* __restrict__ part, int64_t psplit, int32_t nsum,
@@ -104,16 +134,24 @@ __global__ __launch_bounds__(256) void finish_kernel(const uint64_t* __restrict_
 
 struct Layout {
   fpi::SplitK p;
-  int64_t ldA;      // digit matrix leading dimension (bytes)
+  bool packed;      // digit rows in the packed-weight layout (the packed-weight kernel)
+  int64_t ldA;      // row-major digit matrix leading dimension (bytes)
   size_t a_bytes;   // digit matrix
   size_t z_bytes;   // field values of the reduction chunks (none without a split)
 };
 
+// From 16 requests (128 digit rows) on, the digit rows fill the packed-weight
+// kernel's 256-row tiles well enough for its faster loop; fewer stay on the
+// row-major kernel's 128-row tiles.
+constexpr int32_t PACKED_MIN_R = 16;
+
 Layout layout(int32_t rows, int32_t cols, int32_t R) {
   Layout L{};
-  L.p = fpi::splitk_plan(cols, rows, 8 * R);
+  L.packed = R >= PACKED_MIN_R;
+  L.p = L.packed ? fpi::splitk_plan_packed(cols, rows, 8 * R) : fpi::splitk_plan(cols, rows, 8 * R);
   L.ldA = (int64_t)fpi::align_up((size_t)(rows > 0 ? rows : 1), 16);
-  L.a_bytes = fpi::align_up((size_t)(8 * (int64_t)R) * (size_t)L.ldA, 256);
+  L.a_bytes = L.packed ? fpi::align_up(fpi::packed_rows_bytes(8 * R, rows > 0 ? rows : 1), 256)
+                       : fpi::align_up((size_t)(8 * (int64_t)R) * (size_t)L.ldA, 256);
   L.z_bytes = L.p.ksplit > 1 ? fpi::align_up((size_t)L.p.ksplit * (size_t)R * (size_t)cols * 8, 256) : 0;
   return L;
 }
@@ -175,19 +213,33 @@ extern "C" int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t
       return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, L.a_bytes + L.z_bytes);
     if (((uintptr_t)ws) & 255) return fpi::fail(FP_EARG, "%s: workspace must be 256-byte aligned", fn);
     int8_t* A = (int8_t*)ws;
-    const int64_t threads = (int64_t)R * (L.ldA / 4);
-    hipLaunchKernelGGL(digits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, E, lde, rows, R,
-                       A, L.ldA);
-    int rc = fpi::check_launch("digits_kernel");
+    int rc;
+    if (L.packed) {
+      const int32_t nkb = (rows + fpi::PACK_BK - 1) / fpi::PACK_BK;
+      const int32_t nrb = (8 * R + 31) / 32;
+      const int64_t frags = (int64_t)nrb * nkb * 2;
+      hipLaunchKernelGGL(digits_packed_kernel, dim3((unsigned)((frags + 3) / 4)), dim3(256), 0, stream, E, lde, rows, R,
+                         nrb, nkb, A);
+      rc = fpi::check_launch("digits_packed_kernel");
+    } else {
+      const int64_t threads = (int64_t)R * (L.ldA / 4);
+      hipLaunchKernelGGL(digits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, E, lde, rows,
+                         R, A, L.ldA);
+      rc = fpi::check_launch("digits_kernel");
+    }
     if (rc) return rc;
+    auto gemm_into = [&](uint64_t* dst, int64_t ldp, int64_t ps) {
+      return L.packed ? fpi::witness_fold_splitk_packed(Mt, ldt, A, cols, rows, 8 * R, colsum, L.p, dst, ldp, ps, stream)
+                      : fpi::witness_fold_splitk(Mt, ldt, A, L.ldA, cols, rows, 8 * R, colsum, L.p, dst, ldp, ps, stream);
+    };
     if (L.p.ksplit > 1) {  // chunks into the workspace, added below
       part = (uint64_t*)((char*)ws + L.a_bytes);
       psplit = (int64_t)R * cols;
       nsum = L.p.ksplit;
-      rc = fpi::witness_fold_splitk(Mt, ldt, A, L.ldA, cols, rows, 8 * R, colsum, L.p, part, cols, psplit, stream);
+      rc = gemm_into(part, cols, psplit);
     } else {  // straight into out; only the padding is left
       k0 = cols;
-      rc = fpi::witness_fold_splitk(Mt, ldt, A, L.ldA, cols, rows, 8 * R, colsum, L.p, out, ldo, 0, stream);
+      rc = gemm_into(out, ldo, 0);
     }
     if (rc) return rc;
   }

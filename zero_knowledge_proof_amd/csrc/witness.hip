@@ -183,6 +183,25 @@ __device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (
   }
 }
 
+// Limb-fold epilogue: a lane's 16 outputs o0.. of token t are the byte limbs
+// l = 0..7 of digit-row group o0 / 8 (z[0..7]) and of the next group
+// (z[8..15]); the group's value sum_l 2^(8l) z[l] is exact as L + 2^32 H with
+// |L|, |H| < 2^55, then reduced, plus the digits' offset term in chunk 0.
+__device__ __forceinline__ void limb_fold_store(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int ks) {
+  uint64_t cterm = 0;
+  if (ks == 0) cterm = gl::mul(gl::from_i64(128 * (int64_t)a.colsum[t]), 0x0101010101010101ull);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int o = o0 + 8 * g;
+    if (o >= a.N) break;
+    const int32_t* zz = z + 8 * g;
+    const int64_t L = (int64_t)zz[0] + (int64_t)zz[1] * 256 + (int64_t)zz[2] * 65536 + (int64_t)zz[3] * 16777216;
+    const int64_t H = (int64_t)zz[4] + (int64_t)zz[5] * 256 + (int64_t)zz[6] * 65536 + (int64_t)zz[7] * 16777216;
+    const uint64_t v = gl::add(gl::from_i64(L), gl::mul(gl::from_i64(H), 1ull << 32));
+    a.part[(int64_t)ks * a.psplit + (int64_t)(o >> 3) * a.ldp + t] = gl::add(v, cterm);
+  }
+}
+
 // LDS of one GEMM workgroup: double-buffered W and X tiles.
 template <int BO, int BT, int BK>
 struct WitLds {
@@ -349,21 +368,7 @@ __device__ __forceinline__ void witness_body(const WitArgs& a, const GroupTab& g
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
       if (t >= t_lim || o0 >= a.N) continue;
       if constexpr (EPI == 1) {
-        // z[0..7] are the byte limbs l = 0..7 of output group o0 / 8 at token t,
-        // z[8..15] those of the next group: value = sum_l 2^(8l) z[l], exact as
-        // L + 2^32 H with |L|, |H| < 2^55, then reduced.
-        uint64_t cterm = 0;
-        if (ks == 0) cterm = gl::mul(gl::from_i64(128 * (int64_t)a.colsum[t]), 0x0101010101010101ull);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int o = o0 + 8 * g;
-          if (o >= a.N) break;
-          const int32_t* zz = z + 8 * g;
-          const int64_t L = (int64_t)zz[0] + (int64_t)zz[1] * 256 + (int64_t)zz[2] * 65536 + (int64_t)zz[3] * 16777216;
-          const int64_t H = (int64_t)zz[4] + (int64_t)zz[5] * 256 + (int64_t)zz[6] * 65536 + (int64_t)zz[7] * 16777216;
-          uint64_t v = gl::add(gl::from_i64(L), gl::mul(gl::from_i64(H), 1ull << 32));
-          a.part[(int64_t)ks * a.psplit + (int64_t)(o >> 3) * a.ldp + t] = gl::add(v, cterm);
-        }
+        limb_fold_store(a, z, t, o0, ks);
         continue;
       }
       store_fragment(a, z, t, o0, s);
@@ -405,7 +410,7 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(
 // wave needs, and only X (shared by the workgroup's waves) passes through LDS:
 // half the LDS traffic per MFMA of the tile above, and the register copy of
 // each W byte is used against all of the workgroup's tokens.
-constexpr int WP_BK = 64;
+constexpr int WP_BK = fpi::PACK_BK;
 
 __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restrict__ W, int64_t ldw, int32_t N,
                                                            int32_t K, int32_t nrb, int32_t nkb, int vec,
@@ -501,13 +506,22 @@ struct WsCfg {
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
 };
 
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int nblocks, int8_t* lds) {
   using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
   constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
   constexpr int KS = C::KS, HB = C::HB;
   int8_t (*sB)[BT * PITCH] = reinterpret_cast<int8_t (*)[BT * PITCH]>(lds);
-  const int tile = xcd_tile(bid, nblocks);
+  int tile = xcd_tile(bid, nblocks);
+  int ks = 0;  // split K: workgroup (tile, ks) reduces over K blocks [kb0, kb0 + KT)
+  if (a.ksplit > 1) {
+    const int per = a.tiles_t * a.tiles_o;
+    ks = tile / per;
+    tile -= ks * per;
+  }
+  const int kb0 = a.ksplit > 1 ? ks * (a.kchunk / BK) : 0;
+  const int KT = a.ksplit > 1 ? min(a.kchunk / BK, a.wp_kb - kb0) : a.wp_kb;
+  const int klim = a.K - kb0 * BK;  // X columns left from the range's start
   const int tt = tile % a.tiles_t, to = tile / a.tiles_t;
   const int t_base = tt * BT, o_base = to * BO;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -516,14 +530,15 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   const int64_t rb_bytes = (int64_t)a.wp_kb * BK * 32;  // one 32-row block of the packed weights
   const int8_t* pw[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) pw[i] = a.W + (int64_t)min((o_base + wo0) / 32 + i, a.wp_rb - 1) * rb_bytes + lane * 16;
+  for (int i = 0; i < TM; ++i)
+    pw[i] = a.W + (int64_t)min((o_base + wo0) / 32 + i, a.wp_rb - 1) * rb_bytes + (int64_t)kb0 * (BK * 32) + lane * 16;
   const int8_t* px[CB];
   int kc[CB], so[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     const int ch = tid + c * NT, row = ch / CPR;
     kc[c] = (ch % CPR) * 16;
-    px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx;
+    px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx + (int64_t)kb0 * BK;
     so[c] = row * PITCH + kc[c];
   }
   v4i wf[PFW][TM][KS];
@@ -538,7 +553,7 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const int k = kblk * BK + kc[c];
-      xr[slot][c] = *(const v4i*)(px[c] + (k < a.K ? k : 0));
+      xr[slot][c] = *(const v4i*)(px[c] + (k < klim ? k : 0));
     }
   };
   auto sstore = [&](int slot, int buf) {
@@ -571,7 +586,6 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   // the other buffer and refill its slot with block s+1+PFX; one barrier.
   constexpr int L1 = (PFW % 2 == 0) ? PFW : 2 * PFW;
   constexpr int U = ((L1 % PFX == 0) ? L1 : L1 * PFX) * UNR;
-  const int KT = a.wp_kb;
   if (KT > 0) {  // d_in = 0: every output is 0
 #pragma unroll
     for (int p = 0; p < PFW; ++p) wload(p, min(p, KT - 1));
@@ -598,6 +612,19 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
     }(std::make_integer_sequence<int, U>{});
   }
 
+  if constexpr (EPI == 1) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        int32_t z[16];
+        fragment_outputs(acc[i][j], z);
+        const int t = t_base + 32 * j + r;
+        const int o0 = o_base + wo0 + 32 * i + 16 * h;
+        if (t < a.T && o0 < a.N) limb_fold_store(a, z, t, o0, ks);
+      }
+    return;
+  }
   const int s = a.s;
   // Z leaves through LDS: a lane's fragment holds 16 outputs of one token,
   // so direct stores write 32-byte pieces of 32 rows; staged, eight lanes
@@ -724,8 +751,9 @@ __device__ __forceinline__ void eq_aux_block(const EqAux& eq, int b) {
 }
 
 // Workgroups [0, n_tail): sum-check tails (as witness_sc_kernel); the next
-// eq.block_start[eq.count]: eq tables; the rest: GEMM tiles.
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+// eq.block_start[eq.count]: eq tables; the rest: GEMM tiles (times the K
+// split). EPI 1: the limb-fold epilogue instead of the rescale.
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_kernel(
     WitArgs a, sct::TailArgs ta, int n_tail, EqAux eq) {
   constexpr int NT = NW * 64;
@@ -744,21 +772,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     eq_aux_block(eq, b);
     return;
   }
-  witness_body_ws<NW, TM, TN, PFW, PFX, UNR>(a, b - n_eq, gridDim.x - n_tail - n_eq, lds);
+  witness_body_ws<NW, TM, TN, PFW, PFX, UNR, EPI>(a, b - n_eq, gridDim.x - n_tail - n_eq, lds);
 }
 
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR>
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, hipStream_t st) {
   using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
   a.tiles_t = (a.T + C::BT - 1) / C::BT;
   a.tiles_o = (a.N + C::BO - 1) / C::BO;
-  const int64_t tiles = (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o : 0;
+  const int64_t tiles =
+      (a.T > 0 && a.N > 0) ? (int64_t)a.tiles_t * a.tiles_o * (a.ksplit > 1 ? a.ksplit : 1) : 0;
   const int64_t total = tiles + n_tail + eq.block_start[eq.count];
   if (total > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
   if (total == 0) return FP_OK;
   sct::TailArgs none{};
-  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR>), dim3((unsigned)total), dim3(C::NT), 0, st, a,
-                     ta ? *ta : none, n_tail, eq);
+  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR, EPI>), dim3((unsigned)total), dim3(C::NT), 0, st,
+                     a, ta ? *ta : none, n_tail, eq);
   return fpi::check_launch("witness_ws_kernel");
 }
 
@@ -1046,6 +1075,39 @@ int witness_fold_splitk(const int8_t* Xt, int64_t ldx, const int8_t* D, int64_t 
   a.vecW = ((ldd & 15) == 0) && ((((uintptr_t)D) & 15) == 0);
   GroupTab gt{};
   return launch<WIT_M, 1>(a, gt, st);
+}
+
+// The packed-weight kernel's 256x128 tiles (digit rows x columns of Xt), the
+// reduction split so that there is about one workgroup per compute unit.
+SplitK splitk_plan_packed(int32_t T, int32_t K, int32_t N) {
+  SplitK p{};
+  const int64_t tiles = (int64_t)((T + 127) / 128) * ((N + 255) / 256);
+  int64_t want = tiles > 0 ? (256 + tiles - 1) / tiles : 1;
+  const int64_t kb = ((int64_t)K + WP_BK - 1) / WP_BK;  // K blocks
+  if (want > kb) want = kb > 0 ? kb : 1;
+  int64_t chunk = (kb + want - 1) / want * WP_BK;
+  if (chunk > SPLITK_MAX_CHUNK) chunk = SPLITK_MAX_CHUNK;
+  p.kchunk = (int32_t)chunk;
+  p.ksplit = (int32_t)(K > 0 ? ((int64_t)K + chunk - 1) / chunk : 1);
+  return p;
+}
+
+size_t packed_rows_bytes(int32_t N, int32_t K) {
+  return (size_t)((N + 31) / 32) * 32 * (size_t)((K + WP_BK - 1) / WP_BK) * WP_BK;
+}
+
+int witness_fold_splitk_packed(const int8_t* Xt, int64_t ldx, const int8_t* Dp, int32_t T, int32_t K, int32_t N,
+                               const int32_t* colsum, const SplitK& p, uint64_t* part, int64_t ldp, int64_t psplit,
+                               hipStream_t st) {
+  WitArgs a{};
+  a.X = Xt; a.ldx = ldx; a.W = Dp; a.ldw = 0;
+  a.T = T; a.N = N; a.K = K; a.s = 1;
+  a.wp_rb = (N + 31) / 32;
+  a.wp_kb = (K + WP_BK - 1) / WP_BK;
+  a.ksplit = p.ksplit; a.kchunk = p.kchunk;
+  a.colsum = colsum; a.part = part; a.ldp = ldp; a.psplit = psplit;
+  vec_flags(a);
+  return launch_ws<WIT_WS_L, 1>(a, nullptr, 0, EqAux{}, st);
 }
 
 }  // namespace fpi
