@@ -165,11 +165,9 @@ def cpu_baseline(cfg, inp, ch, one_core: bool = True) -> dict:
 def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, R: int = 64) -> dict:
     """Request vectors of a batch: the first weight matrix of the workload
     folded by R requests' eq vectors (points drawn like the layer's r_o) in one
-    fp_fold_matrix_multi_blocked call (from the K-blocked copy prepared once per
-    matrix; the call from the plain transpose is timed beside it), against the
-    same R folds done one matrix pass each (fp_fold_matrix_batched). Inputs and
-    the prepared copies are resident before timing; each is timed as per_graph
-    calls in one HIP graph."""
+    fp_fold_matrix_multi call, against the same R folds done one matrix pass
+    each (fp_fold_matrix_batched). Inputs and the prepared transpose are
+    resident before timing; each is timed as per_graph calls in one HIP graph."""
     import numpy as np
     import torch
 
@@ -188,9 +186,8 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    Mb, c = fp.fold_weights_prepare_blocked(W)  # the K-blocked copy the call reads
+    Mt, c = fp.fold_weights_prepare(W)
     t1.record(stream)
-    Mt, _ = fp.fold_weights_prepare(W)  # the plain transpose, for comparison
     out = torch.empty((R, cols), dtype=torch.int64, device=dev)
     outs1 = [torch.empty(cols, dtype=torch.int64, device=dev) for _ in range(R)]
     jobs = [(W, E[j], cols, outs1[j]) for j in range(R)]
@@ -212,12 +209,9 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * per_graph) * 1e-3
 
-    out_t = torch.empty_like(out)
-    t_plain = timed(lambda: fp.fold_matrix_multi(Mt, c, rows, E, cols, out=out_t))
-    t_multi = timed(lambda: fp.fold_matrix_multi(Mb, c, rows, E, cols, out=out))
-    del Mt
+    t_multi = timed(lambda: fp.fold_matrix_multi(Mt, c, rows, E, cols, out=out))
     t_single = timed(lambda: fp.fold_matrix_batched(jobs))
-    same = all(torch.equal(outs1[j], out[j]) for j in range(R)) and torch.equal(out_t, out)
+    same = all(torch.equal(outs1[j], out[j]) for j in range(R))
     ops = 2 * 8 * R * rows * cols
     res = {
         "workload": "%s weights [%d x %d] (int8), %d requests' eq vectors over its %d rows" % (m.name, rows, cols, R,
@@ -226,7 +220,6 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
         "one_pass_per_request_ms": round(t_single * 1e3, 5), "speedup": round(t_single / t_multi, 2),
         "outputs_equal_one_pass_per_request": bool(same),
         "prepare_ms_once_per_matrix": round(t0.elapsed_time(t1), 4),
-        "from_plain_transpose_ms": round(t_plain * 1e3, 5),
         "roofline": {"bound": "mfma", "achieved": round(ops / t_multi / 1e12, 1), "peak": MFMA_I8_PEAK / 1e12,
                      "unit": "TFLOP/s", "frac": round(ops / t_multi / MFMA_I8_PEAK, 4),
                      "traffic": None, "algorithmic_ops": ops,

@@ -219,24 +219,6 @@ int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t* colsum, i
                          size_t ws_bytes, hipStream_t stream);
 size_t fp_fold_matrix_multi_workspace(int32_t rows, int32_t cols, int32_t R);
 
-/* The same folds from a K-blocked copy of M, which the matrix product reads as
- * one contiguous piece per tile and reduction step instead of 64-byte pieces of
- * Mt's rows. fp_fold_weights_prepare_blocked writes, once per matrix, Mb with
- * Mb[(c*cols + k)*64 + i] = M[64c + i, k] for c < ceil(rows/64) (0 where
- * 64c + i >= rows): fp_fold_weights_blocked_bytes(rows, cols) bytes, 16-byte
- * aligned; and colsum as fp_fold_weights_prepare does. M has leading dim
- * ld >= cols. fp_fold_matrix_multi_blocked takes Mb in place of Mt and
- * writes exactly what fp_fold_matrix_multi writes, under the same conditions;
- * ws: fp_fold_matrix_multi_blocked_workspace(rows, cols, R) bytes, 256-byte
- * aligned. */
-size_t fp_fold_weights_blocked_bytes(int32_t rows, int32_t cols);
-int fp_fold_weights_prepare_blocked(const int8_t* M, int64_t ld, int32_t rows, int32_t cols, int8_t* Mb,
-                                    int32_t* colsum, hipStream_t stream);
-int fp_fold_matrix_multi_blocked(const int8_t* Mb, const int32_t* colsum, int32_t rows, int32_t cols, int32_t R,
-                                 const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo, int32_t cols_pad, void* ws,
-                                 size_t ws_bytes, hipStream_t stream);
-size_t fp_fold_matrix_multi_blocked_workspace(int32_t rows, int32_t cols, int32_t R);
-
 /* ---------------------------------------------------------- commitment --- */
 /* Commitment of committed tables such as Y and R ("How fast can FlashProve
  * go", §3.1: values are cut into 8-bit limbs packed three to a field element in

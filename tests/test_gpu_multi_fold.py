@@ -3,8 +3,7 @@ fp_fold_weights_prepare against the transpose and column sums it defines,
 fp_fold_matrix_multi against the oracle's request vectors, bit-exact, over
 ragged shapes, split reductions, extreme weights and eq entries, strided
 operands, the empty cases, and the up-projection's full weight matrix, on both
-of its kernels (row-major digit rows below 16 requests, packed from 16 on) and
-from the K-blocked copy of fp_fold_weights_prepare_blocked."""
+of its kernels (row-major digit rows below 16 requests, packed from 16 on)."""
 import numpy as np
 import pytest
 import torch
@@ -52,25 +51,8 @@ MULTI = [  # rows, cols, cols_pad, R (from 16 requests on the digit rows go thro
 ]
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (17, 37), (300, 256), (1000, 333), (70, 4100), (0, 9)])
-def test_fold_weights_prepare_blocked(fp, rows, cols):
-    """The K-blocked copy against its definition Mb[(c cols + k) 64 + i] = M[64 c + i, k] (zero past rows), built
-    in numpy, and the column sums."""
-    rng = _rng(rows * 3 + cols)
-    M = rng.integers(-128, 128, size=(rows, cols), dtype=np.int8)
-    Mb, c = fp.fold_weights_prepare_blocked(_dev(M))
-    torch.cuda.synchronize()
-    nkb = (rows + 63) // 64
-    Mpad = np.zeros((nkb * 64, cols), np.int8)
-    Mpad[:rows] = M
-    want = Mpad.reshape(nkb, 64, cols).transpose(0, 2, 1).reshape(-1)
-    assert np.array_equal(Mb.data.cpu().numpy()[: want.size], want)
-    assert np.array_equal(c.cpu().numpy(), M.astype(np.int64).sum(axis=0))
-
-
-@pytest.mark.parametrize("blocked", [False, True])
 @pytest.mark.parametrize("rows,cols,cols_pad,R", MULTI)
-def test_fold_multi(fp, rows, cols, cols_pad, R, blocked):
+def test_fold_multi(fp, rows, cols, cols_pad, R):
     rng = _rng(rows * 13 + cols * 7 + R)
     M = rng.integers(-128, 128, size=(rows, cols), dtype=np.int8)
     M.flat[: min(5, M.size)] = [-128, 127, -128, 127, 0][: min(5, M.size)]
@@ -78,7 +60,7 @@ def test_fold_multi(fp, rows, cols, cols_pad, R, blocked):
     Es[0][: min(3, rows)] = [P - 1, 0, 1][: min(3, rows)]  # bytes 0xFF.. and 0x00..
     if R > 1:
         Es[1][:] = P - 1
-    Mt, c = fp.fold_weights_prepare_blocked(_dev(M)) if blocked else fp.fold_weights_prepare(_dev(M))
+    Mt, c = fp.fold_weights_prepare(_dev(M))
     out = fp.fold_matrix_multi(Mt, c, rows, _fields(fp, np.stack(Es)), cols_pad)
     torch.cuda.synchronize()
     got = fp.field_numpy(out)
@@ -128,15 +110,14 @@ def test_fold_multi_empty(fp):
     del M
 
 
-@pytest.mark.parametrize("blocked", [False, True])
-def test_fold_multi_full_up_projection(fp, blocked):
+def test_fold_multi_full_up_projection(fp):
     # the up-projection's weights [14336, 4096] folded by 64 requests' eq vectors
     rows, cols, R = 14336, 4096, 64
     g = torch.Generator(device="cuda").manual_seed(17)
     W = torch.randint(-128, 128, (rows, cols), dtype=torch.int8, device="cuda", generator=g)
     rng = _rng(18)
     Es = [O.eq_table([int(v) for v in synth.challenges(500 + j, 14)])[:rows] for j in range(R)]
-    Mt, c = fp.fold_weights_prepare_blocked(W) if blocked else fp.fold_weights_prepare(W)
+    Mt, c = fp.fold_weights_prepare(W)
     out = fp.fold_matrix_multi(Mt, c, rows, _fields(fp, np.stack(Es)), cols)
     torch.cuda.synchronize()
     got = fp.field_numpy(out)

@@ -26,8 +26,7 @@ EXPORTS = [
     "fp_sumcheck_prove_multi", "fp_combine_claims", "fp_claim_eval_batched", "fp_claim_eval_batched_workspace",
     "fp_linear_combine", "fp_fold_claim_batched", "fp_fold_claim_batched_workspace",
     "fp_witness_linear_with_sumcheck", "fp_fold_weights_prepare", "fp_fold_matrix_multi",
-    "fp_fold_matrix_multi_workspace", "fp_fold_weights_blocked_bytes", "fp_fold_weights_prepare_blocked",
-    "fp_fold_matrix_multi_blocked", "fp_fold_matrix_multi_blocked_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
+    "fp_fold_matrix_multi_workspace", "fp_commit_pack", "fp_rs_encode", "fp_rs_encode_workspace",
     "fp_merkle_commit", "fp_lookup_tree", "fp_lookup_counts", "fp_sumcheck3_prove", "fp_sumcheck3_workspace",
     "fp_lookup_prove", "fp_lookup_prove_workspace", "fp_fs_init", "fp_fs_absorb", "fp_fs_challenges",
     "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
@@ -93,10 +92,6 @@ def lib():
             "fp_fold_weights_prepare": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, vp]),
             "fp_fold_matrix_multi": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, vp, i64, vp, i64, i32, vp, sz, vp]),
             "fp_fold_matrix_multi_workspace": (sz, [i32, i32, i32]),
-            "fp_fold_weights_blocked_bytes": (sz, [i32, i32]),
-            "fp_fold_weights_prepare_blocked": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp]),
-            "fp_fold_matrix_multi_blocked": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, i64, vp, i64, i32, vp, sz, vp]),
-            "fp_fold_matrix_multi_blocked_workspace": (sz, [i32, i32, i32]),
             "fp_commit_pack": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, vp, vp]),
             "fp_rs_encode": (ctypes.c_int, [vp, i64, i32, i32, vp, i64, vp, sz, vp]),
             "fp_rs_encode_workspace": (sz, [i32, i32]),
@@ -451,48 +446,21 @@ def fold_weights_prepare(M, Mt=None, colsum=None):
     return Mt, colsum
 
 
-class BlockedWeights:
-    """K-blocked copy of an int8 matrix M [rows, cols] (fp_fold_weights_prepare_blocked)."""
-
-    def __init__(self, data, rows: int, cols: int):
-        self.data, self.rows, self.cols = data, rows, cols
-
-
-def fold_weights_prepare_blocked(M, colsum=None):
-    """K-blocked copy and column sums [cols] int32 of an int8 matrix M [rows, cols], for fold_matrix_multi."""
-    rows, cols = M.shape
-    nbytes = lib().fp_fold_weights_blocked_bytes(rows, cols)
-    data = torch.empty(max(nbytes, 16), dtype=torch.int8, device=M.device)
-    colsum = torch.empty(cols, dtype=torch.int32, device=M.device) if colsum is None else colsum
-    assert M.dtype == torch.int8 and (M.numel() == 0 or M.stride(1) == 1)
-    _check(lib().fp_fold_weights_prepare_blocked(_ptr(M) if M.numel() else None, _ld(M), rows, cols, _ptr(data),
-                                                 _ptr(colsum), _stream()), "fp_fold_weights_prepare_blocked")
-    return BlockedWeights(data, rows, cols), colsum
-
-
 def fold_matrix_multi(Mt, colsum, rows: int, E, cols_pad: int | None = None, out=None):
     """out[j, k] = sum_t E[j, t] M[t, k] for every row j of E [R, >= rows]
-    (int64 field tensor), from fold_weights_prepare's Mt (or
-    fold_weights_prepare_blocked's copy) and colsum."""
-    blocked = isinstance(Mt, BlockedWeights)
-    cols = Mt.cols if blocked else Mt.shape[0]
-    dev = Mt.data.device if blocked else Mt.device
+    (int64 field tensor), from fold_weights_prepare's Mt and colsum."""
+    cols = Mt.shape[0]
     R = E.shape[0]
     cols_pad = cols if cols_pad is None else cols_pad
-    out = torch.empty((R, cols_pad), dtype=torch.int64, device=dev) if out is None else out
+    out = torch.empty((R, cols_pad), dtype=torch.int64, device=Mt.device) if out is None else out
     assert E.dtype == torch.int64 and E.stride(1) == 1 and out.stride(1) == 1
     lde = E.stride(0) if R > 1 else max(E.stride(0), rows)
     ldo = out.stride(0) if R > 1 else max(out.stride(0), cols_pad)
-    pe, po = (_ptr(E) if E.numel() else None), (_ptr(out) if out.numel() else None)
-    if blocked:
-        assert Mt.rows == rows
-        p, nb = _ws_multi.get(lib().fp_fold_matrix_multi_blocked_workspace(rows, cols, R))
-        _check(lib().fp_fold_matrix_multi_blocked(_ptr(Mt.data), _ptr(colsum), rows, cols, R, pe, lde, po, ldo,
-                                                  cols_pad, p, nb, _stream()), "fp_fold_matrix_multi_blocked")
-        return out
-    p, nb = _ws_multi.get(lib().fp_fold_matrix_multi_workspace(rows, cols, R))
+    need = lib().fp_fold_matrix_multi_workspace(rows, cols, R)
+    p, nb = _ws_multi.get(need)
     _check(lib().fp_fold_matrix_multi(_ptr(Mt) if Mt.numel() else None, Mt.stride(0), _ptr(colsum), rows, cols, R,
-                                      pe, lde, po, ldo, cols_pad, p, nb, _stream()), "fp_fold_matrix_multi")
+                                      _ptr(E) if E.numel() else None, lde, _ptr(out) if out.numel() else None, ldo,
+                                      cols_pad, p, nb, _stream()), "fp_fold_matrix_multi")
     return out
 
 

@@ -39,14 +39,12 @@ int witness_fold_splitk(const int8_t* Xt, int64_t ldx, const int8_t* D, int64_t 
 // fp_witness_pack_weights lays out N rows of reduction length K: 1 KiB
 // fragments, zero past N and K) on the packed-weight kernel, for which Xt's
 // rows must be 16-byte aligned (ldx % 16 == 0); chunks from splitk_plan_packed.
-// xt_blocked: Xt K-blocked instead (block c of row t at Xt + (c T + t) 64,
-// zero past K; ldx unused).
 constexpr int PACK_BK = 64;  // K block of the packed layout
 SplitK splitk_plan_packed(int32_t T, int32_t K, int32_t N);
 size_t packed_rows_bytes(int32_t N, int32_t K);
 int witness_fold_splitk_packed(const int8_t* Xt, int64_t ldx, const int8_t* Dp, int32_t T, int32_t K, int32_t N,
                                const int32_t* colsum, const SplitK& p, uint64_t* part, int64_t ldp, int64_t psplit,
-                               hipStream_t st, bool xt_blocked = false);
+                               hipStream_t st);
 
 // Wave64 reductions of a 64-bit value held as two 32-bit halves.
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {

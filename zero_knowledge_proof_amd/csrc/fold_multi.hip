@@ -61,45 +61,6 @@ __global__ __launch_bounds__(256) void colsum_kernel(const int8_t* __restrict__ 
   if (lane == 0) c[k] = s;
 }
 
-// M K-blocked by 64 rows: Mb[(c cols + k) 64 + i] = M[64 c + i, k] (0 past
-// rows), so that a tile of columns reads one contiguous piece per 64 rows.
-// Thread (c, 16-byte piece q, column k), k fastest: each of its 16 one-byte
-// loads is a coalesced row segment across the wave.
-__global__ __launch_bounds__(256) void block_rows_kernel(const int8_t* __restrict__ M, int64_t ld, int32_t rows,
-                                                         int32_t cols, int32_t nkb, int8_t* __restrict__ Mb) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= (int64_t)nkb * 4 * cols) return;
-  const int k = (int)(g % cols);
-  const int64_t cq = g / cols;
-  const int q = (int)(cq & 3);
-  const int64_t c = cq >> 2;
-  const int64_t t0 = 64 * c + 16 * q;
-  uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (t0 + i < rows) w[i >> 2] |= (uint32_t)(uint8_t)M[(t0 + i) * ld + k] << (8 * (i & 3));
-  *(u32x4*)(Mb + (c * cols + k) * 64 + 16 * q) = u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// c[k] = sum_t M[t, k] from the K-blocked copy (its padding is zero), one wave
-// per column: lane l adds the 64 bytes of blocks l, l + 64, ...
-__global__ __launch_bounds__(256) void colsum_blocked_kernel(const int8_t* __restrict__ Mb, int32_t cols, int32_t nkb,
-                                                             int32_t* __restrict__ c) {
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (k >= cols) return;
-  int s = 0;
-  for (int b = lane; b < nkb; b += 64) {
-    const int8_t* p = Mb + ((int64_t)b * cols + k) * 64;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) s += p[i];
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-  if (lane == 0) c[k] = s;
-}
-
 // A[8j + l, t] = byte_l(E_j[t]) - 128 for t < rows, 0 for rows <= t < ldA.
 // One thread per (j, 4 consecutive t): 32 bytes in, one dword into each of 8 rows.
 __global__ __launch_bounds__(256) void digits_kernel(const uint64_t* __restrict__ E, int64_t lde, int32_t rows,
@@ -184,10 +145,9 @@ struct Layout {
 // row-major kernel's 128-row tiles.
 constexpr int32_t PACKED_MIN_R = 16;
 
-// blocked: Mt is the K-blocked copy, which only the packed-weight kernel reads.
-Layout layout(int32_t rows, int32_t cols, int32_t R, bool blocked = false) {
+Layout layout(int32_t rows, int32_t cols, int32_t R) {
   Layout L{};
-  L.packed = blocked || R >= PACKED_MIN_R;
+  L.packed = R >= PACKED_MIN_R;
   L.p = L.packed ? fpi::splitk_plan_packed(cols, rows, 8 * R) : fpi::splitk_plan(cols, rows, 8 * R);
   L.ldA = (int64_t)fpi::align_up((size_t)(rows > 0 ? rows : 1), 16);
   L.a_bytes = L.packed ? fpi::align_up(fpi::packed_rows_bytes(8 * R, rows > 0 ? rows : 1), 256)
@@ -223,66 +183,27 @@ extern "C" int fp_fold_weights_prepare(const int8_t* M, int64_t ld, int32_t rows
   return rc ? rc : fpi::ok();
 }
 
-extern "C" size_t fp_fold_weights_blocked_bytes(int32_t rows, int32_t cols) {
-  if (rows < 0 || cols < 0) return 0;
-  return (size_t)((rows + fpi::PACK_BK - 1) / fpi::PACK_BK) * (size_t)cols * fpi::PACK_BK;
-}
-
-extern "C" int fp_fold_weights_prepare_blocked(const int8_t* M, int64_t ld, int32_t rows, int32_t cols, int8_t* Mb,
-                                               int32_t* colsum, hipStream_t stream) {
-  const char* fn = "fp_fold_weights_prepare_blocked";
-  if (rows < 0 || cols < 0) return fpi::fail(FP_EARG, "%s: negative size", fn);
-  if (rows > FP_MAX_FOLD_ROWS) return fpi::fail(FP_ESHAPE, "%s: rows=%d > %d", fn, rows, FP_MAX_FOLD_ROWS);
-  if (ld < cols) return fpi::fail(FP_ESHAPE, "%s: ld < cols", fn);
-  if (cols == 0) return fpi::ok();
-  if (!colsum || (rows > 0 && (!M || !Mb))) return fpi::fail(FP_EARG, "%s: null pointer", fn);
-  if ((((uintptr_t)Mb) & 15) != 0) return fpi::fail(FP_EARG, "%s: Mb must be 16-byte aligned", fn);
-  if (rows > 0) {
-    const int32_t nkb = (rows + fpi::PACK_BK - 1) / fpi::PACK_BK;
-    const int64_t threads = (int64_t)nkb * 4 * cols;
-    hipLaunchKernelGGL(block_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, M, ld, rows,
-                       cols, nkb, Mb);
-    int rc = fpi::check_launch("block_rows_kernel");
-    if (rc) return rc;
-  }
-  // rows == 0: no blocks, every sum is 0
-  hipLaunchKernelGGL(colsum_blocked_kernel, dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, stream, Mb, cols,
-                     (rows + fpi::PACK_BK - 1) / fpi::PACK_BK, colsum);
-  int rc = fpi::check_launch("colsum_blocked_kernel");
-  return rc ? rc : fpi::ok();
-}
-
 extern "C" size_t fp_fold_matrix_multi_workspace(int32_t rows, int32_t cols, int32_t R) {
   if (rows < 0 || cols < 0 || R <= 0) return 0;
   const Layout L = layout(rows, cols, R);
   return L.a_bytes + L.z_bytes;
 }
 
-extern "C" size_t fp_fold_matrix_multi_blocked_workspace(int32_t rows, int32_t cols, int32_t R) {
-  if (rows < 0 || cols < 0 || R <= 0) return 0;
-  const Layout L = layout(rows, cols, R, true);
-  return L.a_bytes + L.z_bytes;
-}
-
-namespace {
-
-// Both entry points: Mt row-major with leading dim ldt, or (blocked) the
-// K-blocked copy of fp_fold_weights_prepare_blocked.
-int multi_fold(const char* fn, const int8_t* Mt, int64_t ldt, bool blocked, const int32_t* colsum, int32_t rows,
-               int32_t cols, int32_t R, const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo, int32_t cols_pad,
-               void* ws, size_t ws_bytes, hipStream_t stream) {
+extern "C" int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t* colsum, int32_t rows, int32_t cols,
+                                    int32_t R, const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo,
+                                    int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_fold_matrix_multi";
   if (rows < 0 || cols < 0 || R < 0) return fpi::fail(FP_EARG, "%s: negative size", fn);
   if (R > FP_MAX_REQUESTS) return fpi::fail(FP_ESHAPE, "%s: R=%d > %d", fn, R, FP_MAX_REQUESTS);
   if (rows > FP_MAX_FOLD_ROWS) return fpi::fail(FP_ESHAPE, "%s: rows=%d > %d", fn, rows, FP_MAX_FOLD_ROWS);
   if (cols_pad < cols) return fpi::fail(FP_ESHAPE, "%s: cols_pad < cols", fn);
-  if (!blocked && (ldt < rows || (ldt & 15)))
-    return fpi::fail(FP_ESHAPE, "%s: ldt must be >= rows and a multiple of 16", fn);
+  if (ldt < rows || (ldt & 15)) return fpi::fail(FP_ESHAPE, "%s: ldt must be >= rows and a multiple of 16", fn);
   if (lde < rows || ldo < cols_pad) return fpi::fail(FP_ESHAPE, "%s: lde < rows or ldo < cols_pad", fn);
   if (R == 0 || cols_pad == 0) return fpi::ok();
   if (!out) return fpi::fail(FP_EARG, "%s: null out", fn);
   if (cols > 0 && (!colsum || (rows > 0 && (!Mt || !E)))) return fpi::fail(FP_EARG, "%s: null input", fn);
   if (cols > 0 && rows > 0 && (((uintptr_t)Mt) & 15)) return fpi::fail(FP_EARG, "%s: Mt must be 16-byte aligned", fn);
-  const Layout L = layout(rows, cols, R, blocked);
+  const Layout L = layout(rows, cols, R);
   const bool gemm = cols > 0 && rows > 0;
   int32_t nsum = 0, k0 = 0;
   uint64_t* part = nullptr;
@@ -308,8 +229,7 @@ int multi_fold(const char* fn, const int8_t* Mt, int64_t ldt, bool blocked, cons
     }
     if (rc) return rc;
     auto gemm_into = [&](uint64_t* dst, int64_t ldp, int64_t ps) {
-      return L.packed ? fpi::witness_fold_splitk_packed(Mt, ldt, A, cols, rows, 8 * R, colsum, L.p, dst, ldp, ps, stream,
-                                                        blocked)
+      return L.packed ? fpi::witness_fold_splitk_packed(Mt, ldt, A, cols, rows, 8 * R, colsum, L.p, dst, ldp, ps, stream)
                       : fpi::witness_fold_splitk(Mt, ldt, A, L.ldA, cols, rows, 8 * R, colsum, L.p, dst, ldp, ps, stream);
     };
     if (L.p.ksplit > 1) {  // chunks into the workspace, added below
@@ -331,20 +251,4 @@ int multi_fold(const char* fn, const int8_t* Mt, int64_t ldt, bool blocked, cons
     if (rc) return rc;
   }
   return fpi::ok();
-}
-
-}  // namespace
-
-extern "C" int fp_fold_matrix_multi(const int8_t* Mt, int64_t ldt, const int32_t* colsum, int32_t rows, int32_t cols,
-                                    int32_t R, const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo,
-                                    int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return multi_fold("fp_fold_matrix_multi", Mt, ldt, false, colsum, rows, cols, R, E, lde, out, ldo, cols_pad, ws,
-                    ws_bytes, stream);
-}
-
-extern "C" int fp_fold_matrix_multi_blocked(const int8_t* Mb, const int32_t* colsum, int32_t rows, int32_t cols,
-                                            int32_t R, const fp_elem* E, int64_t lde, fp_elem* out, int64_t ldo,
-                                            int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return multi_fold("fp_fold_matrix_multi_blocked", Mb, 0, true, colsum, rows, cols, R, E, lde, out, ldo, cols_pad, ws,
-                    ws_bytes, stream);
 }

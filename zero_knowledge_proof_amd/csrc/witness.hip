@@ -506,10 +506,7 @@ struct WsCfg {
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
 };
 
-// XBLK: X is K-blocked instead of row-major: K block c of row t at
-// X + (c T + t) 64 (64 bytes, zero past K), so a tile's X block for one K step
-// is one contiguous piece of HBM.
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0, bool XBLK = false>
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int nblocks, int8_t* lds) {
   using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
   constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
@@ -541,11 +538,9 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   for (int c = 0; c < CB; ++c) {
     const int ch = tid + c * NT, row = ch / CPR;
     kc[c] = (ch % CPR) * 16;
-    px[c] = XBLK ? a.X + ((int64_t)kb0 * a.T + min(t_base + row, a.T - 1)) * BK + kc[c]
-                 : a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx + (int64_t)kb0 * BK;
+    px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx + (int64_t)kb0 * BK;
     so[c] = row * PITCH + kc[c];
   }
-  const int64_t xblk_stride = (int64_t)a.T * BK;  // XBLK: bytes per K block
   v4i wf[PFW][TM][KS];
   v4i xr[PFX][CB];
   auto wload = [&](int slot, int kblk) {
@@ -557,12 +552,8 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   auto xload = [&](int slot, int kblk) {
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      if constexpr (XBLK) {
-        xr[slot][c] = *(const v4i*)(px[c] + kblk * xblk_stride);
-      } else {
-        const int k = kblk * BK + kc[c];
-        xr[slot][c] = *(const v4i*)(px[c] + (k < klim ? k : 0));
-      }
+      const int k = kblk * BK + kc[c];
+      xr[slot][c] = *(const v4i*)(px[c] + (k < klim ? k : 0));
     }
   };
   auto sstore = [&](int slot, int buf) {
@@ -762,7 +753,7 @@ __device__ __forceinline__ void eq_aux_block(const EqAux& eq, int b) {
 // Workgroups [0, n_tail): sum-check tails (as witness_sc_kernel); the next
 // eq.block_start[eq.count]: eq tables; the rest: GEMM tiles (times the K
 // split). EPI 1: the limb-fold epilogue instead of the rescale.
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0, bool XBLK = false>
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_ws_kernel(
     WitArgs a, sct::TailArgs ta, int n_tail, EqAux eq) {
   constexpr int NT = NW * 64;
@@ -781,10 +772,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     eq_aux_block(eq, b);
     return;
   }
-  witness_body_ws<NW, TM, TN, PFW, PFX, UNR, EPI, XBLK>(a, b - n_eq, gridDim.x - n_tail - n_eq, lds);
+  witness_body_ws<NW, TM, TN, PFW, PFX, UNR, EPI>(a, b - n_eq, gridDim.x - n_tail - n_eq, lds);
 }
 
-template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0, bool XBLK = false>
+template <int NW, int TM, int TN, int PFW, int PFX, int UNR, int EPI = 0>
 int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, hipStream_t st) {
   using C = WsCfg<NW, TM, TN, PFW, PFX, UNR>;
   a.tiles_t = (a.T + C::BT - 1) / C::BT;
@@ -795,8 +786,8 @@ int launch_ws(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& eq, h
   if (total > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "witness: too many tiles");
   if (total == 0) return FP_OK;
   sct::TailArgs none{};
-  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR, EPI, XBLK>), dim3((unsigned)total), dim3(C::NT), 0,
-                     st, a, ta ? *ta : none, n_tail, eq);
+  hipLaunchKernelGGL((witness_ws_kernel<NW, TM, TN, PFW, PFX, UNR, EPI>), dim3((unsigned)total), dim3(C::NT), 0, st,
+                     a, ta ? *ta : none, n_tail, eq);
   return fpi::check_launch("witness_ws_kernel");
 }
 
@@ -1107,7 +1098,7 @@ size_t packed_rows_bytes(int32_t N, int32_t K) {
 
 int witness_fold_splitk_packed(const int8_t* Xt, int64_t ldx, const int8_t* Dp, int32_t T, int32_t K, int32_t N,
                                const int32_t* colsum, const SplitK& p, uint64_t* part, int64_t ldp, int64_t psplit,
-                               hipStream_t st, bool xt_blocked) {
+                               hipStream_t st) {
   WitArgs a{};
   a.X = Xt; a.ldx = ldx; a.W = Dp; a.ldw = 0;
   a.T = T; a.N = N; a.K = K; a.s = 1;
@@ -1116,7 +1107,6 @@ int witness_fold_splitk_packed(const int8_t* Xt, int64_t ldx, const int8_t* Dp, 
   a.ksplit = p.ksplit; a.kchunk = p.kchunk;
   a.colsum = colsum; a.part = part; a.ldp = ldp; a.psplit = psplit;
   vec_flags(a);
-  if (xt_blocked) return launch_ws<WIT_WS_L, 1, true>(a, nullptr, 0, EqAux{}, st);
   return launch_ws<WIT_WS_L, 1>(a, nullptr, 0, EqAux{}, st);
 }
 
