@@ -292,7 +292,8 @@ size_t fp_sumcheck3_workspace(int32_t m);
  * (L(L+1)/2 elements): rho are level d's round challenges and the block is
  * z_d (z_L is empty). Outputs in the same level order: rounds (L(L-1)/2
  * rounds of 4 values) and finals (3 per level). ws:
- * fp_lookup_prove_workspace(L) bytes, 256-byte aligned. */
+ * fp_lookup_prove_workspace(L) bytes, 256-byte aligned (every level's eq table,
+ * built up front from chal in one launch, then the sum-check's tables). */
 int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals, void* ws,
                     size_t ws_bytes, hipStream_t stream);
 size_t fp_lookup_prove_workspace(int32_t L);

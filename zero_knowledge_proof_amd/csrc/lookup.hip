@@ -517,9 +517,11 @@ extern "C" int fp_sumcheck3_prove(const fp_elem* E, const fp_elem* V, int32_t m,
   return rc ? rc : fpi::ok();
 }
 
+// Workspace: every level's eq table (the level with m variables at entry
+// 2^m - 1, 2^L - 1 entries in all), then the sum-check's tables.
 extern "C" size_t fp_lookup_prove_workspace(int32_t L) {
   if (L < 1 || L > FP_MAX_N) return 0;
-  return fpi::align_up(((size_t)1 << (L - 1)) * 8, 256) + sc3_layout(L - 1).bytes;
+  return fpi::align_up(((size_t)1 << L) * 8, 256) + sc3_layout(L - 1).bytes;
 }
 
 extern "C" int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals,
@@ -531,16 +533,23 @@ extern "C" int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* ch
   if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   if (((uintptr_t)ws) & 255) return fpi::fail(FP_EARG, "%s: workspace must be 256-byte aligned", fn);
   uint64_t* E = (uint64_t*)ws;
-  void* sc_ws = (char*)ws + fpi::align_up(((size_t)1 << (L - 1)) * 8, 256);
+  void* sc_ws = (char*)ws + fpi::align_up(((size_t)1 << L) * 8, 256);
+  // the claim on level d+1 sits at z = level d+1's challenges (empty at the
+  // root); the challenges are inputs, so every level's eq table is built up
+  // front in one batched launch (level d's table: m = L-1-d variables, at E + 2^m - 1)
+  fp_eq_desc eq[FP_MAX_N];
+  for (int32_t d = L - 1; d >= 0; --d) {
+    const int32_t m = L - 1 - d;
+    const int64_t off_next = (int64_t)(L - 2 - d) * (L - 1 - d) / 2;  // start of level d+1's challenges
+    eq[L - 1 - d] = fp_eq_desc{m ? chal + off_next : nullptr, m, E + ((int64_t)1 << m) - 1};
+  }
+  int rc = fpi::launch_eq_list(L, eq, stream);
+  if (rc) return rc;
   int64_t round_off = 0;
   for (int32_t d = L - 1; d >= 0; --d) {
     const int32_t m = L - 1 - d;
-    // the claim on level d+1 sits at z = level d+1's challenges (empty at the root)
-    const int64_t off_next = (int64_t)(L - 2 - d) * (L - 1 - d) / 2;  // start of level d+1's challenges
-    int rc = fp_eq_table(m ? chal + off_next : nullptr, m, E, stream);
-    if (rc) return rc;
     const int64_t off = (int64_t)(L - 1 - d) * (L - d) / 2;  // [lambda_d, rho_1 .. rho_m]
-    rc = sc3_enqueue(E, tree + level_offset(L, d), m, chal + off + 1, rounds + round_off * 4,
+    rc = sc3_enqueue(E + ((int64_t)1 << m) - 1, tree + level_offset(L, d), m, chal + off + 1, rounds + round_off * 4,
                      finals + (int64_t)(L - 1 - d) * 3, sc_ws, stream);
     if (rc) return rc;
     round_off += m;
