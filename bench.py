@@ -349,26 +349,24 @@ def commitment_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, lo
     return res
 
 
-def lookup_bytes(L: int, n_keys: int, tail: int = 2048) -> int:
+def lookup_bytes(L: int, n_keys: int, tail: int = 2048, kmax: int = 3) -> int:
     """Algorithmic HBM bytes of the remainder lookup: the tree (keys in, every
     level out once), then per level its eq table written once and, per
-    sum-check round launch, the three tables read once (after the first round
-    also written folded), until they fit one workgroup's LDS, whose launch
-    reads them once more."""
+    sum-check launch of up to kmax rounds, the three tables read once and
+    written folded by all of that launch's challenges, until they fit one
+    workgroup (tail entries), whose launch reads them once more."""
     b = n_keys + 8 * ((2 << L) - 1)
-    for d in range(L - 1, -1, -1):
-        size = 1 << (L - 1 - d)
+    for m in range(L):
+        size = 1 << m
         b += 8 * size                # eq table
-        read = 24 * size             # E, and level d's 2 size entries
-        fold = False
-        while (size // 2 if fold else size) > tail:
-            b += read
-            if fold:
-                size //= 2
-                b += 24 * size       # folded E, A, B written
-                read = 24 * size
-            fold = True
-        b += read
+        while size > tail:
+            left = 0
+            while (size >> left) > tail:
+                left += 1
+            b += 24 * size           # E and the level's 2 size entries (then E, A, B) read
+            size >>= min(left, kmax)
+            b += 24 * size           # folded E, A, B written
+        b += 24 * size
     return b
 
 
@@ -444,8 +442,9 @@ def lookup_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool) -> dic
         "roofline": {"bound": "hbm", "achieved": round(nbytes / t["lookup"] / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(nbytes / t["lookup"] / HBM_PEAK, 4), "traffic": None,
                      "algorithmic_bytes": nbytes,
-                     "note": "the whole lookup; its %d rounds are sequential (each level's point comes from the "
-                             "level above), so the small levels are latency-bound" % (L * (L - 1) // 2)},
+                     "note": "the whole lookup; the challenges are inputs, so its %d levels are proved side by "
+                             "side: launches of up to 3 rounds each while a level's tables exceed 2048 entries, "
+                             "then one workgroup per level for the last rounds (latency-bound)" % L},
     }
     if with_cpu:
         import oracle

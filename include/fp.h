@@ -293,7 +293,9 @@ size_t fp_sumcheck3_workspace(int32_t m);
  * z_d (z_L is empty). Outputs in the same level order: rounds (L(L-1)/2
  * rounds of 4 values) and finals (3 per level). ws:
  * fp_lookup_prove_workspace(L) bytes, 256-byte aligned (every level's eq table,
- * built up front from chal in one launch, then the sum-check's tables). */
+ * built up front from chal in one launch, then each level's own sum-check
+ * tables: since chal is an input no level waits for another, and the levels'
+ * sum-checks run side by side). */
 int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals, void* ws,
                     size_t ws_bytes, hipStream_t stream);
 size_t fp_lookup_prove_workspace(int32_t L);

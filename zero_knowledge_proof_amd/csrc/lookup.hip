@@ -15,7 +15,10 @@
 // three tables by the previous challenge and emits per-workgroup partial sums
 // of the round polynomial's values at 0..3 (the next launch's first workgroup
 // adds them); at most 2048 entries are finished by one workgroup, first 8 per
-// thread in registers, then in one wave with no barriers.
+// thread in registers, then in one wave with no barriers. The levels'
+// challenges are inputs, so the levels are independent instances: one launch
+// runs round k of every level that still has wide rounds, and one launch runs
+// every level's tail, a workgroup each.
 #include <algorithm>
 
 #include "common.hpp"
@@ -188,67 +191,142 @@ __device__ __forceinline__ void load3(const Sc3Tables& t, int64_t x, uint64_t& e
   }
 }
 
-// Sum of the nb partial value-quadruples of a round (workgroup-wide; every
-// thread gets the totals).
+// Adds the previous launch's per-workgroup partial sums, kp rounds of 4
+// values from each of nb workgroups (part[b][kp][4]), into out[kp][4]
+// (workgroup-wide).
 template <int NT>
-__device__ __forceinline__ void sum_partials(const uint64_t* __restrict__ part, int nb, uint64_t (&g)[4],
-                                             uint64_t* red) {
+__device__ __forceinline__ void add_partials(const uint64_t* __restrict__ part, int nb, int kp,
+                                             uint64_t* __restrict__ out, uint64_t* red) {
+  for (int rr = 0; rr < kp; ++rr) {
+    uint64_t g[4] = {0, 0, 0, 0};
+    for (int b = threadIdx.x; b < nb; b += NT)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) g[c] = 0;
-  for (int b = threadIdx.x; b < nb; b += NT)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[c] = gl::add(g[c], part[(int64_t)b * 4 + c]);
-  block_sum4<NT>(g, red);
+      for (int c = 0; c < 4; ++c) g[c] = gl::add(g[c], part[((int64_t)b * kp + rr) * 4 + c]);
+    block_sum4<NT>(g, red);
+    if (threadIdx.x < 4) out[rr * 4 + threadIdx.x] = g[threadIdx.x];
+  }
 }
 
-// One wide round i. fold = 0: the round polynomial of `in` (pairs q < pairs).
-// fold = 1: `in` folded by r[i-1] into `out` (out[x] = in[2x] + r (in[2x+1] -
-// in[2x])), then the round polynomial of `out`. Partial sums go to
-// part[block][4]; workgroup 0 first adds the previous round's partials
-// (prev, nb_prev > 0) into rounds[i-1].
-__global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t* __restrict__ Eo,
-                                                         uint64_t* __restrict__ Ao, uint64_t* __restrict__ Bo,
-                                                         const uint64_t* __restrict__ r, int32_t fold, int64_t pairs,
-                                                         uint64_t* __restrict__ part, const uint64_t* __restrict__ prev,
-                                                         int32_t nb_prev, uint64_t* __restrict__ prev_round) {
+// Rounds i .. i+k-1 of one instance in one launch (1 <= k <= SC3_KMAX). The
+// challenges are inputs, so a thread takes 2^k consecutive entries of E, A, B
+// and runs the k rounds on them in registers: the pairs of round i + rr are
+// adjacent entries after the folds by r_i .. r_{i+rr-1}, so they never leave
+// the thread. It adds its pairs' terms to the k round sums and writes its
+// entry of the tables folded by all k challenges (out, out + buf, out + 2 buf:
+// chunks = size / 2^k entries). Per-workgroup partial sums go to
+// part[block][k][4]; the instance's first workgroup first adds the previous
+// launch's partials (prev, nb_prev workgroups of k_prev rounds) into
+// prev_round.
+constexpr int SC3_KMAX = 3;              // rounds per wide launch
+constexpr int SC3_CW = 1 << SC3_KMAX;    // entries per thread
+
+struct Sc3RoundJob {
+  Sc3Tables in;
+  uint64_t* out;
+  int64_t buf;
+  const uint64_t* r;  // r_i .. r_{i+k-1}
+  int64_t chunks;
+  uint64_t* part;
+  const uint64_t* prev;
+  uint64_t* prev_round;
+  int32_t k, k_prev, nb_prev;
+  int32_t block_start, nb;  // the instance's workgroups in the launch
+};
+
+constexpr int SC3_RJ = 16;  // instances per wide-round launch
+struct Sc3RoundList {
+  Sc3RoundJob j[SC3_RJ];
+  int32_t count;
+};
+
+__global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3RoundList jl) {
   __shared__ uint64_t red[(LK_T / 64) * 4 + 4];
-  uint64_t g[4];
-  if (blockIdx.x == 0 && nb_prev > 0) {
-    sum_partials<LK_T>(prev, nb_prev, g, red);
-    if (threadIdx.x < 4) prev_round[threadIdx.x] = g[threadIdx.x];
+  int q = 0;
+#pragma unroll 1
+  for (int x = 1; x < jl.count; ++x)
+    if (jl.j[x].block_start <= (int)blockIdx.x) q = x;
+  const Sc3RoundJob& j = jl.j[q];
+  const int blk = (int)blockIdx.x - j.block_start;
+  if (blk == 0 && j.nb_prev > 0) add_partials<LK_T>(j.prev, j.nb_prev, j.k_prev, j.prev_round, red);
+  const int K = j.k, C = 1 << K;
+  uint64_t rk[SC3_KMAX], g[SC3_KMAX][4];
+#pragma unroll
+  for (int rr = 0; rr < SC3_KMAX; ++rr) {
+    rk[rr] = rr < K ? j.r[rr] : 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[rr][c] = 0;
   }
+  const Sc3Tables in = j.in;
+  uint64_t* __restrict__ Eo = j.out;
+  uint64_t* __restrict__ Ao = j.out + j.buf;
+  uint64_t* __restrict__ Bo = j.out + 2 * j.buf;
+  const int64_t chunks = j.chunks, stride = (int64_t)j.nb * LK_T;
+  for (int64_t t = (int64_t)blk * LK_T + threadIdx.x; t < chunks; t += stride) {
+    // The chunk's C entries are taken a pair at a time and reduced like a
+    // binary counter: a pair's round-0 terms are added and its fold is an
+    // entry of level 1; two level-l entries make a pair of round l, whose
+    // fold is an entry of level l+1. One pending entry per level stays live.
+    // The whole chunk is loaded first, in one burst: a lane's entries are
+    // consecutive, so each cache line is read by the loads of a few lanes
+    // issued together, before L2 can evict it.
+    uint64_t ve[SC3_CW], va[SC3_CW], vb[SC3_CW];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) g[c] = 0;
-  const uint64_t rr = fold ? *r : 0;
-  for (int64_t q = (int64_t)blockIdx.x * LK_T + threadIdx.x; q < pairs; q += (int64_t)gridDim.x * LK_T) {
-    uint64_t e[2], a[2], b[2];
-    if (fold) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint64_t e0, a0, b0, e1, a1, b1;
-        load3(in, 4 * q + 2 * h, e0, a0, b0);
-        load3(in, 4 * q + 2 * h + 1, e1, a1, b1);
-        e[h] = lerp(e0, e1, rr);
-        a[h] = lerp(a0, a1, rr);
-        b[h] = lerp(b0, b1, rr);
-        Eo[2 * q + h] = e[h];
-        Ao[2 * q + h] = a[h];
-        Bo[2 * q + h] = b[h];
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) load3(in, 2 * q + h, e[h], a[h], b[h]);
+    for (int x = 0; x < SC3_CW; ++x) {
+      ve[x] = va[x] = vb[x] = 0;
+      if (x < C) load3(in, t * C + x, ve[x], va[x], vb[x]);
     }
-    pair_terms(e[0], e[1], a[0], a[1], b[0], b[1], g);
+    uint64_t se[SC3_KMAX + 1], sa[SC3_KMAX + 1], sb[SC3_KMAX + 1];
+#pragma unroll
+    for (int l = 0; l <= SC3_KMAX; ++l) se[l] = sa[l] = sb[l] = 0;
+#pragma unroll
+    for (int p = 0; p < SC3_CW / 2; ++p) {
+      if (p < (C >> 1)) {
+        const uint64_t e0 = ve[2 * p], a0 = va[2 * p], b0 = vb[2 * p];
+        const uint64_t e1 = ve[2 * p + 1], a1 = va[2 * p + 1], b1 = vb[2 * p + 1];
+        pair_terms(e0, e1, a0, a1, b0, b1, g[0]);
+        uint64_t ce = lerp(e0, e1, rk[0]), ca = lerp(a0, a1, rk[0]), cb = lerp(b0, b1, rk[0]);
+        int l = 1;
+#pragma unroll
+        for (; l < SC3_KMAX; ++l) {
+          if (((p + 1) & ((1 << l) - 1)) != 0) break;  // the level-l entry waits for its partner
+          pair_terms(se[l], ce, sa[l], ca, sb[l], cb, g[l]);
+          ce = lerp(se[l], ce, rk[l]);
+          ca = lerp(sa[l], ca, rk[l]);
+          cb = lerp(sb[l], cb, rk[l]);
+        }
+        se[l] = ce;
+        sa[l] = ca;
+        sb[l] = cb;
+      }
+    }
+    // p < C/2 = 2^(K-1) never completes a level past K-1, so the chunk's entry
+    // folded by all K challenges is the pending entry of level K
+    uint64_t oe = se[1], oa = sa[1], ob = sb[1];
+#pragma unroll
+    for (int l = 2; l <= SC3_KMAX; ++l)
+      if (K == l) {
+        oe = se[l];
+        oa = sa[l];
+        ob = sb[l];
+      }
+    Eo[t] = oe;
+    Ao[t] = oa;
+    Bo[t] = ob;
   }
-  block_sum4<LK_T>(g, red);
-  if (threadIdx.x < 4) part[(int64_t)blockIdx.x * 4 + threadIdx.x] = g[threadIdx.x];
+#pragma unroll
+  for (int rr = 0; rr < SC3_KMAX; ++rr) {
+    if (rr < K) {
+      block_sum4<LK_T>(g[rr], red);
+      if (threadIdx.x < 4) j.part[((int64_t)blk * K + rr) * 4 + threadIdx.x] = g[rr][threadIdx.x];
+    }
+  }
 }
 
-// The last rounds in one workgroup of SC3_TT = 256 threads. The first adds the
-// previous wide round's partials (nb_prev > 0) into rounds[i0-1]. Then `in`
-// (size_in entries, folded by r[i0-1] first when fold; S <= 2048 entries after
-// that) is held as 8 consecutive entries per thread, and rounds run:
+// The last rounds of one instance in one workgroup of SC3_TT = 256 threads.
+// The first adds the previous wide launch's partials (nb_prev > 0, k_prev
+// rounds) into rounds[i0-k_prev .. i0-1]. Then `in` (size_in entries, folded by r[i0-1] first when fold;
+// S <= 2048 entries after that) is held as 8 consecutive entries per thread,
+// and rounds i0 .. m-1 run:
 //  - while a thread holds 2 or more entries, pairs are inside the thread and
 //    only the round sums cross threads (LDS, two barriers);
 //  - the <= 256 left go to wave 0, up to 4 per lane, pairs inside the lane,
@@ -256,23 +334,38 @@ __global__ __launch_bounds__(LK_T) void sc3_round_kernel(Sc3Tables in, uint64_t*
 //  - with one entry per lane (<= 64), partners are lane distance 1, 2, 4 ...
 //    apart (shuffles), round sums within the wave.
 // r_i is applied only after g_i is complete. finals = E, A, B at the point.
+struct Sc3TailJob {
+  Sc3Tables in;
+  int64_t size_in;
+  const uint64_t* r;
+  uint64_t* rounds;
+  uint64_t* finals;
+  const uint64_t* prev;
+  int32_t fold, i0, m, nb_prev, k_prev;
+};
+
+constexpr int SC3_TJ = 24;  // instances per tail launch, one workgroup each
+struct Sc3TailList {
+  Sc3TailJob j[SC3_TJ];
+  int32_t count;
+};
+
 constexpr int TQ = SC3_TAIL / SC3_TT;  // entries per thread in the first stage (8)
 
-__global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t fold, int64_t size_in,
-                                                          const uint64_t* __restrict__ r, int32_t i0, int32_t m,
-                                                          uint64_t* __restrict__ rounds, uint64_t* __restrict__ finals,
-                                                          const uint64_t* __restrict__ prev, int32_t nb_prev) {
+__global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3TailList jl) {
   __shared__ uint64_t red[(SC3_TT / 64) * 4 + 4];
   __shared__ uint64_t xE[SC3_TT], xA[SC3_TT], xB[SC3_TT];
   __shared__ uint64_t rs[FP_MAX_N];
+  const Sc3TailJob& j = jl.j[blockIdx.x];
+  const Sc3Tables in = j.in;
+  const int32_t fold = j.fold, i0 = j.i0, m = j.m;
+  const uint64_t* __restrict__ r = j.r;
+  uint64_t* __restrict__ rounds = j.rounds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t g[4];
-  if (nb_prev > 0) {
-    sum_partials<SC3_TT>(prev, nb_prev, g, red);
-    if (tid < 4) rounds[(int64_t)(i0 - 1) * 4 + tid] = g[tid];
-  }
+  if (j.nb_prev > 0) add_partials<SC3_TT>(j.prev, j.nb_prev, j.k_prev, rounds + (int64_t)(i0 - j.k_prev) * 4, red);
   if (tid < m - i0) rs[tid] = r[i0 + tid];
-  const int64_t S = fold ? size_in / 2 : size_in;  // entries after the first fold
+  const int64_t S = fold ? j.size_in / 2 : j.size_in;  // entries after the first fold
   const uint64_t r0 = fold ? r[i0 - 1] : 0;
   // stage 1: thread t holds entries t q .. t q + q - 1, q = max(1, S / 256)
   int q = S >= SC3_TT ? (int)(S / SC3_TT) : 1;
@@ -368,9 +461,9 @@ __global__ __launch_bounds__(SC3_TT) void sc3_tail_kernel(Sc3Tables in, int32_t 
     }
   }
   if (lane == 0) {
-    finals[0] = ev;
-    finals[1] = av;
-    finals[2] = bv;
+    j.finals[0] = ev;
+    j.finals[1] = av;
+    j.finals[2] = bv;
   }
 }
 
@@ -384,50 +477,109 @@ Sc3Layout sc3_layout(int32_t m) {
   Sc3Layout l{};
   const int64_t S = (int64_t)1 << m;
   l.buf = S > SC3_TAIL ? (size_t)(S / 2) : 0;
-  const int64_t pairs = S / 2;
+  const int64_t pairs = S / 2;  // bounds the threads of any wide launch
   l.nb = (int)std::min<int64_t>(SC3_MAXB, std::max<int64_t>(1, (pairs + LK_T - 1) / LK_T));
-  l.bytes = 6 * l.buf * 8 + 2 * fpi::align_up((size_t)l.nb * 4 * 8, 256);
+  l.bytes = 6 * l.buf * 8 + 2 * fpi::align_up((size_t)l.nb * SC3_KMAX * 4 * 8, 256);
   return l;
 }
 
-// Enqueues the degree-3 sum-check (m <= FP_MAX_N - 1); ws of sc3_layout(m).bytes.
-int sc3_enqueue(const uint64_t* E, const uint64_t* V, int32_t m, const uint64_t* r, uint64_t* rounds,
-                uint64_t* finals, void* ws, hipStream_t st) {
-  const Sc3Layout l = sc3_layout(m);
-  uint64_t* bufs = (uint64_t*)ws;
+// One degree-3 sum-check: sum_x E[x] V[2x] V[2x+1] over x < 2^m, challenges
+// r[0..m), ws of sc3_layout(m).bytes (its own; instances share nothing).
+struct Sc3Inst {
+  const uint64_t* E;
+  const uint64_t* V;
+  int32_t m;
+  const uint64_t* r;
+  uint64_t* rounds;
+  uint64_t* finals;
+  void* ws;
+};
+
+// Where an instance stands between launches.
+struct Sc3State {
+  Sc3Tables in;
+  int64_t size;  // entries of `in` (folded by every challenge so far)
+  int i;         // next round
+  int cur, lc;   // table buffer and partials buffer to write next
+  int nb_prev, k_prev, nb;
+  const uint64_t* last;  // the last launch's partials
+  uint64_t* bufs;
+  size_t buf;
   uint64_t* parts[2];
-  parts[0] = bufs + 6 * l.buf;
-  parts[1] = parts[0] + fpi::align_up((size_t)l.nb * 4 * 8, 256) / 8;
-  Sc3Tables in{E, V, nullptr, 1};
-  int64_t size = (int64_t)1 << m;  // entries of `in`
-  int i = 0;
-  int fold = 0;
-  int cur = 0;
-  int nb_prev = 0;  // partials of round i - 1 still to add
-  // wide rounds while the folded tables would exceed the tail's entries
-  while ((fold ? size / 2 : size) > SC3_TAIL) {
-    const int64_t out_size = fold ? size / 2 : size;
-    const int64_t pairs = out_size / 2;
-    uint64_t* Eo = bufs + (size_t)(3 * cur) * l.buf;
-    uint64_t* Ao = Eo + l.buf;
-    uint64_t* Bo = Ao + l.buf;
-    const int nb = (int)std::min<int64_t>(l.nb, (pairs + LK_T - 1) / LK_T);
-    hipLaunchKernelGGL(sc3_round_kernel, dim3(nb), dim3(LK_T), 0, st, in, Eo, Ao, Bo, fold ? r + (i - 1) : r, fold,
-                       pairs, parts[i & 1], parts[(i + 1) & 1], nb_prev, rounds + (size_t)(i - 1) * 4);
-    const int rc = fpi::check_launch("sc3_round_kernel");
-    if (rc) return rc;
-    if (fold) {
-      in = Sc3Tables{Eo, Ao, Bo, 0};
-      cur ^= 1;
-      size = out_size;
-    }
-    fold = 1;
-    nb_prev = nb;
-    ++i;
+};
+
+// Enqueues `count` independent instances (m <= FP_MAX_N - 1 each). Since
+// their challenges are inputs, each wide launch runs up to SC3_KMAX rounds of
+// every instance whose tables still exceed the tail's 2048 entries, and one
+// launch runs all the tails, one workgroup per instance.
+int sc3_enqueue_many(int count, const Sc3Inst* inst, hipStream_t st) {
+  Sc3State s[FP_MAX_N];
+  if (count < 0 || count > FP_MAX_N) return fpi::fail(FP_EARG, "sc3: %d instances", count);
+  for (int k = 0; k < count; ++k) {
+    const Sc3Layout l = sc3_layout(inst[k].m);
+    Sc3State& t = s[k];
+    t.in = Sc3Tables{inst[k].E, inst[k].V, nullptr, 1};
+    t.size = (int64_t)1 << inst[k].m;
+    t.i = t.cur = t.lc = t.nb_prev = t.k_prev = 0;
+    t.nb = l.nb;
+    t.last = nullptr;
+    t.bufs = (uint64_t*)inst[k].ws;
+    t.buf = l.buf;
+    t.parts[0] = t.bufs + 6 * l.buf;
+    t.parts[1] = t.parts[0] + fpi::align_up((size_t)l.nb * SC3_KMAX * 4 * 8, 256) / 8;
   }
-  hipLaunchKernelGGL(sc3_tail_kernel, dim3(1), dim3(SC3_TT), 0, st, in, fold, size, r, i, m, rounds, finals,
-                     parts[(i + 1) & 1], nb_prev);
-  return fpi::check_launch("sc3_tail_kernel");
+  for (;;) {
+    Sc3RoundList jl{};
+    int64_t blocks = 0;
+    bool any = false;
+    for (int k = 0; k <= count; ++k) {
+      const bool wide = k < count && s[k].size > SC3_TAIL;
+      if ((k == count || (wide && jl.count == SC3_RJ)) && jl.count > 0) {
+        hipLaunchKernelGGL(sc3_round_kernel, dim3((unsigned)blocks), dim3(LK_T), 0, st, jl);
+        const int rc = fpi::check_launch("sc3_round_kernel");
+        if (rc) return rc;
+        jl = Sc3RoundList{};
+        blocks = 0;
+      }
+      if (!wide) continue;
+      any = true;
+      Sc3State& t = s[k];
+      int left = 0;  // rounds until the tables fit the tail
+      while ((t.size >> left) > SC3_TAIL) ++left;
+      const int kk = std::min(left, SC3_KMAX);
+      const int64_t chunks = t.size >> kk;
+      const int nb = (int)std::min<int64_t>(t.nb, (chunks + LK_T - 1) / LK_T);
+      uint64_t* out = t.bufs + (size_t)(3 * t.cur) * t.buf;
+      uint64_t* part = t.parts[t.lc & 1];
+      jl.j[jl.count++] = Sc3RoundJob{t.in, out, (int64_t)t.buf, inst[k].r + t.i, chunks, part, t.last,
+                                     inst[k].rounds + (size_t)(t.i - t.k_prev) * 4, kk, t.k_prev, t.nb_prev,
+                                     (int32_t)blocks, nb};
+      blocks += nb;
+      t.in = Sc3Tables{out, out + t.buf, out + 2 * t.buf, 0};
+      t.size = chunks;
+      t.i += kk;
+      t.cur ^= 1;
+      t.lc ^= 1;
+      t.last = part;
+      t.nb_prev = nb;
+      t.k_prev = kk;
+    }
+    if (!any) break;
+  }
+  Sc3TailList tl{};
+  for (int k = 0; k <= count; ++k) {
+    if ((k == count || tl.count == SC3_TJ) && tl.count > 0) {
+      hipLaunchKernelGGL(sc3_tail_kernel, dim3((unsigned)tl.count), dim3(SC3_TT), 0, st, tl);
+      const int rc = fpi::check_launch("sc3_tail_kernel");
+      if (rc) return rc;
+      tl = Sc3TailList{};
+    }
+    if (k == count) break;
+    const Sc3State& t = s[k];
+    tl.j[tl.count++] = Sc3TailJob{t.in, t.size, inst[k].r, inst[k].rounds, inst[k].finals, t.last, 0, t.i,
+                                  inst[k].m, t.nb_prev, t.k_prev};
+  }
+  return FP_OK;
 }
 
 int64_t level_offset(int32_t L, int32_t d) { return ((int64_t)2 << L) - ((int64_t)2 << (L - d)); }
@@ -513,15 +665,23 @@ extern "C" int fp_sumcheck3_prove(const fp_elem* E, const fp_elem* V, int32_t m,
   if (!E || !V || !finals || (m > 0 && (!r || !rounds))) return fpi::fail(FP_EARG, "%s: null pointer", fn);
   const Sc3Layout l = sc3_layout(m);
   if (!ws || ws_bytes < l.bytes) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, l.bytes);
-  const int rc = sc3_enqueue(E, V, m, r, rounds, finals, ws, stream);
+  const Sc3Inst one{E, V, m, r, rounds, finals, ws};
+  const int rc = sc3_enqueue_many(1, &one, stream);
   return rc ? rc : fpi::ok();
 }
 
 // Workspace: every level's eq table (the level with m variables at entry
-// 2^m - 1, 2^L - 1 entries in all), then the sum-check's tables.
+// 2^m - 1, 2^L - 1 entries in all), then each level's sum-check tables (its
+// own, so that the levels run side by side).
+size_t lookup_sc_bytes(int32_t L) {
+  size_t b = 0;
+  for (int32_t m = 0; m < L; ++m) b += fpi::align_up(sc3_layout(m).bytes, 256);
+  return b;
+}
+
 extern "C" size_t fp_lookup_prove_workspace(int32_t L) {
   if (L < 1 || L > FP_MAX_N) return 0;
-  return fpi::align_up(((size_t)1 << L) * 8, 256) + sc3_layout(L - 1).bytes;
+  return fpi::align_up(((size_t)1 << L) * 8, 256) + lookup_sc_bytes(L);
 }
 
 extern "C" int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* chal, fp_elem* rounds, fp_elem* finals,
@@ -533,26 +693,27 @@ extern "C" int fp_lookup_prove(const fp_elem* tree, int32_t L, const fp_elem* ch
   if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   if (((uintptr_t)ws) & 255) return fpi::fail(FP_EARG, "%s: workspace must be 256-byte aligned", fn);
   uint64_t* E = (uint64_t*)ws;
-  void* sc_ws = (char*)ws + fpi::align_up(((size_t)1 << L) * 8, 256);
-  // the claim on level d+1 sits at z = level d+1's challenges (empty at the
-  // root); the challenges are inputs, so every level's eq table is built up
-  // front in one batched launch (level d's table: m = L-1-d variables, at E + 2^m - 1)
+  char* sc_ws = (char*)ws + fpi::align_up(((size_t)1 << L) * 8, 256);
+  // The claim on level d+1 sits at z = level d+1's challenges (empty at the
+  // root). The challenges are inputs, so no level waits for another: every
+  // level's eq table is built up front in one batched launch (level d's
+  // table: m = L-1-d variables, at E + 2^m - 1), and the levels' sum-checks
+  // run side by side.
   fp_eq_desc eq[FP_MAX_N];
-  for (int32_t d = L - 1; d >= 0; --d) {
-    const int32_t m = L - 1 - d;
-    const int64_t off_next = (int64_t)(L - 2 - d) * (L - 1 - d) / 2;  // start of level d+1's challenges
-    eq[L - 1 - d] = fp_eq_desc{m ? chal + off_next : nullptr, m, E + ((int64_t)1 << m) - 1};
-  }
-  int rc = fpi::launch_eq_list(L, eq, stream);
-  if (rc) return rc;
+  Sc3Inst inst[FP_MAX_N];
   int64_t round_off = 0;
   for (int32_t d = L - 1; d >= 0; --d) {
     const int32_t m = L - 1 - d;
-    const int64_t off = (int64_t)(L - 1 - d) * (L - d) / 2;  // [lambda_d, rho_1 .. rho_m]
-    rc = sc3_enqueue(E + ((int64_t)1 << m) - 1, tree + level_offset(L, d), m, chal + off + 1, rounds + round_off * 4,
-                     finals + (int64_t)(L - 1 - d) * 3, sc_ws, stream);
-    if (rc) return rc;
+    const int64_t off_next = (int64_t)(L - 2 - d) * (L - 1 - d) / 2;  // start of level d+1's challenges
+    const int64_t off = (int64_t)(L - 1 - d) * (L - d) / 2;           // [lambda_d, rho_1 .. rho_m]
+    eq[m] = fp_eq_desc{m ? chal + off_next : nullptr, m, E + ((int64_t)1 << m) - 1};
+    inst[m] = Sc3Inst{E + ((int64_t)1 << m) - 1, tree + level_offset(L, d), m, chal + off + 1,
+                      rounds + round_off * 4, finals + (int64_t)m * 3, sc_ws};
+    sc_ws += fpi::align_up(sc3_layout(m).bytes, 256);
     round_off += m;
   }
-  return fpi::ok();
+  int rc = fpi::launch_eq_list(L, eq, stream);
+  if (rc) return rc;
+  rc = sc3_enqueue_many(L, inst, stream);
+  return rc ? rc : fpi::ok();
 }
