@@ -126,3 +126,24 @@ def test_lookup_full_remainders(fp):
     want = O.grand_product_prove(lev, chal)
     for k in (L - 1, L - 2):
         assert np.array_equal(got[k][0], np.asarray(want[k][0], np.uint64).reshape(-1, 4)) and got[k][1] == want[k][1]
+
+
+def test_lookup_prove_many_levels(fp):
+    # 2^25 leaves, ragged: 13 levels take wide launches and 25 take tails, more
+    # than one launch holds of either, so both are split over two launches;
+    # every level's rounds and finals against the oracle's
+    rng = np.random.default_rng(25)
+    L, s = 25, 8
+    n = (1 << L) - 12345
+    keys = _keys(rng, n, s)
+    gamma = int(synth.challenges(1100, 1)[0])
+    chal = synth.challenges(1101, O.lookup_challenges_len(L))
+    tree = fp.lookup_tree(_dev(keys), L, _f([gamma]))
+    rounds, finals = fp.lookup_prove(tree, L, _f(chal))
+    torch.cuda.synchronize()
+    got = _split(_u64(rounds).reshape(-1, 4), _u64(finals).reshape(L, 3), L)
+    del tree, rounds, finals
+    lev = O.product_tree(keys, L, gamma)
+    want = O.grand_product_prove(lev, chal)
+    for (gr, gf), (wr, wf) in zip(got, want):
+        assert np.array_equal(gr, np.asarray(wr, np.uint64).reshape(-1, 4)) and gf == wf

@@ -233,7 +233,7 @@ struct Sc3RoundJob {
   int32_t block_start, nb;  // the instance's workgroups in the launch
 };
 
-constexpr int SC3_RJ = 16;  // instances per wide-round launch
+constexpr int SC3_RJ = 12;  // instances per wide-round launch
 struct Sc3RoundList {
   Sc3RoundJob j[SC3_RJ];
   int32_t count;
