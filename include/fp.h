@@ -84,7 +84,10 @@ const char* fp_last_error(void);
 int fp_witness_linear(const int8_t* X, int64_t ldx, const int8_t* W, int64_t ldw, int32_t T, int32_t d_in,
                       int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
 
-/* Grouped witness: G independent layers sharing d_in, d_out and s in ONE
+/* Grouped witness ("How fast can FlashProve go", §2: in the MoE model each
+ * token is sent to one routed expert, so an expert's matmul covers only its
+ * tokens; "flashprove-consumer-gpu" README, patch table: every expert's GEMM
+ * in one launch): G independent layers sharing d_in, d_out and s in ONE
  * launch (one group per MoE expert). Group g owns rows [row_off[g],
  * row_off[g+1]) of X (int8 [row_off[G], d_in], leading dim ldx) and of the
  * outputs Z/Y/R ([row_off[G], d_out], dense); its weight is W_ptrs[g]
@@ -256,10 +259,9 @@ int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t
 
 /* -------------------------------------------------------------- lookup --- */
 /* The lookup that shows the remainders R are small ("How fast can FlashProve
- * go", §3.1: a lookup checks that each rescale remainder is small; §4: a
- * lookup shows two products equal, one over the keys and one over the table,
- * the keys' product built as a binary tree whose levels are each proved with
- * sum-check).
+ * go", §3.1: the remainders of each rescale are range-checked by a lookup;
+ * §4: the lookup is a grand-product argument whose key side is a binary
+ * product tree, reduced level by level with sum-check).
  *
  * fp_lookup_tree: tree receives 2^(L+1) - 1 field elements: level 0 = the 2^L
  * leaves gamma - key_i (keys[i] as a field element for i < n, 0 for
@@ -419,6 +421,52 @@ int fp_layer_step(const int8_t* X, int64_t ldx, const int8_t* Wp, int32_t T, int
 size_t fp_layer_step_workspace(int32_t T, int32_t d_out, int32_t own_claim, int32_t n_fold,
                                const fp_fold_desc* folds, int32_t n_claim, const fp_claim_desc* claims);
 
+/* ------------------------------------------ all the maps of one layer --- */
+/* The witness GEMMs of up to FP_MAX_MULTI linear maps in ONE launch, each
+ * map's claim taken from its accumulators ("How fast can FlashProve go", §2:
+ * each linear map of the integer model is a matmul whose output is rescaled,
+ * clamped and committed with its remainder, and whose claim sum-check reduces
+ * to its folded tables; §3.1: that claim is about the product 2^k g_w + r,
+ * i.e. about Z, so Z itself need not be stored). For map m (desc mm[m]):
+ *   X: int8 [T, d_in] (leading dim ldx >= d_in, rows 16-byte aligned, d_in %
+ *   16 == 0); Wp: the map's weights W [d_out, d_in] packed by
+ *   fp_witness_pack_weights (16-byte aligned); writes Y, R int8 [T, d_out]
+ *   exactly as fp_witness_linear (rescale by 2^s, ties up; R against the
+ *   unclamped quotient; Y clamped to [-128, 127]) and Z int32 [T, d_out] when
+ *   Z is non-NULL (all dense row-major). With E_t non-NULL (device tables of
+ *   >= T and >= d_out entries, complete before the call) it also writes
+ *   *claim = sum_t sum_o E_t[t] E_o[o] Z[t, o] mod p (the value
+ *   fp_claim_eval_batched gives for Z); such a map needs T, d_out > 0.
+ * Maps run in the order given (the longest reduction first balances the
+ * launch's end); group_o >= 1 output tiles are walked at a time with the token
+ * tiles outermost (1: a weight panel's token tiles one after another). The
+ * n_eq eq tables (as fp_eq_table_batched, at most 8) are built by spare
+ * workgroups of the same launch: tables of another proof, not ones this
+ * launch's claims read. ws: fp_witness_multi_workspace(count, mm) bytes,
+ * 256-byte aligned, needed when some map forms a claim (else may be NULL);
+ * its first FP_MAX_MULTI * 64 bytes (arrival counters) must be zero on entry
+ * and every call leaves them zero. Errors: FP_EARG (count outside [1,
+ * FP_MAX_MULTI], null pointers, group_o < 1), FP_ESHAPE (alignment, d_in >
+ * FP_MAX_DIN, a claim without outputs), FP_ERANGE (s outside [1, 8]),
+ * FP_EWORKSPACE. Maps must not write each other's inputs. */
+#define FP_MAX_MULTI 8
+typedef struct {
+  const int8_t* X;
+  int64_t ldx;
+  int32_t T, d_in, d_out;
+  const int8_t* Wp;
+  int32_t* Z;
+  int8_t* Y;
+  int8_t* R;
+  const fp_elem* E_t;
+  const fp_elem* E_o;
+  fp_elem* claim;
+} fp_matmul_desc;
+int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                     const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Bytes of fp_witness_multi's workspace for these maps; 0 on bad arguments. */
+size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm);
+
 /* ----------------------------------------------------------- sum-check --- */
 /* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of
  * tables of 2^n entries ("How fast can FlashProve go", §2: sum-check reduces
@@ -455,7 +503,9 @@ int fp_witness_linear_with_sumcheck(const int8_t* X, int64_t ldx, const int8_t* 
                                     fp_elem* finals, fp_elem* claim0, hipStream_t stream);
 
 /* n_inst independent single-pair sum-checks of 2^n entries in one launch
- * (one MoE expert's claim each). A, B: device [n_inst][2^n]; r: [n_inst][n];
+ * (one MoE expert's claim each: "How fast can FlashProve go", §2, each
+ * routed expert's matmul is its own claim, and sum-check reduces each to its
+ * folded tables; the round message and binding are fp_sumcheck_prove's). A, B: device [n_inst][2^n]; r: [n_inst][n];
  * rounds: [n_inst][n][3]; finals: [n_inst][2]; claim0: [n_inst] or NULL.
  * n in [1, 13]. */
 int fp_sumcheck_prove_multi(int32_t n_inst, int32_t n, const fp_elem* A, const fp_elem* B, const fp_elem* r,

@@ -14,8 +14,8 @@ Python integers with ``% P``. The commitment of Y and R (§3.1: limbs packed
 three to a field element, each row Reed-Solomon encoded by an NTT, each column
 a salted BLAKE2b Merkle leaf) uses the C code for packing and encoding and the
 host's ``hashlib.blake2b`` for every hash. The lookup that shows the
-remainders are small (§3.1, §4: two products, the keys' one a binary tree whose
-levels are each proved with sum-check) is a product tree, a degree-3
+remainders are small (§3.1, §4: a grand-product argument with the key side as
+a binary tree, reduced level by level) is a product tree, a degree-3
 sum-check per level in C, and its verifier here.
 """
 from __future__ import annotations
@@ -356,10 +356,9 @@ def merkle_verify(root: bytes, leaf: bytes, j: int, path: list) -> bool:
 
 
 # ----------------------------------------------------------------- lookup --
-# "How fast can FlashProve go", §3.1 (a lookup checks that each rescale
-# remainder is small) and §4 (a lookup shows that two products are equal, one
-# over the keys and one over the table; the keys' product is a binary tree and
-# each level is proved with sum-check).
+# "How fast can FlashProve go", §3.1 (rescale remainders are range-checked by
+# a lookup) and §4 (a grand-product argument: the keys' product, built as a
+# binary tree and reduced level by level with sum-check, against the table's).
 LOOKUP_REASONS = {0: "OK", 1: "LEVEL_SUM", 2: "ROUND_SUM", 3: "LEVEL_FINAL", 4: "LEAF_OPENING", 5: "MULTISET"}
 
 

@@ -437,10 +437,10 @@ uint64_t or_rs_eval(const uint64_t* msg, int32_t logn, int64_t j) {
 }
 
 /* ---------------------------------------------------------------- lookup --
- * [HF] §3.1: a lookup checks that each rescale remainder is small; §4: a lookup
- * shows its keys are rows of a table by showing two products equal, one over
- * the keys and one over the table, the keys' product built as a binary tree
- * whose levels are each proved with sum-check. Readings where the page is
+ * [HF] §3.1 (rescale remainders are range-checked by a lookup) and §4 (the
+ * lookup is a grand-product argument: the keys' product, formed as a binary
+ * tree reduced level by level with sum-check, is matched against the table's
+ * product). Readings where the page is
  * silent: keys are int8 values; the tree has 2^L leaves gamma - key_i, padded
  * with gamma - 0 (0 is a row of every remainder table); level d+1 entry i is
  * the product of level d entries 2i and 2i+1; the table side is

@@ -23,7 +23,7 @@ P = O.P
 
 def _cmp_matmul(got, want, keys=("Z", "Y", "R", "x_fold", "w_fold", "rounds", "finals", "c0", "claim0")):
     for k in keys:
-        if k not in want:
+        if k not in want or (k == "Z" and "Z" not in got):  # Z: only where the prover stores it
             continue
         g, w = got[k], want[k]
         if isinstance(w, (int, np.integer)):
@@ -32,11 +32,11 @@ def _cmp_matmul(got, want, keys=("Z", "Y", "R", "x_fold", "w_fold", "rounds", "f
             assert np.array_equal(np.asarray(g).reshape(np.asarray(w).shape), np.asarray(w)), k
 
 
-def _run(cfg):
+def _run(cfg, keep_z=False):
     inp = synth.make_inputs(cfg)
     route = inp.get("route")
     ch = synth.draw_challenges(cfg, route)
-    prover = make_prover(cfg, inp, ch)
+    prover = make_prover(cfg, inp, ch, keep_z=keep_z)
     prover.run()
     torch.cuda.synchronize()
     return inp, ch, prover.results()
@@ -60,20 +60,30 @@ def test_layer_single_reduced(fp, shape):
     _cmp_matmul(got, want)
 
 
-def test_layer_rlc_reduced(fp):
-    cfg = synth.config(3, T=40, d=320, d_ff=600)
-    inp, ch, got = _run(cfg)
+@pytest.mark.parametrize("shape,keep_z", [(dict(T=40, d=320, d_ff=600), False), (dict(T=40, d=320, d_ff=600), True),
+                                          (dict(T=300, d=256, d_ff=1024), False)])
+def test_layer_rlc_reduced(fp, shape, keep_z):
+    """The dense MLP's three maps: those with d_in % 16 == 0 in one witness launch with their claims from the
+    accumulators (Z stored only with keep_z), the others (down at d_ff = 600) by the row-major witness with their
+    claims from the stored Z; every output, claim, round and the RLC against the oracle."""
+    cfg = synth.config(3, **shape)
+    inp, ch, got = _run(cfg, keep_z)
     want = O.prove_config(cfg, inp, ch)
     for m in cfg.matmuls:
+        assert ("Z" in got[m.name]) == (keep_z or m.d_in % 16 != 0)
         _cmp_matmul(got[m.name], want[m.name])
     assert got["rlc"] == want["rlc"]
 
 
-def test_layer_batched_reduced(fp):
-    cfg = synth.config(5, T=24, d=96, d_kv=40, d_ff=300)
-    inp, ch, got = _run(cfg)
+@pytest.mark.parametrize("shape,keep_z", [(dict(T=24, d=96, d_kv=40, d_ff=300), False),
+                                          (dict(T=24, d=96, d_kv=40, d_ff=300), True),
+                                          (dict(T=200, d=128, d_kv=64, d_ff=320), False)])
+def test_layer_batched_reduced(fp, shape, keep_z):
+    cfg = synth.config(5, **shape)
+    inp, ch, got = _run(cfg, keep_z)
     want = O.prove_config(cfg, inp, ch)
     for m in cfg.matmuls:
+        assert ("Z" in got[m.name]) == (keep_z or m.d_in % 16 != 0)
         _cmp_matmul(got[m.name], want[m.name], keys=("Z", "Y", "R", "x_fold", "w_fold", "c0"))
     for k in ("rounds", "finals"):
         assert np.array_equal(got["batch"][k], want["batch"][k]), k
@@ -228,9 +238,32 @@ def test_full_cfg2_overlapped(fp, keep_z):
     assert np.array_equal(got["Y"][ts, os_], y) and np.array_equal(got["R"][ts, os_], r)
 
 
+def _same_without_z(cfg, inp, ch, got_z):
+    """The benchmark's path (no Z stored, every claim from the accumulators) against a run that stores Z (whose
+    Z is checked against the oracle at sampled entries, through the rescale identity on every entry and through
+    its MLE): every Y, R, fold, claim, round and final equal."""
+    prover = make_prover(cfg, inp, ch)
+    prover.run()
+    torch.cuda.synchronize()
+    got = prover.results()
+    for m in cfg.matmuls:
+        g, gz = got[m.name], got_z[m.name]
+        assert "Z" not in g
+        for k in ("Y", "R", "x_fold", "w_fold", "c0", "rounds", "finals", "claim0"):
+            if k in gz:
+                assert np.array_equal(np.asarray(g[k]), np.asarray(gz[k])), (m.name, k)
+    for k in ("rlc", "batch"):
+        if k in got_z:
+            if k == "batch":
+                for kk in ("rounds", "finals", "claim0", "c0"):
+                    assert np.array_equal(np.asarray(got[k][kk]), np.asarray(got_z[k][kk])), kk
+            else:
+                assert got[k] == got_z[k]
+
+
 def test_full_cfg3(fp):
     cfg = synth.config(3)
-    inp, ch, got = _run(cfg)
+    inp, ch, got = _run(cfg, keep_z=True)
     C = 0
     for m in cfg.matmuls:
         _check_full_matmul(inp[m.x], inp[m.w], cfg.s, got[m.name], ch["r_t"], ch["r_o/" + m.name],
@@ -239,11 +272,12 @@ def test_full_cfg3(fp):
         C = (C + int(ch["rho/" + m.name][0]) * O.eval_deg2(int(g[0]), int(g[1]), int(g[2]),
                                                           int(ch["rounds/" + m.name][-1]))) % P
     assert got["rlc"] == C
+    _same_without_z(cfg, inp, ch, got)
 
 
 def test_full_cfg5(fp):
     cfg = synth.config(5)
-    inp, ch, got = _run(cfg)
+    inp, ch, got = _run(cfg, keep_z=True)
     n = cfg.batched_n
     As, Bs, rho = [], [], []
     xcache = {}
@@ -262,6 +296,7 @@ def test_full_cfg5(fp):
     b = got["batch"]
     assert np.array_equal(b["rounds"], rounds) and np.array_equal(b["finals"], finals)
     assert b["claim0"] == claim0 == c0 == b["c0"]
+    _same_without_z(cfg, inp, ch, got)
 
 
 def test_full_cfg4_sampled_experts(fp):

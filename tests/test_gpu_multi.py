@@ -1,0 +1,169 @@
+"""fp_witness_multi: the witness GEMMs of several linear maps in one launch, each
+map's claim sum_t sum_o E_t[t] E_o[o] Z[t, o] taken from its accumulators,
+against the CPU oracle (witness, rescale, MLE of Z or the claim's definition),
+bit-exact, on ragged shapes spanning several tiles, with Z stored or not, eq
+tables and arbitrary field tables (0, 1, p - 1), several tile walks, eq tables
+of another proof in the same launch, two calls in a row on one workspace, and
+the error cases."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+P = O.P
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _field(rng, n):
+    v = rng.integers(0, 2**63, size=n, dtype=np.uint64) * np.uint64(2) + rng.integers(0, 2, size=n, dtype=np.uint64)
+    v = np.where(v >= np.uint64(P), v - np.uint64(P), v).astype(np.uint64)
+    if n >= 4:
+        v[:3] = [0, 1, P - 1]
+    return v
+
+
+def _i8(rng, shape):
+    return rng.integers(-128, 128, size=shape, dtype=np.int8)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _claim_def(Z, Et, Eo):
+    """sum_t sum_o E_t[t] E_o[o] Z[t, o] mod p by its definition (the oracle's fold of Z's rows by E_t, then the
+    E_o-weighted sum of the folded row)."""
+    u = O.fold_rows(Z, Et)
+    want = 0
+    for o in range(Z.shape[1]):
+        want = O.add(want, O.mul(int(Eo[o]), int(u[o])))
+    return want
+
+
+# (T, d_in, d_out, keep_z, claim): claim "eq" (eq tables of random points: the oracle's MLE of Z), "rand"
+# (arbitrary field tables: the claim's definition) or None
+CASES = {
+    "layer": [(300, 1024, 700, False, "eq"), (300, 1024, 256, True, "eq"), (300, 4096, 130, False, "rand"),
+              (300, 64, 1000, True, None)],
+    "ragged": [(1, 16, 1, True, "rand"), (33, 48, 257, False, "eq"), (129, 2000, 31, True, "eq"),
+               (257, 96, 513, False, "rand"), (5, 0, 40, True, "eq")],
+    "one": [(700, 512, 900, False, "eq")],
+}
+
+
+@pytest.mark.parametrize("case,group_o,with_eq", [("layer", 1, False), ("layer", 3, True), ("ragged", 1, True),
+                                                   ("ragged", 2, False), ("one", 5, False)])
+def test_witness_multi(fp, case, group_o, with_eq):
+    rng = _rng(zlib.crc32(('%s/%d' % (case, group_o)).encode()))
+    maps, jobs = [], []
+    for (T, d_in, d_out, keep_z, claim) in CASES[case]:
+        X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+        want = {}
+        want["Z"], want["Y"], want["R"] = O.witness(X, W, 7)
+        Et = Eo = c = None
+        if claim == "eq":
+            rt = _field(rng, max(1, (T - 1).bit_length()))
+            ro = _field(rng, max(1, (d_out - 1).bit_length()))
+            want["c"] = O.mle_matrix(want["Z"], rt, ro)
+            Et, Eo = fp.to_field_tensor(O.eq_table(rt)), fp.to_field_tensor(O.eq_table(ro))
+        elif claim == "rand":
+            Et_h, Eo_h = _field(rng, T), _field(rng, d_out)
+            want["c"] = _claim_def(want["Z"], Et_h, Eo_h)
+            Et, Eo = fp.to_field_tensor(Et_h), fp.to_field_tensor(Eo_h)
+        if claim:
+            c = torch.empty(1, dtype=torch.int64, device="cuda")
+        Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda") if keep_z else None
+        Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+        R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+        jobs.append(fp.MatmulJob(_dev(X), fp.pack_weights(_dev(W)), Y, R, Z, Et, Eo, c))
+        maps.append(want)
+    eq, eq_want = None, []
+    if with_eq:
+        rs = [_field(rng, n) for n in (0, 5, 13)]
+        Es = [torch.empty(1 << len(r), dtype=torch.int64, device="cuda") for r in rs]
+        eq = [(fp.to_field_tensor(r) if len(r) else torch.empty(0, dtype=torch.int64, device="cuda"), E)
+              for r, E in zip(rs, Es)]
+        eq_want = [O.eq_table(r) for r in rs]
+    ws = fp.StepWorkspace()
+    for rep in range(2):
+        for j in jobs:
+            j.Y.fill_(3)
+            j.R.fill_(3)
+            if j.claim is not None:
+                j.claim.fill_(-1)
+        fp.witness_multi(jobs, 7, group_o=group_o, eq=eq, ws=ws)
+        torch.cuda.synchronize()
+        for j, want in zip(jobs, maps):
+            assert np.array_equal(j.Y.cpu().numpy(), want["Y"]) and np.array_equal(j.R.cpu().numpy(), want["R"])
+            if j.Z is not None:
+                assert np.array_equal(j.Z.cpu().numpy(), want["Z"])
+            if j.claim is not None:
+                assert int(fp.field_numpy(j.claim)[0]) == want["c"]
+        for (r, E), w in zip(eq or [], eq_want):
+            assert np.array_equal(fp.field_numpy(E), w)
+        assert ws.buf is None or int(ws.buf[:512].count_nonzero()) == 0
+
+
+def test_witness_multi_seven_maps_one_token_axis(fp):
+    """Seven maps over one token axis and shared inputs, in the layer's order (longest reduction first), the
+    claims of eq tables sharing E_t: every output and claim is the oracle's."""
+    rng = _rng(77)
+    T = 200
+    Xa, Xo, Xm, H = _i8(rng, (T, 256)), _i8(rng, (T, 256)), _i8(rng, (T, 256)), _i8(rng, (T, 640))
+    shapes = [("down", H, 256), ("q", Xa, 256), ("k", Xa, 64), ("v", Xa, 64), ("o", Xo, 256), ("gate", Xm, 640),
+              ("up", Xm, 640)]
+    rt = _field(rng, 8)
+    Et_h = O.eq_table(rt)
+    Et = fp.to_field_tensor(Et_h)
+    jobs, wants = [], []
+    for name, X, d_out in shapes:
+        W = _i8(rng, (d_out, X.shape[1]))
+        ro = _field(rng, (d_out - 1).bit_length())
+        Z, Y, R = O.witness(X, W, 8)
+        wants.append((Y, R, O.mle_matrix(Z, rt, ro)))
+        jobs.append(fp.MatmulJob(_dev(X), fp.pack_weights(_dev(W)), torch.empty((T, d_out), dtype=torch.int8,
+                                 device="cuda"), torch.empty((T, d_out), dtype=torch.int8, device="cuda"), None, Et,
+                                 fp.to_field_tensor(O.eq_table(ro)), torch.empty(1, dtype=torch.int64, device="cuda")))
+    fp.witness_multi(jobs, 8)
+    torch.cuda.synchronize()
+    for j, (Y, R, c) in zip(jobs, wants):
+        assert np.array_equal(j.Y.cpu().numpy(), Y) and np.array_equal(j.R.cpu().numpy(), R)
+        assert int(fp.field_numpy(j.claim)[0]) == c
+
+
+def test_witness_multi_errors(fp):
+    """Bad counts, a claim without its E_o or without outputs, unaligned X, s and group_o out of range, a
+    short workspace: each is refused before any launch."""
+    X = torch.zeros((8, 16), dtype=torch.int8, device="cuda")
+    Wp = fp.pack_weights(torch.zeros((8, 16), dtype=torch.int8, device="cuda"))
+    Y = torch.empty((8, 8), dtype=torch.int8, device="cuda")
+    R = torch.empty((8, 8), dtype=torch.int8, device="cuda")
+    E = torch.zeros(8, dtype=torch.int64, device="cuda")
+    c = torch.empty(1, dtype=torch.int64, device="cuda")
+    ok = fp.MatmulJob(X, Wp, Y, R, None, E, E, c)
+    fp.witness_multi([ok], 8)
+    with pytest.raises(AssertionError):
+        fp.witness_multi([], 8)
+    with pytest.raises(RuntimeError):
+        fp.witness_multi([ok] * 9, 8)
+    with pytest.raises(RuntimeError):
+        fp.witness_multi([ok], 9)
+    with pytest.raises(RuntimeError):
+        fp.witness_multi([ok], 8, group_o=0)
+    bad = fp.MatmulJob(X, Wp, Y, R, None, E, None, c)
+    with pytest.raises((RuntimeError, ValueError)):
+        fp.witness_multi([bad], 8)
+    Xu = torch.zeros(8 * 16 + 1, dtype=torch.int8, device="cuda")[1:].view(8, 16)
+    with pytest.raises(RuntimeError):
+        fp.witness_multi([fp.MatmulJob(Xu, Wp, Y, R)], 8)
+    lib = fp.lib()
+    arr = fp._multi_descs([ok])
+    with pytest.raises(RuntimeError):
+        fp._check(lib.fp_witness_multi(1, arr, 8, 1, 0, None, None, 0, fp._stream()), "fp_witness_multi")

@@ -134,6 +134,32 @@ def test_witness_against_numpy_matmul_and_rounding():
         _ = tie
 
 
+def test_witness_entries_against_numpy_matmul():
+    # the sampled-entry witness (the checker of every full-size Z sample) against
+    # numpy's int64 matmul: rows and columns of different counts and lengths, so a
+    # swapped (t, o) pair, a transposed operand or a dropped k term fails
+    rng = np.random.default_rng(11)
+    for (T, d_in, d_out) in [(1, 1, 1), (5, 3, 7), (33, 257, 19), (64, 4096, 48), (3, 14336, 5)]:
+        X = rng.integers(-128, 128, size=(T, d_in), dtype=np.int8)
+        W = rng.integers(-128, 128, size=(d_out, d_in), dtype=np.int8)
+        Zref = X.astype(np.int64) @ W.astype(np.int64).T
+        ts = np.concatenate([[0, T - 1], rng.integers(0, T, 200)]).astype(np.int32)
+        os_ = np.concatenate([[d_out - 1, 0], rng.integers(0, d_out, 200)]).astype(np.int32)
+        got = O.witness_entries(X, W, ts, os_)
+        assert got.dtype == np.int64
+        assert np.array_equal(got, Zref[ts, os_])
+    # extremes: every product (-128)(-128), the largest |Z| the int32 witness allows
+    X = np.full((2, 131071), -128, np.int8)
+    W = np.full((3, 131071), -128, np.int8)
+    assert list(O.witness_entries(X, W, [1, 0], [2, 1])) == [16384 * 131071] * 2
+    # agrees with the full witness on a small case
+    X = rng.integers(-128, 128, size=(9, 40), dtype=np.int8)
+    W = rng.integers(-128, 128, size=(11, 40), dtype=np.int8)
+    Z, _, _ = O.witness(X, W, 8)
+    tt, oo = np.meshgrid(np.arange(9), np.arange(11), indexing="ij")
+    assert np.array_equal(O.witness_entries(X, W, tt.ravel(), oo.ravel()), Z.astype(np.int64).ravel())
+
+
 def test_witness_extremes_and_overflow():
     X = np.full((2, 4096), -128, np.int8)
     W = np.full((3, 4096), -128, np.int8)

@@ -31,7 +31,7 @@ EXPORTS = [
     "fp_lookup_prove", "fp_lookup_prove_workspace", "fp_fs_init", "fp_fs_absorb", "fp_fs_challenges",
     "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
     "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
-    "fp_layer_step", "fp_layer_step_workspace",
+    "fp_layer_step", "fp_layer_step_workspace", "fp_witness_multi", "fp_witness_multi_workspace",
 ]
 
 _lib = None
@@ -48,6 +48,12 @@ class _EqDesc(ctypes.Structure):
 class _ClaimDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
                 ("E_rows", ctypes.c_void_p), ("E_cols", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class _MatmulDesc(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("T", ctypes.c_int32), ("d_in", ctypes.c_int32),
+                ("d_out", ctypes.c_int32), ("Wp", ctypes.c_void_p), ("Z", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("R", ctypes.c_void_p), ("E_t", ctypes.c_void_p), ("E_o", ctypes.c_void_p), ("claim", ctypes.c_void_p)]
 
 
 class _FoldDesc(ctypes.Structure):
@@ -116,6 +122,8 @@ def lib():
                                                                       vp]),
             "fp_layer_step": (ctypes.c_int, [vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp,
                                              i32, vp, vp, sz, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_witness_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "fp_witness_multi_workspace": (sz, [i32, vp]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -142,6 +150,19 @@ def _ptr(t) -> int | None:
         return None
     assert t.is_cuda, "device tensor expected"
     return t.data_ptr()
+
+
+def _need(t, dtype, numel: int, name: str):
+    """Check a buffer handed to the library: its dtype, contiguity and at least
+    numel elements (a short buffer would be written past its end on the device)."""
+    if t is None:
+        raise ValueError("%s: missing buffer" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.numel() and not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+    if t.numel() < numel:
+        raise ValueError("%s: %d elements, at least %d needed" % (name, t.numel(), numel))
 
 
 def _ld(M) -> int:
@@ -341,6 +362,48 @@ def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=
                                _ptr(finals), _ptr(claim0), _stream()), "fp_layer_step")
 
 
+class MatmulJob:
+    """One linear map of fp_witness_multi: X int8 [T, d_in], its packed weights, the outputs Y, R
+    (and Z, or None) int8/int32 [T, d_out], and for the claim from the accumulators the eq tables
+    E_t, E_o and the one-element claim output (all None: no claim)."""
+
+    def __init__(self, X, Wp: PackedWeights, Y, R, Z=None, E_t=None, E_o=None, claim=None):
+        self.X, self.Wp, self.Y, self.R, self.Z = X, Wp, Y, R, Z
+        self.E_t, self.E_o, self.claim = E_t, E_o, claim
+
+
+def _multi_descs(jobs):
+    """fp_matmul_desc array of MatmulJobs (buffers checked)."""
+    assert len(jobs) > 0, "no maps"
+    descs = []
+    for j in jobs:
+        T, d_in = j.X.shape
+        assert j.X.dtype == torch.int8 and d_in == j.Wp.d_in and (j.X.numel() == 0 or j.X.stride(1) == 1)
+        d_out = j.Wp.d_out
+        _need(j.Y, torch.int8, T * d_out, "Y")
+        _need(j.R, torch.int8, T * d_out, "R")
+        if j.Z is not None:
+            _need(j.Z, torch.int32, T * d_out, "Z")
+        if j.E_t is not None:
+            _need(j.E_t, torch.int64, T, "E_t")
+            _need(j.E_o, torch.int64, d_out, "E_o")
+            _need(j.claim, torch.int64, 1, "claim")
+        descs.append(_MatmulDesc(_ptr(j.X), _ld(j.X), T, d_in, d_out, _ptr(j.Wp.data), _ptr(j.Z), _ptr(j.Y),
+                                 _ptr(j.R), _ptr(j.E_t), _ptr(j.E_o), _ptr(j.claim)))
+    return (_MatmulDesc * len(descs))(*descs)
+
+
+def witness_multi(jobs, s: int, group_o: int = 1, eq=None, ws: StepWorkspace | None = None):
+    """The witness GEMMs of several linear maps (MatmulJob) in one launch, each map's claim
+    sum_t sum_o E_t[t] E_o[o] Z[t, o] taken from its accumulators; eq: (r, E) tables of another
+    proof built by the same launch."""
+    arr = _multi_descs(jobs)
+    ne, eqd = _eq_descs(eq)
+    ws = _ws_step if ws is None else ws
+    p, nb = ws.get(lib().fp_witness_multi_workspace(len(jobs), arr))
+    _check(lib().fp_witness_multi(len(jobs), arr, s, group_o, ne, eqd, p, nb, _stream()), "fp_witness_multi")
+
+
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):
     """Xg: int8 [row_off[-1], d_in]; Ws: list of int8 [d_out, d_in]; row_off: host ints (G+1)."""
     G = len(Ws)
@@ -518,7 +581,11 @@ def lookup_tree(keys, L: int, gamma, tree=None):
     """Product tree [2^(L+1) - 1] of the leaves gamma - key (int8 keys, padded
     with 0 to 2^L), levels from the leaves up; gamma: device int64 [1]."""
     n = keys.numel()
+    _need(keys, torch.int8, n, "keys")
+    assert 0 <= L <= 30 and n <= (1 << L), "keys must fit the 2^L leaves"
+    _need(gamma, torch.int64, 1, "gamma")
     tree = torch.empty((2 << L) - 1, dtype=torch.int64, device=gamma.device) if tree is None else tree
+    _need(tree, torch.int64, (2 << L) - 1, "tree")
     _check(lib().fp_lookup_tree(_ptr(keys) if n else None, n, L, _ptr(gamma), _ptr(tree), _stream()),
            "fp_lookup_tree")
     return tree
@@ -529,7 +596,10 @@ def lookup_counts(keys, L: int, s: int, counts=None):
     -2^(s-1) + i among the padded keys; the last entry counts keys outside."""
     n = keys.numel()
     dev = keys.device if n else _dev()
+    _need(keys, torch.int8, n, "keys")
+    assert 1 <= s <= 8, "s outside [1, 8]"
     counts = torch.empty((1 << s) + 1, dtype=torch.int32, device=dev) if counts is None else counts
+    _need(counts, torch.int32, (1 << s) + 1, "counts")
     _check(lib().fp_lookup_counts(_ptr(keys) if n else None, n, L, s, _ptr(counts), _stream()), "fp_lookup_counts")
     return counts
 
@@ -540,6 +610,11 @@ def sumcheck3_prove(E, V, r, rounds=None, finals=None):
     dev = E.device
     rounds = torch.empty((max(m, 1), 4), dtype=torch.int64, device=dev) if rounds is None else rounds
     finals = torch.empty(3, dtype=torch.int64, device=dev) if finals is None else finals
+    _need(E, torch.int64, 1 << m, "E")
+    _need(V, torch.int64, 2 << m, "V")
+    _need(r, torch.int64, m, "r")
+    _need(rounds, torch.int64, 4 * m, "rounds")
+    _need(finals, torch.int64, 3, "finals")
     need = lib().fp_sumcheck3_workspace(m)
     p, nbytes = _ws_lookup.get(need)
     _check(lib().fp_sumcheck3_prove(_ptr(E), _ptr(V), m, _ptr(r) if m else None, _ptr(rounds), _ptr(finals), p,
@@ -554,6 +629,10 @@ def lookup_prove(tree, L: int, chal, rounds=None, finals=None):
     nr = L * (L - 1) // 2
     rounds = torch.empty((max(nr, 1), 4), dtype=torch.int64, device=dev) if rounds is None else rounds
     finals = torch.empty((L, 3), dtype=torch.int64, device=dev) if finals is None else finals
+    _need(tree, torch.int64, (2 << L) - 1, "tree")
+    _need(chal, torch.int64, L * (L + 1) // 2, "chal")
+    _need(rounds, torch.int64, 4 * nr, "rounds")
+    _need(finals, torch.int64, 3 * L, "finals")
     need = lib().fp_lookup_prove_workspace(L)
     p, nbytes = _ws_lookup.get(need)
     _check(lib().fp_lookup_prove(_ptr(tree), L, _ptr(chal), _ptr(rounds), _ptr(finals), p, nbytes, _stream()),

@@ -1,10 +1,10 @@
 // lookup.hip - the lookup that shows committed remainders are small.
 //
-// "How fast can FlashProve go", §3.1: every rescale commits its remainder and a
-// lookup checks that the remainder is small; §4: a lookup shows its keys are
-// rows of a table by showing two products equal, one over the keys and one
-// over the table; the keys' product is built as a binary tree and each level of
-// the tree is proved with sum-check. Here the tree has 2^L leaves gamma - key
+// "How fast can FlashProve go", §3.1 (each rescale remainder is committed and
+// range-checked by a lookup) and §4 (the lookup as a grand-product argument:
+// the product of gamma - key over the keys is matched against the table's
+// product, the key side computed as a binary product tree that is proved one
+// level at a time by sum-check). Here the tree has 2^L leaves gamma - key
 // (padded with gamma - 0), level d+1 entry i = level d entries 2i times 2i+1,
 // and the claim on level d+1 at a point z is reduced to level d by the
 // degree-3 sum-check of eq(z, x) V_d(2x) V_d(2x+1); the next point is

@@ -6,10 +6,11 @@
 // matmul's sum-check uses in place of g^ (so Z itself is kept for the claim).
 // Per output entry:
 //   Z = sum_k X[t,k] W[o,k]          (int8 x int8 -> int32, exact)
-//   Q = floor((Z + 2^(s-1)) / 2^s)   (ties up)  = (Z >> s) + bit_{s-1}(Z)
-//   R = Z - 2^s Q                    = (Z & (2^s - 1)) - bit_{s-1}(Z) 2^s
+//   Q = floor((Z + 2^(s-1)) / 2^s)   (ties up), computed as (Z + 2^(s-1)) >> s
+//   R = Z - 2^s Q
 //   Y = clamp(Q, -128, 127)
-// The bit form never forms Z + 2^(s-1) or 2^s Q, so it cannot overflow int32.
+// Z + 2^(s-1) cannot overflow int32: |Z| <= 2^14 d_in <= 2^31 - 2^14 for
+// d_in <= FP_MAX_DIN, and 2^(s-1) <= 128.
 //
 // Kernel. X [T, K] and W [d_out, K] are both K-contiguous, the operand order
 // of v_mfma_i32_32x32x32_i8: lane l feeds row l%32 with the 16 bytes at
@@ -32,175 +33,9 @@
 #include "eq.hpp"
 #include "fold.hpp"
 #include "sc_tail.hpp"
+#include "witness_dev.hpp"
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int MAXG = 128;  // groups per grouped launch
-
-struct WitArgs {
-  const int8_t* X;
-  int64_t ldx;
-  const int8_t* W;
-  int64_t ldw;
-  int32_t T, N, K, s;  // tokens, outputs (d_out), reduction (d_in), shift
-  int32_t* Z;
-  int8_t* Y;
-  int8_t* R;
-  int32_t tiles_t, tiles_o;
-  int32_t vecX, vecW, vecZ, vecYR;
-  // split K: each tile is computed by ksplit workgroups, workgroup j reducing
-  // over [j kchunk, (j+1) kchunk) (0 or 1: no split)
-  int32_t ksplit, kchunk;
-  // limb-fold epilogue: field value of each group of 8 output rows at token t
-  // into part[j psplit + (o / 8) ldp + t], plus the column-sum term in split 0
-  const int32_t* colsum;
-  uint64_t* part;
-  int64_t ldp, psplit;
-  // packed weights (W then points at them): 32-row blocks and WP_BK-byte K blocks
-  int32_t wp_rb, wp_kb;
-  // packed kernel: the claim sum_{t,o} cEt[t] cEo[o] Z[t, o] of the launch's own
-  // product, taken from the accumulators (none when cEt is NULL): one value per
-  // wave into cpart, and the last tile to arrive at *cctr writes the sum to *cout
-  const uint64_t* cEt = nullptr;
-  const uint64_t* cEo = nullptr;
-  uint64_t* cpart = nullptr;
-  uint64_t* cout = nullptr;
-  uint32_t* cctr = nullptr;
-};
-
-struct GroupTab {
-  const int8_t* W[MAXG];
-  int32_t row_off[MAXG + 1];   // token rows of each group
-  int32_t tile_off[MAXG + 1];  // first token tile of each group
-  int32_t G;
-};
-
-__device__ __forceinline__ v4i load16(const int8_t* rowp, int k, int K, bool vec) {
-  if (vec && k + 16 <= K) return *(const v4i*)(rowp + k);
-  int w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int b = 0; b < 16; ++b)
-    if (k + b < K) w[b >> 2] |= (int)((uint32_t)(uint8_t)rowp[k + b] << (8 * (b & 3)));
-  v4i r = {w[0], w[1], w[2], w[3]};
-  return r;
-}
-
-// Map a linear workgroup id to a tile id so that each XCD gets a contiguous
-// range of tiles (ids are dealt to XCDs round-robin).
-__device__ __forceinline__ int xcd_tile(int bid, int nb) {
-  constexpr int NX = 8;
-  const int x = bid % NX, li = bid / NX;
-  const int q = nb / NX, rm = nb % NX;
-  const int start = (x < rm) ? x * (q + 1) : rm * (q + 1) + (x - rm) * q;
-  return start + li;
-}
-
-// Q = floor((z + 2^(s-1)) / 2^s) by an arithmetic shift, R = z - 2^s Q, Y = Q
-// clamped to int8. The sum cannot overflow: |z| <= 2^14 d_in <= 2^31 - 2^14
-// (d_in <= FP_MAX_DIN) and 2^(s-1) <= 128 (s in [1, 8]). Results in the low
-// byte (the packing keeps only that byte).
-__device__ __forceinline__ void rescale(int32_t z, int s, int32_t& y, int32_t& r) {
-  const int32_t q = (z + (1 << (s - 1))) >> s;
-  r = z - (q << s);
-  y = q < -128 ? -128 : (q > 127 ? 127 : q);
-}
-
-// Low bytes of a, b, c, d as one dword (byte 0 = a).
-__device__ __forceinline__ uint32_t pack_low_bytes(int32_t a, int32_t b, int32_t c, int32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);  // a0 b0 0 0
-  const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0c0c0400u);  // c0 d0 0 0
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// One 32x32 accumulator fragment as 16 consecutive outputs per lane: lanes
-// 0-31 keep o = 0..15 of the 32-block, lanes 32-63 take o = 16..31 (two
-// v_permlane32_swap per 4 accumulators), then the o offsets are in register
-// order 0-3, 8-11, 4-7, 12-15.
-__device__ __forceinline__ void fragment_outputs(const v16i& accv, int32_t (&z)[16]) {
-  int32_t v[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) v[k] = accv[k];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v[k], (unsigned)v[k + 8], false, false);
-    v[k] = (int32_t)sw[0];
-    v[k + 8] = (int32_t)sw[1];
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    z[q] = v[q];
-    z[4 + q] = v[8 + q];
-    z[8 + q] = v[4 + q];
-    z[12 + q] = v[12 + q];
-  }
-}
-
-// Y, R (and Z unless NULL) of 16 consecutive outputs o0.. of token t, held by one
-// lane after the swap; the caller has checked t < T and o0 < N.
-__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s) {
-  const int64_t idx = (int64_t)t * a.N + o0;
-  uint32_t yw[4], rw[4];
-  int32_t y[16], r[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) rescale(z[q], s, y[q], r[q]);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    yw[g] = pack_low_bytes(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]);
-    rw[g] = pack_low_bytes(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
-  }
-  if (o0 + 16 <= a.N) {
-    if (a.Z) {
-      if (a.vecZ) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *(v4i*)(a.Z + idx + 4 * q) = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) a.Z[idx + q] = z[q];
-      }
-    }
-    if (a.vecYR) {
-      *(v4i*)(a.Y + idx) = v4i{(int)yw[0], (int)yw[1], (int)yw[2], (int)yw[3]};
-      *(v4i*)(a.R + idx) = v4i{(int)rw[0], (int)rw[1], (int)rw[2], (int)rw[3]};
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
-        a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (o0 + q < a.N) {
-        if (a.Z) a.Z[idx + q] = z[q];
-        a.Y[idx + q] = (int8_t)(yw[q >> 2] >> (8 * (q & 3)));
-        a.R[idx + q] = (int8_t)(rw[q >> 2] >> (8 * (q & 3)));
-      }
-    }
-  }
-}
-
-// Limb-fold epilogue: a lane's 16 outputs o0.. of token t are the byte limbs
-// l = 0..7 of digit-row group o0 / 8 (z[0..7]) and of the next group
-// (z[8..15]); the group's value sum_l 2^(8l) z[l] is exact as L + 2^32 H with
-// |L|, |H| < 2^55, then reduced, plus the digits' offset term in chunk 0.
-__device__ __forceinline__ void limb_fold_store(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int ks) {
-  uint64_t cterm = 0;
-  if (ks == 0) cterm = gl::mul(gl::from_i64(128 * (int64_t)a.colsum[t]), 0x0101010101010101ull);
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int o = o0 + 8 * g;
-    if (o >= a.N) break;
-    const int32_t* zz = z + 8 * g;
-    const int64_t L = (int64_t)zz[0] + (int64_t)zz[1] * 256 + (int64_t)zz[2] * 65536 + (int64_t)zz[3] * 16777216;
-    const int64_t H = (int64_t)zz[4] + (int64_t)zz[5] * 256 + (int64_t)zz[6] * 65536 + (int64_t)zz[7] * 16777216;
-    const uint64_t v = gl::add(gl::from_i64(L), gl::mul(gl::from_i64(H), 1ull << 32));
-    a.part[(int64_t)ks * a.psplit + (int64_t)(o >> 3) * a.ldp + t] = gl::add(v, cterm);
-  }
-}
 
 // LDS of one GEMM workgroup: double-buffered W and X tiles.
 template <int BO, int BT, int BK>
@@ -410,7 +245,6 @@ __global__ __launch_bounds__((BO / WO) * (BT / WT) * 64) void witness_sc_kernel(
 // wave needs, and only X (shared by the workgroup's waves) passes through LDS:
 // half the LDS traffic per MFMA of the tile above, and the register copy of
 // each W byte is used against all of the workgroup's tokens.
-constexpr int WP_BK = fpi::PACK_BK;
 
 __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restrict__ W, int64_t ldw, int32_t N,
                                                            int32_t K, int32_t nrb, int32_t nkb, int vec,
@@ -429,59 +263,6 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
     v4i val = {0, 0, 0, 0};
     if (row < N) val = load16(W + (int64_t)row * ldw, k, K, vec != 0);
     *(v4i*)(Wp + u * 16) = val;
-  }
-}
-
-// ---- the claim of a launch's own product, from the accumulators ---------
-// Each wave contracts its fragments over the outputs on the matrix cores:
-// the 7-bit limbs of E_o (CL_LIMBS per element, rows 0..9 of the A operand)
-// against the four byte planes of Z (the B operand: after the swap a lane
-// holds 16 consecutive outputs of one token, which is the operand's layout
-// with the outputs as k). Planes 0-2 are unsigned bytes, fed as b - 128;
-// plane 3 is Z's signed top byte. Row m of the products, weighted
-// 2^(7m + 8p), plus the offsets' share, then gives sum_o E_o[o] Z[t, o] for
-// the lane's token t, which E_t[t] weights.
-constexpr int CL_LIMBS = 10;
-
-// Lane (t, h) of the plane products D[p]: register v holds row m = 8 (v / 4)
-// + 4 h + v % 4; rows below CL_LIMBS carry limbs (v < 4 for both halves,
-// v = 4, 5 for h = 0). Returns sum_m 2^(7m) sum_p 2^(8p) D_p[m] mod p (the
-// offsets of planes 0-2 are added back per wave: sum_m 2^(7m) 128 (1 + 2^8 +
-// 2^16) sum_o limb_m(E_o[o]) is 128 * 65793 * sum_o E_o[o]).
-__device__ __forceinline__ uint64_t claim_row_value(const v16i (&D)[4], int h) {
-  // sum_p 2^(8p) D_p for register v, |.| < 2^46
-  auto rowsum = [&](int v) -> __int128 {
-    const int32_t s01 = D[0][v] + (D[1][v] << 8);  // |D| < 2^21: exact in 32 bits
-    const int32_t s23 = D[2][v] + (D[3][v] << 8);
-    return (__int128)((int64_t)s01 + ((int64_t)s23 << 16));
-  };
-  // registers 0-3 hold rows v + 4h: scale by 2^(7v), then by 2^28 in the upper half
-  __int128 x = rowsum(0) + (rowsum(1) << 7) + (rowsum(2) << 14) + (rowsum(3) << 21);
-  x = h ? (x << 28) : x;
-  // registers 4, 5 hold rows 8, 9 (h = 0; rows 12, 13 of the upper half are zero)
-  x += (rowsum(4) << 56) + (rowsum(5) << 63);
-  // p 2^48 keeps the sum positive (|x| < 2^110)
-  const unsigned __int128 y = (unsigned __int128)x + ((unsigned __int128)0xFFFFFFFF00000001ull << 48);
-  return gl::reduce128((uint64_t)y, (uint64_t)(y >> 64));
-}
-
-// The wave's claim value to its slot; the last tile to arrive adds them all.
-__device__ __forceinline__ void claim_arrive(const WitArgs& a, uint64_t wsum, int bid, int nblocks, int nwaves,
-                                             uint64_t* red, uint32_t* flag) {
-  const int tid = threadIdx.x;
-  wsum = fpi::wave_total(wsum);
-  if ((tid & 63) == 0) foldk::store_part(a.cpart + (int64_t)bid * nwaves + (tid >> 6), wsum, true);
-  if (!foldk::arrive_last(a.cctr, (uint32_t)nblocks, flag)) return;
-  const int nv = nblocks * nwaves;
-  uint64_t v = 0;
-  for (int i = tid; i < nv; i += (int)blockDim.x) v = gl::add(v, foldk::load_part(a.cpart + i));
-  v = fpi::wave_total(v);
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t t = 0;
-    for (int w = 0; w < nwaves; ++w) t = gl::add(t, red[w]);
-    *a.cout = t;
   }
 }
 
@@ -723,32 +504,6 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
 // 256x128 tiles (4 waves of 64x128): each weight fragment in registers meets
 // twice the tokens, for shapes with enough tiles to fill the GPU.
 #define WIT_WS_L 4, 2, 4, 2, 2, 2
-
-// eq tables built by spare workgroups of a witness launch (a proof's eq
-// tables depend on its challenges only, so they can be made while its GEMM
-// runs): table i takes aux workgroups [block_start[i], block_start[i+1]),
-// each writing 2^(8 + eq_aux_mid(n)) entries.
-constexpr int WIT_MAX_EQ = 8;
-struct EqAux {
-  const fp_elem* r[WIT_MAX_EQ];
-  fp_elem* E[WIT_MAX_EQ];
-  int32_t n[WIT_MAX_EQ];
-  int32_t block_start[WIT_MAX_EQ + 1];
-  int32_t count;
-};
-__host__ __device__ inline int eq_aux_mid(int n) {
-  return n <= 8 ? 0 : (n - 8 < eqk::EQ_MAX_MID ? n - 8 : eqk::EQ_MAX_MID);
-}
-inline int64_t eq_aux_blocks(int n) { return n <= 8 ? 1 : (int64_t)1 << (n - 8 - eq_aux_mid(n)); }
-
-// Aux workgroup b of the launch's eq tables.
-__device__ __forceinline__ void eq_aux_block(const EqAux& eq, int b) {
-  int k = 0;
-#pragma unroll 1
-  for (int q = 1; q < eq.count; ++q)
-    if (eq.block_start[q] <= b) k = q;
-  eqk::eq_block(eq.r[k], eq.n[k], eq.E[k], b - eq.block_start[k], eq_aux_mid(eq.n[k]));
-}
 
 // Workgroups [0, n_tail): sum-check tails (as witness_sc_kernel); the next
 // eq.block_start[eq.count]: eq tables; the rest: GEMM tiles (times the K
@@ -1130,28 +885,6 @@ int launch_ws_auto(WitArgs a, const sct::TailArgs* ta, int n_tail, const EqAux& 
   const int64_t large_tiles = (int64_t)((a.N + 255) / 256) * ((a.T + 127) / 128);
   if (large_tiles >= 192) return launch_ws<WIT_WS_L>(a, ta, n_tail, eq, st);
   return launch_ws<WIT_WS>(a, ta, n_tail, eq, st);
-}
-
-// The eq tables a packed witness launch builds beside its GEMM.
-int eq_aux(const char* fn, int32_t n_eq, const fp_eq_desc* eq, EqAux& aux) {
-  aux = EqAux{};
-  if (n_eq < 0 || n_eq > WIT_MAX_EQ) return fpi::fail(FP_EARG, "%s: n_eq=%d outside [0, %d]", fn, n_eq, WIT_MAX_EQ);
-  if (n_eq > 0 && !eq) return fpi::fail(FP_EARG, "%s: null eq descs", fn);
-  int64_t blocks = 0;
-  for (int32_t i = 0; i < n_eq; ++i) {
-    if (eq[i].n < 0 || eq[i].n > FP_MAX_N)
-      return fpi::fail(FP_ESHAPE, "%s: eq table %d has n=%d outside [0, %d]", fn, i, eq[i].n, FP_MAX_N);
-    if (!eq[i].E || (eq[i].n > 0 && !eq[i].r)) return fpi::fail(FP_EARG, "%s: eq table %d has a null pointer", fn, i);
-    aux.r[i] = eq[i].r;
-    aux.E[i] = eq[i].E;
-    aux.n[i] = eq[i].n;
-    aux.block_start[i] = (int32_t)blocks;
-    blocks += eq_aux_blocks(eq[i].n);
-    if (blocks > (1 << 24)) return fpi::fail(FP_ESHAPE, "%s: eq tables too large for one launch", fn);
-  }
-  aux.block_start[n_eq] = (int32_t)blocks;
-  aux.count = n_eq;
-  return FP_OK;
 }
 
 // Shared checks of the packed-weight witness entry points.

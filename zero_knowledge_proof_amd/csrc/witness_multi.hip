@@ -1,0 +1,436 @@
+// witness_multi.hip - the witness GEMMs of all the linear maps of one layer in
+// one launch, each map's claim taken from its GEMM's accumulators.
+//
+// "How fast can FlashProve go", §2: every linear map of the integer model is a
+// matmul whose rescaled output and remainder are committed and whose claim is
+// reduced by sum-check; §3.1: the claim is about the product g^ = 2^k g_w + r,
+// i.e. about Z, which therefore never has to be stored: each map's claim
+//   c0_m = sum_t sum_o E_t[t] E_o[o] Z_m[t, o]
+// is contracted out of the int32 accumulators where Z is produced (the
+// claim epilogue in witness_dev.hpp), and only Y and R leave the chip.
+//
+// One grid covers every map's tiles (the seven maps of a transformer layer:
+// Q, K, V and O over d, gate and up over d_ff, down; or the dense MLP's three),
+// so that no map's tail wave idles the GPU and maps sharing an input (Q/K/V,
+// gate/up) keep it in the L2s together. Tiles are dealt to the 8 XCDs
+// (workgroup b runs on XCD b % 8) map by map: each map's tiles are cut into 8
+// contiguous chunks, chunk x to XCD x, so every XCD gets an equal share of
+// every map (the long-K down projection included) and a run of neighbouring
+// weight panels that its L2 shares; maps run in the caller's order (longest
+// reduction first balances the end of the launch). Within a chunk, tiles walk
+// `group_o` weight panels at a time with the token tiles outermost.
+//
+// The K loop: weights come packed (fp_witness_pack_weights: a wave's operand
+// for one v_mfma_i32_32x32x32_i8 is one coalesced 1 KiB load), PFW K blocks
+// ahead into registers; X passes through NBUF LDS stages, loaded PFX blocks
+// ahead; with three stages the next block's first X fragments are read before
+// the block's barrier, so the matrix cores restart at once after it.
+#include <utility>
+
+#include "common.hpp"
+#include "eq.hpp"
+#include "witness_dev.hpp"
+
+namespace {
+
+constexpr int MM_MAX = FP_MAX_MULTI;
+constexpr int NXCD = 8;
+
+struct MmDev {
+  const int8_t* X;
+  int64_t ldx;
+  const int8_t* Wp;
+  int32_t* Z;
+  int8_t* Y;
+  int8_t* R;
+  const uint64_t* Et;
+  const uint64_t* Eo;
+  uint64_t* cout;
+  uint64_t* cpart;
+  uint32_t* cctr;
+  int32_t T, K, N, wp_rb, wp_kb, tiles_t, tiles_o, vecZ, vecYR;
+};
+
+struct MultiArgs {
+  MmDev m[MM_MAX];
+  int32_t split[MM_MAX][NXCD + 1];  // map m's tiles [split[m][x], split[m][x+1]) run on XCD x
+  int32_t count, s, group_o, gemm_blocks;
+};
+
+// Tile config: NW waves of 32 TM weight rows x 32 TN tokens.
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF>
+struct MCfg {
+  static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
+  static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32;
+  static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
+  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8;
+  static constexpr int LOOP_BYTES = NBUF * BT * PITCH;
+  static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
+  static constexpr int LDS_BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+  static_assert((BT * CPR) % NT == 0, "X chunks per thread");
+  static_assert(KS == 2, "two k-steps per packed K block");
+};
+
+// Tile `lt` of `nt` tiles of one map (a already holds the map's arguments).
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+__device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int group_o, int8_t* lds) {
+  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
+  constexpr int KS = C::KS;
+  int8_t (*sB)[BT * PITCH] = reinterpret_cast<int8_t (*)[BT * PITCH]>(lds);
+  // tile -> (token tile, output tile): groups of group_o output tiles, token tiles outermost
+  const int gsz = group_o * a.tiles_t;
+  const int g = lt / gsz, in = lt - g * gsz;
+  const int go = min(group_o, a.tiles_o - g * group_o);
+  const int to = g * group_o + in % go, tt = in / go;
+  const int t_base = tt * BT, o_base = to * BO;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int wo0 = wave * 32 * TM;
+  const int NS = a.wp_kb;
+  const int64_t rb_bytes = (int64_t)a.wp_kb * BK * 32;
+  const int8_t* pw[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) pw[i] = a.W + (int64_t)min((o_base + wo0) / 32 + i, a.wp_rb - 1) * rb_bytes + lane * 16;
+  const int8_t* px[CB];
+  int kc[CB], so[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int ch = tid + c * NT, row = ch / CPR;
+    kc[c] = (ch % CPR) * 16;
+    px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx;  // rows past T: the last row (never stored)
+    so[c] = row * PITCH + kc[c];
+  }
+  const int klim = a.K;
+  v4i wf[PFW][TM][KS];
+  v4i xr[PFX][CB];
+  v4i fb[2][TN];
+  auto wload = [&](int slot, int st) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < KS; ++q) wf[slot][i][q] = *(const v4i*)(pw[i] + (int64_t)st * (BK * 32) + 1024 * q);
+  };
+  // X chunks past d_in are read from column 0: they meet zero weights
+  auto xload = [&](int slot, int st) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int k = st * BK + kc[c];
+      xr[slot][c] = *(const v4i*)(px[c] + (k < klim ? k : 0));
+    }
+  };
+  auto sstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) *(v4i*)&sB[buf][so[c]] = xr[slot][c];
+  };
+  // X fragments of k-step q of LDS stage buf (lane: token r of each 32-row block,
+  // the 16 bytes of k the weight fragment's lane half holds)
+  auto fread = [&](int fs, int buf, int q) {
+    const int8_t* B = &sB[buf][r * PITCH + 32 * h + 16 * q];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[fs][j] = *(const v4i*)(B + 32 * j * PITCH);
+  };
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+  auto mma = [&](int fs, int ws, int q) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ws][i][q], fb[fs][j], acc[i][j], 0, 0, 0);
+  };
+  // Block st: multiply stage st % NBUF with weight slot st % PFW; store block
+  // st + NBUF - 1 (loaded PFX blocks ago) into its stage and load block
+  // st + NBUF - 1 + PFX; refill the weight slot with block st + PFW; one
+  // barrier. Every load is issued unconditionally (past the end the last block
+  // is re-read), so the code between barriers is straight-line.
+  constexpr int L2 = (PFW % 2 == 0) ? PFW : 2 * PFW;
+  constexpr int L3 = (L2 % PFX == 0) ? L2 : L2 * PFX;
+  constexpr int U = (L3 % NBUF == 0) ? L3 : L3 * NBUF;
+  if (NS > 0) {  // d_in = 0: every output is 0
+#pragma unroll
+    for (int p = 0; p < PFW; ++p) wload(p, min(p, NS - 1));
+#pragma unroll
+    for (int p = 0; p < PFX; ++p) xload(p, min(p, NS - 1));
+#pragma unroll
+    for (int sidx = 0; sidx < NBUF - 1; ++sidx) {
+      sstore(sidx % PFX, sidx);
+      xload(sidx % PFX, min(sidx + PFX, NS - 1));
+    }
+    __syncthreads();
+    if constexpr (NBUF >= 3) fread(0, 0, 0);
+    auto step = [&](auto uc, int st) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int buf = u % NBUF, ws = u % PFW;
+      if constexpr (NBUF < 3) fread(0, buf, 0);
+      fread(1, buf, 1);
+      mma(0, ws, 0);
+      constexpr int ss = (u + NBUF - 1) % PFX;
+      sstore(ss, (u + NBUF - 1) % NBUF);
+      xload(ss, min(st + NBUF - 1 + PFX, NS - 1));
+      mma(1, ws, 1);
+      wload(ws, min(st + PFW, NS - 1));
+      if constexpr (NBUF >= 3) fread(0, (u + 1) % NBUF, 0);
+      if constexpr (SCHED == 1) {
+#pragma unroll
+        for (int m = 0; m < TM * TN * KS; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        }
+      }
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + U <= NS; kt += U) {
+      [&]<int... I>(std::integer_sequence<int, I...>) { (step(std::integral_constant<int, I>{}, kt + I), ...); }(
+          std::make_integer_sequence<int, U>{});
+    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((kt + I < NS ? step(std::integral_constant<int, I>{}, kt + I) : void()), ...);
+    }(std::make_integer_sequence<int, U>{});
+  }
+
+  // ---- epilogue: Y and R (and Z through LDS if asked), the claim from the accumulators
+  const int s = a.s;
+  const bool stage = a.Z != nullptr && a.vecZ;
+  const bool claim = a.cEt != nullptr;
+  if (stage || claim) __syncthreads();  // every wave is done with the X stages
+  int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
+  uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::STAGE_BYTES;
+  uint64_t* etl = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);  // E_t of the tile's tokens
+  uint64_t* red = etl + BT;
+  v4i Aop[TM];
+  uint64_t corr = 0;  // the planes' offsets, added once per token (by the h = 0 lanes)
+  if (claim) {
+    for (int x = tid; x < BT; x += NT) {
+      const int t = t_base + x;
+      etl[x] = t < a.T ? a.cEt[t] : 0;
+    }
+    // limb table of the tile's outputs (zero past d_out: rows of Z there come
+    // from clamped weight blocks and must not count)
+    uint64_t se = 0;
+    for (int x = tid; x < BO; x += NT) {
+      const int o = o_base + x;
+      const uint64_t e = o < a.N ? a.cEo[o] : 0;
+#pragma unroll
+      for (int m = 0; m < CL_LIMBS; ++m) limbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
+      if constexpr (BO == NT) se = e;  // output tid is lane tid % 64 of its wave's range
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      Aop[i] = r < CL_LIMBS ? *(const v4i*)&limbs[r * BO + wo0 + 32 * i + 16 * h] : v4i{0, 0, 0, 0};
+    if constexpr (BO != NT) {
+#pragma unroll
+      for (int x = lane; x < 32 * TM; x += 64) {
+        const int o = o_base + wo0 + x;
+        if (o < a.N) se = gl::add(se, a.cEo[o]);
+      }
+    }
+    se = fpi::wave_total(se);  // every lane takes part
+    corr = h == 0 ? gl::mul_small(se, 128u * 65793u) : 0;
+  }
+  WitArgs yr = a;
+  if (stage) yr.Z = nullptr;
+  uint64_t wsum = 0;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    v16i D[4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int32_t z[16];
+      fragment_outputs(acc[i][j], z);
+      const int t = t_base + 32 * j + r;
+      const int o0 = o_base + wo0 + 32 * i + 16 * h;
+      if (t < a.T && o0 < a.N) store_fragment(yr, z, t, o0, s);
+      if (stage) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(v4i*)&E[r * C::EP + 16 * h + 4 * q] = v4i{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int row = 8 * p + (lane >> 3), c4 = (lane & 7) * 4;
+          const v4i v = *(const v4i*)&E[row * C::EP + c4];
+          const int tz = t_base + 32 * j + row, oz = o_base + wo0 + 32 * i + c4;
+          if (tz < a.T && oz < a.N) *(v4i*)(a.Z + (int64_t)tz * a.N + oz) = v;  // N % 4 == 0
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      if (claim) {
+        v4i P[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          uint32_t w0, w1, w2, w3;
+          foldk::transpose4((uint32_t)z[4 * gg], (uint32_t)z[4 * gg + 1], (uint32_t)z[4 * gg + 2],
+                            (uint32_t)z[4 * gg + 3], w0, w1, w2, w3);
+          P[0][gg] = (int)(w0 ^ 0x80808080u);
+          P[1][gg] = (int)(w1 ^ 0x80808080u);
+          P[2][gg] = (int)(w2 ^ 0x80808080u);
+          P[3][gg] = (int)w3;
+        }
+        const v16i zero = {};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          D[p] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop[i], P[p], i == 0 ? zero : D[p], 0, 0, 0);
+      }
+    }
+    if (claim) wsum = gl::add(wsum, gl::mul(gl::add(claim_row_value(D, h), corr), etl[32 * j + r]));
+  }
+  if (claim) claim_arrive(a, wsum, lt, nt, NW, red, reinterpret_cast<uint32_t*>(red + 8));
+}
+
+// Workgroups [0, gemm_blocks): GEMM tiles of every map (map and tile from the
+// XCD split); the rest: eq tables (for another proof: this launch's claims
+// read tables that are complete before it starts).
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_multi_kernel(
+    MultiArgs ma, EqAux eq) {
+  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  static_assert(C::NT == 256, "the eq blocks are written for 256 threads");
+  __shared__ __align__(16) int8_t lds[C::LDS_BYTES];
+  const int b = blockIdx.x;
+  if (b >= ma.gemm_blocks) {
+    eq_aux_block(eq, b - ma.gemm_blocks);
+    return;
+  }
+  const int x = b % NXCD;
+  int li = b / NXCD, m = 0;
+  for (; m < ma.count - 1; ++m) {
+    const int c = ma.split[m][x + 1] - ma.split[m][x];
+    if (li < c) break;
+    li -= c;
+  }
+  const MmDev& d = ma.m[m];
+  WitArgs a{};
+  a.X = d.X; a.ldx = d.ldx; a.W = d.Wp;
+  a.T = d.T; a.N = d.N; a.K = d.K; a.s = ma.s;
+  a.Z = d.Z; a.Y = d.Y; a.R = d.R;
+  a.tiles_t = d.tiles_t; a.tiles_o = d.tiles_o;
+  a.vecZ = d.vecZ; a.vecYR = d.vecYR;
+  a.wp_rb = d.wp_rb; a.wp_kb = d.wp_kb;
+  a.cEt = d.Et; a.cEo = d.Eo; a.cpart = d.cpart; a.cout = d.cout; a.cctr = d.cctr;
+  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED>(a, ma.split[m][x] + li, d.tiles_t * d.tiles_o, ma.group_o, lds);
+}
+
+// 256 x 128 tiles (4 waves of 64 x 128), weights 3 blocks ahead, X 3 blocks
+// ahead through 3 LDS stages.
+#define WIT_MULTI 4, 2, 4, 3, 3, 3, 0
+using MC = MCfg<4, 2, 4, 3, 3, 3>;
+constexpr int MULTI_WAVES = 4;
+
+struct MultiPlan {
+  int64_t tiles[MM_MAX];
+  size_t part_off[MM_MAX];
+  size_t bytes;
+};
+
+// Workspace: arrival counters (one 64-byte line per map), then one slot per
+// GEMM wave of every map that forms a claim.
+int multi_plan(const char* fn, int32_t count, const fp_matmul_desc* mm, MultiPlan& p) {
+  if (count < 1 || count > MM_MAX) return fpi::fail(FP_EARG, "%s: count=%d outside [1, %d]", fn, count, MM_MAX);
+  if (!mm) return fpi::fail(FP_EARG, "%s: null descs", fn);
+  size_t off = fpi::align_up((size_t)MM_MAX * 64, 256);
+  for (int i = 0; i < count; ++i) {
+    const fp_matmul_desc& d = mm[i];
+    if (d.T < 0 || d.d_in < 0 || d.d_out < 0) return fpi::fail(FP_EARG, "%s: map %d has a negative size", fn, i);
+    const int64_t tiles = (int64_t)((d.T + MC::BT - 1) / MC::BT) * ((d.d_out + MC::BO - 1) / MC::BO);
+    p.tiles[i] = tiles;
+    p.part_off[i] = off;
+    if (d.E_t) off += fpi::align_up((size_t)tiles * MULTI_WAVES * 8, 256);
+  }
+  p.bytes = off;
+  return FP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm) {
+  MultiPlan p;
+  if (multi_plan("fp_witness_multi_workspace", count, mm, p)) return 0;
+  return p.bytes;
+}
+
+extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                                const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_witness_multi";
+  MultiPlan p;
+  int rc = multi_plan(fn, count, mm, p);
+  if (rc) return rc;
+  if (s < 1 || s > 8) return fpi::fail(FP_ERANGE, "%s: s=%d outside [1, 8]", fn, s);
+  if (group_o < 1) return fpi::fail(FP_EARG, "%s: group_o=%d < 1", fn, group_o);
+  bool any_claim = false;
+  MultiArgs ma{};
+  ma.count = count;
+  ma.s = s;
+  ma.group_o = group_o;
+  int64_t total = 0, rem_before = 0;
+  for (int i = 0; i < count; ++i) {
+    const fp_matmul_desc& d = mm[i];
+    if (d.d_in > FP_MAX_DIN) return fpi::fail(FP_ESHAPE, "%s: map %d has d_in=%d > %d", fn, i, d.d_in, FP_MAX_DIN);
+    const bool work = d.T > 0 && d.d_out > 0;
+    if (work && (!d.Y || !d.R)) return fpi::fail(FP_EARG, "%s: map %d has a null Y or R", fn, i);
+    if (work && d.d_in > 0) {
+      if (!d.X || !d.Wp) return fpi::fail(FP_EARG, "%s: map %d has a null X or packed W", fn, i);
+      if (d.d_in % 16 != 0 || d.ldx % 16 != 0 || (((uintptr_t)d.X) & 15) != 0 || (((uintptr_t)d.Wp) & 15) != 0)
+        return fpi::fail(FP_ESHAPE, "%s: map %d needs d_in %% 16 == 0 and 16-byte aligned X rows and packed W", fn,
+                         i);
+    }
+    if (d.ldx < d.d_in) return fpi::fail(FP_ESHAPE, "%s: map %d has ldx < d_in", fn, i);
+    if (d.E_t) {
+      if (!work) return fpi::fail(FP_ESHAPE, "%s: map %d forms a claim but has no outputs", fn, i);
+      if (!d.E_o || !d.claim) return fpi::fail(FP_EARG, "%s: map %d has E_t but a null E_o or claim", fn, i);
+      any_claim = true;
+    }
+    MmDev& m = ma.m[i];
+    m.X = d.X; m.ldx = d.ldx; m.Wp = d.Wp;
+    m.Z = d.Z; m.Y = d.Y; m.R = d.R;
+    m.T = d.T; m.K = d.d_in; m.N = d.d_out;
+    m.wp_rb = (d.d_out + 31) / 32;
+    m.wp_kb = (d.d_in + WP_BK - 1) / WP_BK;
+    m.tiles_t = (d.T + MC::BT - 1) / MC::BT;
+    m.tiles_o = (d.d_out + MC::BO - 1) / MC::BO;
+    m.vecZ = ((d.d_out & 3) == 0) && ((((uintptr_t)d.Z) & 15) == 0);
+    m.vecYR = ((d.d_out & 15) == 0) && ((((uintptr_t)d.Y) & 15) == 0) && ((((uintptr_t)d.R) & 15) == 0);
+    if (d.E_t) {
+      m.Et = d.E_t; m.Eo = d.E_o; m.cout = d.claim;
+      m.cctr = (uint32_t*)((char*)ws + 64 * i);
+      m.cpart = (uint64_t*)((char*)ws + p.part_off[i]);
+    }
+    // deal the map's tiles to the XCDs: equal contiguous chunks, the remainders
+    // rotating across maps so that XCD x gets exactly the workgroups b % 8 == x
+    const int64_t n = work ? p.tiles[i] : 0;
+    const int64_t base = n / NXCD, rem = n % NXCD;
+    int64_t off = 0;
+    for (int x = 0; x < NXCD; ++x) {
+      ma.split[i][x] = (int32_t)off;
+      const int64_t extra = ((x - rem_before) % NXCD + NXCD) % NXCD < rem ? 1 : 0;
+      off += base + extra;
+    }
+    ma.split[i][NXCD] = (int32_t)off;
+    rem_before += rem;
+    total += n;
+  }
+  if (any_claim) {
+    if (!ws || ws_bytes < p.bytes)
+      return fpi::fail(FP_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, p.bytes);
+    if ((((uintptr_t)ws) & 255) != 0) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
+  }
+  EqAux aux;
+  rc = eq_aux(fn, n_eq, eq, aux);
+  if (rc) return rc;
+  if (total + aux.block_start[aux.count] > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many tiles", fn);
+  ma.gemm_blocks = (int32_t)total;
+  const int64_t grid = total + aux.block_start[aux.count];
+  if (grid == 0) return fpi::ok();
+  hipLaunchKernelGGL((witness_multi_kernel<WIT_MULTI>), dim3((unsigned)grid), dim3(MC::NT), 0, stream, ma, aux);
+  rc = fpi::check_launch("witness_multi_kernel");
+  return rc ? rc : fpi::ok();
+}

@@ -23,11 +23,12 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (StepWorkspace, combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
+from . import (MatmulJob, StepWorkspace, combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
                ext_claim_combine, field_numpy, fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows,
                layer_step, linear_combine, merkle_commit, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs,
                sumcheck_prove, sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped,
-               witness_linear_packed, witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck)
+               witness_linear_packed, witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck,
+               witness_multi)
 
 
 def _nomark(name):
@@ -343,21 +344,32 @@ class MultiMatmulProver(_Prover):
     merged by a random linear combination (the dense MLP's gate/up/down).
     mode "batched": the claims are merged first (rho-weighted) and proved by
     one batched sum-check over tables padded to 2^batched_n (all seven maps of
-    a transformer layer)."""
+    a transformer layer).
+
+    Maps whose d_in is a multiple of 16 (every map of the full-size layers)
+    run their witness GEMMs in ONE launch (fp_witness_multi, longest reduction
+    first) that also forms each map's claim c0 = Z~(r_o || r_t) from the GEMM's
+    accumulators, so Z is neither stored nor read back; the eq tables are built
+    first, since that launch's claims read them. Other maps take the row-major
+    witness and their claims are taken from the stored Z in the fold launch.
+    keep_z: also store Z (for tests)."""
 
     def output_tensors(self):
         out = [self.E_t]
         for d in self.mm:
-            out += [d[k] for k in ("Z", "Y", "R", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0") if k in d]
+            out += [d[k] for k in ("Z", "Y", "R", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0")
+                    if d.get(k) is not None]
         for k in ("rlc", "c0_batch", "rounds", "finals", "claim0"):
             if hasattr(self, k):
                 out.append(getattr(self, k))
         return out
 
-    def __init__(self, cfg, inp: dict, ch: dict, dev=None):
+    def __init__(self, cfg, inp: dict, ch: dict, dev=None, keep_z: bool = False, group_o: int = 1):
         dev = dev or torch.device("cuda")
         self.cfg = cfg
         self.mode = cfg.kind
+        self.keep_z = keep_z
+        self.group_o = group_o
         s = cfg.s
         self.s = s
         self.tens = {}
@@ -371,13 +383,16 @@ class MultiMatmulProver(_Prover):
         self.mm = []
         nb = cfg.batched_n if self.mode == "batched" else None
         xf = {}
+        self.packed = {m.w: _packed(self.tens[m.w]) for m in cfg.matmuls}
         for m in cfg.matmuls:
             n = nb if nb is not None else m.n
             key = (m.x, n)
             if key not in xf:
                 xf[key] = _f(1 << n, dev)
+            fused = self.packed[m.w] is not None
             d = {"m": m, "n": n, "xf": xf[key], "wf": _f(1 << n, dev), "E_o": _f(1 << m.n_o, dev),
-                 "Z": torch.empty((T, m.d_out), dtype=torch.int32, device=dev),
+                 "fused": fused,
+                 "Z": torch.empty((T, m.d_out), dtype=torch.int32, device=dev) if (keep_z or not fused) else None,
                  "Y": torch.empty((T, m.d_out), dtype=torch.int8, device=dev),
                  "R": torch.empty((T, m.d_out), dtype=torch.int8, device=dev), "c0": _f(1, dev)}
             if self.mode == "rlc_out":
@@ -385,43 +400,36 @@ class MultiMatmulProver(_Prover):
                          finals=torch.empty((1, 2), dtype=torch.int64, device=dev), claim0=_f(1, dev))
             self.mm.append(d)
         self.x_jobs = [(self.tens[x], None, 1 << n, buf) for (x, n), buf in xf.items()]
-        self.packed = {m.w: _packed(self.tens[m.w]) for m in cfg.matmuls}
+        # the maps of the one-launch witness, longest reduction first
+        fused = sorted((d for d in self.mm if d["fused"]), key=lambda d: -d["m"].d_in)
+        self.jobs = [MatmulJob(self.tens[d["m"].x], self.packed[d["m"].w], d["Y"], d["R"], d["Z"], self.E_t, d["E_o"],
+                               d["c0"]) for d in fused]
+        self.ws = StepWorkspace()
+        self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
         if self.mode == "rlc_out":
-            self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
             self.rlc = _f(1, dev)
         else:
-            self.rho = torch.cat([self.ch["rho/" + m.name] for m in cfg.matmuls]).contiguous()
             self.c0_batch = _f(1, dev)
             self.rounds = torch.empty((nb, 3), dtype=torch.int64, device=dev)
             self.finals = torch.empty((len(cfg.matmuls), 2), dtype=torch.int64, device=dev)
             self.claim0 = _f(1, dev)
 
-    def _eq_pairs(self):
-        return [(self.ch["r_t"], self.E_t)] + [(self.ch["r_o/" + d["m"].name], d["E_o"]) for d in self.mm]
-
-    def _fuse_eq(self) -> bool:
-        # the first packed witness launch can build all eq tables (at most 8 per launch)
-        return any(v is not None for v in self.packed.values()) and len(self.mm) + 1 <= 8
-
-    def _witness(self, with_eq: bool = False):
-        eq = self._eq_pairs() if with_eq else None
-        for d in self.mm:
-            m = d["m"]
-            Wp = self.packed[m.w]
-            if Wp is not None:
-                witness_linear_packed(self.tens[m.x], Wp, self.s, d["Z"], d["Y"], d["R"], eq=eq)
-                eq = None
-            else:
-                witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
-
     def _eq(self):
         eq_table_batched([self.ch["r_t"]] + [self.ch["r_o/" + d["m"].name] for d in self.mm],
                          [self.E_t] + [d["E_o"] for d in self.mm])
 
+    def _witness(self):
+        if self.jobs:
+            witness_multi(self.jobs, self.s, group_o=self.group_o, ws=self.ws)
+        for d in self.mm:
+            if not d["fused"]:
+                m = d["m"]
+                witness_linear(self.tens[m.x], self.tens[m.w], self.s, d["Z"], d["Y"], d["R"])
+
     def _fold_claim(self):
         jobs = [(M, self.E_t, cp, out) for (M, _, cp, out) in self.x_jobs]
         jobs += [(self.tens[d["m"].w], d["E_o"], 1 << d["n"], d["wf"]) for d in self.mm]
-        fold_claim_batched(jobs, [(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm])
+        fold_claim_batched(jobs, [(d["Z"], self.E_t, d["E_o"], d["c0"]) for d in self.mm if not d["fused"]])
 
     def _sumcheck(self):
         if self.mode == "rlc_out":
@@ -438,12 +446,10 @@ class MultiMatmulProver(_Prover):
                        [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=self.rlc)
 
     def phases(self):
-        if self._fuse_eq():
-            ph = [("witness+eq", lambda: self._witness(with_eq=True)), ("fold+claim", self._fold_claim),
-                  ("sumcheck", self._sumcheck)]
-        else:
-            ph = [("witness", self._witness), ("eq", self._eq), ("fold+claim", self._fold_claim),
-                  ("sumcheck", self._sumcheck)]
+        all_fused = all(d["fused"] for d in self.mm)
+        wname = "witness(Y,R)+claim(acc)" if all_fused and not self.keep_z else "witness+claim(acc)"
+        ph = [("eq", self._eq), (wname, self._witness), ("fold" if all_fused else "fold+claim", self._fold_claim),
+              ("sumcheck", self._sumcheck)]
         if self.mode == "rlc_out":
             ph.append(("merge", self._merge))
         return ph
@@ -451,9 +457,11 @@ class MultiMatmulProver(_Prover):
     def results(self) -> dict:
         out = {"E_t": field_numpy(self.E_t)}
         for d in self.mm:
-            r = {"Z": d["Z"].cpu().numpy(), "Y": d["Y"].cpu().numpy(), "R": d["R"].cpu().numpy(),
+            r = {"Y": d["Y"].cpu().numpy(), "R": d["R"].cpu().numpy(),
                  "E_o": field_numpy(d["E_o"]), "x_fold": field_numpy(d["xf"]), "w_fold": field_numpy(d["wf"]),
                  "c0": int(field_numpy(d["c0"])[0])}
+            if d["Z"] is not None:
+                r["Z"] = d["Z"].cpu().numpy()
             if self.mode == "rlc_out":
                 r.update(rounds=field_numpy(d["rounds"]), finals=field_numpy(d["finals"]),
                          claim0=int(field_numpy(d["claim0"])[0]))
@@ -706,7 +714,7 @@ def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, ove
     if pipelined:
         raise ValueError("pipelined proofs are implemented for single-matmul layers")
     if cfg.kind in ("rlc_out", "batched"):
-        return MultiMatmulProver(cfg, inp, ch, dev)
+        return MultiMatmulProver(cfg, inp, ch, dev, keep_z=keep_z)
     if cfg.kind == "moe":
         return MoEBlockProver(cfg, inp, ch, dev)
     raise ValueError(cfg.kind)
