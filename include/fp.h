@@ -467,6 +467,21 @@ int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t
 /* Bytes of fp_witness_multi's workspace for these maps; 0 on bad arguments. */
 size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm);
 
+/* fp_witness_multi without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the arrival counters and claim slots live
+ * in a scratch array of FP_WITNESS_MULTI_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends. The call allocates nothing; on its
+ * first call on a device it looks the array's address up (hipGetSymbolAddress).
+ * Arguments, outputs and errors as fp_witness_multi; maps whose
+ * fp_witness_multi_workspace exceeds the array are refused with
+ * FP_EWORKSPACE. Every call on a GPU shares that GPU's array: the call first
+ * clears its counters on the stream, and calls that overlap on one GPU (other
+ * streams, other threads) race and must not be issued. */
+#define FP_WITNESS_MULTI_SCRATCH_BYTES (1 << 20)
+int fp_witness_multi_noalloc(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                             const fp_eq_desc* eq, hipStream_t stream);
+
 /* ----------------------------------------------------------- sum-check --- */
 /* Sum-check of the claim sum_j rho_j sum_k A_j[k] B_j[k] over n_pairs pairs of
  * tables of 2^n entries ("How fast can FlashProve go", §2: sum-check reduces

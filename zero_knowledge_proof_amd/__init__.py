@@ -32,6 +32,7 @@ EXPORTS = [
     "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
     "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
     "fp_layer_step", "fp_layer_step_workspace", "fp_witness_multi", "fp_witness_multi_workspace",
+    "fp_witness_multi_noalloc",
 ]
 
 _lib = None
@@ -124,6 +125,7 @@ def lib():
                                              i32, vp, vp, sz, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
             "fp_witness_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp, sz, vp]),
             "fp_witness_multi_workspace": (sz, [i32, vp]),
+            "fp_witness_multi_noalloc": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -402,6 +404,14 @@ def witness_multi(jobs, s: int, group_o: int = 1, eq=None, ws: StepWorkspace | N
     ws = _ws_step if ws is None else ws
     p, nb = ws.get(lib().fp_witness_multi_workspace(len(jobs), arr))
     _check(lib().fp_witness_multi(len(jobs), arr, s, group_o, ne, eqd, p, nb, _stream()), "fp_witness_multi")
+
+
+def witness_multi_noalloc(jobs, s: int, group_o: int = 1, eq=None):
+    """witness_multi without a workspace: the library's own scratch array holds the claims' slots and
+    counters (calls that overlap on one GPU race)."""
+    arr = _multi_descs(jobs)
+    ne, eqd = _eq_descs(eq)
+    _check(lib().fp_witness_multi_noalloc(len(jobs), arr, s, group_o, ne, eqd, _stream()), "fp_witness_multi_noalloc")
 
 
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):

@@ -25,6 +25,7 @@
 // ahead into registers; X passes through NBUF LDS stages, loaded PFX blocks
 // ahead; with three stages the next block's first X fragments are read before
 // the block's barrier, so the matrix cores restart at once after it.
+#include <mutex>
 #include <utility>
 
 #include "common.hpp"
@@ -350,6 +351,39 @@ int multi_plan(const char* fn, int32_t count, const fp_matmul_desc* mm, MultiPla
   return FP_OK;
 }
 
+// Scratch of the allocation-free variant: arrival counters and claim slots in
+// a file-scope device array (each GPU holds its own copy until the process
+// ends). Host code reaches it only through the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[FP_WITNESS_MULTI_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The scratch array's device address on the current device (looked up once per device).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return fpi::fail(FP_EHIP, "%s: no current device (or device index >= %d)", fn, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fpi::fail(FP_EHIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP_OK;
+}
+
+// Zeroes n 32-bit words (the arrival counters before an allocation-free call).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0;
+}
+
 }  // namespace
 
 extern "C" size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm) {
@@ -358,9 +392,12 @@ extern "C" size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc
   return p.bytes;
 }
 
-extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
-                                const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "fp_witness_multi";
+namespace {
+
+// fp_witness_multi's checks and launch; noalloc: ws is the scratch array (its
+// counters cleared first on the stream).
+int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                 const fp_eq_desc* eq, void* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
   MultiPlan p;
   int rc = multi_plan(fn, count, mm, p);
   if (rc) return rc;
@@ -419,6 +456,9 @@ extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t
     total += n;
   }
   if (any_claim) {
+    if (noalloc && p.bytes > FP_WITNESS_MULTI_SCRATCH_BYTES)
+      return fpi::fail(FP_EWORKSPACE, "%s: these maps need %zu bytes of scratch, more than the %d the library holds", fn,
+                       p.bytes, FP_WITNESS_MULTI_SCRATCH_BYTES);
     if (!ws || ws_bytes < p.bytes)
       return fpi::fail(FP_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, p.bytes);
     if ((((uintptr_t)ws) & 255) != 0) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
@@ -430,7 +470,28 @@ extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t
   ma.gemm_blocks = (int32_t)total;
   const int64_t grid = total + aux.block_start[aux.count];
   if (grid == 0) return fpi::ok();
+  if (noalloc && any_claim) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, (uint32_t*)ws, MM_MAX * 16);
+    rc = fpi::check_launch("clear_words_kernel");
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL((witness_multi_kernel<WIT_MULTI>), dim3((unsigned)grid), dim3(MC::NT), 0, stream, ma, aux);
   rc = fpi::check_launch("witness_multi_kernel");
   return rc ? rc : fpi::ok();
+}
+
+}  // namespace
+
+extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                                const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return multi_launch("fp_witness_multi", count, mm, s, group_o, n_eq, eq, ws, ws_bytes, false, stream);
+}
+
+extern "C" int fp_witness_multi_noalloc(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o,
+                                        int32_t n_eq, const fp_eq_desc* eq, hipStream_t stream) {
+  const char* fn = "fp_witness_multi_noalloc";
+  void* ws = nullptr;
+  const int rc = scratch_address(fn, &ws);
+  if (rc) return rc;
+  return multi_launch(fn, count, mm, s, group_o, n_eq, eq, ws, FP_WITNESS_MULTI_SCRATCH_BYTES, true, stream);
 }
