@@ -569,8 +569,12 @@ def main():
     cfg = synth.config(args.config)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
-    pipelined = (not args.no_pipeline) and can_pipeline(cfg)
-    overlapped = pipelined and (not args.no_overlap) and can_overlap(cfg)
+    if cfg.kind in ("rlc_out", "batched"):  # multi-map layers: one proof in flight, or three
+        pipelined = False
+        overlapped = (not args.no_pipeline) and (not args.no_overlap) and can_overlap(cfg)
+    else:
+        pipelined = (not args.no_pipeline) and can_pipeline(cfg)
+        overlapped = pipelined and (not args.no_overlap) and can_overlap(cfg)
     prover = make_prover(cfg, inp, ch, dev, pipelined=pipelined, overlapped=overlapped)
     stream = torch.cuda.current_stream()
 

@@ -444,8 +444,9 @@ size_t fp_layer_step_workspace(int32_t T, int32_t d_out, int32_t own_claim, int3
  * workgroups of the same launch: tables of another proof, not ones this
  * launch's claims read. ws: fp_witness_multi_workspace(count, mm) bytes,
  * 256-byte aligned, needed when some map forms a claim (else may be NULL);
- * its first FP_MAX_MULTI * 64 bytes (arrival counters) must be zero on entry
- * and every call leaves them zero. Errors: FP_EARG (count outside [1,
+ * its first FP_MAX_MULTI * 64 + FP_FOLD_COUNTER_BYTES bytes (arrival counters,
+ * the same layout as fp_layer_step_multi's, so one workspace serves both) must
+ * be zero on entry and every call leaves them zero. Errors: FP_EARG (count outside [1,
  * FP_MAX_MULTI], null pointers, group_o < 1), FP_ESHAPE (alignment, d_in >
  * FP_MAX_DIN, a claim without outputs), FP_ERANGE (s outside [1, 8]),
  * FP_EWORKSPACE. Maps must not write each other's inputs. */
@@ -466,6 +467,48 @@ int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t
                      const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream);
 /* Bytes of fp_witness_multi's workspace for these maps; 0 on bad arguments. */
 size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm);
+
+/* One step of a stream of proofs of a multi-map layer in ONE launch: the
+ * witness GEMMs and claims of proof k (exactly fp_witness_multi(count, mm, s,
+ * group_o, n_eq, eq, ...)), the int8 folds of proof k-1 (exactly
+ * fp_fold_matrix_batched(FP_I8, n_fold, folds, ...)) and the n_sc sum-check
+ * instances of proof k-2 (each exactly fp_sumcheck_prove(n_pairs, A, B, rho,
+ * n, r, rounds, finals, claim0)). The three share no data ("How fast can
+ * FlashProve go", §2: each map's witness, then its folds and its sum-check),
+ * so their workgroups run side by side: each sum-check instance is one
+ * workgroup (its first rounds stream the tables through the workspace, the
+ * rest run in registers; every round's sums are complete across the
+ * workgroup before its challenge is applied), the folds' cross-chunk sums are
+ * done by the last workgroup of each column strip, and the GEMM tiles fill
+ * the GPU. Inputs of one part must not be written by another part of the
+ * same call (the sum-check tables are proof k-2's folds, the folds write
+ * proof k-1's). At most FP_STEP_MULTI_MAX_FOLD folds (each with rows and
+ * columns) and FP_STEP_MULTI_MAX_SUMCHECK instances of 1..8 pairs with
+ * 1 <= n <= FP_STEP_MULTI_MAX_SC_N and 16-byte aligned tables. ws:
+ * fp_layer_step_multi_workspace(...) bytes, 256-byte aligned; its first
+ * FP_MAX_MULTI * 64 + FP_FOLD_COUNTER_BYTES bytes (arrival counters) must be
+ * zero on entry, and every call leaves them zero. Errors as fp_witness_multi,
+ * plus FP_EARG/FP_ESHAPE for the folds' and sum-checks' arguments. */
+#define FP_STEP_MULTI_MAX_FOLD 12
+#define FP_STEP_MULTI_MAX_SUMCHECK 4
+#define FP_STEP_MULTI_MAX_SC_N 20
+#define FP_SC_DESC_MAX_PAIRS 8
+typedef struct {
+  int32_t n_pairs, n;
+  const fp_elem* A[FP_SC_DESC_MAX_PAIRS]; /* device tables of 2^n entries */
+  const fp_elem* B[FP_SC_DESC_MAX_PAIRS];
+  const fp_elem* rho; /* device n_pairs weights, or NULL (all ones) */
+  const fp_elem* r;   /* device n challenges */
+  fp_elem* rounds;    /* device [n][3] */
+  fp_elem* finals;    /* device [n_pairs][2] */
+  fp_elem* claim0;    /* device 1, or NULL */
+} fp_sumcheck_desc;
+int fp_layer_step_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                        const fp_eq_desc* eq, int32_t n_fold, const fp_fold_desc* folds, int32_t n_sc,
+                        const fp_sumcheck_desc* sc, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Bytes of fp_layer_step_multi's workspace; 0 on bad arguments. */
+size_t fp_layer_step_multi_workspace(int32_t count, const fp_matmul_desc* mm, int32_t n_fold,
+                                     const fp_fold_desc* folds, int32_t n_sc, const fp_sumcheck_desc* sc);
 
 /* fp_witness_multi without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

@@ -144,6 +144,38 @@ def test_layer_overlapped(fp, cid, shape, runs, keep_z):
     assert got["c0"] == got["claim0"]
 
 
+@pytest.mark.parametrize("cid,shape,runs,keep_z", [(3, dict(T=300, d=256, d_ff=1024), 1, False),
+                                                   (3, dict(T=300, d=256, d_ff=1024), 4, True),
+                                                   (5, dict(T=200, d=128, d_kv=64, d_ff=320), 2, False),
+                                                   (5, dict(T=200, d=128, d_kv=64, d_ff=320), 5, False)])
+def test_layer_overlapped_multi(fp, cid, shape, runs, keep_z):
+    """Three proofs of a multi-map layer in flight (each step one launch: this proof's GEMMs with every claim
+    from the accumulators, the next proof's eq tables, the previous proof's folds and the sum-check of the one
+    before, each instance one workgroup; then the merge of that proof's claims): after the runs and the drain,
+    every proof still held (each has its own outputs) equals the oracle's."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg)
+    prover = make_prover(cfg, inp, ch, overlapped=True, keep_z=keep_z)
+    for _ in range(runs):
+        prover.run()
+    prover.drain()
+    torch.cuda.synchronize()
+    want = O.prove_config(cfg, inp, ch)
+    for k in range(max(0, runs - 3), runs):
+        got = prover.results(k)
+        for m in cfg.matmuls:
+            assert ("Z" in got[m.name]) == keep_z
+            keys = ("Z", "Y", "R", "x_fold", "w_fold", "c0") + (("rounds", "finals", "claim0") if cid == 3 else ())
+            _cmp_matmul(got[m.name], want[m.name], keys=keys)
+        if cid == 3:
+            assert got["rlc"] == want["rlc"]
+        else:
+            for kk in ("rounds", "finals"):
+                assert np.array_equal(got["batch"][kk], want["batch"][kk]), kk
+            assert got["batch"]["claim0"] == want["batch"]["claim0"] == want["batch"]["c0"] == got["batch"]["c0"]
+
+
 # ------------------------------------------------------- full-size checks --
 def _sampled_witness(X, W, got, s, n=2048, seed=0):
     rng = np.random.default_rng(seed)
@@ -297,6 +329,52 @@ def test_full_cfg5(fp):
     assert np.array_equal(b["rounds"], rounds) and np.array_equal(b["finals"], finals)
     assert b["claim0"] == claim0 == c0 == b["c0"]
     _same_without_z(cfg, inp, ch, got)
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_full_overlapped_multi(fp, cid):
+    """The benchmark's launch configuration for the dense MLP and the seven-map layer: three proofs in flight,
+    six steps per graph replay, two replays, the drain: each of the last three proofs equals a one-proof run
+    that stores Z (whose Z, Y, R, folds, claims and rounds are checked against the oracle in test_full_cfg3/5)
+    output by output, and its folds, rounds and claims equal the oracle's."""
+    cfg = synth.config(cid)
+    inp = synth.make_inputs(cfg)
+    ch = synth.draw_challenges(cfg)
+    ref = make_prover(cfg, inp, ch)
+    ref.run()
+    torch.cuda.synchronize()
+    want = ref.results()
+    del ref
+    prover = make_prover(cfg, inp, ch, overlapped=True)
+    prover.capture(steps=6)
+    prover.replay()
+    prover.replay()
+    prover.drain()
+    torch.cuda.synchronize()
+    E_t = O.eq_table(ch["r_t"])
+    xs = {}
+    for k in range(prover.k - 3, prover.k):
+        got = prover.results(k)
+        for m in cfg.matmuls:
+            g, w = got[m.name], want[m.name]
+            for key in ("Y", "R", "x_fold", "w_fold", "c0", "rounds", "finals", "claim0"):
+                if key in w:
+                    assert np.array_equal(np.asarray(g[key]), np.asarray(w[key])), (k, m.name, key)
+            n = cfg.batched_n if cid == 5 else m.n
+            if (m.x, n) not in xs:
+                xs[(m.x, n)] = O.fold_rows(inp[m.x], E_t, 1 << n)
+            assert np.array_equal(g["x_fold"], xs[(m.x, n)])
+            assert np.array_equal(g["w_fold"], O.fold_rows(inp[m.w], O.eq_table(ch["r_o/" + m.name]), 1 << n))
+        if cid == 3:
+            assert got["rlc"] == want["rlc"]
+        else:
+            for key in ("rounds", "finals", "claim0", "c0"):
+                assert np.array_equal(np.asarray(got["batch"][key]), np.asarray(want["batch"][key])), key
+            As = [xs[(m.x, cfg.batched_n)] for m in cfg.matmuls]
+            Bs = [got[m.name]["w_fold"] for m in cfg.matmuls]
+            rounds, finals, claim0 = O.sumcheck(As, Bs, ch["rounds"], rho=[int(ch["rho/" + m.name][0])
+                                                                           for m in cfg.matmuls])
+            assert np.array_equal(got["batch"]["rounds"], rounds) and got["batch"]["claim0"] == claim0
 
 
 def test_full_cfg4_sampled_experts(fp):

@@ -167,3 +167,99 @@ def test_witness_multi_errors(fp):
     arr = fp._multi_descs([ok])
     with pytest.raises(RuntimeError):
         fp._check(lib.fp_witness_multi(1, arr, 8, 1, 0, None, None, 0, fp._stream()), "fp_witness_multi")
+
+
+# ------------------------------------------------- fp_layer_step_multi ---
+def _small_map(fp, rng, T=64, d_in=64, d_out=96):
+    X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+    Z, Y, R = O.witness(X, W, 8)
+    Y_d = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R_d = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    return fp.MatmulJob(_dev(X), fp.pack_weights(_dev(W)), Y_d, R_d), (Y, R)
+
+
+@pytest.mark.parametrize("insts", [[(1, 1)], [(1, 12)], [(1, 13)], [(1, 14)], [(3, 12), (2, 9)], [(7, 14)],
+                                   [(8, 16), (1, 5), (5, 13), (2, 3)], [(2, 18)]])
+def test_layer_step_multi_sumchecks(fp, insts):
+    """Whole sum-check instances run by single workgroups of the step launch (streamed rounds, then the register
+    tail; i0 from 0 to 9), with and without rho, beside a GEMM: rounds, finals and the initial claim equal the
+    oracle's sum-check, on two calls in a row."""
+    rng = _rng(zlib.crc32(repr(insts).encode()))
+    job, (Y, R) = _small_map(fp, rng)
+    scs, wants = [], []
+    for idx, (k, n) in enumerate(insts):
+        As = [_field(rng, 1 << n) for _ in range(k)]
+        Bs = [_field(rng, 1 << n) for _ in range(k)]
+        r = _field(rng, n)
+        rho = [int(v) for v in _field(rng, k)] if idx % 2 == 0 else None
+        wants.append(O.sumcheck(As, Bs, r, rho=rho))
+        scs.append(fp.SumcheckJob([fp.to_field_tensor(a) for a in As], [fp.to_field_tensor(b) for b in Bs],
+                                  fp.to_field_tensor(r), torch.empty((n, 3), dtype=torch.int64, device="cuda"),
+                                  torch.empty((k, 2), dtype=torch.int64, device="cuda"),
+                                  torch.empty(1, dtype=torch.int64, device="cuda"),
+                                  rho=fp.to_field_tensor(np.array(rho, np.uint64)) if rho else None))
+    ws = fp.StepWorkspace()
+    for rep in range(2):
+        for j in scs:
+            j.rounds.fill_(-1)
+            j.claim0.fill_(-1)
+        fp.layer_step_multi([job], 8, sumchecks=scs, ws=ws)
+        torch.cuda.synchronize()
+        for j, (rounds, finals, claim0) in zip(scs, wants):
+            assert np.array_equal(fp.field_numpy(j.rounds), rounds)
+            assert np.array_equal(fp.field_numpy(j.finals).reshape(-1, 2), finals)
+            assert int(fp.field_numpy(j.claim0)[0]) == claim0
+        assert np.array_equal(job.Y.cpu().numpy(), Y) and np.array_equal(job.R.cpu().numpy(), R)
+        assert int(ws.buf[:512 + 16384].count_nonzero()) == 0
+
+
+def test_layer_step_multi_folds_claims_and_eq(fp):
+    """All the parts in one launch: two maps' GEMMs with claims from the accumulators, eleven folds of other
+    tables (int8, ragged, padded columns) in arrival mode, eq tables and a sum-check: every output equals the
+    oracle's, and the arrival counters are zero after each of two calls."""
+    rng = _rng(909)
+    T = 300
+    maps, wants = [], []
+    rt = _field(rng, 9)
+    Et = fp.to_field_tensor(O.eq_table(rt))
+    for d_in, d_out in ((1024, 700), (512, 256)):
+        X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+        ro = _field(rng, (d_out - 1).bit_length())
+        Z, Y, R = O.witness(X, W, 8)
+        wants.append((Y, R, O.mle_matrix(Z, rt, ro)))
+        maps.append(fp.MatmulJob(_dev(X), fp.pack_weights(_dev(W)), torch.empty((T, d_out), dtype=torch.int8,
+                                 device="cuda"), torch.empty((T, d_out), dtype=torch.int8, device="cuda"), None, Et,
+                                 fp.to_field_tensor(O.eq_table(ro)), torch.empty(1, dtype=torch.int64, device="cuda")))
+    folds, fwant = [], []
+    for (rows, cols, cp) in [(300, 1000, 1024), (1, 16, 16), (4100, 96, 128), (77, 4096, 4096), (2048, 5120, 8192),
+                             (700, 200, 256), (33, 1024, 1024), (14336, 256, 256), (5, 5, 8), (64, 64, 128),
+                             (1000, 300, 512)]:
+        M = _i8(rng, (rows, cols))
+        E = _field(rng, rows)
+        out = torch.full((cp,), -1, dtype=torch.int64, device="cuda")
+        folds.append((_dev(M), fp.to_field_tensor(E), cp, out))
+        fwant.append(O.fold_rows(M, E, cp))
+    re = [_field(rng, 12), _field(rng, 3)]
+    Es = [torch.empty(1 << 12, dtype=torch.int64, device="cuda"), torch.empty(8, dtype=torch.int64, device="cuda")]
+    As, Bs, r = [_field(rng, 1 << 13)], [_field(rng, 1 << 13)], _field(rng, 13)
+    sc = fp.SumcheckJob([fp.to_field_tensor(As[0])], [fp.to_field_tensor(Bs[0])], fp.to_field_tensor(r),
+                        torch.empty((13, 3), dtype=torch.int64, device="cuda"),
+                        torch.empty((1, 2), dtype=torch.int64, device="cuda"))
+    swant = O.sumcheck(As, Bs, r)
+    ws = fp.StepWorkspace()
+    for rep in range(2):
+        for (_, _, _, out) in folds:
+            out.fill_(-1)
+        fp.layer_step_multi(maps, 8, group_o=2, eq=[(fp.to_field_tensor(x), E) for x, E in zip(re, Es)],
+                            folds=folds, sumchecks=[sc], ws=ws)
+        torch.cuda.synchronize()
+        for j, (Y, R, c) in zip(maps, wants):
+            assert np.array_equal(j.Y.cpu().numpy(), Y) and np.array_equal(j.R.cpu().numpy(), R)
+            assert int(fp.field_numpy(j.claim)[0]) == c
+        for (_, _, _, out), w in zip(folds, fwant):
+            assert np.array_equal(fp.field_numpy(out), w)
+        for x, E in zip(re, Es):
+            assert np.array_equal(fp.field_numpy(E), O.eq_table(x))
+        assert np.array_equal(fp.field_numpy(sc.rounds), swant[0])
+        assert np.array_equal(fp.field_numpy(sc.finals).reshape(-1, 2), swant[1])
+        assert int(ws.buf[:512 + 16384].count_nonzero()) == 0

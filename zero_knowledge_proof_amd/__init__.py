@@ -32,7 +32,7 @@ EXPORTS = [
     "fp_eq_table_ext", "fp_ext_claim_combine", "fp_sumcheck_ext_fs", "fp_witness_packed_weights_bytes",
     "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
     "fp_layer_step", "fp_layer_step_workspace", "fp_witness_multi", "fp_witness_multi_workspace",
-    "fp_witness_multi_noalloc",
+    "fp_witness_multi_noalloc", "fp_layer_step_multi", "fp_layer_step_multi_workspace",
 ]
 
 _lib = None
@@ -55,6 +55,12 @@ class _MatmulDesc(ctypes.Structure):
     _fields_ = [("X", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("T", ctypes.c_int32), ("d_in", ctypes.c_int32),
                 ("d_out", ctypes.c_int32), ("Wp", ctypes.c_void_p), ("Z", ctypes.c_void_p), ("Y", ctypes.c_void_p),
                 ("R", ctypes.c_void_p), ("E_t", ctypes.c_void_p), ("E_o", ctypes.c_void_p), ("claim", ctypes.c_void_p)]
+
+
+class _SumcheckDesc(ctypes.Structure):
+    _fields_ = [("n_pairs", ctypes.c_int32), ("n", ctypes.c_int32), ("A", ctypes.c_void_p * 8),
+                ("B", ctypes.c_void_p * 8), ("rho", ctypes.c_void_p), ("r", ctypes.c_void_p),
+                ("rounds", ctypes.c_void_p), ("finals", ctypes.c_void_p), ("claim0", ctypes.c_void_p)]
 
 
 class _FoldDesc(ctypes.Structure):
@@ -126,6 +132,8 @@ def lib():
             "fp_witness_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp, sz, vp]),
             "fp_witness_multi_workspace": (sz, [i32, vp]),
             "fp_witness_multi_noalloc": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp]),
+            "fp_layer_step_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
+            "fp_layer_step_multi_workspace": (sz, [i32, vp, i32, vp, i32, vp]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -404,6 +412,56 @@ def witness_multi(jobs, s: int, group_o: int = 1, eq=None, ws: StepWorkspace | N
     ws = _ws_step if ws is None else ws
     p, nb = ws.get(lib().fp_witness_multi_workspace(len(jobs), arr))
     _check(lib().fp_witness_multi(len(jobs), arr, s, group_o, ne, eqd, p, nb, _stream()), "fp_witness_multi")
+
+
+class SumcheckJob:
+    """One sum-check instance of layer_step_multi: pairs of tables As[j], Bs[j] (int64 [2^n]), the round
+    challenges r [n], weights rho [n_pairs] or None, outputs rounds [n, 3], finals [n_pairs, 2] and claim0 [1]
+    (or None)."""
+
+    def __init__(self, As, Bs, r, rounds, finals, claim0=None, rho=None):
+        self.As, self.Bs, self.r, self.rounds, self.finals, self.claim0, self.rho = As, Bs, r, rounds, finals, claim0, rho
+
+
+def _sc_descs(scs):
+    out = []
+    for j in scs:
+        n, k = j.r.numel(), len(j.As)
+        assert 1 <= k <= 8 and len(j.Bs) == k
+        for t in list(j.As) + list(j.Bs):
+            _need(t, torch.int64, 1 << n, "sum-check table")
+        _need(j.r, torch.int64, n, "r")
+        _need(j.rounds, torch.int64, 3 * n, "rounds")
+        _need(j.finals, torch.int64, 2 * k, "finals")
+        if j.rho is not None:
+            _need(j.rho, torch.int64, k, "rho")
+        d = _SumcheckDesc()
+        d.n_pairs, d.n = k, n
+        for i in range(k):
+            d.A[i], d.B[i] = j.As[i].data_ptr(), j.Bs[i].data_ptr()
+        d.rho, d.r, d.rounds, d.finals, d.claim0 = _ptr(j.rho), _ptr(j.r), _ptr(j.rounds), _ptr(j.finals), _ptr(j.claim0)
+        out.append(d)
+    return len(out), (_SumcheckDesc * max(len(out), 1))(*out)
+
+
+def _fold_descs(folds):
+    nf = len(folds)
+    return nf, (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
+                                                   out.data_ptr()) for (M, E, cp, out) in folds])
+
+
+def layer_step_multi(jobs, s: int, group_o: int = 1, eq=None, folds=(), sumchecks=(), ws: StepWorkspace | None = None):
+    """One launch: the witness GEMMs and claims of a proof's maps (as witness_multi), the int8 folds
+    (M, E, cols_pad, out) of another proof (as fold_matrix_batched) and whole sum-check instances
+    (SumcheckJob) of a third, side by side."""
+    arr = _multi_descs(jobs)
+    ne, eqd = _eq_descs(eq)
+    nf, fd = _fold_descs(folds)
+    ns, sd = _sc_descs(sumchecks)
+    ws = _ws_step if ws is None else ws
+    p, nb = ws.get(lib().fp_layer_step_multi_workspace(len(jobs), arr, nf, fd, ns, sd))
+    _check(lib().fp_layer_step_multi(len(jobs), arr, s, group_o, ne, eqd, nf, fd, ns, sd, p, nb, _stream()),
+           "fp_layer_step_multi")
 
 
 def witness_multi_noalloc(jobs, s: int, group_o: int = 1, eq=None):

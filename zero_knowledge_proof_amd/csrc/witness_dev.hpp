@@ -282,4 +282,88 @@ inline int eq_aux(const char* fn, int32_t n_eq, const fp_eq_desc* eq, EqAux& aux
   return FP_OK;
 }
 
+// Fold and claim jobs run by workgroups of a witness launch in arrival mode
+// (the last workgroup of each column strip, or of a claim, adds the chunks):
+// their descriptors, the arrival counters at the start of the workspace
+// (FP_FOLD_COUNTER_BYTES, zero on entry and left zero) and the workgroups.
+template <int MAXJ>
+struct FoldAuxT {
+  foldk::FoldJob j[MAXJ];
+  uint32_t* ctrs;
+  int32_t count;
+  int32_t blocks;
+};
+
+// Plans the folds (int8) and claims (int32) of a launch's fold workgroups:
+// workspace = arrival counters, then every job's partial values, then (with
+// own_parts > 0) own_parts slots for the claim taken from the accumulators,
+// whose counter follows the jobs'.
+template <int MAXJ>
+int plan_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_t n_claim,
+               const fp_claim_desc* claims, int64_t own_parts, void* ws, size_t ws_bytes, bool plan_only,
+               size_t* need, FoldAuxT<MAXJ>& fa, uint64_t** own_part, uint32_t** own_ctr) {
+  fa = FoldAuxT<MAXJ>{};
+  if (n_fold < 0 || n_claim < 0 || n_fold + n_claim > MAXJ)
+    return fpi::fail(FP_EARG, "%s: %d folds and %d claims (at most %d in all)", fn, n_fold, n_claim, MAXJ);
+  if ((n_fold > 0 && !folds) || (n_claim > 0 && !claims)) return fpi::fail(FP_EARG, "%s: null descs", fn);
+  size_t off = FP_FOLD_COUNTER_BYTES;
+  int64_t blocks = 0;
+  int32_t nctr = 0;
+  for (int32_t i = 0; i < n_fold + n_claim; ++i) {
+    const bool claim = i >= n_fold;
+    foldk::FoldJob j{};
+    if (!claim) {
+      const fp_fold_desc& d = folds[i];
+      if (d.rows < 0 || d.cols < 0 || d.cols_pad < d.cols || d.ld < d.cols)
+        return fpi::fail(FP_ESHAPE, "%s: fold %d has bad sizes", fn, i);
+      if ((d.cols_pad > 0 && !d.out) || (d.rows > 0 && d.cols > 0 && (!d.M || !d.E)))
+        return fpi::fail(FP_EARG, "%s: fold %d has a null pointer", fn, i);
+      j.M = d.M; j.ld = d.ld; j.E = d.E; j.Ecol = nullptr; j.out = d.out;
+      j.rows = d.rows; j.cols = d.cols; j.cols_pad = d.cols_pad; j.eb = 1;
+    } else {
+      const fp_claim_desc& d = claims[i - n_fold];
+      if (d.rows < 0 || d.cols < 0 || d.ld < d.cols) return fpi::fail(FP_ESHAPE, "%s: claim %d has bad sizes", fn, i);
+      if (!d.out || (d.rows > 0 && d.cols > 0 && (!d.M || !d.E_rows || !d.E_cols)))
+        return fpi::fail(FP_EARG, "%s: claim %d has a null pointer", fn, i);
+      j.M = d.M; j.ld = d.ld; j.E = d.E_rows; j.Ecol = d.E_cols; j.out = d.out;
+      j.rows = d.rows; j.cols = d.cols; j.cols_pad = d.cols; j.eb = 4;
+    }
+    if (j.rows == 0 || j.cols == 0)
+      return fpi::fail(FP_ESHAPE, "%s: job %d is empty (the step's folds and claims need rows and columns)", fn, i);
+    const int64_t span = (int64_t)j.ld * j.eb * (j.rows < foldk::FMAX_CHUNK ? j.rows : foldk::FMAX_CHUNK);
+    if (span > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: job %d spans more than 2^31 bytes per chunk", fn, i);
+    const foldk::Plan p = foldk::plan_job(j.rows, j.cols, j.cols_pad, j.eb, claim, true);
+    const uintptr_t align = j.eb == 1 ? 3 : 15;
+    j.vec = (j.cols % 4 == 0) && (j.ld % 4 == 0) && (((uintptr_t)j.M & align) == 0);
+    j.chunk_rows = p.chunk_rows;
+    j.n_chunks = p.n_chunks;
+    j.n_strips = p.n_strips;
+    j.n_pad_strips = p.n_pad_strips;
+    j.part = p.part_bytes ? (fp_elem*)((char*)ws + off) : nullptr;
+    off += p.part_bytes;
+    j.block_start = (int32_t)blocks;
+    j.ctr = nctr;
+    blocks += p.blocks;
+    nctr += p.ctrs;
+    fa.j[fa.count++] = j;
+  }
+  *own_part = nullptr;
+  *own_ctr = nullptr;
+  if (own_parts > 0) {
+    *own_part = (uint64_t*)((char*)ws + off);
+    off += fpi::align_up((size_t)own_parts * 8, 256);
+    *own_ctr = (uint32_t*)ws + nctr;
+    nctr += 1;
+  }
+  if (nctr > (int32_t)(FP_FOLD_COUNTER_BYTES / 4) || blocks > (1 << 24))
+    return fpi::fail(FP_ESHAPE, "%s: folds too large for one step", fn);
+  fa.blocks = (int32_t)blocks;
+  fa.ctrs = (uint32_t*)ws;
+  *need = (n_fold + n_claim || own_parts > 0) ? off : 0;
+  if (plan_only) return FP_OK;
+  if (*need && (!ws || ws_bytes < *need)) return fpi::fail(FP_EWORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, *need);
+  if (*need && (((uintptr_t)ws) & 255)) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
+  return FP_OK;
+}
+
 }  // namespace

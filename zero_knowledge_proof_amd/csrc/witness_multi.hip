@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "eq.hpp"
+#include "sc_stream.hpp"
 #include "witness_dev.hpp"
 
 namespace {
@@ -57,6 +58,19 @@ struct MultiArgs {
   int32_t split[MM_MAX][NXCD + 1];  // map m's tiles [split[m][x], split[m][x+1]) run on XCD x
   int32_t count, s, group_o, gemm_blocks;
 };
+
+// Fold jobs of another proof (arrival mode) and whole sum-check instances of a
+// third, run by workgroups of the same launch.
+constexpr int MULTI_MAX_FOLD = FP_STEP_MULTI_MAX_FOLD;
+constexpr int MULTI_MAX_SC = FP_STEP_MULTI_MAX_SUMCHECK;
+using MultiFolds = FoldAuxT<MULTI_MAX_FOLD>;
+struct SumAux {
+  scs::Inst inst[MULTI_MAX_SC];
+  int32_t count;
+  int32_t blocks;  // count rounded up to a multiple of 8, so the GEMM tiles keep blockIdx % 8 as their XCD
+};
+// the claim counters come first in the workspace, the folds' counters and parts after them
+constexpr size_t CLAIM_CTR_BYTES = (size_t)MM_MAX * 64;
 
 // Tile config: NW waves of 32 TM weight rows x 32 TN tokens.
 template <int NW, int TM, int TN, int PFW, int PFX, int NBUF>
@@ -288,18 +302,41 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   if (claim) claim_arrive(a, wsum, lt, nt, NW, red, reinterpret_cast<uint32_t*>(red + 8));
 }
 
-// Workgroups [0, gemm_blocks): GEMM tiles of every map (map and tile from the
-// XCD split); the rest: eq tables (for another proof: this launch's claims
-// read tables that are complete before it starts).
+// Workgroups, in order: [0, sa.blocks) whole sum-check instances (first, so
+// their chains of rounds start at once; the count is padded to a multiple of
+// 8); then the GEMM tiles of every map (map and tile from the XCD split); then
+// fold jobs in arrival mode; then eq tables. The sum-checks, folds and eq
+// tables belong to other proofs than the GEMMs (this launch's claims read eq
+// tables that are complete before it starts), so nothing in one launch waits
+// for another part of it.
 template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_multi_kernel(
-    MultiArgs ma, EqAux eq) {
+    MultiArgs ma, EqAux eq, MultiFolds mf, SumAux sa) {
   using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
-  static_assert(C::NT == 256, "the eq blocks are written for 256 threads");
-  __shared__ __align__(16) int8_t lds[C::LDS_BYTES];
-  const int b = blockIdx.x;
+  static_assert(C::NT == 256 && scs::ST == 256 && foldk::FT == 256,
+                "the eq, fold and sum-check workgroups are written for 256 threads");
+  constexpr int FOLD_LDS = foldk::LDS_WORDS * 4 + foldk::MAXG_ALL * 8 + 16;
+  constexpr int TAIL_LDS = (int)sizeof(sct::TailLds<256>);
+  constexpr int B1 = C::LDS_BYTES > TAIL_LDS ? C::LDS_BYTES : TAIL_LDS;
+  constexpr int BYTES = B1 > FOLD_LDS ? B1 : FOLD_LDS;
+  __shared__ __align__(16) int8_t lds[BYTES];
+  int b = blockIdx.x;
+  if (b < sa.blocks) {
+    if (b < sa.count) scs::stream_body(sa.inst[b], *reinterpret_cast<sct::TailLds<256>*>(lds));
+    return;
+  }
+  b -= sa.blocks;
   if (b >= ma.gemm_blocks) {
-    eq_aux_block(eq, b - ma.gemm_blocks);
+    b -= ma.gemm_blocks;
+    if (b < mf.blocks) {
+      const foldk::FoldJob& job = mf.j[foldk::find_job(mf.j, mf.count, b)];
+      uint32_t* fl = reinterpret_cast<uint32_t*>(lds);
+      uint64_t* gsum = reinterpret_cast<uint64_t*>(lds + foldk::LDS_WORDS * 4);
+      uint32_t* flag = reinterpret_cast<uint32_t*>(gsum + foldk::MAXG_ALL);
+      foldk::fold_block_arrive(job, b - job.block_start, mf.ctrs, fl, gsum, flag);
+      return;
+    }
+    eq_aux_block(eq, b - mf.blocks);
     return;
   }
   const int x = b % NXCD;
@@ -324,28 +361,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // 256 x 128 tiles (4 waves of 64 x 128), weights 3 blocks ahead, X 3 blocks
 // ahead through 3 LDS stages.
 #define WIT_MULTI 4, 2, 4, 3, 3, 3, 0
-using MC = MCfg<4, 2, 4, 3, 3, 3>;
-constexpr int MULTI_WAVES = 4;
 
 struct MultiPlan {
   int64_t tiles[MM_MAX];
   size_t part_off[MM_MAX];
+  size_t sc_off[MULTI_MAX_SC];
   size_t bytes;
 };
 
-// Workspace: arrival counters (one 64-byte line per map), then one slot per
-// GEMM wave of every map that forms a claim.
-int multi_plan(const char* fn, int32_t count, const fp_matmul_desc* mm, MultiPlan& p) {
+// Workspace: the claims' arrival counters (one 64-byte line per map); the
+// folds' counters and partial values (fold_bytes of them, from plan_folds;
+// the counters' FP_FOLD_COUNTER_BYTES even without folds);
+// one slot per GEMM wave of every map that forms a claim; each sum-check's
+// table buffers.
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+int multi_plan(const char* fn, int32_t count, const fp_matmul_desc* mm, size_t fold_bytes, int32_t n_sc,
+               const fp_sumcheck_desc* sc, MultiPlan& p) {
+  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
   if (count < 1 || count > MM_MAX) return fpi::fail(FP_EARG, "%s: count=%d outside [1, %d]", fn, count, MM_MAX);
   if (!mm) return fpi::fail(FP_EARG, "%s: null descs", fn);
-  size_t off = fpi::align_up((size_t)MM_MAX * 64, 256);
+  size_t off = CLAIM_CTR_BYTES + fpi::align_up(fold_bytes, 256);
   for (int i = 0; i < count; ++i) {
     const fp_matmul_desc& d = mm[i];
     if (d.T < 0 || d.d_in < 0 || d.d_out < 0) return fpi::fail(FP_EARG, "%s: map %d has a negative size", fn, i);
     const int64_t tiles = (int64_t)((d.T + MC::BT - 1) / MC::BT) * ((d.d_out + MC::BO - 1) / MC::BO);
     p.tiles[i] = tiles;
     p.part_off[i] = off;
-    if (d.E_t) off += fpi::align_up((size_t)tiles * MULTI_WAVES * 8, 256);
+    if (d.E_t) off += fpi::align_up((size_t)tiles * NW * 8, 256);
+  }
+  if (n_sc < 0 || n_sc > MULTI_MAX_SC)
+    return fpi::fail(FP_EARG, "%s: %d sum-checks (at most %d)", fn, n_sc, MULTI_MAX_SC);
+  if (n_sc > 0 && !sc) return fpi::fail(FP_EARG, "%s: null sum-check descs", fn);
+  for (int k = 0; k < n_sc; ++k) {
+    if (sc[k].n_pairs < 1 || sc[k].n_pairs > scs::MAX_PAIRS)
+      return fpi::fail(FP_EARG, "%s: sum-check %d has n_pairs=%d outside [1, %d]", fn, k, sc[k].n_pairs, scs::MAX_PAIRS);
+    if (sc[k].n < 1 || sc[k].n > FP_STEP_MULTI_MAX_SC_N)
+      return fpi::fail(FP_ESHAPE, "%s: sum-check %d has n=%d outside [1, %d]", fn, k, sc[k].n, FP_STEP_MULTI_MAX_SC_N);
+    p.sc_off[k] = off;
+    off += fpi::align_up((size_t)scs::workspace_entries(sc[k].n_pairs, sc[k].n) * 8, 256);
   }
   p.bytes = off;
   return FP_OK;
@@ -388,19 +441,38 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
 
 extern "C" size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm) {
   MultiPlan p;
-  if (multi_plan("fp_witness_multi_workspace", count, mm, p)) return 0;
+  if (multi_plan<WIT_MULTI>("fp_witness_multi_workspace", count, mm, 0, 0, nullptr, p)) return 0;
   return p.bytes;
 }
 
 namespace {
 
-// fp_witness_multi's checks and launch; noalloc: ws is the scratch array (its
-// counters cleared first on the stream).
+// fp_witness_multi's checks and launch for one tile configuration; noalloc:
+// ws is the scratch array (its counters cleared first on the stream).
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
 int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
-                 const fp_eq_desc* eq, void* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
-  MultiPlan p;
-  int rc = multi_plan(fn, count, mm, p);
+                 const fp_eq_desc* eq, int32_t n_fold, const fp_fold_desc* folds, int32_t n_sc,
+                 const fp_sumcheck_desc* sc, void* ws, size_t ws_bytes, bool noalloc, bool plan_only, size_t* need,
+                 hipStream_t stream) {
+  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  // the folds' counters and parts follow the claims' counters
+  MultiFolds mf;
+  size_t fold_bytes = 0;
+  uint64_t* unused_part;
+  uint32_t* unused_ctr;
+  int rc = plan_folds<MULTI_MAX_FOLD>(fn, n_fold, folds, 0, nullptr, 0, ws ? (char*)ws + CLAIM_CTR_BYTES : nullptr, 0,
+                                      true, &fold_bytes, mf, &unused_part, &unused_ctr);
   if (rc) return rc;
+  // the folds' counter region is always there, so that one workspace serves
+  // calls with and without folds (its counters stay zero between calls)
+  if (fold_bytes < (size_t)FP_FOLD_COUNTER_BYTES) fold_bytes = FP_FOLD_COUNTER_BYTES;
+  MultiPlan p;
+  rc = multi_plan<NW, TM, TN, PFW, PFX, NBUF, SCHED>(fn, count, mm, fold_bytes, n_sc, sc, p);
+  if (rc) return rc;
+  if (plan_only) {
+    *need = p.bytes;
+    return FP_OK;
+  }
   if (s < 1 || s > 8) return fpi::fail(FP_ERANGE, "%s: s=%d outside [1, 8]", fn, s);
   if (group_o < 1) return fpi::fail(FP_EARG, "%s: group_o=%d < 1", fn, group_o);
   bool any_claim = false;
@@ -455,7 +527,7 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
     rem_before += rem;
     total += n;
   }
-  if (any_claim) {
+  if (any_claim || n_fold > 0 || n_sc > 0) {
     if (noalloc && p.bytes > FP_WITNESS_MULTI_SCRATCH_BYTES)
       return fpi::fail(FP_EWORKSPACE, "%s: these maps need %zu bytes of scratch, more than the %d the library holds", fn,
                        p.bytes, FP_WITNESS_MULTI_SCRATCH_BYTES);
@@ -466,16 +538,44 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
   EqAux aux;
   rc = eq_aux(fn, n_eq, eq, aux);
   if (rc) return rc;
-  if (total + aux.block_start[aux.count] > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many tiles", fn);
+  SumAux sa{};
+  sa.count = n_sc;
+  sa.blocks = (n_sc + NXCD - 1) / NXCD * NXCD;
+  for (int k = 0; k < n_sc; ++k) {
+    const fp_sumcheck_desc& d = sc[k];
+    if (!d.r || !d.rounds || !d.finals) return fpi::fail(FP_EARG, "%s: sum-check %d has a null pointer", fn, k);
+    scs::Inst& in = sa.inst[k];
+    for (int j = 0; j < d.n_pairs; ++j) {
+      if (!d.A[j] || !d.B[j] || (((uintptr_t)d.A[j]) & 15) || (((uintptr_t)d.B[j]) & 15))
+        return fpi::fail(FP_EARG, "%s: sum-check %d table %d is null or not 16-byte aligned", fn, k, j);
+      in.A[j] = d.A[j];
+      in.B[j] = d.B[j];
+    }
+    in.rho = d.rho; in.r = d.r; in.rounds = d.rounds; in.finals = d.finals; in.claim0 = d.claim0;
+    in.scratch = (fp_elem*)((char*)ws + p.sc_off[k]);
+    in.n = d.n;
+    in.n_pairs = d.n_pairs;
+    in.i0 = scs::stream_rounds(d.n_pairs, d.n);
+  }
+  // the fold jobs again, now against the real workspace
+  if (n_fold > 0) {
+    rc = plan_folds<MULTI_MAX_FOLD>(fn, n_fold, folds, 0, nullptr, 0, (char*)ws + CLAIM_CTR_BYTES,
+                                    ws_bytes - CLAIM_CTR_BYTES, false, &fold_bytes, mf, &unused_part, &unused_ctr);
+    if (rc) return rc;
+  }
+  const int64_t grid = (int64_t)sa.blocks + total + mf.blocks + aux.block_start[aux.count];
+  if (grid > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many workgroups", fn);
   ma.gemm_blocks = (int32_t)total;
-  const int64_t grid = total + aux.block_start[aux.count];
   if (grid == 0) return fpi::ok();
   if (noalloc && any_claim) {
-    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, (uint32_t*)ws, MM_MAX * 16);
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, (uint32_t*)ws, (int)(CLAIM_CTR_BYTES / 4));
     rc = fpi::check_launch("clear_words_kernel");
     if (rc) return rc;
   }
-  hipLaunchKernelGGL((witness_multi_kernel<WIT_MULTI>), dim3((unsigned)grid), dim3(MC::NT), 0, stream, ma, aux);
+  static_assert(sizeof(MultiArgs) + sizeof(EqAux) + sizeof(MultiFolds) + sizeof(SumAux) <= 4096,
+                "kernel arguments must fit 4 KiB");
+  hipLaunchKernelGGL((witness_multi_kernel<NW, TM, TN, PFW, PFX, NBUF, SCHED>), dim3((unsigned)grid), dim3(MC::NT), 0,
+                     stream, ma, aux, mf, sa);
   rc = fpi::check_launch("witness_multi_kernel");
   return rc ? rc : fpi::ok();
 }
@@ -484,7 +584,24 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
 
 extern "C" int fp_witness_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
                                 const fp_eq_desc* eq, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return multi_launch("fp_witness_multi", count, mm, s, group_o, n_eq, eq, ws, ws_bytes, false, stream);
+  return multi_launch<WIT_MULTI>("fp_witness_multi", count, mm, s, group_o, n_eq, eq, 0, nullptr, 0, nullptr, ws,
+                                 ws_bytes, false, false, nullptr, stream);
+}
+
+extern "C" int fp_layer_step_multi(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
+                                   const fp_eq_desc* eq, int32_t n_fold, const fp_fold_desc* folds, int32_t n_sc,
+                                   const fp_sumcheck_desc* sc, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return multi_launch<WIT_MULTI>("fp_layer_step_multi", count, mm, s, group_o, n_eq, eq, n_fold, folds, n_sc, sc, ws,
+                                 ws_bytes, false, false, nullptr, stream);
+}
+
+extern "C" size_t fp_layer_step_multi_workspace(int32_t count, const fp_matmul_desc* mm, int32_t n_fold,
+                                                const fp_fold_desc* folds, int32_t n_sc, const fp_sumcheck_desc* sc) {
+  size_t need = 0;
+  if (multi_launch<WIT_MULTI>("fp_layer_step_multi_workspace", count, mm, 8, 1, 0, nullptr, n_fold, folds, n_sc, sc,
+                              nullptr, 0, false, true, &need, nullptr))
+    return 0;
+  return need;
 }
 
 extern "C" int fp_witness_multi_noalloc(int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o,
@@ -493,5 +610,6 @@ extern "C" int fp_witness_multi_noalloc(int32_t count, const fp_matmul_desc* mm,
   void* ws = nullptr;
   const int rc = scratch_address(fn, &ws);
   if (rc) return rc;
-  return multi_launch(fn, count, mm, s, group_o, n_eq, eq, ws, FP_WITNESS_MULTI_SCRATCH_BYTES, true, stream);
+  return multi_launch<WIT_MULTI>(fn, count, mm, s, group_o, n_eq, eq, 0, nullptr, 0, nullptr, ws,
+                                 FP_WITNESS_MULTI_SCRATCH_BYTES, true, false, nullptr, stream);
 }

@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MatmulJob, StepWorkspace, combine_claims, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
+from . import (MatmulJob, StepWorkspace, SumcheckJob, combine_claims, layer_step_multi, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
                ext_claim_combine, field_numpy, fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows,
                layer_step, linear_combine, merkle_commit, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs,
                sumcheck_prove, sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped,
@@ -474,6 +474,186 @@ class MultiMatmulProver(_Prover):
         return out
 
 
+class OverlappedMultiProver(MultiMatmulProver):
+    """A stream of proofs of a multi-map layer (the dense MLP, the seven-map
+    layer), three in flight: step k is ONE launch (fp_layer_step_multi) that runs
+    proof k's witness GEMMs with every map's claim taken from the accumulators,
+    proof k+1's eq tables, proof k-1's folds of X and W, and proof k-2's
+    sum-check(s), each instance one workgroup. A proof's eq tables depend on its
+    challenges alone, so they are built a step ahead; its folds read only its
+    own tables and its sum-check only its own folds, so each proof keeps the
+    protocol order. Then a small launch merges proof k-2's claims (the RLC of
+    the three output claims, or the rho-combination of the seven input claims
+    that the batched sum-check starts from). A proof's buffers (Y, R, tables,
+    folds, claims, rounds, finals) live from the step that builds its eq
+    tables to the one that merges it, so they rotate over three sets and a
+    captured graph holds a multiple of three steps; ``drain()`` finishes the
+    last two proofs. Needs every map's d_in % 16 == 0."""
+
+    SETS = 3
+    GRAPH_QUANTUM = 3
+    PER_SET = ("E_t", "E_o", "Y", "R", "c0", "xf", "wf", "rounds", "finals", "claim0", "rlc", "c0_batch")
+
+    def __init__(self, cfg, inp: dict, ch: dict, dev=None, keep_z: bool = False, group_o: int = 1):
+        super().__init__(cfg, inp, ch, dev, keep_z=keep_z, group_o=group_o)
+        if not all(d["fused"] for d in self.mm):
+            raise ValueError("overlapped proofs need every map's d_in % 16 == 0")
+        dev = self.E_t.device
+        T = cfg.T
+        self.sets = []
+        for b in range(self.SETS):
+            st = {"E_t": self.E_t if b == 0 else _f(self.E_t.numel(), dev), "maps": []}
+            xf = {}
+            for d in self.mm:
+                m = d["m"]
+                key = (m.x, d["n"])
+                if key not in xf:
+                    xf[key] = d["xf"] if b == 0 else torch.zeros_like(d["xf"])
+                e = {"E_o": d["E_o"] if b == 0 else _f(d["E_o"].numel(), dev), "xf": xf[key],
+                     "wf": d["wf"] if b == 0 else torch.zeros_like(d["wf"]),
+                     "Y": d["Y"] if b == 0 else torch.empty_like(d["Y"]),
+                     "R": d["R"] if b == 0 else torch.empty_like(d["R"]),
+                     "Z": (d["Z"] if b == 0 else torch.empty_like(d["Z"])) if d["Z"] is not None else None,
+                     "c0": d["c0"] if b == 0 else _f(1, dev)}
+                if self.mode == "rlc_out":
+                    e.update(rounds=torch.zeros((d["n"], 3), dtype=torch.int64, device=dev),
+                             finals=torch.zeros((1, 2), dtype=torch.int64, device=dev),
+                             claim0=torch.zeros(1, dtype=torch.int64, device=dev))
+                st["maps"].append(e)
+            st["x_jobs"] = [(self.tens[x], cp, buf) for (x, n), buf in
+                            ((k, xf[k]) for k in xf) for cp in [1 << n]]
+            if self.mode == "rlc_out":
+                st["rlc"] = _f(1, dev)
+            else:
+                st["c0_batch"] = _f(1, dev)
+                st["rounds"] = torch.zeros((cfg.batched_n, 3), dtype=torch.int64, device=dev)
+                st["finals"] = torch.zeros((len(self.mm), 2), dtype=torch.int64, device=dev)
+                st["claim0"] = torch.zeros(1, dtype=torch.int64, device=dev)
+            self.sets.append(st)
+        self.k = 0
+        self.step_ws = StepWorkspace()
+        # maps in the launch order (longest reduction first), as in the parent's jobs
+        self.order = sorted(range(len(self.mm)), key=lambda i: -self.mm[i]["m"].d_in)
+
+    def _set(self, k):
+        return self.sets[k % self.SETS]
+
+    def _eq_pairs(self, st):
+        return [(self.ch["r_t"], st["E_t"])] + [(self.ch["r_o/" + d["m"].name], e["E_o"])
+                                                for d, e in zip(self.mm, st["maps"])]
+
+    def _jobs(self, st):
+        return [MatmulJob(self.tens[self.mm[i]["m"].x], self.packed[self.mm[i]["m"].w], st["maps"][i]["Y"],
+                          st["maps"][i]["R"], st["maps"][i]["Z"], st["E_t"], st["maps"][i]["E_o"], st["maps"][i]["c0"])
+                for i in self.order]
+
+    def _folds(self, st):
+        jobs = [(M, st["E_t"], cp, out) for (M, cp, out) in st["x_jobs"]]
+        jobs += [(self.tens[d["m"].w], e["E_o"], 1 << d["n"], e["wf"]) for d, e in zip(self.mm, st["maps"])]
+        return jobs
+
+    def _sumchecks(self, st):
+        if self.mode == "rlc_out":
+            return [SumcheckJob([e["xf"]], [e["wf"]], self.ch["rounds/" + d["m"].name], e["rounds"], e["finals"],
+                                e["claim0"]) for d, e in zip(self.mm, st["maps"])]
+        return [SumcheckJob([e["xf"] for e in st["maps"]], [e["wf"] for e in st["maps"]], self.ch["rounds"],
+                            st["rounds"], st["finals"], st["claim0"], rho=self.rho)]
+
+    def _merge_set(self, st):
+        if self.mode == "rlc_out":
+            combine_claims([e["rounds"][-1] for e in st["maps"]],
+                           [self.ch["rounds/" + d["m"].name][-1:] for d in self.mm], self.rho, out=st["rlc"])
+        else:
+            linear_combine([e["c0"] for e in st["maps"]], self.rho, out=st["c0_batch"])
+
+    def _step(self, k, fold: bool, tail: bool):
+        cur, nxt, prev, old = self._set(k), self._set(k + 1), self._set(k - 1), self._set(k - 2)
+        layer_step_multi(self._jobs(cur), self.s, group_o=self.group_o, eq=self._eq_pairs(nxt),
+                         folds=self._folds(prev) if fold else (), sumchecks=self._sumchecks(old) if tail else (),
+                         ws=self.step_ws)
+        if tail:
+            self._merge_set(old)
+
+    def run(self, mark=_nomark):
+        mark("step")
+        if self.k == 0:
+            st = self._set(0)
+            eq_table_batched([r for r, _ in self._eq_pairs(st)], [E for _, E in self._eq_pairs(st)])
+        self._step(self.k, self.k >= 1, self.k >= 2)
+        mark("end")
+        self.k += 1
+
+    def phases(self):
+        wit = "witness" if self.keep_z else "witness(Y,R)"
+        return [(wit + "+claim(acc)+eq+fold+sumcheck", lambda: self._step(2, True, True))]
+
+    def capture(self, steps: int = 1):
+        if steps % self.GRAPH_QUANTUM:
+            raise ValueError("a captured graph holds a multiple of %d steps" % self.GRAPH_QUANTUM)
+        while self.k < 2:
+            self.run()
+        self.run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+        self.graph_steps = steps
+        self.k_graph = self.k
+        return g
+
+    def replay(self):
+        self.graph.replay()
+        self.k = self.k_graph
+
+    def drain(self):
+        """The sum-check of the next-to-last proof, then the folds and sum-check of the last one."""
+        last = self.k - 1
+        if last < 0:
+            return
+        if last >= 1:
+            self._finish(self._set(last - 1))
+        st = self._set(last)
+        fold_claim_batched(self._folds(st), [])
+        self._finish(st)
+
+    def _finish(self, st):
+        for j in self._sumchecks(st):
+            sumcheck_prove(j.As, j.Bs, j.r, rho=j.rho, rounds=j.rounds, finals=j.finals, claim0=j.claim0)
+        self._merge_set(st)
+
+    def output_tensors(self):
+        out = []
+        for st in self.sets:
+            out.append(st["E_t"])
+            for e in st["maps"]:
+                out += [v for v in e.values() if v is not None]
+            out += [st[k] for k in ("rlc", "c0_batch", "rounds", "finals", "claim0") if k in st]
+        return out
+
+    def results(self, k: int | None = None) -> dict:
+        """Outputs of proof k (default: the last one)."""
+        st = self._set(self.k - 1 if k is None else k)
+        out = {"E_t": field_numpy(st["E_t"])}
+        for d, e in zip(self.mm, st["maps"]):
+            r = {"Y": e["Y"].cpu().numpy(), "R": e["R"].cpu().numpy(), "E_o": field_numpy(e["E_o"]),
+                 "x_fold": field_numpy(e["xf"]), "w_fold": field_numpy(e["wf"]), "c0": int(field_numpy(e["c0"])[0])}
+            if e["Z"] is not None:
+                r["Z"] = e["Z"].cpu().numpy()
+            if self.mode == "rlc_out":
+                r.update(rounds=field_numpy(e["rounds"]), finals=field_numpy(e["finals"]),
+                         claim0=int(field_numpy(e["claim0"])[0]))
+            out[d["m"].name] = r
+        if self.mode == "rlc_out":
+            out["rlc"] = int(field_numpy(st["rlc"])[0])
+        else:
+            out["batch"] = {"rounds": field_numpy(st["rounds"]), "finals": field_numpy(st["finals"]),
+                            "claim0": int(field_numpy(st["claim0"])[0]), "c0": int(field_numpy(st["c0_batch"])[0])}
+        return out
+
+
 class MoEBlockProver(_Prover):
     """MoE block: top-1 routed tokens grouped by expert (stable, ascending
     token order), one grouped witness launch per projection, and an
@@ -697,7 +877,10 @@ def can_pipeline(cfg) -> bool:
 
 
 def can_overlap(cfg) -> bool:
-    """Whether three proofs can be in flight (pipelined, and the packed witness applies)."""
+    """Whether three proofs can be in flight (the packed witness applies to every map, and a single layer's
+    sum-check fits the workgroup inside the witness launch)."""
+    if cfg.kind in ("rlc_out", "batched"):
+        return all(m.d_in % 16 == 0 for m in cfg.matmuls)
     return can_pipeline(cfg) and cfg.matmuls[0].d_in % 16 == 0
 
 
@@ -711,10 +894,15 @@ def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, ove
         if overlapped:
             return OverlappedLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, keep_z=keep_z)
         return SingleLayerProver(inp[m.x], inp[m.w], cfg.s, ch, dev, pipelined=pipelined)
+    if cfg.kind in ("rlc_out", "batched"):
+        group_o = 4 if cfg.T >= 2048 else 1
+        if overlapped:
+            return OverlappedMultiProver(cfg, inp, ch, dev, keep_z=keep_z, group_o=group_o)
+        if pipelined:
+            raise ValueError("multi-map layers keep one proof in flight or three (overlapped)")
+        return MultiMatmulProver(cfg, inp, ch, dev, keep_z=keep_z, group_o=group_o)
     if pipelined:
         raise ValueError("pipelined proofs are implemented for single-matmul layers")
-    if cfg.kind in ("rlc_out", "batched"):
-        return MultiMatmulProver(cfg, inp, ch, dev, keep_z=keep_z)
     if cfg.kind == "moe":
         return MoEBlockProver(cfg, inp, ch, dev)
     raise ValueError(cfg.kind)
