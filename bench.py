@@ -85,7 +85,9 @@ def kernel_work(cfg, name: str, prover) -> tuple:
     return 0, 0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_T512_step_traffic.txt")
+TRAFFIC_FILES = {2: os.path.join(ROOT, "profiles", "layer_T512_step_traffic.txt"),
+                 5: os.path.join(ROOT, "profiles", "layer_T4096_7maps_step_traffic.txt"),
+                 3: os.path.join(ROOT, "profiles", "mlp_T1024_step_traffic.txt")}
 
 
 def measured_traffic(cfg, kernel_phase: str):
@@ -93,10 +95,11 @@ def measured_traffic(cfg, kernel_phase: str):
     summary, or None when there is none for this workload and launch or its
     kernel sources changed since the counters were taken."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(cfg.cid)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.startswith("#") or ":" not in line:
             continue
         k, v = line.split(":", 1)
@@ -138,12 +141,13 @@ print(time.perf_counter() - t0)
 
 def cpu_baseline(cfg, inp, ch, one_core: bool = True) -> dict:
     """The oracle's whole layer proof of the workload on the host cores (all
-    OpenMP threads, and once more on one core in a child process)."""
+    OpenMP threads, and once more on one core in a child process); for the
+    large workloads a bounded sample (cpu_baseline_sampled)."""
     import subprocess
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     if cfg.cid not in (1, 2):
-        return None
+        return cpu_baseline_sampled(cfg, inp, ch)
     oracle.lib()
     t0 = time.perf_counter()
     oracle.prove_config(cfg, inp, ch)
@@ -160,6 +164,92 @@ def cpu_baseline(cfg, inp, ch, one_core: bool = True) -> dict:
             out["value_1core"] = cfg.T / d1
             out["sample_1core"] = "the same proof with OMP_NUM_THREADS=1, %.2f s" % d1
     return out
+
+
+def cpu_baseline_sampled(cfg, inp, ch, t_sample: int = 2048, max_experts: int = 6) -> dict:
+    """The oracle on a bounded sample of a large workload, extrapolated to the
+    whole proof: the work that grows with the tokens (every map's witness, the
+    claim of each Z, the folds of the activations) is timed on the first
+    t_sample tokens (the MoE block: on max_experts experts, the largest among
+    them) and scaled; the folds of the weights and the sum-checks, which do not
+    grow with the tokens, are timed in full (MoE: per expert, scaled by the
+    experts present). Runs on all the host's OpenMP threads."""
+    import numpy as np
+    import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    O.lib()
+
+    def clock(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    if cfg.kind == "moe":
+        groups = O.group_tokens(inp["route"], cfg.n_experts)
+        present = [e for e in range(cfg.n_experts) if len(groups[e])]
+        by_size = sorted(present, key=lambda e: -len(groups[e]))
+        pick = sorted(set(by_size[:max_experts // 2] + by_size[-(max_experts - max_experts // 2):]))
+        tok_work = sum(len(groups[e]) for e in pick)
+        t_tok = t_fix = 0.0
+        for e in pick:
+            toks = groups[e]
+            for side, Xs, W in (("up", inp["X"], inp["W1_%d" % e]), ("down", inp["H"], inp["W2_%d" % e])):
+                Xe = np.ascontiguousarray(Xs[toks])
+                r_t = ch["r_t/%d" % e]
+                r_o = ch["r_o_%s/%d" % (side, e)]
+                rr = ch["rounds_%s/%d" % (side, e)]
+                n = len(rr)
+                (Z, _, _), dt = clock(lambda: O.witness(Xe, W, cfg.s))
+                t_tok += dt
+                _, dt = clock(lambda: O.mle_matrix(Z, r_t, r_o))
+                t_tok += dt
+                xf, dt = clock(lambda: O.fold_rows(Xe, O.eq_table(r_t), 1 << n))
+                t_tok += dt
+                wf, dt = clock(lambda: O.fold_rows(W, O.eq_table(r_o), 1 << n))
+                t_fix += dt
+                _, dt = clock(lambda: O.sumcheck([xf], [wf], rr))
+                t_fix += dt
+        total = t_tok * cfg.T / tok_work + t_fix * len(present) / len(pick)
+        sample = ("%d of the %d experts present (the %d largest and the %d smallest, %d tokens): witness, claim and "
+                  "activation folds %.2f s scaled by %d / %d tokens; weight folds and sum-checks %.2f s scaled by "
+                  "%d / %d experts; whole block extrapolated to %.1f s" %
+                  (len(pick), len(present), max_experts // 2, max_experts - max_experts // 2, tok_work, t_tok,
+                   cfg.T, tok_work, t_fix, len(present), len(pick), total))
+    else:
+        Ts = min(t_sample, cfg.T)
+        ns = max(0, (Ts - 1).bit_length())
+        r_t = ch["r_t"][:ns]
+        E_ts = O.eq_table(r_t)
+        t_tok = t_fix = 0.0
+        xfs, As, Bs, rho = {}, [], [], []
+        for m in cfg.matmuls:
+            n = cfg.batched_n if cfg.kind == "batched" else m.n
+            Xs = np.ascontiguousarray(inp[m.x][:Ts])
+            (Z, _, _), dt = clock(lambda: O.witness(Xs, inp[m.w], cfg.s))
+            t_tok += dt
+            _, dt = clock(lambda: O.mle_matrix(Z, r_t, ch["r_o/" + m.name]))
+            t_tok += dt
+            if (m.x, n) not in xfs:
+                xfs[(m.x, n)], dt = clock(lambda: O.fold_rows(Xs, E_ts, 1 << n))
+                t_tok += dt
+            wf, dt = clock(lambda: O.fold_rows(inp[m.w], O.eq_table(ch["r_o/" + m.name]), 1 << n))
+            t_fix += dt
+            if cfg.kind == "batched":
+                As.append(xfs[(m.x, n)])
+                Bs.append(wf)
+                rho.append(int(ch["rho/" + m.name][0]))
+            else:
+                _, dt = clock(lambda: O.sumcheck([xfs[(m.x, n)]], [wf], ch["rounds/" + m.name]))
+                t_fix += dt
+        if cfg.kind == "batched":
+            _, dt = clock(lambda: O.sumcheck(As, Bs, ch["rounds"], rho=rho))
+            t_fix += dt
+        total = t_tok * cfg.T / Ts + t_fix
+        sample = ("the first %d of %d tokens: every map's witness, its claim and the activation folds %.2f s, scaled "
+                  "by %d / %d; the weight folds and the sum-check(s) in full, %.2f s; whole proof extrapolated to "
+                  "%.1f s" % (Ts, cfg.T, t_tok, cfg.T, Ts, t_fix, total))
+    return {"value": cfg.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "host_cpu": _host_cpu(), "nproc": os.cpu_count()}
 
 
 def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool, R: int = 64) -> dict:
@@ -519,54 +609,16 @@ def faithful_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool) -> d
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=90)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-pipeline", action="store_true",
-                    help="prove steps one after another instead of overlapping each step's sum-check with the "
-                         "next step's witness GEMM")
-    ap.add_argument("--no-overlap", action="store_true",
-                    help="keep two proofs in flight instead of three (the folds of the previous proof then run after "
-                         "the witness instead of beside it)")
-    ap.add_argument("--no-faithful", action="store_true",
-                    help="skip the soundness-faithful proof (commitment, Fiat-Shamir, extension-field challenges)")
-    ap.add_argument("--no-lookup", action="store_true",
-                    help="skip the remainder lookup measurement (product tree, multiplicities, proof of the tree)")
-    ap.add_argument("--no-commitment", action="store_true",
-                    help="skip the commitment measurement (Y and R packed, Reed-Solomon encoded, Merkle hashed)")
-    ap.add_argument("--no-request-vectors", action="store_true",
-                    help="skip the batch request-vector measurement (64 eq vectors folded against the first weight "
-                         "matrix in one pass)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="first run one device-to-device copy of MIB MiB (a reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: this prover runs on one GPU; --gpus %d is not supported (each box has one GPU)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-
+def layer_bench(cid: int, args, dev, with_cpu: bool, legs: bool):
+    """Times K steps of a stream of proofs of workload `cid` (three in flight where it allows) and returns the
+    JSON dict of the measurement (with the inputs, for the legs)."""
     import torch
 
     import synth
     import zero_knowledge_proof_amd as fp
     from zero_knowledge_proof_amd.prover import can_overlap, can_pipeline, make_prover
 
-    fp.require_gpu()
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    cfg = synth.config(args.config)
+    cfg = synth.config(cid)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))
     if cfg.kind in ("rlc_out", "batched"):  # multi-map layers: one proof in flight, or three
@@ -582,12 +634,9 @@ def main():
         prover.run()
     torch.cuda.synchronize()
 
-    # the whole step as one HIP graph; timed region = K replays on this stream
-    # (pipelined: each replay also runs the previous step's sum-check, and the
-    # last step's sum-check runs inside the timed region after the replays)
-    # several steps per graph spread the graph-launch cost (K must be a multiple)
-    # (three proofs in flight: a multiple of three steps per graph; steps beyond
-    # whole graphs run eagerly after the replays, inside the timed region)
+    # several steps per HIP graph spread the graph-launch cost (K must be a multiple; with three
+    # proofs in flight a multiple of three steps per graph; steps beyond whole graphs run eagerly
+    # after the replays, inside the timed region, and so does the drain of the last proofs)
     quantum = getattr(prover, "GRAPH_QUANTUM", 1)
     per_graph = next((d for d in (30, 12, 10, 6, 5, 4, 3, 2, 1) if d % quantum == 0 and args.steps % d == 0), quantum)
     per_graph = min(per_graph, max(quantum, args.steps - args.steps % quantum))
@@ -613,14 +662,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
-    # per-replay spread (each replay holds per_graph steps; the drain is not in these)
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) / per_graph for i in range(len(marks) - 1))
-    tokens = cfg.T
-    value = tokens / (ms * 1e-3)
+    value = cfg.T / (ms * 1e-3)
 
-    # per-phase launch durations: each phase captured alone, per_graph times in one
-    # graph (so the graph-launch cost is spread as in the step graph), K launches
-    # back to back between two events on the stream the kernels run on
+    # per-phase launch durations: each phase captured alone, per_graph times in one graph (so the
+    # graph-launch cost is spread as in the step graph), K launches back to back between two events
+    # on the stream the kernels run on
     phase_ms = {}
     for name, fn in prover.phases():
         g = torch.cuda.CUDAGraph()
@@ -659,7 +706,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(cfg, dom)  # HBM bytes per launch (counters), None if stale
     roof["algorithmic_bytes"] = b
+    roof["algorithmic_int8_ops"] = ops
     roof["kernel"] = dom
+    roof["launch_ms"] = round(phase_ms[dom], 5)
     extras = {}
     for k, v in phase_ms.items():
         bb, oo = kernel_work(cfg, k, prover)
@@ -671,11 +720,12 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "ms_per_step_replays": {"median": round(per_step[len(per_step) // 2], 5), "min": round(per_step[0], 5),
-                                "max": round(per_step[-1], 5), "replays": len(per_step)}, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8->int32 witness; u64 Goldilocks field", "data": "synthetic",
+                                "max": round(per_step[-1], 5), "replays": len(per_step)}, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8->int32 witness; u64 Goldilocks field",
+        "data": "synthetic",
         "config": {"workload": WORKLOADS[cfg.cid], "T": cfg.T, "seed": cfg.seed, "s": cfg.s,
                    "matmuls": [[m.name, m.d_in, m.d_out] for m in cfg.matmuls] if cfg.matmuls else None,
-                   "pipelined": pipelined, "proofs_in_flight": 3 if overlapped else (2 if pipelined else 1),
+                   "pipelined": pipelined or overlapped, "proofs_in_flight": 3 if overlapped else (2 if pipelined else 1),
                    "steps_per_graph": per_graph},
         "roofline": roof,
         "fold_claim_GBps": extras.get("fold+claim", {}).get("GB/s"),
@@ -685,15 +735,81 @@ def main():
         "weights_packed": packed,
         "wall_s": round(wall, 3),
     }
+    del prover
+    torch.cuda.empty_cache()
+    out["cpu_baseline"] = cpu_baseline(cfg, inp, ch) if with_cpu else None
+    return out, (cfg, inp)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=90)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--config", type=int, default=5,
+                    help="the workload timed (default 5: the seven maps of a T=4096 transformer layer, the largest "
+                         "that fits one GPU)")
+    ap.add_argument("--secondary-config", type=int, default=2,
+                    help="a second workload timed the same way and reported under 'secondary' (0: none)")
+    ap.add_argument("--legs-config", type=int, default=2,
+                    help="the workload whose first matrix the faithful, lookup, commitment and request-vector legs "
+                         "use")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="prove steps one after another instead of overlapping consecutive proofs")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="single layers: two proofs in flight instead of three; multi-map layers: one")
+    ap.add_argument("--no-faithful", action="store_true",
+                    help="skip the soundness-faithful proof (commitment, Fiat-Shamir, extension-field challenges)")
+    ap.add_argument("--no-lookup", action="store_true",
+                    help="skip the remainder lookup measurement (product tree, multiplicities, proof of the tree)")
+    ap.add_argument("--no-commitment", action="store_true",
+                    help="skip the commitment measurement (Y and R packed, Reed-Solomon encoded, Merkle hashed)")
+    ap.add_argument("--no-request-vectors", action="store_true",
+                    help="skip the batch request-vector measurement (64 eq vectors folded against the first weight "
+                         "matrix in one pass)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one device-to-device copy of MIB MiB (a reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this prover runs on one GPU; --gpus %d is not supported (each box has one GPU)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+
+    fp.require_gpu()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    out, _ = layer_bench(args.config, args, dev, not args.no_cpu_baseline, True)
+    if args.secondary_config and args.secondary_config != args.config:
+        sec, _ = layer_bench(args.secondary_config, args, dev, False, False)
+        out["secondary"] = {k: sec[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_replays", "config",
+                                                  "roofline", "witness_mfma_frac", "phases")}
+    legs = synth.config(args.legs_config)
+    need_legs = not (args.no_faithful and args.no_lookup and args.no_commitment and args.no_request_vectors)
+    linp = synth.make_inputs(legs) if need_legs else None
+    quantum_graph = 10
+    with_cpu = not args.no_cpu_baseline
     if not args.no_faithful:
-        out["faithful"] = faithful_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
+        out["faithful"] = faithful_leg(legs, linp, dev, args.steps, quantum_graph, with_cpu)
     if not args.no_lookup:
-        out["lookup"] = lookup_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
+        out["lookup"] = lookup_leg(legs, linp, dev, args.steps, quantum_graph, with_cpu)
     if not args.no_commitment:
-        out["commitment"] = commitment_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
+        out["commitment"] = commitment_leg(legs, linp, dev, args.steps, quantum_graph, with_cpu)
     if not args.no_request_vectors:
-        out["request_vectors"] = request_vectors_leg(cfg, inp, dev, args.steps, per_graph, not args.no_cpu_baseline)
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(cfg, inp, ch)
+        out["request_vectors"] = request_vectors_leg(legs, linp, dev, args.steps, quantum_graph, with_cpu)
     print(json.dumps(out))
 
 
