@@ -54,6 +54,14 @@ def kernel_work(cfg, name: str, prover) -> tuple:
         wbytes = ne * 2 * d * dff
         if name == "witness":
             return wbytes + T * (d + dff) + 6 * T * (d + dff), 2 * T * d * dff * 2
+        if name == "witness(Y,R)":  # Z stays in the accumulators
+            return wbytes + T * (d + dff) + 2 * T * (d + dff), 2 * T * d * dff * 2
+        if name == "claim(acc)":  # the tile's eq-table entries
+            return 8 * (T + ne * (dff + d)), 0
+        if name == "eq":
+            return 8 * (sum(1 << k for k in prover.nt) + ne * ((1 << prover.n_up) + (1 << prover.n_dn))), 0
+        if name == "group":
+            return 2 * T * (d + dff), 0
         if name == "fold":
             return wbytes + T * (d + dff) + 8 * 2 * ne * ((1 << prover.n_up) + (1 << prover.n_dn)), 0
         if name == "claim":

@@ -99,6 +99,30 @@ int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int8_t* const*
                               const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out, int32_t s,
                               int32_t* Z, int8_t* Y, int8_t* R, hipStream_t stream);
 
+/* Grouped witness from packed weights, each group's claim taken from its
+ * accumulators ("How fast can FlashProve go", §2: each token goes to one
+ * routed expert, so each expert's matmul covers its own rows; §3.1: the claim
+ * is about the product, so Z need not be stored): as fp_witness_linear_grouped
+ * (group g owns rows [row_off[g], row_off[g+1]) of X, int8 [row_off[G], d_in]
+ * with 16-byte aligned rows and d_in % 16 == 0, and of Y, R (and Z unless
+ * NULL), [row_off[G], d_out] dense), with group g's weights packed by
+ * fp_witness_pack_weights (Wp: host array of G device pointers, 16-byte
+ * aligned). E_t non-NULL (host array of G device pointers, each a table of >=
+ * the group's rows): claims[g] = sum_t sum_o E_t[g][t] E_o[g ldeo + o] Z_g[t, o]
+ * for every non-empty group (E_o: device, ldeo >= d_out; claims: device [G];
+ * the tables complete before the call), with ws of
+ * fp_witness_grouped_packed_workspace(row_off, G, d_out) bytes, 256-byte
+ * aligned, whose first G * 64 bytes (arrival counters) are zero on entry and
+ * left zero. row_off (host, G + 1, non-decreasing, row_off[0] = 0), Wp and E_t
+ * are read during the call only. G <= FP_MAX_GROUPS (one launch per 128
+ * groups). Empty groups own no tiles and get no claim. */
+int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int8_t* const* Wp, const int32_t* row_off,
+                              int32_t G, int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R,
+                              const fp_elem* const* E_t, const fp_elem* E_o, int64_t ldeo, fp_elem* claims,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+/* Bytes of fp_witness_grouped_packed's workspace; 0 on bad arguments. */
+size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_out);
+
 /* ----------------------------------------------------------- grouping --- */
 /* MoE grouping plan, host only (no device work). route (host, T entries in
  * [0, n_experts)) gives each token's expert. Writes counts[e] (host,

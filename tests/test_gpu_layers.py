@@ -90,9 +90,15 @@ def test_layer_batched_reduced(fp, shape, keep_z):
     assert got["batch"]["claim0"] == want["batch"]["claim0"] == want["batch"]["c0"] == got["batch"]["c0"]
 
 
-def test_layer_moe_reduced(fp):
-    cfg = synth.config(4, T=200, d=96, d_ff=160, n_experts=12)
-    inp, ch, got = _run(cfg)
+@pytest.mark.parametrize("shape,keep_z", [(dict(T=200, d=96, d_ff=160, n_experts=12), False),
+                                          (dict(T=200, d=96, d_ff=168, n_experts=12), False),
+                                          (dict(T=300, d=128, d_ff=256, n_experts=9), True)])
+def test_layer_moe_reduced(fp, shape, keep_z):
+    """The MoE block on reduced shapes: packed weights with every expert's claim from the accumulators where d
+    and d_ff are multiples of 16, else the row-major grouped witness with the claims from the stored Z; every
+    expert's outputs against the oracle."""
+    cfg = synth.config(4, **shape)
+    inp, ch, got = _run(cfg, keep_z)
     want = O.prove_config(cfg, inp, ch)
     assert sorted(got.keys()) == sorted(want.keys())
     for e in want:
@@ -377,26 +383,33 @@ def test_full_overlapped_multi(fp, cid):
             assert np.array_equal(got["batch"]["rounds"], rounds) and got["batch"]["claim0"] == claim0
 
 
-def test_full_cfg4_sampled_experts(fp):
+def test_full_cfg4_every_expert(fp):
+    """The full MoE block (2,048 tokens over 128 experts, every projection's claim from the accumulators): for
+    every expert present, the folds x' and w', the claim c0 (equal to the oracle's initial claim
+    sum_k x'[k] w'[k], since Z = X W^T), every round and the finals equal the oracle's, computed from the
+    oracle's own folds; Y and R at sampled entries of every expert against the oracle's witness entries."""
     cfg = synth.config(4)
     inp, ch, got = _run(cfg)
     groups = O.group_tokens(inp["route"], cfg.n_experts)
     present = [e for e in range(cfg.n_experts) if len(groups[e])]
     assert sorted(got.keys()) == present
-    sizes = {e: len(groups[e]) for e in present}
-    pick = sorted({present[0], present[-1], max(present, key=lambda e: sizes[e]), min(present, key=lambda e: sizes[e]),
-                   present[len(present) // 2], present[len(present) // 3]})
-    for e in pick:
+    rng = np.random.default_rng(44)
+    for e in present:
         toks = groups[e]
         assert np.array_equal(got[e]["tokens"], toks)
-        Xe, He = np.ascontiguousarray(inp["X"][toks]), np.ascontiguousarray(inp["H"][toks])
-        _check_full_matmul(Xe, inp["W1_%d" % e], cfg.s, got[e]["up"], ch["r_t/%d" % e], ch["r_o_up/%d" % e],
-                           ch["rounds_up/%d" % e])
-        _check_full_matmul(He, inp["W2_%d" % e], cfg.s, got[e]["down"], ch["r_t/%d" % e], ch["r_o_down/%d" % e],
-                           ch["rounds_down/%d" % e])
-    # every expert: the sum-check transcript verifies against its own claim
-    for e in present:
-        for side in ("up", "down"):
+        for side, Xs, W in (("up", inp["X"], inp["W1_%d" % e]), ("down", inp["H"], inp["W2_%d" % e])):
             g = got[e][side]
-            key = "rounds_up/%d" % e if side == "up" else "rounds_down/%d" % e
-            assert O.check_sumcheck(g["rounds"], g["finals"], ch[key], g["c0"])[0] == "OK"
+            Xe = np.ascontiguousarray(Xs[toks])
+            r_t, r_o = ch["r_t/%d" % e], ch["r_o_%s/%d" % (side, e)]
+            rr = ch["rounds_%s/%d" % (side, e)]
+            want = O.prove_matmul(Xe, W, cfg.s, r_t, r_o, rr, witness_full=False)
+            for k in ("x_fold", "w_fold", "rounds", "claim0"):
+                assert np.array_equal(np.asarray(g[k]), np.asarray(want[k])), (e, side, k)
+            assert np.array_equal(np.asarray(g["finals"]).reshape(-1, 2), want["finals"]), (e, side)
+            assert g["c0"] == want["claim0"], (e, side)
+            n = min(64, Xe.shape[0] * W.shape[0])
+            ts = rng.integers(0, Xe.shape[0], n).astype(np.int32)
+            os_ = rng.integers(0, W.shape[0], n).astype(np.int32)
+            z = O.witness_entries(Xe, W, ts, os_)
+            _, r, y = O.rescale(z, cfg.s)
+            assert np.array_equal(g["Y"][ts, os_], y) and np.array_equal(g["R"][ts, os_], r), (e, side)

@@ -263,3 +263,58 @@ def test_layer_step_multi_folds_claims_and_eq(fp):
         assert np.array_equal(fp.field_numpy(sc.rounds), swant[0])
         assert np.array_equal(fp.field_numpy(sc.finals).reshape(-1, 2), swant[1])
         assert int(ws.buf[:512 + 16384].count_nonzero()) == 0
+
+
+# ------------------------------------------------ fp_witness_grouped_packed ---
+@pytest.mark.parametrize("rows,d_in,d_out,claims,keep_z", [
+    ([5, 0, 40, 1, 300, 33], 96, 700, True, False), ([1, 2, 3], 64, 256, True, True),
+    ([0, 0, 129], 2000, 31, True, True), ([32, 64, 17], 512, 300, False, True), ([0, 0], 64, 64, True, False)])
+def test_witness_grouped_packed(fp, rows, d_in, d_out, claims, keep_z):
+    """Groups of rows (empty ones included) each with their own packed weights: Y, R (and Z) of every group and
+    every non-empty group's claim from the accumulators against the oracle, on two calls in a row; the counters
+    are zero after each call."""
+    rng = _rng(zlib.crc32(repr((rows, d_in, d_out)).encode()))
+    G = len(rows)
+    row_off = [0]
+    for r in rows:
+        row_off.append(row_off[-1] + r)
+    T = row_off[-1]
+    X = _i8(rng, (T, d_in))
+    Ws = [_i8(rng, (d_out, d_in)) for _ in range(G)]
+    Wps = [fp.pack_weights(_dev(w)) for w in Ws]
+    E_ts, Eo_h, want_c = [], [], []
+    for g in range(G):
+        a, b = row_off[g], row_off[g + 1]
+        Et_h = _field(rng, max(1, b - a))
+        Eo = _field(rng, d_out)
+        E_ts.append(fp.to_field_tensor(Et_h))
+        Eo_h.append(Eo)
+        if b > a:
+            Z, _, _ = O.witness(X[a:b], Ws[g], 8)
+            want_c.append(_claim_def(Z, Et_h[:b - a], Eo))
+        else:
+            want_c.append(None)
+    E_o = fp.to_field_tensor(np.stack(Eo_h)).reshape(G, d_out)
+    c = torch.full((G,), -1, dtype=torch.int64, device="cuda")
+    Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
+    Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda") if keep_z else None
+    ws = fp.StepWorkspace()
+    for rep in range(2):
+        Y.fill_(3)
+        R.fill_(3)
+        fp.witness_grouped_packed(_dev(X), Wps, row_off, 8, Y, R, Z, E_ts if claims else None,
+                                  E_o if claims else None, c if claims else None, ws=ws)
+        torch.cuda.synchronize()
+        for g in range(G):
+            a, b = row_off[g], row_off[g + 1]
+            if b == a:
+                continue
+            wz, wy, wr = O.witness(X[a:b], Ws[g], 8)
+            assert np.array_equal(Y[a:b].cpu().numpy(), wy) and np.array_equal(R[a:b].cpu().numpy(), wr)
+            if keep_z:
+                assert np.array_equal(Z[a:b].cpu().numpy(), wz)
+            if claims:
+                assert int(fp.field_numpy(c[g:g + 1])[0]) == want_c[g]
+        if claims:
+            assert ws.buf is None or int(ws.buf[:G * 64].count_nonzero()) == 0

@@ -33,6 +33,7 @@ EXPORTS = [
     "fp_witness_pack_weights", "fp_witness_linear_packed", "fp_witness_linear_packed_with_sumcheck",
     "fp_layer_step", "fp_layer_step_workspace", "fp_witness_multi", "fp_witness_multi_workspace",
     "fp_witness_multi_noalloc", "fp_layer_step_multi", "fp_layer_step_multi_workspace",
+    "fp_witness_grouped_packed", "fp_witness_grouped_packed_workspace",
 ]
 
 _lib = None
@@ -134,6 +135,9 @@ def lib():
             "fp_witness_multi_noalloc": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, vp]),
             "fp_layer_step_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
             "fp_layer_step_multi_workspace": (sz, [i32, vp, i32, vp, i32, vp]),
+            "fp_witness_grouped_packed": (ctypes.c_int, [vp, i64, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
+                                                         vp, vp, sz, vp]),
+            "fp_witness_grouped_packed_workspace": (sz, [vp, i32, i32]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -470,6 +474,40 @@ def witness_multi_noalloc(jobs, s: int, group_o: int = 1, eq=None):
     arr = _multi_descs(jobs)
     ne, eqd = _eq_descs(eq)
     _check(lib().fp_witness_multi_noalloc(len(jobs), arr, s, group_o, ne, eqd, _stream()), "fp_witness_multi_noalloc")
+
+
+def witness_grouped_packed(Xg, Wps, row_off, s: int, Y, R, Z=None, E_ts=None, E_o=None, claims=None,
+                           ws: StepWorkspace | None = None):
+    """Grouped witness from packed weights (Wps: PackedWeights per group), rows row_off (host ints, G + 1);
+    with E_ts (per-group tables), E_o (int64 [G, >= d_out]) and claims (int64 [G]) every non-empty group's
+    claim sum_t sum_o E_t[t] E_o[o] Z[t, o] from the accumulators."""
+    G = len(Wps)
+    T, d_in = Xg.shape
+    d_out = Wps[0].d_out if G else 0
+    assert Xg.dtype == torch.int8 and (Xg.numel() == 0 or Xg.stride(1) == 1) and len(row_off) == G + 1
+    assert all(w.d_in == d_in and w.d_out == d_out for w in Wps) and row_off[-1] <= T
+    _need(Y, torch.int8, row_off[-1] * d_out, "Y")
+    _need(R, torch.int8, row_off[-1] * d_out, "R")
+    if Z is not None:
+        _need(Z, torch.int32, row_off[-1] * d_out, "Z")
+    ro = (ctypes.c_int32 * (G + 1))(*row_off)
+    wp = (ctypes.c_void_p * max(G, 1))(*[w.data.data_ptr() for w in Wps])
+    et = None
+    ldeo = 0
+    p, nb = None, 0
+    if E_ts is not None:
+        for g in range(G):
+            if row_off[g + 1] > row_off[g]:
+                _need(E_ts[g], torch.int64, row_off[g + 1] - row_off[g], "E_t")
+        assert E_o.dim() == 2 and E_o.shape[0] >= G and E_o.stride(1) == 1 and E_o.dtype == torch.int64
+        _need(claims, torch.int64, G, "claims")
+        et = (ctypes.c_void_p * max(G, 1))(*[e.data_ptr() for e in E_ts])
+        ldeo = E_o.stride(0)
+        ws = _ws_step if ws is None else ws
+        p, nb = ws.get(lib().fp_witness_grouped_packed_workspace(ro, G, d_out))
+    _check(lib().fp_witness_grouped_packed(_ptr(Xg), _ld(Xg), wp, ro, G, d_in, d_out, s, _ptr(Z), _ptr(Y), _ptr(R),
+                                           et, _ptr(E_o), ldeo, _ptr(claims), p, nb, _stream()),
+           "fp_witness_grouped_packed")
 
 
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):

@@ -75,14 +75,14 @@ constexpr size_t CLAIM_CTR_BYTES = (size_t)MM_MAX * 64;
 // Tile config: NW waves of 32 TM weight rows x 32 TN tokens.
 template <int NW, int TM, int TN, int PFW, int PFX, int NBUF>
 struct MCfg {
-  static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
-  static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32;
+  static constexpr int NWAVES = NW, NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
+  static constexpr int PITCH = BK + 16, CPR = BK / 16, NCB = BT * CPR, CB = (NCB + NT - 1) / NT, KS = BK / 32;
   static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
   static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8;
   static constexpr int LOOP_BYTES = NBUF * BT * PITCH;
   static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
   static constexpr int LDS_BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
-  static_assert((BT * CPR) % NT == 0, "X chunks per thread");
+  static_assert(NCB % NT == 0 || NCB < NT, "X chunks: whole rounds, or fewer chunks than threads");
   static_assert(KS == 2, "two k-steps per packed K block");
 };
 
@@ -111,11 +111,13 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   int kc[CB], so[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
-    const int ch = tid + c * NT, row = ch / CPR;
+    // with fewer chunks than threads the upper threads load a duplicate and do not store it
+    const int ch = (tid + c * NT) % C::NCB, row = ch / CPR;
     kc[c] = (ch % CPR) * 16;
     px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx;  // rows past T: the last row (never stored)
     so[c] = row * PITCH + kc[c];
   }
+  const bool xstore = C::NCB >= NT || tid < C::NCB;  // wave-uniform
   const int klim = a.K;
   v4i wf[PFW][TM][KS];
   v4i xr[PFX][CB];
@@ -135,8 +137,10 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
     }
   };
   auto sstore = [&](int slot, int buf) {
+    if (xstore) {
 #pragma unroll
-    for (int c = 0; c < CB; ++c) *(v4i*)&sB[buf][so[c]] = xr[slot][c];
+      for (int c = 0; c < CB; ++c) *(v4i*)&sB[buf][so[c]] = xr[slot][c];
+    }
   };
   // X fragments of k-step q of LDS stage buf (lane: token r of each 32-row block,
   // the 16 bytes of k the weight fragment's lane half holds)
@@ -362,6 +366,76 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // ahead through 3 LDS stages.
 #define WIT_MULTI 4, 2, 4, 3, 3, 3, 0
 
+// ---- groups of rows, one weight matrix each (the experts of an MoE block) --
+// Group g owns rows [row_off[g], row_off[g+1]) of X and of the outputs and its
+// own packed weights; its tiles are [tile_off[g], tile_off[g+1]) of the
+// launch (256 outputs x 32 tokens: an expert holds few tokens), dealt to the
+// XCDs in contiguous runs, so a weight panel's token tiles share one L2.
+constexpr int GRP_MAX = 128;
+struct GroupArgs {
+  const int8_t* X;
+  int64_t ldx;
+  int32_t* Z;
+  int8_t* Y;
+  int8_t* R;
+  const int8_t* Wp[GRP_MAX];
+  const uint64_t* Et[GRP_MAX];  // group g's E_t (claims), or all NULL
+  const uint64_t* Eo;           // group g's E_o at Eo + g ldeo
+  int64_t ldeo;
+  uint64_t* cout;               // group g's claim at cout[g]
+  uint64_t* cpart;              // one slot per GEMM wave of the launch
+  uint32_t* cctr;               // one 64-byte counter line per group
+  int32_t row_off[GRP_MAX + 1];
+  int32_t tile_off[GRP_MAX + 1];
+  int32_t gid[GRP_MAX];         // the caller's index of each (non-empty) group of the launch
+  int32_t G, N, K, s, wp_rb, wp_kb, vecZ, vecYR, tiles_o;
+};
+#define WIT_GROUPED 4, 2, 1, 3, 3, 3, 0
+
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void witness_grouped_kernel(
+    GroupArgs ga) {
+  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  __shared__ __align__(16) int8_t lds[C::LDS_BYTES];
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  int lo = 0, hi = ga.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ga.tile_off[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int r0 = ga.row_off[g];
+  WitArgs a{};
+  a.X = ga.X + (int64_t)r0 * ga.ldx; a.ldx = ga.ldx; a.W = ga.Wp[g];
+  a.T = ga.row_off[g + 1] - r0; a.N = ga.N; a.K = ga.K; a.s = ga.s;
+  a.Z = ga.Z ? ga.Z + (int64_t)r0 * ga.N : nullptr;
+  a.Y = ga.Y + (int64_t)r0 * ga.N;
+  a.R = ga.R + (int64_t)r0 * ga.N;
+  a.tiles_t = (a.T + C::BT - 1) / C::BT; a.tiles_o = ga.tiles_o;
+  a.vecZ = ga.vecZ; a.vecYR = ga.vecYR;
+  a.wp_rb = ga.wp_rb; a.wp_kb = ga.wp_kb;
+  if (ga.Et[g]) {
+    const int id = ga.gid[g];
+    a.cEt = ga.Et[g];
+    a.cEo = ga.Eo + (int64_t)id * ga.ldeo;
+    a.cout = ga.cout + id;
+    a.cpart = ga.cpart + (int64_t)ga.tile_off[g] * NW;
+    a.cctr = ga.cctr + 16 * id;
+  }
+  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED>(a, tile - ga.tile_off[g], ga.tile_off[g + 1] - ga.tile_off[g], 1, lds);
+}
+
+using GC = MCfg<4, 2, 1, 3, 3, 3>;
+
+// Workspace of a grouped call: a 64-byte counter line per group, then one claim
+// slot per GEMM wave of every tile.
+size_t grouped_ws_bytes(const int32_t* row_off, int32_t G, int32_t d_out) {
+  int64_t tiles = 0;
+  for (int g = 0; g < G; ++g) tiles += (int64_t)((row_off[g + 1] - row_off[g] + GC::BT - 1) / GC::BT);
+  tiles *= (d_out + GC::BO - 1) / GC::BO;
+  return fpi::align_up((size_t)G * 64, 256) + fpi::align_up((size_t)tiles * GC::NWAVES * 8, 256);
+}
+
 struct MultiPlan {
   int64_t tiles[MM_MAX];
   size_t part_off[MM_MAX];
@@ -438,6 +512,93 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
 }
 
 }  // namespace
+
+extern "C" size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_out) {
+  if (G < 0 || G > FP_MAX_GROUPS || !row_off || d_out < 0) return 0;
+  for (int g = 0; g < G; ++g)
+    if (row_off[g + 1] < row_off[g]) return 0;
+  return grouped_ws_bytes(row_off, G, d_out);
+}
+
+extern "C" int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int8_t* const* Wp, const int32_t* row_off,
+                                         int32_t G, int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
+                                         int8_t* R, const fp_elem* const* E_t, const fp_elem* E_o, int64_t ldeo,
+                                         fp_elem* claims, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_witness_grouped_packed";
+  if (G < 0 || G > FP_MAX_GROUPS) return fpi::fail(FP_EARG, "%s: G=%d outside [0, %d]", fn, G, FP_MAX_GROUPS);
+  if (G == 0) return fpi::ok();
+  if (!row_off || !Wp) return fpi::fail(FP_EARG, "%s: null host array", fn);
+  if (row_off[0] != 0) return fpi::fail(FP_EARG, "%s: row_off[0] != 0", fn);
+  for (int g = 0; g < G; ++g)
+    if (row_off[g + 1] < row_off[g]) return fpi::fail(FP_EARG, "%s: row_off decreases at %d", fn, g);
+  const int32_t total = row_off[G];
+  if (d_in < 0 || d_out < 0) return fpi::fail(FP_EARG, "%s: negative size", fn);
+  if (d_in > FP_MAX_DIN) return fpi::fail(FP_ESHAPE, "%s: d_in=%d > %d", fn, d_in, FP_MAX_DIN);
+  if (s < 1 || s > 8) return fpi::fail(FP_ERANGE, "%s: s=%d outside [1, 8]", fn, s);
+  if (ldx < d_in) return fpi::fail(FP_ESHAPE, "%s: ldx < d_in", fn);
+  if (total == 0 || d_out == 0) return fpi::ok();
+  if (!Y || !R) return fpi::fail(FP_EARG, "%s: null Y or R", fn);
+  if (d_in > 0) {
+    if (!X) return fpi::fail(FP_EARG, "%s: null X", fn);
+    if (d_in % 16 != 0 || ldx % 16 != 0 || (((uintptr_t)X) & 15) != 0)
+      return fpi::fail(FP_ESHAPE, "%s: needs d_in %% 16 == 0 and 16-byte aligned X rows", fn);
+  }
+  const bool claim = E_t != nullptr;
+  if (claim) {
+    if (!E_o || !claims || ldeo < d_out) return fpi::fail(FP_EARG, "%s: claims need E_o (ldeo >= d_out) and outputs", fn);
+    const size_t need = grouped_ws_bytes(row_off, G, d_out);
+    if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    if ((((uintptr_t)ws) & 255) != 0) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
+  }
+  for (int g = 0; g < G; ++g) {
+    if (row_off[g + 1] == row_off[g]) continue;
+    if (d_in > 0 && (!Wp[g] || (((uintptr_t)Wp[g]) & 15)))
+      return fpi::fail(FP_EARG, "%s: packed W of group %d is null or not 16-byte aligned", fn, g);
+    if (claim && !E_t[g]) return fpi::fail(FP_EARG, "%s: null E_t for group %d", fn, g);
+  }
+  GroupArgs ga{};
+  ga.X = X; ga.ldx = ldx; ga.Z = Z; ga.Y = Y; ga.R = R;
+  ga.N = d_out; ga.K = d_in; ga.s = s;
+  ga.wp_rb = (d_out + 31) / 32;
+  ga.wp_kb = (d_in + WP_BK - 1) / WP_BK;
+  ga.tiles_o = (d_out + GC::BO - 1) / GC::BO;
+  ga.vecZ = ((d_out & 3) == 0) && ((((uintptr_t)Z) & 15) == 0);
+  ga.vecYR = ((d_out & 15) == 0) && ((((uintptr_t)Y) & 15) == 0) && ((((uintptr_t)R) & 15) == 0);
+  ga.Eo = E_o;
+  ga.ldeo = ldeo;
+  static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments must fit 4 KiB");
+  const size_t ctr_bytes = fpi::align_up((size_t)G * 64, 256);
+  ga.cout = claims;
+  ga.cctr = claim ? (uint32_t*)ws : nullptr;
+  int64_t tile_base = 0;  // tiles of the launches before (their claim slots)
+  for (int g0 = 0; g0 < G; g0 += GRP_MAX) {
+    const int gc = (G - g0) < GRP_MAX ? (G - g0) : GRP_MAX;
+    int ng = 0;
+    int64_t tiles = 0;
+    for (int g = g0; g < g0 + gc; ++g) {
+      const int rows = row_off[g + 1] - row_off[g];
+      if (rows == 0) continue;  // empty groups own no tiles
+      ga.Wp[ng] = Wp[g];
+      ga.Et[ng] = claim ? E_t[g] : nullptr;
+      ga.gid[ng] = g;
+      ga.row_off[ng] = row_off[g];
+      ga.row_off[ng + 1] = row_off[g + 1];
+      ga.tile_off[ng] = (int32_t)tiles;
+      tiles += (int64_t)((rows + GC::BT - 1) / GC::BT) * ga.tiles_o;
+      ++ng;
+    }
+    if (ng == 0) continue;
+    if (tiles > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many tiles", fn);
+    ga.tile_off[ng] = (int32_t)tiles;
+    ga.G = ng;
+    ga.cpart = claim ? (uint64_t*)((char*)ws + ctr_bytes) + tile_base * GC::NWAVES : nullptr;
+    hipLaunchKernelGGL((witness_grouped_kernel<WIT_GROUPED>), dim3((unsigned)tiles), dim3(GC::NT), 0, stream, ga);
+    const int rc = fpi::check_launch("witness_grouped_kernel");
+    if (rc) return rc;
+    tile_base += tiles;
+  }
+  return fpi::ok();
+}
 
 extern "C" size_t fp_witness_multi_workspace(int32_t count, const fp_matmul_desc* mm) {
   MultiPlan p;

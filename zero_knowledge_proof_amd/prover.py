@@ -27,8 +27,8 @@ from . import (MatmulJob, StepWorkspace, SumcheckJob, combine_claims, layer_step
                ext_claim_combine, field_numpy, fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows,
                layer_step, linear_combine, merkle_commit, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs,
                sumcheck_prove, sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped,
-               witness_linear_packed, witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck,
-               witness_multi)
+               witness_grouped_packed, witness_linear_packed, witness_linear_packed_with_sumcheck,
+               witness_linear_with_sumcheck, witness_multi)
 
 
 def _nomark(name):
@@ -658,12 +658,19 @@ class MoEBlockProver(_Prover):
     """MoE block: top-1 routed tokens grouped by expert (stable, ascending
     token order), one grouped witness launch per projection, and an
     independent claim + sum-check per expert and projection. A group of T_e
-    tokens is logically padded with zero rows to 2^ceil(log2 T_e)."""
+    tokens is logically padded with zero rows to 2^ceil(log2 T_e).
+
+    With d and d_ff multiples of 16 (the full-size block) every expert's
+    weights are packed once and the grouped witness reads them
+    (fp_witness_grouped_packed), forming each expert's claim from its GEMM's
+    accumulators, so Z is neither stored nor read back; the eq tables are
+    built before it. Otherwise the row-major grouped witness stores Z and the
+    claims come from it in the fold launch. keep_z: also store Z (tests)."""
 
     OUTPUTS = ("Xg", "Hg", "Zu", "Yu", "Ru", "Zd", "Yd", "Rd", "E_t", "E_ou", "E_od", "Au", "Bu", "Ad", "Bd", "c0",
                "rounds_u", "rounds_d", "finals", "claim0")
 
-    def __init__(self, cfg, inp: dict, ch: dict, dev=None):
+    def __init__(self, cfg, inp: dict, ch: dict, dev=None, keep_z: bool = False):
         dev = dev or torch.device("cuda")
         self.cfg = cfg
         s, d, dff = cfg.s, cfg.d_model, cfg.d_ff
@@ -677,15 +684,20 @@ class MoEBlockProver(_Prover):
         self.X, self.H = _i8(inp["X"], dev), _i8(inp["H"], dev)
         self.W1 = [_i8(inp["W1_%d" % e], dev) for e in self.experts]
         self.W2 = [_i8(inp["W2_%d" % e], dev) for e in self.experts]
+        self.packed = d % 16 == 0 and dff % 16 == 0
+        self.keep_z = keep_z or not self.packed
+        if self.packed:
+            self.W1p = [pack_weights(w) for w in self.W1]
+            self.W2p = [pack_weights(w) for w in self.W2]
         T = len(route)
         self.Xg = torch.empty((T, d), dtype=torch.int8, device=dev)
         self.Hg = torch.empty((T, dff), dtype=torch.int8, device=dev)
         self.row_off = [0] + [int(offsets[e + 1]) for e in self.experts]
         self.n_up, self.n_dn = log2ceil(d), log2ceil(dff)   # sum-check rounds over each d_in
-        self.Zu = torch.empty((T, dff), dtype=torch.int32, device=dev)
+        self.Zu = torch.empty((T, dff), dtype=torch.int32, device=dev) if self.keep_z else None
         self.Yu = torch.empty((T, dff), dtype=torch.int8, device=dev)
         self.Ru = torch.empty((T, dff), dtype=torch.int8, device=dev)
-        self.Zd = torch.empty((T, d), dtype=torch.int32, device=dev)
+        self.Zd = torch.empty((T, d), dtype=torch.int32, device=dev) if self.keep_z else None
         self.Yd = torch.empty((T, d), dtype=torch.int8, device=dev)
         self.Rd = torch.empty((T, d), dtype=torch.int8, device=dev)
         # challenges rearranged per kind (host-side marshalling, once)
@@ -711,6 +723,7 @@ class MoEBlockProver(_Prover):
         self.rounds_d = torch.empty((ne, nd, 3), dtype=torch.int64, device=dev)
         self.finals = torch.empty((2 * ne, 2), dtype=torch.int64, device=dev)
         self.claim0 = _f(2 * ne, dev)
+        self.ws = StepWorkspace()
         # eq descriptor lists
         pos = 0
         self.rt_views = []
@@ -729,16 +742,24 @@ class MoEBlockProver(_Prover):
             self.fold_jobs.append((self.W1[i], self.E_ou[i], 1 << nu, self.Bu[i]))
             self.fold_jobs.append((self.Hg[a:b], self.E_t[i], 1 << nd, self.Ad[i]))
             self.fold_jobs.append((self.W2[i], self.E_od[i], 1 << nd, self.Bd[i]))
-            self.claim_jobs.append((self.Zu[a:b], self.E_t[i], self.E_ou[i], self.c0[i:i + 1]))
-            self.claim_jobs.append((self.Zd[a:b], self.E_t[i], self.E_od[i], self.c0[ne + i:ne + i + 1]))
+            if not self.packed:
+                self.claim_jobs.append((self.Zu[a:b], self.E_t[i], self.E_ou[i], self.c0[i:i + 1]))
+                self.claim_jobs.append((self.Zd[a:b], self.E_t[i], self.E_od[i], self.c0[ne + i:ne + i + 1]))
 
     def _group(self):
         gather_rows(self.X, self.perm, self.Xg)
         gather_rows(self.H, self.perm, self.Hg)
 
     def _witness(self):
-        witness_linear_grouped(self.Xg, self.W1, self.row_off, self.s, self.Zu, self.Yu, self.Ru)
-        witness_linear_grouped(self.Hg, self.W2, self.row_off, self.s, self.Zd, self.Yd, self.Rd)
+        ne = len(self.experts)
+        if self.packed:
+            witness_grouped_packed(self.Xg, self.W1p, self.row_off, self.s, self.Yu, self.Ru, self.Zu, self.E_t,
+                                   self.E_ou, self.c0[:ne], ws=self.ws)
+            witness_grouped_packed(self.Hg, self.W2p, self.row_off, self.s, self.Yd, self.Rd, self.Zd, self.E_t,
+                                   self.E_od, self.c0[ne:], ws=self.ws)
+        else:
+            witness_linear_grouped(self.Xg, self.W1, self.row_off, self.s, self.Zu, self.Yu, self.Ru)
+            witness_linear_grouped(self.Hg, self.W2, self.row_off, self.s, self.Zd, self.Yd, self.Rd)
 
     def _sumcheck(self):
         ne = len(self.experts)
@@ -748,8 +769,12 @@ class MoEBlockProver(_Prover):
                              claim0=self.claim0[ne:])
 
     def phases(self):
-        return [("group", self._group), ("witness", self._witness),
-                ("eq", lambda: eq_table_batched(self.eq_r, self.eq_E)),
+        eq = ("eq", lambda: eq_table_batched(self.eq_r, self.eq_E))
+        if self.packed:
+            wname = "witness+claim(acc)" if self.keep_z else "witness(Y,R)+claim(acc)"
+            return [("group", self._group), eq, (wname, self._witness),
+                    ("fold", lambda: fold_claim_batched(self.fold_jobs, [])), ("sumcheck", self._sumcheck)]
+        return [("group", self._group), ("witness", self._witness), eq,
                 ("fold+claim", lambda: fold_claim_batched(self.fold_jobs, self.claim_jobs)),
                 ("sumcheck", self._sumcheck)]
 
@@ -758,19 +783,24 @@ class MoEBlockProver(_Prover):
         Au, Bu, Ad, Bd = (field_numpy(t) for t in (self.Au, self.Bu, self.Ad, self.Bd))
         ru, rd, finals = field_numpy(self.rounds_u), field_numpy(self.rounds_d), field_numpy(self.finals)
         c0, cl = field_numpy(self.c0), field_numpy(self.claim0)
-        Zu, Yu, Ru = self.Zu.cpu().numpy(), self.Yu.cpu().numpy(), self.Ru.cpu().numpy()
-        Zd, Yd, Rd = self.Zd.cpu().numpy(), self.Yd.cpu().numpy(), self.Rd.cpu().numpy()
+        Yu, Ru = self.Yu.cpu().numpy(), self.Ru.cpu().numpy()
+        Yd, Rd = self.Yd.cpu().numpy(), self.Rd.cpu().numpy()
+        Zu = self.Zu.cpu().numpy() if self.Zu is not None else None
+        Zd = self.Zd.cpu().numpy() if self.Zd is not None else None
         out = {}
         for i, e in enumerate(self.experts):
             a, b = self.row_off[i], self.row_off[i + 1]
             toks = self.perm[a:b].cpu().numpy()
             out[e] = {"tokens": toks,
-                      "up": {"Z": Zu[a:b], "Y": Yu[a:b], "R": Ru[a:b], "x_fold": Au[i], "w_fold": Bu[i],
+                      "up": {"Y": Yu[a:b], "R": Ru[a:b], "x_fold": Au[i], "w_fold": Bu[i],
                              "c0": int(c0[i]), "rounds": ru[i], "finals": finals[i:i + 1],
                              "claim0": int(cl[i])},
-                      "down": {"Z": Zd[a:b], "Y": Yd[a:b], "R": Rd[a:b], "x_fold": Ad[i], "w_fold": Bd[i],
+                      "down": {"Y": Yd[a:b], "R": Rd[a:b], "x_fold": Ad[i], "w_fold": Bd[i],
                                "c0": int(c0[ne + i]), "rounds": rd[i], "finals": finals[ne + i:ne + i + 1],
                                "claim0": int(cl[ne + i])}}
+            if Zu is not None:
+                out[e]["up"]["Z"] = Zu[a:b]
+                out[e]["down"]["Z"] = Zd[a:b]
         return out
 
 
@@ -904,5 +934,5 @@ def make_prover(cfg, inp: dict, ch: dict, dev=None, pipelined: bool = False, ove
     if pipelined:
         raise ValueError("pipelined proofs are implemented for single-matmul layers")
     if cfg.kind == "moe":
-        return MoEBlockProver(cfg, inp, ch, dev)
+        return MoEBlockProver(cfg, inp, ch, dev, keep_z=keep_z)
     raise ValueError(cfg.kind)
