@@ -58,6 +58,10 @@ def kernel_work(cfg, name: str, prover) -> tuple:
             return wbytes + T * (d + dff) + 2 * T * (d + dff), 2 * T * d * dff * 2
         if name == "claim(acc)":  # the tile's eq-table entries
             return 8 * (T + ne * (dff + d)), 0
+        if name == "wfold(acc)":  # the weight folds from the witness's pass: outputs only (the weights are counted)
+            return 8 * ne * ((1 << prover.n_up) + (1 << prover.n_dn)), 0
+        if name == "xfold":
+            return T * (d + dff) + 8 * ne * ((1 << prover.n_up) + (1 << prover.n_dn)), 0
         if name == "eq":
             return 8 * (sum(1 << k for k in prover.nt) + ne * ((1 << prover.n_up) + (1 << prover.n_dn))), 0
         if name == "group":

@@ -115,13 +115,23 @@ int fp_witness_linear_grouped(const int8_t* X, int64_t ldx, const int8_t* const*
  * aligned, whose first G * 64 bytes (arrival counters) are zero on entry and
  * left zero. row_off (host, G + 1, non-decreasing, row_off[0] = 0), Wp and E_t
  * are read during the call only. G <= FP_MAX_GROUPS (one launch per 128
- * groups). Empty groups own no tiles and get no claim. */
+ * groups). Empty groups own no tiles and get no claim.
+ * w_fold non-NULL (device [G][ld_fold], E_o given): also the weight folds
+ * w_fold[g ld_fold + k] = sum_o E_o[g ldeo + o] W_g[o, k] for k < d_in, zero for
+ * d_in <= k < fold_cols_pad ("How fast can FlashProve go", §4: the matmuls'
+ * sum-checks need a pass over the weights; here it is the witness's own pass),
+ * for every non-empty group (empty groups' rows are left alone): the first token
+ * tile of each weight panel folds the fragments it streams on the matrix cores,
+ * and a second launch of the same call adds the panels. */
 int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int8_t* const* Wp, const int32_t* row_off,
                               int32_t G, int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y, int8_t* R,
                               const fp_elem* const* E_t, const fp_elem* E_o, int64_t ldeo, fp_elem* claims,
-                              void* ws, size_t ws_bytes, hipStream_t stream);
-/* Bytes of fp_witness_grouped_packed's workspace; 0 on bad arguments. */
-size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_out);
+                              fp_elem* w_fold, int64_t ld_fold, int32_t fold_cols_pad, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+/* Bytes of fp_witness_grouped_packed's workspace (with_fold: with weight
+ * folds); 0 on bad arguments. */
+size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out,
+                                           int32_t with_fold);
 
 /* ----------------------------------------------------------- grouping --- */
 /* MoE grouping plan, host only (no device work). route (host, T entries in

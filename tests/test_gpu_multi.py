@@ -266,13 +266,15 @@ def test_layer_step_multi_folds_claims_and_eq(fp):
 
 
 # ------------------------------------------------ fp_witness_grouped_packed ---
-@pytest.mark.parametrize("rows,d_in,d_out,claims,keep_z", [
-    ([5, 0, 40, 1, 300, 33], 96, 700, True, False), ([1, 2, 3], 64, 256, True, True),
-    ([0, 0, 129], 2000, 31, True, True), ([32, 64, 17], 512, 300, False, True), ([0, 0], 64, 64, True, False)])
-def test_witness_grouped_packed(fp, rows, d_in, d_out, claims, keep_z):
-    """Groups of rows (empty ones included) each with their own packed weights: Y, R (and Z) of every group and
-    every non-empty group's claim from the accumulators against the oracle, on two calls in a row; the counters
-    are zero after each call."""
+@pytest.mark.parametrize("rows,d_in,d_out,claims,keep_z,fold", [
+    ([5, 0, 40, 1, 300, 33], 96, 700, True, False, True), ([1, 2, 3], 64, 256, True, True, False),
+    ([0, 0, 129], 2000, 31, True, True, True), ([32, 64, 17], 512, 300, False, True, True),
+    ([0, 0], 64, 64, True, False, True), ([7, 40], 5120, 8192, True, False, True)])
+def test_witness_grouped_packed(fp, rows, d_in, d_out, claims, keep_z, fold):
+    """Groups of rows (empty ones included) each with their own packed weights: Y, R (and Z) of every group,
+    every non-empty group's claim from the accumulators and its weight fold sum_o E_o[o] W[o, k] from the same
+    pass (ragged panels, padded columns) against the oracle, on two calls in a row; the counters are zero after
+    each call."""
     rng = _rng(zlib.crc32(repr((rows, d_in, d_out)).encode()))
     G = len(rows)
     row_off = [0]
@@ -296,6 +298,8 @@ def test_witness_grouped_packed(fp, rows, d_in, d_out, claims, keep_z):
             want_c.append(None)
     E_o = fp.to_field_tensor(np.stack(Eo_h)).reshape(G, d_out)
     c = torch.full((G,), -1, dtype=torch.int64, device="cuda")
+    cols_pad = 1 << max(0, (d_in - 1).bit_length())
+    wf = torch.full((G, cols_pad), -1, dtype=torch.int64, device="cuda") if fold else None
     Y = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
     R = torch.empty((T, d_out), dtype=torch.int8, device="cuda")
     Z = torch.empty((T, d_out), dtype=torch.int32, device="cuda") if keep_z else None
@@ -304,8 +308,15 @@ def test_witness_grouped_packed(fp, rows, d_in, d_out, claims, keep_z):
         Y.fill_(3)
         R.fill_(3)
         fp.witness_grouped_packed(_dev(X), Wps, row_off, 8, Y, R, Z, E_ts if claims else None,
-                                  E_o if claims else None, c if claims else None, ws=ws)
+                                  E_o if (claims or fold) else None, c if claims else None, w_fold=wf, ws=ws)
         torch.cuda.synchronize()
+        if fold:
+            got = fp.field_numpy(wf).reshape(G, cols_pad)
+            for g in range(G):
+                if row_off[g + 1] > row_off[g]:
+                    assert np.array_equal(got[g], O.fold_rows(Ws[g], Eo_h[g], cols_pad)), g
+                else:
+                    assert np.all(got[g] == np.uint64(2**64 - 1))  # left alone
         for g in range(G):
             a, b = row_off[g], row_off[g + 1]
             if b == a:

@@ -136,8 +136,8 @@ def lib():
             "fp_layer_step_multi": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
             "fp_layer_step_multi_workspace": (sz, [i32, vp, i32, vp, i32, vp]),
             "fp_witness_grouped_packed": (ctypes.c_int, [vp, i64, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
-                                                         vp, vp, sz, vp]),
-            "fp_witness_grouped_packed_workspace": (sz, [vp, i32, i32]),
+                                                         vp, vp, i64, i32, vp, sz, vp]),
+            "fp_witness_grouped_packed_workspace": (sz, [vp, i32, i32, i32, i32]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -476,11 +476,12 @@ def witness_multi_noalloc(jobs, s: int, group_o: int = 1, eq=None):
     _check(lib().fp_witness_multi_noalloc(len(jobs), arr, s, group_o, ne, eqd, _stream()), "fp_witness_multi_noalloc")
 
 
-def witness_grouped_packed(Xg, Wps, row_off, s: int, Y, R, Z=None, E_ts=None, E_o=None, claims=None,
+def witness_grouped_packed(Xg, Wps, row_off, s: int, Y, R, Z=None, E_ts=None, E_o=None, claims=None, w_fold=None,
                            ws: StepWorkspace | None = None):
     """Grouped witness from packed weights (Wps: PackedWeights per group), rows row_off (host ints, G + 1);
     with E_ts (per-group tables), E_o (int64 [G, >= d_out]) and claims (int64 [G]) every non-empty group's
-    claim sum_t sum_o E_t[t] E_o[o] Z[t, o] from the accumulators."""
+    claim sum_t sum_o E_t[t] E_o[o] Z[t, o] from the accumulators; with w_fold (int64 [G, cols_pad], E_o
+    given) every non-empty group's weight fold sum_o E_o[o] W[o, k] from the same pass over the weights."""
     G = len(Wps)
     T, d_in = Xg.shape
     d_out = Wps[0].d_out if G else 0
@@ -495,19 +496,26 @@ def witness_grouped_packed(Xg, Wps, row_off, s: int, Y, R, Z=None, E_ts=None, E_
     et = None
     ldeo = 0
     p, nb = None, 0
+    ld_fold, cols_pad = 0, 0
+    if E_o is not None:
+        assert E_o.dim() == 2 and E_o.shape[0] >= G and E_o.stride(1) == 1 and E_o.dtype == torch.int64
+        assert E_o.shape[1] >= d_out
+        ldeo = E_o.stride(0)
     if E_ts is not None:
         for g in range(G):
             if row_off[g + 1] > row_off[g]:
                 _need(E_ts[g], torch.int64, row_off[g + 1] - row_off[g], "E_t")
-        assert E_o.dim() == 2 and E_o.shape[0] >= G and E_o.stride(1) == 1 and E_o.dtype == torch.int64
         _need(claims, torch.int64, G, "claims")
         et = (ctypes.c_void_p * max(G, 1))(*[e.data_ptr() for e in E_ts])
-        ldeo = E_o.stride(0)
+    if w_fold is not None:
+        assert w_fold.dim() == 2 and w_fold.shape[0] >= G and w_fold.stride(1) == 1 and w_fold.dtype == torch.int64
+        ld_fold, cols_pad = w_fold.stride(0), w_fold.shape[1]
+    if E_ts is not None or w_fold is not None:
         ws = _ws_step if ws is None else ws
-        p, nb = ws.get(lib().fp_witness_grouped_packed_workspace(ro, G, d_out))
+        p, nb = ws.get(lib().fp_witness_grouped_packed_workspace(ro, G, d_in, d_out, int(w_fold is not None)))
     _check(lib().fp_witness_grouped_packed(_ptr(Xg), _ld(Xg), wp, ro, G, d_in, d_out, s, _ptr(Z), _ptr(Y), _ptr(R),
-                                           et, _ptr(E_o), ldeo, _ptr(claims), p, nb, _stream()),
-           "fp_witness_grouped_packed")
+                                           et, _ptr(E_o), ldeo, _ptr(claims), _ptr(w_fold), ld_fold, cols_pad, p, nb,
+                                           _stream()), "fp_witness_grouped_packed")
 
 
 def witness_linear_grouped(Xg, Ws, row_off, s: int, Z=None, Y=None, R=None, with_z: bool = True):

@@ -45,6 +45,11 @@ struct WitArgs {
   uint64_t* cpart = nullptr;
   uint64_t* cout = nullptr;
   uint32_t* cctr = nullptr;
+  // weight fold beside the GEMM (the first token tile of each weight panel):
+  // sum_o E_o[o] W[o, k] over the panel's rows into fpart[panel fpitch + k]
+  // (cEo: the E_o table), none when fpart is NULL
+  uint64_t* fpart = nullptr;
+  int64_t fpitch = 0;
 };
 
 struct GroupTab {

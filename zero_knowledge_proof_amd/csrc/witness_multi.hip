@@ -82,12 +82,28 @@ struct MCfg {
   static constexpr int LOOP_BYTES = NBUF * BT * PITCH;
   static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
   static constexpr int LDS_BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+  // the weight fold's region after it: the panel's limb table, then two K
+  // blocks of int32 limb sums [2 k-steps][32 columns][FL words]
+  static constexpr int FL = 11;  // an odd row pitch: the 32 columns of one limb fall in distinct banks
+  static constexpr int FOLD_ACC_WORDS = 2 * 32 * FL;
+  static constexpr int FOLD_BYTES = CL_LIMBS * BO + 2 * FOLD_ACC_WORDS * 4;
+  static constexpr int LDS_FOLD_BYTES = LDS_BYTES + FOLD_BYTES;
   static_assert(NCB % NT == 0 || NCB < NT, "X chunks: whole rounds, or fewer chunks than threads");
   static_assert(KS == 2, "two k-steps per packed K block");
 };
 
 // Tile `lt` of `nt` tiles of one map (a already holds the map's arguments).
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+// FOLDW: the first token tile of each weight panel also folds the panel's
+// rows by E_o (a.fpart), from the weight fragments the GEMM streams: an MFMA
+// against the identity puts a fragment's 32 rows x 32 columns into the
+// accumulator layout, where after the v_permlane32_swap a lane holds 16
+// consecutive rows of one column, which is an MFMA B operand with the rows as
+// the reduction index; an MFMA with the 7-bit limbs of E_o as the A operand
+// then gives sum_o limb_m(E_o[o]) W[o, k] for the fragment's columns. The
+// waves' int32 limb sums meet in LDS (exact: |sum| < 2^7 2^7 BO), and after the
+// K block's barrier wave 0 turns each column's limbs into one field value
+// sum_m 2^(7m) sum_o ... = sum_o E_o[o] W[o, k] mod p for the panel.
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int FOLDW = 0>
 __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int group_o, int8_t* lds) {
   using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
   constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
@@ -163,6 +179,81 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ws][i][q], fb[fs][j], acc[i][j], 0, 0, 0);
   };
+  // ---- the weight fold's set-up (FOLDW, first token tile of the panel)
+  const bool fold_on = FOLDW && a.fpart != nullptr && tt == 0;  // uniform over the workgroup
+  uint8_t* flimbs = reinterpret_cast<uint8_t*>(lds + C::LDS_BYTES);
+  int32_t* facc = reinterpret_cast<int32_t*>(lds + C::LDS_BYTES + CL_LIMBS * BO);  // [2][FOLD_ACC_WORDS]
+  v4i FA[TM];   // limbs of E_o for the wave's row blocks (A operand, reduction over the rows)
+  v4i FI = {};  // the identity as a B operand: lane (n, h) holds rows 16 h .. 16 h + 15 of column n
+  if constexpr (FOLDW) {
+    if (fold_on) {
+      for (int x = tid; x < BO; x += NT) {
+        const int o = o_base + x;
+        const uint64_t e = o < a.N ? a.cEo[o] : 0;
+#pragma unroll
+        for (int m = 0; m < CL_LIMBS; ++m) flimbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
+      }
+      for (int x = tid; x < 2 * C::FOLD_ACC_WORDS; x += NT) facc[x] = 0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w |= (16 * h + 4 * d + b == r ? 1u : 0u) << (8 * b);
+        FI[d] = (int)w;
+      }
+      __syncthreads();
+      // byte j = 4 d + b of lane (r, h): limb r of row 8 d + 4 h + b of the row block
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          FA[i][d] = r < CL_LIMBS ? *(const int*)&flimbs[r * BO + wo0 + 32 * i + 8 * d + 4 * h] : 0;
+    }
+  }
+  // K block st's fragments folded into LDS buffer st % 2. The transpose's
+  // accumulators hold, in lane (r, h) register v, row 8 (v / 4) + 4 h + v % 4
+  // of column r: packed in register order they are the B operand, the limb
+  // operand FA pairing the same rows with the same reduction index.
+  auto fold_block = [&](int ws, int st) {
+    int32_t* F = facc + (st & 1) * C::FOLD_ACC_WORDS;
+    const v16i zero = {};
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      v16i Ff = zero;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v16i T = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[ws][i][q], FI, zero, 0, 0, 0);
+        const v4i Bf = {(int)pack_low_bytes(T[0], T[1], T[2], T[3]), (int)pack_low_bytes(T[4], T[5], T[6], T[7]),
+                        (int)pack_low_bytes(T[8], T[9], T[10], T[11]),
+                        (int)pack_low_bytes(T[12], T[13], T[14], T[15])};
+        Ff = __builtin_amdgcn_mfma_i32_32x32x32_i8(FA[i], Bf, Ff, 0, 0, 0);
+      }
+      // lane (r, h), register v: limb row 8 (v / 4) + 4 h + v % 4 of column r
+#pragma unroll
+      for (int v = 0; v < 6; ++v) {
+        const int m = v < 4 ? 4 * h + v : 8 + (v - 4);
+        if (v < 4 || h == 0) atomicAdd(&F[(q * 32 + r) * C::FL + m], Ff[v]);
+      }
+    }
+  };
+  // wave 0: K block st's limb sums -> one field value per column, then the
+  // buffer cleared for block st + 2. The limbs of each half are exact in int64
+  // (|sum| < 2^22, 5 limbs of 7 bits): lo + 2^35 hi.
+  auto fold_flush = [&](int st) {
+    if (wave != 0) return;
+    int32_t* F = facc + (st & 1) * C::FOLD_ACC_WORDS + lane * C::FL;  // lane = column q * 32 + n
+    int64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+      lo += (int64_t)F[m] << (7 * m);
+      hi += (int64_t)F[m + 5] << (7 * m);
+    }
+    const int q = lane >> 5, n = lane & 31;
+    const int k = st * BK + 32 * (n >> 4) + 16 * q + (n & 15);
+    a.fpart[(int64_t)to * a.fpitch + k] = gl::add(gl::from_i64(lo), gl::mul(gl::from_i64(hi), 1ull << 35));
+#pragma unroll
+    for (int m = 0; m < CL_LIMBS; ++m) F[m] = 0;
+  };
   // Block st: multiply stage st % NBUF with weight slot st % PFW; store block
   // st + NBUF - 1 (loaded PFX blocks ago) into its stage and load block
   // st + NBUF - 1 + PFX; refill the weight slot with block st + PFW; one
@@ -186,6 +277,9 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
     auto step = [&](auto uc, int st) {
       constexpr int u = decltype(uc)::value;
       constexpr int buf = u % NBUF, ws = u % PFW;
+      if constexpr (FOLDW) {
+        if (fold_on && st > 0) fold_flush(st - 1);
+      }
       if constexpr (NBUF < 3) fread(0, buf, 0);
       fread(1, buf, 1);
       mma(0, ws, 0);
@@ -193,6 +287,9 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       sstore(ss, (u + NBUF - 1) % NBUF);
       xload(ss, min(st + NBUF - 1 + PFX, NS - 1));
       mma(1, ws, 1);
+      if constexpr (FOLDW) {
+        if (fold_on) fold_block(ws, st);
+      }
       wload(ws, min(st + PFW, NS - 1));
       if constexpr (NBUF >= 3) fread(0, (u + 1) % NBUF, 0);
       if constexpr (SCHED == 1) {
@@ -214,6 +311,9 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ((kt + I < NS ? step(std::integral_constant<int, I>{}, kt + I) : void()), ...);
     }(std::make_integer_sequence<int, U>{});
+    if constexpr (FOLDW) {
+      if (fold_on) fold_flush(NS - 1);  // the last K block (its sums are complete after the last barrier)
+    }
   }
 
   // ---- epilogue: Y and R (and Z through LDS if asked), the claim from the accumulators
@@ -388,6 +488,8 @@ struct GroupArgs {
   int32_t row_off[GRP_MAX + 1];
   int32_t tile_off[GRP_MAX + 1];
   int32_t gid[GRP_MAX];         // the caller's index of each (non-empty) group of the launch
+  uint64_t* fpart;              // the weight folds' panel values: group g's at fpart + g tiles_o fpitch (or NULL)
+  int64_t fpitch;
   int32_t G, N, K, s, wp_rb, wp_kb, vecZ, vecYR, tiles_o;
 };
 #define WIT_GROUPED 4, 2, 1, 3, 3, 3, 0
@@ -396,7 +498,7 @@ template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void witness_grouped_kernel(
     GroupArgs ga) {
   using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
-  __shared__ __align__(16) int8_t lds[C::LDS_BYTES];
+  __shared__ __align__(16) int8_t lds[C::LDS_FOLD_BYTES];
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   int lo = 0, hi = ga.G - 1;
   while (lo < hi) {
@@ -414,26 +516,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
   a.tiles_t = (a.T + C::BT - 1) / C::BT; a.tiles_o = ga.tiles_o;
   a.vecZ = ga.vecZ; a.vecYR = ga.vecYR;
   a.wp_rb = ga.wp_rb; a.wp_kb = ga.wp_kb;
+  const int id = ga.gid[g];
+  if (ga.Eo) a.cEo = ga.Eo + (int64_t)id * ga.ldeo;
   if (ga.Et[g]) {
-    const int id = ga.gid[g];
     a.cEt = ga.Et[g];
-    a.cEo = ga.Eo + (int64_t)id * ga.ldeo;
     a.cout = ga.cout + id;
     a.cpart = ga.cpart + (int64_t)ga.tile_off[g] * NW;
     a.cctr = ga.cctr + 16 * id;
   }
-  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED>(a, tile - ga.tile_off[g], ga.tile_off[g + 1] - ga.tile_off[g], 1, lds);
+  if (ga.fpart) {
+    a.fpart = ga.fpart + (int64_t)id * ga.tiles_o * ga.fpitch;
+    a.fpitch = ga.fpitch;
+  }
+  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED, 1>(a, tile - ga.tile_off[g], ga.tile_off[g + 1] - ga.tile_off[g], 1,
+                                                   lds);
+}
+
+// The weight folds from their panels' values: out[g ldout + k] = sum over the
+// panels p of part[(g tiles_o + p) fpitch + k] for k < K, zero up to cols_pad;
+// groups whose flag is 0 (no rows, so no tiles and no panel values) are left alone.
+struct PanelSumArgs {
+  const uint64_t* part;
+  uint64_t* out;
+  int64_t fpitch, ldout;
+  int32_t tiles_o, K, cols_pad;
+  uint8_t live[FP_MAX_GROUPS];
+};
+__global__ __launch_bounds__(256) void panel_sum_kernel(PanelSumArgs pa) {
+  const int g = blockIdx.y;
+  if (!pa.live[g]) return;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= pa.cols_pad) return;
+  uint64_t v = 0;
+  if (k < pa.K) {
+    const uint64_t* p = pa.part + (int64_t)g * pa.tiles_o * pa.fpitch + k;
+    for (int t = 0; t < pa.tiles_o; ++t) v = gl::add(v, p[(int64_t)t * pa.fpitch]);
+  }
+  pa.out[(int64_t)g * pa.ldout + k] = v;
 }
 
 using GC = MCfg<4, 2, 1, 3, 3, 3>;
 
-// Workspace of a grouped call: a 64-byte counter line per group, then one claim
-// slot per GEMM wave of every tile.
-size_t grouped_ws_bytes(const int32_t* row_off, int32_t G, int32_t d_out) {
+// Workspace of a grouped call: a 64-byte counter line per group, one claim slot
+// per GEMM wave of every tile, then (with weight folds) each group's panel values.
+struct GroupedWs {
+  size_t ctr_bytes, part_bytes, fold_bytes;
+  int64_t fpitch;
+};
+GroupedWs grouped_ws(const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out, bool fold) {
   int64_t tiles = 0;
   for (int g = 0; g < G; ++g) tiles += (int64_t)((row_off[g + 1] - row_off[g] + GC::BT - 1) / GC::BT);
-  tiles *= (d_out + GC::BO - 1) / GC::BO;
-  return fpi::align_up((size_t)G * 64, 256) + fpi::align_up((size_t)tiles * GC::NWAVES * 8, 256);
+  const int64_t tiles_o = (d_out + GC::BO - 1) / GC::BO;
+  tiles *= tiles_o;
+  GroupedWs w{};
+  w.ctr_bytes = fpi::align_up((size_t)G * 64, 256);
+  w.part_bytes = fpi::align_up((size_t)tiles * GC::NWAVES * 8, 256);
+  w.fpitch = (int64_t)((d_in + WP_BK - 1) / WP_BK) * WP_BK;
+  w.fold_bytes = fold ? fpi::align_up((size_t)G * tiles_o * w.fpitch * 8, 256) : 0;
+  return w;
 }
 
 struct MultiPlan {
@@ -513,17 +653,20 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
 
 }  // namespace
 
-extern "C" size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_out) {
-  if (G < 0 || G > FP_MAX_GROUPS || !row_off || d_out < 0) return 0;
+extern "C" size_t fp_witness_grouped_packed_workspace(const int32_t* row_off, int32_t G, int32_t d_in, int32_t d_out,
+                                                      int32_t with_fold) {
+  if (G < 0 || G > FP_MAX_GROUPS || !row_off || d_out < 0 || d_in < 0) return 0;
   for (int g = 0; g < G; ++g)
     if (row_off[g + 1] < row_off[g]) return 0;
-  return grouped_ws_bytes(row_off, G, d_out);
+  const GroupedWs w = grouped_ws(row_off, G, d_in, d_out, with_fold != 0);
+  return w.ctr_bytes + w.part_bytes + w.fold_bytes;
 }
 
 extern "C" int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int8_t* const* Wp, const int32_t* row_off,
                                          int32_t G, int32_t d_in, int32_t d_out, int32_t s, int32_t* Z, int8_t* Y,
                                          int8_t* R, const fp_elem* const* E_t, const fp_elem* E_o, int64_t ldeo,
-                                         fp_elem* claims, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                         fp_elem* claims, fp_elem* w_fold, int64_t ld_fold, int32_t fold_cols_pad,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fp_witness_grouped_packed";
   if (G < 0 || G > FP_MAX_GROUPS) return fpi::fail(FP_EARG, "%s: G=%d outside [0, %d]", fn, G, FP_MAX_GROUPS);
   if (G == 0) return fpi::ok();
@@ -544,9 +687,14 @@ extern "C" int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int
       return fpi::fail(FP_ESHAPE, "%s: needs d_in %% 16 == 0 and 16-byte aligned X rows", fn);
   }
   const bool claim = E_t != nullptr;
-  if (claim) {
-    if (!E_o || !claims || ldeo < d_out) return fpi::fail(FP_EARG, "%s: claims need E_o (ldeo >= d_out) and outputs", fn);
-    const size_t need = grouped_ws_bytes(row_off, G, d_out);
+  const bool fold = w_fold != nullptr;
+  if (claim && !claims) return fpi::fail(FP_EARG, "%s: claims need an output", fn);
+  if ((claim || fold) && (!E_o || ldeo < d_out)) return fpi::fail(FP_EARG, "%s: claims and folds need E_o, ldeo >= d_out", fn);
+  if (fold && (fold_cols_pad < d_in || ld_fold < fold_cols_pad))
+    return fpi::fail(FP_ESHAPE, "%s: weight folds need d_in <= fold_cols_pad <= ld_fold", fn);
+  const GroupedWs gw = grouped_ws(row_off, G, d_in, d_out, fold);
+  if (claim || fold) {
+    const size_t need = gw.ctr_bytes + gw.part_bytes + gw.fold_bytes;
     if (!ws || ws_bytes < need) return fpi::fail(FP_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
     if ((((uintptr_t)ws) & 255) != 0) return fpi::fail(FP_EARG, "%s: workspace not 256-byte aligned", fn);
   }
@@ -567,8 +715,10 @@ extern "C" int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int
   ga.Eo = E_o;
   ga.ldeo = ldeo;
   static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments must fit 4 KiB");
-  const size_t ctr_bytes = fpi::align_up((size_t)G * 64, 256);
+  const size_t ctr_bytes = gw.ctr_bytes;
   ga.cout = claims;
+  ga.fpart = fold ? (uint64_t*)((char*)ws + gw.ctr_bytes + gw.part_bytes) : nullptr;
+  ga.fpitch = gw.fpitch;
   ga.cctr = claim ? (uint32_t*)ws : nullptr;
   int64_t tile_base = 0;  // tiles of the launches before (their claim slots)
   for (int g0 = 0; g0 < G; g0 += GRP_MAX) {
@@ -596,6 +746,21 @@ extern "C" int fp_witness_grouped_packed(const int8_t* X, int64_t ldx, const int
     const int rc = fpi::check_launch("witness_grouped_kernel");
     if (rc) return rc;
     tile_base += tiles;
+  }
+  if (fold && fold_cols_pad > 0) {
+    PanelSumArgs pa{};
+    pa.part = ga.fpart;
+    pa.out = w_fold;
+    pa.fpitch = gw.fpitch;
+    pa.ldout = ld_fold;
+    pa.tiles_o = ga.tiles_o;
+    pa.K = d_in;
+    pa.cols_pad = fold_cols_pad;
+    for (int g = 0; g < G; ++g) pa.live[g] = row_off[g + 1] > row_off[g] ? 1 : 0;
+    hipLaunchKernelGGL(panel_sum_kernel, dim3((unsigned)((fold_cols_pad + 255) / 256), (unsigned)G), dim3(256), 0,
+                       stream, pa);
+    const int rc = fpi::check_launch("panel_sum_kernel");
+    if (rc) return rc;
   }
   return fpi::ok();
 }

@@ -738,10 +738,13 @@ class MoEBlockProver(_Prover):
         self.claim_jobs = []
         for i in range(ne):
             a, b = self.row_off[i], self.row_off[i + 1]
+            # with packed weights the weight folds come from the witness's own pass over the weights
             self.fold_jobs.append((self.Xg[a:b], self.E_t[i], 1 << nu, self.Au[i]))
-            self.fold_jobs.append((self.W1[i], self.E_ou[i], 1 << nu, self.Bu[i]))
+            if not self.packed:
+                self.fold_jobs.append((self.W1[i], self.E_ou[i], 1 << nu, self.Bu[i]))
             self.fold_jobs.append((self.Hg[a:b], self.E_t[i], 1 << nd, self.Ad[i]))
-            self.fold_jobs.append((self.W2[i], self.E_od[i], 1 << nd, self.Bd[i]))
+            if not self.packed:
+                self.fold_jobs.append((self.W2[i], self.E_od[i], 1 << nd, self.Bd[i]))
             if not self.packed:
                 self.claim_jobs.append((self.Zu[a:b], self.E_t[i], self.E_ou[i], self.c0[i:i + 1]))
                 self.claim_jobs.append((self.Zd[a:b], self.E_t[i], self.E_od[i], self.c0[ne + i:ne + i + 1]))
@@ -754,9 +757,9 @@ class MoEBlockProver(_Prover):
         ne = len(self.experts)
         if self.packed:
             witness_grouped_packed(self.Xg, self.W1p, self.row_off, self.s, self.Yu, self.Ru, self.Zu, self.E_t,
-                                   self.E_ou, self.c0[:ne], ws=self.ws)
+                                   self.E_ou, self.c0[:ne], w_fold=self.Bu, ws=self.ws)
             witness_grouped_packed(self.Hg, self.W2p, self.row_off, self.s, self.Yd, self.Rd, self.Zd, self.E_t,
-                                   self.E_od, self.c0[ne:], ws=self.ws)
+                                   self.E_od, self.c0[ne:], w_fold=self.Bd, ws=self.ws)
         else:
             witness_linear_grouped(self.Xg, self.W1, self.row_off, self.s, self.Zu, self.Yu, self.Ru)
             witness_linear_grouped(self.Hg, self.W2, self.row_off, self.s, self.Zd, self.Yd, self.Rd)
@@ -771,9 +774,9 @@ class MoEBlockProver(_Prover):
     def phases(self):
         eq = ("eq", lambda: eq_table_batched(self.eq_r, self.eq_E))
         if self.packed:
-            wname = "witness+claim(acc)" if self.keep_z else "witness(Y,R)+claim(acc)"
+            wname = "witness+claim(acc)+wfold(acc)" if self.keep_z else "witness(Y,R)+claim(acc)+wfold(acc)"
             return [("group", self._group), eq, (wname, self._witness),
-                    ("fold", lambda: fold_claim_batched(self.fold_jobs, [])), ("sumcheck", self._sumcheck)]
+                    ("xfold", lambda: fold_claim_batched(self.fold_jobs, [])), ("sumcheck", self._sumcheck)]
         return [("group", self._group), ("witness", self._witness), eq,
                 ("fold+claim", lambda: fold_claim_batched(self.fold_jobs, self.claim_jobs)),
                 ("sumcheck", self._sumcheck)]
