@@ -103,7 +103,7 @@ class _Prover:
         out = []
         for name in self.OUTPUTS:
             v = getattr(self, name)
-            out.extend(v if isinstance(v, list) else [v])
+            out.extend(t for t in (v if isinstance(v, list) else [v]) if t is not None)
         return out
 
 
@@ -230,10 +230,12 @@ class OverlappedLayerProver(SingleLayerProver):
     protocol order. The buffers of a proof (Y, R, tables, folds, c0) live from
     the step that builds its eq tables to the one that runs its sum-check, so
     they rotate over three sets, and a captured graph holds a multiple of three
-    steps. ``drain()`` finishes the last two proofs; outputs are those of the
-    last proof. keep_z: also write Z (which the proof never reads back)."""
+    steps. ``drain()`` finishes the last two proofs. Each set also holds its
+    proof's rounds, finals and initial claim, so the last three proofs can be
+    read back (``results(k)``). keep_z: also write Z (which the proof never
+    reads back)."""
 
-    PER_PROOF = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0")
+    PER_PROOF = ("Z", "Y", "R", "E_t", "E_o", "xf", "wf", "c0", "rounds", "finals", "claim0")
     SETS = 3
     GRAPH_QUANTUM = 3  # steps per captured graph must be a multiple of this
 
@@ -248,6 +250,7 @@ class OverlappedLayerProver(SingleLayerProver):
         self.bufs = [first] + [
             {k: (None if v is None else torch.zeros_like(v) if k in ("xf", "wf") else torch.empty_like(v))
              for k, v in first.items()} for _ in range(self.SETS - 1)]
+        # the sum-check outputs of a proof stay with its set (read after the step that finishes it)
         self.k = 0
         self.ws = StepWorkspace()
 
@@ -266,7 +269,7 @@ class OverlappedLayerProver(SingleLayerProver):
         layer_step(self.X, self.Wp, self.s, cur["Z"], cur["Y"], cur["R"], own_claim=(cur["E_t"], cur["E_o"], cur["c0"]),
                    eq=self._eq_jobs(nxt), folds=self._folds(prev) if fold else (),
                    As=[old["xf"]] if tail else (), Bs=[old["wf"]] if tail else (), r=self.ch["rounds"],
-                   rounds=self.rounds, finals=self.finals, claim0=self.claim0, ws=self.ws)
+                   rounds=old["rounds"], finals=old["finals"], claim0=old["claim0"], ws=self.ws)
 
     def run(self, mark=_nomark):
         mark("step")
@@ -315,23 +318,24 @@ class OverlappedLayerProver(SingleLayerProver):
             return
         if last >= 1:
             prev = self._buf(last - 1)
-            sumcheck_prove([prev["xf"]], [prev["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                           claim0=self.claim0)
+            sumcheck_prove([prev["xf"]], [prev["wf"]], self.ch["rounds"], rounds=prev["rounds"],
+                           finals=prev["finals"], claim0=prev["claim0"])
         cur = self._buf(last)
         fold_claim_batched(self._folds(cur), [])
-        sumcheck_prove([cur["xf"]], [cur["wf"]], self.ch["rounds"], rounds=self.rounds, finals=self.finals,
-                       claim0=self.claim0)
+        sumcheck_prove([cur["xf"]], [cur["wf"]], self.ch["rounds"], rounds=cur["rounds"], finals=cur["finals"],
+                       claim0=cur["claim0"])
 
     def output_tensors(self):
-        return [t for b in self.bufs for t in b.values() if t is not None] + [self.rounds, self.finals, self.claim0]
+        return [t for b in self.bufs for t in b.values() if t is not None]
 
-    def results(self) -> dict:
-        b = self._buf(self.k - 1)
+    def results(self, k: int | None = None) -> dict:
+        """Outputs of proof k (default: the last one; the last three are held)."""
+        b = self._buf(self.k - 1 if k is None else k)
         out = {"Y": b["Y"].cpu().numpy(), "R": b["R"].cpu().numpy(),
                "E_t": field_numpy(b["E_t"]), "E_o": field_numpy(b["E_o"]),
                "x_fold": field_numpy(b["xf"]), "w_fold": field_numpy(b["wf"]),
-               "c0": int(field_numpy(b["c0"])[0]), "rounds": field_numpy(self.rounds),
-               "finals": field_numpy(self.finals), "claim0": int(field_numpy(self.claim0)[0])}
+               "c0": int(field_numpy(b["c0"])[0]), "rounds": field_numpy(b["rounds"]),
+               "finals": field_numpy(b["finals"]), "claim0": int(field_numpy(b["claim0"])[0])}
         if b["Z"] is not None:
             out["Z"] = b["Z"].cpu().numpy()
         return out
