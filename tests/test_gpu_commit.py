@@ -122,23 +122,15 @@ def test_commit_layer_outputs(fp):
     want_code = O.rs_encode(want_msg)
     assert np.array_equal(c, want_code)
     t = tree.cpu().numpy()
-    # sampled leaves, and every parent on the paths of sampled leaves
-    levels_off = [0]
-    w = W
-    while w > 1:
-        levels_off.append(levels_off[-1] + w)
-        w //= 2
-    for j in [0, 1, W // 2 + 3, W - 1, 1234567]:
-        assert bytes(t[j]) == O.merkle_leaf(want_code, salts, j)
-        idx = j
-        for d in range(len(levels_off) - 1):
-            par = idx // 2
-            left, right = bytes(t[levels_off[d] + 2 * par]), bytes(t[levels_off[d] + 2 * par + 1])
-            assert bytes(t[levels_off[d + 1] + par]) == O.blake2b(left + right), (j, d)
-            idx = par
-    # the top 12 levels entirely
-    for d in range(len(levels_off) - 13, len(levels_off) - 1):
-        n = W >> (d + 1)
-        for par in range(n):
-            left, right = bytes(t[levels_off[d] + 2 * par]), bytes(t[levels_off[d] + 2 * par + 1])
-            assert bytes(t[levels_off[d + 1] + par]) == O.blake2b(left + right)
+    # every leaf: the oracle's leaf message of each column (salt, then the column's elements as 8 little-endian
+    # bytes), hashed by the oracle's BLAKE2b-256, against the GPU's whole leaf level
+    assert bytes(t[1234567]) == O.merkle_leaf(want_code, salts, 1234567)
+    msgs = np.concatenate([salts.astype(np.uint8), np.ascontiguousarray(c.T).astype("<u8").view(np.uint8)], axis=1)
+    leaves = [O.blake2b(row.tobytes()) for row in msgs]
+    assert leaves == [bytes(x) for x in t[:W]]
+    # every level above, from the oracle's own leaves, against the GPU's whole tree
+    level, off = leaves, W
+    while len(level) > 1:
+        level = [O.blake2b(level[2 * i] + level[2 * i + 1]) for i in range(len(level) // 2)]
+        assert level == [bytes(x) for x in t[off:off + len(level)]], len(level)
+        off += len(level)
