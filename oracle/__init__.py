@@ -16,7 +16,11 @@ a salted BLAKE2b Merkle leaf) uses the C code for packing and encoding and the
 host's ``hashlib.blake2b`` for every hash. The lookup that shows the
 remainders are small (§3.1, §4: a grand-product argument with the key side as
 a binary tree, reduced level by level) is a product tree, a degree-3
-sum-check per level in C, and its verifier here.
+sum-check per level in C, and its verifier here. The layer proof with the
+rescale committed (§2 and §3.1: Q, R and Y committed, the matmul's claim read as
+2^s Q~ + R~ from folded rows of the commitment, columns opened against the root,
+challenges from the transcript over F_p[u]/(u^2 - 7)) is strung together here
+from those pieces, with a verifier that never forms the witness.
 """
 from __future__ import annotations
 
@@ -63,6 +67,8 @@ def lib():
             "or_eq_at": (u64, [vp, i32, i64]),
             "or_fold_rows": (None, [vp, i32, i64, i32, i32, vp, vp, i32]),
             "or_fold_cols": (None, [vp, i32, i64, i32, vp, i64, vp, vp]),
+            "or_fold_field_rows": (None, [vp, i64, i32, i32, vp, vp]),
+            "or_dot": (u64, [vp, vp, i64]),
             "or_mle_brute": (u64, [vp, i32, vp]),
             "or_mle_seq": (u64, [vp, i32, vp]),
             "or_mle_matrix": (u64, [vp, i32, i64, i32, i32, vp, i32, vp, i32]),
@@ -718,77 +724,374 @@ def e2_eval_deg2(g, x):
     return e2_add(e2_add(e2_mul(g[0], l0), e2_mul(g[1], l1)), e2_mul(g[2], l2))
 
 
-def prove_layer_fs(X: np.ndarray, W: np.ndarray, s: int, root: bytes) -> dict:
-    """The layer's matmul proof with Fiat-Shamir over the extension: the
-    transcript absorbs the layer's shape and the commitment root of Y and R,
-    yields r_t and r_o, absorbs the claim c0 = Z~(r_o || r_t), then runs the
-    sum-check of sum_k x'(k) w'(k) over d_in (padded to 2^n), and absorbs the
-    finals."""
-    T, d_in = X.shape
-    d_out = W.shape[0]
-    Z, Y, R = witness(X, W, s)
-    n_t, n_o, n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
-    tr = Transcript(layer_params(T, d_in, d_out, s))
-    tr.absorb(root)
-    ch = tr.challenges(n_t + n_o)
-    r_t, r_o = ch[:n_t], ch[n_t:]
-    Et, Eo = eq_table_e2(r_t), eq_table_e2(r_o)
-    xf = fold_rows_e2(X, Et[:T], 1 << n)
-    wf = fold_rows_e2(W, Eo[:d_out], 1 << n)
-    G = fold_rows_e2(np.ascontiguousarray(Z.T), Eo[:d_out], T)  # G[t] = sum_o Eo[o] Z[t, o]
-    c0 = (0, 0)
-    for t in range(T):
-        c0 = e2_add(c0, e2_mul(Et[t], G[t]))
-    tr.absorb(e2_words(c0))
-    rounds, rs, finals = sumcheck_e2(xf, wf, tr)
-    tr.absorb(e2_words(finals[0]) + e2_words(finals[1]))
-    return {"Z": Z, "Y": Y, "R": R, "r_t": r_t, "r_o": r_o, "c0": c0, "rounds": rounds, "r": rs,
-            "finals": finals, "state": tr.s, "x_fold": xf, "w_fold": wf}
-
-
-def verify_layer_fs(X: np.ndarray, W: np.ndarray, s: int, root: bytes, proof: dict):
-    """Replays the transcript from the root and the prover's messages, checks
-    every round sum and the finals against x~' and w~' at the point, and the
-    claim against Z = X W^T. Returns a reason from REASONS."""
-    T, d_in = X.shape
-    d_out = W.shape[0]
-    n_t, n_o, n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
-    tr = Transcript(layer_params(T, d_in, d_out, s))
-    tr.absorb(root)
-    ch = tr.challenges(n_t + n_o)
-    r_t, r_o = ch[:n_t], ch[n_t:]
-    Et, Eo = eq_table_e2(r_t), eq_table_e2(r_o)
-    Z = witness(X, W, s)[0]
-    G = fold_rows_e2(np.ascontiguousarray(Z.T), Eo[:d_out], T)
-    c0 = (0, 0)
-    for t in range(T):
-        c0 = e2_add(c0, e2_mul(Et[t], G[t]))
-    if tuple(proof["c0"]) != c0:
-        return "INITIAL_CLAIM"
-    tr.absorb(e2_words(c0))
-    claim, rs = c0, []
-    for g in proof["rounds"]:
-        g = [tuple(x) for x in g]
-        if e2_add(g[0], g[1]) != claim:
-            return "ROUND_SUM"
+def sumcheck_e2_multi(As: list, Bs: list, rho, tr: Transcript):
+    """Sum-check of sum_j rho_j sum_k A_j[k] B_j[k] over the extension with the
+    transcript (rho None: all ones): round i sends g_i(c) = sum_j rho_j
+    sum_q A_j,c[q] B_j,c[q] for c = 0, 1, 2, absorbs them, takes r_i as the
+    first challenge of the new state and binds every table; at the end the
+    finals (A_j(r), B_j(r)) of all pairs are absorbed as one message.
+    Returns (rounds, r, finals)."""
+    a = [list(x) for x in As]
+    b = [list(x) for x in Bs]
+    rho = [(1, 0)] * len(a) if rho is None else [tuple(x) for x in rho]
+    rounds, rs = [], []
+    while len(a[0]) > 1:
+        h = len(a[0]) // 2
+        g = [(0, 0)] * 3
+        for j in range(len(a)):
+            gj = [(0, 0)] * 3
+            for q in range(h):
+                da, db = e2_sub(a[j][2 * q + 1], a[j][2 * q]), e2_sub(b[j][2 * q + 1], b[j][2 * q])
+                ac, bc = a[j][2 * q], b[j][2 * q]
+                for c in range(3):
+                    gj[c] = e2_add(gj[c], e2_mul(ac, bc))
+                    ac, bc = e2_add(ac, da), e2_add(bc, db)
+            g = [e2_add(g[c], e2_mul(rho[j], gj[c])) for c in range(3)]
+        rounds.append(g)
         tr.absorb(b"".join(e2_words(x) for x in g))
         r = tr.challenges(1)[0]
         rs.append(r)
-        claim = e2_eval_deg2(g, r)
-    a, b = (tuple(x) for x in proof["finals"])
-    if e2_mul(a, b) != claim:
-        return "FINAL_CLAIM"
-    # the finals are the folded rows' extensions at the point
-    xf = fold_rows_e2(X, Et[:T], 1 << n)
-    wf = fold_rows_e2(W, Eo[:d_out], 1 << n)
-    Er = eq_table_e2(rs)
-    xa, wa = (0, 0), (0, 0)
-    for k in range(1 << n):
-        xa = e2_add(xa, e2_mul(Er[k], xf[k]))
-        wa = e2_add(wa, e2_mul(Er[k], wf[k]))
-    if (xa, wa) != (a, b):
-        return "FINAL_OPENING"
-    tr.absorb(e2_words(a) + e2_words(b))
-    if proof.get("state") is not None and proof["state"] != tr.s:
-        return "FINAL_OPENING"
+        for j in range(len(a)):
+            a[j] = [e2_add(a[j][2 * q], e2_mul(r, e2_sub(a[j][2 * q + 1], a[j][2 * q]))) for q in range(h)]
+            b[j] = [e2_add(b[j][2 * q], e2_mul(r, e2_sub(b[j][2 * q + 1], b[j][2 * q]))) for q in range(h)]
+    finals = [(a[j][0], b[j][0]) for j in range(len(a))]
+    tr.absorb(b"".join(e2_words(x) + e2_words(y) for x, y in finals))
+    return rounds, rs, finals
+
+
+# ------------------------------ layer proof with the rescale committed --
+# "How fast can FlashProve go", §2 (the prover commits intermediate values and
+# sum-check reduces each matmul to claims about the committed tables and the
+# weights, settled by openings; an opening sends a table's folded row, the
+# eq-weighted sum of its rows, and opens a few columns; every challenge hashes
+# all the prover has sent so far) and §3.1 (the rescaled value g_w and the
+# remainder r are committed, never g^ itself, and the matmul's sum-check uses
+# 2^k g_w + r in its place; the clamped value is committed too). Readings where
+# the pages are silent:
+#   - each map's Q (the rounded value before the clamp), R and Y are
+#     [2^n_t, 2^n_o] tables of field elements (v < 0 as p + v), zero padded and
+#     flattened with the output index in the low bits; rows hold 2^L elements,
+#     L = min(18, min over maps of n_t + n_o); the tables follow each other in
+#     the order Q_0, R_0, Y_0, Q_1, ..., each a run of whole rows; the rows are
+#     Reed-Solomon encoded and the columns Merkle hashed exactly as in the
+#     commitment above (one value per element here, no limb packing, so that a
+#     claim about a table is a claim about the committed rows);
+#   - the transcript starts from the label and the layer's shape (T, s, the
+#     number of maps M, the mode, L, the number of opened columns, then every
+#     map's d_in and d_out, as 32-bit little-endian words), absorbs the Merkle
+#     root, and yields r_t, each map's r_o and a point r_prox of
+#     log2ceil(rows) coordinates;
+#   - the prover sends 2M + 1 folded rows: the proximity row (row i weighted by
+#     eq(r_prox, i), every row of the commitment) and, per map, the rows of Q
+#     and of R weighted by eq(z_hi, .), where z = (r_o || r_t) splits into its
+#     first L coordinates z_lo and the rest z_hi; the transcript absorbs the
+#     Merkle root (zero salts) of these rows laid out as 2(2M + 1) base rows,
+#     each extension row as its 1 part then its u part;
+#   - the verifier reads Q~(z) = sum_c eq(z_lo, c) u_Q[c] and R~(z) from the
+#     rows, and the matmul's claim is c0 = 2^s Q~(z) + R~(z);
+#   - batched mode: rho (M challenges) and one sum-check of
+#     sum_m rho_m sum_k x'_m[k] w'_m[k] over 2^n, n the largest log2ceil(d_in),
+#     against sum_m rho_m c0_m; separate mode: each map's own sum-check over
+#     2^log2ceil(d_in) against c0_m, then rho and the combination
+#     C = sum_m rho_m x'_m(r_m) w'_m(r_m);
+#   - then 64 column indices, j = (challenge's first part) mod 2^(L+1); each
+#     is opened with its salt, its column of the code and its Merkle path; the
+#     verifier checks the path and that the codeword of every folded row at j
+#     equals the same weighted sum of the column's entries;
+#   - the finals x'_m(r) = X~(r || r_t) and w'_m(r) = W~(r || r_o) are claims
+#     about the layer's input and weights, whose commitments are outside this
+#     proof: the verifier evaluates them from X and W.
+LAYER_LABEL = b"zkp-layer-committed-rescale-v1"
+LAYER_LOG_ROW = 18
+LAYER_OPEN_COLUMNS = 64
+LAYER_REASONS = ("OK", "ROUND_SUM", "FINAL_CLAIM", "FINAL_OPENING", "COLUMN_PATH", "COLUMN_CODE", "STATE")
+
+
+class LayerLayout:
+    """Where each map's Q, R and Y rows sit in the commitment."""
+
+    def __init__(self, T: int, d_outs):
+        self.n_t = log2ceil(T)
+        self.n_o = [log2ceil(d) for d in d_outs]
+        self.L = min(LAYER_LOG_ROW, min(self.n_t + n for n in self.n_o))
+        self.base, self.table_rows = [], []
+        row = 0
+        for n in self.n_o:
+            k = 1 << (self.n_t + n - self.L)
+            self.base.append((row, row + k, row + 2 * k))
+            self.table_rows.append(k)
+            row += 3 * k
+        self.rows = row
+        self.n_prox = log2ceil(row)
+
+
+def layer_params_committed(T, s, maps_shape, batched, L, nq) -> bytes:
+    words = [T, s, len(maps_shape), int(bool(batched)), L, nq]
+    for d_in, d_out in maps_shape:
+        words += [d_in, d_out]
+    return b"".join(int(v).to_bytes(4, "little") for v in words)
+
+
+def field_embed(v: np.ndarray) -> np.ndarray:
+    """Signed integers as field elements (v < 0 as p + v)."""
+    v = np.asarray(v, np.int64)
+    w = v.astype(np.uint64)  # 2^64 + v for v < 0
+    return np.where(v < 0, w - np.uint64((1 << 32) - 1), w)
+
+
+def fold_field_rows(M: np.ndarray, E) -> np.ndarray:
+    """sum_i E[i] M[i, :] for a field-valued [rows, cols] matrix."""
+    M = np.ascontiguousarray(M, np.uint64)
+    rows, cols = M.shape
+    E = _u64(E)
+    assert len(E) >= rows
+    out = np.empty(cols, np.uint64)
+    lib().or_fold_field_rows(_p(M), cols, rows, cols, _p(E), _p(out))
+    return out
+
+
+def dot(a, b) -> int:
+    a, b = _u64(a), _u64(b)
+    assert len(a) == len(b)
+    return int(lib().or_dot(_p(a), _p(b), len(a)))
+
+
+def e2_dot(u, E) -> tuple:
+    """sum_c u[c] E[c] with u given as its parts (u0, u1) and E a list of e2."""
+    E0, E1 = e2_split(E)
+    a00, a11 = dot(u[0], E0), dot(u[1], E1)
+    a01, a10 = dot(u[0], E1), dot(u[1], E0)
+    return ((a00 + EXT_W * a11) % P, (a01 + a10) % P)
+
+
+def e2_fold_rows(M: np.ndarray, E) -> np.ndarray:
+    """Extension-weighted folded row of field rows: [2, cols] (1 part, u part)."""
+    E0, E1 = e2_split(E)
+    return np.stack([fold_field_rows(M, E0), fold_field_rows(M, E1)])
+
+
+def layer_tables(Z: np.ndarray, s: int, n_t: int, n_o: int):
+    """The committed Q, R, Y of one map: zero-padded [2^n_t, 2^n_o] field tables."""
+    T, d_out = Z.shape
+    out = []
+    for v in rescale(Z, s):
+        t = np.zeros((1 << n_t, 1 << n_o), np.int64)
+        t[:T, :d_out] = v
+        out.append(field_embed(t).reshape(-1))
+    return out  # Q, R, Y
+
+
+def _layer_points(lay: LayerLayout, ch):
+    r_t = ch[:lay.n_t]
+    off = lay.n_t
+    r_o = []
+    for n in lay.n_o:
+        r_o.append(ch[off:off + n])
+        off += n
+    return r_t, r_o, ch[off:off + lay.n_prox]
+
+
+def _row_weights(lay: LayerLayout, r_o, r_t, r_prox):
+    """Row weights of the 2M + 1 folded rows (lists of e2 per commitment row,
+    zeros outside a claim's table) and each claim's column point z_lo."""
+    prox = eq_table_e2(r_prox)[:lay.rows]
+    rows_w, z_lo = [prox], []
+    zero = (0, 0)
+    for m, n in enumerate(lay.n_o):
+        z = list(r_o[m]) + list(r_t)
+        z_lo.append(z[:lay.L])
+        Eh = eq_table_e2(z[lay.L:])
+        for which in (0, 1):  # Q, R
+            w = [zero] * lay.rows
+            b = lay.base[m][which]
+            w[b:b + lay.table_rows[m]] = Eh
+            rows_w.append(w)
+    return rows_w, z_lo
+
+
+def _merkle_root_rows(U: np.ndarray) -> bytes:
+    """Merkle root (zero salts) over the columns of the folded rows U [K, 2, 2^L]."""
+    K, _, n = U.shape
+    return merkle_tree(U.reshape(2 * K, n), np.zeros((n, 16), np.uint8))[-1][0]
+
+
+def prove_layer_committed(maps, s: int, batched: bool, salts: np.ndarray, tamper: str | None = None) -> dict:
+    """The layer's proof with the rescale committed (steps and readings above).
+    maps: list of (X, W), every X with the same T rows. tamper names a
+    deliberate mistake of a cheating prover, for the verifier's negative
+    controls: "Q" commits Q + 1 at one entry and proves honestly otherwise;
+    "Q_rows" commits that Q but folds the true one; "prox_row" sends a wrong
+    proximity row and proves consistently with it; "column" sends a wrong
+    entry in the first opened column."""
+    T = maps[0][0].shape[0]
+    shapes = [(X.shape[1], W.shape[0]) for X, W in maps]
+    lay = LayerLayout(T, [d for _, d in shapes])
+    n_cols = 1 << lay.L
+    msg = np.zeros((lay.rows, n_cols), np.uint64)
+    true_msg = None
+    out = {"layout": lay, "Z": [], "tables": []}
+    for m, (X, W) in enumerate(maps):
+        Z = witness(X, W, s)[0]
+        Q, R, Y = layer_tables(Z, s, lay.n_t, lay.n_o[m])
+        out["Z"].append(Z)
+        out["tables"].append((Q, R, Y))
+        for which, tab in enumerate((Q, R, Y)):
+            b = lay.base[m][which]
+            msg[b:b + lay.table_rows[m]] = tab.reshape(-1, n_cols)
+    if tamper in ("Q", "Q_rows"):
+        true_msg = msg.copy()
+        msg[lay.base[0][0], 0] = (int(msg[lay.base[0][0], 0]) + 1) % P
+    code = rs_encode(msg)
+    assert salts.shape == (2 * n_cols, 16)
+    levels = merkle_tree(code, salts)
+    root = levels[-1][0]
+    nq = LAYER_OPEN_COLUMNS
+    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq))
+    tr.absorb(root)
+    ch = tr.challenges(lay.n_t + sum(lay.n_o) + lay.n_prox)
+    r_t, r_o, r_prox = _layer_points(lay, ch)
+    rows_w, z_lo = _row_weights(lay, r_o, r_t, r_prox)
+    fold_src = true_msg if tamper == "Q_rows" else msg
+    U = np.stack([e2_fold_rows(fold_src, w) for w in rows_w])  # [2M+1, 2, 2^L]
+    if tamper == "prox_row":
+        U[0, 0, 0] = (int(U[0, 0, 0]) + 1) % P
+    tr.absorb(_merkle_root_rows(U))
+    Et = eq_table_e2(r_t)
+    xf, wf, c0 = [], [], []
+    n_all = max(log2ceil(d) for d, _ in shapes)
+    for m, (X, W) in enumerate(maps):
+        n = n_all if batched else log2ceil(shapes[m][0])
+        xf.append(fold_rows_e2(X, Et[:T], 1 << n))
+        wf.append(fold_rows_e2(W, eq_table_e2(r_o[m])[:shapes[m][1]], 1 << n))
+        Ez = eq_table_e2(z_lo[m])
+        q, e = e2_dot(U[1 + 2 * m], Ez), e2_dot(U[2 + 2 * m], Ez)
+        c0.append(e2_add(e2_mul((1 << s, 0), q), e))
+    sumchecks = []
+    if batched:
+        rho = tr.challenges(len(maps))
+        rounds, rs, finals = sumcheck_e2_multi(xf, wf, rho, tr)
+        sumchecks.append({"rounds": rounds, "r": rs, "finals": finals})
+        C = None
+    else:
+        for m in range(len(maps)):
+            rounds, rs, finals = sumcheck_e2_multi([xf[m]], [wf[m]], None, tr)
+            sumchecks.append({"rounds": rounds, "r": rs, "finals": finals})
+        rho = tr.challenges(len(maps))
+        C = (0, 0)
+        for m, sc in enumerate(sumchecks):
+            a, b = sc["finals"][0]
+            C = e2_add(C, e2_mul(rho[m], e2_mul(a, b)))
+    state = tr.s
+    idx = [int(c[0]) % (2 * n_cols) for c in tr.challenges(nq)]
+    columns = np.stack([code[:, j] for j in idx])
+    if tamper == "column":
+        columns[0, 0] = (int(columns[0, 0]) + 1) % P
+    out.update(root=root, U=U, c0=c0, rho=rho, C=C, sumchecks=sumchecks, state=state, idx=idx, columns=columns,
+               col_salts=np.stack([salts[j] for j in idx]), paths=[merkle_path(levels, j) for j in idx],
+               r_t=r_t, r_o=r_o, r_prox=r_prox, x_fold=xf, w_fold=wf, msg=msg, code=code)
+    return out
+
+
+def verify_layer_committed(maps, s: int, batched: bool, proof: dict) -> str:
+    """Checks a proof from prove_layer_committed without the witness: replays
+    the transcript, reads the claims from the folded rows, checks every
+    sum-check, the finals against X~ and W~ at the point, and every opened
+    column against the root and the folded rows. Returns a name from
+    LAYER_REASONS."""
+    T = maps[0][0].shape[0]
+    shapes = [(X.shape[1], W.shape[0]) for X, W in maps]
+    lay = LayerLayout(T, [d for _, d in shapes])
+    n_cols = 1 << lay.L
+    nq = LAYER_OPEN_COLUMNS
+    U = np.asarray(proof["U"], np.uint64)
+    assert U.shape == (1 + 2 * len(maps), 2, n_cols)
+    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq))
+    tr.absorb(proof["root"])
+    ch = tr.challenges(lay.n_t + sum(lay.n_o) + lay.n_prox)
+    r_t, r_o, r_prox = _layer_points(lay, ch)
+    rows_w, z_lo = _row_weights(lay, r_o, r_t, r_prox)
+    tr.absorb(_merkle_root_rows(U))
+    c0 = []
+    for m in range(len(maps)):
+        Ez = eq_table_e2(z_lo[m])
+        q, e = e2_dot(U[1 + 2 * m], Ez), e2_dot(U[2 + 2 * m], Ez)
+        c0.append(e2_add(e2_mul((1 << s, 0), q), e))
+
+    def run(claim, sc, n_pairs, rho, n):
+        rs = []
+        if len(sc["rounds"]) != n:
+            return "ROUND_SUM", None
+        for g in sc["rounds"]:
+            g = [tuple(int(v) for v in x) for x in g]
+            if e2_add(g[0], g[1]) != claim:
+                return "ROUND_SUM", None
+            tr.absorb(b"".join(e2_words(x) for x in g))
+            r = tr.challenges(1)[0]
+            rs.append(r)
+            claim = e2_eval_deg2(g, r)
+        fin = [(tuple(int(v) for v in a), tuple(int(v) for v in b)) for a, b in sc["finals"]]
+        if len(fin) != n_pairs:
+            return "FINAL_CLAIM", None
+        tot = (0, 0)
+        for j, (a, b) in enumerate(fin):
+            tot = e2_add(tot, e2_mul(rho[j] if rho else (1, 0), e2_mul(a, b)))
+        if tot != claim:
+            return "FINAL_CLAIM", None
+        tr.absorb(b"".join(e2_words(a) + e2_words(b) for a, b in fin))
+        return None, (rs, fin)
+
+    Et = eq_table_e2(r_t)
+    n_all = max(log2ceil(d) for d, _ in shapes)
+
+    def opening(m, rs, a, b, n):
+        X, W = maps[m]
+        if len(rs) != n:
+            return False
+        Er = eq_table_e2(rs)
+        xa = e2_dot(np.stack(e2_split(fold_rows_e2(X, Et[:T], 1 << n))), Er)
+        wa = e2_dot(np.stack(e2_split(fold_rows_e2(W, eq_table_e2(r_o[m])[:shapes[m][1]], 1 << n))), Er)
+        return (xa, wa) == (a, b)
+
+    scs = proof["sumchecks"]
+    if batched:
+        rho = tr.challenges(len(maps))
+        claim = (0, 0)
+        for m in range(len(maps)):
+            claim = e2_add(claim, e2_mul(rho[m], c0[m]))
+        if len(scs) != 1:
+            return "ROUND_SUM"
+        why, res = run(claim, scs[0], len(maps), rho, n_all)
+        if why:
+            return why
+        rs, fin = res
+        for m in range(len(maps)):
+            if not opening(m, rs, fin[m][0], fin[m][1], n_all):
+                return "FINAL_OPENING"
+    else:
+        if len(scs) != len(maps):
+            return "ROUND_SUM"
+        for m in range(len(maps)):
+            why, res = run(c0[m], scs[m], 1, None, log2ceil(shapes[m][0]))
+            if why:
+                return why
+            rs, fin = res
+            if not opening(m, rs, fin[0][0], fin[0][1], log2ceil(shapes[m][0])):
+                return "FINAL_OPENING"
+        tr.challenges(len(maps))  # rho: drawn from the state, nothing absorbed
+    if proof.get("state") is not None and bytes(proof["state"]) != tr.s:
+        return "STATE"
+    idx = [int(c[0]) % (2 * n_cols) for c in tr.challenges(nq)]
+    columns = np.asarray(proof["columns"], np.uint64)
+    if columns.shape != (nq, lay.rows):
+        return "COLUMN_PATH"
+    for q, j in enumerate(idx):
+        leaf = blake2b(bytes(np.asarray(proof["col_salts"][q], np.uint8)) + columns[q].astype("<u8").tobytes())
+        if not merkle_verify(proof["root"], leaf, j, proof["paths"][q]):
+            return "COLUMN_PATH"
+        for k, w in enumerate(rows_w):
+            got = (rs_eval(U[k, 0], j), rs_eval(U[k, 1], j))
+            W0, W1 = e2_split(w)
+            want = (dot(W0, columns[q]), dot(W1, columns[q]))
+            if got != want:
+                return "COLUMN_CODE"
     return "OK"

@@ -152,6 +152,25 @@ void or_fold_rows(const void* M, int32_t elem_bytes, int64_t ld, int32_t rows, i
   for (int32_t k = cols; k < cols_pad; ++k) out[k] = 0;
 }
 
+/* [HF §2] The folded row of a table whose entries are field elements
+ * (committed tables): out[c] = sum_{i < rows} E[i] * M[i, c], c < cols. */
+void or_fold_field_rows(const uint64_t* M, int64_t ld, int32_t rows, int32_t cols, const uint64_t* E,
+                        uint64_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int32_t c = 0; c < cols; ++c) {
+    uint64_t acc = 0;
+    for (int32_t i = 0; i < rows; ++i) acc = or_add(acc, or_mul(E[i], M[(int64_t)i * ld + c] % OR_P));
+    out[c] = acc;
+  }
+}
+
+/* sum_{i < n} a[i] b[i] (an inner product of field vectors). */
+uint64_t or_dot(const uint64_t* a, const uint64_t* b, int64_t n) {
+  uint64_t acc = 0;
+  for (int64_t i = 0; i < n; ++i) acc = or_add(acc, or_mul(a[i] % OR_P, b[i] % OR_P));
+  return acc;
+}
+
 /* Selected columns of the folded row (for sampled checks at full size). */
 void or_fold_cols(const void* M, int32_t elem_bytes, int64_t ld, int32_t rows, const uint64_t* E,
                   int64_t n, const int32_t* ks, uint64_t* out) {

@@ -668,22 +668,141 @@ def test_sumcheck_e2_against_hypercube_enumeration():
     assert finals == (_mle_e2(A, rs), _mle_e2(B, rs))
 
 
-def test_layer_fs_proof_and_negative_controls():
-    cfg = synth.config(1)
-    inp = synth.make_inputs(cfg)
-    X, W = inp["X"], inp["W"]
-    root = O.blake2b(b"commitment of Y and R")
-    pr = O.prove_layer_fs(X, W, cfg.s, root)
-    assert O.verify_layer_fs(X, W, cfg.s, root, pr) == "OK"
-    # a different commitment changes the challenges, so the claim no longer matches
-    assert O.verify_layer_fs(X, W, cfg.s, O.blake2b(b"other"), pr) == "INITIAL_CLAIM"
-    bad = dict(pr, rounds=[list(g) for g in pr["rounds"]])
-    bad["rounds"][2][1] = O.e2_add(bad["rounds"][2][1], (1, 0))
-    assert O.verify_layer_fs(X, W, cfg.s, root, bad) == "ROUND_SUM"
-    bad = dict(pr, finals=(O.e2_add(pr["finals"][0], (0, 1)), pr["finals"][1]))
-    assert O.verify_layer_fs(X, W, cfg.s, root, bad) == "FINAL_CLAIM"
-    W2 = W.copy()
+def test_sumcheck_e2_multi_one_pair_and_rho_weights():
+    rng = random.Random(43)
+    n = 3
+    rnd = lambda: [(rng.randrange(P), rng.randrange(P)) for _ in range(1 << n)]
+    A, B = rnd(), rnd()
+    # one pair without weights: sumcheck_e2's rounds, then the finals absorbed
+    t1, t2 = O.Transcript(b"x"), O.Transcript(b"x")
+    r1, s1, f1 = O.sumcheck_e2(A, B, t1)
+    t1.absorb(O.e2_words(f1[0]) + O.e2_words(f1[1]))
+    r2, s2, f2 = O.sumcheck_e2_multi([A], [B], None, t2)
+    assert (r1, s1, [f1]) == (r2, s2, f2) and t1.s == t2.s
+    # three pairs: every round is the rho combination of the pairs' own round
+    # values at the shared challenges (by enumeration), the finals the MLEs at r
+    As, Bs = [rnd() for _ in range(3)], [rnd() for _ in range(3)]
+    rho = [(rng.randrange(P), rng.randrange(P)) for _ in range(3)]
+    rounds, rs, finals = O.sumcheck_e2_multi(As, Bs, rho, O.Transcript(b"y"))
+    for i in range(n):
+        for c in range(3):
+            tot = (0, 0)
+            for j in range(3):
+                for bits in itertools.product((0, 1), repeat=n - i - 1):
+                    pt = list(rs[:i]) + [(c, 0)] + [(x, 0) for x in bits]
+                    tot = O.e2_add(tot, O.e2_mul(rho[j], O.e2_mul(_mle_e2(As[j], pt), _mle_e2(Bs[j], pt))))
+            assert rounds[i][c] == tot
+    assert finals == [(_mle_e2(As[j], rs), _mle_e2(Bs[j], rs)) for j in range(3)]
+
+
+def test_field_embed_and_field_fold():
+    v = np.array([0, 1, -1, 127, -128, (1 << 31) - 1, -(1 << 31)], np.int64)
+    assert [int(x) for x in O.field_embed(v)] == [int(x) % P for x in v]
+    rng = np.random.default_rng(44)
+    M = rng.integers(0, P, size=(5, 7), dtype=np.uint64)
+    E = [int(x) for x in rng.integers(0, P, size=5, dtype=np.uint64)]
+    got = O.fold_field_rows(M, E)
+    assert [int(x) for x in got] == [sum(E[i] * int(M[i, c]) for i in range(5)) % P for c in range(7)]
+    assert O.dot(M[0], M[1]) == sum(int(a) * int(b) for a, b in zip(M[0], M[1])) % P
+
+
+def test_layer_layout_of_the_seven_map_layer():
+    # T = 4096; outputs of Q, K, V, O, gate, up, down (14336 pads to 2^14)
+    lay = O.LayerLayout(4096, [4096, 1024, 1024, 4096, 14336, 14336, 4096])
+    assert lay.L == 18 and lay.n_t == 12
+    assert lay.table_rows == [64, 16, 16, 64, 256, 256, 64]
+    assert lay.rows == 3 * 736 and lay.n_prox == 12
+    assert lay.base[1] == (192, 208, 224) and lay.base[6][2] == lay.rows - 64
+    # a small layer: rows as short as the smallest table
+    lay = O.LayerLayout(24, [48, 20, 40])
+    assert (lay.L, lay.rows) == (5 + 5, 3 * (2 + 1 + 2)) and lay.base[1] == (6, 7, 8)
+
+
+def _small_layer(seed=45):
+    rng = np.random.default_rng(seed)
+    r8 = lambda *sh: rng.integers(-127, 128, size=sh).astype(np.int8)
+    T = 24
+    X, H = r8(T, 40), r8(T, 72)
+    maps = [(X, r8(48, 40)), (X, r8(20, 40)), (H, r8(40, 72))]
+    lay = O.LayerLayout(T, [48, 20, 40])
+    salts = rng.integers(0, 256, size=(2 << lay.L, 16), dtype=np.uint8)
+    return maps, salts
+
+
+@pytest.mark.parametrize("batched", [True, False])
+def test_layer_committed_claims_by_enumeration(batched):
+    """The claims read from the folded rows are the witness's MLE at (r_o || r_t)
+    (summed over every (t, o) with extension eq weights, independently of the
+    layout), and each folded row is the weighted sum of its rows."""
+    maps, salts = _small_layer()
+    s = 7
+    pr = O.prove_layer_committed(maps, s, batched, salts)
+    lay = pr["layout"]
+    for m, (X, W) in enumerate(maps):
+        Z = X.astype(np.int64) @ W.astype(np.int64).T
+        Et, Eo = O.eq_table_e2(pr["r_t"]), O.eq_table_e2(pr["r_o"][m])
+        want = (0, 0)
+        for t in range(Z.shape[0]):
+            for o in range(Z.shape[1]):
+                want = O.e2_add(want, O.e2_mul(O.e2_mul(Et[t], Eo[o]), (int(Z[t, o]) % P, 0)))
+        assert pr["c0"][m] == want
+        # the Q table is the rounded value before the clamp, element by element
+        Q = pr["tables"][m][0].reshape(1 << lay.n_t, 1 << lay.n_o[m])
+        q_int = np.floor_divide(Z + (1 << (s - 1)), 1 << s)
+        assert all(int(Q[t, o]) == int(q_int[t, o]) % P for t in range(Z.shape[0]) for o in range(Z.shape[1]))
+        assert not Q[Z.shape[0]:].any() and not Q[:, Z.shape[1]:].any()
+    # the R row of map 2: its weights put eq(z_hi, i) on the table's rows only
+    z = list(pr["r_o"][2]) + list(pr["r_t"])
+    Eh = O.eq_table_e2(z[lay.L:])
+    b = lay.base[2][1]
+    for c in (0, 5, (1 << lay.L) - 1):
+        acc = (0, 0)
+        for i in range(lay.table_rows[2]):
+            acc = O.e2_add(acc, O.e2_mul(Eh[i], (int(pr["msg"][b + i, c]), 0)))
+        assert acc == (int(pr["U"][2 + 2 * 2][0][c]), int(pr["U"][2 + 2 * 2][1][c]))
+
+
+@pytest.mark.parametrize("batched", [True, False])
+def test_layer_committed_proof_and_negative_controls(batched):
+    maps, salts = _small_layer()
+    s = 7
+    pr = O.prove_layer_committed(maps, s, batched, salts)
+    V = lambda proof, mp=maps: O.verify_layer_committed(mp, s, batched, proof)
+    assert V(pr) == "OK"
+    assert len(pr["sumchecks"]) == (1 if batched else 3) and len(pr["idx"]) == O.LAYER_OPEN_COLUMNS
+    # the challenges live in the extension, not in F_p
+    assert any(r[1] != 0 for sc in pr["sumchecks"] for r in sc["r"])
+    # a committed Q off by one at one entry: the claim 2^s Q~ + R~ is no longer Z~
+    assert V(O.prove_layer_committed(maps, s, batched, salts, tamper="Q")) == "ROUND_SUM"
+    # the same commitment with the true Q's folded rows: the columns disagree
+    assert V(O.prove_layer_committed(maps, s, batched, salts, tamper="Q_rows")) == "COLUMN_CODE"
+    assert V(O.prove_layer_committed(maps, s, batched, salts, tamper="prox_row")) == "COLUMN_CODE"
+    assert V(O.prove_layer_committed(maps, s, batched, salts, tamper="column")) == "COLUMN_PATH"
+    # a message changed after the fact
+    bad = dict(pr, sumchecks=[dict(sc, rounds=[list(g) for g in sc["rounds"]]) for sc in pr["sumchecks"]])
+    g = bad["sumchecks"][-1]["rounds"][1]
+    g[2] = O.e2_add(g[2], (1, 0))
+    assert V(bad) == "ROUND_SUM"
+    bad = dict(pr, sumchecks=[dict(sc, finals=list(sc["finals"])) for sc in pr["sumchecks"]])
+    a, b = bad["sumchecks"][0]["finals"][0]
+    bad["sumchecks"][0]["finals"][0] = (O.e2_add(a, (0, 1)), b)
+    assert V(bad) == "FINAL_CLAIM"
+    bad = dict(pr, root=O.blake2b(b"other"))
+    assert V(bad) == "ROUND_SUM"
+    bad = dict(pr, state=O.blake2b(b"other"))
+    assert V(bad) == "STATE"
+    # other weights than the proof's: the finals are not W~ at the point
+    W2 = maps[1][1].copy()
     W2[3, 7] ^= 1
-    assert O.verify_layer_fs(X, W2, cfg.s, root, pr) == "INITIAL_CLAIM"
-    # the finals are extension elements, not base ones: the challenges left F_p
-    assert any(r[1] != 0 for r in pr["r"]) and any(x[1] != 0 for x in pr["finals"])
+    assert V(pr, [maps[0], (maps[1][0], W2), maps[2]]) == "FINAL_OPENING"
+
+
+def test_layer_committed_single_map_and_tiny_rows():
+    rng = np.random.default_rng(46)
+    X = rng.integers(-127, 128, size=(2, 3)).astype(np.int8)
+    W = rng.integers(-127, 128, size=(3, 3)).astype(np.int8)
+    lay = O.LayerLayout(2, [3])
+    assert (lay.L, lay.rows) == (3, 3)
+    salts = rng.integers(0, 256, size=(2 << lay.L, 16), dtype=np.uint8)
+    pr = O.prove_layer_committed([(X, W)], 1, False, salts)
+    assert O.verify_layer_committed([(X, W)], 1, False, pr) == "OK"
