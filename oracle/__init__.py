@@ -648,8 +648,8 @@ def e2_words(x) -> bytes:
 
 
 class Transcript:
-    def __init__(self, params: bytes):
-        self.s = blake2b(FS_LABEL + params)
+    def __init__(self, params: bytes, label: bytes = FS_LABEL):
+        self.s = blake2b(label + params)
 
     def absorb(self, msg: bytes):
         self.s = blake2b(self.s + msg)
@@ -946,7 +946,7 @@ def prove_layer_committed(maps, s: int, batched: bool, salts: np.ndarray, tamper
     levels = merkle_tree(code, salts)
     root = levels[-1][0]
     nq = LAYER_OPEN_COLUMNS
-    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq))
+    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq), LAYER_LABEL)
     tr.absorb(root)
     ch = tr.challenges(lay.n_t + sum(lay.n_o) + lay.n_prox)
     r_t, r_o, r_prox = _layer_points(lay, ch)
@@ -1005,7 +1005,7 @@ def verify_layer_committed(maps, s: int, batched: bool, proof: dict) -> str:
     nq = LAYER_OPEN_COLUMNS
     U = np.asarray(proof["U"], np.uint64)
     assert U.shape == (1 + 2 * len(maps), 2, n_cols)
-    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq))
+    tr = Transcript(layer_params_committed(T, s, shapes, batched, lay.L, nq), LAYER_LABEL)
     tr.absorb(proof["root"])
     ch = tr.challenges(lay.n_t + sum(lay.n_o) + lay.n_prox)
     r_t, r_o, r_prox = _layer_points(lay, ch)

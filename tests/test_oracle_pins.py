@@ -634,6 +634,8 @@ def test_transcript_derivation_and_sensitivity():
     assert ch[0] == (w[0] % P, w[1] % P) and ch[1] == (w[2] % P, w[3] % P)
     d1 = h(s1 + (1).to_bytes(4, "little"))
     assert ch[2] == (int.from_bytes(d1[:8], "little") % P, int.from_bytes(d1[8:16], "little") % P)
+    # another label starts another transcript
+    assert O.Transcript(b"params", O.LAYER_LABEL).s == h(O.LAYER_LABEL + b"params") != s0
     # any change to an absorbed byte changes every later challenge
     tr2 = O.Transcript(b"params")
     tr2.absorb(b"rooT")
