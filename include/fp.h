@@ -291,6 +291,65 @@ size_t fp_rs_encode_workspace(int32_t rows, int32_t logn);
 int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t log_width, const uint8_t* salts,
                      uint8_t* tree, hipStream_t stream);
 
+/* Committed tables of a layer whose rescale is committed ("How fast can
+ * FlashProve go", §3.1: the rescaled value g_w = round(g^ / 2^k) and the
+ * remainder r = g^ - 2^k g_w are committed, never g^, and the clamped value
+ * is committed too). For each of the count maps (at most FP_MAX_MULTI), with
+ * Z int32 [T, ldz] its witness: Q = floor((Z + 2^(s-1)) / 2^s) (before the
+ * clamp), R = Z - 2^s Q and Y = clamp(Q, -128, 127), each as a zero-padded
+ * [2^n_t, 2^n_o] table of field elements (v < 0 as p + v) flattened with the
+ * output index in the low bits, written into rows row_q, row_r, row_y
+ * onwards of msg [rows, ld], 2^log_cols elements per row (entry i of a table
+ * at row i >> log_cols, column i mod 2^log_cols); each table takes
+ * 2^(n_t + n_o - log_cols) whole rows. Needs T <= 2^n_t, d_out <= 2^n_o,
+ * n_t + n_o >= log_cols, s in [1, 8]. Errors: FP_EARG, FP_ESHAPE, FP_ERANGE. */
+typedef struct {
+  const int32_t* Z;
+  int64_t ldz;
+  int32_t T, d_out, n_o;
+  int32_t row_q, row_r, row_y;
+} fp_table_desc;
+int fp_commit_tables(int32_t count, const fp_table_desc* d, int32_t n_t, int32_t s, int32_t log_cols, fp_elem* msg,
+                     int64_t ld, int32_t rows, hipStream_t stream);
+
+/* Folded rows of a committed message matrix over the extension, for
+ * openings ("How fast can FlashProve go", §2: an opening sends the folded
+ * row, the eq-weighted sum of the table's rows, and opens a few columns; §4
+ * footnote 20: over the extension). msg [rows, ld] holds 2^log_cols field
+ * elements per row. U [(1 + n_claims)][2][2^log_cols] receives, as 1 and u
+ * parts: row 0, the proximity row sum_{i < rows} eq(r_prox, i) msg[i] (r_prox:
+ * device [n_prox][2], 2^n_prox >= rows); row 1 + k, claim k's row
+ * sum_{i < nrows} eq(z, i) msg[row0 + i], z the n1 coordinates at z1 followed
+ * by the n2 at z2 (device [.][2] each), nrows = 2^(n1 + n2). Claims are sorted
+ * by row0 and disjoint, at most FP_MAX_OPEN_CLAIMS. ws:
+ * fp_commit_fold_ext_workspace(rows) bytes, 256-byte aligned (row weights).
+ * Errors: FP_EARG, FP_ESHAPE, FP_EWORKSPACE. */
+#define FP_MAX_OPEN_CLAIMS 16
+typedef struct {
+  int32_t row0, nrows;
+  const fp_elem* z1;
+  int32_t n1;
+  const fp_elem* z2;
+  int32_t n2;
+} fp_open_claim;
+int fp_commit_fold_ext(const fp_elem* msg, int64_t ld, int32_t rows, int32_t log_cols, const fp_elem* r_prox,
+                       int32_t n_prox, int32_t n_claims, const fp_open_claim* claims, fp_elem* U, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+size_t fp_commit_fold_ext_workspace(int32_t rows);
+
+/* Openings of nq columns of a committed code [rows, ld_code] with its salts
+ * and tree from fp_merkle_commit (2^log_width columns) ("How fast can
+ * FlashProve go", §2: an opening opens a few columns; each is checked
+ * against the Merkle root): column q is j = chal[2q] mod 2^log_width (chal:
+ * device challenges, 2 words each, the first used). Writes cols [nq][rows] =
+ * code[.][j], col_salts [nq][16 bytes] = salt_j, paths [nq][log_width][32
+ * bytes] = the siblings of j's nodes from the leaf level up (the root
+ * excluded) and idx [nq] = j (idx may be NULL). salts, tree, col_salts, paths
+ * 8-byte aligned. Errors: FP_EARG, FP_ESHAPE. */
+int fp_merkle_open(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t log_width, const uint8_t* salts,
+                   const uint8_t* tree, const fp_elem* chal, int32_t nq, fp_elem* cols, uint8_t* col_salts,
+                   uint8_t* paths, int32_t* idx, hipStream_t stream);
+
 /* -------------------------------------------------------------- lookup --- */
 /* The lookup that shows the remainders R are small ("How fast can FlashProve
  * go", §3.1: the remainders of each rescale are range-checked by a lookup;
@@ -373,6 +432,25 @@ int fp_ext_claim_combine(const fp_elem* c4, fp_elem* c0, hipStream_t stream);
  * workgroup. */
 int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp_elem* B0, const fp_elem* B1, int32_t n,
                        uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals, hipStream_t stream);
+
+/* The same for sum_j rho_j sum_{k < 2^n} A_j(k) B_j(k) over 1..8 pairs
+ * ("How fast can FlashProve go", §2: the maps of a layer share one sum-check
+ * when their claims are batched; §4 footnote 20: over the extension). A0, A1,
+ * B0, B1 are HOST arrays of n_pairs device pointers (each table 2^n canonical
+ * elements as its 1 and u parts); rho: device [n_pairs][2] or NULL (all ones);
+ * n <= 24. Round i writes rounds[6i .. 6i+5] = g_i(0), g_i(1), g_i(2) with
+ *   g_i(c) = sum_j rho_j sum_q A_j,c[q] B_j,c[q],  A_c[q] = A[2q] + c (A[2q+1] - A[2q]),
+ * absorbs those 6 words, takes r_i = challenge 0 of the new state (r[2i],
+ * r[2i+1]) and only then binds every table. At the end finals[4j .. 4j+3] =
+ * A_j(r), B_j(r) for every pair, absorbed as one message of 4 n_pairs words.
+ * One workgroup streams the tables through ws
+ * (fp_sumcheck_ext_fs_multi_workspace(n_pairs, n) bytes, 256-byte aligned;
+ * none for n = 0). Errors: FP_EARG, FP_ESHAPE (n), FP_EWORKSPACE. */
+int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A0, const fp_elem* const* A1,
+                             const fp_elem* const* B0, const fp_elem* const* B1, const fp_elem* rho, int32_t n,
+                             uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+size_t fp_sumcheck_ext_fs_multi_workspace(int32_t n_pairs, int32_t n);
 
 /* ----------------------------------------------------------------- MLE --- */
 /* out[0] = M~(r_cols || r_rows) for an int8/int32 matrix [rows, cols] (leading

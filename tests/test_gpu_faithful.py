@@ -1,15 +1,17 @@
 """GPU parity of the soundness-faithful proof: the BLAKE2b transcript on the
-device, eq tables and the sum-check over F_p[u]/(u^2 - 7), and whole layer
-proofs with Fiat-Shamir challenges drawn from the commitment of Y and R,
-against the oracle (which computes its own witness, commitment root and
-transcript) and accepted by its verifier."""
+device, eq tables and the sum-checks over F_p[u]/(u^2 - 7) (one pair in
+registers, up to eight streamed), the committed tables, folded rows and opened
+columns, and whole layer proofs with the rescale committed (Q, R and Y) and
+every challenge from the transcript, against the oracle's prover (which
+computes its own witness, commitment and transcript) and accepted by its
+verifier, which forms no witness."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import synth
-from zero_knowledge_proof_amd.prover import FaithfulLayerProver, commit_logn
+from zero_knowledge_proof_amd.prover import FaithfulProver
 
 pytestmark = pytest.mark.gpu
 P = O.P
@@ -77,42 +79,167 @@ def test_sumcheck_ext_fs(fp, n):
     assert bytes(st.cpu().numpy().view(np.uint8)) == tr.s
 
 
-def _oracle_root(X, W, s, salts):
-    Z, Y, R = O.witness(X, W, s)
-    logn = commit_logn(2 * Y.size)
-    code = O.rs_encode(O.pack_limbs(Y, R, logn))
-    return O.merkle_tree(code, salts)[-1][0], logn
+@pytest.mark.parametrize("np_,n,with_rho", [(1, 0, False), (1, 3, False), (3, 1, True), (3, 9, True), (7, 6, True),
+                                            (8, 5, False), (2, 13, True), (7, 14, True)])
+def test_sumcheck_ext_fs_multi(fp, np_, n, with_rho):
+    rng = np.random.default_rng(200 + 10 * np_ + n)
+    As = [_rand_e2(rng, 1 << n) for _ in range(np_)]
+    Bs = [_rand_e2(rng, 1 << n) for _ in range(np_)]
+    As[0][0] = (P - 1, P - 1)
+    rho = _rand_e2(rng, np_) if with_rho else None
+    st = _state(fp, b"scm%d" % n)
+    tr = O.Transcript(b"scm%d" % n)
+    part = lambda V, k: _f([v[k] for v in V])
+    rho_t = _f([x for p in rho for x in p]).reshape(np_, 2) if rho else None
+    rounds, r, finals = fp.sumcheck_ext_fs_multi([part(A, 0) for A in As], [part(A, 1) for A in As],
+                                                 [part(B, 0) for B in Bs], [part(B, 1) for B in Bs], st, rho=rho_t)
+    torch.cuda.synchronize()
+    want_rounds, want_r, want_f = O.sumcheck_e2_multi(As, Bs, rho, tr)
+    assert [_pairs(rounds[i]) for i in range(n)] == [list(g) for g in want_rounds]
+    assert _pairs(r) == want_r
+    got_f = _pairs(finals)
+    assert [(got_f[2 * j], got_f[2 * j + 1]) for j in range(np_)] == want_f
+    assert bytes(st.cpu().numpy().view(np.uint8)) == tr.s
+
+
+def _u64(t):
+    return t.detach().cpu().numpy().view(np.uint64)
+
+
+def test_commit_tables_and_folded_rows(fp):
+    """Each map's Q, R, Y rows from its Z, and the folded rows over the extension, against the oracle's tables
+    and folds (rows of 2^4: the tables of the 20-wide map take whole rows)."""
+    rng = np.random.default_rng(300)
+    T, s = 6, 5
+    d_outs = [20, 3, 32]
+    Zs = [rng.integers(-(1 << 20), 1 << 20, size=(T, d)).astype(np.int32) for d in d_outs]
+    Zs[0][0, :4] = [(1 << 31) - 1, -(1 << 31), 2 ** (s - 1), -(2 ** (s - 1)) - 1]
+    n_t = O.log2ceil(T)
+    n_o = [O.log2ceil(d) for d in d_outs]
+    L = 4
+    rows, base = 0, []
+    for n in n_o:
+        k = 1 << (n_t + n - L)
+        base.append((rows, rows + k, rows + 2 * k, k))
+        rows += 3 * k
+    msg = torch.full((rows + 1, 1 << L), 7, dtype=torch.int64, device="cuda")  # a row past the tables stays 7
+    fp.commit_tables([(torch.from_numpy(Z).cuda(), n_o[j], *base[j][:3]) for j, Z in enumerate(Zs)], n_t, s, msg)
+    torch.cuda.synchronize()
+    got = _u64(msg)
+    want = np.full((rows + 1, 1 << L), 7, np.uint64)
+    for j, Z in enumerate(Zs):
+        for w, tab in enumerate(O.layer_tables(Z, s, n_t, n_o[j])):
+            want[base[j][w]:base[j][w] + base[j][3]] = tab.reshape(-1, 1 << L)
+    assert np.array_equal(got, want)
+    # folded rows: the proximity row over all rows (the extra one too) and two claims, map 0's R and map 2's
+    # Q (16 rows each: 4 coordinates, split 2 + 2 and 3 + 1 between the two pointers)
+    assert base[0][3] == base[2][3] == 16
+    n_prox = O.log2ceil(rows + 1)
+    pts = _rand_e2(rng, n_prox + 8)
+    r_prox = pts[:n_prox]
+    chal = _f([x for p in pts for x in p]).reshape(-1, 2)
+    a = n_prox
+    claims = [(base[0][1], chal[a:a + 2], chal[a + 2:a + 4]), (base[2][0], chal[a + 4:a + 7], chal[a + 7:a + 8])]
+    zq = [pts[a:a + 4], pts[a + 4:a + 8]]
+    U = torch.empty((3, 2, 1 << L), dtype=torch.int64, device="cuda")
+    fp.commit_fold_ext(msg, chal[:n_prox], claims, U)
+    torch.cuda.synchronize()
+    gU = _u64(U)
+    assert np.array_equal(gU[0], O.e2_fold_rows(want, O.eq_table_e2(r_prox)[:rows + 1]))
+    for k, (row0, z) in enumerate(zip((base[0][1], base[2][0]), zq)):
+        Ez = O.eq_table_e2(z)
+        assert np.array_equal(gU[1 + k], O.e2_fold_rows(want[row0:row0 + len(Ez)], Ez)), k
+
+
+def test_merkle_open(fp):
+    rng = np.random.default_rng(301)
+    rows, W = 5, 64
+    code = rng.integers(0, P, size=(rows, W), dtype=np.uint64)
+    salts = rng.integers(0, 256, size=(W, 16), dtype=np.uint8)
+    levels = O.merkle_tree(code, salts)
+    code_t, salts_t = _f(code).reshape(rows, W), torch.from_numpy(salts).cuda()
+    tree = fp.merkle_commit(code_t, salts_t)
+    chal = _f(rng.integers(0, P, size=(9, 2), dtype=np.uint64)).reshape(9, 2)
+    cols, cs, paths, idx = fp.merkle_open(code_t, salts_t, tree, chal)
+    torch.cuda.synchronize()
+    ch = _u64(chal)
+    for q in range(9):
+        j = int(ch[q, 0]) % W
+        assert int(idx[q]) == j
+        assert np.array_equal(_u64(cols[q]), code[:, j])
+        assert bytes(cs[q].cpu().numpy()) == bytes(salts[j])
+        path = [bytes(paths[q, d].cpu().numpy()) for d in range(6)]
+        assert path == O.merkle_path(levels, j)
+        assert O.merkle_verify(levels[-1][0], O.merkle_leaf(code, salts, j), j, path)
 
 
 def _salts(cfg, width):
     return synth.raw(synth.data_seed(cfg.seed, 1 << 23), width * 2).view(np.uint8).reshape(width, 16)
 
 
-@pytest.mark.parametrize("cid", [1, 2])
-def test_faithful_layer(fp, cid):
-    cfg = synth.config(cid)
+def _layer(cfg, inp):
+    maps = [(inp[m.x], inp[m.w]) for m in cfg.matmuls]
+    lay = O.LayerLayout(cfg.T, [m.d_out for m in cfg.matmuls])
+    return maps, _salts(cfg, 2 << lay.L)
+
+
+FAITHFUL_CASES = [(1, {}), (2, dict(T=24, d_in=96, d_out=200)), (3, dict(T=40, d=320, d_ff=600)),
+                  (3, dict(T=16, d=64, d_ff=96)), (5, dict(T=24, d=96, d_kv=40, d_ff=300)),
+                  (5, dict(T=8, d=32, d_kv=16, d_ff=48))]
+
+
+@pytest.mark.parametrize("cid,shape", FAITHFUL_CASES)
+def test_faithful_layer(fp, cid, shape):
+    """The whole proof (commitment root, folded rows, every round, challenge and final, rho, the final
+    transcript state, the opened columns with their salts and paths) against the oracle's prover, accepted by
+    the oracle's verifier, and again after a graph replay."""
+    cfg = synth.config(cid, **shape)
     inp = synth.make_inputs(cfg)
-    m = cfg.matmuls[0]
-    X, W = inp[m.x], inp[m.w]
-    logn = commit_logn(2 * cfg.T * m.d_out)
-    salts = _salts(cfg, 2 << logn)
-    pr = FaithfulLayerProver(X, W, cfg.s, salts)
+    maps, salts = _layer(cfg, inp)
+    batched = cfg.kind == "batched"
+    pr = FaithfulProver(cfg, inp, salts)
     pr.run()
     torch.cuda.synchronize()
     got = pr.results()
-    root, _ = _oracle_root(X, W, cfg.s, salts)
-    assert got["root"] == root
-    want = O.prove_layer_fs(X, W, cfg.s, root)
-    assert got["chal"] == want["r_t"] + want["r_o"]
-    assert got["c0"] == want["c0"]
-    assert got["rounds"] == [list(g) for g in want["rounds"]]
-    assert got["r"] == want["r"]
-    assert got["finals"] == want["finals"]
-    assert got["state"] == want["state"]
-    assert O.verify_layer_fs(X, W, cfg.s, root, got) == "OK"
-    # a replay of the captured step gives the same proof
+    want = O.prove_layer_committed(maps, cfg.s, batched, salts)
+    assert got["root"] == want["root"]
+    assert np.array_equal(got["U"], want["U"])
+    assert len(got["sumchecks"]) == len(want["sumchecks"])
+    for g, w in zip(got["sumchecks"], want["sumchecks"]):
+        assert g["rounds"] == [list(x) for x in w["rounds"]]
+        assert g["r"] == w["r"] and g["finals"] == w["finals"]
+    assert got["rho"] == want["rho"] and got["state"] == want["state"] and got["idx"] == want["idx"]
+    assert np.array_equal(got["columns"], want["columns"]) and np.array_equal(got["col_salts"], want["col_salts"])
+    assert got["paths"] == want["paths"]
+    for j, m in enumerate(cfg.matmuls):
+        _, Y, R = O.witness(*maps[j], cfg.s)
+        assert np.array_equal(got["Y"][j], Y) and np.array_equal(got["R"][j], R), m.name
+    assert O.verify_layer_committed(maps, cfg.s, batched, got) == "OK"
     pr.capture()
     pr.replay()
     torch.cuda.synchronize()
     again = pr.results()
-    assert again["rounds"] == got["rounds"] and again["state"] == got["state"]
+    assert again["sumchecks"] == got["sumchecks"] and again["state"] == got["state"]
+    assert np.array_equal(again["columns"], got["columns"])
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_faithful_full_size(fp, cid):
+    """The full-size proof of the up-projection, the dense MLP and the seven-map layer, checked by the oracle's
+    verifier alone (no witness: the claims come from the opened commitment), and rejected once an opened column
+    or a folded row is altered."""
+    cfg = synth.config(cid)
+    inp = synth.make_inputs(cfg)
+    maps, salts = _layer(cfg, inp)
+    batched = cfg.kind == "batched"
+    pr = FaithfulProver(cfg, inp, salts)
+    pr.run()
+    torch.cuda.synchronize()
+    got = pr.results()
+    assert O.verify_layer_committed(maps, cfg.s, batched, got) == "OK"
+    bad = dict(got, columns=got["columns"].copy())
+    bad["columns"][3, 1] = (int(bad["columns"][3, 1]) + 1) % P
+    assert O.verify_layer_committed(maps, cfg.s, batched, bad) == "COLUMN_PATH"
+    bad = dict(got, U=got["U"].copy())
+    bad["U"][2, 0, 5] = (int(bad["U"][2, 0, 5]) + 1) % P
+    assert O.verify_layer_committed(maps, cfg.s, batched, bad) != "OK"

@@ -34,6 +34,8 @@ EXPORTS = [
     "fp_layer_step", "fp_layer_step_workspace", "fp_witness_multi", "fp_witness_multi_workspace",
     "fp_witness_multi_noalloc", "fp_layer_step_multi", "fp_layer_step_multi_workspace",
     "fp_witness_grouped_packed", "fp_witness_grouped_packed_workspace",
+    "fp_sumcheck_ext_fs_multi", "fp_sumcheck_ext_fs_multi_workspace", "fp_commit_tables", "fp_commit_fold_ext",
+    "fp_commit_fold_ext_workspace", "fp_merkle_open",
 ]
 
 _lib = None
@@ -50,6 +52,17 @@ class _EqDesc(ctypes.Structure):
 class _ClaimDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
                 ("E_rows", ctypes.c_void_p), ("E_cols", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class _TableDesc(ctypes.Structure):
+    _fields_ = [("Z", ctypes.c_void_p), ("ldz", ctypes.c_int64), ("T", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("n_o", ctypes.c_int32), ("row_q", ctypes.c_int32), ("row_r", ctypes.c_int32),
+                ("row_y", ctypes.c_int32)]
+
+
+class _OpenClaim(ctypes.Structure):
+    _fields_ = [("row0", ctypes.c_int32), ("nrows", ctypes.c_int32), ("z1", ctypes.c_void_p), ("n1", ctypes.c_int32),
+                ("z2", ctypes.c_void_p), ("n2", ctypes.c_int32)]
 
 
 class _MatmulDesc(ctypes.Structure):
@@ -139,6 +152,12 @@ def lib():
                                                          vp, vp, i64, i32, vp, sz, vp]),
             "fp_witness_grouped_packed_workspace": (sz, [vp, i32, i32, i32, i32]),
             "fp_layer_step_workspace": (sz, [i32, i32, i32, i32, vp, i32, vp]),
+            "fp_sumcheck_ext_fs_multi": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "fp_sumcheck_ext_fs_multi_workspace": (sz, [i32, i32]),
+            "fp_commit_tables": (ctypes.c_int, [i32, vp, i32, i32, i32, vp, i64, i32, vp]),
+            "fp_commit_fold_ext": (ctypes.c_int, [vp, i64, i32, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
+            "fp_commit_fold_ext_workspace": (sz, [i32]),
+            "fp_merkle_open": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -209,6 +228,7 @@ class Workspace:
 
 _ws_fold, _ws_claim, _ws_mle, _ws_sc = Workspace(), Workspace(), Workspace(), Workspace()
 _ws_multi, _ws_rs, _ws_lookup = Workspace(), Workspace(), Workspace()
+_ws_open, _ws_scx = Workspace(), Workspace()
 
 
 def to_field_tensor(vals, device=None) -> torch.Tensor:
@@ -801,6 +821,97 @@ def sumcheck_ext_fs(A0, A1, B0, B1, state, rounds=None, r=None, finals=None):
     _check(lib().fp_sumcheck_ext_fs(_ptr(A0), _ptr(A1), _ptr(B0), _ptr(B1), n, _ptr(state), _ptr(rounds), _ptr(r),
                                     _ptr(finals), _stream()), "fp_sumcheck_ext_fs")
     return rounds[:n], r[:n], finals
+
+
+def sumcheck_ext_fs_multi(A0s, A1s, B0s, B1s, state, rho=None, rounds=None, r=None, finals=None):
+    """Extension sum-check of sum_j rho_j sum_k A_j[k] B_j[k] (A_j = A0s[j] + u A1s[j], 1..8 pairs of int64
+    [2^n] tables; rho device [n_pairs, 2] or None) with the transcript: rounds [n, 3, 2], r [n, 2],
+    finals [n_pairs, 2, 2]."""
+    k = len(A0s)
+    assert 1 <= k <= 8 and len(A1s) == len(B0s) == len(B1s) == k
+    N = A0s[0].numel()
+    n = N.bit_length() - 1
+    assert N == 1 << n
+    for t in list(A0s) + list(A1s) + list(B0s) + list(B1s):
+        _need(t, torch.int64, N, "sum-check table")
+    dev = A0s[0].device
+    rounds = torch.empty((max(n, 1), 3, 2), dtype=torch.int64, device=dev) if rounds is None else rounds
+    r = torch.empty((max(n, 1), 2), dtype=torch.int64, device=dev) if r is None else r
+    finals = torch.empty((k, 2, 2), dtype=torch.int64, device=dev) if finals is None else finals
+    _need(rounds, torch.int64, 6 * n, "rounds")
+    _need(r, torch.int64, 2 * n, "r")
+    _need(finals, torch.int64, 4 * k, "finals")
+    assert state.is_contiguous() and state.numel() * state.element_size() >= 32, "state: 32 bytes"
+    if rho is not None:
+        _need(rho, torch.int64, 2 * k, "rho")
+    arr = lambda ts: (ctypes.c_void_p * k)(*[t.data_ptr() for t in ts])
+    p, nb = _ws_scx.get(lib().fp_sumcheck_ext_fs_multi_workspace(k, n))
+    _check(lib().fp_sumcheck_ext_fs_multi(k, arr(A0s), arr(A1s), arr(B0s), arr(B1s), _ptr(rho), n, _ptr(state),
+                                          _ptr(rounds), _ptr(r), _ptr(finals), p, nb, _stream()),
+           "fp_sumcheck_ext_fs_multi")
+    return rounds[:n], r[:n], finals
+
+
+def commit_tables(maps, n_t: int, s: int, msg):
+    """Each map's Q (before the clamp), R and Y as zero-padded [2^n_t, 2^n_o] field tables in whole rows of
+    msg [rows, 2^L]; maps: (Z int32 [T, d_out], n_o, row_q, row_r, row_y)."""
+    rows, cols = msg.shape
+    L = cols.bit_length() - 1
+    assert 1 << L == cols and msg.is_contiguous() and msg.dtype == torch.int64
+    descs = []
+    for Z, n_o, rq, rr, ry in maps:
+        T, d_out = Z.shape
+        _need(Z, torch.int32, T * d_out, "Z")
+        descs.append(_TableDesc(_ptr(Z) if Z.numel() else None, max(d_out, 1), T, d_out, n_o, rq, rr, ry))
+    arr = (_TableDesc * len(descs))(*descs)
+    _check(lib().fp_commit_tables(len(descs), arr, n_t, s, L, _ptr(msg), cols, rows, _stream()), "fp_commit_tables")
+    return msg
+
+
+def commit_fold_ext(msg, r_prox, claims, U):
+    """Folded rows over the extension of msg [rows, 2^L]: U [1 + len(claims), 2, 2^L] receives the proximity row
+    (row weights eq(r_prox, i); r_prox [n_prox, 2]) and each claim's row; claims: (row0, z1 [n1, 2], z2 [n2, 2])
+    with 2^(n1 + n2) rows from row0, sorted and disjoint."""
+    rows, cols = msg.shape
+    L = cols.bit_length() - 1
+    assert 1 << L == cols and msg.is_contiguous() and msg.dtype == torch.int64
+    _need(U, torch.int64, (1 + len(claims)) * 2 * cols, "U")
+    cs = []
+    for row0, z1, z2 in claims:
+        n1, n2 = z1.shape[0], z2.shape[0]
+        for z in (z1, z2):
+            assert z.dtype == torch.int64 and (z.numel() == 0 or z.is_contiguous())
+        cs.append(_OpenClaim(row0, 1 << (n1 + n2), _ptr(z1) if n1 else None, n1, _ptr(z2) if n2 else None, n2))
+    arr = (_OpenClaim * max(1, len(cs)))(*cs)
+    n_prox = r_prox.shape[0]
+    assert r_prox.dtype == torch.int64 and r_prox.is_contiguous()
+    p, nb = _ws_open.get(lib().fp_commit_fold_ext_workspace(rows))
+    _check(lib().fp_commit_fold_ext(_ptr(msg), cols, rows, L, _ptr(r_prox) if n_prox else None, n_prox, len(cs), arr,
+                                    _ptr(U), p, nb, _stream()), "fp_commit_fold_ext")
+    return U
+
+
+def merkle_open(code, salts, tree, chal, cols=None, col_salts=None, paths=None, idx=None):
+    """Columns j = chal[q, 0] mod W of code [rows, W] with their salts and Merkle paths: cols [nq, rows] int64,
+    col_salts [nq, 16] uint8, paths [nq, log2 W, 32] uint8, idx [nq] int32."""
+    rows, W = code.shape
+    logw = W.bit_length() - 1
+    nq = chal.shape[0]
+    assert 1 << logw == W and code.is_contiguous() and chal.dtype == torch.int64 and chal.is_contiguous()
+    _need(salts, torch.uint8, W * SALT_BYTES, "salts")
+    _need(tree, torch.uint8, (2 * W - 1) * DIGEST_BYTES, "tree")
+    dev = code.device
+    cols = torch.empty((nq, rows), dtype=torch.int64, device=dev) if cols is None else cols
+    col_salts = torch.empty((nq, SALT_BYTES), dtype=torch.uint8, device=dev) if col_salts is None else col_salts
+    paths = torch.empty((nq, logw, DIGEST_BYTES), dtype=torch.uint8, device=dev) if paths is None else paths
+    idx = torch.empty(nq, dtype=torch.int32, device=dev) if idx is None else idx
+    _need(cols, torch.int64, nq * rows, "cols")
+    _need(col_salts, torch.uint8, nq * SALT_BYTES, "col_salts")
+    _need(paths, torch.uint8, nq * logw * DIGEST_BYTES, "paths")
+    _need(idx, torch.int32, nq, "idx")
+    _check(lib().fp_merkle_open(_ptr(code), W, rows, logw, _ptr(salts), _ptr(tree), _ptr(chal), nq, _ptr(cols),
+                                _ptr(col_salts), _ptr(paths), _ptr(idx), _stream()), "fp_merkle_open")
+    return cols, col_salts, paths, idx
 
 
 def mle_eval(M, r_rows, r_cols, out=None):

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfp.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "commit.hip", "eq.hip", "fold.hip", "fold_multi.hip", "fs.hip", "lookup.hip", "sumcheck.hip", "witness.hip", "witness_multi.hip"]
+SOURCES = ["api.hip", "commit.hip", "eq.hip", "fold.hip", "fold_multi.hip", "fs.hip", "lookup.hip", "opening.hip", "sumcheck.hip", "witness.hip", "witness_multi.hip"]
 FLAGS = ["-O3", "-std=c++20", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

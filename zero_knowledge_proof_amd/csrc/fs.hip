@@ -18,23 +18,13 @@
 // BLAKE2b compression per round, computed by wave 0.
 #include "blake2b.hpp"
 #include "common.hpp"
+#include "ext.hpp"
 #include "gl.hpp"
 #include "sc_tail.hpp"
 
 namespace {
 
-// ---------------------------------------------------------------- F_{p^2}
-struct E2 {
-  uint64_t a, b;  // a + u b
-};
-__device__ __forceinline__ E2 e2_add(E2 x, E2 y) { return E2{gl::add(x.a, y.a), gl::add(x.b, y.b)}; }
-__device__ __forceinline__ E2 e2_sub(E2 x, E2 y) { return E2{gl::sub(x.a, y.a), gl::sub(x.b, y.b)}; }
-__device__ __forceinline__ E2 e2_mul(E2 x, E2 y) {
-  return E2{gl::add(gl::mul(x.a, y.a), gl::mul_small(gl::mul(x.b, y.b), 7u)),
-            gl::add(gl::mul(x.a, y.b), gl::mul(x.b, y.a))};
-}
-__device__ __forceinline__ E2 e2_lerp(E2 x0, E2 x1, E2 r) { return e2_add(x0, e2_mul(r, e2_sub(x1, x0))); }
-__device__ __forceinline__ uint64_t canon(uint64_t w) { return w >= gl::P ? w - gl::P : w; }
+using namespace fpx;
 
 // ----------------------------------------------------------- the transcript
 constexpr int FS_MAX_INIT_WORDS = 16;
@@ -345,6 +335,128 @@ __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restr
   }
 }
 
+// ------------------------------------- the multi-pair extension sum-check
+// sum_j rho_j sum_k A_j[k] B_j[k] over 2^n with up to 8 pairs, for tables too
+// large for registers: one workgroup streams every round through a workspace.
+// Round i reads T_i (the caller's base parts for i = 0, else the workspace),
+// sums each pair's terms exactly (96-bit), weighs them by rho_j, completes
+// g_i across the workgroup, lets wave 0 absorb it and read r_i, and only then
+// binds every table with r_i into T_{i+1}, which alternates between two
+// workspace buffers (pair j's A at 2j 2^(n-1), its B at (2j+1) 2^(n-1)).
+constexpr int SM_T = 1024;
+constexpr int SM_MAX_PAIRS = 8;
+constexpr int SM_MAXN = 24;
+
+struct ExtScArgs {
+  const uint64_t* A0[SM_MAX_PAIRS];
+  const uint64_t* A1[SM_MAX_PAIRS];
+  const uint64_t* B0[SM_MAX_PAIRS];
+  const uint64_t* B1[SM_MAX_PAIRS];
+  const uint64_t* rho;  // 2 n_pairs words, or NULL (all ones)
+  int32_t np, n;
+  uint64_t* state;
+  uint64_t* rounds;  // [n][3][2]
+  uint64_t* r_out;   // [n][2]
+  uint64_t* finals;  // [np][4]: A_j(r), B_j(r)
+  E2* ws;
+};
+
+__global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
+  __shared__ sct::S96 red[SM_T / 64][6];
+  __shared__ uint64_t rsh[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int np = a.np, n = a.n;
+  const int64_t H = n > 0 ? (int64_t)1 << (n - 1) : 0;
+  E2* buf[2] = {a.ws, a.ws + 2 * np * H};
+  uint64_t s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = a.state[i];
+  for (int i = 0; i < n; ++i) {
+    const int64_t h = (int64_t)1 << (n - 1 - i);
+    const E2* src = i > 0 ? buf[(i - 1) & 1] : nullptr;
+    auto load = [&](int j, int64_t q, E2& a0, E2& a1, E2& b0, E2& b1) {
+      if (i == 0) {
+        a0 = E2{a.A0[j][2 * q], a.A1[j][2 * q]};
+        a1 = E2{a.A0[j][2 * q + 1], a.A1[j][2 * q + 1]};
+        b0 = E2{a.B0[j][2 * q], a.B1[j][2 * q]};
+        b1 = E2{a.B0[j][2 * q + 1], a.B1[j][2 * q + 1]};
+      } else {
+        const E2* A = src + 2 * j * H;
+        const E2* B = src + (2 * j + 1) * H;
+        a0 = A[2 * q];
+        a1 = A[2 * q + 1];
+        b0 = B[2 * q];
+        b1 = B[2 * q + 1];
+      }
+    };
+    E2 g[3] = {E2{0, 0}, E2{0, 0}, E2{0, 0}};
+    for (int j = 0; j < np; ++j) {
+      sct::S96 acc[6] = {};
+      for (int64_t q = tid; q < h; q += SM_T) {
+        E2 a0, a1, b0, b1;
+        load(j, q, a0, a1, b0, b1);
+        pair_terms_e2(a0, a1, b0, b1, acc);
+      }
+      const E2 rj = a.rho ? E2{a.rho[2 * j], a.rho[2 * j + 1]} : E2{1, 0};
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+        g[c] = e2_add(g[c], e2_mul(rj, E2{sct::reduce96(acc[2 * c]), sct::reduce96(acc[2 * c + 1])}));
+    }
+    sct::S96 t[6];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      t[2 * c] = sct::wave_sum96(sct::to96(g[c].a));
+      t[2 * c + 1] = sct::wave_sum96(sct::to96(g[c].b));
+    }
+    if (lane == 63)
+#pragma unroll
+      for (int c = 0; c < 6; ++c) red[wave][c] = t[c];
+    __syncthreads();
+    if (wave == 0) {
+      uint64_t v[6];
+#pragma unroll
+      for (int c = 0; c < 6; ++c) {
+        sct::S96 x = red[0][c];
+        for (int w = 1; w < SM_T / 64; ++w) x = sct::add96(x, red[w][c]);
+        v[c] = sct::reduce96(x);
+      }
+      E2 G[3];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) G[c] = E2{v[2 * c], v[2 * c + 1]};
+      const E2 r = emit_round(s, G, a.rounds, a.r_out, i, lane == 0);
+      if (lane == 0) {
+        rsh[0] = r.a;
+        rsh[1] = r.b;
+      }
+    }
+    __syncthreads();  // r_i known to every wave, and g_i's reads of red done
+    const E2 r{rsh[0], rsh[1]};
+    E2* dst = buf[i & 1];
+    for (int j = 0; j < np; ++j) {
+      for (int64_t q = tid; q < h; q += SM_T) {
+        E2 a0, a1, b0, b1;
+        load(j, q, a0, a1, b0, b1);
+        dst[2 * j * H + q] = e2_lerp(a0, a1, r);
+        dst[(2 * j + 1) * H + q] = e2_lerp(b0, b1, r);
+      }
+    }
+    __syncthreads();  // T_{i+1} complete before round i+1 reads it
+  }
+  if (wave != 0) return;
+  // finals A_j(r), B_j(r) of every pair, absorbed as one message
+  auto fin = [&](int w) -> uint64_t {  // word w of the finals message
+    const int j = w / 4, k = w % 4;
+    E2 x;
+    if (n == 0) x = k < 2 ? E2{a.A0[j][0], a.A1[j][0]} : E2{a.B0[j][0], a.B1[j][0]};
+    else x = buf[(n - 1) & 1][(2 * j + (k >= 2)) * H];
+    return (k & 1) ? x.b : x.a;
+  };
+  uint64_t d[4];
+  b2_digest([&](int w) { return w < 4 ? s[w] : fin(w - 4); }, 8 * (4 + 4 * np), d);
+  if (lane < 4 * np) a.finals[lane] = fin(lane);
+  if (lane < 4) a.state[lane] = d[lane];
+}
+
 }  // namespace
 
 extern "C" int fp_fs_init(uint8_t* state, const uint8_t* msg, int32_t nbytes, hipStream_t stream) {
@@ -410,5 +522,46 @@ extern "C" int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp
   hipLaunchKernelGGL(sc_ext_fs_kernel, dim3(1), dim3(SE_T), 0, stream, A0, A1, B0, B1, n, (uint64_t*)state, rounds,
                      r, finals);
   const int rc = fpi::check_launch("sc_ext_fs_kernel");
+  return rc ? rc : fpi::ok();
+}
+
+extern "C" size_t fp_sumcheck_ext_fs_multi_workspace(int32_t n_pairs, int32_t n) {
+  if (n_pairs < 1 || n_pairs > SM_MAX_PAIRS || n < 0 || n > SM_MAXN) return 0;
+  return n == 0 ? 0 : fpi::align_up((size_t)n_pairs << (n + 5), 256);
+}
+
+extern "C" int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A0, const fp_elem* const* A1,
+                                        const fp_elem* const* B0, const fp_elem* const* B1, const fp_elem* rho,
+                                        int32_t n, uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fp_sumcheck_ext_fs_multi";
+  if (n_pairs < 1 || n_pairs > SM_MAX_PAIRS)
+    return fpi::fail(FP_EARG, "%s: n_pairs=%d outside [1, %d]", fn, n_pairs, SM_MAX_PAIRS);
+  if (n < 0 || n > SM_MAXN) return fpi::fail(FP_ESHAPE, "%s: n=%d outside [0, %d]", fn, n, SM_MAXN);
+  if (!A0 || !A1 || !B0 || !B1 || !state || !finals || (n > 0 && (!rounds || !r)))
+    return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  if (((uintptr_t)state) & 7) return fpi::fail(FP_EARG, "%s: state must be 8-byte aligned", fn);
+  const size_t need = fp_sumcheck_ext_fs_multi_workspace(n_pairs, n);
+  if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 255)))
+    return fpi::fail(FP_EWORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) needed, %zu given", fn, need,
+                     ws_bytes);
+  ExtScArgs a{};
+  for (int j = 0; j < n_pairs; ++j) {
+    if (!A0[j] || !A1[j] || !B0[j] || !B1[j]) return fpi::fail(FP_EARG, "%s: null table of pair %d", fn, j);
+    a.A0[j] = A0[j];
+    a.A1[j] = A1[j];
+    a.B0[j] = B0[j];
+    a.B1[j] = B1[j];
+  }
+  a.rho = rho;
+  a.np = n_pairs;
+  a.n = n;
+  a.state = (uint64_t*)state;
+  a.rounds = rounds;
+  a.r_out = r;
+  a.finals = finals;
+  a.ws = (E2*)ws;
+  hipLaunchKernelGGL(sc_ext_multi_kernel, dim3(1), dim3(SM_T), 0, stream, a);
+  const int rc = fpi::check_launch("sc_ext_multi_kernel");
   return rc ? rc : fpi::ok();
 }

@@ -23,12 +23,13 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MatmulJob, StepWorkspace, SumcheckJob, combine_claims, layer_step_multi, commit_pack, commit_rows, eq_table_batched, eq_table_ext,
-               ext_claim_combine, field_numpy, fold_claim_batched, fs_absorb, fs_challenges, fs_init, gather_rows,
-               layer_step, linear_combine, merkle_commit, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs,
-               sumcheck_prove, sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped,
-               witness_grouped_packed, witness_linear_packed, witness_linear_packed_with_sumcheck,
-               witness_linear_with_sumcheck, witness_multi)
+from . import (MatmulJob, StepWorkspace, SumcheckJob, combine_claims, commit_fold_ext, commit_tables,
+               eq_table_batched, eq_table_ext, field_numpy, fold_claim_batched, fold_matrix_batched, fs_absorb,
+               fs_challenges, fs_init, gather_rows, layer_step, layer_step_multi, linear_combine, merkle_commit,
+               merkle_open, moe_plan, pack_weights, rs_encode, sumcheck_ext_fs_multi, sumcheck_prove,
+               sumcheck_prove_multi, to_field_tensor, witness_linear, witness_linear_grouped, witness_grouped_packed,
+               witness_linear_packed, witness_linear_packed_with_sumcheck, witness_linear_with_sumcheck,
+               witness_multi)
 
 
 def _nomark(name):
@@ -811,100 +812,208 @@ class MoEBlockProver(_Prover):
         return out
 
 
-FS_LABEL = b"zkp-matmul-sumcheck-fs-v1"
+LAYER_LABEL = b"zkp-layer-committed-rescale-v1"
+LAYER_LOG_ROW = 18      # commitment rows of at most 2^18 elements
+OPEN_COLUMNS = 64       # columns opened per proof
 
 
-def commit_logn(n_limbs: int) -> int:
-    """Row length 2^logn of the commitment of n_limbs limbs: 2^22 elements as on
-    the pages, or the smallest power of two holding them all."""
-    return min(22, log2ceil(max(1, (n_limbs + 2) // 3)))
+class FaithfulProver(_Prover):
+    """A layer's linear maps proved with the rescale committed and every
+    challenge taken from the transcript ("How fast can FlashProve go", §2: the
+    prover commits intermediate values, sum-check reduces each matmul to claims
+    about them and the weights, openings settle the claims, and every challenge
+    hashes all the prover has sent so far; §3.1: g_w and the remainder r are
+    committed, never g^, and the claim about g^ reads 2^k g_w + r; §4 footnote
+    20: the challenges live in an extension). In order:
+      witness    each map's Z, Y, R (Z kept: Q is read from it);
+      commit     each map's Q (before the clamp), R and Y as zero-padded
+                 [2^n_t, 2^n_o] field tables in whole rows of 2^L elements
+                 (L = min(18, min n_t + n_o)), Reed-Solomon encoded, the columns
+                 in a salted BLAKE2b Merkle tree;
+      transcript the label and the layer's shape, then the root; r_t, each
+                 map's r_o and a proximity point r_prox over the rows;
+      eq, folds  E_t, E_o over the extension; x'_m, w'_m (two base folds each);
+      open rows  the proximity row and, per map, the folded rows of Q and of R
+                 at (r_o || r_t) (the verifier reads the claims 2^s Q~ + R~ from
+                 them); their Merkle root (zero salts) is absorbed;
+      sumcheck   batched layers: rho, then one sum-check of
+                 sum_m rho_m x'_m . w'_m; otherwise one sum-check per map, then
+                 rho; every round absorbed before its challenge, the finals after;
+      columns    64 columns drawn from the transcript, gathered with their
+                 salts and Merkle paths.
+    The verifier needs no witness: the claims come from the commitment's
+    openings and the finals are claims about X and W."""
 
-
-class FaithfulLayerProver(_Prover):
-    """One linear map proved with soundness-faithful challenges ("How fast can
-    FlashProve go", §2: every challenge hashes all the prover has sent so far;
-    §4 footnote 20: the challenges live in an extension field). In order:
-    the witness; the commitment of Y and R (limbs packed three per element,
-    rows Reed-Solomon encoded, salted BLAKE2b Merkle tree); the transcript
-    absorbs the layer's shape and the Merkle root and yields r_t, r_o in
-    F_p[u]/(u^2 - 7); the eq tables and the folds of X and W (two base folds
-    each) and the claim c0 (four base claims combined) follow; c0 is absorbed;
-    the sum-check over the extension absorbs each round and draws each r_i
-    from the transcript on the device; the finals are absorbed."""
-
-    def __init__(self, X: np.ndarray, W: np.ndarray, s: int, salts: np.ndarray, dev=None):
+    def __init__(self, cfg, inp: dict, salts: np.ndarray, dev=None):
         dev = dev or torch.device("cuda")
-        self.s = s
-        self.X, self.W = _i8(X, dev), _i8(W, dev)
-        self.Wp = _packed(self.W)
-        T, d_in = X.shape
-        d_out = W.shape[0]
-        self.T, self.d_in, self.d_out = T, d_in, d_out
-        self.n_t, self.n_o, self.n = log2ceil(T), log2ceil(d_out), log2ceil(d_in)
-        self.Z = torch.empty((T, d_out), dtype=torch.int32, device=dev)
-        self.Y = torch.empty((T, d_out), dtype=torch.int8, device=dev)
-        self.R = torch.empty((T, d_out), dtype=torch.int8, device=dev)
-        self.logn = commit_logn(2 * T * d_out)
-        self.rows = commit_rows(T * d_out, T * d_out, self.logn)
-        width = 2 << self.logn
+        self.cfg, self.s = cfg, cfg.s
+        self.batched = cfg.kind == "batched"
+        T = cfg.T
+        self.tens = {}
+        for m in cfg.matmuls:
+            for nm in (m.x, m.w):
+                if nm not in self.tens:
+                    self.tens[nm] = _i8(inp[nm], dev)
+        self.packed = {m.w: _packed(self.tens[m.w]) for m in cfg.matmuls}
+        M = len(cfg.matmuls)
+        self.M = M
+        self.n_t = log2ceil(T)
+        self.n_o = [log2ceil(m.d_out) for m in cfg.matmuls]
+        self.L = min(LAYER_LOG_ROW, min(self.n_t + n for n in self.n_o))
+        self.base, row = [], 0
+        for n in self.n_o:
+            k = 1 << (self.n_t + n - self.L)
+            self.base.append((row, row + k, row + 2 * k, k))
+            row += 3 * k
+        self.rows = row
+        self.n_prox = log2ceil(row)
+        width = 2 << self.L
         assert salts.shape == (width, 16)
         self.salts = _i8(salts.astype(np.uint8), dev)
-        self.msg = torch.empty((self.rows, 1 << self.logn), dtype=torch.int64, device=dev)
+        self.Z = [torch.empty((T, m.d_out), dtype=torch.int32, device=dev) for m in cfg.matmuls]
+        self.Y = [torch.empty((T, m.d_out), dtype=torch.int8, device=dev) for m in cfg.matmuls]
+        self.R = [torch.empty((T, m.d_out), dtype=torch.int8, device=dev) for m in cfg.matmuls]
+        self.msg = torch.empty((self.rows, 1 << self.L), dtype=torch.int64, device=dev)
         self.code = torch.empty((self.rows, width), dtype=torch.int64, device=dev)
         self.tree = torch.empty((2 * width - 1, 32), dtype=torch.uint8, device=dev)
-        self.state = torch.empty(4, dtype=torch.int64, device=dev)
-        self.init_msg = FS_LABEL + b"".join(int(v).to_bytes(4, "little") for v in (T, d_in, d_out, s))
-        self.chal = torch.empty((max(1, self.n_t + self.n_o), 2), dtype=torch.int64, device=dev)
+        self.state = torch.empty(32, dtype=torch.uint8, device=dev)
+        words = [T, cfg.s, M, int(self.batched), self.L, OPEN_COLUMNS]
+        for m in cfg.matmuls:
+            words += [m.d_in, m.d_out]
+        self.init_msg = LAYER_LABEL + b"".join(int(v).to_bytes(4, "little") for v in words)
+        self.n_ch = self.n_t + sum(self.n_o) + self.n_prox
+        self.chal = torch.empty((max(1, self.n_ch), 2), dtype=torch.int64, device=dev)
+        self.r_t = self.chal[:self.n_t]
+        off = self.n_t
+        self.r_o = []
+        for n in self.n_o:
+            self.r_o.append(self.chal[off:off + n])
+            off += n
+        self.r_prox = self.chal[off:off + self.n_prox]
+        # each claim's row point: the coordinates of (r_o || r_t) from L on
+        self.claims = []
+        for m, n in enumerate(self.n_o):
+            if self.L <= n:
+                z1, z2 = self.r_o[m][self.L:], self.r_t
+            else:
+                z1, z2 = self.r_t[self.L - n:], self.r_t[:0]
+            rq, rr, _, _ = self.base[m]
+            self.claims += [(rq, z1, z2), (rr, z1, z2)]
         self.Et = [_f(1 << self.n_t, dev), _f(1 << self.n_t, dev)]
-        self.Eo = [_f(1 << self.n_o, dev), _f(1 << self.n_o, dev)]
-        self.xf = [_f(1 << self.n, dev), _f(1 << self.n, dev)]
-        self.wf = [_f(1 << self.n, dev), _f(1 << self.n, dev)]
-        self.c4 = _f(4, dev)
-        self.c0 = _f(2, dev)
-        self.rounds = torch.empty((max(1, self.n), 3, 2), dtype=torch.int64, device=dev)
-        self.r = torch.empty((max(1, self.n), 2), dtype=torch.int64, device=dev)
-        self.finals = torch.empty((2, 2), dtype=torch.int64, device=dev)
+        self.Eo = [[_f(1 << n, dev), _f(1 << n, dev)] for n in self.n_o]
+        n_all = max(m.n for m in cfg.matmuls)
+        self.n_sc = [n_all if self.batched else m.n for m in cfg.matmuls]
+        xf = {}
+        self.xf, self.wf = [], []
+        for m, n in zip(cfg.matmuls, self.n_sc):
+            if (m.x, n) not in xf:
+                xf[(m.x, n)] = [_f(1 << n, dev), _f(1 << n, dev)]
+            self.xf.append(xf[(m.x, n)])
+            self.wf.append([_f(1 << n, dev), _f(1 << n, dev)])
+        self.x_jobs = [(self.tens[x], n, parts) for (x, n), parts in xf.items()]
+        K = 1 + 2 * M
+        self.U = torch.empty((K, 2, 1 << self.L), dtype=torch.int64, device=dev)
+        self.zero_salts = torch.zeros((1 << self.L, 16), dtype=torch.uint8, device=dev)
+        self.tree_u = torch.empty((2 * (1 << self.L) - 1, 32), dtype=torch.uint8, device=dev)
+        self.rho = torch.empty((M, 2), dtype=torch.int64, device=dev)
+        groups = [list(range(M))] if self.batched else [[m] for m in range(M)]
+        self.sc = []
+        for g in groups:
+            n = self.n_sc[g[0]]
+            self.sc.append({"maps": g, "rounds": torch.empty((max(n, 1), 3, 2), dtype=torch.int64, device=dev),
+                            "r": torch.empty((max(n, 1), 2), dtype=torch.int64, device=dev),
+                            "finals": torch.empty((len(g), 2, 2), dtype=torch.int64, device=dev), "n": n})
+        self.chal_cols = torch.empty((OPEN_COLUMNS, 2), dtype=torch.int64, device=dev)
+        self.cols = torch.empty((OPEN_COLUMNS, self.rows), dtype=torch.int64, device=dev)
+        self.col_salts = torch.empty((OPEN_COLUMNS, 16), dtype=torch.uint8, device=dev)
+        self.paths = torch.empty((OPEN_COLUMNS, self.L + 1, 32), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(OPEN_COLUMNS, dtype=torch.int32, device=dev)
+        fused = sorted((j for j, m in enumerate(cfg.matmuls) if self.packed[m.w] is not None),
+                       key=lambda j: -cfg.matmuls[j].d_in)
+        self.jobs = [MatmulJob(self.tens[cfg.matmuls[j].x], self.packed[cfg.matmuls[j].w], self.Y[j], self.R[j],
+                               self.Z[j]) for j in fused]
+        self.ws = StepWorkspace()
+
+    def _witness(self):
+        if self.jobs:
+            witness_multi(self.jobs, self.s, ws=self.ws)
+        for j, m in enumerate(self.cfg.matmuls):
+            if self.packed[m.w] is None:
+                witness_linear(self.tens[m.x], self.tens[m.w], self.s, self.Z[j], self.Y[j], self.R[j])
 
     def _commit(self):
-        commit_pack(self.Y.reshape(-1), self.R.reshape(-1), self.logn, self.rows, out=self.msg)
+        commit_tables([(self.Z[j], self.n_o[j], *self.base[j][:3]) for j in range(self.M)], self.n_t, self.s,
+                      self.msg)
         rs_encode(self.msg, code=self.code)
         merkle_commit(self.code, self.salts, tree=self.tree)
 
     def _challenges(self):
         fs_init(self.state, self.init_msg)
         fs_absorb(self.state, self.tree[-1].view(torch.int64))
-        fs_challenges(self.state, self.n_t + self.n_o, out=self.chal)
+        fs_challenges(self.state, self.n_ch, out=self.chal)
 
     def _eq(self):
-        eq_table_ext(self.chal[:self.n_t], self.Et[0], self.Et[1])
-        eq_table_ext(self.chal[self.n_t:self.n_t + self.n_o], self.Eo[0], self.Eo[1])
+        eq_table_ext(self.r_t, self.Et[0], self.Et[1])
+        for j in range(self.M):
+            eq_table_ext(self.r_o[j], self.Eo[j][0], self.Eo[j][1])
 
-    def _fold_claim(self):
-        N = 1 << self.n
-        Et, Eo, c4 = self.Et, self.Eo, self.c4
-        fold_claim_batched([(self.X, Et[0], N, self.xf[0]), (self.X, Et[1], N, self.xf[1]),
-                            (self.W, Eo[0], N, self.wf[0]), (self.W, Eo[1], N, self.wf[1])],
-                           [(self.Z, Et[0], Eo[0], c4[0:1]), (self.Z, Et[1], Eo[1], c4[1:2]),
-                            (self.Z, Et[0], Eo[1], c4[2:3]), (self.Z, Et[1], Eo[0], c4[3:4])])
-        ext_claim_combine(self.c4, self.c0)
-        fs_absorb(self.state, self.c0)
+    def _folds(self):
+        jobs = []
+        for X, n, parts in self.x_jobs:
+            jobs += [(X, self.Et[0], 1 << n, parts[0]), (X, self.Et[1], 1 << n, parts[1])]
+        for j, m in enumerate(self.cfg.matmuls):
+            W, n = self.tens[m.w], self.n_sc[j]
+            jobs += [(W, self.Eo[j][0], 1 << n, self.wf[j][0]), (W, self.Eo[j][1], 1 << n, self.wf[j][1])]
+        fold_matrix_batched(jobs)
+
+    def _open_rows(self):
+        commit_fold_ext(self.msg, self.r_prox, self.claims, self.U)
+        merkle_commit(self.U.view(-1, 1 << self.L), self.zero_salts, tree=self.tree_u)
+        fs_absorb(self.state, self.tree_u[-1].view(torch.int64))
 
     def _sumcheck(self):
-        sumcheck_ext_fs(self.xf[0], self.xf[1], self.wf[0], self.wf[1], self.state, rounds=self.rounds, r=self.r,
-                        finals=self.finals)
+        if self.batched:
+            fs_challenges(self.state, self.M, out=self.rho)
+        for sc in self.sc:
+            g = sc["maps"]
+            sumcheck_ext_fs_multi([self.xf[j][0] for j in g], [self.xf[j][1] for j in g],
+                                  [self.wf[j][0] for j in g], [self.wf[j][1] for j in g], self.state,
+                                  rho=self.rho if self.batched else None, rounds=sc["rounds"], r=sc["r"],
+                                  finals=sc["finals"])
+        if not self.batched:
+            fs_challenges(self.state, self.M, out=self.rho)
+
+    def _columns(self):
+        # the columns' challenges are read from the final state (nothing absorbed after)
+        fs_challenges(self.state, OPEN_COLUMNS, out=self.chal_cols)
+        merkle_open(self.code, self.salts, self.tree, self.chal_cols, cols=self.cols, col_salts=self.col_salts,
+                    paths=self.paths, idx=self.idx)
 
     def phases(self):
-        return [("witness", lambda: _witness(self.X, self.W, self.Wp, self.s, self.Z, self.Y, self.R)),
-                ("commit", self._commit), ("transcript", self._challenges), ("eq", self._eq),
-                ("fold+claim", self._fold_claim), ("sumcheck", self._sumcheck)]
+        return [("witness", self._witness), ("commit", self._commit), ("transcript", self._challenges),
+                ("eq", self._eq), ("folds", self._folds), ("open rows", self._open_rows),
+                ("sumcheck", self._sumcheck), ("columns", self._columns)]
+
+    def output_tensors(self):
+        return ([self.U, self.rho, self.state, self.cols, self.col_salts, self.paths, self.idx, self.tree]
+                + [sc[k] for sc in self.sc for k in ("rounds", "r", "finals")])
 
     def results(self) -> dict:
-        u = lambda t: [tuple(int(x) for x in row) for row in field_numpy(t.reshape(-1, 2))]
-        return {"Z": self.Z.cpu().numpy(), "Y": self.Y.cpu().numpy(), "R": self.R.cpu().numpy(),
-                "root": bytes(self.tree[-1].cpu().numpy()), "c0": u(self.c0)[0],
-                "rounds": [u(self.rounds[i]) for i in range(self.n)], "r": u(self.r[:self.n]),
-                "finals": tuple(u(self.finals)), "state": bytes(self.state.cpu().numpy().view(np.uint8)),
-                "chal": u(self.chal[:self.n_t + self.n_o])}
+        e2 = lambda t: [tuple(int(x) for x in row) for row in field_numpy(t.reshape(-1, 2))]
+        sumchecks = []
+        for sc in self.sc:
+            n = sc["n"]
+            rounds = [e2(sc["rounds"][i]) for i in range(n)]
+            fin = e2(sc["finals"])
+            sumchecks.append({"rounds": rounds, "r": e2(sc["r"][:n]),
+                              "finals": [(fin[2 * j], fin[2 * j + 1]) for j in range(len(sc["maps"]))]})
+        paths = self.paths.cpu().numpy()
+        return {"root": bytes(self.tree[-1].cpu().numpy()), "U": field_numpy(self.U),
+                "sumchecks": sumchecks, "rho": e2(self.rho), "state": bytes(self.state.cpu().numpy()),
+                "idx": [int(v) for v in self.idx.cpu().numpy()], "columns": field_numpy(self.cols),
+                "col_salts": self.col_salts.cpu().numpy(),
+                "paths": [[bytes(paths[q, d]) for d in range(self.L + 1)] for q in range(OPEN_COLUMNS)],
+                "Y": [y.cpu().numpy() for y in self.Y], "R": [r.cpu().numpy() for r in self.R]}
 
 
 def can_pipeline(cfg) -> bool:
