@@ -82,6 +82,8 @@ def lib():
             "or_rs_eval": (u64, [vp, i32, i64]),
             "or_product_tree": (None, [vp, i64, i32, u64, vp]),
             "or_lookup_counts": (i64, [vp, i64, i32, i32, vp]),
+            "or_product_tree_field": (None, [vp, i64, i32, u64, vp]),
+            "or_pair_keys": (None, [vp, vp, i64, u64, u64, vp]),
             "or_sumcheck3": (None, [vp, vp, i32, vp, vp, vp]),
             "or_eval_deg3": (u64, [vp, u64]),
         }
@@ -384,6 +386,68 @@ def product_tree(keys: np.ndarray, L: int, gamma: int) -> list:
     return levels
 
 
+def product_tree_field(keys: np.ndarray, L: int, gamma: int) -> list:
+    """product_tree for keys that are field elements (0 past the keys)."""
+    keys = _u64(keys).reshape(-1)
+    assert keys.size <= 1 << L
+    flat = np.empty((2 << L) - 1, np.uint64)
+    lib().or_product_tree_field(_p(keys), keys.size, L, gamma % P, _p(flat))
+    levels, off = [], 0
+    for d in range(L + 1):
+        w = 1 << (L - d)
+        levels.append(flat[off:off + w])
+        off += w
+    return levels
+
+
+# The clamp's lookup ("How fast can FlashProve go", §2: a clamp is not a
+# polynomial, so its output is committed and proved by a lookup; §3.1 and its
+# footnote: the rescaled value g_w and the clamped g_k are both committed, each
+# a 16-bit value). Readings: the key of an entry is the pair (Q, Y) as
+# (Q + 2^15) + 2^16 (Y + 128); the table has one row per 16-bit q,
+# (q + 2^15) + 2^16 (clamp(q, -128, 127) + 128); Q and Y are the committed
+# tables (zero padded, so the padding keys are the row of q = 0). With Q fixed
+# by the matmul (Z = 2^s Q + R, R range-checked) and Y a byte, a key is a row
+# only if Y = clamp(Q); a Q outside 16 bits has no row.
+CLAMP_BITS = 16
+CLAMP_SCALE = 1 << 16
+CLAMP_OFFSET = (1 << 15) + (128 << 16)
+
+
+def clamp_keys(Q: np.ndarray, Y: np.ndarray) -> np.ndarray:
+    """Keys Q + 2^16 Y + 2^15 + 2^23 of field tables Q, Y (as field elements)."""
+    Q, Y = _u64(Q).reshape(-1), _u64(Y).reshape(-1)
+    assert Q.size == Y.size
+    out = np.empty(Q.size, np.uint64)
+    lib().or_pair_keys(_p(Q), _p(Y), Q.size, CLAMP_SCALE, CLAMP_OFFSET, _p(out))
+    return out
+
+
+def field_signed(a: np.ndarray) -> np.ndarray:
+    """Field elements read as signed integers (a > p/2 as a - p)."""
+    a = _u64(a)
+    return np.where(a > np.uint64(P // 2), (a - np.uint64(P)).view(np.int64), a.view(np.int64))
+
+
+def clamp_counts(Q: np.ndarray):
+    """(multiplicities of q = -2^15 + i among the Q entries, entries outside 16 bits)."""
+    q = field_signed(Q).reshape(-1) + (1 << (CLAMP_BITS - 1))
+    inside = (q >= 0) & (q < (1 << CLAMP_BITS))
+    return np.bincount(q[inside], minlength=1 << CLAMP_BITS).astype(np.int64), int((~inside).sum())
+
+
+def clamp_row(q: int) -> int:
+    return (q + (1 << 15)) + (1 << 16) * (min(max(q, -128), 127) + 128)
+
+
+def clamp_table_product(counts: np.ndarray, gamma: int) -> int:
+    """prod_q (gamma - row(q))^(m_q) over the 16-bit q."""
+    acc = 1
+    for i in np.nonzero(counts)[0]:
+        acc = acc * pow((gamma - clamp_row(int(i) - (1 << 15))) % P, int(counts[i]), P) % P
+    return acc
+
+
 def lookup_counts(keys: np.ndarray, L: int, s: int):
     """(multiplicities of t = -2^(s-1) + i among the padded keys, keys outside)."""
     keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
@@ -447,10 +511,12 @@ def grand_product_prove(levels: list, chal) -> list:
     return proof
 
 
-def grand_product_verify(root: int, proof: list, chal, L: int, keys: np.ndarray, gamma: int, counts=None, s=None):
+def grand_product_verify(root: int, proof: list, chal, L: int, keys: np.ndarray, gamma: int, counts=None, s=None,
+                         table_prod=None):
     """Verifier of the lookup: each level's round sums, the final
-    eq(z, rho) a b, the leaf claim against the keys, and (with counts) the
-    root against the table's product. Returns (reason, level)."""
+    eq(z, rho) a b, the leaf claim against the keys (int8 keys, or field
+    elements given as uint64), and (with counts) the root against the table's
+    product, or against table_prod when given. Returns (reason, level)."""
     chal = _u64(chal)
     claim = root % P
     z = []
@@ -473,13 +539,20 @@ def grand_product_verify(root: int, proof: list, chal, L: int, keys: np.ndarray,
         lam = int(chal[off])
         claim = (a + lam * (b - a)) % P
         z = [lam] + rho
-    keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
     E0 = eq_table(z)
-    dot = int(fold_rows(keys.reshape(-1, 1), E0[:keys.size])[0]) if keys.size else 0  # sum_i eq(z, i) key_i
-    leaf = (gamma - dot) % P
+    if isinstance(keys, np.ndarray) and keys.dtype == np.uint64:
+        keys = np.ascontiguousarray(keys).reshape(-1)
+        kz = int(lib().or_dot(_p(np.ascontiguousarray(E0[:keys.size])), _p(keys), keys.size)) if keys.size else 0
+    else:
+        keys = np.ascontiguousarray(keys, np.int8).reshape(-1)
+        kz = int(fold_rows(keys.reshape(-1, 1), E0[:keys.size])[0]) if keys.size else 0  # sum_i eq(z, i) key_i
+    leaf = (gamma - kz) % P
     if leaf != claim:
         return 4, 0
-    if counts is not None and table_product(counts, s, gamma) != root % P:
+    if table_prod is not None:
+        if table_prod % P != root % P:
+            return 5, L
+    elif counts is not None and table_product(counts, s, gamma) != root % P:
         return 5, L
     return 0, -1
 

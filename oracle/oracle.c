@@ -476,6 +476,22 @@ void or_product_tree(const int8_t* keys, int64_t n, int32_t L, uint64_t gamma, u
   }
 }
 
+/* The same tree for keys that are field elements (keys[i] for i < n, 0 past n). */
+void or_product_tree_field(const uint64_t* keys, int64_t n, int32_t L, uint64_t gamma, uint64_t* tree) {
+  const int64_t N = (int64_t)1 << L;
+  for (int64_t i = 0; i < N; ++i) tree[i] = or_sub(gamma, i < n ? keys[i] % OR_P : 0);
+  int64_t off = 0;
+  for (int64_t w = N; w > 1; w /= 2) {
+    for (int64_t i = 0; i < w / 2; ++i) tree[off + w + i] = or_mul(tree[off + 2 * i], tree[off + 2 * i + 1]);
+    off += w;
+  }
+}
+
+/* out[i] = A[i] + scale B[i] + offset: a pair of field tables as one key each. */
+void or_pair_keys(const uint64_t* A, const uint64_t* B, int64_t n, uint64_t scale, uint64_t offset, uint64_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = or_add(or_add(A[i] % OR_P, or_mul(scale, B[i] % OR_P)), offset % OR_P);
+}
+
 /* Multiplicities of the table values t = -2^(s-1) + i, i < 2^s, among the keys
  * and the 2^L - n padding keys (value 0). Returns the number of keys outside
  * the table. */

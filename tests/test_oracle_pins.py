@@ -808,3 +808,61 @@ def test_layer_committed_single_map_and_tiny_rows():
     salts = rng.integers(0, 256, size=(2 << lay.L, 16), dtype=np.uint8)
     pr = O.prove_layer_committed([(X, W)], 1, False, salts)
     assert O.verify_layer_committed([(X, W)], 1, False, pr) == "OK"
+
+
+# ------------------------------------------------------------- clamp lookup --
+def test_clamp_rows_and_keys():
+    # the row of q encodes (q, clamp(q)) without overlap: q + 2^15 in the low 16 bits, clamp(q) + 128 above
+    for q in (-(1 << 15), -129, -128, -1, 0, 1, 127, 128, (1 << 15) - 1):
+        row = O.clamp_row(q)
+        assert row & 0xFFFF == q + (1 << 15) and row >> 16 == min(max(q, -128), 127) + 128
+    rows = {O.clamp_row(q) for q in range(-(1 << 15), 1 << 15)}
+    assert len(rows) == 1 << 16
+    # a key of committed (Q, Y) tables is the row of Q exactly when Y = clamp(Q)
+    Q = np.array([0, 5, -5, 127, 128, 3000, -129, -3000], np.int64)
+    Y = np.clip(Q, -128, 127)
+    keys = O.clamp_keys(O.field_embed(Q), O.field_embed(Y))
+    assert [int(k) for k in keys] == [O.clamp_row(int(q)) for q in Q]
+    bad = O.clamp_keys(O.field_embed(Q), O.field_embed(Y + np.array([0, 0, 0, 0, -1, 0, 0, 0])))
+    assert int(bad[4]) not in rows and all(int(b) in rows for i, b in enumerate(bad) if i != 4)
+    assert list(O.field_signed(O.field_embed(Q))) == list(Q)
+
+
+def _clamp_case(seed, L, lo=-300, hi=300):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(lo, hi, size=1 << L)
+    q[: 1 << (L - 2)] = 0  # padding-like zeros
+    return O.field_embed(q), O.field_embed(np.clip(q, -128, 127))
+
+
+def test_clamp_lookup_proof_and_negative_controls():
+    L = 9
+    Qf, Yf = _clamp_case(50, L)
+    gamma = 0x1234567890ABCDEF % P
+    chal = synth.challenges(77, O.lookup_challenges_len(L))
+    keys = O.clamp_keys(Qf, Yf)
+    levels = O.product_tree_field(keys, L, gamma)
+    # the root is the product of gamma - key over the keys (big integers)
+    acc = 1
+    for k in keys:
+        acc = acc * (gamma - int(k)) % P
+    assert int(levels[-1][0]) == acc
+    counts, outside = O.clamp_counts(Qf)
+    assert outside == 0 and counts.sum() == 1 << L
+    tp = O.clamp_table_product(counts, gamma)
+    assert tp == acc
+    proof = O.grand_product_prove(levels, chal)
+    assert O.grand_product_verify(int(levels[-1][0]), proof, chal, L, keys, gamma, table_prod=tp) == (0, -1)
+    # one clamped output off by one: the key is no row, and the multiset differs
+    Y2 = Yf.copy()
+    j = int(np.nonzero(O.field_signed(Qf) > 127)[0][0])
+    Y2[j] = O.field_embed(np.array([126]))[0]
+    keys2 = O.clamp_keys(Qf, Y2)
+    lev2 = O.product_tree_field(keys2, L, gamma)
+    p2 = O.grand_product_prove(lev2, chal)
+    assert O.grand_product_verify(int(lev2[-1][0]), p2, chal, L, keys2, gamma, table_prod=tp) == (5, L)
+    # keys other than the tree's leaves fail the leaf opening
+    assert O.grand_product_verify(int(levels[-1][0]), proof, chal, L, keys2, gamma, table_prod=tp) == (4, 0)
+    # a Q outside 16 bits has no row
+    Q3 = O.field_embed(np.array([1 << 15, -(1 << 15) - 1, 7]))
+    assert O.clamp_counts(Q3)[1] == 2
