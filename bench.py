@@ -16,9 +16,10 @@ oracle on a bounded sample of the same workload (rank 0, N=1).
 eq vectors (one pass over the weights) beside 64 one-pass folds, with its own
 roofline and oracle time; ``commitment`` measures the commitment of Y and R
 (limb packing, Reed-Solomon encoding of rows of 2^22 into 2^23 by NTT, a salted
-BLAKE2b Merkle tree over the columns); ``lookup`` measures the lookup that shows
-the remainders R are small (product tree, multiplicities, a degree-3 sum-check
-per tree level); ``faithful`` (the up-projection) and ``faithful_main`` (the
+BLAKE2b Merkle tree over the columns); ``lookup`` measures the lookup that
+shows the remainders R are small (product tree, multiplicities, a degree-3
+sum-check per tree level) and, under ``clamp``, the clamp's lookup of the
+pairs (Q, Y); ``faithful`` (the up-projection) and ``faithful_main`` (the
 default workload) the layer's proof with its rescale committed (Q, R, Y) and
 every challenge over F_p[u]/(u^2 - 7) drawn from the transcript, claims opened
 from the commitment.
@@ -563,6 +564,66 @@ def lookup_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: bool) -> dic
         res["cpu_baseline"] = {"value": round(cfg.T / dt, 2), "unit": "tokens/s",
                                "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
                                "kind": "oracle", "sample": "the whole lookup of this layer's remainders, %.2f s" % dt}
+    res["clamp"] = clamp_leg(cfg, X, W, dev, timed, with_cpu)
+    return res
+
+
+def clamp_leg(cfg, X, W, dev, timed, with_cpu: bool) -> dict:
+    """The clamp's lookup over the map's committed Q and Y (zero-padded [2^n_t, 2^n_o] field tables written by
+    fp_commit_tables): the tree of gamma - ((Q + 2^15) + 2^16 (Y + 128)), the multiplicities of the 16-bit
+    table of (q, clamp(q)), and the level-by-level proof of the tree."""
+    import torch
+
+    import synth
+    import zero_knowledge_proof_amd as fp
+    m = cfg.matmuls[0]
+    Z, _, _ = fp.witness_linear(X, W, cfg.s)
+    n_t, n_o = synth.log2ceil(cfg.T), synth.log2ceil(m.d_out)
+    L = n_t + n_o
+    msg = torch.empty((3, 1 << L), dtype=torch.int64, device=dev)
+    fp.commit_tables([(Z, n_o, 0, 1, 2)], n_t, cfg.s, msg)
+    Q, Y = msg[0], msg[2]
+    gamma_h = synth.challenges(synth.data_seed(cfg.seed, 1 << 22 | 2), 1)
+    chal_h = synth.challenges(synth.data_seed(cfg.seed, 1 << 22 | 3), L * (L + 1) // 2)
+    gamma, chal = fp.to_field_tensor(gamma_h), fp.to_field_tensor(chal_h)
+    tree = torch.empty((2 << L) - 1, dtype=torch.int64, device=dev)
+    counts = torch.empty((1 << fp.CLAMP_BITS) + 1, dtype=torch.int32, device=dev)
+    rounds = torch.empty((max(1, L * (L - 1) // 2), 4), dtype=torch.int64, device=dev)
+    finals = torch.empty((L, 3), dtype=torch.int64, device=dev)
+
+    def build():
+        fp.lookup_tree_pairs(Q, Y, L, gamma, tree=tree)
+
+    def count():
+        fp.lookup_counts_field(Q, counts=counts)
+
+    def prove():
+        fp.lookup_prove(tree, L, chal, rounds=rounds, finals=finals)
+
+    def chain():
+        build()
+        count()
+        prove()
+
+    t = {"tree": timed(build), "counts": timed(count), "prove": timed(prove), "lookup": timed(chain)}
+    res = {"workload": "(Q, Y) of %s (%d x %d, padded to 2^%d entries): keys (Q + 2^15) + 2^16 (Y + 128) against "
+                       "the 2^16 rows (q, clamp(q))" % (m.name, cfg.T, m.d_out, L),
+           "ms": round(t["lookup"] * 1e3, 4), "tokens_per_s": round(cfg.T / t["lookup"], 1),
+           "phases_ms": {k: round(v * 1e3, 4) for k, v in t.items() if k != "lookup"},
+           "outside_16_bits": int(counts[-1].item())}
+    if with_cpu:
+        import oracle
+        Qh, Yh = Q.cpu().numpy().view("uint64"), Y.cpu().numpy().view("uint64")
+        c0 = time.perf_counter()
+        keys = oracle.clamp_keys(Qh, Yh)
+        lev = oracle.product_tree_field(keys, L, int(gamma_h[0]))
+        cnt, _ = oracle.clamp_counts(Qh)
+        oracle.clamp_table_product(cnt, int(gamma_h[0]))
+        oracle.grand_product_prove(lev, chal_h)
+        dt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(cfg.T / dt, 2), "unit": "tokens/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                               "kind": "oracle", "sample": "the whole clamp lookup of this map, %.2f s" % dt}
     return res
 
 

@@ -364,6 +364,21 @@ int fp_merkle_open(const fp_elem* code, int64_t ld_code, int32_t rows, int32_t l
 int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp_elem* gamma, fp_elem* tree,
                    hipStream_t stream);
 
+/* The clamp's lookup ("How fast can FlashProve go", §2: a clamp is not a
+ * polynomial, so its output is committed and proved by a lookup; §3.1: g_w and
+ * the clamped value are committed, 16-bit values). fp_lookup_tree_pairs builds
+ * the same tree over the keys A[i] + scale B[i] + offset of two field tables
+ * (for the clamp: A = Q, B = Y, scale = 2^16, offset = 2^15 + 2^23, so a key
+ * is the table row (q + 2^15) + 2^16 (clamp(q) + 128) of q = Q exactly when
+ * Y = clamp(Q)); leaves past n are gamma - 0. fp_lookup_counts_field counts
+ * field keys read as signed integers (a > p/2 as a - p): counts[v - lo] for
+ * lo <= v < lo + 2^bits (bits <= 24), counts[2^bits] for the others; counts:
+ * device, 2^bits + 1 entries, overwritten. Errors: FP_EARG, FP_ESHAPE,
+ * FP_ERANGE. */
+int fp_lookup_tree_pairs(const fp_elem* A, const fp_elem* B, int64_t n, uint64_t scale, uint64_t offset, int32_t L,
+                         const fp_elem* gamma, fp_elem* tree, hipStream_t stream);
+int fp_lookup_counts_field(const fp_elem* A, int64_t n, int64_t lo, int32_t bits, uint32_t* counts, hipStream_t stream);
+
 /* Multiplicities of the table values t = -2^(s-1) + i (i < 2^s, 1 <= s <= 8)
  * among the n keys and the 2^L - n padding keys (value 0): counts[i]; keys
  * outside the table are counted in counts[2^s]. counts: device, 2^s + 1

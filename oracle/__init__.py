@@ -414,13 +414,18 @@ CLAMP_SCALE = 1 << 16
 CLAMP_OFFSET = (1 << 15) + (128 << 16)
 
 
+def pair_keys(A: np.ndarray, B: np.ndarray, scale: int, offset: int) -> np.ndarray:
+    """Keys A + scale B + offset of two field tables."""
+    A, B = _u64(A).reshape(-1), _u64(B).reshape(-1)
+    assert A.size == B.size
+    out = np.empty(A.size, np.uint64)
+    lib().or_pair_keys(_p(A), _p(B), A.size, scale % P, offset % P, _p(out))
+    return out
+
+
 def clamp_keys(Q: np.ndarray, Y: np.ndarray) -> np.ndarray:
     """Keys Q + 2^16 Y + 2^15 + 2^23 of field tables Q, Y (as field elements)."""
-    Q, Y = _u64(Q).reshape(-1), _u64(Y).reshape(-1)
-    assert Q.size == Y.size
-    out = np.empty(Q.size, np.uint64)
-    lib().or_pair_keys(_p(Q), _p(Y), Q.size, CLAMP_SCALE, CLAMP_OFFSET, _p(out))
-    return out
+    return pair_keys(Q, Y, CLAMP_SCALE, CLAMP_OFFSET)
 
 
 def field_signed(a: np.ndarray) -> np.ndarray:

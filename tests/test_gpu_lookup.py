@@ -147,3 +147,84 @@ def test_lookup_prove_many_levels(fp):
     want = O.grand_product_prove(lev, chal)
     for (gr, gf), (wr, wf) in zip(got, want):
         assert np.array_equal(gr, np.asarray(wr, np.uint64).reshape(-1, 4)) and gf == wf
+
+
+# ------------------------------------------------------------- clamp lookup --
+@pytest.mark.parametrize("n,L", [(0, 0), (1, 0), (5, 3), (1000, 10), (70000, 17)])
+def test_lookup_tree_pairs(fp, n, L):
+    rng = np.random.default_rng(400 + L)
+    A, B = _field(rng, n), _field(rng, n)
+    scale, offset, gamma = (int(x) for x in _field(rng, 3))
+    tree = fp.lookup_tree_pairs(_f(A), _f(B), L, _f([gamma]), scale=scale, offset=offset)
+    torch.cuda.synchronize()
+    want = O.product_tree_field(O.pair_keys(A, B, scale, offset), L, gamma)
+    assert np.array_equal(_u64(tree), np.concatenate(want))
+
+
+@pytest.mark.parametrize("bits,lo", [(16, -(1 << 15)), (8, -128), (20, -(1 << 19))])
+def test_lookup_counts_field(fp, bits, lo):
+    rng = np.random.default_rng(410 + bits)
+    n = 300000
+    v = rng.integers(-300, 300, size=n)
+    v[:1000] = rng.integers(lo, lo + (1 << bits), size=1000)      # anywhere in the table, past the LDS window
+    v[1000:1100] = rng.integers(1 << 21, 1 << 30, size=100)       # outside it
+    v[1100:1110] = -rng.integers(1 << 21, 1 << 30, size=10)
+    v[1110:1112] = [lo, lo + (1 << bits) - 1]
+    A = O.field_embed(v)
+    A[1112] = np.uint64(P // 2 + 3)                                # a field element far from any integer key
+    counts = fp.lookup_counts_field(_f(A), lo=lo, bits=bits)
+    torch.cuda.synchronize()
+    got = counts.cpu().numpy().view(np.uint32).astype(np.int64)
+    sv = O.field_signed(A)
+    k = sv - lo
+    inside = (k >= 0) & (k < (1 << bits))
+    assert np.array_equal(got[:-1], np.bincount(k[inside], minlength=1 << bits)) and got[-1] == int((~inside).sum())
+
+
+@pytest.mark.parametrize("cid,shape", [(2, dict(T=24, d_in=1024, d_out=200)), (2, {})])
+def test_clamp_lookup_layer(fp, cid, shape):
+    """The clamp's lookup over a layer's committed Q and Y (the padded [2^n_t, 2^n_o] tables from the GPU
+    witness): the whole tree and the multiplicities against the oracle's from its own witness, the proof
+    accepted by its verifier with the table's product, and a clamped output changed on the device refused."""
+    cfg = synth.config(cid, **shape)
+    inp = synth.make_inputs(cfg)
+    m = cfg.matmuls[0]
+    X, W = _dev(inp[m.x]), _dev(inp[m.w])
+    Z, _, _ = fp.witness_linear(X, W, cfg.s)
+    n_t, n_o = synth.log2ceil(cfg.T), synth.log2ceil(m.d_out)
+    L = n_t + n_o
+    msg = torch.empty((3, 1 << L), dtype=torch.int64, device="cuda")  # one row per table: Q, R, Y
+    fp.commit_tables([(Z, n_o, 0, 1, 2)], n_t, cfg.s, msg)
+    Q, Y = msg[0], msg[2]
+    gamma = int(synth.challenges(1200 + L, 1)[0])
+    chal = synth.challenges(1201 + L, O.lookup_challenges_len(L))
+    tree = fp.lookup_tree_pairs(Q, Y, L, _f([gamma]))
+    counts = fp.lookup_counts_field(Q)
+    rounds, finals = fp.lookup_prove(tree, L, _f(chal))
+    torch.cuda.synchronize()
+    Zo = O.witness(inp[m.x], inp[m.w], cfg.s)[0]
+    Qo, _, Yo = O.layer_tables(Zo, cfg.s, n_t, n_o)
+    keys = O.clamp_keys(Qo, Yo)
+    lev = O.product_tree_field(keys, L, gamma)
+    assert np.array_equal(_u64(tree), np.concatenate(lev))
+    want_c, outside = O.clamp_counts(Qo)
+    got_c = counts.cpu().numpy().view(np.uint32).astype(np.int64)
+    assert outside == 0 and got_c[-1] == 0 and np.array_equal(got_c[:-1], want_c)
+    tp = O.clamp_table_product(want_c, gamma)
+    got = _split(_u64(rounds).reshape(-1, 4), _u64(finals).reshape(L, 3), L)
+    assert O.grand_product_verify(int(lev[-1][0]), got, chal, L, keys, gamma, table_prod=tp) == (0, -1)
+    if L <= 16:
+        want = O.grand_product_prove(lev, chal)
+        for (gr, gf), (wr, wf) in zip(got, want):
+            assert np.array_equal(gr, np.asarray(wr, np.uint64).reshape(-1, 4)) and gf == wf
+    # a clamped output moved by one on the device: its key is no row of the table
+    j = int(np.nonzero(O.field_signed(Qo) > 127)[0][0])
+    Y[j] = int(O.field_embed(np.array([126]))[0])
+    tree2 = fp.lookup_tree_pairs(Q, Y, L, _f([gamma]))
+    rounds2, finals2 = fp.lookup_prove(tree2, L, _f(chal))
+    torch.cuda.synchronize()
+    keys2 = keys.copy()
+    keys2[j] = O.clamp_keys(Qo[j:j + 1], O.field_embed(np.array([126])))[0]
+    got2 = _split(_u64(rounds2).reshape(-1, 4), _u64(finals2).reshape(L, 3), L)
+    root2 = int(_u64(tree2)[-1])
+    assert O.grand_product_verify(root2, got2, chal, L, keys2, gamma, table_prod=tp) == (5, L)

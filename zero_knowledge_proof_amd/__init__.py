@@ -35,7 +35,7 @@ EXPORTS = [
     "fp_witness_multi_noalloc", "fp_layer_step_multi", "fp_layer_step_multi_workspace",
     "fp_witness_grouped_packed", "fp_witness_grouped_packed_workspace",
     "fp_sumcheck_ext_fs_multi", "fp_sumcheck_ext_fs_multi_workspace", "fp_commit_tables", "fp_commit_fold_ext",
-    "fp_commit_fold_ext_workspace", "fp_merkle_open",
+    "fp_commit_fold_ext_workspace", "fp_merkle_open", "fp_lookup_tree_pairs", "fp_lookup_counts_field",
 ]
 
 _lib = None
@@ -89,7 +89,7 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise FPError("libfp.so is not built (run __graft_entry__.build()): %s" % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        vp, i32, i64, sz, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint64
         sig = {
             "fp_last_error": (ctypes.c_char_p, []),
             "fp_witness_linear": (ctypes.c_int, [vp, i64, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp]),
@@ -158,6 +158,8 @@ def lib():
             "fp_commit_fold_ext": (ctypes.c_int, [vp, i64, i32, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "fp_commit_fold_ext_workspace": (sz, [i32]),
             "fp_merkle_open": (ctypes.c_int, [vp, i64, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "fp_lookup_tree_pairs": (ctypes.c_int, [vp, vp, i64, u64, u64, i32, vp, vp, vp]),
+            "fp_lookup_counts_field": (ctypes.c_int, [vp, i64, i64, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -723,6 +725,35 @@ def lookup_tree(keys, L: int, gamma, tree=None):
     _check(lib().fp_lookup_tree(_ptr(keys) if n else None, n, L, _ptr(gamma), _ptr(tree), _stream()),
            "fp_lookup_tree")
     return tree
+
+
+CLAMP_SCALE, CLAMP_OFFSET, CLAMP_BITS = 1 << 16, (1 << 15) + (128 << 16), 16
+
+
+def lookup_tree_pairs(A, B, L: int, gamma, scale: int = CLAMP_SCALE, offset: int = CLAMP_OFFSET, tree=None):
+    """Product tree [2^(L+1) - 1] of the leaves gamma - (A + scale B + offset) of two field tables of 2^L
+    entries (by default the clamp's keys of Q = A and Y = B)."""
+    n = A.numel()
+    _need(A, torch.int64, n, "A")
+    _need(B, torch.int64, n, "B")
+    assert n <= (1 << L) and B.numel() == n
+    _need(gamma, torch.int64, 1, "gamma")
+    tree = torch.empty((2 << L) - 1, dtype=torch.int64, device=A.device) if tree is None else tree
+    _need(tree, torch.int64, (2 << L) - 1, "tree")
+    _check(lib().fp_lookup_tree_pairs(_ptr(A), _ptr(B), n, scale % P, offset % P, L, _ptr(gamma), _ptr(tree),
+                                      _stream()), "fp_lookup_tree_pairs")
+    return tree
+
+
+def lookup_counts_field(A, lo: int = -(1 << 15), bits: int = CLAMP_BITS, counts=None):
+    """Multiplicities [2^bits + 1] of the field values A read as signed integers over [lo, lo + 2^bits) (the
+    last entry: values outside)."""
+    n = A.numel()
+    _need(A, torch.int64, n, "A")
+    counts = torch.empty((1 << bits) + 1, dtype=torch.int32, device=A.device) if counts is None else counts
+    _need(counts, torch.int32, (1 << bits) + 1, "counts")
+    _check(lib().fp_lookup_counts_field(_ptr(A), n, lo, bits, _ptr(counts), _stream()), "fp_lookup_counts_field")
+    return counts
 
 
 def lookup_counts(keys, L: int, s: int, counts=None):

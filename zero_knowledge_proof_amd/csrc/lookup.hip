@@ -37,9 +37,17 @@ static_assert(SC3_TAIL == 8 * SC3_TT, "the tail starts with 8 entries per thread
 // --------------------------------------------------------------- the tree
 // Thread t takes inputs [t 2^K, (t+1) 2^K) of level `in` (or, for the leaves,
 // keys: gamma - key, 0 past n) and writes the K levels above them; with keys,
-// the leaves themselves are written first.
-template <int K, bool LEAVES>
-__global__ __launch_bounds__(LK_T) void tree_kernel(const int8_t* __restrict__ keys, int64_t n,
+// the leaves themselves are written first. MODE 0: int8 keys; MODE 1: pair
+// keys A[j] + scale B[j] + offset of two field tables; MODE 2: a level of the
+// tree as input.
+struct PairKeys {
+  const uint64_t* A;
+  const uint64_t* B;
+  uint64_t scale, offset;
+};
+
+template <int K, int MODE>
+__global__ __launch_bounds__(LK_T) void tree_kernel(const int8_t* __restrict__ keys, int64_t n, PairKeys pk,
                                                     const uint64_t* __restrict__ gamma, const uint64_t* __restrict__ in,
                                                     int64_t n_in, uint64_t* __restrict__ leaves_out,
                                                     uint64_t* __restrict__ out) {
@@ -47,13 +55,18 @@ __global__ __launch_bounds__(LK_T) void tree_kernel(const int8_t* __restrict__ k
   if (t >= (n_in >> K)) return;
   constexpr int W = 1 << K;
   uint64_t v[W];
-  if constexpr (LEAVES) {
+  if constexpr (MODE != 2) {
     const uint64_t g = *gamma;
 #pragma unroll
     for (int i = 0; i < W; ++i) {
       const int64_t j = t * W + i;
-      const int8_t k = j < n ? keys[j] : (int8_t)0;
-      v[i] = gl::sub(g, gl::from_i64(k));
+      uint64_t key = 0;
+      if constexpr (MODE == 0) {
+        key = gl::from_i64(j < n ? keys[j] : (int8_t)0);
+      } else {
+        if (j < n) key = gl::add(gl::add(pk.A[j], gl::mul(pk.scale, pk.B[j])), pk.offset);
+      }
+      v[i] = gl::sub(g, key);
     }
 #pragma unroll
     for (int i = 0; i < W; ++i) leaves_out[t * W + i] = v[i];
@@ -97,6 +110,32 @@ __global__ __launch_bounds__(256) void counts_kernel(const int8_t* __restrict__ 
   __syncthreads();
   for (int i = threadIdx.x; i <= T; i += 256)
     if (h[i]) atomicAdd(&counts[i], h[i]);
+}
+
+// Multiplicities of field keys read as signed integers (a > p/2 as a - p):
+// counts[v - lo] for lo <= v < lo + T, counts[T] for the rest. Table indices
+// [c0, c0 + win) (the window around v = 0, where a rescaled output's values
+// gather) are histogrammed in LDS per workgroup, the others go straight to the
+// global bins.
+constexpr int CF_WIN = 16384;
+__global__ __launch_bounds__(256) void counts_field_kernel(const uint64_t* __restrict__ A, int64_t n, int64_t lo,
+                                                           int64_t T, int64_t c0, int32_t win,
+                                                           uint32_t* __restrict__ counts) {
+  __shared__ uint32_t h[CF_WIN + 1];  // h[win]: keys outside the table
+  for (int i = threadIdx.x; i <= win; i += 256) h[i] = 0;
+  __syncthreads();
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
+    const uint64_t a = A[j];
+    const int64_t v = a > (gl::P >> 1) ? -(int64_t)(gl::P - a) : (int64_t)a;
+    const int64_t k = v - lo;
+    if (k < 0 || k >= T) atomicAdd(&h[win], 1u);
+    else if (k >= c0 && k < c0 + win) atomicAdd(&h[k - c0], 1u);
+    else atomicAdd(&counts[k], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < win; i += 256)
+    if (h[i]) atomicAdd(&counts[c0 + i], h[i]);
+  if (threadIdx.x == 0 && h[win]) atomicAdd(&counts[T], h[win]);
 }
 
 __global__ void counts_pad_kernel(uint32_t* counts, int32_t s, uint32_t pad) {
@@ -586,12 +625,8 @@ int64_t level_offset(int32_t L, int32_t d) { return ((int64_t)2 << L) - ((int64_
 
 }  // namespace
 
-extern "C" int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp_elem* gamma, fp_elem* tree,
-                              hipStream_t stream) {
-  const char* fn = "fp_lookup_tree";
-  if (L < 0 || L > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: L=%d outside [0, %d]", fn, L, FP_MAX_N);
-  if (n < 0 || n > ((int64_t)1 << L)) return fpi::fail(FP_ESHAPE, "%s: n=%lld outside [0, 2^L]", fn, (long long)n);
-  if (!gamma || !tree || (n > 0 && !keys)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+static int tree_launch(int mode, const int8_t* keys, int64_t n, PairKeys pk, int32_t L, const fp_elem* gamma,
+                       fp_elem* tree, hipStream_t stream) {
   // leaves, with up to LK_K levels above them
   int64_t n_in = (int64_t)1 << L;
   int k = L < LK_K ? L : LK_K;
@@ -599,13 +634,19 @@ extern "C" int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp
     const int64_t threads = n_in >> k;
     const dim3 grid((unsigned)((threads + LK_T - 1) / LK_T));
     uint64_t* out = tree + n_in;
+#define LEAF_LAUNCH(KK)                                                                                        \
+  if (mode == 0)                                                                                               \
+    hipLaunchKernelGGL((tree_kernel<KK, 0>), grid, dim3(LK_T), 0, stream, keys, n, pk, gamma, nullptr, n_in, tree, out); \
+  else                                                                                                         \
+    hipLaunchKernelGGL((tree_kernel<KK, 1>), grid, dim3(LK_T), 0, stream, keys, n, pk, gamma, nullptr, n_in, tree, out)
     switch (k) {
-      case 0: hipLaunchKernelGGL((tree_kernel<0, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
-      case 1: hipLaunchKernelGGL((tree_kernel<1, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
-      case 2: hipLaunchKernelGGL((tree_kernel<2, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
-      case 3: hipLaunchKernelGGL((tree_kernel<3, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
-      default: hipLaunchKernelGGL((tree_kernel<4, true>), grid, dim3(LK_T), 0, stream, keys, n, gamma, nullptr, n_in, tree, out); break;
+      case 0: LEAF_LAUNCH(0); break;
+      case 1: LEAF_LAUNCH(1); break;
+      case 2: LEAF_LAUNCH(2); break;
+      case 3: LEAF_LAUNCH(3); break;
+      default: LEAF_LAUNCH(4); break;
     }
+#undef LEAF_LAUNCH
     const int rc = fpi::check_launch("tree_kernel");
     if (rc) return rc;
   }
@@ -616,17 +657,58 @@ extern "C" int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp
     const uint64_t* in = tree + level_offset(L, d);
     uint64_t* out = tree + level_offset(L, d + 1);
     const dim3 grid((unsigned)(((w >> k) + LK_T - 1) / LK_T));
+    const PairKeys none{};
     switch (k) {
-      case 1: hipLaunchKernelGGL((tree_kernel<1, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
-      case 2: hipLaunchKernelGGL((tree_kernel<2, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
-      case 3: hipLaunchKernelGGL((tree_kernel<3, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
-      default: hipLaunchKernelGGL((tree_kernel<4, false>), grid, dim3(LK_T), 0, stream, nullptr, 0, nullptr, in, w, nullptr, out); break;
+      case 1: hipLaunchKernelGGL((tree_kernel<1, 2>), grid, dim3(LK_T), 0, stream, nullptr, 0, none, nullptr, in, w, nullptr, out); break;
+      case 2: hipLaunchKernelGGL((tree_kernel<2, 2>), grid, dim3(LK_T), 0, stream, nullptr, 0, none, nullptr, in, w, nullptr, out); break;
+      case 3: hipLaunchKernelGGL((tree_kernel<3, 2>), grid, dim3(LK_T), 0, stream, nullptr, 0, none, nullptr, in, w, nullptr, out); break;
+      default: hipLaunchKernelGGL((tree_kernel<4, 2>), grid, dim3(LK_T), 0, stream, nullptr, 0, none, nullptr, in, w, nullptr, out); break;
     }
     const int rc = fpi::check_launch("tree_kernel");
     if (rc) return rc;
     d += k;
   }
   return fpi::ok();
+}
+
+extern "C" int fp_lookup_tree(const int8_t* keys, int64_t n, int32_t L, const fp_elem* gamma, fp_elem* tree,
+                              hipStream_t stream) {
+  const char* fn = "fp_lookup_tree";
+  if (L < 0 || L > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: L=%d outside [0, %d]", fn, L, FP_MAX_N);
+  if (n < 0 || n > ((int64_t)1 << L)) return fpi::fail(FP_ESHAPE, "%s: n=%lld outside [0, 2^L]", fn, (long long)n);
+  if (!gamma || !tree || (n > 0 && !keys)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  return tree_launch(0, keys, n, PairKeys{}, L, gamma, tree, stream);
+}
+
+extern "C" int fp_lookup_tree_pairs(const fp_elem* A, const fp_elem* B, int64_t n, uint64_t scale, uint64_t offset,
+                                    int32_t L, const fp_elem* gamma, fp_elem* tree, hipStream_t stream) {
+  const char* fn = "fp_lookup_tree_pairs";
+  if (L < 0 || L > FP_MAX_N) return fpi::fail(FP_ESHAPE, "%s: L=%d outside [0, %d]", fn, L, FP_MAX_N);
+  if (n < 0 || n > ((int64_t)1 << L)) return fpi::fail(FP_ESHAPE, "%s: n=%lld outside [0, 2^L]", fn, (long long)n);
+  if (!gamma || !tree || (n > 0 && (!A || !B))) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const PairKeys pk{A, B, scale % gl::P, offset % gl::P};
+  return tree_launch(1, nullptr, n, pk, L, gamma, tree, stream);
+}
+
+extern "C" int fp_lookup_counts_field(const fp_elem* A, int64_t n, int64_t lo, int32_t bits, uint32_t* counts,
+                                      hipStream_t stream) {
+  const char* fn = "fp_lookup_counts_field";
+  if (bits < 1 || bits > 24) return fpi::fail(FP_ERANGE, "%s: bits=%d outside [1, 24]", fn, bits);
+  if (n < 0 || n > ((int64_t)1 << FP_MAX_N) || lo < -(1LL << 40) || lo > (1LL << 40))
+    return fpi::fail(FP_ESHAPE, "%s: n=%lld, lo=%lld", fn, (long long)n, (long long)lo);
+  if (!counts || (n > 0 && !A)) return fpi::fail(FP_EARG, "%s: null pointer", fn);
+  const int64_t T = (int64_t)1 << bits;
+  const int nbins = (int)(T + 1);
+  hipLaunchKernelGGL(counts_zero_kernel, dim3((nbins + 255) / 256), dim3(256), 0, stream, counts, nbins);
+  int rc = fpi::check_launch("counts_zero_kernel");
+  if (rc) return rc;
+  if (n == 0) return fpi::ok();
+  const int32_t win = (int32_t)std::min<int64_t>(T, CF_WIN);
+  const int64_t c0 = std::min<int64_t>(std::max<int64_t>(-lo - win / 2, 0), T - win);
+  const int64_t blocks = std::min<int64_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(counts_field_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A, n, lo, T, c0, win, counts);
+  rc = fpi::check_launch("counts_field_kernel");
+  return rc ? rc : fpi::ok();
 }
 
 extern "C" int fp_lookup_counts(const int8_t* keys, int64_t n, int32_t L, int32_t s, uint32_t* counts,
