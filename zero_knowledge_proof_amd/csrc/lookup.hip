@@ -51,20 +51,31 @@ __global__ __launch_bounds__(LK_T) void tree_kernel(const int8_t* __restrict__ k
                                                     const uint64_t* __restrict__ gamma, const uint64_t* __restrict__ in,
                                                     int64_t n_in, uint64_t* __restrict__ leaves_out,
                                                     uint64_t* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * LK_T + threadIdx.x;
-  if (t >= (n_in >> K)) return;
   constexpr int W = 1 << K;
+  // pair keys are 8-byte entries of two tables: the workgroup's LK_T W keys are formed from coalesced loads
+  // into LDS (a pad word after every W, so that the threads' runs start on different banks)
+  __shared__ uint64_t kl[MODE == 1 ? LK_T * (W + 1) : 1];
+  const int64_t t = (int64_t)blockIdx.x * LK_T + threadIdx.x;
+  if constexpr (MODE == 1) {
+    const int64_t base = (int64_t)blockIdx.x * LK_T * W;
+    for (int i = threadIdx.x; i < LK_T * W; i += LK_T) {
+      const int64_t j = base + i;
+      kl[i + i / W] = (j < n) ? gl::add(gl::add(pk.A[j], gl::mul(pk.scale, pk.B[j])), pk.offset) : 0;
+    }
+    __syncthreads();
+  }
+  if (t >= (n_in >> K)) return;
   uint64_t v[W];
   if constexpr (MODE != 2) {
     const uint64_t g = *gamma;
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      const int64_t j = t * W + i;
-      uint64_t key = 0;
+      uint64_t key;
       if constexpr (MODE == 0) {
+        const int64_t j = t * W + i;
         key = gl::from_i64(j < n ? keys[j] : (int8_t)0);
       } else {
-        if (j < n) key = gl::add(gl::add(pk.A[j], gl::mul(pk.scale, pk.B[j])), pk.offset);
+        key = kl[threadIdx.x * (W + 1) + i];
       }
       v[i] = gl::sub(g, key);
     }
