@@ -50,8 +50,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ A,
 
 // --------------------------------------------------------------------- NTT
 constexpr int NTT_MAXP = 3;   // passes (N <= 2^24)
-constexpr int TILE_C = 16;   // columns (or transforms) per workgroup (16 measured best of 8, 16, 32)
-constexpr int TILE_P = TILE_C + 1;  // LDS row pitch: a column walk touches 32 distinct banks
+// Columns (or transforms) per workgroup of a pass of 2^lp points: NTT_T / R_b, so that stage A's R_b TC
+// tasks fill the workgroup (and stage B's NTT_T / TC groups cover the R_a outputs); at least 16 (the
+// 256-point pass). The LDS tile [N_p][TC + 1] fits 256 x 17 words for every lp <= 8.
+constexpr int tile_cols(int lp) { return (256 >> (lp / 2)) < 16 ? 16 : (256 >> (lp / 2)); }
+constexpr int TILE_WORDS = 256 * 17;
 constexpr int NTT_T = 256;    // threads
 constexpr int TW_BITS = 12;   // w^e = hi[e >> 12] * lo[e & 4095]
 
@@ -128,7 +131,9 @@ __device__ __forceinline__ uint64_t w_pow(const NttArgs& a, int64_t e) {
 // (between the two register transforms) plus the pass's in-tile twiddles w_{N_p}^i.
 template <int LP>
 __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
-  __shared__ uint64_t tile[256 * TILE_P];
+  constexpr int TILE_C = tile_cols(LP), TILE_P = TILE_C + 1;  // an odd pitch: column walks spread over banks
+  static_assert((1 << LP) * TILE_P <= TILE_WORDS, "LDS tile");
+  __shared__ uint64_t tile[TILE_WORDS];
   __shared__ uint64_t twp[256];
   const int tid = threadIdx.x;
   const int row = blockIdx.x / a.blocks_per_row;
@@ -455,9 +460,10 @@ extern "C" int fp_rs_encode(const fp_elem* msg, int64_t ld_msg, int32_t rows, in
       a.dS[q] = sq;
       t += a.lN[q];
     }
+    const int tc = tile_cols(a.lN[p]);
     int64_t bpr;
-    if (!a.last) bpr = ((int64_t)1 << lT) * ((((int64_t)1 << lS) + TILE_C - 1) / TILE_C);
-    else bpr = (((int64_t)1 << lT) + TILE_C - 1) / TILE_C;
+    if (!a.last) bpr = ((int64_t)1 << lT) * ((((int64_t)1 << lS) + tc - 1) / tc);
+    else bpr = (((int64_t)1 << lT) + tc - 1) / tc;
     if (bpr * rows > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many rows", fn);
     a.blocks_per_row = (int32_t)bpr;
     const dim3 grid((unsigned)(bpr * rows));
