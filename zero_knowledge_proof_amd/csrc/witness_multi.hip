@@ -72,10 +72,10 @@ struct SumAux {
 // the claim counters come first in the workspace, the folds' counters and parts after them
 constexpr size_t CLAIM_CTR_BYTES = (size_t)MM_MAX * 64;
 
-// Tile config: NW waves of 32 TM weight rows x 32 TN tokens.
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF>
+// Tile config: NW waves of 32 TM weight rows x 32 TN tokens; SB packed K blocks per LDS stage.
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SB = 1>
 struct MCfg {
-  static constexpr int NWAVES = NW, NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
+  static constexpr int NWAVES = NW, NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK * SB;
   static constexpr int PITCH = BK + 16, CPR = BK / 16, NCB = BT * CPR, CB = (NCB + NT - 1) / NT, KS = BK / 32;
   static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
   static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8;
@@ -89,7 +89,7 @@ struct MCfg {
   static constexpr int FOLD_BYTES = CL_LIMBS * BO + 2 * FOLD_ACC_WORDS * 4;
   static constexpr int LDS_FOLD_BYTES = LDS_BYTES + FOLD_BYTES;
   static_assert(NCB % NT == 0 || NCB < NT, "X chunks: whole rounds, or fewer chunks than threads");
-  static_assert(KS == 2, "two k-steps per packed K block");
+  static_assert(KS == 2 * SB, "two k-steps per packed K block");
 };
 
 // Tile `lt` of `nt` tiles of one map (a already holds the map's arguments).
@@ -103,9 +103,11 @@ struct MCfg {
 // waves' int32 limb sums meet in LDS (exact: |sum| < 2^7 2^7 BO), and after the
 // K block's barrier wave 0 turns each column's limbs into one field value
 // sum_m 2^(7m) sum_o ... = sum_o E_o[o] W[o, k] mod p for the panel.
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int FOLDW = 0>
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int FOLDW = 0, int SB = 1>
 __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int group_o, int8_t* lds) {
-  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  static_assert(SB == 1 || SB == 2, "one or two packed K blocks per stage");
+  static_assert(!FOLDW || SB == 1, "the weight folds work per packed K block");
+  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF, SB>;
   constexpr int NT = C::NT, BO = C::BO, BT = C::BT, BK = C::BK, PITCH = C::PITCH, CPR = C::CPR, CB = C::CB;
   constexpr int KS = C::KS;
   int8_t (*sB)[BT * PITCH] = reinterpret_cast<int8_t (*)[BT * PITCH]>(lds);
@@ -118,8 +120,9 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int wo0 = wave * 32 * TM;
-  const int NS = a.wp_kb;
-  const int64_t rb_bytes = (int64_t)a.wp_kb * BK * 32;
+  const int NB = a.wp_kb;               // packed K blocks
+  const int NS = (NB + SB - 1) / SB;    // LDS stages
+  const int64_t rb_bytes = (int64_t)NB * WP_BK * 32;
   const int8_t* pw[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) pw[i] = a.W + (int64_t)min((o_base + wo0) / 32 + i, a.wp_rb - 1) * rb_bytes + lane * 16;
@@ -138,11 +141,13 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   v4i wf[PFW][TM][KS];
   v4i xr[PFX][CB];
   v4i fb[2][TN];
+  // stage st's weight fragments: k-step q of packed block st SB + q / 2 (the last block past the end)
   auto wload = [&](int slot, int st) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int q = 0; q < KS; ++q) wf[slot][i][q] = *(const v4i*)(pw[i] + (int64_t)st * (BK * 32) + 1024 * q);
+      for (int q = 0; q < KS; ++q)
+        wf[slot][i][q] = *(const v4i*)(pw[i] + (int64_t)min(st * SB + q / 2, NB - 1) * (WP_BK * 32) + 1024 * (q % 2));
   };
   // X chunks past d_in are read from column 0: they meet zero weights
   auto xload = [&](int slot, int st) {
@@ -161,7 +166,7 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   // X fragments of k-step q of LDS stage buf (lane: token r of each 32-row block,
   // the 16 bytes of k the weight fragment's lane half holds)
   auto fread = [&](int fs, int buf, int q) {
-    const int8_t* B = &sB[buf][r * PITCH + 32 * h + 16 * q];
+    const int8_t* B = &sB[buf][r * PITCH + WP_BK * (q / 2) + 32 * h + 16 * (q % 2)];
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[fs][j] = *(const v4i*)(B + 32 * j * PITCH);
   };
@@ -286,7 +291,17 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       constexpr int ss = (u + NBUF - 1) % PFX;
       sstore(ss, (u + NBUF - 1) % NBUF);
       xload(ss, min(st + NBUF - 1 + PFX, NS - 1));
-      mma(1, ws, 1);
+      if constexpr (SB == 2) {
+        fread(0, buf, 2);
+        mma(1, ws, 1);
+        fread(1, buf, 3);
+        if (st * SB + 1 < NB) {  // the stage's second packed block exists (wave-uniform)
+          mma(0, ws, 2);
+          mma(1, ws, 3);
+        }
+      } else {
+        mma(1, ws, 1);
+      }
       if constexpr (FOLDW) {
         if (fold_on) fold_block(ws, st);
       }
@@ -413,10 +428,10 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
 // tables belong to other proofs than the GEMMs (this launch's claims read eq
 // tables that are complete before it starts), so nothing in one launch waits
 // for another part of it.
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int SB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void witness_multi_kernel(
     MultiArgs ma, EqAux eq, MultiFolds mf, SumAux sa) {
-  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  using C = MCfg<NW, TM, TN, PFW, PFX, NBUF, SB>;
   static_assert(C::NT == 256 && scs::ST == 256 && foldk::FT == 256,
                 "the eq, fold and sum-check workgroups are written for 256 threads");
   constexpr int FOLD_LDS = foldk::LDS_WORDS * 4 + foldk::MAXG_ALL * 8 + 16;
@@ -459,12 +474,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   a.vecZ = d.vecZ; a.vecYR = d.vecYR;
   a.wp_rb = d.wp_rb; a.wp_kb = d.wp_kb;
   a.cEt = d.Et; a.cEo = d.Eo; a.cpart = d.cpart; a.cout = d.cout; a.cctr = d.cctr;
-  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED>(a, ma.split[m][x] + li, d.tiles_t * d.tiles_o, ma.group_o, lds);
+  multi_body<NW, TM, TN, PFW, PFX, NBUF, SCHED, 0, SB>(a, ma.split[m][x] + li, d.tiles_t * d.tiles_o, ma.group_o, lds);
 }
 
-// 256 x 128 tiles (4 waves of 64 x 128), weights 3 blocks ahead, X 3 blocks
-// ahead through 3 LDS stages.
-#define WIT_MULTI 4, 2, 4, 3, 3, 3, 0
+// 256 x 128 tiles (4 waves of 64 x 128); each LDS stage holds two packed K
+// blocks (128 bytes of k: half the barriers per product, and a row pitch of
+// 144 bytes keeps the X stores off each other's banks); weights 2 stages
+// ahead, X 1 stage ahead through 2 LDS stages.
+#define WIT_MULTI 4, 2, 4, 2, 1, 2, 0, 2
 
 // ---- groups of rows, one weight matrix each (the experts of an MoE block) --
 // Group g owns rows [row_off[g], row_off[g+1]) of X and of the outputs and its
@@ -588,10 +605,10 @@ struct MultiPlan {
 // the counters' FP_FOLD_COUNTER_BYTES even without folds);
 // one slot per GEMM wave of every map that forms a claim; each sum-check's
 // table buffers.
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int SB>
 int multi_plan(const char* fn, int32_t count, const fp_matmul_desc* mm, size_t fold_bytes, int32_t n_sc,
                const fp_sumcheck_desc* sc, MultiPlan& p) {
-  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF, SB>;
   if (count < 1 || count > MM_MAX) return fpi::fail(FP_EARG, "%s: count=%d outside [1, %d]", fn, count, MM_MAX);
   if (!mm) return fpi::fail(FP_EARG, "%s: null descs", fn);
   size_t off = CLAIM_CTR_BYTES + fpi::align_up(fold_bytes, 256);
@@ -775,12 +792,12 @@ namespace {
 
 // fp_witness_multi's checks and launch for one tile configuration; noalloc:
 // ws is the scratch array (its counters cleared first on the stream).
-template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED>
+template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int SB>
 int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_t s, int32_t group_o, int32_t n_eq,
                  const fp_eq_desc* eq, int32_t n_fold, const fp_fold_desc* folds, int32_t n_sc,
                  const fp_sumcheck_desc* sc, void* ws, size_t ws_bytes, bool noalloc, bool plan_only, size_t* need,
                  hipStream_t stream) {
-  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF>;
+  using MC = MCfg<NW, TM, TN, PFW, PFX, NBUF, SB>;
   // the folds' counters and parts follow the claims' counters
   MultiFolds mf;
   size_t fold_bytes = 0;
@@ -793,7 +810,7 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
   // calls with and without folds (its counters stay zero between calls)
   if (fold_bytes < (size_t)FP_FOLD_COUNTER_BYTES) fold_bytes = FP_FOLD_COUNTER_BYTES;
   MultiPlan p;
-  rc = multi_plan<NW, TM, TN, PFW, PFX, NBUF, SCHED>(fn, count, mm, fold_bytes, n_sc, sc, p);
+  rc = multi_plan<NW, TM, TN, PFW, PFX, NBUF, SCHED, SB>(fn, count, mm, fold_bytes, n_sc, sc, p);
   if (rc) return rc;
   if (plan_only) {
     *need = p.bytes;
@@ -900,7 +917,7 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
   }
   static_assert(sizeof(MultiArgs) + sizeof(EqAux) + sizeof(MultiFolds) + sizeof(SumAux) <= 4096,
                 "kernel arguments must fit 4 KiB");
-  hipLaunchKernelGGL((witness_multi_kernel<NW, TM, TN, PFW, PFX, NBUF, SCHED>), dim3((unsigned)grid), dim3(MC::NT), 0,
+  hipLaunchKernelGGL((witness_multi_kernel<NW, TM, TN, PFW, PFX, NBUF, SCHED, SB>), dim3((unsigned)grid), dim3(MC::NT), 0,
                      stream, ma, aux, mf, sa);
   rc = fpi::check_launch("witness_multi_kernel");
   return rc ? rc : fpi::ok();
