@@ -151,6 +151,28 @@ def test_commit_tables_and_folded_rows(fp):
         assert np.array_equal(gU[1 + k], O.e2_fold_rows(want[row0:row0 + len(Ez)], Ez)), k
 
 
+def test_commit_tables_one_column_rows(fp):
+    """Rows of one column (a map of one entry sets L = 0): the one-entry-per-thread path, every table's rows
+    against the oracle's tables."""
+    rng = np.random.default_rng(302)
+    s = 8
+    Zs = [rng.integers(-(1 << 20), 1 << 20, size=sh).astype(np.int32) for sh in ((1, 1), (2, 3), (1, 2))]
+    n_t = 1
+    n_o = [0, 2, 1]
+    rows, base = 0, []
+    for n in n_o:
+        k = 1 << (n_t + n)
+        base.append((rows, rows + k, rows + 2 * k, k))
+        rows += 3 * k
+    msg = torch.full((rows, 1), 7, dtype=torch.int64, device="cuda")
+    fp.commit_tables([(torch.from_numpy(Z).cuda(), n_o[j], *base[j][:3]) for j, Z in enumerate(Zs)], n_t, s, msg)
+    torch.cuda.synchronize()
+    got = _u64(msg).reshape(-1)
+    for j, Z in enumerate(Zs):
+        for w, tab in enumerate(O.layer_tables(Z, s, n_t, n_o[j])):
+            assert np.array_equal(got[base[j][w]:base[j][w] + base[j][3]], tab), (j, w)
+
+
 def test_merkle_open(fp):
     rng = np.random.default_rng(301)
     rows, W = 5, 64

@@ -36,23 +36,45 @@ __device__ __forceinline__ uint64_t embed(int64_t v) {
   return v < 0 ? (uint64_t)v - 0xFFFFFFFFull : (uint64_t)v;  // p + v
 }
 
-// One entry of one map's padded [2^n_t, 2^n_o] tables per thread.
+__device__ __forceinline__ void rescale_embed(int64_t z, int s, uint64_t& q, uint64_t& r, uint64_t& y) {
+  const int64_t qq = (z + ((int64_t)1 << (s - 1))) >> s;  // floor: arithmetic shift
+  const int64_t rr = z - (qq << s);
+  const int64_t yy = qq < -128 ? -128 : (qq > 127 ? 127 : qq);
+  q = embed(qq);
+  r = embed(rr);
+  y = embed(yy);
+}
+
+// V consecutive entries of one map's padded [2^n_t, 2^n_o] tables per thread.
+// With V = 2 every table has an even size, rows have an even number of
+// columns and msg is 16-byte aligned, so a thread's two entries share a row
+// and each table's pair is one 16-byte store.
+template <int V>
 __global__ __launch_bounds__(256) void tables_kernel(TabArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t e = V * ((int64_t)blockIdx.x * 256 + threadIdx.x);
   if (e >= a.start[a.count]) return;
   int m = 0;
   while (e >= a.start[m + 1]) ++m;
   const fp_table_desc& d = a.d[m];
   const int64_t i = e - a.start[m];
-  const int64_t t = i >> d.n_o, o = i & (((int64_t)1 << d.n_o) - 1);
-  const int64_t z = (t < d.T && o < d.d_out) ? (int64_t)d.Z[t * d.ldz + o] : 0;
-  const int64_t q = (z + ((int64_t)1 << (a.s - 1))) >> a.s;  // floor: arithmetic shift
-  const int64_t r = z - (q << a.s);
-  const int64_t y = q < -128 ? -128 : (q > 127 ? 127 : q);
   const int64_t row = i >> a.log_cols, col = i & (((int64_t)1 << a.log_cols) - 1);
-  a.msg[(d.row_q + row) * a.ld + col] = embed(q);
-  a.msg[(d.row_r + row) * a.ld + col] = embed(r);
-  a.msg[(d.row_y + row) * a.ld + col] = embed(y);
+  uint64_t q[V], r[V], y[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const int64_t ik = i + k;
+    const int64_t t = ik >> d.n_o, o = ik & (((int64_t)1 << d.n_o) - 1);
+    const int64_t z = (t < d.T && o < d.d_out) ? (int64_t)d.Z[t * d.ldz + o] : 0;
+    rescale_embed(z, a.s, q[k], r[k], y[k]);
+  }
+  if constexpr (V == 2) {
+    *(ulonglong2*)&a.msg[(d.row_q + row) * a.ld + col] = ulonglong2{q[0], q[1]};
+    *(ulonglong2*)&a.msg[(d.row_r + row) * a.ld + col] = ulonglong2{r[0], r[1]};
+    *(ulonglong2*)&a.msg[(d.row_y + row) * a.ld + col] = ulonglong2{y[0], y[1]};
+  } else {
+    a.msg[(d.row_q + row) * a.ld + col] = q[0];
+    a.msg[(d.row_r + row) * a.ld + col] = r[0];
+    a.msg[(d.row_y + row) * a.ld + col] = y[0];
+  }
 }
 
 // ----------------------------------------------------------- folded rows
@@ -175,7 +197,12 @@ extern "C" int fp_commit_tables(int32_t count, const fp_table_desc* d, int32_t n
   }
   const int64_t total = a.start[count];
   if (total == 0) return fpi::ok();
-  hipLaunchKernelGGL(tables_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
+  // two entries per thread (16-byte stores) when every table has an even size, the rows an even number of
+  // columns and msg is 16-byte aligned; else one
+  bool pairs = log_cols >= 1 && ld % 2 == 0 && ((uintptr_t)msg & 15) == 0;
+  for (int m = 0; m < count; ++m) pairs = pairs && ((a.start[m + 1] - a.start[m]) % 2 == 0);
+  if (pairs) hipLaunchKernelGGL(tables_kernel<2>, dim3((unsigned)((total / 2 + 255) / 256)), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(tables_kernel<1>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
   const int rc = fpi::check_launch("tables_kernel");
   return rc ? rc : fpi::ok();
 }
