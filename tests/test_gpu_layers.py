@@ -274,6 +274,15 @@ def test_full_cfg2_overlapped(fp, keep_z):
     z = O.witness_entries(X, W, ts, os_)
     _, r, y = O.rescale(z, cfg.s)
     assert np.array_equal(got["Y"][ts, os_], y) and np.array_equal(got["R"][ts, os_], r)
+    # every Y and R entry equal to a one-proof run that stores Z (its Z is checked against the oracle by
+    # test_full_cfg2: sampled entries, the rescale identity on every entry, the claim of that Z)
+    ref = make_prover(cfg, inp, ch)
+    ref.run()
+    torch.cuda.synchronize()
+    gz = ref.results()
+    assert np.array_equal(got["Y"], gz["Y"]) and np.array_equal(got["R"], gz["R"])
+    _, r_all, y_all = O.rescale(gz["Z"], cfg.s)
+    assert np.array_equal(gz["Y"], y_all) and np.array_equal(gz["R"], r_all)
 
 
 def _same_without_z(cfg, inp, ch, got_z):
