@@ -135,6 +135,45 @@ def test_argument_errors_without_gpu():
     assert L.fp_sumcheck_ext_fs(dummy, dummy, dummy, dummy, 13, dummy, dummy, dummy, dummy, None) == 2
     assert L.fp_fs_absorb(None, dummy, 4, None) == 1
     assert L.fp_eq_table_ext(dummy, 25, dummy, dummy, None) == 2
+    # committed-rescale proof: tables, folded rows, column openings, the streamed extension sum-check
+    td = (fp._TableDesc * 1)(fp._TableDesc(16, 100, 10, 100, 7, 0, 8, 16))  # d_out = 100 > 2^7 fits; T > 2^n_t?
+    assert L.fp_commit_tables(1, td, 3, 8, 7, dummy, 128, 24, None) == 2  # T = 10 > 2^3
+    assert b"map 0" in L.fp_last_error()
+    td = (fp._TableDesc * 1)(fp._TableDesc(16, 100, 8, 100, 7, 0, 8, 16))
+    assert L.fp_commit_tables(1, td, 3, 9, 7, dummy, 128, 24, None) == 3  # s = 9
+    assert L.fp_commit_tables(1, td, 3, 8, 7, dummy, 128, 23, None) == 2  # Y's 8 rows end past 23 rows
+    assert L.fp_commit_tables(1, td, 3, 8, 11, dummy, 2048, 24, None) == 2  # rows of 2^11 > the table's 2^10
+    assert L.fp_commit_tables(9, td, 3, 8, 7, dummy, 128, 24, None) == 1
+    td = (fp._TableDesc * 1)(fp._TableDesc(None, 100, 8, 100, 7, 0, 8, 16))
+    assert L.fp_commit_tables(1, td, 3, 8, 7, dummy, 128, 24, None) == 1  # null Z with entries
+    cl = (fp._OpenClaim * 2)(fp._OpenClaim(0, 8, dummy, 2, dummy, 1), fp._OpenClaim(4, 4, dummy, 2, None, 0))
+    ws = 256  # a 256-byte aligned (never dereferenced) workspace address
+    need = L.fp_commit_fold_ext_workspace(16)
+    assert need >= 16 * 32
+    assert L.fp_commit_fold_ext(dummy, 64, 16, 6, dummy, 4, 2, cl, dummy, ws, need, None) == 2  # overlap
+    assert b"claim 1" in L.fp_last_error()
+    cl = (fp._OpenClaim * 1)(fp._OpenClaim(0, 8, dummy, 2, dummy, 2))
+    assert L.fp_commit_fold_ext(dummy, 64, 16, 6, dummy, 4, 1, cl, dummy, ws, need, None) == 2  # 8 != 2^4
+    cl = (fp._OpenClaim * 1)(fp._OpenClaim(0, 8, dummy, 2, dummy, 1))
+    assert L.fp_commit_fold_ext(dummy, 64, 16, 6, dummy, 3, 1, cl, dummy, ws, need, None) == 2  # 2^3 < 16 rows
+    assert L.fp_commit_fold_ext(dummy, 64, 16, 6, dummy, 4, 1, cl, dummy, ws, need - 1, None) == 4
+    assert L.fp_commit_fold_ext(dummy, 64, 16, 6, dummy, 4, 17, cl, dummy, ws, need, None) == 1
+    assert L.fp_merkle_open(dummy, 64, 4, 7, dummy, dummy, dummy, 3, dummy, dummy, dummy, None, None) == 2  # ld < 2^7
+    assert L.fp_merkle_open(dummy, 128, 4, 7, dummy, dummy, None, 3, dummy, dummy, dummy, None, None) == 1
+    assert L.fp_merkle_open(dummy, 128, 4, 7, dummy, dummy, dummy, 0, dummy, dummy, dummy, None, None) == 0
+    arr = (ctypes.c_void_p * 9)(*([dummy] * 9))
+    assert L.fp_sumcheck_ext_fs_multi(9, arr, arr, arr, arr, None, 4, dummy, dummy, dummy, dummy, None, 0, None) == 1
+    assert L.fp_sumcheck_ext_fs_multi(2, arr, arr, arr, arr, None, 25, dummy, dummy, dummy, dummy, None, 0, None) == 2
+    need = L.fp_sumcheck_ext_fs_multi_workspace(7, 14)
+    assert need >= 7 * (1 << 19)
+    assert L.fp_sumcheck_ext_fs_multi(7, arr, arr, arr, arr, None, 14, dummy, dummy, dummy, dummy, ws, need - 1,
+                                      None) == 4
+    assert L.fp_sumcheck_ext_fs_multi_workspace(7, 0) == 0
+    # the clamp lookup: sizes and table bits
+    assert L.fp_lookup_tree_pairs(dummy, dummy, 17, 1 << 16, 0, 4, dummy, dummy, None) == 2  # n > 2^L
+    assert L.fp_lookup_tree_pairs(None, dummy, 16, 1 << 16, 0, 4, dummy, dummy, None) == 1
+    assert L.fp_lookup_counts_field(dummy, 100, -(1 << 15), 25, dummy, None) == 3
+    assert L.fp_lookup_counts_field(dummy, 100, -(1 << 15), 16, None, None) == 1
     # moe plan is host-only and runs here
     import numpy as np
     counts, offsets, perm = fp.moe_plan(np.array([2, 0, 2, 1, 0], np.int32), 4)
