@@ -16,6 +16,8 @@
 // each round's values g(0), g(1), g(2) are absorbed and r_i is read from the
 // new state before any table is bound by it, so the round chain includes one
 // BLAKE2b compression per round, computed by wave 0.
+#include <algorithm>
+
 #include "blake2b.hpp"
 #include "common.hpp"
 #include "ext.hpp"
@@ -337,12 +339,16 @@ __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restr
 
 // ------------------------------------- the multi-pair extension sum-check
 // sum_j rho_j sum_k A_j[k] B_j[k] over 2^n with up to 8 pairs, for tables too
-// large for registers: one workgroup streams every round through a workspace.
-// Round i reads T_i (the caller's base parts for i = 0, else the workspace),
-// sums each pair's terms exactly (96-bit), weighs them by rho_j, completes
-// g_i across the workgroup, lets wave 0 absorb it and read r_i, and only then
-// binds every table with r_i into T_{i+1}, which alternates between two
-// workspace buffers (pair j's A at 2j 2^(n-1), its B at (2j+1) 2^(n-1)).
+// large for registers, streamed through a workspace. T_i (the tables of round
+// i) is the caller's base parts for i = 0, else it alternates between two
+// workspace buffers (T_i in buffer (i-1) mod 2; pair j's A at 2j 2^(n-1), its
+// B at (2j+1) 2^(n-1)). While the tables are large, round i is two launches:
+// many workgroups bind T_{i-1} with r_{i-1} into T_i and sum each pair's terms
+// of round i exactly (96-bit), weighted by rho_j, into per-workgroup partials;
+// then one workgroup adds the partials, absorbs g_i and reads r_i. The rest of
+// the rounds run in one workgroup: round i reads T_i, completes g_i across the
+// workgroup, lets wave 0 absorb it and read r_i, and only then binds every
+// table with r_i into T_{i+1}.
 constexpr int SM_T = 1024;
 constexpr int SM_MAX_PAIRS = 8;
 constexpr int SM_MAXN = 24;
@@ -353,7 +359,7 @@ struct ExtScArgs {
   const uint64_t* B0[SM_MAX_PAIRS];
   const uint64_t* B1[SM_MAX_PAIRS];
   const uint64_t* rho;  // 2 n_pairs words, or NULL (all ones)
-  int32_t np, n;
+  int32_t np, n, i0;  // i0: the first round this workgroup runs (T_i0 already in the workspace)
   uint64_t* state;
   uint64_t* rounds;  // [n][3][2]
   uint64_t* r_out;   // [n][2]
@@ -371,7 +377,7 @@ __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
   uint64_t s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = a.state[i];
-  for (int i = 0; i < n; ++i) {
+  for (int i = a.i0; i < n; ++i) {
     const int64_t h = (int64_t)1 << (n - 1 - i);
     const E2* src = i > 0 ? buf[(i - 1) & 1] : nullptr;
     auto load = [&](int j, int64_t q, E2& a0, E2& a1, E2& b0, E2& b1) {
@@ -457,6 +463,92 @@ __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
   if (lane < 4) a.state[lane] = d[lane];
 }
 
+// A wide round i of the streamed sum-check (see above): workgroup b binds its
+// pairs q of T_{i-1} with r_{i-1} into T_i (i > 0) and, unless bind_only, sums
+// their round-i terms into partials[b].
+constexpr int SW_T = 256, SW_MAXB = 1024;
+__global__ __launch_bounds__(SW_T) void sc_ext_wide_kernel(ExtScArgs a, int32_t i, int32_t bind_only,
+                                                          uint64_t* __restrict__ partials) {
+  __shared__ sct::S96 red[SW_T / 64][6];
+  const int np = a.np, n = a.n, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t H = (int64_t)1 << (n - 1);
+  E2* buf[2] = {a.ws, a.ws + 2 * np * H};
+  const int64_t h = (int64_t)1 << (n - 1 - i);  // pairs per table in round i
+  const E2 rp = i > 0 ? E2{a.r_out[2 * (i - 1)], a.r_out[2 * (i - 1) + 1]} : E2{0, 0};
+  E2* dst = i > 0 ? buf[(i - 1) & 1] : nullptr;
+  const E2* prev = i > 1 ? buf[i & 1] : nullptr;  // T_{i-1} in buffer (i-2) mod 2
+  E2 g[3] = {E2{0, 0}, E2{0, 0}, E2{0, 0}};
+  for (int j = 0; j < np; ++j) {
+    sct::S96 acc[6] = {};
+    // entry e of T_{i-1} for table (j, which), from the caller's parts when i - 1 = 0
+    auto ent = [&](int which, int64_t e) -> E2 {
+      if (i == 1) return which ? E2{a.B0[j][e], a.B1[j][e]} : E2{a.A0[j][e], a.A1[j][e]};
+      return prev[(2 * j + which) * H + e];
+    };
+    for (int64_t q = (int64_t)blockIdx.x * SW_T + tid; q < h; q += (int64_t)gridDim.x * SW_T) {
+      E2 a0, a1, b0, b1;
+      if (i == 0) {
+        a0 = E2{a.A0[j][2 * q], a.A1[j][2 * q]};
+        a1 = E2{a.A0[j][2 * q + 1], a.A1[j][2 * q + 1]};
+        b0 = E2{a.B0[j][2 * q], a.B1[j][2 * q]};
+        b1 = E2{a.B0[j][2 * q + 1], a.B1[j][2 * q + 1]};
+      } else {
+        a0 = e2_lerp(ent(0, 4 * q), ent(0, 4 * q + 1), rp);
+        a1 = e2_lerp(ent(0, 4 * q + 2), ent(0, 4 * q + 3), rp);
+        b0 = e2_lerp(ent(1, 4 * q), ent(1, 4 * q + 1), rp);
+        b1 = e2_lerp(ent(1, 4 * q + 2), ent(1, 4 * q + 3), rp);
+        E2* DA = dst + 2 * j * H;
+        E2* DB = dst + (2 * j + 1) * H;
+        DA[2 * q] = a0;
+        DA[2 * q + 1] = a1;
+        DB[2 * q] = b0;
+        DB[2 * q + 1] = b1;
+      }
+      if (!bind_only) pair_terms_e2(a0, a1, b0, b1, acc);
+    }
+    if (bind_only) continue;
+    const E2 rj = a.rho ? E2{a.rho[2 * j], a.rho[2 * j + 1]} : E2{1, 0};
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      g[c] = e2_add(g[c], e2_mul(rj, E2{sct::reduce96(acc[2 * c]), sct::reduce96(acc[2 * c + 1])}));
+  }
+  if (bind_only) return;
+  sct::S96 t[6];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    t[2 * c] = sct::wave_sum96(sct::to96(g[c].a));
+    t[2 * c + 1] = sct::wave_sum96(sct::to96(g[c].b));
+  }
+  if (lane == 63)
+#pragma unroll
+    for (int c = 0; c < 6; ++c) red[wave][c] = t[c];
+  __syncthreads();
+  if (tid < 6) {
+    sct::S96 x = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < SW_T / 64; ++w) x = sct::add96(x, red[w][tid]);
+    partials[(int64_t)blockIdx.x * 6 + tid] = sct::reduce96(x);
+  }
+}
+
+// The end of a wide round i: one wave adds the workgroups' partials, absorbs
+// g_i, reads r_i and writes both out.
+__global__ __launch_bounds__(64) void sc_ext_hash_kernel(ExtScArgs a, int32_t i, int32_t nb,
+                                                         const uint64_t* __restrict__ partials) {
+  const int lane = threadIdx.x;
+  sct::S96 acc[6] = {};
+  for (int b = lane; b < nb; b += 64)
+#pragma unroll
+    for (int c = 0; c < 6; ++c) acc[c] = sct::add96(acc[c], sct::to96(partials[(int64_t)b * 6 + c]));
+  uint64_t s[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s[k] = a.state[k];
+  E2 g[3];
+  wave_g(acc, g);
+  emit_round(s, g, a.rounds, a.r_out, i, lane == 0);
+  if (lane < 4) a.state[lane] = s[lane];
+}
+
 }  // namespace
 
 extern "C" int fp_fs_init(uint8_t* state, const uint8_t* msg, int32_t nbytes, hipStream_t stream) {
@@ -525,9 +617,19 @@ extern "C" int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp
   return rc ? rc : fpi::ok();
 }
 
+// Rounds run wide before the single workgroup takes over: while the pairs' tables hold more than 2^10
+// entries in all (one workgroup's round then costs little more than its hash).
+static int ext_wide_rounds(int np, int n) {
+  int i0 = 0;
+  while (i0 < n && ((int64_t)np << (n - i0)) > (1 << 10)) ++i0;
+  return i0;
+}
+
 extern "C" size_t fp_sumcheck_ext_fs_multi_workspace(int32_t n_pairs, int32_t n) {
   if (n_pairs < 1 || n_pairs > SM_MAX_PAIRS || n < 0 || n > SM_MAXN) return 0;
-  return n == 0 ? 0 : fpi::align_up((size_t)n_pairs << (n + 5), 256);
+  if (n == 0) return 0;
+  const size_t tables = fpi::align_up((size_t)n_pairs << (n + 5), 256);
+  return tables + (ext_wide_rounds(n_pairs, n) > 0 ? (size_t)SW_MAXB * 6 * 8 : 0);
 }
 
 extern "C" int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A0, const fp_elem* const* A1,
@@ -556,11 +658,28 @@ extern "C" int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A
   a.rho = rho;
   a.np = n_pairs;
   a.n = n;
+  a.i0 = ext_wide_rounds(n_pairs, n);
   a.state = (uint64_t*)state;
   a.rounds = rounds;
   a.r_out = r;
   a.finals = finals;
   a.ws = (E2*)ws;
+  if (a.i0 > 0) {
+    uint64_t* partials = (uint64_t*)((char*)ws + fpi::align_up((size_t)n_pairs << (n + 5), 256));
+    // rounds 0 .. i0-1 wide (each: bind T_{i-1} into T_i for i > 0, sums, then the hash), then T_i0 bound
+    for (int i = 0; i <= a.i0; ++i) {
+      const int bind_only = i == a.i0;
+      const int64_t h = (int64_t)1 << (n - 1 - i);
+      const int nb = (int)std::min<int64_t>(SW_MAXB, (h + SW_T - 1) / SW_T);
+      hipLaunchKernelGGL(sc_ext_wide_kernel, dim3(nb), dim3(SW_T), 0, stream, a, i, bind_only, partials);
+      int rc = fpi::check_launch("sc_ext_wide_kernel");
+      if (rc) return rc;
+      if (bind_only) break;
+      hipLaunchKernelGGL(sc_ext_hash_kernel, dim3(1), dim3(64), 0, stream, a, i, nb, (const uint64_t*)partials);
+      rc = fpi::check_launch("sc_ext_hash_kernel");
+      if (rc) return rc;
+    }
+  }
   hipLaunchKernelGGL(sc_ext_multi_kernel, dim3(1), dim3(SM_T), 0, stream, a);
   const int rc = fpi::check_launch("sc_ext_multi_kernel");
   return rc ? rc : fpi::ok();
