@@ -458,9 +458,11 @@ int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp_elem* B0, 
  * absorbs those 6 words, takes r_i = challenge 0 of the new state (r[2i],
  * r[2i+1]) and only then binds every table. At the end finals[4j .. 4j+3] =
  * A_j(r), B_j(r) for every pair, absorbed as one message of 4 n_pairs words.
- * One workgroup streams the tables through ws
- * (fp_sumcheck_ext_fs_multi_workspace(n_pairs, n) bytes, 256-byte aligned;
- * none for n = 0). Errors: FP_EARG, FP_ESHAPE (n), FP_EWORKSPACE. */
+ * The tables stream through ws (fp_sumcheck_ext_fs_multi_workspace(n_pairs, n)
+ * bytes, 256-byte aligned; none for n = 0): while they are large a round is
+ * one launch over many workgroups for its sums and one for its transcript
+ * step, the last rounds run in one workgroup. Errors: FP_EARG, FP_ESHAPE (n),
+ * FP_EWORKSPACE. */
 int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A0, const fp_elem* const* A1,
                              const fp_elem* const* B0, const fp_elem* const* B1, const fp_elem* rho, int32_t n,
                              uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals, void* ws, size_t ws_bytes,
