@@ -321,9 +321,11 @@ int fp_commit_tables(int32_t count, const fp_table_desc* d, int32_t n_t, int32_t
  * device [n_prox][2], 2^n_prox >= rows); row 1 + k, claim k's row
  * sum_{i < nrows} eq(z, i) msg[row0 + i], z the n1 coordinates at z1 followed
  * by the n2 at z2 (device [.][2] each), nrows = 2^(n1 + n2). Claims are sorted
- * by row0 and disjoint, at most FP_MAX_OPEN_CLAIMS. ws:
- * fp_commit_fold_ext_workspace(rows) bytes, 256-byte aligned (row weights).
- * Errors: FP_EARG, FP_ESHAPE, FP_EWORKSPACE. */
+ * by row0 and disjoint, at most FP_MAX_OPEN_CLAIMS. Any canonical entries are
+ * folded exactly; entries that are 32-bit signed integers (as everywhere in
+ * the committed tables) take a cheaper path. ws:
+ * fp_commit_fold_ext_workspace(rows) bytes, 256-byte aligned (row weights and
+ * the weights' sums). Errors: FP_EARG, FP_ESHAPE, FP_EWORKSPACE. */
 #define FP_MAX_OPEN_CLAIMS 16
 typedef struct {
   int32_t row0, nrows;
@@ -459,10 +461,11 @@ int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp_elem* B0, 
  * r[2i+1]) and only then binds every table. At the end finals[4j .. 4j+3] =
  * A_j(r), B_j(r) for every pair, absorbed as one message of 4 n_pairs words.
  * The tables stream through ws (fp_sumcheck_ext_fs_multi_workspace(n_pairs, n)
- * bytes, 256-byte aligned; none for n = 0): while they are large a round is
- * one launch over many workgroups for its sums and one for its transcript
- * step, the last rounds run in one workgroup. Errors: FP_EARG, FP_ESHAPE (n),
- * FP_EWORKSPACE. */
+ * bytes, 256-byte aligned; none for n = 0): while the A tables hold more than
+ * 1024 entries in all, a round is one launch over many workgroups (each on a
+ * run of one pair's entries) for its sums and one for its transcript step;
+ * the last rounds run in one workgroup with the tables in LDS. Errors:
+ * FP_EARG, FP_ESHAPE (n), FP_EWORKSPACE. */
 int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A0, const fp_elem* const* A1,
                              const fp_elem* const* B0, const fp_elem* const* B1, const fp_elem* rho, int32_t n,
                              uint8_t* state, fp_elem* rounds, fp_elem* r, fp_elem* finals, void* ws, size_t ws_bytes,

@@ -80,7 +80,8 @@ def test_sumcheck_ext_fs(fp, n):
 
 
 @pytest.mark.parametrize("np_,n,with_rho", [(1, 0, False), (1, 3, False), (3, 1, True), (3, 9, True), (7, 6, True),
-                                            (8, 5, False), (2, 13, True), (7, 14, True)])
+                                            (8, 5, False), (2, 13, True), (7, 14, True), (1, 12, False),
+                                            (8, 8, True)])
 def test_sumcheck_ext_fs_multi(fp, np_, n, with_rho):
     rng = np.random.default_rng(200 + 10 * np_ + n)
     As = [_rand_e2(rng, 1 << n) for _ in range(np_)]
@@ -149,6 +150,50 @@ def test_commit_tables_and_folded_rows(fp):
     for k, (row0, z) in enumerate(zip((base[0][1], base[2][0]), zq)):
         Ez = O.eq_table_e2(z)
         assert np.array_equal(gU[1 + k], O.e2_fold_rows(want[row0:row0 + len(Ez)], Ez)), k
+
+
+# (rows, log2 cols, entries, claims as (row0, n1, n2))
+_FOLD_CASES = [
+    (1100, 9, "mixed", [(0, 5, 4), (600, 8, 0), (1024, 0, 6), (1090, 3, 0)]),
+    (1100, 5, "small", [(64, 3, 3), (1099, 0, 0)]),
+    (513, 3, "edge", [(0, 4, 4), (256, 2, 6), (512, 0, 0)]),
+    (7, 0, "mixed", [(1, 1, 0), (4, 0, 0)]),
+]
+
+
+@pytest.mark.parametrize("rows,L,kind,cl", _FOLD_CASES)
+def test_folded_rows_general_entries(fp, rows, L, kind, cl):
+    """Folded rows of message matrices that are not all small integers: entries on both sides of the bounds
+    +-2^31 of the small-integer sums (2^31 - 1 and 2^31, p - 2^31 and p - 2^31 - 1, p - 1, 2^63), random field
+    elements among small ones, more rows than one LDS chunk of weights, a ragged last group of rows, rows
+    narrower than a workgroup and one-row claims, against the oracle's folds."""
+    rng = np.random.default_rng(rows * 31 + L)
+    cols = 1 << L
+    m = rng.integers(-(1 << 31), 1 << 31, size=(rows, cols), dtype=np.int64)
+    M = np.where(m < 0, np.uint64(P) - (-m).astype(np.uint64), m.astype(np.uint64))
+    if kind == "mixed":
+        pick = rng.random((rows, cols)) < 0.1
+        M[pick] = rng.integers(0, P, size=int(pick.sum()), dtype=np.uint64)
+    elif kind == "edge":
+        edge = np.array([0, 1, (1 << 31) - 1, 1 << 31, P - (1 << 31), P - (1 << 31) - 1, P - 1, 1 << 63,
+                         1 << 32], np.uint64)
+        M = edge[rng.integers(0, len(edge), size=(rows, cols))]
+    n_prox = O.log2ceil(rows)
+    pts = _rand_e2(rng, n_prox + sum(a + b for _, a, b in cl))
+    chal = _f([x for p in pts for x in p]).reshape(-1, 2)
+    claims, zs, a = [], [], n_prox
+    for row0, n1, n2 in cl:
+        claims.append((row0, chal[a:a + n1], chal[a + n1:a + n1 + n2]))
+        zs.append(pts[a:a + n1 + n2])
+        a += n1 + n2
+    U = torch.empty((1 + len(cl), 2, cols), dtype=torch.int64, device="cuda")
+    fp.commit_fold_ext(_f(M).reshape(rows, cols), chal[:n_prox], claims, U)
+    torch.cuda.synchronize()
+    gU = U.cpu().numpy().view(np.uint64)
+    assert np.array_equal(gU[0], O.e2_fold_rows(M, O.eq_table_e2(pts[:n_prox])[:rows]))
+    for k, ((row0, _, _), z) in enumerate(zip(cl, zs)):
+        Ez = O.eq_table_e2(z)
+        assert np.array_equal(gU[1 + k], O.e2_fold_rows(M[row0:row0 + len(Ez)], Ez)), k
 
 
 def test_commit_tables_one_column_rows(fp):

@@ -342,16 +342,19 @@ __global__ __launch_bounds__(SE_T) void sc_ext_fs_kernel(const uint64_t* __restr
 // large for registers, streamed through a workspace. T_i (the tables of round
 // i) is the caller's base parts for i = 0, else it alternates between two
 // workspace buffers (T_i in buffer (i-1) mod 2; pair j's A at 2j 2^(n-1), its
-// B at (2j+1) 2^(n-1)). While the tables are large, round i is two launches:
-// many workgroups bind T_{i-1} with r_{i-1} into T_i and sum each pair's terms
-// of round i exactly (96-bit), weighted by rho_j, into per-workgroup partials;
-// then one workgroup adds the partials, absorbs g_i and reads r_i. The rest of
-// the rounds run in one workgroup: round i reads T_i, completes g_i across the
-// workgroup, lets wave 0 absorb it and read r_i, and only then binds every
-// table with r_i into T_{i+1}.
+// B at (2j+1) 2^(n-1)). While the tables are large (rounds before i0), round i
+// is two launches: workgroups own runs of one pair's entries, bind T_{i-1}
+// with r_{i-1} into T_i and sum their terms of round i exactly (96-bit), each
+// workgroup's sums weighted by its pair's rho_j into its partials; then one
+// wave adds the partials, absorbs g_i and reads r_i. Rounds i0 onwards run in
+// one workgroup with the tables in LDS (T_i0, bound from T_{i0-1} on the way
+// in): round i lets every pair of entries of every table add its terms,
+// completes g_i across the workgroup, lets wave 0 absorb it and read r_i, and
+// only then binds the pairs in place.
 constexpr int SM_T = 1024;
 constexpr int SM_MAX_PAIRS = 8;
 constexpr int SM_MAXN = 24;
+constexpr int SM_LDS_ENTRIES = 1024;  // entries of all A tables (and of all B) at round i0
 
 struct ExtScArgs {
   const uint64_t* A0[SM_MAX_PAIRS];
@@ -359,7 +362,7 @@ struct ExtScArgs {
   const uint64_t* B0[SM_MAX_PAIRS];
   const uint64_t* B1[SM_MAX_PAIRS];
   const uint64_t* rho;  // 2 n_pairs words, or NULL (all ones)
-  int32_t np, n, i0;  // i0: the first round this workgroup runs (T_i0 already in the workspace)
+  int32_t np, n, i0;  // i0: the first round of the workgroup (n_pairs 2^(n - i0) <= SM_LDS_ENTRIES)
   uint64_t* state;
   uint64_t* rounds;  // [n][3][2]
   uint64_t* r_out;   // [n][2]
@@ -367,52 +370,68 @@ struct ExtScArgs {
   E2* ws;
 };
 
+__device__ __forceinline__ E2 rho_of(const ExtScArgs& a, int j) {
+  return a.rho ? E2{a.rho[2 * j], a.rho[2 * j + 1]} : E2{1, 0};
+}
+
+// entry e of table (j, which) of T_i, i < i0, from the caller's parts (i = 0) or the workspace
+__device__ __forceinline__ E2 ext_entry(const ExtScArgs& a, int i, int j, int which, int64_t e) {
+  if (i == 0) return which ? E2{a.B0[j][e], a.B1[j][e]} : E2{a.A0[j][e], a.A1[j][e]};
+  const int64_t H = (int64_t)1 << (a.n - 1);
+  return a.ws[(int64_t)(2 * ((i - 1) & 1)) * a.np * H + (2 * j + which) * H + e];
+}
+
 __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
+  __shared__ E2 TA[SM_LDS_ENTRIES], TB[SM_LDS_ENTRIES];
   __shared__ sct::S96 red[SM_T / 64][6];
   __shared__ uint64_t rsh[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int np = a.np, n = a.n;
-  const int64_t H = n > 0 ? (int64_t)1 << (n - 1) : 0;
-  E2* buf[2] = {a.ws, a.ws + 2 * np * H};
+  const int np = a.np, n = a.n, i0 = a.i0;
+  const int lh0 = n - i0;  // log2 of the entries per table at round i0
+  const int64_t H0 = (int64_t)1 << lh0;
   uint64_t s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = a.state[i];
-  for (int i = a.i0; i < n; ++i) {
-    const int64_t h = (int64_t)1 << (n - 1 - i);
-    const E2* src = i > 0 ? buf[(i - 1) & 1] : nullptr;
-    auto load = [&](int j, int64_t q, E2& a0, E2& a1, E2& b0, E2& b1) {
-      if (i == 0) {
-        a0 = E2{a.A0[j][2 * q], a.A1[j][2 * q]};
-        a1 = E2{a.A0[j][2 * q + 1], a.A1[j][2 * q + 1]};
-        b0 = E2{a.B0[j][2 * q], a.B1[j][2 * q]};
-        b1 = E2{a.B0[j][2 * q + 1], a.B1[j][2 * q + 1]};
-      } else {
-        const E2* A = src + 2 * j * H;
-        const E2* B = src + (2 * j + 1) * H;
-        a0 = A[2 * q];
-        a1 = A[2 * q + 1];
-        b0 = B[2 * q];
-        b1 = B[2 * q + 1];
-      }
-    };
-    E2 g[3] = {E2{0, 0}, E2{0, 0}, E2{0, 0}};
-    for (int j = 0; j < np; ++j) {
-      sct::S96 acc[6] = {};
-      for (int64_t q = tid; q < h; q += SM_T) {
-        E2 a0, a1, b0, b1;
-        load(j, q, a0, a1, b0, b1);
-        pair_terms_e2(a0, a1, b0, b1, acc);
-      }
-      const E2 rj = a.rho ? E2{a.rho[2 * j], a.rho[2 * j + 1]} : E2{1, 0};
-#pragma unroll
-      for (int c = 0; c < 3; ++c)
-        g[c] = e2_add(g[c], e2_mul(rj, E2{sct::reduce96(acc[2 * c]), sct::reduce96(acc[2 * c + 1])}));
+  // T_i0 into LDS: pair j's entries at j H0
+  if (i0 == 0) {
+    for (int64_t p = tid; p < np * H0; p += SM_T) {
+      const int j = (int)(p >> lh0);
+      const int64_t e = p & (H0 - 1);
+      TA[p] = ext_entry(a, 0, j, 0, e);
+      TB[p] = ext_entry(a, 0, j, 1, e);
     }
+  } else {
+    const E2 r{a.r_out[2 * (i0 - 1)], a.r_out[2 * (i0 - 1) + 1]};
+    for (int64_t p = tid; p < np * H0; p += SM_T) {
+      const int j = (int)(p >> lh0);
+      const int64_t e = p & (H0 - 1);
+      TA[p] = e2_lerp(ext_entry(a, i0 - 1, j, 0, 2 * e), ext_entry(a, i0 - 1, j, 0, 2 * e + 1), r);
+      TB[p] = e2_lerp(ext_entry(a, i0 - 1, j, 1, 2 * e), ext_entry(a, i0 - 1, j, 1, 2 * e + 1), r);
+    }
+  }
+  __syncthreads();
+  for (int i = i0; i < n; ++i) {
+    const int lh = n - 1 - i;  // log2 of the pairs of entries per table in round i
+    const bool act = tid < (np << lh);
+    const int j = act ? tid >> lh : 0;
+    const int64_t q = tid & (((int64_t)1 << lh) - 1);
+    const int64_t base = j * H0;
+    E2 a0{0, 0}, a1{0, 0}, b0{0, 0}, b1{0, 0};
+    sct::S96 acc[6] = {};
+    if (act) {
+      a0 = TA[base + 2 * q];
+      a1 = TA[base + 2 * q + 1];
+      b0 = TB[base + 2 * q];
+      b1 = TB[base + 2 * q + 1];
+      pair_terms_e2(a0, a1, b0, b1, acc);
+    }
+    const E2 rj = rho_of(a, j);
     sct::S96 t[6];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-      t[2 * c] = sct::wave_sum96(sct::to96(g[c].a));
-      t[2 * c + 1] = sct::wave_sum96(sct::to96(g[c].b));
+      const E2 g = act ? e2_mul(rj, E2{sct::reduce96(acc[2 * c]), sct::reduce96(acc[2 * c + 1])}) : E2{0, 0};
+      t[2 * c] = sct::wave_sum96(sct::to96(g.a));
+      t[2 * c + 1] = sct::wave_sum96(sct::to96(g.b));
     }
     if (lane == 63)
 #pragma unroll
@@ -435,16 +454,11 @@ __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
         rsh[1] = r.b;
       }
     }
-    __syncthreads();  // r_i known to every wave, and g_i's reads of red done
-    const E2 r{rsh[0], rsh[1]};
-    E2* dst = buf[i & 1];
-    for (int j = 0; j < np; ++j) {
-      for (int64_t q = tid; q < h; q += SM_T) {
-        E2 a0, a1, b0, b1;
-        load(j, q, a0, a1, b0, b1);
-        dst[2 * j * H + q] = e2_lerp(a0, a1, r);
-        dst[(2 * j + 1) * H + q] = e2_lerp(b0, b1, r);
-      }
+    __syncthreads();  // r_i known to every wave, and every read of round i done
+    if (act) {
+      const E2 r{rsh[0], rsh[1]};
+      TA[base + q] = e2_lerp(a0, a1, r);
+      TB[base + q] = e2_lerp(b0, b1, r);
     }
     __syncthreads();  // T_{i+1} complete before round i+1 reads it
   }
@@ -452,9 +466,7 @@ __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
   // finals A_j(r), B_j(r) of every pair, absorbed as one message
   auto fin = [&](int w) -> uint64_t {  // word w of the finals message
     const int j = w / 4, k = w % 4;
-    E2 x;
-    if (n == 0) x = k < 2 ? E2{a.A0[j][0], a.A1[j][0]} : E2{a.B0[j][0], a.B1[j][0]};
-    else x = buf[(n - 1) & 1][(2 * j + (k >= 2)) * H];
+    const E2 x = k < 2 ? TA[j * H0] : TB[j * H0];
     return (k & 1) ? x.b : x.a;
   };
   uint64_t d[4];
@@ -463,71 +475,58 @@ __global__ __launch_bounds__(SM_T) void sc_ext_multi_kernel(ExtScArgs a) {
   if (lane < 4) a.state[lane] = d[lane];
 }
 
-// A wide round i of the streamed sum-check (see above): workgroup b binds its
-// pairs q of T_{i-1} with r_{i-1} into T_i (i > 0) and, unless bind_only, sums
-// their round-i terms into partials[b].
+// A wide round i < i0 of the streamed sum-check (see above): workgroup b owns
+// pairs q of pair j = b / bpp's tables (runs of SW_T, every bpp-th); for i > 0
+// it binds them from T_{i-1} with r_{i-1} into T_i, and it writes rho_j times
+// its sums of their round-i terms into partials[b].
 constexpr int SW_T = 256, SW_MAXB = 1024;
-__global__ __launch_bounds__(SW_T) void sc_ext_wide_kernel(ExtScArgs a, int32_t i, int32_t bind_only,
+__global__ __launch_bounds__(SW_T) void sc_ext_wide_kernel(ExtScArgs a, int32_t i, int32_t bpp,
                                                           uint64_t* __restrict__ partials) {
   __shared__ sct::S96 red[SW_T / 64][6];
-  const int np = a.np, n = a.n, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = blockIdx.x / bpp, chunk = blockIdx.x % bpp;
   const int64_t H = (int64_t)1 << (n - 1);
-  E2* buf[2] = {a.ws, a.ws + 2 * np * H};
   const int64_t h = (int64_t)1 << (n - 1 - i);  // pairs per table in round i
   const E2 rp = i > 0 ? E2{a.r_out[2 * (i - 1)], a.r_out[2 * (i - 1) + 1]} : E2{0, 0};
-  E2* dst = i > 0 ? buf[(i - 1) & 1] : nullptr;
-  const E2* prev = i > 1 ? buf[i & 1] : nullptr;  // T_{i-1} in buffer (i-2) mod 2
-  E2 g[3] = {E2{0, 0}, E2{0, 0}, E2{0, 0}};
-  for (int j = 0; j < np; ++j) {
-    sct::S96 acc[6] = {};
-    // entry e of T_{i-1} for table (j, which), from the caller's parts when i - 1 = 0
-    auto ent = [&](int which, int64_t e) -> E2 {
-      if (i == 1) return which ? E2{a.B0[j][e], a.B1[j][e]} : E2{a.A0[j][e], a.A1[j][e]};
-      return prev[(2 * j + which) * H + e];
-    };
-    for (int64_t q = (int64_t)blockIdx.x * SW_T + tid; q < h; q += (int64_t)gridDim.x * SW_T) {
-      E2 a0, a1, b0, b1;
-      if (i == 0) {
-        a0 = E2{a.A0[j][2 * q], a.A1[j][2 * q]};
-        a1 = E2{a.A0[j][2 * q + 1], a.A1[j][2 * q + 1]};
-        b0 = E2{a.B0[j][2 * q], a.B1[j][2 * q]};
-        b1 = E2{a.B0[j][2 * q + 1], a.B1[j][2 * q + 1]};
-      } else {
-        a0 = e2_lerp(ent(0, 4 * q), ent(0, 4 * q + 1), rp);
-        a1 = e2_lerp(ent(0, 4 * q + 2), ent(0, 4 * q + 3), rp);
-        b0 = e2_lerp(ent(1, 4 * q), ent(1, 4 * q + 1), rp);
-        b1 = e2_lerp(ent(1, 4 * q + 2), ent(1, 4 * q + 3), rp);
-        E2* DA = dst + 2 * j * H;
-        E2* DB = dst + (2 * j + 1) * H;
-        DA[2 * q] = a0;
-        DA[2 * q + 1] = a1;
-        DB[2 * q] = b0;
-        DB[2 * q + 1] = b1;
-      }
-      if (!bind_only) pair_terms_e2(a0, a1, b0, b1, acc);
+  E2* DA = a.ws + (int64_t)(2 * ((i - 1) & 1)) * a.np * H + 2 * j * H;  // T_i's tables of pair j (i > 0)
+  E2* DB = DA + H;
+  sct::S96 acc[6] = {};
+  for (int64_t q = (int64_t)chunk * SW_T + tid; q < h; q += (int64_t)bpp * SW_T) {
+    E2 a0, a1, b0, b1;
+    if (i == 0) {
+      a0 = ext_entry(a, 0, j, 0, 2 * q);
+      a1 = ext_entry(a, 0, j, 0, 2 * q + 1);
+      b0 = ext_entry(a, 0, j, 1, 2 * q);
+      b1 = ext_entry(a, 0, j, 1, 2 * q + 1);
+    } else {
+      a0 = e2_lerp(ext_entry(a, i - 1, j, 0, 4 * q), ext_entry(a, i - 1, j, 0, 4 * q + 1), rp);
+      a1 = e2_lerp(ext_entry(a, i - 1, j, 0, 4 * q + 2), ext_entry(a, i - 1, j, 0, 4 * q + 3), rp);
+      b0 = e2_lerp(ext_entry(a, i - 1, j, 1, 4 * q), ext_entry(a, i - 1, j, 1, 4 * q + 1), rp);
+      b1 = e2_lerp(ext_entry(a, i - 1, j, 1, 4 * q + 2), ext_entry(a, i - 1, j, 1, 4 * q + 3), rp);
+      DA[2 * q] = a0;
+      DA[2 * q + 1] = a1;
+      DB[2 * q] = b0;
+      DB[2 * q + 1] = b1;
     }
-    if (bind_only) continue;
-    const E2 rj = a.rho ? E2{a.rho[2 * j], a.rho[2 * j + 1]} : E2{1, 0};
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-      g[c] = e2_add(g[c], e2_mul(rj, E2{sct::reduce96(acc[2 * c]), sct::reduce96(acc[2 * c + 1])}));
+    pair_terms_e2(a0, a1, b0, b1, acc);
   }
-  if (bind_only) return;
   sct::S96 t[6];
 #pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    t[2 * c] = sct::wave_sum96(sct::to96(g[c].a));
-    t[2 * c + 1] = sct::wave_sum96(sct::to96(g[c].b));
-  }
+  for (int c = 0; c < 6; ++c) t[c] = sct::wave_sum96(sct::to96(sct::reduce96(acc[c])));
   if (lane == 63)
 #pragma unroll
     for (int c = 0; c < 6; ++c) red[wave][c] = t[c];
   __syncthreads();
-  if (tid < 6) {
-    sct::S96 x = red[0][tid];
+  if (tid < 3) {
+    sct::S96 x0 = red[0][2 * tid], x1 = red[0][2 * tid + 1];
 #pragma unroll
-    for (int w = 1; w < SW_T / 64; ++w) x = sct::add96(x, red[w][tid]);
-    partials[(int64_t)blockIdx.x * 6 + tid] = sct::reduce96(x);
+    for (int w = 1; w < SW_T / 64; ++w) {
+      x0 = sct::add96(x0, red[w][2 * tid]);
+      x1 = sct::add96(x1, red[w][2 * tid + 1]);
+    }
+    const E2 g = e2_mul(rho_of(a, j), E2{sct::reduce96(x0), sct::reduce96(x1)});
+    partials[(int64_t)blockIdx.x * 6 + 2 * tid] = g.a;
+    partials[(int64_t)blockIdx.x * 6 + 2 * tid + 1] = g.b;
   }
 }
 
@@ -617,11 +616,12 @@ extern "C" int fp_sumcheck_ext_fs(const fp_elem* A0, const fp_elem* A1, const fp
   return rc ? rc : fpi::ok();
 }
 
-// Rounds run wide before the single workgroup takes over: while the pairs' tables hold more than 2^10
-// entries in all (one workgroup's round then costs little more than its hash).
+// Rounds run wide before the single workgroup takes over: while the pairs' A tables hold more than
+// SM_LDS_ENTRIES entries in all (the workgroup's LDS; one workgroup's round then costs little more than its
+// hash).
 static int ext_wide_rounds(int np, int n) {
   int i0 = 0;
-  while (i0 < n && ((int64_t)np << (n - i0)) > (1 << 10)) ++i0;
+  while (i0 < n && ((int64_t)np << (n - i0)) > SM_LDS_ENTRIES) ++i0;
   return i0;
 }
 
@@ -666,15 +666,14 @@ extern "C" int fp_sumcheck_ext_fs_multi(int32_t n_pairs, const fp_elem* const* A
   a.ws = (E2*)ws;
   if (a.i0 > 0) {
     uint64_t* partials = (uint64_t*)((char*)ws + fpi::align_up((size_t)n_pairs << (n + 5), 256));
-    // rounds 0 .. i0-1 wide (each: bind T_{i-1} into T_i for i > 0, sums, then the hash), then T_i0 bound
-    for (int i = 0; i <= a.i0; ++i) {
-      const int bind_only = i == a.i0;
+    // rounds 0 .. i0-1 wide: each binds T_{i-1} into T_i for i > 0 and sums its terms, then the hash
+    for (int i = 0; i < a.i0; ++i) {
       const int64_t h = (int64_t)1 << (n - 1 - i);
-      const int nb = (int)std::min<int64_t>(SW_MAXB, (h + SW_T - 1) / SW_T);
-      hipLaunchKernelGGL(sc_ext_wide_kernel, dim3(nb), dim3(SW_T), 0, stream, a, i, bind_only, partials);
+      const int bpp = (int)std::min<int64_t>(SW_MAXB / n_pairs, (h + SW_T - 1) / SW_T);
+      const int nb = n_pairs * bpp;
+      hipLaunchKernelGGL(sc_ext_wide_kernel, dim3(nb), dim3(SW_T), 0, stream, a, i, bpp, partials);
       int rc = fpi::check_launch("sc_ext_wide_kernel");
       if (rc) return rc;
-      if (bind_only) break;
       hipLaunchKernelGGL(sc_ext_hash_kernel, dim3(1), dim3(64), 0, stream, a, i, nb, (const uint64_t*)partials);
       rc = fpi::check_launch("sc_ext_hash_kernel");
       if (rc) return rc;

@@ -86,6 +86,7 @@ struct FoldArgs {
   int64_t ld;
   E2* wp;  // [rows] proximity weights
   E2* wc;  // [rows] claim weights (rows outside every claim: unused)
+  uint64_t* corr;  // [n_claims + 1][2]: 2^31 times each weight vector's sum
   uint64_t* U;
 };
 
@@ -110,37 +111,149 @@ __global__ __launch_bounds__(256) void row_weights_kernel(FoldArgs a) {
   a.wc[i] = w;
 }
 
+// The offsets of the fast sums below: corr[k] = 2^31 sum_i w_k[i] over the
+// rows of weight vector k (claims k < n_claims, the proximity weights at
+// k = n_claims), one workgroup each.
+__global__ __launch_bounds__(256) void weight_sums_kernel(FoldArgs a) {
+  __shared__ sct::S96 red[4][2];
+  const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool prox = k == a.n_claims;
+  const int64_t r0 = prox ? 0 : a.c[k].row0, r1 = prox ? a.rows : r0 + a.c[k].nrows;
+  const E2* w = prox ? a.wp : a.wc;
+  sct::S96 s0{0, 0, 0}, s1{0, 0, 0};
+  for (int64_t i = r0 + tid; i < r1; i += 256) {
+    s0 = sct::add96(s0, sct::to96(w[i].a));
+    s1 = sct::add96(s1, sct::to96(w[i].b));
+  }
+  s0 = sct::wave_sum96(s0);
+  s1 = sct::wave_sum96(s1);
+  if (lane == 63) {
+    red[wave][0] = s0;
+    red[wave][1] = s1;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    sct::S96 x = red[0][tid];
+    for (int v = 1; v < 4; ++v) x = sct::add96(x, red[v][tid]);
+    a.corr[2 * k + tid] = gl::mul(sct::reduce96(x), 0x80000000ull);
+  }
+}
+
+// A fast sum: sum_i e_i m'_i for 64-bit e_i = e0 + 2^32 e1 and 32-bit m'_i,
+// kept exactly as l + 2^64 lc + 2^32 (h + 2^64 hc).
+struct Fast {
+  uint64_t l, h;
+  uint32_t lc, hc;
+};
+
+__device__ __forceinline__ void fast_add(Fast& f, uint64_t e, uint32_t m) {
+  unsigned long long c0, c1;
+  f.l = __builtin_addcll(f.l, (uint64_t)(uint32_t)e * m, 0ull, &c0);
+  f.h = __builtin_addcll(f.h, (e >> 32) * m, 0ull, &c1);
+  f.lc += (uint32_t)c0;
+  f.hc += (uint32_t)c1;
+}
+
+// The fast sum mod p (2^64 = 2^32 - 1, 2^96 = -1), less its offset.
+__device__ __forceinline__ uint64_t fast_value(const Fast& f, uint64_t corr) {
+  uint64_t v = gl::canon(f.l);
+  v = gl::add(v, ((uint64_t)f.lc << 32) - f.lc);
+  v = gl::add(v, gl::reduce128(f.h << 32, f.h >> 32));
+  v = gl::sub(v, f.hc);
+  return gl::sub(v, corr);
+}
+
 // One column per thread: the proximity row and every claim's row at that
-// column, summed exactly (96-bit) over the rows and reduced once. Claims are
-// sorted by row0 and disjoint, so one walk down the rows serves them all.
-__global__ __launch_bounds__(256) void fold_rows_ext_kernel(FoldArgs a) {
+// column. The committed tables hold small signed integers m (|m| < 2^31), so
+// an entry v = m mod p is taken as m' = m + 2^31 in [0, 2^32): each weight
+// half times m' is one 32 x 32-bit product, summed exactly without reduction,
+// and the offset 2^31 sum_i w_i (the same for every column) is taken off at the
+// end. Any other entry is multiplied in full and summed exactly (96-bit) on
+// the side, while its m' is 2^31, which the offset cancels. The rows stream
+// through a ring of FR_D loads in flight per thread; the weights pass through
+// LDS FR_CH rows at a time. Claims are sorted by row0 and disjoint, so one walk
+// down the rows serves them all.
+constexpr int FR_T = 256, FR_D = 8, FR_CH = 512;
+static_assert(FR_CH % FR_D == 0, "weight chunks of whole groups of rows");
+
+__global__ __launch_bounds__(FR_T) void fold_rows_ext_kernel(FoldArgs a) {
+  __shared__ E2 swp[FR_CH], swc[FR_CH];
   const int64_t cols = (int64_t)1 << a.log_cols;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  sct::S96 p0{0, 0, 0}, p1{0, 0, 0}, q0{0, 0, 0}, q1{0, 0, 0};
+  const int64_t c = (int64_t)blockIdx.x * FR_T + threadIdx.x;
+  const bool live = c < cols;
+  const uint64_t* src = a.msg + (live ? c : 0);
+  const int64_t ld = a.ld, rows = a.rows;
+  Fast fp0{0, 0, 0, 0}, fp1{0, 0, 0, 0}, fq0{0, 0, 0, 0}, fq1{0, 0, 0, 0};
+  sct::S96 gp0{0, 0, 0}, gp1{0, 0, 0}, gq0{0, 0, 0}, gq1{0, 0, 0};
   int k = 0;
-  int64_t end = a.n_claims > 0 ? (int64_t)a.c[0].row0 + a.c[0].nrows : -1;
-  for (int64_t i = 0; i < a.rows; ++i) {
-    const uint64_t v = a.msg[i * a.ld + c];
-    const E2 wp = a.wp[i];
-    p0 = sct::add96(p0, sct::to96(gl::mul(wp.a, v)));
-    p1 = sct::add96(p1, sct::to96(gl::mul(wp.b, v)));
-    if (k < a.n_claims && i >= a.c[k].row0) {
-      const E2 wc = a.wc[i];
-      q0 = sct::add96(q0, sct::to96(gl::mul(wc.a, v)));
-      q1 = sct::add96(q1, sct::to96(gl::mul(wc.b, v)));
-      if (i + 1 == end) {
-        uint64_t* u = a.U + (int64_t)(1 + k) * 2 * cols;
-        u[c] = sct::reduce96(q0);
-        u[cols + c] = sct::reduce96(q1);
-        q0 = q1 = sct::S96{0, 0, 0};
+  int64_t beg = a.n_claims > 0 ? a.c[0].row0 : rows, end = a.n_claims > 0 ? beg + a.c[0].nrows : rows;
+  uint64_t nxt[FR_D];
+#pragma unroll
+  for (int d = 0; d < FR_D; ++d) nxt[d] = (live && d < rows) ? src[d * ld] : 0;
+  for (int64_t i0 = 0; i0 < rows; i0 += FR_D) {
+    if (i0 % FR_CH == 0) {
+      __syncthreads();  // the previous chunk's weights read
+      for (int t = threadIdx.x; t < FR_CH; t += FR_T) {
+        const int64_t i = i0 + t;
+        if (i < rows) {
+          swp[t] = a.wp[i];
+          swc[t] = a.wc[i];
+        }
+      }
+      __syncthreads();
+    }
+    uint64_t cur[FR_D];
+#pragma unroll
+    for (int d = 0; d < FR_D; ++d) {
+      cur[d] = nxt[d];
+      const int64_t j = i0 + FR_D + d;
+      nxt[d] = (live && j < rows) ? src[j * ld] : 0;
+    }
+#pragma unroll
+    for (int d = 0; d < FR_D; ++d) {
+      const int64_t i = i0 + d;
+      if (i >= rows) continue;  // the last group's rows past the matrix
+      const uint64_t v = cur[d];
+      const uint64_t t = v + 0x80000000ull;
+      const bool lo = t >= v && (t >> 32) == 0;  // v < 2^31
+      const bool hi = t >= gl::P;                // v in [p - 2^31, p): v - p + 2^31 = t - p
+      const uint32_t m = lo ? (uint32_t)t : (hi ? (uint32_t)(t - gl::P) : 0x80000000u);
+      const E2 wp = swp[i % FR_CH];
+      fast_add(fp0, wp.a, m);
+      fast_add(fp1, wp.b, m);
+      const bool claim = i >= beg;  // beg <= i < end
+      E2 wc{0, 0};
+      if (claim) {
+        wc = swc[i % FR_CH];
+        fast_add(fq0, wc.a, m);
+        fast_add(fq1, wc.b, m);
+      }
+      if (!(lo || hi)) {
+        gp0 = sct::add96(gp0, sct::to96(gl::mul(wp.a, v)));
+        gp1 = sct::add96(gp1, sct::to96(gl::mul(wp.b, v)));
+        if (claim) {
+          gq0 = sct::add96(gq0, sct::to96(gl::mul(wc.a, v)));
+          gq1 = sct::add96(gq1, sct::to96(gl::mul(wc.b, v)));
+        }
+      }
+      if (i + 1 == end && claim) {
+        if (live) {
+          uint64_t* u = a.U + (int64_t)(1 + k) * 2 * cols;
+          u[c] = gl::add(fast_value(fq0, a.corr[2 * k]), sct::reduce96(gq0));
+          u[cols + c] = gl::add(fast_value(fq1, a.corr[2 * k + 1]), sct::reduce96(gq1));
+        }
+        fq0 = fq1 = Fast{0, 0, 0, 0};
+        gq0 = gq1 = sct::S96{0, 0, 0};
         ++k;
-        end = k < a.n_claims ? (int64_t)a.c[k].row0 + a.c[k].nrows : -1;
+        beg = k < a.n_claims ? a.c[k].row0 : rows;
+        end = k < a.n_claims ? beg + a.c[k].nrows : rows;
       }
     }
   }
-  a.U[c] = sct::reduce96(p0);
-  a.U[cols + c] = sct::reduce96(p1);
+  if (!live) return;
+  const uint64_t* cp = a.corr + 2 * a.n_claims;
+  a.U[c] = gl::add(fast_value(fp0, cp[0]), sct::reduce96(gp0));
+  a.U[cols + c] = gl::add(fast_value(fp1, cp[1]), sct::reduce96(gp1));
 }
 
 // ------------------------------------------------------------ column opening
@@ -209,7 +322,7 @@ extern "C" int fp_commit_tables(int32_t count, const fp_table_desc* d, int32_t n
 
 extern "C" size_t fp_commit_fold_ext_workspace(int32_t rows) {
   if (rows < 0) return 0;
-  return fpi::align_up((size_t)rows * 2 * sizeof(E2), 256);
+  return fpi::align_up((size_t)rows * 2 * sizeof(E2), 256) + fpi::align_up((FP_MAX_OPEN_CLAIMS + 1) * sizeof(E2), 256);
 }
 
 extern "C" int fp_commit_fold_ext(const fp_elem* msg, int64_t ld, int32_t rows, int32_t log_cols, const fp_elem* r_prox,
@@ -247,12 +360,16 @@ extern "C" int fp_commit_fold_ext(const fp_elem* msg, int64_t ld, int32_t rows, 
   a.ld = ld;
   a.wp = (E2*)ws;
   a.wc = a.wp + rows;
+  a.corr = (uint64_t*)((char*)ws + fpi::align_up((size_t)rows * 2 * sizeof(E2), 256));
   a.U = U;
   hipLaunchKernelGGL(row_weights_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, a);
   int rc = fpi::check_launch("row_weights_kernel");
   if (rc) return rc;
+  hipLaunchKernelGGL(weight_sums_kernel, dim3((unsigned)(n_claims + 1)), dim3(256), 0, stream, a);
+  rc = fpi::check_launch("weight_sums_kernel");
+  if (rc) return rc;
   const int64_t cols = (int64_t)1 << log_cols;
-  hipLaunchKernelGGL(fold_rows_ext_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(fold_rows_ext_kernel, dim3((unsigned)((cols + FR_T - 1) / FR_T)), dim3(FR_T), 0, stream, a);
   rc = fpi::check_launch("fold_rows_ext_kernel");
   return rc ? rc : fpi::ok();
 }

@@ -268,14 +268,16 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   constexpr int L3 = (L2 % PFX == 0) ? L2 : L2 * PFX;
   constexpr int U = (L3 % NBUF == 0) ? L3 : L3 * NBUF;
   if (NS > 0) {  // d_in = 0: every output is 0
+    // The steps before block 0, without their products: step v stores X block v + NBUF - 1, loads X block
+    // v + NBUF - 1 + PFX, then weight block v + PFW, as every step of the loop does. Entering the loop with
+    // the loads in the loop's own order lets every X store wait for its own loads only (the waits at the loop
+    // head hold for both ways in); block b uses X slot b % PFX and weight slot b % PFW.
+    constexpr int V0 = (PFW > NBUF - 1 + PFX) ? PFW : NBUF - 1 + PFX;
 #pragma unroll
-    for (int p = 0; p < PFW; ++p) wload(p, min(p, NS - 1));
-#pragma unroll
-    for (int p = 0; p < PFX; ++p) xload(p, min(p, NS - 1));
-#pragma unroll
-    for (int sidx = 0; sidx < NBUF - 1; ++sidx) {
-      sstore(sidx % PFX, sidx);
-      xload(sidx % PFX, min(sidx + PFX, NS - 1));
+    for (int v = -V0; v < 0; ++v) {
+      if (v + NBUF - 1 >= 0) sstore((v + NBUF - 1) % PFX, (v + NBUF - 1) % NBUF);
+      if (v + NBUF - 1 + PFX >= 0) xload((v + NBUF - 1 + PFX) % PFX, min(v + NBUF - 1 + PFX, NS - 1));
+      if (v + PFW >= 0) wload((v + PFW) % PFW, min(v + PFW, NS - 1));
     }
     __syncthreads();
     if constexpr (NBUF >= 3) fread(0, 0, 0);
