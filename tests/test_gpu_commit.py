@@ -86,8 +86,10 @@ def _salts(rng, W):
 
 
 @pytest.mark.parametrize("rows,logw", [(0, 0), (1, 0), (1, 1), (2, 4), (3, 9), (14, 5), (15, 5), (30, 3), (2, 10),
-                                       (1, 12)])
+                                       (1, 12), (1, 17), (2, 18)])
 def test_merkle_tree(fp, rows, logw):
+    """Every node of the tree against the oracle's: widths up to 2^16 climb near the root only (up to nine levels
+    per launch), 2^17 and 2^18 first take three levels per launch while a level holds 2^17 nodes or more."""
     rng = np.random.default_rng(rows * 31 + logw)
     W = 1 << logw
     code = _field(rng, (max(rows, 1), W))[:rows]

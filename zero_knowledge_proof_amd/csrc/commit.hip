@@ -350,6 +350,55 @@ __global__ __launch_bounds__(256) void subtree_kernel(const uint64_t* __restrict
   }
 }
 
+// The levels near the root, where a level holds too few nodes to fill the chip:
+// workgroup b takes children [b 2^L, (b+1) 2^L) of level `in` (n_in digests)
+// and climbs L <= TOP_LEVELS levels with one node per thread per level (the
+// children of level 1 from memory, later ones from LDS), writing every node
+// to its level (out: the level above `in`, then the next, ...).
+constexpr int TOP_T = 256, TOP_LEVELS = 9;
+__global__ __launch_bounds__(TOP_T) void tree_top_kernel(const uint64_t* __restrict__ in, int64_t n_in, int32_t L,
+                                                        uint64_t* __restrict__ out) {
+  __shared__ uint64_t nd[TOP_T][4];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  int64_t n_level = n_in >> 1;  // nodes in the level being written
+  uint64_t* level = out;
+  for (int lev = 1; lev <= L; ++lev) {
+    const int cnt = 1 << (L - lev);  // nodes of this level in the workgroup's subtree
+    uint64_t h[8];
+    if (t < cnt) {
+      uint64_t m[16];
+      if (lev == 1) {
+        const uint64_t* c = in + ((b << L) + 2 * t) * 4;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) m[w] = c[w];
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          m[w] = nd[2 * t][w];
+          m[w + 4] = nd[2 * t + 1][w];
+        }
+      }
+#pragma unroll
+      for (int w = 8; w < 16; ++w) m[w] = 0;
+      b2_init32(h);
+      b2_compress(h, m, 64, true);
+    }
+    __syncthreads();  // this level's reads of nd done
+    if (t < cnt) {
+      uint64_t* o = level + (b * cnt + t) * 4;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        nd[t][w] = h[w];
+        o[w] = h[w];
+      }
+    }
+    __syncthreads();
+    level += n_level * 4;
+    n_level >>= 1;
+  }
+}
+
 int plan_passes(int L, int (&lN)[NTT_MAXP]) {
   const int P = (L + 7) / 8;
   for (int q = 0; q < P; ++q) lN[q] = L / P + (q < L % P ? 1 : 0);
@@ -500,19 +549,25 @@ extern "C" int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t ro
                      width, (const uint64_t*)salts, nodes);
   int rc = fpi::check_launch("leaf_kernel");
   if (rc) return rc;
-  // levels above the leaves, up to 3 per launch (a subtree of 8 children per thread)
+  // levels above the leaves: 3 per launch (a subtree of 8 children per thread) while a level holds at least
+  // 2^17 nodes, then up to TOP_LEVELS per launch (one node per thread and level)
   int64_t n_in = width;
   uint64_t* in = nodes;
   while (n_in > 1) {
-    int levels = 0;
-    while (levels < 3 && (n_in >> levels) > 1) ++levels;
-    const int64_t threads = n_in >> levels;
+    int levels;
     uint64_t* out = in + n_in * 4;
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (levels == 3) hipLaunchKernelGGL(subtree_kernel<3>, grid, dim3(256), 0, stream, in, n_in, out);
-    else if (levels == 2) hipLaunchKernelGGL(subtree_kernel<2>, grid, dim3(256), 0, stream, in, n_in, out);
-    else hipLaunchKernelGGL(subtree_kernel<1>, grid, dim3(256), 0, stream, in, n_in, out);
-    rc = fpi::check_launch("subtree_kernel");
+    if (n_in >= ((int64_t)1 << 17)) {
+      levels = 3;
+      hipLaunchKernelGGL(subtree_kernel<3>, dim3((unsigned)(((n_in >> 3) + 255) / 256)), dim3(256), 0, stream, in,
+                         n_in, out);
+      rc = fpi::check_launch("subtree_kernel");
+    } else {
+      levels = 0;
+      while (levels < TOP_LEVELS && (n_in >> levels) > 1) ++levels;
+      hipLaunchKernelGGL(tree_top_kernel, dim3((unsigned)(n_in >> levels)), dim3(TOP_T), 0, stream, in, n_in, levels,
+                         out);
+      rc = fpi::check_launch("tree_top_kernel");
+    }
     if (rc) return rc;
     // the last level this launch wrote starts after the levels before it
     uint64_t* last = out;
