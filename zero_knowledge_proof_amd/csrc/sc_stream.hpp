@@ -8,15 +8,16 @@
 // then binds A[q] <- A[2q] + r_i (A[2q+1] - A[2q]) (B likewise).
 //
 // Such a workgroup runs beside the GEMM tiles of a later proof (a chain of
-// dependent rounds occupies one compute unit, not the GPU). Rounds 0..i0-2
-// read T_i (the caller's tables for i = 0, else the workspace), sum the terms
-// of every pair weighted by rho_j exactly (96-bit), complete g_i across the
-// workgroup, and only then bind with r_i into T_{i+1}, which ping-pongs
-// between two workspace buffers: pair j's A at j 2^(n-i-1), its B at
-// (n_pairs + j) 2^(n-i-1). Round i0-1 leaves g as the tail's partial sum and
-// T_{i0-1} unbound: the tail binds it with r_{i0-1} while loading (sc_tail.hpp,
-// entry at i0). i0 is the first round after which the virtual pairs fit the
-// tail's registers.
+// dependent rounds occupies one compute unit, not the GPU). The round
+// challenges are known in advance here, so streamed round i (i < i0) forms
+// T_i and sums its terms in one pass: round 0 reads the caller's tables, round
+// i > 0 binds T_{i-1} with r_{i-1} into T_i on the way (T_i ping-pongs between
+// two workspace buffers, T_i in buffer i mod 2: pair j's A at j 2^(n-i), its B
+// at (n_pairs + j) 2^(n-i)). The terms of every pair are summed exactly
+// (96-bit) and weighted by rho_j, and g_i is completed across the workgroup.
+// Round i0-1 leaves g as the tail's partial sum and T_{i0-1} unbound: the
+// tail binds it with r_{i0-1} while loading (sc_tail.hpp, entry at i0). i0 is
+// the first round after which the virtual pairs fit the tail's registers.
 #pragma once
 #include "common.hpp"
 #include "gl.hpp"
@@ -62,6 +63,57 @@ __device__ __forceinline__ void load2(const fp_elem* p, int64_t q, uint64_t& x0,
   x1 = v.y;
 }
 
+__device__ __forceinline__ void store2(fp_elem* p, int64_t q, uint64_t x0, uint64_t x1) {
+  *reinterpret_cast<ulonglong2*>(p + 2 * q) = ulonglong2{x0, x1};
+}
+
+constexpr int SU = 4;  // pairs of entries per thread whose loads are in flight together
+
+// One pair's run of a streamed round i (see the file comment): FIRST (i = 0)
+// reads T_0's pairs of entries from the caller's tables; otherwise pair q of
+// T_i is bound from entries 4q .. 4q+3 of T_{i-1} with r_{i-1} and written to
+// the workspace in the same pass. The terms of round i are added into s.
+template <bool FIRST>
+__device__ __forceinline__ void stream_pair(const fp_elem* A, const fp_elem* B, fp_elem* DA, fp_elem* DB,
+                                            int64_t half, uint64_t rp, sct::S96& s0, sct::S96& s1, sct::S96& s2) {
+  constexpr int E = FIRST ? 2 : 4;  // entries of the source tables per pair of T_i
+  for (int64_t q0 = threadIdx.x; q0 < half; q0 += SU * ST) {
+    uint64_t a[SU][E], b[SU][E];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int64_t q = q0 + (int64_t)u * ST;
+      if (q < half) {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          load2(A, (E / 2) * q + e / 2, a[u][e], a[u][e + 1]);
+          load2(B, (E / 2) * q + e / 2, b[u][e], b[u][e + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int64_t q = q0 + (int64_t)u * ST;
+      if (q < half) {
+        uint64_t a0, a1, b0, b1, da, db;
+        if constexpr (FIRST) {
+          a0 = a[u][0];
+          a1 = a[u][1];
+          b0 = b[u][0];
+          b1 = b[u][1];
+        } else {
+          a0 = sct::bind(a[u][0], a[u][1], rp);
+          a1 = sct::bind(a[u][2], a[u][3], rp);
+          b0 = sct::bind(b[u][0], b[u][1], rp);
+          b1 = sct::bind(b[u][2], b[u][3], rp);
+          store2(DA, q, a0, a1);
+          store2(DB, q, b0, b1);
+        }
+        sct::round_terms96(a0, a1, b0, b1, s0, s1, s2, da, db);
+      }
+    }
+  }
+}
+
 // The instance, run by one workgroup of ST threads (sh: the tail's LDS).
 __device__ __forceinline__ void stream_body(const Inst& in, sct::TailLds<ST>& sh) {
   constexpr int SW = ST / 64;
@@ -71,19 +123,19 @@ __device__ __forceinline__ void stream_body(const Inst& in, sct::TailLds<ST>& sh
   fp_elem* part = in.scratch + ((int64_t)2 * np << n);
   int par = 0;
   for (int i = 0; i < i0; ++i) {
-    const int64_t m = (int64_t)1 << (n - i), half = m >> 1;
-    auto tabA = [&](int j) -> const fp_elem* { return i == 0 ? in.A[j] : buf[i & 1] + j * m; };
-    auto tabB = [&](int j) -> const fp_elem* { return i == 0 ? in.B[j] : buf[i & 1] + (np + j) * m; };
+    const int64_t m = (int64_t)1 << (n - i), half = m >> 1;  // entries of each table of T_i, its pairs
+    const uint64_t rp = i > 0 ? in.r[i - 1] : 0;
+    fp_elem* D = buf[i & 1];
+    const fp_elem* S = buf[(i - 1) & 1];  // T_{i-1} (i >= 2): 2m entries per table
     sct::S96 t0{0, 0, 0}, t1{0, 0, 0}, t2{0, 0, 0};
     for (int j = 0; j < np; ++j) {
-      const fp_elem* A = tabA(j);
-      const fp_elem* B = tabB(j);
       sct::S96 s0{0, 0, 0}, s1{0, 0, 0}, s2{0, 0, 0};
-      for (int64_t q = tid; q < half; q += ST) {
-        uint64_t a0, a1, b0, b1, da, db;
-        load2(A, q, a0, a1);
-        load2(B, q, b0, b1);
-        sct::round_terms96(a0, a1, b0, b1, s0, s1, s2, da, db);
+      if (i == 0) {
+        stream_pair<true>(in.A[j], in.B[j], nullptr, nullptr, half, 0, s0, s1, s2);
+      } else {
+        const fp_elem* A = i == 1 ? in.A[j] : S + j * 2 * m;
+        const fp_elem* B = i == 1 ? in.B[j] : S + (np + j) * 2 * m;
+        stream_pair<false>(A, B, D + j * m, D + (np + j) * m, half, rp, s0, s1, s2);
       }
       if (in.rho) sct::weigh(s0, s1, s2, in.rho[j]);
       t0 = sct::add96(t0, s0);
@@ -91,30 +143,17 @@ __device__ __forceinline__ void stream_body(const Inst& in, sct::TailLds<ST>& sh
       t2 = sct::add96(t2, s2);
     }
     uint64_t g0, g1, g2;
-    sct::block_round<SW>(t0, t1, t2, g0, g1, g2, sh.red, par);  // g_i complete in every wave
+    // g_i complete in every wave; its barrier also orders this round's writes of T_i before the next round
+    sct::block_round<SW>(t0, t1, t2, g0, g1, g2, sh.red, par);
     par ^= 1;
-    if (i + 1 < i0) {
-      if (tid == 0) sct::emit_round(in.rounds, in.claim0, i, g0, g1, g2);
-      const uint64_t ri = in.r[i];
-      fp_elem* D = buf[(i + 1) & 1];
-      for (int j = 0; j < np; ++j) {
-        const fp_elem* A = tabA(j);
-        const fp_elem* B = tabB(j);
-        fp_elem* DA = D + j * half;
-        fp_elem* DB = D + (np + j) * half;
-        for (int64_t q = tid; q < half; q += ST) {
-          uint64_t a0, a1, b0, b1;
-          load2(A, q, a0, a1);
-          load2(B, q, b0, b1);
-          DA[q] = sct::bind(a0, a1, ri);
-          DB[q] = sct::bind(b0, b1, ri);
-        }
+    if (tid == 0) {
+      if (i + 1 < i0) {
+        sct::emit_round(in.rounds, in.claim0, i, g0, g1, g2);
+      } else {
+        part[0] = g0;
+        part[1] = g1;
+        part[2] = g2;
       }
-      __syncthreads();  // T_{i+1} complete before the next round reads it
-    } else if (tid == 0) {
-      part[0] = g0;
-      part[1] = g1;
-      part[2] = g2;
     }
   }
   __syncthreads();
