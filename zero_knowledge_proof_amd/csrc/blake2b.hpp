@@ -76,6 +76,79 @@ __device__ __forceinline__ void b2_compress(uint64_t (&h)[8], const uint64_t (&m
   for (int i = 0; i < 8; ++i) h[i] ^= v[i] ^ v[i + 8];
 }
 
+// ---- one compression spread over the 4 lanes of a quad
+// Lane k of the quad holds column k of the working state (v[k], v[4+k],
+// v[8+k], v[12+k]) and the chaining words h[k], h[4+k]; the message block is
+// in LDS. The column step is one G per lane; for the diagonal step lane k
+// takes b, c, d from columns k+1, k+2, k+3 (quad permutes) and returns them
+// afterwards. A lane's four message words of round r are m[sigma_r[2k]],
+// m[sigma_r[2k+1]] (column step) and m[sigma_r[8+2k]], m[sigma_r[9+2k]]
+// (diagonal step): their indices, four nibbles per round, are packed into six
+// words per lane (B2Q_SIG). About 2.6 times fewer instructions per lane than
+// one lane's whole compression, so a chain of dependent compressions (the
+// levels near a Merkle root) waits that much less per step.
+struct B2QSig {
+  uint32_t w[4][6];
+};
+constexpr B2QSig b2q_sig() {
+  B2QSig t{};
+  for (int k = 0; k < 4; ++k)
+    for (int r = 0; r < 12; ++r) {
+      const unsigned char* s = B2_SIGMA[r];
+      const uint32_t v = s[2 * k] | (s[2 * k + 1] << 4) | (s[8 + 2 * k] << 8) | (s[9 + 2 * k] << 12);
+      t.w[k][r / 2] |= v << (16 * (r % 2));
+    }
+  return t;
+}
+constexpr B2QSig B2Q_SIG = b2q_sig();
+
+// lane k of its quad takes lane (k + ROT) mod 4's value
+template <int ROT>
+__device__ __forceinline__ uint64_t quad_rot(uint64_t x) {
+  constexpr int CTRL = ((0 + ROT) & 3) | (((1 + ROT) & 3) << 2) | (((2 + ROT) & 3) << 4) | (((3 + ROT) & 3) << 6);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t quad_pick(int k, uint64_t a0, uint64_t a1, uint64_t a2, uint64_t a3) {
+  return k == 0 ? a0 : (k == 1 ? a1 : (k == 2 ? a2 : a3));
+}
+
+// (h0, h1) = (h[k], h[4+k]) <- compress(h, m, t, last) for lane k of a quad;
+// m: the block's 16 words (LDS); every lane of the quad must take part.
+__device__ __forceinline__ void b2q_compress(uint64_t& h0, uint64_t& h1, const uint64_t* m, uint64_t t, bool last,
+                                             int k) {
+  uint32_t sg[6];
+#pragma unroll
+  for (int w = 0; w < 6; ++w)
+    sg[w] = k == 0 ? B2Q_SIG.w[0][w] : (k == 1 ? B2Q_SIG.w[1][w] : (k == 2 ? B2Q_SIG.w[2][w] : B2Q_SIG.w[3][w]));
+  uint64_t a = h0, b = h1;
+  uint64_t c = quad_pick(k, B2_IV_H[0], B2_IV_H[1], B2_IV_H[2], B2_IV_H[3]);
+  uint64_t d = quad_pick(k, B2_IV_H[4] ^ t, B2_IV_H[5], last ? ~B2_IV_H[6] : B2_IV_H[6], B2_IV_H[7]);
+#pragma unroll
+  for (int r = 0; r < 12; ++r) {
+    const uint32_t ix = sg[r / 2] >> (16 * (r % 2));
+    const uint64_t x0 = m[ix & 15], y0 = m[(ix >> 4) & 15], x1 = m[(ix >> 8) & 15], y1 = m[(ix >> 12) & 15];
+    b2_g(a, b, c, d, x0, y0);
+    b = quad_rot<1>(b);
+    c = quad_rot<2>(c);
+    d = quad_rot<3>(d);
+    b2_g(a, b, c, d, x1, y1);
+    b = quad_rot<3>(b);
+    c = quad_rot<2>(c);
+    d = quad_rot<1>(d);
+  }
+  h0 ^= a ^ c;
+  h1 ^= b ^ d;
+}
+
+// lane k's chaining words (h[k], h[4+k]) of an unkeyed 32-byte digest before its first block
+__device__ __forceinline__ void b2q_init32(int k, uint64_t& h0, uint64_t& h1) {
+  h0 = quad_pick(k, B2_IV_H[0] ^ 0x01010020ull, B2_IV_H[1], B2_IV_H[2], B2_IV_H[3]);
+  h1 = quad_pick(k, B2_IV_H[4], B2_IV_H[5], B2_IV_H[6], B2_IV_H[7]);
+}
+
 // parameter block of an unkeyed 32-byte digest: h0 ^= 0x01010000 | 32
 __device__ __forceinline__ void b2_init32(uint64_t (&h)[8]) {
 #pragma unroll

@@ -350,50 +350,51 @@ __global__ __launch_bounds__(256) void subtree_kernel(const uint64_t* __restrict
   }
 }
 
-// The levels near the root, where a level holds too few nodes to fill the chip:
-// workgroup b takes children [b 2^L, (b+1) 2^L) of level `in` (n_in digests)
-// and climbs L <= TOP_LEVELS levels with one node per thread per level (the
-// children of level 1 from memory, later ones from LDS), writing every node
-// to its level (out: the level above `in`, then the next, ...).
-constexpr int TOP_T = 256, TOP_LEVELS = 9;
+// The levels near the root, where a level holds too few nodes to fill the chip
+// and each level waits for one compression: workgroup b takes children
+// [b 2^L, (b+1) 2^L) of level `in` (n_in digests) and climbs L <= TOP_LEVELS
+// levels, each node hashed by the four lanes of a quad (b2q_compress: a
+// shorter chain per level than one lane's compression). Lane k of node q's
+// quad brings message words 2k, 2k+1 (child 2q + k/2, words 2(k%2), 2(k%2)+1:
+// from memory at level 1, later from LDS), and after the compression holds
+// digest word k, which it writes to the node's level (out: the level above
+// `in`, then the next, ...) and to LDS for the level above.
+constexpr int TOP_T = 1024, TOP_LEVELS = 9;
 __global__ __launch_bounds__(TOP_T) void tree_top_kernel(const uint64_t* __restrict__ in, int64_t n_in, int32_t L,
                                                         uint64_t* __restrict__ out) {
-  __shared__ uint64_t nd[TOP_T][4];
-  const int t = threadIdx.x;
+  __shared__ uint64_t nd[TOP_T / 4][4];   // the last level's digests of the workgroup's subtree
+  __shared__ uint64_t mq[TOP_T / 4][16];  // each quad's message block
+  const int t = threadIdx.x, q = t >> 2, k = t & 3;
   const int64_t b = blockIdx.x;
   int64_t n_level = n_in >> 1;  // nodes in the level being written
   uint64_t* level = out;
   for (int lev = 1; lev <= L; ++lev) {
-    const int cnt = 1 << (L - lev);  // nodes of this level in the workgroup's subtree
-    uint64_t h[8];
-    if (t < cnt) {
-      uint64_t m[16];
+    const int cnt = 1 << (L - lev);  // nodes of this level in the workgroup's subtree (whole quads: uniform)
+    const int ch = 2 * q + (k >> 1), w = 2 * (k & 1);
+    if (q < cnt) {
+      uint64_t x0, x1;
       if (lev == 1) {
-        const uint64_t* c = in + ((b << L) + 2 * t) * 4;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) m[w] = c[w];
+        const uint64_t* c = in + ((b << L) + ch) * 4 + w;
+        x0 = c[0];
+        x1 = c[1];
       } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          m[w] = nd[2 * t][w];
-          m[w + 4] = nd[2 * t + 1][w];
-        }
+        x0 = nd[ch][w];
+        x1 = nd[ch][w + 1];
       }
-#pragma unroll
-      for (int w = 8; w < 16; ++w) m[w] = 0;
-      b2_init32(h);
-      b2_compress(h, m, 64, true);
+      mq[q][2 * k] = x0;
+      mq[q][2 * k + 1] = x1;
+      mq[q][8 + 2 * k] = 0;
+      mq[q][9 + 2 * k] = 0;
     }
-    __syncthreads();  // this level's reads of nd done
-    if (t < cnt) {
-      uint64_t* o = level + (b * cnt + t) * 4;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        nd[t][w] = h[w];
-        o[w] = h[w];
-      }
+    __syncthreads();  // this level's blocks complete, and every read of nd done
+    if (q < cnt) {
+      uint64_t h0, h1;
+      b2q_init32(k, h0, h1);
+      b2q_compress(h0, h1, mq[q], 64, true, k);
+      nd[q][k] = h0;
+      level[(b * cnt + q) * 4 + k] = h0;
     }
-    __syncthreads();
+    __syncthreads();  // nd holds this level before the next reads it
     level += n_level * 4;
     n_level >>= 1;
   }
