@@ -135,6 +135,7 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
   static_assert((1 << LP) * TILE_P <= TILE_WORDS, "LDS tile");
   __shared__ uint64_t tile[TILE_WORDS];
   __shared__ uint64_t twp[256];
+  __shared__ uint64_t twk[256];  // a middle pass's twiddles w^(n S_p K) for the tile's one K
   const int tid = threadIdx.x;
   const int row = blockIdx.x / a.blocks_per_row;
   const int blk = blockIdx.x % a.blocks_per_row;
@@ -167,8 +168,13 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
     return b;
   };
 
-  // in-tile twiddles w_{N_p}^i = w_N^(i N / N_p)
-  for (int i = tid; i < Np; i += NTT_T) twp[i] = w_pow(a, (int64_t)i << (a.L - lp));
+  // in-tile twiddles w_{N_p}^i = w_N^(i N / N_p); in a middle pass (neither the first nor the last) every
+  // column of the tile has the same K, so its pass twiddles are one table of N_p values
+  const bool mid = p > 0 && !a.last;
+  for (int i = tid; i < Np; i += NTT_T) {
+    twp[i] = w_pow(a, (int64_t)i << (a.L - lp));
+    if (mid) twk[i] = w_pow(a, ((int64_t)i << lS) * kidx);
+  }
   __syncthreads();
 
   // ---- N_p = R_a R_b. Stage A: each task (n_b, column) loads its R_a elements
@@ -203,7 +209,10 @@ __global__ __launch_bounds__(NTT_T) void ntt_pass_kernel(NttArgs a) {
       const int n = i * Rb + nb;
       v[i] = (ok && !(a.first && n >= Np / 2)) ? src[rowbase + ((int64_t)n << sh)] : 0;
     }
-    if (p > 0 && K != 0) {
+    if (mid && K != 0) {
+#pragma unroll
+      for (int i = 0; i < Ra; ++i) v[i] = gl::mul(v[i], twk[i * Rb + nb]);
+    } else if (p > 0 && K != 0) {  // the last pass: K differs between the tile's columns
       uint64_t cur = w_pow(a, ((int64_t)nb << sh) * K);
       const uint64_t y = w_pow(a, ((int64_t)Rb << sh) * K);
 #pragma unroll
