@@ -560,7 +560,7 @@ extern "C" int fp_merkle_commit(const fp_elem* code, int64_t ld_code, int32_t ro
   int rc = fpi::check_launch("leaf_kernel");
   if (rc) return rc;
   // levels above the leaves: 3 per launch (a subtree of 8 children per thread) while a level holds at least
-  // 2^17 nodes, then up to TOP_LEVELS per launch (one node per thread and level)
+  // 2^17 nodes, then up to TOP_LEVELS per launch (one node per quad of lanes and level)
   int64_t n_in = width;
   uint64_t* in = nodes;
   while (n_in > 1) {
