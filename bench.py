@@ -91,6 +91,10 @@ def kernel_work(cfg, name: str, prover) -> tuple:
         xs = {(m.x, m.d_in) for m in mms}
         b = sum(m.d_in * m.d_out for m in mms) + sum(T * di for _, di in xs)
         return b, 0
+    if name == "fold(W/2)":  # the weights read once for two proofs' folds: half a read per step
+        xs = {(m.x, m.d_in) for m in mms}
+        b = sum(m.d_in * m.d_out for m in mms) // 2 + sum(T * di for _, di in xs)
+        return b, 0
     if name == "claim":
         return sum(4 * T * m.d_out for m in mms), 0
     if name == "sumcheck":

@@ -222,6 +222,13 @@ typedef struct {
   int32_t rows, cols, cols_pad;
   const fp_elem* E; /* device, >= rows */
   fp_elem* out;     /* device, cols_pad */
+  /* Optional, in the step launches' int8 folds only (fp_layer_step,
+   * fp_layer_step_multi): a second row-weight vector (device, >= rows) folded
+   * from the same read of M into out2 (device, cols_pad), e.g. the weight
+   * folds of two proofs of one layer. Both NULL or both set; the other calls
+   * that take fold descriptors refuse it (FP_EARG). */
+  const fp_elem* E2;
+  fp_elem* out2;
 } fp_fold_desc;
 
 /* Several folds of one dtype (descs: HOST array read during the call; the

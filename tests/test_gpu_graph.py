@@ -70,13 +70,14 @@ def test_pipelined_graph_replays(fp, cid, shape):
 
 
 @pytest.mark.parametrize("cid,shape,steps,keep_z", [(1, {}, 3, False), (2, dict(T=100, d_in=1008, d_out=700), 6, True),
-                                                    (3, dict(T=300, d=256, d_ff=1024), 3, False),
+                                                    (3, dict(T=300, d=256, d_ff=1024), 6, False),
                                                     (5, dict(T=200, d=128, d_kv=64, d_ff=320), 6, False)])
 def test_overlapped_graph_replays(fp, cid, shape, steps, keep_z):
     """Three proofs in flight recorded as a graph (one launch per step; single layers and multi-map layers):
     replays followed by the drain give the eager outputs for each of the last three proofs (each keeps its own
     outputs, its sum-check's included), with every buffer cleared between replays and eager steps in between; a
-    graph of a number of steps that is not a multiple of three is refused."""
+    graph of a number of steps that is not a multiple of the prover's period (three sets of buffers; six steps
+    for the multi-map layers, whose weight folds of two proofs run every other step) is refused."""
     cfg = synth.config(cid, **shape)
     inp = synth.make_inputs(cfg)
     ch = synth.draw_challenges(cfg, inp.get("route"))

@@ -265,6 +265,61 @@ def test_layer_step_multi_folds_claims_and_eq(fp):
         assert int(ws.buf[:512 + 16384].count_nonzero()) == 0
 
 
+def test_layer_step_two_vector_folds(fp):
+    """Folds of one int8 matrix by two row-weight vectors from one read (the weight folds of two proofs of a
+    layer): mixed with one-vector folds in the step launches (fp_layer_step_multi and fp_layer_step), ragged
+    and padded, one chunk and many, unaligned rows; both folded rows equal the oracle's on two calls in a row
+    with the arrival counters zero after each; the other fold calls and a half-given pair are refused."""
+    rng = _rng(4242)
+    job, (Y, R) = _small_map(fp, rng)
+    folds, fwant = [], []
+    for idx, (rows, cols, cp) in enumerate([(300, 1000, 1024), (1, 16, 16), (4100, 96, 128), (77, 4096, 4096),
+                                            (14336, 256, 256), (5, 5, 8), (2048, 5120, 8192), (1000, 300, 512)]):
+        M = _i8(rng, (rows, cols))
+        E, E2 = _field(rng, rows), _field(rng, rows)
+        out = torch.full((cp,), -1, dtype=torch.int64, device="cuda")
+        f = (_dev(M), fp.to_field_tensor(E), cp, out)
+        w = [O.fold_rows(M, E, cp)]
+        if idx != 3:
+            f += (fp.to_field_tensor(E2), torch.full((cp,), -1, dtype=torch.int64, device="cuda"))
+            w.append(O.fold_rows(M, E2, cp))
+        folds.append(f)
+        fwant.append(w)
+    # one workspace per entry point: their arrival counters sit at different offsets
+    wss = [fp.StepWorkspace(), fp.StepWorkspace()]
+    for call in range(4):
+        ws = wss[call % 2]
+        for f in folds:
+            for o in f[3::2]:
+                o.fill_(-1)
+        if call % 2 == 0:
+            fp.layer_step_multi([job], 8, folds=folds, ws=ws)
+        else:
+            Z = torch.empty((job.X.shape[0], job.Wp.d_out), dtype=torch.int32, device="cuda")
+            fp.layer_step(job.X, job.Wp, 8, Z, job.Y, job.R, folds=folds[:4], ws=ws)  # at most four jobs
+        torch.cuda.synchronize()
+        for f, w in zip(folds if call % 2 == 0 else folds[:4], fwant):
+            assert np.array_equal(fp.field_numpy(f[3]), w[0])
+            if len(f) > 4:
+                assert np.array_equal(fp.field_numpy(f[5]), w[1])
+        assert np.array_equal(job.Y.cpu().numpy(), Y) and np.array_equal(job.R.cpu().numpy(), R)
+        # the arrival counters: the multi launch's map counters and then the folds', or the folds' alone
+        assert int(ws.buf[:(512 if call % 2 == 0 else 0) + 16384].count_nonzero()) == 0
+    with pytest.raises(RuntimeError):
+        fp.fold_matrix_batched([folds[0]])
+    with pytest.raises(RuntimeError):
+        fp.fold_claim_batched([folds[0]], [])
+    M, E, cp, out, E2, out2 = folds[0]
+    half = fp._FoldDesc(M.data_ptr(), fp._ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(), out.data_ptr(),
+                        E2.data_ptr(), None)
+    arr = fp._multi_descs([job])
+    fd = (fp._FoldDesc * 1)(half)
+    sd = (fp._SumcheckDesc * 1)()
+    with pytest.raises(RuntimeError):
+        fp._check(fp.lib().fp_layer_step_multi(1, arr, 8, 1, 0, None, 1, fd, 0, sd, wss[0].buf.data_ptr(),
+                                               wss[0].buf.numel(), fp._stream()), "fp_layer_step_multi")
+
+
 # ------------------------------------------------ fp_witness_grouped_packed ---
 @pytest.mark.parametrize("rows,d_in,d_out,claims,keep_z,fold", [
     ([5, 0, 40, 1, 300, 33], 96, 700, True, False, True), ([1, 2, 3], 64, 256, True, True, False),

@@ -79,7 +79,17 @@ class _SumcheckDesc(ctypes.Structure):
 
 class _FoldDesc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_void_p), ("ld", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
-                ("cols_pad", ctypes.c_int32), ("E", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+                ("cols_pad", ctypes.c_int32), ("E", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("E2", ctypes.c_void_p), ("out2", ctypes.c_void_p)]
+
+
+def _fold_desc(f):
+    """(M, E, cols_pad, out) or, in the step launches, (M, E, cols_pad, out, E2, out2): M folded by E into
+    out and by E2 into out2 from one read."""
+    M, E, cp, out = f[:4]
+    E2, out2 = f[4:6] if len(f) > 4 else (None, None)
+    return _FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(), out.data_ptr(), _ptr(E2),
+                     _ptr(out2))
 
 
 def lib():
@@ -372,7 +382,7 @@ _ws_step = StepWorkspace()
 def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=(), As=(), Bs=(), r=None, rho=None,
                rounds=None, finals=None, claim0=None, ws: StepWorkspace | None = None, own_claim=None):
     """One launch: the witness and eq tables of a proof (as witness_linear_packed), the int8 folds
-    (M, E, cols_pad, out) and int32 claims (M, E_rows, E_cols, out) of another (as fold_claim_batched), and
+    (M, E, cols_pad, out[, E2, out2]) and int32 claims (M, E_rows, E_cols, out) of another (as fold_claim_batched), and
     the sum-check of a third (as sumcheck_prove over As, Bs, r; none when As is empty). own_claim =
     (E_t, E_o, out): the witness's own claim sum E_t[t] E_o[o] Z[t, o] from the accumulators (Z may then
     be None; E_t and E_o must be finished before the call)."""
@@ -381,8 +391,7 @@ def layer_step(X, Wp: PackedWeights, s: int, Z, Y, R, eq=None, folds=(), claims=
     assert X.numel() == 0 or X.stride(1) == 1, "rows must be contiguous"
     ne, eqd = _eq_descs(eq)
     nf, nc = len(folds), len(claims)
-    fd = (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
-                                              out.data_ptr()) for (M, E, cp, out) in folds])
+    fd = (_FoldDesc * max(nf, 1))(*[_fold_desc(f) for f in folds])
     cd = (_ClaimDesc * max(nc, 1))(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
                                                 Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in claims])
     ws = _ws_step if ws is None else ws
@@ -472,14 +481,14 @@ def _sc_descs(scs):
 
 def _fold_descs(folds):
     nf = len(folds)
-    return nf, (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
-                                                   out.data_ptr()) for (M, E, cp, out) in folds])
+    return nf, (_FoldDesc * max(nf, 1))(*[_fold_desc(f) for f in folds])
 
 
 def layer_step_multi(jobs, s: int, group_o: int = 1, eq=None, folds=(), sumchecks=(), ws: StepWorkspace | None = None):
     """One launch: the witness GEMMs and claims of a proof's maps (as witness_multi), the int8 folds
-    (M, E, cols_pad, out) of another proof (as fold_matrix_batched) and whole sum-check instances
-    (SumcheckJob) of a third, side by side."""
+    (M, E, cols_pad, out) of another proof (as fold_matrix_batched; (M, E, cols_pad, out, E2, out2) also
+    folds M by E2 into out2 from the same read) and whole sum-check instances (SumcheckJob) of a third, side
+    by side."""
     arr = _multi_descs(jobs)
     ne, eqd = _eq_descs(eq)
     nf, fd = _fold_descs(folds)
@@ -623,8 +632,7 @@ def fold_matrix_batched(jobs):
     """jobs: list of (M, E, cols_pad, out); all M of one dtype."""
     k = len(jobs)
     dt = _dt(jobs[0][0])
-    descs = (_FoldDesc * k)(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
-                                        out.data_ptr()) for (M, E, cp, out) in jobs])
+    descs = (_FoldDesc * k)(*[_fold_desc(f) for f in jobs])
     need = lib().fp_fold_matrix_batched_workspace(dt, k, descs)
     p, nb = _ws_fold.get(need)
     _check(lib().fp_fold_matrix_batched(dt, k, descs, p, nb, _stream()), "fp_fold_matrix_batched")
@@ -1015,8 +1023,7 @@ def fold_claim_batched(fold_jobs, claim_jobs):
     nf, nc = len(fold_jobs), len(claim_jobs)
     fdt = _dt(fold_jobs[0][0]) if nf else FP_I8
     cdt = _dt(claim_jobs[0][0]) if nc else FP_I32
-    fd = (_FoldDesc * max(nf, 1))(*[_FoldDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], cp, E.data_ptr(),
-                                              out.data_ptr()) for (M, E, cp, out) in fold_jobs])
+    fd = (_FoldDesc * max(nf, 1))(*[_fold_desc(f) for f in fold_jobs])
     cd = (_ClaimDesc * max(nc, 1))(*[_ClaimDesc(M.data_ptr(), _ld(M), M.shape[0], M.shape[1], Er.data_ptr(),
                                                 Ec.data_ptr(), out.data_ptr()) for (M, Er, Ec, out) in claim_jobs])
     need = lib().fp_fold_claim_batched_workspace(fdt, nf, fd, cdt, nc, cd)

@@ -251,6 +251,8 @@ int validate_folds(const char* fn, fp_dtype dt, int32_t count, const fp_fold_des
   if (count < 0) return fpi::fail(FP_EARG, "%s: count < 0", fn);
   if (count > 0 && !d) return fpi::fail(FP_EARG, "%s: null descs", fn);
   for (int32_t i = 0; i < count; ++i) {
+    if (d[i].E2 || d[i].out2)
+      return fpi::fail(FP_EARG, "%s: fold %d has a second weight vector (the step launches' folds only)", fn, i);
     int rc = validate_fold(fn, dt, d[i].M, d[i].ld, d[i].rows, d[i].cols, d[i].E, d[i].out, d[i].cols_pad);
     if (rc) return rc;
   }
@@ -260,13 +262,13 @@ int validate_folds(const char* fn, fp_dtype dt, int32_t count, const fp_fold_des
 }  // namespace
 
 extern "C" size_t fp_fold_matrix_workspace(fp_dtype dt, int32_t rows, int32_t cols) {
-  fp_fold_desc d{nullptr, cols, rows, cols, cols, nullptr, nullptr};
+  fp_fold_desc d{nullptr, cols, rows, cols, cols, nullptr, nullptr, nullptr, nullptr};
   return fp_fold_matrix_batched_workspace(dt, 1, &d);
 }
 
 extern "C" int fp_fold_matrix(fp_dtype dt, const void* M, int64_t ld, int32_t rows, int32_t cols, const fp_elem* E,
                               fp_elem* out, int32_t cols_pad, void* ws, size_t ws_bytes, hipStream_t stream) {
-  fp_fold_desc d{M, ld, rows, cols, cols_pad, E, out};
+  fp_fold_desc d{M, ld, rows, cols, cols_pad, E, out, nullptr, nullptr};
   return fp_fold_matrix_batched(dt, 1, &d, ws, ws_bytes, stream);
 }
 

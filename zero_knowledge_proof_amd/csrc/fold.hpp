@@ -22,6 +22,9 @@ struct FoldJob {
   const fp_elem* Ecol;  // claim: column weights; nullptr for a folded row
   fp_elem* out;         // folded row (cols_pad) or the claim (1)
   fp_elem* part;        // per-chunk column values [n_chunks][cols] or per-workgroup values
+  const fp_elem* E2;    // a second row-weight vector folded from the same read of M (int8 rows), or nullptr
+  fp_elem* out2;        // its folded row (cols_pad)
+  fp_elem* part2;       // its per-chunk column values [n_chunks][cols]
   int32_t rows, cols, cols_pad;
   int32_t chunk_rows, n_chunks, n_strips;  // strips holding data columns
   int32_t n_pad_strips;                    // strips wholly inside [cols, cols_pad)
@@ -99,8 +102,15 @@ __device__ __forceinline__ uint64_t load_part(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int EB, bool VEC, bool COH>
+// NE = 2: the rows are folded by E and E2 from one read of them (int8 rows;
+// the second vector's digits follow the first's in LDS, and its weight sum
+// travels through four words after the exchange area).
+template <int EB> constexpr int kDig2 = kMaxG<EB> * 8;       // LDS word of the second vector's digits
+template <int EB> constexpr int kEs2 = 3 * FRG * FCT * kNL<EB>;  // LDS word of its per-wave weight sums
+
+template <int EB, bool VEC, bool COH, int NE = 1>
 __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* lds, uint64_t* gsum) {
+  static_assert(NE == 1 || (NE == 2 && EB == 1), "two row-weight vectors for int8 rows only");
   constexpr int NL = kNL<EB>;
   constexpr int U = kU<EB>;
   constexpr int STEP = kStep<EB>;
@@ -161,11 +171,13 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
       }
   };
 
-  uint32_t acc[4][NL];
+  uint32_t acc[NE][4][NL];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int e = 0; e < NE; ++e)
 #pragma unroll
-    for (int l = 0; l < NL; ++l) acc[c][l] = 0;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int l = 0; l < NL; ++l) acc[e][c][l] = 0;
   auto compute = [&](const uint32_t (&v)[U][4][W], int bi) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -174,13 +186,24 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
       const u32x4 d1 = *(const u32x4*)&lds[g * 8 + 4];
       const uint32_t dg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
       if constexpr (EB == 1) {
+        uint32_t dh[8];
+        if constexpr (NE == 2) {
+          const u32x4 h0 = *(const u32x4*)&lds[kDig2<EB> + g * 8];
+          const u32x4 h1 = *(const u32x4*)&lds[kDig2<EB> + g * 8 + 4];
+          dh[0] = h0[0]; dh[1] = h0[1]; dh[2] = h0[2]; dh[3] = h0[3];
+          dh[4] = h1[0]; dh[5] = h1[1]; dh[6] = h1[2]; dh[7] = h1[3];
+        }
         uint32_t w[4];
         transpose4(v[u][0][0], v[u][1][0], v[u][2][0], v[u][3][0], w[0], w[1], w[2], w[3]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t uu = w[c] ^ 0x80808080u;  // m + 128 per byte
 #pragma unroll
-          for (int l = 0; l < 8; ++l) acc[c][l] = udot4(uu, dg[l], acc[c][l]);
+          for (int l = 0; l < 8; ++l) acc[0][c][l] = udot4(uu, dg[l], acc[0][c][l]);
+          if constexpr (NE == 2) {
+#pragma unroll
+            for (int l = 0; l < 8; ++l) acc[1][c][l] = udot4(uu, dh[l], acc[1][c][l]);
+          }
         }
       } else {
 #pragma unroll
@@ -191,7 +214,7 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
 #pragma unroll
           for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int l = 0; l < 8; ++l) acc[c][b + l] = udot4(pl[b], dg[l], acc[c][b + l]);
+            for (int l = 0; l < 8; ++l) acc[0][c][b + l] = udot4(pl[b], dg[l], acc[0][c][b + l]);
         }
       }
     }
@@ -202,20 +225,27 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
   load(A, 0);
 
   // ---- digits of E for this chunk (zero past its rows), and group sums of E ----
+  uint64_t es2 = 0;  // NE = 2: this thread's share of the chunk's sum of E2
   for (int g = tid; g < gpad; g += FT) {
-    uint32_t dg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    uint64_t es = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      const uint64_t e = (t < nrows) ? job.E[row0 + t] : 0;
-      es = gl::add(es, e);
+    for (int e = 0; e < NE; ++e) {
+      const fp_elem* Ev = e == 0 ? job.E : job.E2;
+      uint32_t dg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint64_t es = 0;
 #pragma unroll
-      for (int l = 0; l < 8; ++l) dg[l] |= (uint32_t)((e >> (8 * l)) & 0xFF) << (8 * i);
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        const uint64_t x = (t < nrows) ? Ev[row0 + t] : 0;
+        es = gl::add(es, x);
+#pragma unroll
+        for (int l = 0; l < 8; ++l) dg[l] |= (uint32_t)((x >> (8 * l)) & 0xFF) << (8 * i);
+      }
+      const int base = e == 0 ? 0 : kDig2<EB>;
+      *(u32x4*)&lds[base + g * 8] = u32x4{dg[0], dg[1], dg[2], dg[3]};
+      *(u32x4*)&lds[base + g * 8 + 4] = u32x4{dg[4], dg[5], dg[6], dg[7]};
+      if (e == 0) gsum[g] = es;
+      else es2 = gl::add(es2, es);
     }
-    *(u32x4*)&lds[g * 8] = u32x4{dg[0], dg[1], dg[2], dg[3]};
-    *(u32x4*)&lds[g * 8 + 4] = u32x4{dg[4], dg[5], dg[6], dg[7]};
-    gsum[g] = es;
   }
   __syncthreads();
 
@@ -233,64 +263,91 @@ __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* 
   compute(B, bi + 1);
 
   // ---- exchange: wave v stores its other three columns (lane-contiguous), and
-  // each wave finishes column c0 + v of its lanes ----
-  __syncthreads();  // digits no longer needed
+  // each wave finishes column c0 + v of its lanes (for each weight vector in turn) ----
+  uint64_t* es2w = reinterpret_cast<uint64_t*>(lds + kEs2<EB>);
+  if constexpr (NE == 2) es2 = fpi::wave_total(es2);
+  uint64_t val[NE];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (c == rg) continue;
-    const int slot = rg * 3 + (c < rg ? c : c - 1);
+  for (int e = 0; e < NE; ++e) {
+    __syncthreads();  // digits (or the previous vector's exchange) no longer needed
 #pragma unroll
-    for (int l = 0; l < NL; ++l) lds[(slot * NL + l) * FCT + ct] = acc[c][l];
+    for (int c = 0; c < 4; ++c) {
+      if (c == rg) continue;
+      const int slot = rg * 3 + (c < rg ? c : c - 1);
+#pragma unroll
+      for (int l = 0; l < NL; ++l) lds[(slot * NL + l) * FCT + ct] = acc[e][c][l];
+    }
+    if (NE == 2 && e == 0 && ct == 0) es2w[rg] = es2;
+    __syncthreads();
+    uint32_t sl[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+      sl[l] = rg == 0 ? acc[e][0][l] : rg == 1 ? acc[e][1][l] : rg == 2 ? acc[e][2][l] : acc[e][3][l];
+#pragma unroll
+    for (int v = 0; v < FRG; ++v) {
+      if (v == rg) continue;
+      const int slot = v * 3 + (rg < v ? rg : rg - 1);
+#pragma unroll
+      for (int l = 0; l < NL; ++l) sl[l] += lds[(slot * NL + l) * FCT + ct];  // exact: < 2^32
+    }
+    uint64_t es = 0;
+    if (e == 0) {
+      for (int g = ct; g < gpad; g += FCT) es = gl::add(es, gsum[g]);
+      es = fpi::wave_total(es);
+    } else {
+#pragma unroll
+      for (int v = 0; v < FRG; ++v) es = gl::add(es, es2w[v]);
+    }
+    // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
+    const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
+    uint64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) acc128(lo, hi, sl[l], 8 * l);
+    val[e] = gl::sub(gl::reduce128(lo, hi), corr);
   }
-  __syncthreads();
-  uint32_t sl[NL];
-#pragma unroll
-  for (int l = 0; l < NL; ++l) sl[l] = rg == 0 ? acc[0][l] : rg == 1 ? acc[1][l] : rg == 2 ? acc[2][l] : acc[3][l];
-#pragma unroll
-  for (int v = 0; v < FRG; ++v) {
-    if (v == rg) continue;
-    const int slot = v * 3 + (rg < v ? rg : rg - 1);
-#pragma unroll
-    for (int l = 0; l < NL; ++l) sl[l] += lds[(slot * NL + l) * FCT + ct];  // exact: < 2^32
-  }
-  uint64_t es = 0;
-  for (int g = ct; g < gpad; g += FCT) es = gl::add(es, gsum[g]);
-  es = fpi::wave_total(es);
-  // offset correction: off * sum E, off = 128 (int8) or 2^31 (int32)
-  const uint64_t corr = gl::mul_small(es, EB == 1 ? 128u : 0x80000000u);
-  uint64_t lo = 0, hi = 0;
-#pragma unroll
-  for (int l = 0; l < NL; ++l) acc128(lo, hi, sl[l], 8 * l);
-  const uint64_t val = gl::sub(gl::reduce128(lo, hi), corr);
 
   if (job.Ecol) {
     // claim: weight the column by its eq value; one value per wave
-    const uint64_t s = fpi::wave_total(gl::mul(val, ecol));
+    const uint64_t s = fpi::wave_total(gl::mul(val[0], ecol));
     if (ct == 0) store_part(job.part + lb * FRG + rg, s, COH);
     return;
   }
-  if (job.n_chunks == 1) {
-    if (col < job.cols) job.out[col] = val;
-    else if (col < job.cols_pad) job.out[col] = 0;
-    return;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    fp_elem* out = e == 0 ? job.out : job.out2;
+    fp_elem* part = e == 0 ? job.part : job.part2;
+    if (job.n_chunks == 1) {
+      if (col < job.cols) out[col] = val[e];
+      else if (col < job.cols_pad) out[col] = 0;
+    } else if (col < job.cols) {
+      store_part(part + (int64_t)chunk * job.cols + col, val[e], COH);
+    }
   }
-  if (col < job.cols) store_part(job.part + (int64_t)chunk * job.cols + col, val, COH);
 }
 
 constexpr int LDS_WORDS = kLdsWords<1> > kLdsWords<4> ? kLdsWords<1> : kLdsWords<4>;
+static_assert(2 * kDig2<1> <= LDS_WORDS && kEs2<1> + 2 * FRG <= LDS_WORDS,
+              "the second vector's digits and weight sums fit the fold's LDS");
 constexpr int MAXG_ALL = kMaxG<1> > kMaxG<4> ? kMaxG<1> : kMaxG<4>;
 
 
 // Workgroup lb of a job: strips wholly in the padding write zeros; the others
 // fold their chunk of rows over their 256 columns.
-template <bool COH>
+// DUAL: jobs with a second row-weight vector may occur (the step launches' folds).
+template <bool COH, bool DUAL = false>
 __device__ __forceinline__ void fold_block(const FoldJob& job, int lb, uint32_t* lds, uint64_t* gsum) {
   if (lb >= job.n_chunks * job.n_strips) {
     const int strip = job.n_strips + (lb - job.n_chunks * job.n_strips);
-    for (int c = strip * FCOLS + (int)threadIdx.x; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) job.out[c] = 0;
+    for (int c = strip * FCOLS + (int)threadIdx.x; c < min((strip + 1) * FCOLS, job.cols_pad); c += FT) {
+      job.out[c] = 0;
+      if (job.E2) job.out2[c] = 0;
+    }
     return;
   }
-  if (job.eb == 1) {
+  if (DUAL && job.eb == 1 && job.E2) {
+    if (job.vec) fold_body<1, true, COH, 2>(job, lb, lds, gsum);
+    else fold_body<1, false, COH, 2>(job, lb, lds, gsum);
+  } else if (job.eb == 1) {
     if (job.vec) fold_body<1, true, COH>(job, lb, lds, gsum);
     else fold_body<1, false, COH>(job, lb, lds, gsum);
   } else {
@@ -324,12 +381,16 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t n, uint32_t*
 // out[c] = sum over chunks of part[chunk][c]; zeros for the strip's padding.
 __device__ __forceinline__ void strip_total(const FoldJob& job, int strip) {
   const int c = strip * FCOLS + (int)threadIdx.x;
-  if (c < job.cols) {
-    uint64_t v = 0;
-    for (int ch = 0; ch < job.n_chunks; ++ch) v = gl::add(v, load_part(job.part + (int64_t)ch * job.cols + c));
-    job.out[c] = v;
-  } else if (c < job.cols_pad) {
-    job.out[c] = 0;
+  for (int e = 0; e < (job.E2 ? 2 : 1); ++e) {
+    const fp_elem* part = e == 0 ? job.part : job.part2;
+    fp_elem* out = e == 0 ? job.out : job.out2;
+    if (c < job.cols) {
+      uint64_t v = 0;
+      for (int ch = 0; ch < job.n_chunks; ++ch) v = gl::add(v, load_part(part + (int64_t)ch * job.cols + c));
+      out[c] = v;
+    } else if (c < job.cols_pad) {
+      out[c] = 0;
+    }
   }
 }
 
@@ -351,7 +412,7 @@ __device__ __forceinline__ void claim_total(const FoldJob& job, uint64_t* red) {
 // Workgroup lb of a job in arrival mode: fold, then the sums by the last.
 __device__ __forceinline__ void fold_block_arrive(const FoldJob& job, int lb, uint32_t* ctrs, uint32_t* lds,
                                                   uint64_t* gsum, uint32_t* flag) {
-  fold_block<true>(job, lb, lds, gsum);
+  fold_block<true, true>(job, lb, lds, gsum);
   if (lb >= job.n_chunks * job.n_strips) return;
   if (job.Ecol) {
     if (arrive_last(ctrs + job.ctr, (uint32_t)(job.n_chunks * job.n_strips), flag)) claim_total(job, gsum);

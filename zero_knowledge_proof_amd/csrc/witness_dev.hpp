@@ -323,7 +323,10 @@ int plan_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_
         return fpi::fail(FP_ESHAPE, "%s: fold %d has bad sizes", fn, i);
       if ((d.cols_pad > 0 && !d.out) || (d.rows > 0 && d.cols > 0 && (!d.M || !d.E)))
         return fpi::fail(FP_EARG, "%s: fold %d has a null pointer", fn, i);
+      if ((d.E2 != nullptr) != (d.out2 != nullptr))
+        return fpi::fail(FP_EARG, "%s: fold %d has a second weight vector without its output, or the reverse", fn, i);
       j.M = d.M; j.ld = d.ld; j.E = d.E; j.Ecol = nullptr; j.out = d.out;
+      j.E2 = d.E2; j.out2 = d.out2;
       j.rows = d.rows; j.cols = d.cols; j.cols_pad = d.cols_pad; j.eb = 1;
     } else {
       const fp_claim_desc& d = claims[i - n_fold];
@@ -346,6 +349,11 @@ int plan_folds(const char* fn, int32_t n_fold, const fp_fold_desc* folds, int32_
     j.n_pad_strips = p.n_pad_strips;
     j.part = p.part_bytes ? (fp_elem*)((char*)ws + off) : nullptr;
     off += p.part_bytes;
+    j.part2 = nullptr;
+    if (j.E2 && p.part_bytes) {  // the second vector's chunk values after the first's
+      j.part2 = (fp_elem*)((char*)ws + off);
+      off += p.part_bytes;
+    }
     j.block_start = (int32_t)blocks;
     j.ctr = nctr;
     blocks += p.blocks;

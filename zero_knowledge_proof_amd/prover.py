@@ -20,6 +20,8 @@ only enqueues kernels. Inputs are host numpy arrays uploaded once.
 """
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 import torch
 
@@ -483,20 +485,23 @@ class OverlappedMultiProver(MultiMatmulProver):
     """A stream of proofs of a multi-map layer (the dense MLP, the seven-map
     layer), three in flight: step k is ONE launch (fp_layer_step_multi) that runs
     proof k's witness GEMMs with every map's claim taken from the accumulators,
-    proof k+1's eq tables, proof k-1's folds of X and W, and proof k-2's
-    sum-check(s), each instance one workgroup. A proof's eq tables depend on its
-    challenges alone, so they are built a step ahead; its folds read only its
-    own tables and its sum-check only its own folds, so each proof keeps the
-    protocol order. Then a small launch merges proof k-2's claims (the RLC of
-    the three output claims, or the rho-combination of the seven input claims
-    that the batched sum-check starts from). A proof's buffers (Y, R, tables,
-    folds, claims, rounds, finals) live from the step that builds its eq
-    tables to the one that merges it, so they rotate over three sets and a
-    captured graph holds a multiple of three steps; ``drain()`` finishes the
-    last two proofs. Needs every map's d_in % 16 == 0."""
+    proof k+1's eq tables, proof k-1's folds of X, and proof k-2's
+    sum-check(s), each instance one workgroup; on even k the same launch folds
+    the weights for proofs k-1 and k together, from one read of each weight
+    matrix (the proofs of a layer share its weights, and a weight fold needs
+    only its proof's eq tables). A proof's eq tables depend on its challenges
+    alone, so they are built a step ahead; its folds read only its own tables
+    and its sum-check only its own folds, so each proof keeps the protocol
+    order. Then a small launch merges proof k-2's claims (the RLC of the three
+    output claims, or the rho-combination of the seven input claims that the
+    batched sum-check starts from). A proof's buffers (Y, R, tables, folds,
+    claims, rounds, finals) live from the step that builds its eq tables to the
+    one that merges it, so they rotate over three sets; with the weight folds'
+    two-step period a captured graph holds a multiple of six steps.
+    ``drain()`` finishes the last two proofs. Needs every map's d_in % 16 == 0."""
 
     SETS = 3
-    GRAPH_QUANTUM = 3
+    GRAPH_QUANTUM = 6
     PER_SET = ("E_t", "E_o", "Y", "R", "c0", "xf", "wf", "rounds", "finals", "claim0", "rlc", "c0_batch")
 
     def __init__(self, cfg, inp: dict, ch: dict, dev=None, keep_z: bool = False, group_o: int = 1):
@@ -552,9 +557,26 @@ class OverlappedMultiProver(MultiMatmulProver):
                           st["maps"][i]["R"], st["maps"][i]["Z"], st["E_t"], st["maps"][i]["E_o"], st["maps"][i]["c0"])
                 for i in self.order]
 
-    def _folds(self, st):
-        jobs = [(M, st["E_t"], cp, out) for (M, cp, out) in st["x_jobs"]]
-        jobs += [(self.tens[d["m"].w], e["E_o"], 1 << d["n"], e["wf"]) for d, e in zip(self.mm, st["maps"])]
+    def _x_folds(self, st):
+        return [(M, st["E_t"], cp, out) for (M, cp, out) in st["x_jobs"]]
+
+    def _w_folds(self, st, st2=None):
+        """Every map's weight fold of one proof, or of two proofs from one read of the weights."""
+        out = []
+        for i, d in enumerate(self.mm):
+            e = st["maps"][i]
+            job = (self.tens[d["m"].w], e["E_o"], 1 << d["n"], e["wf"])
+            if st2 is not None:
+                job += (st2["maps"][i]["E_o"], st2["maps"][i]["wf"])
+            out.append(job)
+        return out
+
+    def _step_folds(self, k):
+        """Proof k-1's folds of X; on even k the weight folds of proofs k-1 and k (the layer's weights
+        read once for both: proof k's fold needs only its eq tables, built in step k-1)."""
+        jobs = self._x_folds(self._set(k - 1)) if k >= 1 else []
+        if k % 2 == 0:
+            jobs += self._w_folds(self._set(k - 1), self._set(k)) if k >= 1 else self._w_folds(self._set(k))
         return jobs
 
     def _sumchecks(self, st):
@@ -571,11 +593,10 @@ class OverlappedMultiProver(MultiMatmulProver):
         else:
             linear_combine([e["c0"] for e in st["maps"]], self.rho, out=st["c0_batch"])
 
-    def _step(self, k, fold: bool, tail: bool):
-        cur, nxt, prev, old = self._set(k), self._set(k + 1), self._set(k - 1), self._set(k - 2)
+    def _step(self, k, tail: bool):
+        cur, nxt, old = self._set(k), self._set(k + 1), self._set(k - 2)
         layer_step_multi(self._jobs(cur), self.s, group_o=self.group_o, eq=self._eq_pairs(nxt),
-                         folds=self._folds(prev) if fold else (), sumchecks=self._sumchecks(old) if tail else (),
-                         ws=self.step_ws)
+                         folds=self._step_folds(k), sumchecks=self._sumchecks(old) if tail else (), ws=self.step_ws)
         if tail:
             self._merge_set(old)
 
@@ -584,13 +605,15 @@ class OverlappedMultiProver(MultiMatmulProver):
         if self.k == 0:
             st = self._set(0)
             eq_table_batched([r for r, _ in self._eq_pairs(st)], [E for _, E in self._eq_pairs(st)])
-        self._step(self.k, self.k >= 1, self.k >= 2)
+        self._step(self.k, self.k >= 2)
         mark("end")
         self.k += 1
 
     def phases(self):
+        # the steady state alternates a step with two proofs' weight folds and one without
         wit = "witness" if self.keep_z else "witness(Y,R)"
-        return [(wit + "+claim(acc)+eq+fold+sumcheck", lambda: self._step(2, True, True))]
+        n = itertools.count()
+        return [(wit + "+claim(acc)+eq+fold(W/2)+sumcheck", lambda: self._step(2 + next(n) % 2, True))]
 
     def capture(self, steps: int = 1):
         if steps % self.GRAPH_QUANTUM:
@@ -614,14 +637,15 @@ class OverlappedMultiProver(MultiMatmulProver):
         self.k = self.k_graph
 
     def drain(self):
-        """The sum-check of the next-to-last proof, then the folds and sum-check of the last one."""
+        """The sum-check of the next-to-last proof, then the folds and sum-check of the last one (its
+        weight folds were made in its own step when its index is even)."""
         last = self.k - 1
         if last < 0:
             return
         if last >= 1:
             self._finish(self._set(last - 1))
         st = self._set(last)
-        fold_claim_batched(self._folds(st), [])
+        fold_claim_batched(self._x_folds(st) + (self._w_folds(st) if last % 2 else []), [])
         self._finish(st)
 
     def _finish(self, st):
