@@ -69,7 +69,7 @@ def test_pipelined_graph_replays(fp, cid, shape):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cid,shape,steps,keep_z", [(1, {}, 3, False), (2, dict(T=100, d_in=1008, d_out=700), 6, True),
+@pytest.mark.parametrize("cid,shape,steps,keep_z", [(1, {}, 6, False), (2, dict(T=100, d_in=1008, d_out=700), 6, True),
                                                     (3, dict(T=300, d=256, d_ff=1024), 6, False),
                                                     (5, dict(T=200, d=128, d_kv=64, d_ff=320), 6, False)])
 def test_overlapped_graph_replays(fp, cid, shape, steps, keep_z):

@@ -78,8 +78,12 @@ __device__ __forceinline__ void acc128(uint64_t& lo, uint64_t& hi, uint32_t v, i
 }
 
 // 4-row groups per wave and batch: int8 rows are 4 bytes a lane, int32 rows 16.
+// kU: the fold launch's batches; kUMax: the step launches' int8 batches, whose
+// fold workgroups run at the GEMM's occupancy (two per CU) and so keep twice
+// the loads in flight each, in registers the GEMM has reserved anyway.
 template <int EB> constexpr int kU = (EB == 1) ? 2 : 1;
-template <int EB> constexpr int kStep = FRG * kU<EB>;                  // groups per batch (workgroup)
+template <int EB> constexpr int kUMax = (EB == 1) ? 4 : 1;
+template <int EB> constexpr int kStep = FRG * kUMax<EB>;                 // groups per batch (workgroup), at most
 template <int EB> constexpr int kMaxG = FMAX_CHUNK / 4 + 2 * kStep<EB>;  // digit groups incl. padding
 // rows of a chunk are a multiple of this (whole pairs of batches)
 template <int EB> constexpr int kRowQuantum = 8 * kStep<EB>;
@@ -108,12 +112,12 @@ __device__ __forceinline__ uint64_t load_part(const uint64_t* p) {
 template <int EB> constexpr int kDig2 = kMaxG<EB> * 8;       // LDS word of the second vector's digits
 template <int EB> constexpr int kEs2 = 3 * FRG * FCT * kNL<EB>;  // LDS word of its per-wave weight sums
 
-template <int EB, bool VEC, bool COH, int NE = 1>
+template <int EB, bool VEC, bool COH, int NE = 1, int U = kU<EB>>
 __device__ __forceinline__ void fold_body(const FoldJob& job, int lb, uint32_t* lds, uint64_t* gsum) {
   static_assert(NE == 1 || (NE == 2 && EB == 1), "two row-weight vectors for int8 rows only");
+  static_assert(U >= 1 && U <= kUMax<EB>, "batch within the digit table's padding");
   constexpr int NL = kNL<EB>;
-  constexpr int U = kU<EB>;
-  constexpr int STEP = kStep<EB>;
+  constexpr int STEP = FRG * U;
   constexpr int W = (EB == 1) ? 1 : 4;    // dwords per lane and row
   const int tid = threadIdx.x;
   const int ct = tid % FCT;
@@ -333,7 +337,8 @@ constexpr int MAXG_ALL = kMaxG<1> > kMaxG<4> ? kMaxG<1> : kMaxG<4>;
 
 // Workgroup lb of a job: strips wholly in the padding write zeros; the others
 // fold their chunk of rows over their 256 columns.
-// DUAL: jobs with a second row-weight vector may occur (the step launches' folds).
+// DUAL (the step launches' folds): jobs with a second row-weight vector may
+// occur, and int8 rows go in the larger batches.
 template <bool COH, bool DUAL = false>
 __device__ __forceinline__ void fold_block(const FoldJob& job, int lb, uint32_t* lds, uint64_t* gsum) {
   if (lb >= job.n_chunks * job.n_strips) {
@@ -344,9 +349,15 @@ __device__ __forceinline__ void fold_block(const FoldJob& job, int lb, uint32_t*
     }
     return;
   }
-  if (DUAL && job.eb == 1 && job.E2) {
-    if (job.vec) fold_body<1, true, COH, 2>(job, lb, lds, gsum);
-    else fold_body<1, false, COH, 2>(job, lb, lds, gsum);
+  if (DUAL && job.eb == 1) {
+    constexpr int U = kUMax<1>;
+    if (job.E2) {
+      if (job.vec) fold_body<1, true, COH, 2, U>(job, lb, lds, gsum);
+      else fold_body<1, false, COH, 2, U>(job, lb, lds, gsum);
+    } else {
+      if (job.vec) fold_body<1, true, COH, 1, U>(job, lb, lds, gsum);
+      else fold_body<1, false, COH, 1, U>(job, lb, lds, gsum);
+    }
   } else if (job.eb == 1) {
     if (job.vec) fold_body<1, true, COH>(job, lb, lds, gsum);
     else fold_body<1, false, COH>(job, lb, lds, gsum);
@@ -437,14 +448,18 @@ inline Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool 
   p.n_strips = (cols + FCOLS - 1) / FCOLS;
   const int pad_total = (cols_pad + FCOLS - 1) / FCOLS;
   p.n_pad_strips = claim ? 0 : (pad_total - p.n_strips);
-  // about one workgroup per compute unit (measured against 128-1536 on the
-  // up-projection: fewer chunks also shorten the cross-chunk sums), chunks in
-  // whole pairs of batches
+  // a launch of its own: about one workgroup per compute unit (measured
+  // against 128-1536 on the up-projection: fewer chunks also shorten the
+  // cross-chunk sums), chunks in whole pairs of batches. Inside a step launch
+  // the folds of several tables share the GPU with the GEMM's last tiles:
+  // the longest chunks (measured against 256-row and 512-row minimums on the
+  // seven-map layer: 6 us per step less than one workgroup per CU per job).
   const int target_blocks = 256;
   const int q = eb == 1 ? kRowQuantum<1> : kRowQuantum<4>;
   const int want_chunks = (target_blocks + p.n_strips - 1) / p.n_strips;
   int64_t cr = (rows + want_chunks - 1) / want_chunks;
   cr = (cr + q - 1) / q * q;
+  if (arrive) cr = FMAX_CHUNK;
   if (cr > FMAX_CHUNK) cr = FMAX_CHUNK;
   if (cr >= rows) cr = rows;
   p.chunk_rows = (int32_t)cr;
