@@ -111,6 +111,48 @@ def test_witness_multi(fp, case, group_o, with_eq):
         assert ws.buf is None or int(ws.buf[:512].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("group_o", [1, 4])
+def test_witness_multi_tile_pool(fp, group_o):
+    """Launches of more than two full waves of tiles hand each XCD's last tiles to workgroups that take them at
+    run time (from their own XCD's pool or another's): with ragged tokens and outputs, claims of eq tables and of
+    arbitrary tables, Z kept on one map, every output and claim equals the oracle's on three calls in a row, and
+    the pool's counters (in the workspace's first 512 bytes) are zero after each."""
+    rng = _rng(1201 + group_o)
+    T = 1000
+    jobs, wants = [], []
+    for i, (d_in, d_out, claim) in enumerate([(64, 12900, "eq"), (48, 12800, "rand"), (96, 12544, "eq")]):
+        X, W = _i8(rng, (T, d_in)), _i8(rng, (d_out, d_in))
+        Z, Y, R = O.witness(X, W, 8)
+        if claim == "eq":
+            rt, ro = _field(rng, 10), _field(rng, (d_out - 1).bit_length())
+            c = O.mle_matrix(Z, rt, ro)
+            Et, Eo = fp.to_field_tensor(O.eq_table(rt)), fp.to_field_tensor(O.eq_table(ro))
+        else:
+            Et_h, Eo_h = _field(rng, T), _field(rng, d_out)
+            c = _claim_def(Z, Et_h, Eo_h)
+            Et, Eo = fp.to_field_tensor(Et_h), fp.to_field_tensor(Eo_h)
+        Zd = torch.empty((T, d_out), dtype=torch.int32, device="cuda") if i == 1 else None
+        jobs.append(fp.MatmulJob(_dev(X), fp.pack_weights(_dev(W)), torch.empty((T, d_out), dtype=torch.int8,
+                                 device="cuda"), torch.empty((T, d_out), dtype=torch.int8, device="cuda"), Zd, Et, Eo,
+                                 torch.empty(1, dtype=torch.int64, device="cuda")))
+        wants.append((Z, Y, R, c))
+    assert sum(((T + 127) // 128) * ((j.Y.shape[1] + 255) // 256) for j in jobs) >= 1024  # the pool is used
+    ws = fp.StepWorkspace()
+    for rep in range(3):
+        for j in jobs:
+            j.Y.fill_(3)
+            j.R.fill_(3)
+            j.claim.fill_(-1)
+        fp.witness_multi(jobs, 8, group_o=group_o, ws=ws)
+        torch.cuda.synchronize()
+        for j, (Z, Y, R, c) in zip(jobs, wants):
+            assert np.array_equal(j.Y.cpu().numpy(), Y) and np.array_equal(j.R.cpu().numpy(), R)
+            if j.Z is not None:
+                assert np.array_equal(j.Z.cpu().numpy(), Z)
+            assert int(fp.field_numpy(j.claim)[0]) == c
+        assert int(ws.buf[:512].count_nonzero()) == 0
+
+
 def test_witness_multi_seven_maps_one_token_axis(fp):
     """Seven maps over one token axis and shared inputs, in the layer's order (longest reduction first), the
     claims of eq tables sharing E_t: every output and claim is the oracle's."""

@@ -57,7 +57,50 @@ struct MultiArgs {
   MmDev m[MM_MAX];
   int32_t split[MM_MAX][NXCD + 1];  // map m's tiles [split[m][x], split[m][x+1]) run on XCD x
   int32_t count, s, group_o, gemm_blocks;
+  // the last `pool` tiles of each XCD's list are taken by `ndyn` workgroups at
+  // run time (qctr: the pool's counters in the workspace's first lines)
+  int32_t pool, ndyn;
+  uint32_t* qctr;
 };
+
+// The tiles of one launch are dealt to the XCDs in equal shares, but the XCDs
+// do not run at one speed (on the seven-map layer one finishes its share up to
+// 100 us, ~12%, after another, and which one varies from launch to launch). So
+// each XCD's last tiles form a pool: after the statically placed tiles come
+// 2 x 8 x pool workgroups that each reserve one pool tile (a reservation
+// counter bounds the takers), take it from their own XCD's pool or else from
+// another's, and exit at once when every tile is taken; those on the XCDs that
+// are ahead arrive first. The counters sit in the workspace's claim-counter
+// lines (word 16x + 8: XCD x's pool; word 9: reservations; word 25: exits),
+// zero on entry; the last workgroup to exit sets them to zero again.
+constexpr int POOL_PERCENT = 12;  // of an XCD's tiles, from 2 full waves of tiles on
+constexpr int GPU_SLOTS = 512;    // GEMM workgroups resident at once (2 per CU)
+__device__ __forceinline__ uint32_t* q_pool(uint32_t* q, int x) { return q + 16 * x + 8; }
+__device__ __forceinline__ uint32_t q_add(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The pool tile of a dynamic workgroup on XCD y (x * pool + j), or -1.
+__device__ __forceinline__ int pool_pick(const MultiArgs& ma, int y) {
+  uint32_t* q = ma.qctr;
+  int pick = -1;
+  if (q_add(q + 9) < (uint32_t)(NXCD * ma.pool)) {
+    // a reservation guarantees a tile: every pool full would mean as many other takers as tiles
+    for (int j = 0; j < NXCD; ++j) {
+      const int x = (y + j) % NXCD;
+      const uint32_t g = q_add(q_pool(q, x));
+      if (g < (uint32_t)ma.pool) {
+        pick = x * ma.pool + (int)g;
+        break;
+      }
+    }
+  }
+  if (q_add(q + 25) == (uint32_t)(ma.ndyn - 1)) {  // every taker is done taking
+    for (int x = 0; x < NXCD; ++x) __hip_atomic_store(q_pool(q, x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 9, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 25, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return pick;
+}
 
 // Fold jobs of another proof (arrival mode) and whole sum-check instances of a
 // third, run by workgroups of the same launch.
@@ -425,8 +468,9 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
 
 // Workgroups, in order: [0, sa.blocks) whole sum-check instances (first, so
 // their chains of rounds start at once; the count is padded to a multiple of
-// 8); then the GEMM tiles of every map (map and tile from the XCD split); then
-// fold jobs in arrival mode; then eq tables. The sum-checks, folds and eq
+// 8); then the GEMM tiles of every map placed by the XCD split, all but each
+// XCD's last ma.pool; then the pool's takers; then fold jobs in arrival mode;
+// then eq tables. The sum-checks, folds and eq
 // tables belong to other proofs than the GEMMs (this launch's claims read eq
 // tables that are complete before it starts), so nothing in one launch waits
 // for another part of it.
@@ -441,27 +485,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int B1 = C::LDS_BYTES > TAIL_LDS ? C::LDS_BYTES : TAIL_LDS;
   constexpr int BYTES = B1 > FOLD_LDS ? B1 : FOLD_LDS;
   __shared__ __align__(16) int8_t lds[BYTES];
+  __shared__ int pick;
   int b = blockIdx.x;
   if (b < sa.blocks) {
     if (b < sa.count) scs::stream_body(sa.inst[b], *reinterpret_cast<sct::TailLds<256>*>(lds));
     return;
   }
   b -= sa.blocks;
-  if (b >= ma.gemm_blocks) {
-    b -= ma.gemm_blocks;
-    if (b < mf.blocks) {
-      const foldk::FoldJob& job = mf.j[foldk::find_job(mf.j, mf.count, b)];
-      uint32_t* fl = reinterpret_cast<uint32_t*>(lds);
-      uint64_t* gsum = reinterpret_cast<uint64_t*>(lds + foldk::LDS_WORDS * 4);
-      uint32_t* flag = reinterpret_cast<uint32_t*>(gsum + foldk::MAXG_ALL);
-      foldk::fold_block_arrive(job, b - job.block_start, mf.ctrs, fl, gsum, flag);
+  const int nstat = ma.gemm_blocks - NXCD * ma.pool;  // statically placed tiles
+  int x = b % NXCD, li = b / NXCD, m = 0;
+  if (b >= nstat) {
+    // after the placed tiles: the pool's takers, then fold jobs, then eq tables
+    // (folds ahead of the takers measured slower: their stream then meets
+    // the last tiles' reuse in L2)
+    int c = b - nstat;
+    if (c >= ma.ndyn) {
+      c -= ma.ndyn;
+      if (c < mf.blocks) {
+        const foldk::FoldJob& job = mf.j[foldk::find_job(mf.j, mf.count, c)];
+        uint32_t* fl = reinterpret_cast<uint32_t*>(lds);
+        uint64_t* gsum = reinterpret_cast<uint64_t*>(lds + foldk::LDS_WORDS * 4);
+        uint32_t* flag = reinterpret_cast<uint32_t*>(gsum + foldk::MAXG_ALL);
+        foldk::fold_block_arrive(job, c - job.block_start, mf.ctrs, fl, gsum, flag);
+        return;
+      }
+      eq_aux_block(eq, c - mf.blocks);
       return;
     }
-    eq_aux_block(eq, b - mf.blocks);
-    return;
+    // a pool tile, if one is left
+    if (threadIdx.x == 0) pick = pool_pick(ma, (int)(blockIdx.x % NXCD));
+    __syncthreads();
+    const int t = pick;
+    if (t < 0) return;
+    x = t / ma.pool;
+    li = (ma.gemm_blocks - x + NXCD - 1) / NXCD - ma.pool + t % ma.pool;  // XCD x holds tiles [0, L_x)
   }
-  const int x = b % NXCD;
-  int li = b / NXCD, m = 0;
   for (; m < ma.count - 1; ++m) {
     const int c = ma.split[m][x + 1] - ma.split[m][x];
     if (li < c) break;
@@ -908,7 +966,16 @@ int multi_launch(const char* fn, int32_t count, const fp_matmul_desc* mm, int32_
                                     ws_bytes - CLAIM_CTR_BYTES, false, &fold_bytes, mf, &unused_part, &unused_ctr);
     if (rc) return rc;
   }
-  const int64_t grid = (int64_t)sa.blocks + total + mf.blocks + aux.block_start[aux.count];
+  // the tile pool needs the workspace's counter lines (zero on entry)
+  ma.pool = 0;
+  ma.ndyn = 0;
+  ma.qctr = nullptr;
+  if (!noalloc && (any_claim || n_fold > 0 || n_sc > 0) && total >= 2 * GPU_SLOTS) {
+    ma.pool = (int32_t)(total / NXCD * POOL_PERCENT / 100);
+    ma.ndyn = 2 * NXCD * ma.pool;
+    ma.qctr = (uint32_t*)ws;
+  }
+  const int64_t grid = (int64_t)sa.blocks + total + (ma.ndyn - NXCD * ma.pool) + mf.blocks + aux.block_start[aux.count];
   if (grid > 0x7FFFFFFF) return fpi::fail(FP_ESHAPE, "%s: too many workgroups", fn);
   ma.gemm_blocks = (int32_t)total;
   if (grid == 0) return fpi::ok();
