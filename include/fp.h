@@ -585,7 +585,10 @@ size_t fp_layer_step_workspace(int32_t T, int32_t d_out, int32_t own_claim, int3
  * 256-byte aligned, needed when some map forms a claim (else may be NULL);
  * its first FP_MAX_MULTI * 64 + FP_FOLD_COUNTER_BYTES bytes (arrival counters,
  * the same layout as fp_layer_step_multi's, so one workspace serves both) must
- * be zero on entry and every call leaves them zero. Errors: FP_EARG (count outside [1,
+ * be zero on entry and every call leaves them zero. With a workspace and at
+ * least 1024 tiles (256 outputs x 128 tokens each), each XCD's last tiles are
+ * taken at run time by whichever workgroups get there first (counters in the
+ * same first lines); the results do not depend on who takes them. Errors: FP_EARG (count outside [1,
  * FP_MAX_MULTI], null pointers, group_o < 1), FP_ESHAPE (alignment, d_in >
  * FP_MAX_DIN, a claim without outputs), FP_ERANGE (s outside [1, 8]),
  * FP_EWORKSPACE. Maps must not write each other's inputs. */
