@@ -119,11 +119,8 @@ __device__ __forceinline__ void fragment_outputs(const v16i& accv, int32_t (&z)[
   }
 }
 
-// Y, R (and Z unless NULL) of 16 consecutive outputs o0.. of token t, held by one
-// lane after the swap; the caller has checked t < T and o0 < N.
-__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s) {
-  const int64_t idx = (int64_t)t * a.N + o0;
-  uint32_t yw[4], rw[4];
+// The Y and R bytes of 16 outputs, four to a word.
+__device__ __forceinline__ void yr_bytes(const int32_t (&z)[16], int s, uint32_t (&yw)[4], uint32_t (&rw)[4]) {
   int32_t y[16], r[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) rescale(z[q], s, y[q], r[q]);
@@ -132,6 +129,14 @@ __device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (
     yw[g] = pack_low_bytes(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]);
     rw[g] = pack_low_bytes(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
   }
+}
+
+// Y, R (and Z unless NULL) of 16 consecutive outputs o0.. of token t, held by one
+// lane after the swap; the caller has checked t < T and o0 < N.
+__device__ __forceinline__ void store_fragment(const WitArgs& a, const int32_t (&z)[16], int t, int o0, int s) {
+  const int64_t idx = (int64_t)t * a.N + o0;
+  uint32_t yw[4], rw[4];
+  yr_bytes(z, s, yw, rw);
   if (o0 + 16 <= a.N) {
     if (a.Z) {
       if (a.vecZ) {

@@ -125,6 +125,10 @@ struct MCfg {
   static constexpr int LOOP_BYTES = NBUF * BT * PITCH;
   static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
   static constexpr int LDS_BYTES = LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES;
+  // Y and R of one 32-token block of the tile staged below the claim's tables
+  // ([2][32][YP] bytes, double-buffered when it fits)
+  static constexpr int YP = BO + 16, YS_BYTES = 2 * 32 * YP;
+  static constexpr int NYB = 2 * YS_BYTES <= STAGE_BYTES ? 2 : (YS_BYTES <= STAGE_BYTES ? 1 : 0);
   // the weight fold's region after it: the panel's limb table, then two K
   // blocks of int32 limb sums [2 k-steps][32 columns][FL words]
   static constexpr int FL = 11;  // an odd row pitch: the 32 columns of one limb fall in distinct banks
@@ -380,7 +384,12 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   const int s = a.s;
   const bool stage = a.Z != nullptr && a.vecZ;
   const bool claim = a.cEt != nullptr;
-  if (stage || claim) __syncthreads();  // every wave is done with the X stages
+  // Y and R through LDS (the grouped launch, whose tiles are 32 tokens): each
+  // token block of the tile leaves as whole BO-byte row pieces (lanes of a
+  // fragment hold 16 bytes of 32 rows each). 0.8% faster on the MoE block;
+  // the layer's 128-token tiles measured no faster, so they store directly.
+  const bool yrs = FOLDW && C::NYB > 0 && a.Z == nullptr && a.vecYR;
+  if (stage || claim || yrs) __syncthreads();  // every wave is done with the X stages
   int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
   uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::STAGE_BYTES;
   uint64_t* etl = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);  // E_t of the tile's tokens
@@ -421,6 +430,7 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   uint64_t wsum = 0;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
+    uint8_t* yb = reinterpret_cast<uint8_t*>(lds) + (C::NYB > 1 ? j % C::NYB : 0) * C::YS_BYTES;
     v16i D[4];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -428,7 +438,15 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       fragment_outputs(acc[i][j], z);
       const int t = t_base + 32 * j + r;
       const int o0 = o_base + wo0 + 32 * i + 16 * h;
-      if (t < a.T && o0 < a.N) store_fragment(yr, z, t, o0, s);
+      if (yrs) {
+        uint32_t yw[4], rw[4];
+        yr_bytes(z, s, yw, rw);
+        const int c = wo0 + 32 * i + 16 * h;
+        *(v4i*)&yb[r * C::YP + c] = v4i{(int)yw[0], (int)yw[1], (int)yw[2], (int)yw[3]};
+        *(v4i*)&yb[(32 + r) * C::YP + c] = v4i{(int)rw[0], (int)rw[1], (int)rw[2], (int)rw[3]};
+      } else if (t < a.T && o0 < a.N) {
+        store_fragment(yr, z, t, o0, s);
+      }
       if (stage) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -462,6 +480,17 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       }
     }
     if (claim) wsum = gl::add(wsum, gl::mul(gl::add(claim_row_value(D, h), corr), etl[32 * j + r]));
+    if (yrs) {
+      __syncthreads();  // the block's rows are in LDS
+      constexpr int PR = BO / 16;  // 16-byte pieces per row
+      for (int q = tid; q < 2 * 32 * PR; q += NT) {
+        const int row = q / PR, c16 = q % PR;  // rows 0-31: Y, 32-63: R
+        const int t = t_base + 32 * j + (row & 31), o = o_base + 16 * c16;
+        if (t < a.T && o < a.N)  // N % 16 == 0: a piece is inside or past the row
+          *(v4i*)((row < 32 ? a.Y : a.R) + (int64_t)t * a.N + o) = *(const v4i*)&yb[row * C::YP + 16 * c16];
+      }
+      if constexpr (C::NYB == 1) __syncthreads();  // before the next block overwrites them
+    }
   }
   if (claim) claim_arrive(a, wsum, lt, nt, NW, red, reinterpret_cast<uint32_t*>(red + 8));
 }
