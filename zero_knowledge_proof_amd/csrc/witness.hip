@@ -279,11 +279,15 @@ struct WsCfg {
   static constexpr int NT = NW * 64, BO = NW * 32 * TM, BT = 32 * TN, BK = WP_BK;
   static constexpr int PITCH = BK + 16, CPR = BK / 16, CB = BT * CPR / NT, KS = BK / 32, HB = BK / 2;
   // the epilogue stages each wave's 32x32 int32 fragments in rows of EP words;
-  // the claim's limb table [CL_LIMBS][BO], the tile's E_t and reduction words follow
+  // the claim's limb table [CL_LIMBS][BO], the tile's E_t, reduction words and
+  // the waves' offset terms sit past both that and the X tiles
   static constexpr int EP = 36, STAGE_BYTES = NW * 32 * EP * 4;
-  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8;
-  static constexpr int EPI_BYTES = STAGE_BYTES + CLAIM_BYTES;
-  static constexpr int LDS_BYTES = 2 * BT * PITCH > EPI_BYTES ? 2 * BT * PITCH : EPI_BYTES;
+  static constexpr int LOOP_BYTES = 2 * BT * PITCH;
+  // the claim's tables sit past the X tiles and the Z staging: they are
+  // filled while the K loop runs
+  static constexpr int CLAIM_OFF = LOOP_BYTES > STAGE_BYTES ? LOOP_BYTES : STAGE_BYTES;
+  static constexpr int CLAIM_BYTES = CL_LIMBS * BO + 8 * BT + 16 * 8 + 8 * NW;
+  static constexpr int LDS_BYTES = CLAIM_OFF + CLAIM_BYTES;
   static_assert((BT * CPR) % NT == 0, "X chunks per thread");
 };
 
@@ -322,6 +326,44 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
     px[c] = a.X + (int64_t)min(t_base + row, a.T - 1) * a.ldx + (int64_t)kb0 * BK;
     so[c] = row * PITCH + kc[c];
   }
+  // the claim's tables: E_t and E_o are read before the K loop's first loads
+  // and put in LDS once those are issued (the loop's barriers order the
+  // writes before the epilogue's reads). The layer step runs one wave of
+  // tiles, so the tables' latency was on its critical path: 1% of a T=512
+  // step. (Y and R staged through LDS as whole row pieces measured 2% slower.)
+  uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::CLAIM_OFF;
+  uint64_t* etl = reinterpret_cast<uint64_t*>(lds + C::CLAIM_OFF + CL_LIMBS * BO);  // E_t of the tile's tokens
+  uint64_t* red = etl + BT;
+  uint64_t* wcorr = red + 16;
+  const bool claim = EPI == 0 && a.cEt != nullptr;
+  static_assert(BT <= NT && BO <= NT, "one E_t and one E_o entry per thread");
+  uint64_t et_v = 0, eo_v = 0;
+  auto load_tables = [&]() {
+    if (!claim) return;
+    if (tid < BT && t_base + tid < a.T) et_v = a.cEt[t_base + tid];
+    // zero past d_out, so rows of Z there, computed from clamped weight blocks, do not count
+    if (tid < BO && o_base + tid < a.N) eo_v = a.cEo[o_base + tid];
+  };
+  auto write_tables = [&]() {
+    if (!claim) return;
+    if (tid < BT) etl[tid] = et_v;
+    uint64_t se = 0;
+    if (tid < BO) {
+#pragma unroll
+      for (int m = 0; m < CL_LIMBS; ++m) limbs[m * BO + tid] = (uint8_t)((eo_v >> (7 * m)) & 127u);
+      if constexpr (BO == NT) se = eo_v;  // output tid is lane tid % 64 of its wave's range
+    }
+    if constexpr (BO != NT) {
+#pragma unroll
+      for (int x = lane; x < 32 * TM; x += 64) {
+        const int o = o_base + wo0 + x;
+        if (o < a.N) se = gl::add(se, a.cEo[o]);
+      }
+    }
+    se = fpi::wave_total(se);  // every lane takes part
+    if (lane == 0) wcorr[wave] = gl::mul_small(se, 128u * 65793u);
+  };
+  load_tables();
   v4i wf[PFW][TM][KS];
   v4i xr[PFX][CB];
   auto wload = [&](int slot, int kblk) {
@@ -374,6 +416,7 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
     for (int p = 0; p < PFX; ++p) xload(p, min(p, KT - 1));
     sstore(0, 0);
     xload(0, min(PFX, KT - 1));
+    write_tables();
     __syncthreads();
     auto step = [&](auto uc, int st) {
       constexpr int u = decltype(uc)::value;
@@ -391,6 +434,8 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ((kt + I < KT ? step(std::integral_constant<int, I>{}, kt + I) : void()), ...);
     }(std::make_integer_sequence<int, U>{});
+  } else {
+    write_tables();
   }
 
   if constexpr (EPI == 1) {
@@ -411,42 +456,15 @@ __device__ __forceinline__ void witness_body_ws(const WitArgs& a, int bid, int n
   // so direct stores write 32-byte pieces of 32 rows; staged, eight lanes
   // write a row's whole 128 bytes.
   const bool stage = a.Z != nullptr && a.vecZ;
-  const bool claim = a.cEt != nullptr;
   if (stage || claim) __syncthreads();  // every wave is done with the X tiles
   int32_t* E = reinterpret_cast<int32_t*>(lds) + wave * 32 * C::EP;
-  uint8_t* limbs = reinterpret_cast<uint8_t*>(lds) + C::STAGE_BYTES;
-  uint64_t* etl = reinterpret_cast<uint64_t*>(lds + C::STAGE_BYTES + CL_LIMBS * BO);  // E_t of the tile's tokens
-  uint64_t* red = etl + BT;
   v4i Aop[TM];
   uint64_t corr = 0;  // the planes' offsets, added once per token (by the h = 0 lanes)
   if (claim) {
-    for (int x = tid; x < BT; x += NT) {
-      const int t = t_base + x;
-      etl[x] = t < a.T ? a.cEt[t] : 0;
-    }
-    // limb table of the tile's outputs (zero past d_out, so rows of Z there,
-    // computed from clamped weight blocks, do not count)
-    uint64_t se = 0;
-    for (int x = tid; x < BO; x += NT) {
-      const int o = o_base + x;
-      const uint64_t e = o < a.N ? a.cEo[o] : 0;
-#pragma unroll
-      for (int m = 0; m < CL_LIMBS; ++m) limbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
-      if constexpr (BO == NT) se = e;  // output tid is lane tid % 64 of its wave's range
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       Aop[i] = r < CL_LIMBS ? *(const v4i*)&limbs[r * BO + wo0 + 32 * i + 16 * h] : v4i{0, 0, 0, 0};
-    if constexpr (BO != NT) {
-#pragma unroll
-      for (int x = lane; x < 32 * TM; x += 64) {
-        const int o = o_base + wo0 + x;
-        if (o < a.N) se = gl::add(se, a.cEo[o]);
-      }
-    }
-    se = fpi::wave_total(se);  // every lane takes part (outside the lane-dependent select below)
-    corr = h == 0 ? gl::mul_small(se, 128u * 65793u) : 0;
+    corr = h == 0 ? wcorr[wave] : 0;
   }
   WitArgs yr = a;
   if (stage) yr.Z = nullptr;
