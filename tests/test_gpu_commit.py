@@ -45,7 +45,7 @@ def test_commit_pack(fp, na, nb, logn, extra):
 
 
 @pytest.mark.parametrize("rows,logn", [(1, 0), (1, 1), (2, 3), (3, 7), (1, 8), (2, 9), (1, 11), (3, 12), (2, 15),
-                                       (1, 16), (2, 17), (1, 19)])
+                                       (1, 16), (3, 16), (2, 17), (2, 18), (1, 19)])
 def test_rs_encode(fp, rows, logn):
     rng = np.random.default_rng(100 + logn)
     msg = _field(rng, (rows, 1 << logn))
