@@ -161,12 +161,24 @@ void add_claims(std::vector<Item>& v, fp_dtype dt, int32_t count, const fp_claim
   }
 }
 
+// Workgroups per job: a launch of int8 folds alone runs best at about two per
+// compute unit (the up-projection's folds of X and W: 17.3 us with 512, 19.0
+// with 256, 18.5 with 768, 19.4 with 1024: more chunks lengthen the cross-chunk
+// sums); with an int32 claim in the launch, about one per compute unit (those
+// folds beside the claim of its Z: 22.6 us, against 23.0 with 512 for the folds).
+int target_blocks(const std::vector<Item>& v) {
+  for (const Item& it : v)
+    if (it.claim || it.j.eb != 1) return 256;
+  return 512;
+}
+
 // Workspace: the partials of every job, back to back.
 size_t items_ws(const std::vector<Item>& v) {
   size_t parts = 0;
+  const int tb = target_blocks(v);
   for (const Item& it : v) {
     if (it.j.rows <= 0 || it.j.cols <= 0) continue;
-    parts += plan_job(it.j.rows, it.j.cols, it.j.cols_pad, it.j.eb, it.claim, false).part_bytes;
+    parts += plan_job(it.j.rows, it.j.cols, it.j.cols_pad, it.j.eb, it.claim, false, tb).part_bytes;
   }
   return parts;
 }
@@ -178,6 +190,7 @@ int run_items(std::vector<Item>& v, char* ws, hipStream_t st) {
   JobList jl{};
   SumList sl{};
   int64_t blocks = 0, sblocks = 0;
+  const int tb = target_blocks(v);
   auto flush = [&]() -> int {
     int rc = launch_list(jl, blocks, st);
     if (!rc && sblocks > 0) {
@@ -204,7 +217,7 @@ int run_items(std::vector<Item>& v, char* ws, hipStream_t st) {
       return fpi::fail(FP_ESHAPE, "fold: row stride %lld x %d rows exceeds 2^31 bytes", (long long)j.ld, FMAX_CHUNK);
     const uintptr_t align = eb == 1 ? 3 : 15;
     j.vec = (j.cols % 4 == 0) && (j.ld % 4 == 0) && (((uintptr_t)j.M & align) == 0);
-    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, eb, claim, false);
+    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, eb, claim, false, tb);
     j.chunk_rows = p.chunk_rows;
     j.n_chunks = p.n_chunks;
     j.n_strips = p.n_strips;

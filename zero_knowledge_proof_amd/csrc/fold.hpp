@@ -443,18 +443,18 @@ struct Plan {
 
 // arrive: the sums are done by the last workgroups of the same launch (the
 // padding strips are then always workgroups of their own).
-inline Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool claim, bool arrive) {
+inline Plan plan_job(int32_t rows, int32_t cols, int32_t cols_pad, int eb, bool claim, bool arrive,
+                     int target_blocks = 256) {
   Plan p{};
   p.n_strips = (cols + FCOLS - 1) / FCOLS;
   const int pad_total = (cols_pad + FCOLS - 1) / FCOLS;
   p.n_pad_strips = claim ? 0 : (pad_total - p.n_strips);
-  // a launch of its own: about one workgroup per compute unit (measured
-  // against 128-1536 on the up-projection: fewer chunks also shorten the
-  // cross-chunk sums), chunks in whole pairs of batches. Inside a step launch
+  // a launch of its own: about target_blocks workgroups per job (fold.hip
+  // asks for two per compute unit when a launch holds int8 folds only, one
+  // otherwise), chunks in whole pairs of batches. Inside a step launch
   // the folds of several tables share the GPU with the GEMM's last tiles:
   // the longest chunks (measured against 256-row and 512-row minimums on the
   // seven-map layer: 6 us per step less than one workgroup per CU per job).
-  const int target_blocks = 256;
   const int q = eb == 1 ? kRowQuantum<1> : kRowQuantum<4>;
   const int want_chunks = (target_blocks + p.n_strips - 1) / p.n_strips;
   int64_t cr = (rows + want_chunks - 1) / want_chunks;
