@@ -161,24 +161,33 @@ void add_claims(std::vector<Item>& v, fp_dtype dt, int32_t count, const fp_claim
   }
 }
 
-// Workgroups per job: a launch of int8 folds alone runs best at about two per
-// compute unit (the up-projection's folds of X and W: 17.3 us with 512, 19.0
-// with 256, 18.5 with 768, 19.4 with 1024: more chunks lengthen the cross-chunk
-// sums); with an int32 claim in the launch, about one per compute unit (those
-// folds beside the claim of its Z: 22.6 us, against 23.0 with 512 for the folds).
-int target_blocks(const std::vector<Item>& v) {
-  for (const Item& it : v)
-    if (it.claim || it.j.eb != 1) return 256;
-  return 512;
+// Workgroups per job: about 256 (one per compute unit), except that a launch
+// of int8 folds alone aims at about 512 in all (two per compute unit), shared
+// by its jobs in proportion to their rows. The up-projection's folds of X and
+// W: 17.3 us with 512 for W, 19.0 with 256, 18.5 with 768, 19.4 with 1024 (more
+// chunks lengthen the cross-chunk sums); with the claim of its Z beside them,
+// 22.6 us at 256 per job against 23.0 with 512 for the folds; the seven-map
+// layer's 28 extension folds: 0.111 ms at 256 per job, 0.128 with 512 each.
+int64_t fold_rows_only(const std::vector<Item>& v) {  // rows of a launch of int8 folds alone, else 0
+  int64_t rows = 0;
+  for (const Item& x : v) {
+    if (x.claim || x.j.eb != 1) return 0;
+    if (x.j.rows > 0 && x.j.cols > 0) rows += x.j.rows;
+  }
+  return rows;
+}
+int job_target(int64_t launch_rows, const Item& it) {
+  const int64_t t = launch_rows > 0 ? 512 * (int64_t)it.j.rows / launch_rows : 256;
+  return t > 256 ? (int)t : 256;
 }
 
 // Workspace: the partials of every job, back to back.
 size_t items_ws(const std::vector<Item>& v) {
   size_t parts = 0;
-  const int tb = target_blocks(v);
+  const int64_t lr = fold_rows_only(v);
   for (const Item& it : v) {
     if (it.j.rows <= 0 || it.j.cols <= 0) continue;
-    parts += plan_job(it.j.rows, it.j.cols, it.j.cols_pad, it.j.eb, it.claim, false, tb).part_bytes;
+    parts += plan_job(it.j.rows, it.j.cols, it.j.cols_pad, it.j.eb, it.claim, false, job_target(lr, it)).part_bytes;
   }
   return parts;
 }
@@ -190,7 +199,7 @@ int run_items(std::vector<Item>& v, char* ws, hipStream_t st) {
   JobList jl{};
   SumList sl{};
   int64_t blocks = 0, sblocks = 0;
-  const int tb = target_blocks(v);
+  const int64_t lr = fold_rows_only(v);
   auto flush = [&]() -> int {
     int rc = launch_list(jl, blocks, st);
     if (!rc && sblocks > 0) {
@@ -217,7 +226,7 @@ int run_items(std::vector<Item>& v, char* ws, hipStream_t st) {
       return fpi::fail(FP_ESHAPE, "fold: row stride %lld x %d rows exceeds 2^31 bytes", (long long)j.ld, FMAX_CHUNK);
     const uintptr_t align = eb == 1 ? 3 : 15;
     j.vec = (j.cols % 4 == 0) && (j.ld % 4 == 0) && (((uintptr_t)j.M & align) == 0);
-    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, eb, claim, false, tb);
+    const Plan p = plan_job(j.rows, j.cols, j.cols_pad, eb, claim, false, job_target(lr, it));
     j.chunk_rows = p.chunk_rows;
     j.n_chunks = p.n_chunks;
     j.n_strips = p.n_strips;
