@@ -333,7 +333,12 @@ def request_vectors_leg(cfg, inp, dev, steps: int, per_graph: int, with_cpu: boo
         "roofline": {"bound": "mfma", "achieved": round(ops / t_multi / 1e12, 1), "peak": MFMA_I8_PEAK / 1e12,
                      "unit": "TFLOP/s", "frac": round(ops / t_multi / MFMA_I8_PEAK, 4),
                      "traffic": None, "algorithmic_ops": ops,
-                     "note": "the whole call (digits, limb GEMM, chunk sum) timed; int8 ops of the limb GEMM"},
+                     # the method's own bytes: the weights once, the R eq vectors, the R folded rows
+                     "algorithmic_bytes": rows * cols + 8 * R * rows + 8 * R * cols,
+                     "hbm_GBps": round((rows * cols + 8 * R * rows + 8 * R * cols) / t_multi / 1e9, 1),
+                     "note": "the whole call (digits, limb GEMM, chunk sum) timed; int8 ops of the limb GEMM, whose "
+                             "byte digits expand each eq weight into 8 rows; hbm_GBps: the method's own bytes (weights "
+                             "once, eq vectors, folded rows) over the call's time"},
     }
     if with_cpu:
         import oracle
