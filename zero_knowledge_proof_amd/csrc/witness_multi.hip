@@ -129,11 +129,13 @@ struct MCfg {
   // ([2][32][YP] bytes, double-buffered when it fits)
   static constexpr int YP = BO + 16, YS_BYTES = 2 * 32 * YP;
   static constexpr int NYB = 2 * YS_BYTES <= STAGE_BYTES ? 2 : (YS_BYTES <= STAGE_BYTES ? 1 : 0);
-  // the weight fold's region after it: the panel's limb table, then two K
-  // blocks of int32 limb sums [2 k-steps][32 columns][FL words]
+  // the weight fold's region after it: the panel's limb table, then 2 NW K
+  // blocks of int32 limb sums [2 k-steps][32 columns][FL words] (two groups
+  // of NW blocks: one filling while the other is turned into field values)
   static constexpr int FL = 11;  // an odd row pitch: the 32 columns of one limb fall in distinct banks
   static constexpr int FOLD_ACC_WORDS = 2 * 32 * FL;
-  static constexpr int FOLD_BYTES = CL_LIMBS * BO + 2 * FOLD_ACC_WORDS * 4;
+  static constexpr int FOLD_SLOTS = 2 * NW;
+  static constexpr int FOLD_BYTES = CL_LIMBS * BO + FOLD_SLOTS * FOLD_ACC_WORDS * 4;
   static constexpr int LDS_FOLD_BYTES = LDS_BYTES + FOLD_BYTES;
   static_assert(NCB % NT == 0 || NCB < NT, "X chunks: whole rounds, or fewer chunks than threads");
   static_assert(KS == 2 * SB, "two k-steps per packed K block");
@@ -147,9 +149,12 @@ struct MCfg {
 // consecutive rows of one column, which is an MFMA B operand with the rows as
 // the reduction index; an MFMA with the 7-bit limbs of E_o as the A operand
 // then gives sum_o limb_m(E_o[o]) W[o, k] for the fragment's columns. The
-// waves' int32 limb sums meet in LDS (exact: |sum| < 2^7 2^7 BO), and after the
-// K block's barrier wave 0 turns each column's limbs into one field value
-// sum_m 2^(7m) sum_o ... = sum_o E_o[o] W[o, k] mod p for the panel.
+// waves' int32 limb sums meet in LDS (exact: |sum| < 2^7 2^7 BO), and once a
+// group of NW K blocks is complete (after a barrier) each wave turns one block's
+// limbs into field values sum_m 2^(7m) sum_o ... = sum_o E_o[o] W[o, k] mod p
+// for the panel, at the end of the step that completes the next group, after
+// its products are issued (wave 0 turning every block at the start of the next
+// step held the matrix cores: the MoE block's step 2.70 ms, 2.32 without it).
 template <int NW, int TM, int TN, int PFW, int PFX, int NBUF, int SCHED, int FOLDW = 0, int SB = 1>
 __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int group_o, int8_t* lds) {
   static_assert(SB == 1 || SB == 2, "one or two packed K blocks per stage");
@@ -234,7 +239,7 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
   // ---- the weight fold's set-up (FOLDW, first token tile of the panel)
   const bool fold_on = FOLDW && a.fpart != nullptr && tt == 0;  // uniform over the workgroup
   uint8_t* flimbs = reinterpret_cast<uint8_t*>(lds + C::LDS_BYTES);
-  int32_t* facc = reinterpret_cast<int32_t*>(lds + C::LDS_BYTES + CL_LIMBS * BO);  // [2][FOLD_ACC_WORDS]
+  int32_t* facc = reinterpret_cast<int32_t*>(lds + C::LDS_BYTES + CL_LIMBS * BO);  // [FOLD_SLOTS][FOLD_ACC_WORDS]
   v4i FA[TM];   // limbs of E_o for the wave's row blocks (A operand, reduction over the rows)
   v4i FI = {};  // the identity as a B operand: lane (n, h) holds rows 16 h .. 16 h + 15 of column n
   if constexpr (FOLDW) {
@@ -245,7 +250,7 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
 #pragma unroll
         for (int m = 0; m < CL_LIMBS; ++m) flimbs[m * BO + x] = (uint8_t)((e >> (7 * m)) & 127u);
       }
-      for (int x = tid; x < 2 * C::FOLD_ACC_WORDS; x += NT) facc[x] = 0;
+      for (int x = tid; x < C::FOLD_SLOTS * C::FOLD_ACC_WORDS; x += NT) facc[x] = 0;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         uint32_t w = 0;
@@ -262,12 +267,12 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
           FA[i][d] = r < CL_LIMBS ? *(const int*)&flimbs[r * BO + wo0 + 32 * i + 8 * d + 4 * h] : 0;
     }
   }
-  // K block st's fragments folded into LDS buffer st % 2. The transpose's
+  // K block st's fragments folded into LDS slot st % FOLD_SLOTS. The transpose's
   // accumulators hold, in lane (r, h) register v, row 8 (v / 4) + 4 h + v % 4
   // of column r: packed in register order they are the B operand, the limb
   // operand FA pairing the same rows with the same reduction index.
   auto fold_block = [&](int ws, int st) {
-    int32_t* F = facc + (st & 1) * C::FOLD_ACC_WORDS;
+    int32_t* F = facc + (st % C::FOLD_SLOTS) * C::FOLD_ACC_WORDS;
     const v16i zero = {};
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
@@ -288,12 +293,11 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       }
     }
   };
-  // wave 0: K block st's limb sums -> one field value per column, then the
-  // buffer cleared for block st + 2. The limbs of each half are exact in int64
-  // (|sum| < 2^22, 5 limbs of 7 bits): lo + 2^35 hi.
+  // the calling wave: K block st's limb sums -> one field value per column,
+  // then its slot cleared for block st + FOLD_SLOTS. The limbs of each half are
+  // exact in int64 (|sum| < 2^22, 5 limbs of 7 bits): lo + 2^35 hi.
   auto fold_flush = [&](int st) {
-    if (wave != 0) return;
-    int32_t* F = facc + (st & 1) * C::FOLD_ACC_WORDS + lane * C::FL;  // lane = column q * 32 + n
+    int32_t* F = facc + (st % C::FOLD_SLOTS) * C::FOLD_ACC_WORDS + lane * C::FL;  // lane = column q * 32 + n
     int64_t lo = 0, hi = 0;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
@@ -331,9 +335,7 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
     auto step = [&](auto uc, int st) {
       constexpr int u = decltype(uc)::value;
       constexpr int buf = u % NBUF, ws = u % PFW;
-      if constexpr (FOLDW) {
-        if (fold_on && st > 0) fold_flush(st - 1);
-      }
+
       if constexpr (NBUF < 3) fread(0, buf, 0);
       fread(1, buf, 1);
       mma(0, ws, 0);
@@ -353,6 +355,10 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
       }
       if constexpr (FOLDW) {
         if (fold_on) fold_block(ws, st);
+        // a group of NW blocks ends with this one: the group before it (complete
+        // since an earlier barrier) is turned into field values, one block per
+        // wave, while this step's products are still in the matrix cores
+        if (fold_on && (st + 1) % NW == 0 && st + 1 >= 2 * NW) fold_flush(st + 1 - 2 * NW + wave);
       }
       wload(ws, min(st + PFW, NS - 1));
       if constexpr (NBUF >= 3) fread(0, (u + 1) % NBUF, 0);
@@ -375,8 +381,11 @@ __device__ __forceinline__ void multi_body(const WitArgs& a, int lt, int nt, int
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ((kt + I < NS ? step(std::integral_constant<int, I>{}, kt + I) : void()), ...);
     }(std::make_integer_sequence<int, U>{});
-    if constexpr (FOLDW) {
-      if (fold_on) fold_flush(NS - 1);  // the last K block (its sums are complete after the last barrier)
+    if constexpr (FOLDW) {  // the groups not yet turned (complete after the last barrier)
+      if (fold_on) {
+        for (int g = (NS / NW >= 1 ? NS / NW - 1 : 0) * NW; g < NS; g += NW)
+          if (g + wave < NS) fold_flush(g + wave);
+      }
     }
   }
 
