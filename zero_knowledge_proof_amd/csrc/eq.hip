@@ -16,11 +16,14 @@ struct EqJob {
   int32_t n;
   int32_t block_start;
 };
-constexpr int EQ_INLINE = 48;  // descriptors carried in one launch's arguments
+// descriptors carried in one launch's arguments (the MoE block's ~370 tables
+// of a step in three launches instead of eight)
+constexpr int EQ_INLINE = 160;
 struct EqList {
   EqJob j[EQ_INLINE];
   int32_t count;
 };
+static_assert(sizeof(EqList) <= 4096, "an eq list travels in the kernel arguments");
 
 // Mid variables of an n-variable table: 4 (4096 entries per workgroup) once
 // the table has at least 2^16 entries, none below (256 per workgroup, more
@@ -28,11 +31,15 @@ struct EqList {
 __host__ __device__ constexpr int eq_mid(int n) { return n >= 16 ? 4 : 0; }
 
 __global__ __launch_bounds__(256) void eq_kernel(EqList jl) {
-  int k = 0;
+  // the last job whose first workgroup is at or before this one (binary search)
+  int lo = 0, hi = jl.count - 1;
 #pragma unroll 1
-  for (int q = 1; q < jl.count; ++q)
-    if (jl.j[q].block_start <= (int)blockIdx.x) k = q;
-  const EqJob& j = jl.j[k];
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (jl.j[mid].block_start <= (int)blockIdx.x) lo = mid;
+    else hi = mid - 1;
+  }
+  const EqJob& j = jl.j[lo];
   eqk::eq_block(j.r, j.n, j.E, (int)blockIdx.x - j.block_start, eq_mid(j.n));
 }
 
